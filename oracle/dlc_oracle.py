@@ -1,0 +1,355 @@
+"""fp64 CPU oracle: what the CSA/HCA hot path computes, written out plainly.
+
+TEST INFRASTRUCTURE ONLY (tests, smoke check, benchmark CPU baseline).
+
+Sources, cited by page title and section:
+
+* [Scratch] "DeepSeek-V4 Hybrid Attention: CSA and HCA from Scratch"
+  (prathamp.com).  The authority on what the method computes.
+* [Stack] "DeepSeek's attention stack: how DSA, CSA, HCA and mHC fit
+  together" (dev.to).  Hyper-parameters and context only.
+* [Evolution] "From MHA, GQA to MLA, DSA, HCA/CSA" (bhhxx.wiki, Chinese).
+  A second formula source; where it differs from [Scratch], [Scratch] wins.
+
+Everything is numpy float64.  Inputs stored in bf16 or fp32 are upcast
+exactly.  Where the method stores an intermediate (projected streams,
+compressed caches, queries), ``store`` mirrors that rounding so an
+end-to-end chain sees the same values a device that stores them would.
+
+Readings of points the pages leave open (each listed in the design notes):
+
+* joint softmax over all 2m rows of a CSA window ([Scratch] §4), not two
+  separate block softmaxes as [Evolution] §6.2.2 writes;
+* the i = 0 window's missing b-rows are excluded from the softmax (their
+  logit is -inf and weight exactly 0, [Scratch] §4 "Block i = 0");
+* visibility s < floor(t/m) for CSA and s < floor(t/m') for HCA
+  ([Scratch] §7 and §10);
+* k larger than the visible count keeps everything (k_eff = min(k, vis));
+* top-k ties: larger score first, then smaller index; -0.0 equals +0.0;
+* nothing visible: output 0 and log-sum-exp -inf;
+* both attentions scale logits by 1/sqrt(c) ([Scratch] §8, applied to HCA
+  through the unified operator of §11); the indexer is unscaled (§6.4).
+"""
+
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+__all__ = [
+    "f64",
+    "round_bf16",
+    "store_as",
+    "project",
+    "column_softmax",
+    "csa_window_weights",
+    "csa_compress",
+    "hca_window_weights",
+    "hca_compress",
+    "csa_visible",
+    "hca_visible",
+    "index_scores",
+    "topk_select",
+    "mqa_attend",
+    "csa_attend",
+    "hca_attend",
+    "split_heads",
+    "queries_from_hidden",
+    "decode_chain",
+    "gqa_kv_bytes_per_token_layer",
+    "compressed_bytes_per_token_layer",
+    "ledger",
+    "indexer_flops_per_query",
+]
+
+
+# --------------------------------------------------------------------------
+# number formats
+# --------------------------------------------------------------------------
+
+def f64(x) -> np.ndarray:
+    """Exact upcast to float64 (bf16 and fp32 values are all representable)."""
+    if hasattr(x, "detach"):  # a torch tensor: go through float32, which is exact for bf16
+        x = x.detach().to("cpu").float().numpy()
+    return np.asarray(x, dtype=np.float64)
+
+
+def round_bf16(x) -> np.ndarray:
+    """Round float64 values to the nearest bfloat16 (ties to even), as float64.
+
+    bfloat16 keeps 8 significant bits.  frexp gives x = f * 2**e with
+    0.5 <= |f| < 1, so f * 2**8 lies in [128, 256) and rounding it to an
+    integer with ties-to-even (np.rint) keeps exactly 8 significant bits.
+    Values here stay far from the bf16 subnormal and overflow ranges.
+    """
+    x = f64(x)
+    f, e = np.frexp(x)
+    return np.ldexp(np.rint(f * 256.0), e - 8)
+
+
+def store_as(x, dtype: str) -> np.ndarray:
+    """Mirror the rounding of storing ``x`` in ``dtype`` ('bf16' | 'f32' | 'f64')."""
+    if dtype == "bf16":
+        return round_bf16(x)
+    if dtype == "f32":
+        return f64(np.asarray(f64(x), dtype=np.float32))
+    if dtype == "f64":
+        return f64(x)
+    raise ValueError(f"unknown storage dtype {dtype!r}")
+
+
+# --------------------------------------------------------------------------
+# projections ([Scratch] §3 and §6.1-6.3, §8, §10)
+# --------------------------------------------------------------------------
+
+def project(H, W) -> np.ndarray:
+    """Dense projection of hidden states, e.g. C^a = H W^{aKV} ([Scratch] §3)."""
+    return f64(H) @ f64(W)
+
+
+def split_heads(v, n_heads: int, width: int) -> np.ndarray:
+    """[q_1; ...; q_nh] = v: head h takes columns h*width ... (h+1)*width-1
+    ([Scratch] §6.2 and §8 write the heads side by side)."""
+    v = f64(v)
+    assert v.shape[-1] == n_heads * width
+    return v.reshape(v.shape[:-1] + (n_heads, width))
+
+
+# --------------------------------------------------------------------------
+# compressor ([Scratch] §2, §4, §5, §10)
+# --------------------------------------------------------------------------
+
+def column_softmax(logits) -> np.ndarray:
+    """Softmax down the rows, independently for every column ([Scratch] §4,
+    "Softmax_row").  Computed max-subtracted, which is the same value."""
+    L = f64(logits)
+    e = np.exp(L - L.max(axis=0, keepdims=True))
+    return e / e.sum(axis=0, keepdims=True)
+
+
+def csa_window_weights(Za, Zb, m: int, i: int, Ba=None, Bb=None):
+    """Softmax weights of CSA entry i ([Scratch] §4).
+
+    The window stacks the a-rows m*i ... m*(i+1)-1 (current block) over the
+    b-rows m*(i-1) ... m*i-1 (previous block); one softmax per column runs
+    jointly over all 2m stacked logits Z + B.  For i = 0 the b-rows do not
+    exist: their logit is -inf, so they are left out and get weight 0.
+
+    Returns (S_a [m][c], S_b [m][c]); S_b is all zeros for i = 0.
+    """
+    Za, Zb = f64(Za), f64(Zb)
+    c = Za.shape[1]
+    Ba = np.zeros((m, c)) if Ba is None else f64(Ba)
+    Bb = np.zeros((m, c)) if Bb is None else f64(Bb)
+    la = Za[m * i:m * (i + 1)] + Ba
+    if i == 0:
+        return column_softmax(la), np.zeros((m, c))
+    lb = Zb[m * (i - 1):m * i] + Bb
+    S = column_softmax(np.vstack([la, lb]))
+    return S[:m], S[m:]
+
+
+def csa_compress(Za, Zb, Ca, Cb, m: int, Ba=None, Bb=None, i_begin: int = 0, i_end=None):
+    """CSA compressed entries i_begin ... i_end-1 ([Scratch] §5, boxed formula):
+
+        C^Comp_i = sum_{j in block i} S^a_j (.) C^a_j + sum_{j in block i-1} S^b_j (.) C^b_j
+    """
+    Za, Zb, Ca, Cb = f64(Za), f64(Zb), f64(Ca), f64(Cb)
+    n, c = Za.shape
+    if i_end is None:
+        i_end = n // m
+    assert 0 <= i_begin <= i_end <= n // m
+    out = np.zeros((i_end - i_begin, c))
+    for i in range(i_begin, i_end):
+        Sa, Sb = csa_window_weights(Za, Zb, m, i, Ba, Bb)
+        acc = (Sa * Ca[m * i:m * (i + 1)]).sum(axis=0)
+        if i > 0:
+            acc = acc + (Sb * Cb[m * (i - 1):m * i]).sum(axis=0)
+        out[i - i_begin] = acc
+    return out
+
+
+def hca_window_weights(Z, m_prime: int, i: int, B=None):
+    """HCA weights of entry i: one softmax per column over the m' rows of the
+    non-overlapping block i ([Scratch] §10)."""
+    Z = f64(Z)
+    c = Z.shape[1]
+    B = np.zeros((m_prime, c)) if B is None else f64(B)
+    return column_softmax(Z[m_prime * i:m_prime * (i + 1)] + B)
+
+
+def hca_compress(Z, C, m_prime: int, B=None, i_begin: int = 0, i_end=None):
+    """HCA compressed entries ([Scratch] §10, boxed formula):
+    C_i = sum_{j in block i} S_j (.) C_j, blocks of m' rows, no overlap."""
+    Z, C = f64(Z), f64(C)
+    n, c = Z.shape
+    if i_end is None:
+        i_end = n // m_prime
+    assert 0 <= i_begin <= i_end <= n // m_prime
+    out = np.zeros((i_end - i_begin, c))
+    for i in range(i_begin, i_end):
+        S = hca_window_weights(Z, m_prime, i, B)
+        out[i - i_begin] = (S * C[m_prime * i:m_prime * (i + 1)]).sum(axis=0)
+    return out
+
+
+# --------------------------------------------------------------------------
+# visibility, indexer, selection ([Scratch] §6, §7, §10)
+# --------------------------------------------------------------------------
+
+def csa_visible(t: int, m: int) -> int:
+    """Number of CSA entries query t may see: s < floor(t/m) ([Scratch] §7)."""
+    return t // m
+
+
+def hca_visible(t: int, m_prime: int) -> int:
+    """Number of HCA entries query t may see: s < floor(t/m') ([Scratch] §10)."""
+    return t // m_prime
+
+
+def index_scores(qI, wI, KI, t: int, m: int) -> np.ndarray:
+    """Lightning-indexer scores over the visible CSA entries ([Scratch] §6.4):
+
+        I_{t,s} = sum_h w^I_{t,h} * ReLU(q^I_{t,h} . K^IComp_s),   s < floor(t/m)
+
+    No softmax and no scale.  -0.0 is returned as +0.0.
+    """
+    qI, wI, KI = f64(qI), f64(wI), f64(KI)
+    nvis = csa_visible(t, m)
+    dots = KI[:nvis] @ qI.T                 # [nvis][n_hI]
+    scores = np.maximum(dots, 0.0) @ wI     # [nvis]
+    return scores + 0.0
+
+
+def topk_select(scores, k: int) -> np.ndarray:
+    """Indices of the k largest scores, returned in ascending index order
+    ([Scratch] §7).  k larger than the candidate count keeps them all.
+    Ties: the larger score ranks first, then the smaller index."""
+    s = f64(scores)
+    n = s.shape[0]
+    k_eff = min(int(k), n)
+    order = np.lexsort((np.arange(n), -s))  # last key is primary
+    return np.sort(order[:k_eff]).astype(np.int64)
+
+
+# --------------------------------------------------------------------------
+# shared-KV multi-query attention ([Scratch] §8, §10, §11)
+# --------------------------------------------------------------------------
+
+def mqa_attend(q, KV, scale=None):
+    """Shared-KV MQA ([Scratch] §8): for every head h,
+
+        o_h = sum_s softmax_s(q_h . KV_s * scale) KV_s,   lse_h = log sum_s exp(q_h . KV_s * scale)
+
+    with key = value = KV_s and scale = 1/sqrt(c).  An empty KV set gives
+    o = 0 and lse = -inf.
+    """
+    q, KV = f64(q), f64(KV)
+    nh, c = q.shape
+    if scale is None or scale <= 0:
+        scale = 1.0 / math.sqrt(c)
+    if KV.shape[0] == 0:
+        return np.zeros((nh, c)), np.full(nh, -np.inf)
+    logits = (q @ KV.T) * scale                       # [nh][N]
+    mx = logits.max(axis=1, keepdims=True)
+    e = np.exp(logits - mx)
+    ssum = e.sum(axis=1)
+    o = (e @ KV) / ssum[:, None]
+    lse = mx[:, 0] + np.log(ssum)
+    return o, lse
+
+
+def csa_attend(q, Ccomp, idx, scale=None):
+    """Core CSA attention over the selected entries C^SprsComp ([Scratch] §8)."""
+    Ccomp = f64(Ccomp)
+    idx = np.asarray(idx, dtype=np.int64)
+    return mqa_attend(q, Ccomp[idx], scale)
+
+
+def hca_attend(q, Chca, t: int, m_prime: int, scale=None):
+    """Dense HCA attention over every visible HCA entry ([Scratch] §10)."""
+    Chca = f64(Chca)
+    return mqa_attend(q, Chca[:hca_visible(t, m_prime)], scale)
+
+
+# --------------------------------------------------------------------------
+# a whole decode query, from hidden states ([Scratch] §3-§10)
+# --------------------------------------------------------------------------
+
+def queries_from_hidden(h_t, W_DQ, W_IUQ, W_w, W_UQ, W_UQ_hca, n_h, c, n_hI, cI, dtype="f64"):
+    """Query side of one token ([Scratch] §6.1-6.3 and §8).
+
+    c^Q = h_t W^{DQ};  [q^I_1; ...] = c^Q W^{IUQ};  w^I = h_t W^w;
+    [q_1; ...] = c^Q W^{UQ}.  HCA gets its own up-projection W^{UQ,HCA} of
+    the same latent (the pages name no HCA query projection of their own).
+    Stored intermediates are rounded as ``dtype`` storage would; w^I is kept
+    in fp32.
+    """
+    cQ = store_as(project(h_t, W_DQ), dtype)
+    qI = store_as(split_heads(project(cQ, W_IUQ), n_hI, cI), dtype)
+    wI = store_as(project(h_t, W_w), "f32")
+    q = store_as(split_heads(project(cQ, W_UQ), n_h, c), dtype)
+    q_hca = store_as(split_heads(project(cQ, W_UQ_hca), n_h, c), dtype)
+    return dict(cQ=cQ, qI=qI, wI=wI, q=q, q_hca=q_hca)
+
+
+def decode_chain(H, W, t, m, m_prime, k, n_h, c, n_hI, cI, dtype="f64", KI_override=None,
+                 Ba=None, Bb=None, BIa=None, BIb=None, Bh=None):
+    """One CSA layer and one HCA layer for the query at position t, from H.
+
+    ``W`` maps names to weight matrices: aKV bKV aZ bZ (CSA, [Scratch] §3),
+    IaKV IbKV IaZ IbZ (the indexer's own compressor weights, [Scratch] §6.4),
+    KV Z (HCA, [Scratch] §10), DQ IUQ w UQ UQ_hca (queries).  ``dtype`` is the
+    storage format the chain mirrors.  ``KI_override`` injects indexer keys
+    directly, as the worked example of [Scratch] §6.4 does.
+    """
+    H = f64(H)
+    st = lambda x: store_as(x, dtype)  # noqa: E731
+    Ca, Cb = st(project(H, W["aKV"])), st(project(H, W["bKV"]))
+    Za, Zb = st(project(H, W["aZ"])), st(project(H, W["bZ"]))
+    Ccomp = st(csa_compress(Za, Zb, Ca, Cb, m, Ba, Bb))
+    if KI_override is not None:
+        KI = f64(KI_override)
+    else:
+        ICa, ICb = st(project(H, W["IaKV"])), st(project(H, W["IbKV"]))
+        IZa, IZb = st(project(H, W["IaZ"])), st(project(H, W["IbZ"]))
+        KI = st(csa_compress(IZa, IZb, ICa, ICb, m, BIa, BIb))
+    Ch, Zh = st(project(H, W["KV"])), st(project(H, W["Z"]))
+    Chca = st(hca_compress(Zh, Ch, m_prime, Bh))
+    Q = queries_from_hidden(H[t], W["DQ"], W["IUQ"], W["w"], W["UQ"], W["UQ_hca"],
+                            n_h, c, n_hI, cI, dtype)
+    scores = index_scores(Q["qI"], Q["wI"], KI, t, m)
+    idx = topk_select(scores, k)
+    o_csa, lse_csa = csa_attend(Q["q"], Ccomp, idx)
+    o_hca, lse_hca = hca_attend(Q["q_hca"], Chca, t, m_prime)
+    return dict(Ca=Ca, Cb=Cb, Za=Za, Zb=Zb, Ccomp=Ccomp, KI=KI, Chca=Chca, scores=scores,
+                idx=idx, o_csa=o_csa, lse_csa=lse_csa, o_hca=o_hca, lse_hca=lse_hca, **Q)
+
+
+# --------------------------------------------------------------------------
+# the efficiency ledger ([Scratch] §1, §12)
+# --------------------------------------------------------------------------
+
+def gqa_kv_bytes_per_token_layer(n_kv_heads: int = 8, d_h: int = 128, b: int = 2) -> int:
+    """Raw GQA KV cache: one key and one value per KV head ([Scratch] §1)."""
+    return 2 * n_kv_heads * d_h * b
+
+
+def compressed_bytes_per_token_layer(c: int, ratio: int, b: int = 2) -> float:
+    """One c-wide entry per ``ratio`` tokens ([Scratch] §12.1): c*b/m or c*b/m'."""
+    return c * b / ratio
+
+
+def ledger(c=512, m=4, m_prime=128, b=2, baseline=2048, n_csa=30, n_hca=31):
+    """KV-cache ledger of [Scratch] §12.1: per-layer bytes per token and the
+    ratios against a raw baseline of ``baseline`` bytes per token per layer."""
+    csa = compressed_bytes_per_token_layer(c, m, b)
+    hca = compressed_bytes_per_token_layer(c, m_prime, b)
+    mix = (n_csa * csa + n_hca * hca) / ((n_csa + n_hca) * baseline)
+    return dict(csa=csa, hca=hca, csa_ratio=csa / baseline, hca_ratio=hca / baseline, mix=mix)
+
+
+def indexer_flops_per_query(n: int, m: int, n_hI: int, cI: int) -> float:
+    """Indexer cost per query, counted as in [Scratch] §12.2: (n/m) * n_h^I * c^I."""
+    return n / m * n_hI * cI
