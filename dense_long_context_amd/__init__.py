@@ -1,0 +1,22 @@
+"""CSA/HCA compressed-attention hot path for AMD MI355X (gfx950).
+
+The computation lives in libdlc.so (HIP kernels behind the C ABI declared in
+include/dlc.h); this package is its Python binding plus the in-tree build.
+"""
+
+from .binding import (  # noqa: F401
+    DlcError,
+    csa_attend,
+    csa_attend_ws,
+    csa_compress,
+    csa_index_topk,
+    csa_index_topk_ws,
+    default_scale,
+    dlc_project,
+    hca_attend,
+    hca_attend_ws,
+    hca_compress,
+    last_error,
+    lib,
+    status_str,
+)

@@ -1,0 +1,243 @@
+"""Thin ctypes binding of libdlc.so (include/dlc.h).
+
+Argument marshalling only: tensors become device pointers, sizes and
+strides; every step of the computation runs in the HIP kernels behind the
+C ABI.  The functions carry the C names.  Outputs and workspaces that the
+caller does not pass are allocated here with torch on the tensors' device
+(PyTorch serves as the device allocator and stream provider).  There is no
+fallback: if the library is missing or a call fails, an exception says so.
+"""
+
+from __future__ import annotations
+
+import ctypes as C
+import math
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libdlc.so")
+
+DLC_F32, DLC_BF16 = 0, 1
+_DTYPES = {torch.float32: DLC_F32, torch.bfloat16: DLC_BF16}
+
+_i64, _vp, _f32, _sz, _i32 = C.c_int64, C.c_void_p, C.c_float, C.c_size_t, C.c_int
+
+# name -> (restype, argtypes), mirroring include/dlc.h
+SIGNATURES = {
+    "dlc_abi_version": (_i32, []),
+    "dlc_status_str": (C.c_char_p, [_i32]),
+    "dlc_last_error": (C.c_char_p, []),
+    "csa_compress": (_i32, [_i32, _i64, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _i64, _i64, _vp, _vp,
+                            _i64, _i64, _vp, _i64, _vp]),
+    "hca_compress": (_i32, [_i32, _i64, _i64, _i64, _i64, _vp, _vp, _i64, _i64, _vp, _i64, _i64,
+                            _vp, _i64, _vp]),
+    "csa_index_topk_ws": (_sz, [_i64, _i64, _i64, _i64]),
+    "csa_index_topk": (_i32, [_i32, _i64, _i64, _i64, _i64, _i64, _i64, _vp, _vp, _vp, _i64, _vp,
+                              _i64, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "csa_attend_ws": (_sz, [_i64, _i64, _i64, _i64, _i64]),
+    "csa_attend": (_i32, [_i32, _i64, _i64, _i64, _i64, _i64, _vp, _vp, _i64, _vp, _vp, _f32, _vp,
+                          _vp, _vp, _sz, _vp]),
+    "hca_attend_ws": (_sz, [_i64, _i64, _i64, _i64, _i64]),
+    "hca_attend": (_i32, [_i32, _i64, _i64, _i64, _i64, _i64, _vp, _vp, _i64, _vp, _i64, _f32, _vp,
+                          _vp, _vp, _sz, _vp]),
+    "dlc_project": (_i32, [_i32, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _i32, _vp]),
+}
+
+
+class DlcError(RuntimeError):
+    def __init__(self, fn, status, detail):
+        self.status = status
+        super().__init__(f"{fn}: {status_str(status)} ({status}): {detail}")
+
+
+_lib = None
+
+
+def lib():
+    """The loaded library (loads it on first use; raises if it was never built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with `python -m dense_long_context_amd.build`")
+        L = C.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            f = getattr(L, name)
+            f.restype, f.argtypes = res, args
+        _lib = L
+    return _lib
+
+
+def status_str(status: int) -> str:
+    return lib().dlc_status_str(status).decode()
+
+
+def last_error() -> str:
+    return lib().dlc_last_error().decode()
+
+
+def _check(fn, status):
+    if status != 0:
+        raise DlcError(fn, status, last_error())
+
+
+def _dt(x: torch.Tensor) -> int:
+    if x.dtype not in _DTYPES:
+        raise TypeError(f"unsupported dtype {x.dtype}")
+    return _DTYPES[x.dtype]
+
+
+def _p(x):
+    return None if x is None else x.data_ptr()
+
+
+def _stream(dev) -> int:
+    return torch.cuda.current_stream(dev).cuda_stream
+
+
+def _need(cond, msg):
+    if not cond:
+        raise ValueError(msg)
+
+
+def _ws(nbytes, dev, ws):
+    if ws is not None:
+        return ws
+    return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=dev)
+
+
+# ------------------------------------------------------------------ compress
+
+def csa_compress(Za, Zb, Ca, Cb, m, out, i_begin=0, i_end=None, Ba=None, Bb=None, n=None):
+    """Compress CSA entries [i_begin, i_end) of every sequence into ``out`` [B][cap][c].
+
+    Streams are [B][rows][c] tensors (views with a row stride are fine) that
+    share one stride pattern; ``n`` is the number of valid rows (default: all).
+    """
+    B, rows, c = Za.shape
+    for x in (Zb, Ca, Cb):
+        _need(x.shape == Za.shape and x.stride() == Za.stride() and x.dtype == Za.dtype,
+              "the four streams must share shape, strides and dtype")
+    _need(Za.stride(2) == 1, "stream rows must be contiguous")
+    n = rows if n is None else n
+    i_end = n // m if i_end is None else i_end
+    _check("csa_compress", lib().csa_compress(
+        _dt(Za), B, n, c, m, _p(Za), _p(Zb), _p(Ca), _p(Cb), Za.stride(1), Za.stride(0),
+        _p(Ba), _p(Bb), i_begin, i_end, _p(out), out.shape[1], _stream(Za.device)))
+    return out
+
+
+def hca_compress(Z, Cs, m_prime, out, i_begin=0, i_end=None, bias=None, n=None):
+    """Compress HCA entries [i_begin, i_end) into ``out`` [B][cap][c]."""
+    B, rows, c = Z.shape
+    _need(Cs.shape == Z.shape and Cs.stride() == Z.stride() and Cs.dtype == Z.dtype,
+          "Z and C must share shape, strides and dtype")
+    _need(Z.stride(2) == 1, "stream rows must be contiguous")
+    n = rows if n is None else n
+    i_end = n // m_prime if i_end is None else i_end
+    _check("hca_compress", lib().hca_compress(
+        _dt(Z), B, n, c, m_prime, _p(Z), _p(Cs), Z.stride(1), Z.stride(0), _p(bias), i_begin, i_end,
+        _p(out), out.shape[1], _stream(Z.device)))
+    return out
+
+
+# ------------------------------------------------------------ indexer, top-k
+
+def csa_index_topk_ws(B, n_q, cap, k):
+    return lib().csa_index_topk_ws(B, n_q, cap, k)
+
+
+def csa_index_topk(qI, wI, KI, t, t_max, m, k, idx=None, count=None, scores=None, ws=None):
+    """Indexer scores and top-k.  qI [B][n_q][n_hI][cI], wI fp32 [B][n_q][n_hI],
+    KI [B][cap][cI], t int64 [B][n_q] on the device.  Returns (idx, count)."""
+    B, n_q, n_hI, cI = qI.shape
+    cap = KI.shape[1]
+    dev = qI.device
+    for x, nm in ((qI, "qI"), (wI, "wI"), (KI, "KI"), (t, "t")):
+        _need(x.is_contiguous(), f"{nm} must be contiguous")
+    _need(wI.dtype == torch.float32 and t.dtype == torch.int64, "wI must be fp32 and t int64")
+    _need(tuple(wI.shape) == (B, n_q, n_hI) and tuple(t.shape) == (B, n_q), "wI/t shape mismatch")
+    _need(KI.shape[0] == B and KI.shape[2] == cI and KI.dtype == qI.dtype, "KI shape/dtype mismatch")
+    if idx is None:
+        idx = torch.empty((B, n_q, k), dtype=torch.int32, device=dev)
+    if count is None:
+        count = torch.empty((B, n_q), dtype=torch.int32, device=dev)
+    nb = csa_index_topk_ws(B, n_q, cap, k)
+    ws = _ws(nb, dev, ws)
+    _check("csa_index_topk", lib().csa_index_topk(
+        _dt(qI), B, n_q, n_hI, cI, m, k, _p(qI), _p(wI), _p(KI), cap, _p(t), int(t_max), _p(idx),
+        _p(count), _p(scores), _p(ws), ws.numel() * ws.element_size(), _stream(dev)))
+    return idx, count
+
+
+# ---------------------------------------------------------------- attention
+
+def csa_attend_ws(B, n_q, n_h, c, k):
+    return lib().csa_attend_ws(B, n_q, n_h, c, k)
+
+
+def hca_attend_ws(B, n_q, n_h, c, cap):
+    return lib().hca_attend_ws(B, n_q, n_h, c, cap)
+
+
+def csa_attend(q, Ccomp, idx, count, scale=0.0, out=None, lse=None, ws=None):
+    """Shared-KV MQA over the selected CSA entries.  q [B][n_q][n_h][c];
+    Ccomp [B][cap][c]; idx int32 [B][n_q][k]; count int32 [B][n_q].
+    Returns (out fp32 [B][n_q][n_h][c], lse fp32 [B][n_q][n_h])."""
+    B, n_q, n_h, c = q.shape
+    k = idx.shape[2]
+    dev = q.device
+    _need(q.is_contiguous() and Ccomp.is_contiguous() and idx.is_contiguous() and count.is_contiguous(),
+          "inputs must be contiguous")
+    _need(Ccomp.shape[0] == B and Ccomp.shape[2] == c and Ccomp.dtype == q.dtype, "Ccomp shape/dtype mismatch")
+    _need(idx.dtype == torch.int32 and count.dtype == torch.int32, "idx/count must be int32")
+    if out is None:
+        out = torch.empty((B, n_q, n_h, c), dtype=torch.float32, device=dev)
+    if lse is None:
+        lse = torch.empty((B, n_q, n_h), dtype=torch.float32, device=dev)
+    ws = _ws(csa_attend_ws(B, n_q, n_h, c, k), dev, ws)
+    _check("csa_attend", lib().csa_attend(
+        _dt(q), B, n_q, n_h, c, k, _p(q), _p(Ccomp), Ccomp.shape[1], _p(idx), _p(count), float(scale),
+        _p(out), _p(lse), _p(ws), ws.numel() * ws.element_size(), _stream(dev)))
+    return out, lse
+
+
+def hca_attend(q, Chca, t, t_max, m_prime, scale=0.0, out=None, lse=None, ws=None):
+    """Dense shared-KV MQA over the visible HCA entries.  Returns (out, lse)."""
+    B, n_q, n_h, c = q.shape
+    cap = Chca.shape[1]
+    dev = q.device
+    _need(q.is_contiguous() and Chca.is_contiguous() and t.is_contiguous(), "inputs must be contiguous")
+    _need(Chca.shape[0] == B and Chca.shape[2] == c and Chca.dtype == q.dtype, "Chca shape/dtype mismatch")
+    _need(t.dtype == torch.int64 and tuple(t.shape) == (B, n_q), "t must be int64 [B][n_q]")
+    if out is None:
+        out = torch.empty((B, n_q, n_h, c), dtype=torch.float32, device=dev)
+    if lse is None:
+        lse = torch.empty((B, n_q, n_h), dtype=torch.float32, device=dev)
+    ws = _ws(hca_attend_ws(B, n_q, n_h, c, cap), dev, ws)
+    _check("hca_attend", lib().hca_attend(
+        _dt(q), B, n_q, n_h, c, m_prime, _p(q), _p(Chca), cap, _p(t), int(t_max), float(scale),
+        _p(out), _p(lse), _p(ws), ws.numel() * ws.element_size(), _stream(dev)))
+    return out, lse
+
+
+# --------------------------------------------------------------- projection
+
+def dlc_project(A, Wt, out=None, out_dtype=None):
+    """out[M][N] = A[M][K] . W with W given transposed as Wt [N][K]; fp32 accumulation."""
+    M, K = A.shape
+    N = Wt.shape[0]
+    _need(Wt.shape[1] == K and Wt.dtype == A.dtype, "Wt must be [N][K] in A's dtype")
+    _need(A.stride(1) == 1 and Wt.stride(1) == 1, "rows must be contiguous")
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype or A.dtype, device=A.device)
+    _need(out.stride(1) == 1 and tuple(out.shape) == (M, N), "out must be [M][N] with contiguous rows")
+    _check("dlc_project", lib().dlc_project(
+        _dt(A), M, N, K, _p(A), A.stride(0), _p(Wt), Wt.stride(0), _p(out), out.stride(0), _dt(out),
+        _stream(A.device)))
+    return out
+
+
+def default_scale(c: int) -> float:
+    return 1.0 / math.sqrt(c)

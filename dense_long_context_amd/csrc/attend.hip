@@ -1,0 +1,514 @@
+// Shared-KV multi-query attention over compressed entries.
+//
+// "DeepSeek-V4 Hybrid Attention: CSA and HCA from Scratch": §8 (CSA core
+// attention over the top-k set: key = value = the compressed entry, logits
+// q.C/sqrt(c)) and §10-§11 (HCA: the same attention over every visible entry).
+//
+// Flash-decoding split-K: the key range of a query is cut into splits; each
+// workgroup runs an online softmax over its split and writes a normalised
+// partial output plus its log-sum-exp; a combine kernel merges the splits
+// exactly (o = sum_j e^{lse_j - lse} o_j, lse = log sum_j e^{lse_j}).
+//
+// MFMA path (bf16, c in {128, 256, 512}): a workgroup is 8 waves and covers
+// 128 heads.  All heads share each key row, so a 32-key tile is staged once in
+// LDS, row-major for Q.K^T and transposed for P.V.  Wave w owns heads
+// 32*(w/2) .. +31 and half w%2 of the c dimensions, and multiplies with
+// v_mfma_f32_32x32x16_bf16:
+//   S^T[32 keys][32 heads] = K[32 keys][half] . Q^T[half][32 heads]  (Q in registers)
+//   (the two halves' partial S^T are swapped through LDS and added)
+//   O[32 heads][half]     += P[32 heads][32 keys] . V[32 keys][half]
+// Splitting c between two waves keeps Q (64 VGPRs) and O (128 AGPRs) of a
+// wave in registers at two waves per SIMD.  The S^T accumulator already holds,
+// per lane, the 16 keys of one head that the P operand needs, so P never goes
+// through memory.  Tiles are double-buffered: the next tile's global loads are
+// in flight while the current one is used.
+// The VALU path covers fp32 and other shapes.
+#include "common.hpp"
+
+namespace dlc {
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr int kMinKeysPerSplit = 64;
+constexpr int kTargetWorkgroups = 256;
+
+struct AttArgs {
+  const void* q;        // [BQ][n_h][c]
+  const void* kv;       // [B][cap][c]
+  const int32_t* idx;   // gather: [BQ][k]
+  const int32_t* count; // gather: [BQ]
+  const int64_t* t;     // contiguous: [BQ]
+  int64_t n_q, n_h, c, cap, k, m_prime, t_max;
+  int64_t splits, keys_per_split, head_groups;
+  float scale_log2;
+  float* o;             // [BQ][splits][n_h][c] (splits == 1: the final output)
+  float* lse;           // [BQ][splits][n_h] (may be nullptr when splits == 1)
+};
+
+template <bool GATHER>
+__device__ __forceinline__ int64_t n_keys(const AttArgs& a, int64_t bq) {
+  if constexpr (GATHER) {
+    int64_t n = a.count[bq];
+    return n < 0 ? 0 : (n > a.k ? a.k : n);
+  } else {
+    int64_t t = a.t[bq];
+    t = t < 0 ? 0 : (t > a.t_max ? a.t_max : t);
+    const int64_t v = t / a.m_prime;
+    return v < a.cap ? v : a.cap;
+  }
+}
+
+// row of the j-th key of query bq, or -1 if that key is masked
+template <bool GATHER>
+__device__ __forceinline__ int64_t key_row(const AttArgs& a, int64_t bq, int64_t j, int64_t nk) {
+  if (j >= nk) return -1;
+  if constexpr (GATHER) {
+    const int64_t r = a.idx[bq * a.k + j];
+    return (r >= 0 && r < a.cap) ? r : -1;
+  } else {
+    return j;
+  }
+}
+
+// ------------------------------------------------------------------ VALU path
+
+template <typename T, bool GATHER, int MAXD>
+__global__ void __launch_bounds__(64) attend_valu_kernel(AttArgs a) {
+  const int64_t split = blockIdx.x, h = blockIdx.y, bq = blockIdx.z;
+  const int lane = threadIdx.x;
+  const int64_t b = bq / a.n_q;
+  const int64_t nk = n_keys<GATHER>(a, bq);
+  const int64_t k0 = split * a.keys_per_split;
+  const int64_t k1 = min(nk, k0 + a.keys_per_split);
+  const T* q = static_cast<const T*>(a.q) + (bq * a.n_h + h) * a.c;
+  const T* kv = static_cast<const T*>(a.kv) + b * a.cap * a.c;
+
+  float qv[MAXD], acc[MAXD];
+#pragma unroll
+  for (int u = 0; u < MAXD; ++u) {
+    const int64_t d = lane + 64 * u;
+    qv[u] = d < a.c ? Fmt<T>::load(q + d) : 0.f;
+    acc[u] = 0.f;
+  }
+  float mrun = -INFINITY, lrun = 0.f;
+  for (int64_t j = k0; j < k1; ++j) {
+    const int64_t r = key_row<GATHER>(a, bq, j, nk);
+    if (r < 0) continue;
+    const T* row = kv + r * a.c;
+    float cv[MAXD];
+    float dot = 0.f;
+#pragma unroll
+    for (int u = 0; u < MAXD; ++u) {
+      const int64_t d = lane + 64 * u;
+      cv[u] = d < a.c ? Fmt<T>::load(row + d) : 0.f;
+      dot = fmaf(qv[u], cv[u], dot);
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) dot += __shfl_xor(dot, off);
+    const float x = dot * a.scale_log2;
+    const float mnew = fmaxf(mrun, x);
+    const float alpha = exp2f(mrun - mnew);  // mrun = -inf gives 0
+    const float p = exp2f(x - mnew);
+    lrun = lrun * alpha + p;
+#pragma unroll
+    for (int u = 0; u < MAXD; ++u) acc[u] = fmaf(p, cv[u], acc[u] * alpha);
+    mrun = mnew;
+  }
+  const int64_t slot = (bq * a.splits + split) * a.n_h + h;
+  const float inv = lrun > 0.f ? 1.f / lrun : 0.f;
+#pragma unroll
+  for (int u = 0; u < MAXD; ++u) {
+    const int64_t d = lane + 64 * u;
+    if (d < a.c) a.o[slot * a.c + d] = acc[u] * inv;
+  }
+  if (lane == 0 && a.lse) a.lse[slot] = lrun > 0.f ? (mrun + log2f(lrun)) * kLn2 : -INFINITY;
+}
+
+// ------------------------------------------------------------------ MFMA path
+
+template <int CD, bool GATHER>
+__global__ void __launch_bounds__(512) attend_mfma_kernel(AttArgs a) {
+  constexpr int HALF = CD / 2;
+  constexpr int KSH = HALF / 16;  // 16-dim Q.K^T steps in one half of c
+  constexpr int NTH = HALF / 32;  // 32-dim P.V output tiles in one half of c
+  constexpr int KROW = CD + 8;    // padded row of the row-major key tile (bf16)
+  constexpr int VROW = 36;        // padded row of the transposed tile (32 keys + pad)
+  constexpr int UNITS = CD;       // staging units: 8 key-quads x CD/8 dim groups
+  constexpr int UPT = (UNITS + 511) / 512;
+  __shared__ __attribute__((aligned(16))) bf16_raw sK[2][32 * KROW];
+  __shared__ __attribute__((aligned(16))) bf16_raw sV[2][CD * VROW];
+  __shared__ int32_t sValid[2][32];
+  // partial-S^T exchange (8 waves x 16 regs x 64 lanes fp32): inside the key
+  // buffer just consumed when it is large enough (c = 512), else its own array
+  constexpr bool kXInK = 8 * 16 * 64 * 4 <= 32 * KROW * 2;
+  __shared__ float sX[kXInK ? 1 : 8 * 16 * 64];
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int l32 = lane & 31, g2 = lane >> 5;
+  const int hp = wave >> 1, dh = wave & 1;  // head slice of 32, half of c
+  const int64_t bq = blockIdx.y;
+  const int64_t split = blockIdx.x / a.head_groups;
+  const int64_t hg = blockIdx.x - split * a.head_groups;
+  const int64_t b = bq / a.n_q;
+  const int64_t nk = n_keys<GATHER>(a, bq);
+  const int64_t k0 = split * a.keys_per_split;
+  const int64_t k1 = min(nk, k0 + a.keys_per_split);
+  const int64_t hbase = hg * 128 + hp * 32;  // first head of this wave
+  const bool active = hbase < a.n_h;
+  const bf16_raw* kv = static_cast<const bf16_raw*>(a.kv) + b * a.cap * CD;
+
+  // Q^T operand over this wave's half of c: lane holds head hbase + l32,
+  // dims dh*HALF + ks*16 + g2*8 .. +7
+  bf16x8 qf[KSH];
+  {
+    const int64_t h = hbase + l32;
+    const bf16_raw* qp =
+        static_cast<const bf16_raw*>(a.q) + (bq * a.n_h + (h < a.n_h ? h : 0)) * CD + dh * HALF + g2 * 8;
+#pragma unroll
+    for (int ks = 0; ks < KSH; ++ks) {
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (h < a.n_h) v = *reinterpret_cast<const uint4*>(qp + ks * 16);
+      qf[ks] = __builtin_bit_cast(bf16x8, v);
+    }
+  }
+
+  f32x16 o[NTH];
+#pragma unroll
+  for (int nt = 0; nt < NTH; ++nt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) o[nt][r] = 0.f;
+  float mrun = -INFINITY, lrun = 0.f;  // for head hbase + l32
+
+  // staging: unit u -> key quad kq (keys 4kq .. 4kq+3) and 8-dim group dg;
+  // consecutive threads take consecutive 16-byte pieces of the same rows
+  uint4 stg[UPT][4];
+  uint32_t stv[UPT];  // bit j: key 4kq+j is valid
+  auto gload = [&](int64_t kbase) {
+#pragma unroll
+    for (int i = 0; i < UPT; ++i) {
+      const int u = tid + 512 * i;
+      if (u < UNITS) {
+        const int kq = u / (CD / 8), dg = u % (CD / 8);
+        stv[i] = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int64_t r = key_row<GATHER>(a, bq, kbase + 4 * kq + j, k1);
+          stv[i] |= uint32_t(r >= 0) << j;
+          stg[i][j] = r >= 0 ? *reinterpret_cast<const uint4*>(kv + r * CD + dg * 8) : make_uint4(0, 0, 0, 0);
+        }
+      }
+    }
+  };
+  auto swrite = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < UPT; ++i) {
+      const int u = tid + 512 * i;
+      if (u < UNITS) {
+        const int kq = u / (CD / 8), dg = u % (CD / 8);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          *reinterpret_cast<uint4*>(&sK[buf][(4 * kq + j) * KROW + dg * 8]) = stg[i][j];
+        // transpose: for each of the 8 dims, the 4 keys' values side by side
+        const uint32_t* w0 = reinterpret_cast<const uint32_t*>(&stg[i][0]);
+        const uint32_t* w1 = reinterpret_cast<const uint32_t*>(&stg[i][1]);
+        const uint32_t* w2 = reinterpret_cast<const uint32_t*>(&stg[i][2]);
+        const uint32_t* w3 = reinterpret_cast<const uint32_t*>(&stg[i][3]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          // dims 2e (low halves) and 2e+1 (high halves)
+          const uint32_t lo01 = (w0[e] & 0xffffu) | (w1[e] << 16);
+          const uint32_t lo23 = (w2[e] & 0xffffu) | (w3[e] << 16);
+          const uint32_t hi01 = (w0[e] >> 16) | (w1[e] & 0xffff0000u);
+          const uint32_t hi23 = (w2[e] >> 16) | (w3[e] & 0xffff0000u);
+          *reinterpret_cast<uint2*>(&sV[buf][(dg * 8 + 2 * e) * VROW + 4 * kq]) = make_uint2(lo01, lo23);
+          *reinterpret_cast<uint2*>(&sV[buf][(dg * 8 + 2 * e + 1) * VROW + 4 * kq]) = make_uint2(hi01, hi23);
+        }
+        if (dg == 0)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) sValid[buf][4 * kq + j] = (stv[i] >> j) & 1;
+      }
+    }
+  };
+
+  const int64_t ntile = k1 > k0 ? (k1 - k0 + 31) / 32 : 0;
+  if (ntile > 0) {
+    gload(k0);
+    swrite(0);
+  }
+  __syncthreads();
+  for (int64_t it = 0; it < ntile; ++it) {
+    const int buf = int(it & 1);
+    if (it + 1 < ntile) gload(k0 + (it + 1) * 32);
+    // partial S^T over this wave's half of c
+    f32x16 sx;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sx[r] = 0.f;
+    if (active) {
+      const bf16_raw* krow = &sK[buf][l32 * KROW + dh * HALF + g2 * 8];
+      // one LDS fragment in flight ahead of each MFMA; the compiler barrier keeps
+      // the scheduler from hoisting every fragment load (and its registers) up front
+      bf16x8 ka = *reinterpret_cast<const bf16x8*>(krow);
+#pragma unroll
+      for (int ks = 0; ks < KSH; ++ks) {
+        bf16x8 kn = ka;
+        if (ks + 1 < KSH) kn = *reinterpret_cast<const bf16x8*>(krow + (ks + 1) * 16);
+        sx = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[ks], sx, 0, 0, 0);
+        ka = kn;
+        asm volatile("" ::: "memory");
+      }
+    }
+    __syncthreads();  // every wave is done with sK[buf]: reuse it for the exchange
+    float* xch = kXInK ? reinterpret_cast<float*>(&sK[buf][0]) : sX;
+    if (active) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) xch[(wave * 16 + r) * 64 + lane] = sx[r];
+    }
+    __syncthreads();
+    if (active) {
+      // full S^T = both halves; lane holds head l32, keys kr(r) = 8*(r/4) + 4*g2 + r%4
+      float tmax = -INFINITY;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float other = xch[((wave ^ 1) * 16 + r) * 64 + lane];
+        const float full = dh == 0 ? sx[r] + other : other + sx[r];
+        const int kr = 8 * (r >> 2) + 4 * g2 + (r & 3);
+        sx[r] = sValid[buf][kr] ? full * a.scale_log2 : -INFINITY;
+        tmax = fmaxf(tmax, sx[r]);
+      }
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+      // Lazy running max: it moves only when a logit exceeds it by more than 8
+      // (a factor 256), so the O rescale is rare; p stays below 2^8 either way
+      // and the result is the same softmax.
+      const bool move = tmax > mrun + 8.f;
+      if (__any(move)) {
+        const float mnew = move ? tmax : mrun;
+        const float alpha = mrun == -INFINITY ? 0.f : exp2f(mrun - mnew);
+        lrun *= alpha;
+        mrun = mnew;
+        // O rows are heads 8*(r/4) + 4*g2 + r%4: fetch their factors
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float al = __shfl(alpha, 8 * (r >> 2) + 4 * g2 + (r & 3));
+#pragma unroll
+          for (int nt = 0; nt < NTH; ++nt) o[nt][r] *= al;
+        }
+      }
+      float psum = 0.f;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        sx[r] = sx[r] == -INFINITY ? 0.f : exp2f(sx[r] - mrun);
+        psum += sx[r];
+      }
+      psum += __shfl_xor(psum, 32);
+      lrun += psum;
+      bf16x8 pa[2];
+#pragma unroll
+      for (int uu = 0; uu < 2; ++uu)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) pa[uu][e] = (__bf16)sx[8 * uu + e];
+      // P . V over this wave's half of c: B operand lane holds dim
+      // dh*HALF + nt*32 + l32 and keys 16u + 8*(e/4) + 4*g2 + e%4
+      auto vfrag = [&](int f) {
+        const bf16_raw* vrow = &sV[buf][(dh * HALF + (f >> 1) * 32 + l32) * VROW + 4 * g2 + 16 * (f & 1)];
+        const uint2 lo = *reinterpret_cast<const uint2*>(vrow);
+        const uint2 hi = *reinterpret_cast<const uint2*>(vrow + 8);
+        return __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
+      };
+      bf16x8 vb = vfrag(0);
+#pragma unroll
+      for (int f = 0; f < 2 * NTH; ++f) {
+        bf16x8 vn = vb;
+        if (f + 1 < 2 * NTH) vn = vfrag(f + 1);
+        o[f >> 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa[f & 1], vb, o[f >> 1], 0, 0, 0);
+        vb = vn;
+        asm volatile("" ::: "memory");
+      }
+    }
+    if (it + 1 < ntile) swrite(buf ^ 1);
+    __syncthreads();
+  }
+
+  if (!active) return;
+  // normalise and write: lane holds dims dh*HALF + nt*32 + l32 of heads 8*(r/4) + 4*g2 + r%4
+  const int64_t slot0 = (bq * a.splits + split) * a.n_h;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int hr = 8 * (r >> 2) + 4 * g2 + (r & 3);
+    const float l = __shfl(lrun, hr);
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+    const int64_t h = hbase + hr;
+    if (h < a.n_h) {
+      float* op = a.o + (slot0 + h) * CD + dh * HALF + l32;
+#pragma unroll
+      for (int nt = 0; nt < NTH; ++nt) op[nt * 32] = o[nt][r] * inv;
+    }
+  }
+  if (dh == 0 && g2 == 0 && a.lse && hbase + l32 < a.n_h)
+    a.lse[slot0 + hbase + l32] = lrun > 0.f ? (mrun + log2f(lrun)) * kLn2 : -INFINITY;
+}
+
+// ------------------------------------------------------------------ combine
+
+__global__ void __launch_bounds__(256) combine_kernel(const float* op, const float* lp, int64_t splits,
+                                                      int64_t n_h, int64_t c, float* out, float* lse) {
+  const int64_t bh = blockIdx.x;  // bq * n_h + h
+  const int64_t bq = bh / n_h, h = bh - bq * n_h;
+  float M = -INFINITY;
+  for (int64_t j = 0; j < splits; ++j) M = fmaxf(M, lp[(bq * splits + j) * n_h + h]);
+  float L = 0.f;
+  if (M != -INFINITY)
+    for (int64_t j = 0; j < splits; ++j) L += __expf(lp[(bq * splits + j) * n_h + h] - M);
+  const float invL = L > 0.f ? 1.f / L : 0.f;
+  for (int64_t d = threadIdx.x; d < c; d += blockDim.x) {
+    float acc = 0.f;
+    if (M != -INFINITY)
+      for (int64_t j = 0; j < splits; ++j) {
+        const float lj = lp[(bq * splits + j) * n_h + h];
+        if (lj != -INFINITY) acc = fmaf(__expf(lj - M), op[((bq * splits + j) * n_h + h) * c + d], acc);
+      }
+    out[bh * c + d] = acc * invL;
+  }
+  if (threadIdx.x == 0 && lse) lse[bh] = M == -INFINITY ? -INFINITY : M + __logf(L);
+}
+
+// ------------------------------------------------------------------ host
+
+bool mfma_ok(int dtype, int64_t c) { return dtype == DLC_BF16 && (c == 128 || c == 256 || c == 512); }
+
+struct Plan {
+  bool mfma;
+  int64_t splits, kps, head_groups;
+  size_t o_off, l_off, total;
+};
+
+Plan plan(int dtype, int64_t BQ, int64_t n_h, int64_t c, int64_t nkeys) {
+  Plan p{};
+  p.mfma = mfma_ok(dtype, c);
+  p.head_groups = p.mfma ? ceil_div(n_h, 128) : n_h;
+  const int64_t per_split = p.mfma ? BQ * p.head_groups : BQ * n_h;
+  int64_t s = ceil_div(kTargetWorkgroups, per_split);
+  const int64_t smax = ceil_div(nkeys > 0 ? nkeys : 1, kMinKeysPerSplit);
+  s = s < smax ? s : smax;
+  s = s < 1 ? 1 : s;
+  p.splits = s;
+  p.kps = ceil_div(nkeys > 0 ? nkeys : 1, s);
+  if (p.mfma) p.kps = ceil_div(p.kps, 32) * 32;
+  p.o_off = 0;
+  size_t off = 0;
+  if (s > 1) {
+    off = align_up(size_t(BQ) * s * n_h * c * 4, 256);
+    p.l_off = off;
+    off = align_up(off + size_t(BQ) * s * n_h * 4, 256);
+  } else {
+    p.l_off = 0;
+  }
+  p.total = off;
+  return p;
+}
+
+size_t ws_bound(int64_t BQ, int64_t n_h, int64_t c, int64_t nkeys) {
+  const Plan a = plan(DLC_BF16, BQ, n_h, c, nkeys), b = plan(DLC_F32, BQ, n_h, c, nkeys);
+  return a.total > b.total ? a.total : b.total;
+}
+
+template <bool GATHER>
+int run_attend(const char* name, int dtype, AttArgs a, int64_t BQ, int64_t nkeys, float* out, float* lse,
+               void* ws, size_t ws_bytes, hipStream_t s) {
+  const Plan p = plan(dtype, BQ, a.n_h, a.c, nkeys);
+  DLC_REQUIRE(p.total == 0 || (ws != nullptr && ws_bytes >= p.total), DLC_E_WORKSPACE,
+              "%s: workspace of %zu bytes needed, %zu given", name, p.total, ws_bytes);
+  DLC_REQUIRE(ws == nullptr || aligned(ws, 256), DLC_E_WORKSPACE, "%s: workspace must be 256-byte aligned", name);
+  a.splits = p.splits;
+  a.keys_per_split = p.kps;
+  a.head_groups = p.head_groups;
+  if (p.splits > 1) {
+    a.o = reinterpret_cast<float*>(static_cast<char*>(ws) + p.o_off);
+    a.lse = reinterpret_cast<float*>(static_cast<char*>(ws) + p.l_off);
+  } else {
+    a.o = out;
+    a.lse = lse;
+  }
+  DLC_REQUIRE(BQ <= 65535 && p.splits * p.head_groups < (int64_t(1) << 31), DLC_E_UNSUPPORTED,
+              "%s: grid too large", name);
+  if (p.mfma) {
+    dim3 grid{(unsigned)(p.splits * p.head_groups), (unsigned)BQ, 1u};
+    if (a.c == 128) hipLaunchKernelGGL((attend_mfma_kernel<128, GATHER>), grid, dim3(512), 0, s, a);
+    if (a.c == 256) hipLaunchKernelGGL((attend_mfma_kernel<256, GATHER>), grid, dim3(512), 0, s, a);
+    if (a.c == 512) hipLaunchKernelGGL((attend_mfma_kernel<512, GATHER>), grid, dim3(512), 0, s, a);
+  } else {
+    DLC_REQUIRE(a.n_h <= 65535, DLC_E_UNSUPPORTED, "%s: n_h > 65535 on the VALU path", name);
+    dim3 grid{(unsigned)p.splits, (unsigned)a.n_h, (unsigned)BQ};
+    if (dtype == DLC_BF16)
+      hipLaunchKernelGGL((attend_valu_kernel<bf16_raw, GATHER, 16>), grid, dim3(64), 0, s, a);
+    else
+      hipLaunchKernelGGL((attend_valu_kernel<float, GATHER, 16>), grid, dim3(64), 0, s, a);
+  }
+  int rc = check_launch(name);
+  if (rc || p.splits == 1) return rc;
+  hipLaunchKernelGGL(combine_kernel, dim3((unsigned)(BQ * a.n_h)), dim3(a.c < 256 ? unsigned(a.c) : 256u), 0, s,
+                     a.o, a.lse, p.splits, a.n_h, a.c, out, lse);
+  return check_launch(name);
+}
+
+int common_checks(const char* name, int dtype, int64_t B, int64_t n_q, int64_t n_h, int64_t c, const void* q,
+                  const void* kv, int64_t cap, const float* out) {
+  DLC_REQUIRE(dtype == DLC_F32 || dtype == DLC_BF16, DLC_E_DTYPE, "%s: unsupported dtype %d", name, dtype);
+  DLC_REQUIRE(B >= 1 && n_q >= 1 && n_h >= 1 && c >= 1 && cap >= 0, DLC_E_INVAL,
+              "%s: need B, n_q, n_h, c >= 1 and cap >= 0", name);
+  DLC_REQUIRE(q && out && (kv || cap == 0), DLC_E_INVAL, "%s: NULL argument", name);
+  DLC_REQUIRE(c <= 1024 || mfma_ok(dtype, c), DLC_E_UNSUPPORTED, "%s: c=%lld > 1024", name, (long long)c);
+  if (mfma_ok(dtype, c))
+    DLC_REQUIRE(aligned(q, 16) && aligned(kv, 16), DLC_E_INVAL, "%s: q and the cache must be 16-byte aligned", name);
+  return DLC_OK;
+}
+
+}  // namespace
+}  // namespace dlc
+
+extern "C" {
+
+size_t csa_attend_ws(int64_t B, int64_t n_q, int64_t n_h, int64_t c, int64_t k) {
+  if (B < 1 || n_q < 1 || n_h < 1 || c < 1 || k < 1) return 0;
+  return dlc::ws_bound(B * n_q, n_h, c, k);
+}
+
+size_t hca_attend_ws(int64_t B, int64_t n_q, int64_t n_h, int64_t c, int64_t cap) {
+  if (B < 1 || n_q < 1 || n_h < 1 || c < 1 || cap < 0) return 0;
+  return dlc::ws_bound(B * n_q, n_h, c, cap);
+}
+
+int csa_attend(int dtype, int64_t B, int64_t n_q, int64_t n_h, int64_t c, int64_t k, const void* q,
+               const void* Ccomp, int64_t cap, const int32_t* idx, const int32_t* count, float scale, float* out,
+               float* lse, void* ws, size_t ws_bytes, void* stream) {
+  using namespace dlc;
+  int rc = common_checks("csa_attend", dtype, B, n_q, n_h, c, q, Ccomp, cap, out);
+  if (rc) return rc;
+  DLC_REQUIRE(k >= 1, DLC_E_INVAL, "csa_attend: k must be >= 1");
+  DLC_REQUIRE(idx && count, DLC_E_INVAL, "csa_attend: NULL idx or count");
+  AttArgs a{};
+  a.q = q; a.kv = Ccomp; a.idx = idx; a.count = count;
+  a.n_q = n_q; a.n_h = n_h; a.c = c; a.cap = cap; a.k = k;
+  a.scale_log2 = (scale > 0.f ? scale : 1.f / std::sqrt(float(c))) * kLog2e;
+  return run_attend<true>("csa_attend", dtype, a, B * n_q, k, out, lse, ws, ws_bytes, as_stream(stream));
+}
+
+int hca_attend(int dtype, int64_t B, int64_t n_q, int64_t n_h, int64_t c, int64_t m_prime, const void* q,
+               const void* Chca, int64_t cap, const int64_t* t, int64_t t_max, float scale, float* out, float* lse,
+               void* ws, size_t ws_bytes, void* stream) {
+  using namespace dlc;
+  int rc = common_checks("hca_attend", dtype, B, n_q, n_h, c, q, Chca, cap, out);
+  if (rc) return rc;
+  DLC_REQUIRE(m_prime >= 1 && t_max >= 0, DLC_E_INVAL, "hca_attend: need m' >= 1 and t_max >= 0");
+  DLC_REQUIRE(t != nullptr, DLC_E_INVAL, "hca_attend: NULL t");
+  DLC_REQUIRE(t_max / m_prime <= cap, DLC_E_SHAPE, "hca_attend: floor(t_max/m')=%lld exceeds cap=%lld",
+              (long long)(t_max / m_prime), (long long)cap);
+  AttArgs a{};
+  a.q = q; a.kv = Chca; a.t = t;
+  a.n_q = n_q; a.n_h = n_h; a.c = c; a.cap = cap; a.m_prime = m_prime; a.t_max = t_max;
+  a.scale_log2 = (scale > 0.f ? scale : 1.f / std::sqrt(float(c))) * kLog2e;
+  return run_attend<false>("hca_attend", dtype, a, B * n_q, t_max / m_prime, out, lse, ws, ws_bytes,
+                           as_stream(stream));
+}
+
+}  // extern "C"

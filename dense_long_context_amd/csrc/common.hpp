@@ -1,0 +1,101 @@
+// Shared device helpers and host-side validation for the gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stddef.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+
+#include "../../include/dlc.h"
+
+namespace dlc {
+
+// ----------------------------------------------------------------------------
+// host side: error reporting
+// ----------------------------------------------------------------------------
+
+int fail(int status, const char* fmt, ...);       // records a thread-local message
+int check_launch(const char* what);               // DLC_OK or DLC_E_HIP after a launch
+
+#define DLC_REQUIRE(cond, status, ...) \
+  do {                                 \
+    if (!(cond)) return ::dlc::fail((status), __VA_ARGS__); \
+  } while (0)
+
+inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+inline bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+__host__ __device__ inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// ----------------------------------------------------------------------------
+// device side: number formats
+// ----------------------------------------------------------------------------
+
+typedef uint16_t bf16_raw;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t x) { return __uint_as_float(uint32_t(x) << 16); }
+
+// fp32 -> bf16, round to nearest, ties to even (finite inputs)
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0;  // NaN stays NaN
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return uint16_t(u >> 16);
+}
+
+template <typename T> struct Fmt;
+template <> struct Fmt<float> {
+  static constexpr int kVec = 4;  // elements per 16-byte load
+  __device__ static float load(const float* p) { return *p; }
+  __device__ static void store(float* p, float v) { *p = v; }
+  __device__ static void load_vec(const float* p, float* v) {
+    float4 x = *reinterpret_cast<const float4*>(p);
+    v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w;
+  }
+  __device__ static void store_vec(float* p, const float* v) {
+    *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
+  }
+};
+template <> struct Fmt<bf16_raw> {
+  static constexpr int kVec = 8;
+  __device__ static float load(const bf16_raw* p) { return bf16_to_f32(*p); }
+  __device__ static void store(bf16_raw* p, float v) { *p = f32_to_bf16(v); }
+  __device__ static void load_vec(const bf16_raw* p, float* v) {
+    uint4 x = *reinterpret_cast<const uint4*>(p);
+    uint32_t w[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = __uint_as_float(w[i] << 16);
+      v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+  }
+  __device__ static void store_vec(bf16_raw* p, const float* v) {
+    uint32_t w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      w[i] = uint32_t(f32_to_bf16(v[2 * i])) | (uint32_t(f32_to_bf16(v[2 * i + 1])) << 16);
+    *reinterpret_cast<uint4*>(p) = make_uint4(w[0], w[1], w[2], w[3]);
+  }
+};
+
+// Order-preserving map of an fp32 score to uint32: a larger score gives a
+// larger key, and -0.0 maps to the key of +0.0.
+__device__ __forceinline__ uint32_t order_key(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) == 0) u = 0;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// fill kernel: clears workspace on the stream (no memset nodes, so the calls
+// stay safe to capture in a graph)
+__global__ void fill_u32_kernel(uint32_t* p, uint32_t v, int64_t n);
+int fill_u32(uint32_t* p, uint32_t v, int64_t n, hipStream_t s);
+
+}  // namespace dlc

@@ -1,0 +1,161 @@
+// Dense token projections: out[M][N] = A[M][K] . W[K][N], W given as Wt[N][K].
+//
+// "DeepSeek-V4 Hybrid Attention: CSA and HCA from Scratch", §3 (C^a = H W^{aKV}
+// and the other stream projections), §6.1-6.3 and §8 (c^Q, q^I, w^I, q).
+//
+// bf16 path: 128x128 output tile per workgroup of 4 waves (2x2, 64x64 each),
+// 32-deep K steps staged through LDS with padded rows, v_mfma_f32_32x32x16_bf16,
+// fp32 accumulation; the next K step's global loads are in flight during the
+// current step's MFMAs.  Both operands are K-contiguous, so global loads are
+// whole 16-byte vectors along rows.  Other dtypes and shapes use a VALU kernel.
+#include "common.hpp"
+
+namespace dlc {
+namespace {
+
+struct ProjArgs {
+  const void* A;
+  const void* W;
+  void* out;
+  int64_t M, N, K, lda, ldw, ldo;
+  int out_bf16;
+};
+
+template <typename T>
+__global__ void __launch_bounds__(256) project_valu_kernel(ProjArgs a) {
+  const int64_t n = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  const int64_t mrow = blockIdx.y;
+  if (n >= a.N) return;
+  const T* A = static_cast<const T*>(a.A) + mrow * a.lda;
+  const T* W = static_cast<const T*>(a.W) + n * a.ldw;
+  float acc = 0.f;
+  for (int64_t k = 0; k < a.K; ++k) acc = fmaf(Fmt<T>::load(A + k), Fmt<T>::load(W + k), acc);
+  if (a.out_bf16)
+    Fmt<bf16_raw>::store(static_cast<bf16_raw*>(a.out) + mrow * a.ldo + n, acc);
+  else
+    static_cast<float*>(a.out)[mrow * a.ldo + n] = acc;
+}
+
+constexpr int TM = 128, TN = 128, TK = 32;
+constexpr int LROW = TK + 8;  // padded LDS row (bf16): 80 bytes
+
+__global__ void __launch_bounds__(256) project_mfma_kernel(ProjArgs a) {
+  __shared__ __attribute__((aligned(16))) bf16_raw sA[2][TM * LROW];
+  __shared__ __attribute__((aligned(16))) bf16_raw sB[2][TN * LROW];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int l32 = lane & 31, g2 = lane >> 5;
+  const int wm = wave >> 1, wn = wave & 1;
+  // XCD-aware order: consecutive workgroups share the same A rows
+  const int64_t tiles_n = ceil_div(a.N, TN);
+  const int64_t m0 = (int64_t(blockIdx.x) / tiles_n) * TM;
+  const int64_t n0 = (int64_t(blockIdx.x) % tiles_n) * TN;
+  const bf16_raw* A = static_cast<const bf16_raw*>(a.A);
+  const bf16_raw* W = static_cast<const bf16_raw*>(a.W);
+
+  // staging: 128 rows x 32 k = 512 16-byte vectors per operand, 2 per thread
+  uint4 ra[2], rb[2];
+  auto gload = [&](int64_t k0) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int v = tid + 256 * i;
+      const int row = v >> 2, kc = (v & 3) * 8;
+      const int64_t gk = k0 + kc;
+      const int64_t gm = m0 + row, gn = n0 + row;
+      ra[i] = (gm < a.M && gk < a.K) ? *reinterpret_cast<const uint4*>(A + gm * a.lda + gk) : make_uint4(0, 0, 0, 0);
+      rb[i] = (gn < a.N && gk < a.K) ? *reinterpret_cast<const uint4*>(W + gn * a.ldw + gk) : make_uint4(0, 0, 0, 0);
+    }
+  };
+  auto swrite = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int v = tid + 256 * i;
+      const int row = v >> 2, kc = (v & 3) * 8;
+      *reinterpret_cast<uint4*>(&sA[buf][row * LROW + kc]) = ra[i];
+      *reinterpret_cast<uint4*>(&sB[buf][row * LROW + kc]) = rb[i];
+    }
+  };
+
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  const int64_t nk = ceil_div(a.K, TK);
+  gload(0);
+  swrite(0);
+  __syncthreads();
+  for (int64_t kt = 0; kt < nk; ++kt) {
+    const int buf = int(kt & 1);
+    if (kt + 1 < nk) gload((kt + 1) * TK);
+#pragma unroll
+    for (int ks = 0; ks < TK / 16; ++ks) {
+      bf16x8 af[2], bfr[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        af[i] = *reinterpret_cast<const bf16x8*>(&sA[buf][(wm * 64 + i * 32 + l32) * LROW + ks * 16 + g2 * 8]);
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        bfr[j] = *reinterpret_cast<const bf16x8*>(&sB[buf][(wn * 64 + j * 32 + l32) * LROW + ks * 16 + g2 * 8]);
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+    }
+    if (kt + 1 < nk) swrite(buf ^ 1);
+    __syncthreads();
+  }
+  // D: lane holds column l32, rows 8*(r/4) + 4*g2 + r%4
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int64_t gn = n0 + wn * 64 + j * 32 + l32;
+      if (gn >= a.N) continue;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int64_t gm = m0 + wm * 64 + i * 32 + 8 * (r >> 2) + 4 * g2 + (r & 3);
+        if (gm < a.M) {
+          if (a.out_bf16)
+            static_cast<bf16_raw*>(a.out)[gm * a.ldo + gn] = f32_to_bf16(acc[i][j][r]);
+          else
+            static_cast<float*>(a.out)[gm * a.ldo + gn] = acc[i][j][r];
+        }
+      }
+    }
+}
+
+}  // namespace
+}  // namespace dlc
+
+extern "C" int dlc_project(int dtype, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* Wt,
+                           int64_t ldw, void* out, int64_t ldo, int out_dtype, void* stream) {
+  using namespace dlc;
+  DLC_REQUIRE(dtype == DLC_F32 || dtype == DLC_BF16, DLC_E_DTYPE, "dlc_project: unsupported dtype %d", dtype);
+  DLC_REQUIRE(out_dtype == DLC_F32 || out_dtype == dtype, DLC_E_DTYPE,
+              "dlc_project: out_dtype must be DLC_F32 or the input dtype");
+  DLC_REQUIRE(M >= 0 && N >= 0 && K >= 1, DLC_E_INVAL, "dlc_project: need M, N >= 0 and K >= 1");
+  DLC_REQUIRE(lda >= K && ldw >= K && ldo >= N, DLC_E_SHAPE, "dlc_project: leading dimensions too small");
+  DLC_REQUIRE(A && Wt && out, DLC_E_INVAL, "dlc_project: NULL argument");
+  if (M == 0 || N == 0) return DLC_OK;
+  ProjArgs a{A, Wt, out, M, N, K, lda, ldw, ldo, out_dtype == DLC_BF16};
+  hipStream_t s = as_stream(stream);
+  const bool mfma = dtype == DLC_BF16 && K % 8 == 0 && lda % 8 == 0 && ldw % 8 == 0 && aligned(A, 16) &&
+                    aligned(Wt, 16);
+  if (mfma) {
+    const int64_t tiles = ceil_div(M, TM) * ceil_div(N, TN);
+    DLC_REQUIRE(tiles < (int64_t(1) << 31), DLC_E_UNSUPPORTED, "dlc_project: too many tiles");
+    hipLaunchKernelGGL(project_mfma_kernel, dim3((unsigned)tiles), dim3(256), 0, s, a);
+  } else {
+    DLC_REQUIRE(M <= 65535, DLC_E_UNSUPPORTED, "dlc_project: M > 65535 on the VALU path");
+    dim3 grid{(unsigned)ceil_div(N, 256), (unsigned)M, 1u};
+    if (dtype == DLC_BF16)
+      hipLaunchKernelGGL(project_valu_kernel<bf16_raw>, grid, dim3(256), 0, s, a);
+    else
+      hipLaunchKernelGGL(project_valu_kernel<float>, grid, dim3(256), 0, s, a);
+  }
+  return check_launch("dlc_project");
+}

@@ -1,0 +1,181 @@
+/*
+ * dlc.h - C ABI of the CSA/HCA compressed-attention hot path for AMD gfx950.
+ *
+ * The operations are those derived on the page "DeepSeek-V4 Hybrid Attention:
+ * CSA and HCA from Scratch" (cited below as [Scratch] with its section):
+ * the token-level KV compressor (CSA with overlapping 2m windows, HCA with
+ * m' windows), lightning-indexer scoring with top-k over the CSA cache,
+ * shared-KV multi-query attention over the k selected CSA entries, and
+ * dense shared-KV attention over the HCA cache.  Argument names follow the
+ * page's notation: n tokens, query position t, compressed width c, ratios m
+ * and m', budget k, n_h query heads, n_h^I indexer heads of width c^I.
+ *
+ * Conventions for every call:
+ *  - Tensor pointers are DEVICE pointers owned by the caller.  The library
+ *    never allocates, frees, copies to the host or synchronises; every call
+ *    only enqueues kernels on `stream` (a hipStream_t; NULL is the default
+ *    stream) and returns.
+ *  - Arrays are row-major and contiguous unless a stride argument says
+ *    otherwise; the batch index is outermost.  Strides count elements.
+ *  - `dtype` is the storage type of the compressed entries, streams and
+ *    queries (DLC_F32 or DLC_BF16).  Arithmetic always accumulates in fp32;
+ *    outputs documented as float are fp32.
+ *  - Return value: DLC_OK (0) or a negative dlc_status.  Arguments are
+ *    validated on the host before anything is enqueued; on an error nothing
+ *    is enqueued and dlc_last_error() describes the problem.  A failed launch
+ *    returns DLC_E_HIP.  No exception or abort crosses this boundary.
+ *  - Device-side values (query positions t, top-k indices and counts) are
+ *    clamped by the kernels to the ranges the host validated, so malformed
+ *    device data yields wrong numbers, never an out-of-bounds access.
+ *  - The calls hold no state and are reentrant; outputs are bitwise
+ *    reproducible for identical inputs, shapes and device.
+ */
+#ifndef DLC_H
+#define DLC_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DLC_ABI_VERSION 1
+
+typedef enum {
+  DLC_OK = 0,
+  DLC_E_INVAL = -1,       /* bad scalar argument or NULL required pointer */
+  DLC_E_DTYPE = -2,       /* unsupported dtype */
+  DLC_E_SHAPE = -3,       /* inconsistent sizes, strides or ranges */
+  DLC_E_WORKSPACE = -4,   /* workspace missing or smaller than the *_ws query */
+  DLC_E_HIP = -5,         /* a HIP runtime call or kernel launch failed */
+  DLC_E_UNSUPPORTED = -6  /* valid request outside this build's limits */
+} dlc_status;
+
+typedef enum { DLC_F32 = 0, DLC_BF16 = 1 } dlc_dtype;
+
+/* ABI version, status names and the last error of the calling thread. */
+int dlc_abi_version(void);
+const char* dlc_status_str(int status);
+const char* dlc_last_error(void);
+
+/*
+ * csa_compress - CSA compressed entries i_begin .. i_end-1 ([Scratch] §4-§5).
+ *
+ * For entry i and column j: one softmax over the 2m logits
+ *   Z^a[m*i + r][j] + B^a[r][j]        (r < m, current block)
+ *   Z^b[m*(i-1) + r][j] + B^b[r][j]    (r < m, previous block; absent for i = 0)
+ * then C^Comp[i][j] = sum of the weights times the matching C^a / C^b values.
+ * The missing b-rows of entry 0 (the page pads them with -inf) get weight 0.
+ * The same call builds the indexer-key cache K^IComp from the indexer's own
+ * four streams at width c := c^I ([Scratch] §6.4).
+ *
+ *  dtype          storage type of streams and output
+ *  B, n, c, m     sequences, valid stream rows per sequence, width, ratio (m >= 1)
+ *  Za, Zb, Ca, Cb streams; element (b, row, j) at X[b*batch_stride + row*ld + j]
+ *  ld             row stride (>= c); batch_stride (>= (n-1)*ld + c when B > 1)
+ *  Ba, Bb         fp32 [m][c] positional biases, or NULL for zeros
+ *  i_begin,i_end  0 <= i_begin <= i_end <= n/m; entries outside are untouched
+ *  Ccomp, cap     output [B][cap][c] (cap >= i_end); entry i of sequence b
+ *                 at Ccomp[(b*cap + i)*c]
+ * Decode appends one token row at a time; when (t+1) % m == 0 the caller
+ * compresses the entry that row completes with i_begin = (t+1)/m - 1.
+ */
+int csa_compress(int dtype, int64_t B, int64_t n, int64_t c, int64_t m,
+                 const void* Za, const void* Zb, const void* Ca, const void* Cb,
+                 int64_t ld, int64_t batch_stride, const float* Ba, const float* Bb,
+                 int64_t i_begin, int64_t i_end, void* Ccomp, int64_t cap, void* stream);
+
+/*
+ * hca_compress - HCA compressed entries ([Scratch] §10): one softmax per
+ * column over the m' logits Z[m'*i + r][j] + Bias[r][j] of the
+ * non-overlapping block i, then C^HCA[i][j] = sum_r S[r][j] * C[m'*i + r][j].
+ * Arguments as for csa_compress with one stream pair (Z, C) and an fp32
+ * [m'][c] Bias (NULL for zeros).
+ */
+int hca_compress(int dtype, int64_t B, int64_t n, int64_t c, int64_t m_prime,
+                 const void* Z, const void* C, int64_t ld, int64_t batch_stride,
+                 const float* Bias, int64_t i_begin, int64_t i_end,
+                 void* Chca, int64_t cap, void* stream);
+
+/*
+ * csa_index_topk - lightning-indexer scores and top-k ([Scratch] §6.4, §7).
+ *
+ * For query (b, q) at position t = t[b][q], over the visible entries
+ * s < min(floor(t/m), cap):
+ *   I[s] = sum_h w^I[h] * ReLU(q^I[h] . K^I[s])     (no softmax, no scale)
+ * then the k_eff = min(k, visible) largest scores, ranked by score
+ * (descending) and then index (ascending); -0.0 ranks equal to +0.0.
+ *
+ *  qI      [B][n_q][n_hI][cI] in dtype (head h is columns h*cI ... of the
+ *          up-projected latent, [Scratch] §6.2)
+ *  wI      [B][n_q][n_hI] fp32 head weights
+ *  KI,cap  [B][cap][cI] indexer-key cache in dtype
+ *  t       DEVICE int64 [B][n_q] query positions, each in [0, t_max]
+ *  t_max   host bound on t; floor(t_max/m) must not exceed cap
+ *  idx     out int32 [B][n_q][k]: the selected entries in ascending order,
+ *          padded with -1 after count entries
+ *  count   out int32 [B][n_q]: k_eff
+ *  scores  optional out fp32 [B][n_q][cap]: I[s] for visible s (others
+ *          untouched), or NULL
+ *  ws      workspace of at least csa_index_topk_ws(B, n_q, cap, k) bytes,
+ *          256-byte aligned; its contents on entry do not matter
+ * Limits: 1 <= k <= 16384; n_hI*cI <= 16384.
+ */
+size_t csa_index_topk_ws(int64_t B, int64_t n_q, int64_t cap, int64_t k);
+int csa_index_topk(int dtype, int64_t B, int64_t n_q, int64_t n_hI, int64_t cI, int64_t m, int64_t k,
+                   const void* qI, const float* wI, const void* KI, int64_t cap,
+                   const int64_t* t, int64_t t_max, int32_t* idx, int32_t* count, float* scores,
+                   void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * csa_attend - shared-KV multi-query attention over the selected CSA
+ * entries ([Scratch] §8): for every head h,
+ *   o[h] = sum_s softmax_s(scale * q[h] . C^Comp[s]) * C^Comp[s],
+ *   lse[h] = log sum_s exp(scale * q[h] . C^Comp[s]),
+ * over s = idx[b][q][0 .. count-1].  Key and value are the same entry.
+ *
+ *  q         [B][n_q][n_h][c] in dtype
+ *  Ccomp,cap [B][cap][c] compressed cache in dtype
+ *  idx,count as returned by csa_index_topk; indices outside [0, cap) and
+ *            positions past min(count, k) are ignored
+ *  scale     logit scale; <= 0 selects 1/sqrt(c)
+ *  out       fp32 [B][n_q][n_h][c];  lse: fp32 [B][n_q][n_h] or NULL
+ *  ws        at least csa_attend_ws(B, n_q, n_h, c, k) bytes, 256-byte aligned
+ * An empty selection gives o = 0 and lse = -inf.
+ */
+size_t csa_attend_ws(int64_t B, int64_t n_q, int64_t n_h, int64_t c, int64_t k);
+int csa_attend(int dtype, int64_t B, int64_t n_q, int64_t n_h, int64_t c, int64_t k,
+               const void* q, const void* Ccomp, int64_t cap, const int32_t* idx, const int32_t* count,
+               float scale, float* out, float* lse, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * hca_attend - dense shared-KV attention over every visible HCA entry
+ * s < min(floor(t/m'), cap) ([Scratch] §10 and the unified operator of §11,
+ * whose top-k is a no-op for HCA).  Same formula, layouts and empty-case
+ * rule as csa_attend; t and t_max as for csa_index_topk with m := m'.
+ *  ws  at least hca_attend_ws(B, n_q, n_h, c, cap) bytes, 256-byte aligned
+ */
+size_t hca_attend_ws(int64_t B, int64_t n_q, int64_t n_h, int64_t c, int64_t cap);
+int hca_attend(int dtype, int64_t B, int64_t n_q, int64_t n_h, int64_t c, int64_t m_prime,
+               const void* q, const void* Chca, int64_t cap, const int64_t* t, int64_t t_max,
+               float scale, float* out, float* lse, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * dlc_project - dense projection out = A . W with fp32 accumulation, the
+ * token projections that feed the compressor and the queries ([Scratch] §3:
+ * C^a = H W^{aKV} and its siblings; §6.1-6.3 and §8: c^Q, q^I, w^I, q).
+ *
+ *  A    [M][K] rows with stride lda, in dtype
+ *  Wt   the weight matrix W [K][N] stored transposed, Wt[N][K] with row
+ *       stride ldw, in dtype
+ *  out  [M][N] with row stride ldo, stored in out_dtype (DLC_F32 or dtype)
+ */
+int dlc_project(int dtype, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
+                const void* Wt, int64_t ldw, void* out, int64_t ldo, int out_dtype, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DLC_H */

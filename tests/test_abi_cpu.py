@@ -1,0 +1,146 @@
+"""The C ABI on the host: the library loads, exports every declared symbol and
+rejects bad arguments before anything reaches the device (no GPU needed)."""
+
+import ctypes as C
+import os
+import re
+
+import pytest
+
+from dense_long_context_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dlc.h")
+
+OK, E_INVAL, E_DTYPE, E_SHAPE, E_WORKSPACE, E_HIP, E_UNSUPPORTED = 0, -1, -2, -3, -4, -5, -6
+F32, BF16 = 0, 1
+P = 0x1000  # a fake, 256-byte aligned pointer: never dereferenced, validation fails first
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:int|size_t|const char\*)\s+(\w+)\s*\(", text, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    return binding.lib()
+
+
+def test_exports_every_declared_symbol(L):
+    names = declared_functions()
+    assert len(names) >= 12
+    for n in names:
+        assert hasattr(L, n), n
+        assert n in binding.SIGNATURES, f"binding lacks {n}"
+
+
+def test_version_and_status_strings(L):
+    assert L.dlc_abi_version() == 1
+    assert binding.status_str(E_WORKSPACE) == "DLC_E_WORKSPACE"
+    assert binding.status_str(12345) == "DLC_E_UNKNOWN"
+
+
+def _csa_compress(L, **kw):
+    a = dict(dtype=BF16, B=1, n=16, c=8, m=4, Za=P, Zb=P, Ca=P, Cb=P, ld=8, bs=128, Ba=None, Bb=None,
+             i0=0, i1=4, out=P, cap=4)
+    a.update(kw)
+    return L.csa_compress(a["dtype"], a["B"], a["n"], a["c"], a["m"], a["Za"], a["Zb"], a["Ca"], a["Cb"],
+                          a["ld"], a["bs"], a["Ba"], a["Bb"], a["i0"], a["i1"], a["out"], a["cap"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dtype=7), E_DTYPE),
+    (dict(m=0), E_INVAL),
+    (dict(c=0), E_INVAL),
+    (dict(B=0), E_INVAL),
+    (dict(Za=None), E_INVAL),
+    (dict(out=None), E_INVAL),
+    (dict(Zb=None), E_INVAL),          # CSA needs the b-streams
+    (dict(ld=4), E_SHAPE),             # ld < c
+    (dict(B=2, bs=64), E_SHAPE),       # sequences overlap
+    (dict(i1=5), E_SHAPE),             # i_end > n/m
+    (dict(i0=3, i1=2), E_SHAPE),
+    (dict(i0=-1), E_SHAPE),
+    (dict(cap=3), E_SHAPE),            # cap < i_end
+    (dict(i0=2, i1=2), OK),            # empty range: nothing to do, nothing launched
+])
+def test_csa_compress_validation(L, kw, status):
+    assert _csa_compress(L, **kw) == status
+    if status:
+        assert binding.last_error().startswith("csa_compress")
+
+
+def test_hca_compress_validation(L):
+    assert L.hca_compress(BF16, 1, 12, 8, 3, P, P, 8, 96, None, 0, 5, P, 5, None) == E_SHAPE
+    assert L.hca_compress(BF16, 1, 12, 8, 3, P, None, 8, 96, None, 0, 4, P, 4, None) == E_INVAL
+    assert L.hca_compress(BF16, 1, 12, 8, 3, P, P, 8, 96, None, 0, 0, P, 4, None) == OK
+
+
+def _topk(L, **kw):
+    a = dict(dtype=BF16, B=1, n_q=1, n_hI=4, cI=64, m=4, k=8, qI=P, wI=P, KI=P, cap=16, t=P, t_max=64,
+             idx=P, count=P, scores=None, ws=P, ws_bytes=1 << 30)
+    a.update(kw)
+    return L.csa_index_topk(a["dtype"], a["B"], a["n_q"], a["n_hI"], a["cI"], a["m"], a["k"], a["qI"],
+                            a["wI"], a["KI"], a["cap"], a["t"], a["t_max"], a["idx"], a["count"],
+                            a["scores"], a["ws"], a["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dtype=3), E_DTYPE),
+    (dict(k=0), E_UNSUPPORTED),
+    (dict(k=8193), E_UNSUPPORTED),
+    (dict(n_hI=128, cI=128), E_UNSUPPORTED),
+    (dict(m=0), E_INVAL),
+    (dict(t_max=68), E_SHAPE),          # floor(68/4) = 17 > cap
+    (dict(qI=None), E_INVAL),
+    (dict(idx=None), E_INVAL),
+    (dict(ws=None), E_WORKSPACE),
+    (dict(ws_bytes=16), E_WORKSPACE),
+    (dict(ws=P + 8), E_WORKSPACE),      # misaligned
+])
+def test_index_topk_validation(L, kw, status):
+    assert _topk(L, **kw) == status
+
+
+def test_workspace_queries(L):
+    w1 = L.csa_index_topk_ws(4, 1, 262144, 1024)
+    assert w1 > 262144 * 4 * 4
+    assert L.csa_index_topk_ws(4, 2, 262144, 1024) > w1
+    assert L.csa_index_topk_ws(0, 1, 10, 1) == 0
+    assert L.csa_attend_ws(1, 1, 1, 2, 1) == 0           # one split: no partials
+    big = L.hca_attend_ws(16, 1, 128, 512, 8192)
+    assert big > 0 and big % 256 == 0
+    assert L.hca_attend_ws(16, 1, 128, 512, 16384) >= big
+
+
+def test_attend_validation(L):
+    args = lambda **kw: dict(dict(dtype=BF16, B=1, n_q=1, n_h=4, c=128, k=8, q=P, C=P, cap=16, idx=P,  # noqa
+                                  count=P, out=P, lse=None, ws=None, wsb=0), **kw)
+    def csa(**kw):
+        a = args(**kw)
+        return L.csa_attend(a["dtype"], a["B"], a["n_q"], a["n_h"], a["c"], a["k"], a["q"], a["C"], a["cap"],
+                            a["idx"], a["count"], 0.0, a["out"], a["lse"], a["ws"], a["wsb"], None)
+    assert csa(dtype=9) == E_DTYPE
+    assert csa(k=0) == E_INVAL
+    assert csa(idx=None) == E_INVAL
+    assert csa(q=P + 2) == E_INVAL                       # MFMA path needs 16-byte alignment
+    assert csa(dtype=F32, c=2048) == E_UNSUPPORTED
+    assert csa(B=4, n_h=128, c=512, k=1024) == E_WORKSPACE
+    assert L.hca_attend(BF16, 1, 1, 4, 128, 128, P, P, 4, P, 1024, 0.0, P, None, None, 0, None) == E_SHAPE
+    assert L.hca_attend(BF16, 1, 1, 4, 128, 0, P, P, 4, P, 100, 0.0, P, None, None, 0, None) == E_INVAL
+
+
+def test_project_validation(L):
+    assert L.dlc_project(BF16, 4, 4, 0, P, 8, P, 8, P, 4, BF16, None) == E_INVAL
+    assert L.dlc_project(BF16, 4, 4, 8, P, 4, P, 8, P, 4, BF16, None) == E_SHAPE
+    assert L.dlc_project(F32, 4, 4, 8, P, 8, P, 8, P, 4, BF16, None) == E_DTYPE
+    assert L.dlc_project(BF16, 0, 4, 8, P, 8, P, 8, P, 4, BF16, None) == OK
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(binding, "_lib", None)
+    monkeypatch.setattr(binding, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(ImportError):
+        binding.lib()

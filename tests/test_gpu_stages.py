@@ -1,0 +1,267 @@
+"""Stage parity on the GPU: every C-ABI call against the fp64 oracle on the
+same seeded inputs, at sizes that span several tiles with ragged tails, plus
+the degenerate cases (nothing visible, k >= visible, ties, masked indices).
+
+Tolerances (derived in the design notes): fp32 outputs 1e-5 row-relative;
+bf16-stored outputs 8e-3 row-relative (one bf16 rounding of an fp32 result);
+fp32 attention outputs from bf16 inputs 2e-2 row-relative (spec bar);
+top-k per the tie rule in devtools.check_topk.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import dense_long_context_amd as dlc
+import oracle as O
+import synth
+from devtools import DEV, assert_rows_close, check_topk, f64, need_gpu
+
+pytestmark = pytest.mark.gpu
+
+TD = {"f32": torch.float32, "bf16": torch.bfloat16}
+TOL_STORE = {"f32": 1e-5, "bf16": 8e-3}
+TOL_ATT = {"f32": 1e-5, "bf16": 2e-2}
+
+
+def setup_module():
+    need_gpu()
+
+
+def _streams(B, n, c, dtype, seed, nstreams=4, ld=None, scale=1.0):
+    """Streams [B][n][c] drawn as one [B][n][ld] buffer (ld >= c), returned as views."""
+    ld = ld or c
+    full = synth.normal((nstreams, B, n, ld), seed, std=scale, dtype=dtype)
+    return [full[i] for i in range(nstreams)], full
+
+
+# ------------------------------------------------------------------ compress
+
+@pytest.mark.parametrize("dtype,B,n,c,m,ld,bias", [
+    ("f32", 1, 6, 2, 2, 2, False),        # the worked example's shape
+    ("f32", 2, 37, 5, 3, 7, True),        # generic path, ragged tail, strided rows
+    ("f32", 3, 64, 12, 4, 12, True),      # fp32 vector path
+    ("bf16", 2, 130, 6, 4, 6, True),      # bf16 generic path (c not a multiple of 8)
+    ("bf16", 2, 1000, 128, 4, 136, True), # bf16 vector path, strided rows
+    ("bf16", 1, 4096, 512, 4, 512, False),
+    ("bf16", 2, 515, 64, 1, 64, True),    # m = 1
+])
+def test_csa_compress(dtype, B, n, c, m, ld, bias):
+    seed = 100 + n
+    (Za, Zb, Ca, Cb), full = _streams(B, n, ld, dtype, seed, scale=2.0)
+    Za, Zb, Ca, Cb = (x[:, :, :c] for x in (Za, Zb, Ca, Cb))
+    Ba = synth.normal((m, c), seed + 1, dtype="f32") if bias else None
+    Bb = synth.normal((m, c), seed + 2, dtype="f32") if bias else None
+    cap = n // m + 3
+    dev = lambda x: None if x is None else x.to(DEV)  # noqa: E731
+    # same strides on the device: move the full buffer and slice it
+    dfull = full.to(DEV)
+    dZa, dZb, dCa, dCb = (dfull[i][:, :, :c] for i in range(4))
+    out = torch.full((B, cap, c), 7.0, dtype=TD[dtype], device=DEV)
+    nent = n // m
+    mid = nent // 3
+    # two calls (entries [0, mid) then [mid, n/m)) must equal the definition
+    dlc.csa_compress(dZa, dZb, dCa, dCb, m, out, 0, mid, dev(Ba), dev(Bb))
+    dlc.csa_compress(dZa, dZb, dCa, dCb, m, out, mid, nent, dev(Ba), dev(Bb))
+    torch.cuda.synchronize()
+    got = out.cpu()
+    for b in range(B):
+        ref = O.csa_compress(Za[b], Zb[b], Ca[b], Cb[b], m, Ba, Bb)
+        assert_rows_close(got[b, :nent], O.store_as(ref, dtype), TOL_STORE[dtype], f"csa b={b}")
+        assert (got[b, nent:].float() == 7.0).all(), "entries past i_end must be untouched"
+
+
+@pytest.mark.parametrize("dtype,B,n,c,mp,bias", [
+    ("f32", 1, 6, 2, 3, False),
+    ("f32", 2, 100, 9, 7, True),
+    ("bf16", 3, 1000, 64, 128, True),
+    ("bf16", 2, 8 * 128 + 50, 512, 128, False),
+    ("bf16", 1, 77, 16, 1, True),
+])
+def test_hca_compress(dtype, B, n, c, mp, bias):
+    seed = 300 + n
+    (Z, Cs), full = _streams(B, n, c, dtype, seed, nstreams=2, scale=2.0)
+    Bh = synth.normal((mp, c), seed + 1, dtype="f32") if bias else None
+    cap = n // mp
+    dfull = full.to(DEV)
+    out = torch.empty((B, cap, c), dtype=TD[dtype], device=DEV)
+    dlc.hca_compress(dfull[0], dfull[1], mp, out, bias=None if Bh is None else Bh.to(DEV))
+    torch.cuda.synchronize()
+    got = out.cpu()
+    for b in range(B):
+        ref = O.hca_compress(Z[b], Cs[b], mp, Bh)
+        assert_rows_close(got[b], O.store_as(ref, dtype), TOL_STORE[dtype], f"hca b={b}")
+
+
+# ------------------------------------------------------------ indexer, top-k
+
+def _score_slack(qI, wI, KI):
+    """fp32-accumulation error bound of the device scores, per entry."""
+    q, w, K = f64(qI), f64(wI), f64(KI)
+    mag = np.abs(K) @ np.abs(q).T @ np.abs(w)
+    return 2e-6 * mag * (q.shape[1] + q.shape[0]) ** 0.5 + 1e-30
+
+
+@pytest.mark.parametrize("dtype,B,n_q,n_hI,cI,m,k,cap,ts", [
+    ("f32", 1, 1, 1, 2, 2, 1, 3, [5]),                      # worked-example shape
+    ("f32", 2, 2, 3, 5, 4, 7, 50, [200, 37, 3, 150]),       # VALU path, ragged
+    ("bf16", 1, 1, 4, 64, 4, 64, 2048, [8192]),             # decode-8k indexer shape
+    ("bf16", 2, 3, 64, 128, 4, 100, 5000, [20000, 19999, 4, 333, 8000, 0]),
+    ("bf16", 1, 2, 16, 32, 4, 1024, 1500, [6000, 4100]),    # k >= visible for one query
+    ("bf16", 2, 1, 20, 64, 2, 300, 4000, [8000, 7777]),     # head padding (20 -> 32)
+    ("bf16", 1, 1, 64, 256, 4, 16, 600, [2400]),
+])
+def test_index_topk(dtype, B, n_q, n_hI, cI, m, k, cap, ts):
+    seed = 500 + cap
+    qI = synth.normal((B, n_q, n_hI, cI), seed, dtype=dtype)
+    wI = synth.normal((B, n_q, n_hI), seed + 1, dtype="f32")
+    KI = synth.normal((B, cap, cI), seed + 2, dtype=dtype)
+    t = torch.tensor(ts, dtype=torch.int64).reshape(B, n_q)
+    t_max = int(t.max())
+    scores = torch.full((B, n_q, cap), float("nan"), dtype=torch.float32, device=DEV)
+    idx, cnt = dlc.csa_index_topk(qI.to(DEV), wI.to(DEV), KI.to(DEV), t.to(DEV), t_max, m, k, scores=scores)
+    torch.cuda.synchronize()
+    idx, cnt, sc = idx.cpu().numpy(), cnt.cpu().numpy(), scores.cpu().numpy()
+    for b in range(B):
+        for j in range(n_q):
+            tt = int(t[b, j])
+            ref = O.index_scores(qI[b, j], wI[b, j], KI[b], tt, m)
+            nv = len(ref)
+            slack = _score_slack(qI[b, j], wI[b, j], KI[b, :nv])
+            assert np.all(np.abs(sc[b, j, :nv] - ref) <= slack), f"scores b={b} q={j}"
+            check_topk(idx[b, j], cnt[b, j], ref, k, abs_slack=float(slack.max()) if nv else 0.0)
+
+
+def test_index_topk_ties_pick_smallest_indices():
+    # every score equal (zero keys): the k smallest indices, in order
+    B, cap, k = 1, 3000, 100
+    qI = synth.normal((B, 1, 64, 128), 1, dtype="bf16")
+    wI = synth.normal((B, 1, 64), 2, dtype="f32")
+    KI = torch.zeros((B, cap, 128), dtype=torch.bfloat16)
+    t = torch.tensor([[4 * cap]])
+    idx, cnt = dlc.csa_index_topk(qI.to(DEV), wI.to(DEV), KI.to(DEV), t.to(DEV), 4 * cap, 4, k)
+    assert int(cnt[0, 0]) == k
+    assert idx[0, 0].cpu().tolist() == list(range(k))
+
+
+def test_index_topk_duplicate_rows_break_ties_by_index():
+    # 2001 exact copies of the best-scoring row: the top-512 are all tied at the
+    # maximum, so the tie rule alone decides them: the 512 smallest indices
+    cap, k = 4096, 512
+    KI = synth.normal((1, cap, 64), 7, dtype="bf16")
+    qI = synth.normal((1, 1, 8, 64), 8, dtype="bf16")
+    wI = torch.ones((1, 1, 8))
+    best = int(np.argmax(O.index_scores(qI[0, 0], wI[0, 0], KI[0], 4 * cap, 4)))
+    KI[0, 1000:3000] = KI[0, best]
+    ties = sorted(set(range(1000, 3000)) | {best})
+    t = torch.tensor([[4 * cap]])
+    idx, cnt = dlc.csa_index_topk(qI.to(DEV), wI.to(DEV), KI.to(DEV), t.to(DEV), 4 * cap, 4, k)
+    assert int(cnt[0, 0]) == k
+    assert idx[0, 0].cpu().tolist() == ties[:k]
+
+
+def test_index_topk_nothing_visible():
+    qI = synth.normal((2, 1, 4, 64), 3, dtype="bf16")
+    wI = synth.normal((2, 1, 4), 4, dtype="f32")
+    KI = synth.normal((2, 10, 64), 5, dtype="bf16")
+    t = torch.tensor([[3], [0]])
+    idx, cnt = dlc.csa_index_topk(qI.to(DEV), wI.to(DEV), KI.to(DEV), t.to(DEV), 3, 4, 8)
+    assert cnt.cpu().tolist() == [[0], [0]]
+    assert (idx.cpu() == -1).all()
+
+
+# ---------------------------------------------------------------- attention
+
+def _random_selection(B, n_q, k, cap, seed, counts):
+    g = torch.Generator().manual_seed(seed)
+    idx = torch.full((B, n_q, k), -1, dtype=torch.int32)
+    for b in range(B):
+        for j in range(n_q):
+            c = counts[b * n_q + j]
+            sel = torch.randperm(cap, generator=g)[:c].sort().values
+            idx[b, j, :c] = sel.to(torch.int32)
+    cnt = torch.tensor(counts, dtype=torch.int32).reshape(B, n_q)
+    return idx, cnt
+
+
+@pytest.mark.parametrize("dtype,B,n_q,n_h,c,k,cap,counts", [
+    ("f32", 1, 1, 1, 2, 1, 3, [1]),                          # worked-example shape
+    ("f32", 2, 1, 3, 10, 9, 40, [9, 4]),                     # VALU path
+    ("bf16", 1, 1, 16, 128, 64, 2048, [64]),                 # decode-8k shape
+    ("bf16", 2, 2, 128, 512, 1024, 32768, [1024, 1000, 77, 0]),
+    ("bf16", 1, 1, 48, 256, 300, 900, [299]),                # heads not a multiple of 32
+    ("bf16", 1, 3, 128, 512, 40, 5000, [40, 33, 1]),
+])
+def test_csa_attend(dtype, B, n_q, n_h, c, k, cap, counts):
+    seed = 700 + cap + k
+    q = synth.normal((B, n_q, n_h, c), seed, dtype=dtype)
+    C = synth.normal((B, cap, c), seed + 1, dtype=dtype)
+    idx, cnt = _random_selection(B, n_q, k, cap, seed + 2, counts)
+    out, lse = dlc.csa_attend(q.to(DEV), C.to(DEV), idx.to(DEV), cnt.to(DEV))
+    torch.cuda.synchronize()
+    out, lse = out.cpu(), lse.cpu()
+    for b in range(B):
+        for j in range(n_q):
+            sel = idx[b, j, :counts[b * n_q + j]].numpy()
+            o_ref, l_ref = O.csa_attend(q[b, j], C[b], sel)
+            if len(sel) == 0:
+                assert (out[b, j] == 0).all() and torch.isneginf(lse[b, j]).all()
+                continue
+            assert_rows_close(out[b, j], o_ref, TOL_ATT[dtype], f"csa o b={b} q={j}")
+            assert np.abs(f64(lse[b, j]) - l_ref).max() <= 1e-3 + 1e-5 * np.abs(l_ref).max()
+
+
+def test_csa_attend_ignores_invalid_indices():
+    B, k, cap, c, n_h = 1, 16, 100, 128, 32
+    q = synth.normal((B, 1, n_h, c), 11, dtype="bf16")
+    C = synth.normal((B, cap, c), 12, dtype="bf16")
+    idx = torch.tensor([[[3, 7, -1, 250, 9, 11, 5000, 2] + [-1] * 8]], dtype=torch.int32)
+    cnt = torch.tensor([[10]], dtype=torch.int32)  # count beyond the valid run: padding ignored too
+    out, lse = dlc.csa_attend(q.to(DEV), C.to(DEV), idx.to(DEV), cnt.to(DEV))
+    o_ref, l_ref = O.csa_attend(q[0, 0], C[0], [3, 7, 9, 11, 2])
+    assert_rows_close(out[0, 0].cpu(), o_ref, 2e-2, "masked indices")
+
+
+@pytest.mark.parametrize("dtype,B,n_q,n_h,c,mp,cap,ts", [
+    ("f32", 1, 1, 1, 2, 3, 2, [5]),                          # worked-example shape
+    ("f32", 2, 1, 2, 16, 4, 30, [100, 7]),
+    ("bf16", 1, 1, 16, 128, 128, 64, [8192]),                # decode-8k shape
+    ("bf16", 3, 1, 128, 512, 128, 700, [700 * 128, 3 * 128 + 5, 100]),
+    ("bf16", 2, 2, 40, 256, 16, 513, [513 * 16, 16 * 500 + 3, 31, 16 * 64]),
+])
+def test_hca_attend(dtype, B, n_q, n_h, c, mp, cap, ts):
+    seed = 900 + cap
+    q = synth.normal((B, n_q, n_h, c), seed, dtype=dtype)
+    C = synth.normal((B, cap, c), seed + 1, dtype=dtype)
+    t = torch.tensor(ts, dtype=torch.int64).reshape(B, n_q)
+    out, lse = dlc.hca_attend(q.to(DEV), C.to(DEV), t.to(DEV), int(t.max()), mp)
+    torch.cuda.synchronize()
+    out, lse = out.cpu(), lse.cpu()
+    for b in range(B):
+        for j in range(n_q):
+            o_ref, l_ref = O.hca_attend(q[b, j], C[b], int(t[b, j]), mp)
+            if not np.isfinite(l_ref).any():
+                assert (out[b, j] == 0).all() and torch.isneginf(lse[b, j]).all()
+                continue
+            assert_rows_close(out[b, j], o_ref, TOL_ATT[dtype], f"hca o b={b} q={j}")
+            assert np.abs(f64(lse[b, j]) - l_ref).max() <= 1e-3 + 1e-5 * np.abs(l_ref).max()
+
+
+# --------------------------------------------------------------- projection
+
+@pytest.mark.parametrize("dtype,M,N,K,out_dtype", [
+    ("f32", 6, 2, 2, "f32"),
+    ("f32", 33, 70, 19, "f32"),
+    ("bf16", 300, 260, 1024, "bf16"),
+    ("bf16", 129, 64, 72, "f32"),
+    ("bf16", 1, 8192, 512, "bf16"),
+])
+def test_project(dtype, M, N, K, out_dtype):
+    A = synth.normal((M, K), 41, dtype=dtype)
+    W = synth.normal((K, N), 42, std=K ** -0.5, dtype=dtype)
+    out = dlc.dlc_project(A.to(DEV), W.t().contiguous().to(DEV), out_dtype=TD[out_dtype])
+    ref = O.project(A, W)
+    tol = 1e-5 if out_dtype == "f32" else 8e-3
+    assert_rows_close(out.cpu(), O.store_as(ref, out_dtype) if out_dtype == "bf16" else ref, tol, "project")
