@@ -1,0 +1,383 @@
+"""Decode throughput of one CSA layer plus one HCA layer at 1M context on one GPU.
+
+Workload (hybrid1m): B = 4 sequences of 2^20 context tokens, d = 7168 bf16
+hidden states ~N(0,1), projection weights N(0, 1/d); c = 512, m = 4, m' = 128,
+k = 1024, n_h = 128, n_h^I = 64, c^I = 128.  Set-up (untimed): the hidden
+states are projected to the compressor streams (dlc_project), the CSA,
+indexer-key and HCA caches are built by the compressors over all 2^20 + 256
+tokens, and the decode queries of the 256 decode tokens are projected.
+Three copies of the caches stand for three layers' caches and rotate per
+step, so a step does not re-read what the previous step left in the 256 MB
+last-level cache.
+
+One step = the whole hot path for the B decode queries at t = 2^20 + s:
+  csa_compress x2 (KV and indexer keys, when token t completes a CSA block),
+  hca_compress (when t completes an HCA block), csa_index_topk, csa_attend,
+  hca_attend.
+Every call goes through the C ABI with pre-marshalled arguments.
+
+Prints one JSON line.  With --gpus N > 1 it exits: this build runs on one GPU.
+"""
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "decode query-tokens/s per CSA+HCA layer at 1M ctx; achieved HBM GB/s vs peak"
+PEAK_HBM_GBS = 8000.0
+SCORES_KERNEL = "scores_mfma_kernel<4, 4>"
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "indexer_scores_hybrid1m_counters.json")
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def source_hash():
+    h = hashlib.sha256()
+    for f in ("indexer.hip", "common.hpp"):
+        with open(os.path.join(ROOT, "dense_long_context_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+class HipEvents:
+    """Raw hipEvent_t handles (for dlc_timing_arm) through libamdhip64."""
+
+    def __init__(self):
+        import ctypes as C
+
+        self.C = C
+        self.hip = C.CDLL("libamdhip64.so")
+        self.hip.hipEventCreate.argtypes = [C.POINTER(C.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [C.POINTER(C.c_float), C.c_void_p, C.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [C.c_void_p]
+
+    def create(self):
+        e = self.C.c_void_p()
+        assert self.hip.hipEventCreate(self.C.byref(e)) == 0
+        return e.value
+
+    def elapsed_ms(self, a, b):
+        ms = self.C.c_float()
+        assert self.hip.hipEventElapsedTime(self.C.byref(ms), a, b) == 0
+        return ms.value
+
+    def destroy(self, e):
+        self.hip.hipEventDestroy(e)
+
+
+def build_workload(cfg, dev, n_dec):
+    import torch
+
+    import dense_long_context_amd as dlc
+    import synth
+
+    B, d, c, cI, m, mp = cfg.B, cfg.d, cfg.c, cfg.cI, cfg.m, cfg.m_prime
+    n_ctx = cfg.t                       # 2^20 context tokens
+    n_tot = n_ctx + n_dec               # plus the decode tokens
+    std = cfg.weight_std
+    t0 = time.perf_counter()
+    # weights (host draws, moved once); streams are laid out side by side
+    order = ["aKV", "bKV", "aZ", "bZ", "IaKV", "IbKV", "IaZ", "IbZ", "KV", "Z"]
+    width = {nm: (cI if nm.startswith("I") else c) for nm in order}
+    Wt = torch.cat([synth.normal((d, width[nm]), synth.tensor_seed(cfg.seed, nm), std, "bf16").t()
+                    for nm in order], 0).contiguous().to(dev)          # [3584][d]
+    off, o = {}, 0
+    for nm in order:
+        off[nm] = o
+        o += width[nm]
+    NS = o
+    S = torch.empty((B, n_tot, NS), dtype=torch.bfloat16, device=dev)
+    H_dec = torch.empty((B, n_dec, d), dtype=torch.bfloat16, device=dev)  # hidden states of the decode tokens
+    chunk = 1 << 16
+    for b in range(B):
+        base = synth.tensor_seed(cfg.seed, "H") * 16 + b
+        for r0 in range(0, n_tot, chunk):
+            r1 = min(n_tot, r0 + chunk)
+            Hc = synth.normal_chunked_rows(n_tot, d, base, 1.0, "bf16", dev, r0, r1)
+            dlc.dlc_project(Hc, Wt, out=S[b, r0:r1])
+            if r0 <= n_ctx < r1:
+                H_dec[b] = Hc[n_ctx - r0:n_ctx - r0 + n_dec]
+    torch.cuda.synchronize()
+    t_proj = time.perf_counter() - t0
+    col = lambda nm: S[:, :, off[nm]:off[nm] + width[nm]]  # noqa: E731
+
+    cap_csa, cap_hca = n_tot // m, n_tot // mp
+    t1 = time.perf_counter()
+    sets = []
+    for _ in range(3):
+        Cc = torch.empty((B, cap_csa, c), dtype=torch.bfloat16, device=dev)
+        KI = torch.empty((B, cap_csa, cI), dtype=torch.bfloat16, device=dev)
+        Ch = torch.empty((B, cap_hca, c), dtype=torch.bfloat16, device=dev)
+        dlc.csa_compress(col("aZ"), col("bZ"), col("aKV"), col("bKV"), m, Cc)
+        dlc.csa_compress(col("IaZ"), col("IbZ"), col("IaKV"), col("IbKV"), m, KI)
+        dlc.hca_compress(col("Z"), col("KV"), mp, Ch)
+        sets.append((Cc, KI, Ch))
+    torch.cuda.synchronize()
+    t_comp = (time.perf_counter() - t1) / 3
+
+    # decode queries of tokens n_ctx .. n_tot-1 (projected once, stored per step)
+    def W(nm, rows, cols):
+        return synth.normal((rows, cols), synth.tensor_seed(cfg.seed, nm), std if nm in ("DQ", "w") else
+                            cfg.d_c ** -0.5, "bf16").t().contiguous().to(dev)
+    h = H_dec.reshape(B * n_dec, d)
+    cQ = dlc.dlc_project(h, W("DQ", d, cfg.d_c))
+    qI = dlc.dlc_project(cQ, W("IUQ", cfg.d_c, cfg.n_hI * cI))
+    wI = dlc.dlc_project(h, W("w", d, cfg.n_hI), out_dtype=torch.float32)
+    q = dlc.dlc_project(cQ, W("UQ", cfg.d_c, cfg.n_h * c))
+    qh = dlc.dlc_project(cQ, W("UQ_hca", cfg.d_c, cfg.n_h * c))
+    per_step = lambda x, *shape: x.reshape(B, n_dec, *shape).transpose(0, 1).contiguous()  # noqa: E731
+    Q = dict(qI=per_step(qI, 1, cfg.n_hI, cI), wI=per_step(wI, 1, cfg.n_hI), q=per_step(q, 1, cfg.n_h, c),
+             qh=per_step(qh, 1, cfg.n_h, c))
+    torch.cuda.synchronize()
+    del H_dec
+    return dict(S=S, col=col, sets=sets, Q=Q, n_ctx=n_ctx, n_tot=n_tot, cap_csa=cap_csa, cap_hca=cap_hca,
+                t_proj=t_proj, t_comp=t_comp, stream_bytes=S.numel() * 2)
+
+
+def make_steps(cfg, wl, dev, n_dec):
+    """Pre-marshal the C-ABI argument tuples of every decode step."""
+    import torch
+
+    import dense_long_context_amd as dlc
+    from dense_long_context_amd import binding
+
+    L = binding.lib()
+    B, c, cI, m, mp, k, n_h, n_hI = cfg.B, cfg.c, cfg.cI, cfg.m, cfg.m_prime, cfg.k, cfg.n_h, cfg.n_hI
+    BF = binding.DLC_BF16
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    S, col = wl["S"], wl["col"]
+    ld, bs = S.stride(1), S.stride(0)
+    n_tot, cap_csa, cap_hca = wl["n_tot"], wl["cap_csa"], wl["cap_hca"]
+    ws_i = torch.empty(dlc.csa_index_topk_ws(B, 1, cap_csa, k), dtype=torch.uint8, device=dev)
+    ws_c = torch.empty(max(1, dlc.csa_attend_ws(B, 1, n_h, c, k)), dtype=torch.uint8, device=dev)
+    ws_h = torch.empty(max(1, dlc.hca_attend_ws(B, 1, n_h, c, cap_hca)), dtype=torch.uint8, device=dev)
+    idx = torch.empty((B, 1, k), dtype=torch.int32, device=dev)
+    cnt = torch.empty((B, 1), dtype=torch.int32, device=dev)
+    o1 = torch.empty((B, 1, n_h, c), dtype=torch.float32, device=dev)
+    l1 = torch.empty((B, 1, n_h), dtype=torch.float32, device=dev)
+    o2, l2 = torch.empty_like(o1), torch.empty_like(l1)
+    tt = torch.arange(wl["n_ctx"], wl["n_ctx"] + n_dec, dtype=torch.int64, device=dev)
+    tt = tt[:, None, None].expand(n_dec, B, 1).contiguous()
+    p = lambda x: x.data_ptr()  # noqa: E731
+    Q = wl["Q"]
+    steps = []
+    for s in range(n_dec):
+        t = wl["n_ctx"] + s
+        Cc, KI, Ch = wl["sets"][s % 3]
+        calls = []
+        if (t + 1) % m == 0:
+            i = (t + 1) // m - 1
+            calls.append((L.csa_compress, (BF, B, n_tot, c, m, p(col("aZ")), p(col("bZ")), p(col("aKV")),
+                                           p(col("bKV")), ld, bs, None, None, i, i + 1, p(Cc), cap_csa, stream)))
+            calls.append((L.csa_compress, (BF, B, n_tot, cI, m, p(col("IaZ")), p(col("IbZ")), p(col("IaKV")),
+                                           p(col("IbKV")), ld, bs, None, None, i, i + 1, p(KI), cap_csa, stream)))
+        if (t + 1) % mp == 0:
+            i = (t + 1) // mp - 1
+            calls.append((L.hca_compress, (BF, B, n_tot, c, mp, p(col("Z")), p(col("KV")), ld, bs, None, i, i + 1,
+                                           p(Ch), cap_hca, stream)))
+        calls.append((L.csa_index_topk, (BF, B, 1, n_hI, cI, m, k, p(Q["qI"][s]), p(Q["wI"][s]), p(KI), cap_csa,
+                                         p(tt[s]), t, p(idx), p(cnt), None, p(ws_i), ws_i.numel(), stream)))
+        calls.append((L.csa_attend, (BF, B, 1, n_h, c, k, p(Q["q"][s]), p(Cc), cap_csa, p(idx), p(cnt), 0.0,
+                                     p(o1), p(l1), p(ws_c), ws_c.numel(), stream)))
+        calls.append((L.hca_attend, (BF, B, 1, n_h, c, mp, p(Q["qh"][s]), p(Ch), cap_hca, p(tt[s]), t, 0.0,
+                                     p(o2), p(l2), p(ws_h), ws_h.numel(), stream)))
+        steps.append((t, calls))
+    keep = (ws_i, ws_c, ws_h, idx, cnt, o1, l1, o2, l2, tt)
+    return steps, keep
+
+
+def step_bytes(cfg, t):
+    """Algorithmic HBM bytes of one decode step (B queries at position t)."""
+    B, c, cI, m, mp, k, n_h, n_hI = cfg.B, cfg.c, cfg.cI, cfg.m, cfg.m_prime, cfg.k, cfg.n_h, cfg.n_hI
+    v_csa, v_hca = t // m, t // mp
+    idx_b = v_csa * cI * 2 + n_hI * cI * 2 + n_hI * 4
+    csa_b = min(k, v_csa) * c * 2 + n_h * c * 2 + n_h * c * 4 + n_h * 4
+    hca_b = v_hca * c * 2 + n_h * c * 2 + n_h * c * 4 + n_h * 4
+    comp = 0
+    if (t + 1) % m == 0:
+        comp += (4 * m * c * 2 + c * 2) + (4 * m * cI * 2 + cI * 2)
+    if (t + 1) % mp == 0:
+        comp += 2 * mp * c * 2 + c * 2
+    return B * (idx_b + csa_b + hca_b + comp), B * idx_b
+
+
+def run_steps(steps, s0, n, n_dec):
+    for j in range(s0, s0 + n):
+        for fn, args in steps[j % n_dec][1]:
+            rc = fn(*args)
+            if rc != 0:
+                from dense_long_context_amd import binding
+                raise RuntimeError(f"{fn.__name__} failed: {binding.last_error()}")
+
+
+def cpu_baseline(cfg, budget_s=15.0):
+    """The oracle, as it stands, on a bounded sample of the same decode step:
+    the indexer over 2^18 entries, top-k, CSA attention over the k selected
+    entries and HCA attention over 8192 entries, for one query at a time.
+    Inputs are drawn by synth with the workload's shapes and distributions."""
+    import numpy as np
+
+    import oracle as O
+    import synth
+
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count()
+    t = cfg.t
+    nv, nh_v = t // cfg.m, t // cfg.m_prime
+    KI = O.f64(synth.normal((nv, cfg.cI), 9001, dtype="bf16"))
+    Cc = O.f64(synth.normal((nv, cfg.c), 9002, dtype="bf16"))
+    Ch = O.f64(synth.normal((nh_v, cfg.c), 9003, dtype="bf16"))
+    done, t0 = 0, time.perf_counter()
+    while True:
+        qI = synth.normal((cfg.n_hI, cfg.cI), 9100 + done, dtype="bf16")
+        wI = synth.normal((cfg.n_hI,), 9200 + done, dtype="f32")
+        q = synth.normal((cfg.n_h, cfg.c), 9300 + done, dtype="bf16")
+        sc = O.index_scores(qI, wI, KI, t, cfg.m)
+        sel = O.topk_select(sc, cfg.k)
+        O.csa_attend(q, Cc, sel)
+        O.hca_attend(q, Ch, t, cfg.m_prime)
+        done += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or done >= 64:
+            break
+    return {"value": done / el, "unit": "decode query-tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{done} decode queries at t=2^20 (indexer over {nv} entries, top-{cfg.k}, CSA attention "
+                      f"over the selected entries, HCA attention over {nh_v} entries), fp64 numpy, "
+                      f"{el:.1f} s; the per-step compressor work (one entry every m tokens) is omitted"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=240)
+    ap.add_argument("--warmup", type=int, default=16)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--repeat", type=int, default=1, help="time the K steps this many times, report the best")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py runs on one GPU only: the CSA/HCA hot path here is single-device "
+              "(multi-GPU sharding is a design note, not part of this build).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import dense_long_context_amd as dlc
+    from dense_long_context_amd import binding
+    from synth import get_config
+
+    cfg = get_config("hybrid1m")
+    dev = torch.device("cuda:0")
+    n_dec = cfg.n_decode
+    log("building the 2^20-token caches (projection + compressors)")
+    wl = build_workload(cfg, dev, n_dec)
+    log(f"set-up: projection {wl['t_proj']:.2f} s, compressors {wl['t_comp']*1e3:.1f} ms per cache set")
+    steps, keep = make_steps(cfg, wl, dev, n_dec)
+    ev = HipEvents()
+
+    run_steps(steps, 0, args.warmup, n_dec)
+    torch.cuda.synchronize()
+    K = args.steps
+    best = None
+    for rep in range(args.repeat):
+        # live per-kernel timing of the dominant kernel (indexer scores) over the timed steps
+        evs = [(ev.create(), ev.create()) for _ in range(K)]
+        start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        start.record()
+        for j in range(K):
+            s = args.warmup + j
+            binding.dlc_timing_arm(binding.STAGE_INDEX_SCORES, evs[j][0], evs[j][1])
+            for fn, a in steps[s % n_dec][1]:
+                rc = fn(*a)
+                if rc != 0:
+                    raise RuntimeError(binding.last_error())
+        stop.record()
+        torch.cuda.synchronize()
+        ms = start.elapsed_time(stop)
+        k_ms = [ev.elapsed_ms(a, b) for a, b in evs]
+        for a, b in evs:
+            ev.destroy(a)
+            ev.destroy(b)
+        if best is None or ms < best[0]:
+            best = (ms, k_ms)
+    ms, k_ms = best
+    ts = [steps[(args.warmup + j) % n_dec][0] for j in range(K)]
+    total_bytes = sum(step_bytes(cfg, t)[0] for t in ts)
+    idx_bytes = sum(step_bytes(cfg, t)[1] for t in ts) / K
+    k_avg_ms = sum(k_ms) / len(k_ms)
+    achieved = idx_bytes / (k_avg_ms * 1e-3) / 1e9
+    ms_step = ms / K
+    value = cfg.B * K / (ms * 1e-3)
+    hbm_gbs = total_bytes / (ms * 1e-3) / 1e9
+
+    # copy-kernel reference for achievable bandwidth
+    a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    b = torch.empty_like(a)
+    for _ in range(3):
+        binding.dlc_copy(b, a)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(10):
+        binding.dlc_copy(b, a)
+    e1.record()
+    torch.cuda.synchronize()
+    copy_gbs = 2 * (1 << 30) * 10 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del a, b
+
+    traffic = None
+    if os.path.exists(COUNTERS_FILE):
+        with open(COUNTERS_FILE) as f:
+            cnt = json.load(f)
+        if cnt.get("source_hash") == source_hash():
+            traffic = cnt.get("hbm_bytes_per_launch")
+
+    result = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "decode query-tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "hybrid1m decode: one CSA + one HCA layer, B=4 sequences at 2^20 context "
+                               "(t = 2^20 .. 2^20+255), c=512 m=4 m'=128 k=1024 n_h=128 n_hI=64 cI=128, "
+                               "caches built from d=7168 hidden states",
+                   "global_batch": cfg.B, "seq_len": wl["n_ctx"], "parallelism": "single GPU"},
+        "roofline": {"kernel": SCORES_KERNEL, "bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic,
+                     "avg_launch_us": round(k_avg_ms * 1e3, 3),
+                     "algorithmic_bytes_per_launch": int(idx_bytes)},
+        "step_hbm_gbs": round(hbm_gbs, 1),
+        "step_frac_of_peak": round(hbm_gbs / PEAK_HBM_GBS, 4),
+        "copy_kernel_gbs": round(copy_gbs, 1),
+        "setup": {"projection_s": round(wl["t_proj"], 3), "compress_ms_per_cache_set": round(wl["t_comp"] * 1e3, 2),
+                  "compress_stream_gbs": round(wl["stream_bytes"] / wl["t_comp"] / 1e9, 1)},
+    }
+    if not args.no_cpu_baseline:
+        log("timing the oracle on a bounded sample")
+        result["cpu_baseline"] = cpu_baseline(cfg)
+    else:
+        result["cpu_baseline"] = None
+    del keep
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -43,7 +43,11 @@ SIGNATURES = {
     "hca_attend": (_i32, [_i32, _i64, _i64, _i64, _i64, _i64, _vp, _vp, _i64, _vp, _i64, _f32, _vp,
                           _vp, _vp, _sz, _vp]),
     "dlc_project": (_i32, [_i32, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _i32, _vp]),
+    "dlc_timing_arm": (_i32, [_i32, _vp, _vp]),
+    "dlc_copy": (_i32, [_vp, _vp, _sz, _vp]),
 }
+
+STAGE_INDEX_SCORES, STAGE_TOPK_SELECT, STAGE_CSA_ATTEND, STAGE_HCA_ATTEND, STAGE_COMPRESS = 1, 2, 3, 4, 5
 
 
 class DlcError(RuntimeError):
@@ -237,6 +241,19 @@ def dlc_project(A, Wt, out=None, out_dtype=None):
         _dt(A), M, N, K, _p(A), A.stride(0), _p(Wt), Wt.stride(0), _p(out), out.stride(0), _dt(out),
         _stream(A.device)))
     return out
+
+
+def dlc_timing_arm(stage, ev_begin, ev_end):
+    """Arm raw hipEvent_t handles (ints) around the next launch of ``stage``."""
+    _check("dlc_timing_arm", lib().dlc_timing_arm(stage, ev_begin, ev_end))
+
+
+def dlc_copy(dst, src):
+    """Copy kernel (bandwidth reference): dst[:] = src[:] for equal-size device tensors."""
+    nb = src.numel() * src.element_size()
+    _need(dst.numel() * dst.element_size() == nb, "size mismatch")
+    _check("dlc_copy", lib().dlc_copy(_p(dst), _p(src), nb, _stream(src.device)))
+    return dst
 
 
 def default_scale(c: int) -> float:

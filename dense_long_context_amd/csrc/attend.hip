@@ -431,6 +431,7 @@ int run_attend(const char* name, int dtype, AttArgs a, int64_t BQ, int64_t nkeys
   }
   DLC_REQUIRE(BQ <= 65535 && p.splits * p.head_groups < (int64_t(1) << 31), DLC_E_UNSUPPORTED,
               "%s: grid too large", name);
+  StageTimer timer(GATHER ? DLC_STAGE_CSA_ATTEND : DLC_STAGE_HCA_ATTEND, s);
   if (p.mfma) {
     dim3 grid{(unsigned)(p.splits * p.head_groups), (unsigned)BQ, 1u};
     if (a.c == 128) hipLaunchKernelGGL((attend_mfma_kernel<128, GATHER>), grid, dim3(512), 0, s, a);

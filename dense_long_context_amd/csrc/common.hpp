@@ -93,6 +93,17 @@ __device__ __forceinline__ uint32_t order_key(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// Records the caller's armed events around a stage's launches (see
+// dlc_timing_arm); a no-op unless armed.
+class StageTimer {
+ public:
+  StageTimer(int stage, hipStream_t s);
+  ~StageTimer();
+ private:
+  int stage_;
+  hipStream_t s_;
+};
+
 // fill kernel: clears workspace on the stream (no memset nodes, so the calls
 // stay safe to capture in a graph)
 __global__ void fill_u32_kernel(uint32_t* p, uint32_t v, int64_t n);

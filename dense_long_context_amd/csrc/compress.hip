@@ -134,6 +134,7 @@ int launch_pool(PoolArgs a, bool overlap, int64_t B, hipStream_t s) {
   const int64_t blocks = ceil_div(threads, 256);
   DLC_REQUIRE(blocks < (int64_t(1) << 31) && B <= 65535, DLC_E_UNSUPPORTED, "compress: grid too large");
   dim3 grid{(unsigned)blocks, (unsigned)B, 1u};
+  StageTimer timer(DLC_STAGE_COMPRESS, s);
   if (overlap)
     hipLaunchKernelGGL((pool_kernel<T, VEC, true>), grid, dim3(256), 0, s, a);
   else

@@ -406,7 +406,9 @@ int csa_index_topk(int dtype, int64_t B, int64_t n_q, int64_t n_hI, int64_t cI, 
   DLC_REQUIRE(B >= 1 && n_q >= 1 && n_hI >= 1 && cI >= 1 && m >= 1 && cap >= 0 && t_max >= 0, DLC_E_INVAL,
               "csa_index_topk: need B, n_q, n_hI, cI, m >= 1 and cap, t_max >= 0");
   DLC_REQUIRE(k >= 1 && k <= kMaxK, DLC_E_UNSUPPORTED, "csa_index_topk: k=%lld outside [1, %d]", (long long)k, kMaxK);
-  DLC_REQUIRE(n_hI * cI <= 8192, DLC_E_UNSUPPORTED, "csa_index_topk: n_hI*cI=%lld > 8192", (long long)(n_hI * cI));
+  const bool mfma_shape = dtype == DLC_BF16 && (cI == 32 || cI == 64 || cI == 128 || cI == 256) && n_hI <= 64;
+  DLC_REQUIRE(mfma_shape || n_hI * cI <= 8192, DLC_E_UNSUPPORTED,
+              "csa_index_topk: n_hI*cI=%lld > 8192 outside the MFMA shapes", (long long)(n_hI * cI));
   DLC_REQUIRE(t_max / m <= cap, DLC_E_SHAPE, "csa_index_topk: floor(t_max/m)=%lld exceeds cap=%lld",
               (long long)(t_max / m), (long long)cap);
   DLC_REQUIRE(cap < (int64_t(1) << 31), DLC_E_UNSUPPORTED, "csa_index_topk: cap must be < 2^31");
@@ -437,8 +439,8 @@ int csa_index_topk(int dtype, int64_t B, int64_t n_q, int64_t n_hI, int64_t cI, 
 
   const int64_t vis_max = t_max / m;
   if (vis_max > 0) {
-    const bool mfma = dtype == DLC_BF16 && (cI == 32 || cI == 64 || cI == 128 || cI == 256) && n_hI <= 64 &&
-                      aligned(qI, 16) && aligned(KI, 16);
+    const bool mfma = mfma_shape && aligned(qI, 16) && aligned(KI, 16);
+    DLC_REQUIRE(mfma || n_hI * cI <= 8192, DLC_E_UNSUPPORTED, "csa_index_topk: MFMA shape needs 16-byte alignment");
     // aim for about 1024 workgroups in flight over the whole batch
     const int64_t tiles = ceil_div(vis_max, 16) * BQ;
     int64_t tiles_per_wave = tiles / (1024 * 4);
@@ -446,6 +448,8 @@ int csa_index_topk(int dtype, int64_t B, int64_t n_q, int64_t n_hI, int64_t cI, 
     a.keys_per_wg = tiles_per_wave * 4 * 16;
     const int64_t nchunks = ceil_div(vis_max, a.keys_per_wg);
     dim3 grid{(unsigned)nchunks, (unsigned)BQ, 1u};
+    {
+    StageTimer timer(DLC_STAGE_INDEX_SCORES, s);
     if (mfma) {
       const int HT = int(ceil_div(n_hI, 16)), KT = int(cI / 32);
 #define DLC_SCORES(ht, kt) \
@@ -462,7 +466,13 @@ int csa_index_topk(int dtype, int64_t B, int64_t n_q, int64_t n_hI, int64_t cI, 
       else
         hipLaunchKernelGGL((scores_valu_kernel<float>), grid, dim3(256), smem, s, a);
     }
+    }
     if ((rc = check_launch("csa_index_topk/scores"))) return rc;
+  }
+  StageTimer timer(DLC_STAGE_TOPK_SELECT, s);
+  if (vis_max > 0) {
+    const int64_t nchunks = ceil_div(vis_max, a.keys_per_wg);
+    dim3 grid{(unsigned)nchunks, (unsigned)BQ, 1u};
     hipLaunchKernelGGL(filter_kernel, grid, dim3(256), 0, s, a);
     if ((rc = check_launch("csa_index_topk/filter"))) return rc;
   }

@@ -120,7 +120,8 @@ int hca_compress(int dtype, int64_t B, int64_t n, int64_t c, int64_t m_prime,
  *          untouched), or NULL
  *  ws      workspace of at least csa_index_topk_ws(B, n_q, cap, k) bytes,
  *          256-byte aligned; its contents on entry do not matter
- * Limits: 1 <= k <= 16384; n_hI*cI <= 16384.
+ * Limits: 1 <= k <= 8192; bf16 with c^I in {32, 64, 128, 256} and n_hI <= 64
+ * (the MFMA shapes), otherwise n_hI*cI <= 8192.
  */
 size_t csa_index_topk_ws(int64_t B, int64_t n_q, int64_t cap, int64_t k);
 int csa_index_topk(int dtype, int64_t B, int64_t n_q, int64_t n_hI, int64_t cI, int64_t m, int64_t k,
@@ -173,6 +174,33 @@ int hca_attend(int dtype, int64_t B, int64_t n_q, int64_t n_h, int64_t c, int64_
  */
 int dlc_project(int dtype, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
                 const void* Wt, int64_t ldw, void* out, int64_t ldo, int out_dtype, void* stream);
+
+/*
+ * Measurement support (not part of the method).
+ *
+ * dlc_timing_arm - the next launch of `stage` on the calling thread records
+ * the caller's HIP events `ev_begin` (before) and `ev_end` (after) on that
+ * launch's stream, then disarms.  The events are hipEvent_t handles owned by
+ * the caller; NULL events disarm the stage.  Stages:
+ *   DLC_STAGE_INDEX_SCORES  the indexer score kernel of csa_index_topk
+ *   DLC_STAGE_TOPK_SELECT   the threshold/filter and finish kernels of csa_index_topk
+ *   DLC_STAGE_CSA_ATTEND    csa_attend (attention and combine kernels)
+ *   DLC_STAGE_HCA_ATTEND    hca_attend (attention and combine kernels)
+ *   DLC_STAGE_COMPRESS      csa_compress / hca_compress
+ *
+ * dlc_copy - device-to-device copy kernel of `bytes` bytes (a multiple of
+ * 16, both pointers 16-byte aligned); the reference for achievable HBM
+ * bandwidth and for scaling hardware byte counters.
+ */
+enum {
+  DLC_STAGE_INDEX_SCORES = 1,
+  DLC_STAGE_TOPK_SELECT = 2,
+  DLC_STAGE_CSA_ATTEND = 3,
+  DLC_STAGE_HCA_ATTEND = 4,
+  DLC_STAGE_COMPRESS = 5
+};
+int dlc_timing_arm(int stage, void* ev_begin, void* ev_end);
+int dlc_copy(void* dst, const void* src, size_t bytes, void* stream);
 
 #ifdef __cplusplus
 }
