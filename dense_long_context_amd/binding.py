@@ -100,6 +100,12 @@ def _stream(dev) -> int:
     return torch.cuda.current_stream(dev).cuda_stream
 
 
+def _stride(x, dim, minimum):
+    """x.stride(dim), or ``minimum`` when that dimension has one element (torch
+    leaves the stride of a size-1 dimension arbitrary)."""
+    return x.stride(dim) if x.shape[dim] > 1 else minimum
+
+
 def _need(cond, msg):
     if not cond:
         raise ValueError(msg)
@@ -127,7 +133,7 @@ def csa_compress(Za, Zb, Ca, Cb, m, out, i_begin=0, i_end=None, Ba=None, Bb=None
     n = rows if n is None else n
     i_end = n // m if i_end is None else i_end
     _check("csa_compress", lib().csa_compress(
-        _dt(Za), B, n, c, m, _p(Za), _p(Zb), _p(Ca), _p(Cb), Za.stride(1), Za.stride(0),
+        _dt(Za), B, n, c, m, _p(Za), _p(Zb), _p(Ca), _p(Cb), _stride(Za, 1, c), _stride(Za, 0, rows * c),
         _p(Ba), _p(Bb), i_begin, i_end, _p(out), out.shape[1], _stream(Za.device)))
     return out
 
@@ -141,7 +147,7 @@ def hca_compress(Z, Cs, m_prime, out, i_begin=0, i_end=None, bias=None, n=None):
     n = rows if n is None else n
     i_end = n // m_prime if i_end is None else i_end
     _check("hca_compress", lib().hca_compress(
-        _dt(Z), B, n, c, m_prime, _p(Z), _p(Cs), Z.stride(1), Z.stride(0), _p(bias), i_begin, i_end,
+        _dt(Z), B, n, c, m_prime, _p(Z), _p(Cs), _stride(Z, 1, c), _stride(Z, 0, rows * c), _p(bias), i_begin, i_end,
         _p(out), out.shape[1], _stream(Z.device)))
     return out
 
@@ -238,7 +244,7 @@ def dlc_project(A, Wt, out=None, out_dtype=None):
         out = torch.empty((M, N), dtype=out_dtype or A.dtype, device=A.device)
     _need(out.stride(1) == 1 and tuple(out.shape) == (M, N), "out must be [M][N] with contiguous rows")
     _check("dlc_project", lib().dlc_project(
-        _dt(A), M, N, K, _p(A), A.stride(0), _p(Wt), Wt.stride(0), _p(out), out.stride(0), _dt(out),
+        _dt(A), M, N, K, _p(A), _stride(A, 0, K), _p(Wt), _stride(Wt, 0, K), _p(out), _stride(out, 0, N), _dt(out),
         _stream(A.device)))
     return out
 
