@@ -30,8 +30,17 @@ namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
-constexpr int kMinKeysPerSplit = 64;
-constexpr int kTargetWorkgroups = 256;
+// split policy: aim for kTargetWorkgroups workgroups, but give every split at
+// least kMinKeysPerSplit keys (the partial output of a split costs as much
+// traffic as 2*heads/keys of its key reads)
+#ifndef DLC_ATTEND_TARGET_WGS
+#define DLC_ATTEND_TARGET_WGS 256
+#endif
+#ifndef DLC_ATTEND_MIN_KEYS
+#define DLC_ATTEND_MIN_KEYS 64
+#endif
+constexpr int kMinKeysPerSplit = DLC_ATTEND_MIN_KEYS;
+constexpr int kTargetWorkgroups = DLC_ATTEND_TARGET_WGS;
 
 struct AttArgs {
   const void* q;        // [BQ][n_h][c]
@@ -348,28 +357,332 @@ __global__ void __launch_bounds__(512) attend_mfma_kernel(AttArgs a) {
     a.lse[slot0 + hbase + l32] = lrun > 0.f ? (mrun + log2f(lrun)) * kLn2 : -INFINITY;
 }
 
+// ------------------------------------------------------------------ MFMA path, c = 512
+//
+// The V4-Pro shape gets a kernel that keeps every 32-key tile in LDS exactly
+// once, row-major, and feeds both products from it:
+//  * tiles arrive by direct global->LDS loads (global_load_lds_dwordx4: one
+//    instruction moves one 1 KB key row), three stages deep with two tiles in
+//    flight; no registers hold staged data;
+//  * Q.K^T reads the A operand (key rows) with ds_read_b128;
+//  * P.V reads the B operand with ds_read_b64_tr_b16, the gfx950 transposing
+//    LDS read: in each 16-lane group, lane j receives element j%4 of the
+//    8-byte chunks addressed by lanes j/4, j/4+4, j/4+8, j/4+12.  Lane i of a
+//    group addresses key row base+i/4 at dims c0+4*(i%4), so lane j ends up
+//    with dim c0+j of keys base..base+3 - four consecutive keys of one dim,
+//    which is the packed-k layout the MFMA wants;
+//  * barriers are plain s_barrier after an LDS-only wait, so the tile loads in
+//    flight are never drained by a barrier; each tile is waited for with an
+//    explicit vmcnt that leaves the younger tile outstanding.
+// Wave w owns heads 32*(w/2) .. +31 and half w%2 of the 512 dims, as in the
+// generic kernel; the two halves' partial S^T are added through LDS.
+
+__device__ __align__(16) bf16_raw g_zero_row[512];  // masked keys load this row
+
+__device__ __forceinline__ void wait_vmcnt(int n) {
+  // s_waitcnt with only the vector-memory counter set
+  if (n == 4)
+    __builtin_amdgcn_s_waitcnt(0x0F74);
+  else
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+}
+
+constexpr int kMaxGatherKeys = 4096;  // keys per split whose rows sit in LDS
+
+// One direct global->LDS load of a 1 KB row: lane i moves the 16 bytes at
+// row + lane_off (lane_off = 16*i) to LDS byte address lds_addr + 16*i.  The
+// row address and the LDS address are wave-uniform (SGPRs).  Issued through
+// asm so the compiler does not fold it into its own wait bookkeeping (it would
+// drain every tile in flight before each LDS read); the kernel waits for it
+// explicitly with wait_vmcnt.  The instruction writes no VGPR.
+__device__ __forceinline__ void dma_row(const void* row, uint32_t lane_off, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(lane_off), "s"(row), "s"(lds_addr)
+               : "memory", "m0");
+}
+
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // LDS and scalar-memory counter only
+  __builtin_amdgcn_s_barrier();
+}
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+#define DLC_LDS(p) ((__attribute__((address_space(3))) void*)(p))
+
+template <bool GATHER>
+__global__ void __launch_bounds__(512) attend512_kernel(AttArgs a) {
+  constexpr int CD = 512, HALF = 256, KSH = 16, NTH = 8;
+  constexpr int KROW = CD + 8;          // padded key row in LDS (bf16): 1040 bytes
+  constexpr int NST = 3;                // tile stages, two tiles in flight
+  constexpr int RPW = 4;                // key rows each wave moves per tile
+  constexpr int HPG = 128;              // heads per workgroup: 4 slices of 32, each split over 2 waves
+  // one array per stage: distinct objects let the compiler see that reads of
+  // the current stage never alias the loads still landing in the others
+  __shared__ __attribute__((aligned(16))) bf16_raw sK0[32 * KROW];
+  __shared__ __attribute__((aligned(16))) bf16_raw sK1[32 * KROW];
+  __shared__ __attribute__((aligned(16))) bf16_raw sK2[32 * KROW];
+  // partial S^T of every wave: lane-major, 16 values + 4 pad per lane so that
+  // four 16-byte accesses per lane are free of bank conflicts
+  constexpr int XROW = 20;
+  __shared__ __attribute__((aligned(16))) float sX[8 * 64 * XROW];
+  __shared__ int32_t sRow[GATHER ? kMaxGatherKeys : 1];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: lets addresses live in SGPRs
+  const int l32 = lane & 31, g2 = lane >> 5, G = lane >> 4, i16 = lane & 15;
+  const int hp = wave >> 1, dh = wave & 1;  // head slice of 32, half of c
+  const int64_t bq = blockIdx.y;
+  // XCD-aware order: workgroups are dealt round-robin to the 8 XCDs, so the
+  // head groups of one key split get ids that are equal mod 8 and share that
+  // XCD's L2 for the split's key rows
+  const int64_t xcd = blockIdx.x & 7, rest = blockIdx.x >> 3;
+  const int64_t hg = rest % a.head_groups;
+  const int64_t split = (rest / a.head_groups) * 8 + xcd;
+  if (split >= a.splits) return;
+  const int64_t b = bq / a.n_q;
+  const int64_t nk = n_keys<GATHER>(a, bq);
+  const int64_t k0 = split * a.keys_per_split;
+  const int64_t k1 = min(nk, k0 + a.keys_per_split);
+  const int64_t hbase = hg * HPG + hp * 32;
+  const bool active = hbase < a.n_h;
+  const bf16_raw* kv = static_cast<const bf16_raw*>(a.kv) + b * a.cap * CD;
+  const int64_t ntile = k1 > k0 ? (k1 - k0 + 31) / 32 : 0;
+
+  if constexpr (GATHER) {
+    for (int64_t j = tid; j < k1 - k0; j += 512) sRow[j] = int32_t(key_row<true>(a, bq, k0 + j, k1));
+  }
+  // Q^T operand over this wave's half of c: lane holds head hbase + l32,
+  // dims dh*HALF + ks*16 + g2*8 .. +7
+  bf16x8 qf[KSH];
+  {
+    const int64_t h = hbase + l32;
+    const bf16_raw* qp =
+        static_cast<const bf16_raw*>(a.q) + (bq * a.n_h + (h < a.n_h ? h : 0)) * CD + dh * HALF + g2 * 8;
+#pragma unroll
+    for (int ks = 0; ks < KSH; ++ks) {
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (h < a.n_h) v = *reinterpret_cast<const uint4*>(qp + ks * 16);
+      qf[ks] = __builtin_bit_cast(bf16x8, v);
+    }
+    // consume the Q loads here, so no wait for them is left inside the tile
+    // loop (where it would also drain the tile loads in flight)
+#pragma unroll
+    for (int ks = 0; ks < KSH; ++ks) asm volatile("" ::"v"(qf[ks]));
+  }
+  f32x16 o[NTH];
+#pragma unroll
+  for (int nt = 0; nt < NTH; ++nt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) o[nt][r] = 0.f;
+  float mrun = -INFINITY, lrun = 0.f;
+  __syncthreads();  // sRow ready; the Q loads drain here, before any tile is in flight
+
+  // each wave moves rows RPW*wave .. +RPW-1 of a tile: one 1 KB DMA load per row
+  auto issue = [&](bf16_raw* dst, int st, int64_t tl) {
+#pragma unroll
+    for (int r = 0; r < RPW; ++r) {
+      const int row = RPW * wave + r;
+      const int64_t j = tl * 32 + row;  // key position within the split
+      int64_t gr;
+      if constexpr (GATHER) {
+        gr = (k0 + j < k1) ? sRow[j] : -1;
+      } else {
+        gr = (k0 + j < k1) ? k0 + j : -1;
+      }
+      gr = __builtin_amdgcn_readfirstlane(int(gr));
+      const bf16_raw* src = gr >= 0 ? kv + gr * CD : g_zero_row;
+      const uint32_t lds_addr = (uint32_t)(uintptr_t)DLC_LDS(dst) + uint32_t(row * KROW * 2);
+      dma_row(src, uint32_t(lane) * 16u, lds_addr);
+    }
+  };
+  // bit j: key j of tile tl is valid (masked keys were loaded as zero rows)
+  auto valid_mask = [&](int64_t tl) -> uint32_t {
+    const int64_t j = tl * 32 + l32;
+    bool v = k0 + j < k1;
+    if constexpr (GATHER) v = v && sRow[j] >= 0;
+    return uint32_t(__ballot(v) & 0xffffffffu);
+  };
+  if (ntile > 0) issue(sK0, 0, 0);
+  if (ntile > 1) issue(sK1, 1, 1);
+
+  auto tile_step = [&](const bf16_raw* tile, bf16_raw* next, int st, int64_t it) {
+    wait_vmcnt(it + 1 < ntile ? RPW : 0);  // tile it has landed (tile it+1 may still fly)
+    lds_barrier();                         // ... for every wave; stage (it+2)%3 and sX are free
+    if (it + 2 < ntile) issue(next, (st + 2) % NST, it + 2);
+    f32x16 sx;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sx[r] = 0.f;
+    if (active) {
+      // partial S^T = K . Q^T over this wave's half of c
+      const bf16_raw* krow = tile + l32 * KROW + dh * HALF + g2 * 8;
+      // fragments in batches of four: one LDS wait per four MFMAs
+#pragma unroll
+      for (int k4 = 0; k4 < KSH; k4 += 4) {
+        bf16x8 ka[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) ka[u] = *reinterpret_cast<const bf16x8*>(krow + (k4 + u) * 16);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) sx = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[u], qf[k4 + u], sx, 0, 0, 0);
+        asm volatile("" ::: "memory");
+      }
+      float4* xw = reinterpret_cast<float4*>(&sX[(wave * 64 + lane) * XROW]);
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4)
+        xw[q4] = make_float4(sx[4 * q4], sx[4 * q4 + 1], sx[4 * q4 + 2], sx[4 * q4 + 3]);
+    }
+    const uint32_t vmask = valid_mask(it);
+    lds_barrier();
+    if (!active) return;
+    // full S^T = both halves; lane holds head l32, keys kr(r) = 8*(r/4) + 4*g2 + r%4
+    // add the partner's half, eight values at a time (bounded register use)
+    {
+      const float4* xr = reinterpret_cast<const float4*>(&sX[((wave ^ 1) * 64 + lane) * XROW]);
+#pragma unroll
+      for (int hq = 0; hq < 2; ++hq) {
+        const float4 v0 = xr[2 * hq], v1 = xr[2 * hq + 1];
+        const float ov[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int r = 8 * hq + e;
+          sx[r] = dh == 0 ? sx[r] + ov[e] : ov[e] + sx[r];
+        }
+        asm volatile("" ::: "memory");
+      }
+    }
+    float tmax = -INFINITY;
+    const uint32_t vm = vmask >> (4 * g2);  // key 8*(r/4) + 4*g2 + r%4 -> bit 8*(r/4) + r%4
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      sx[r] = ((vm >> (8 * (r >> 2) + (r & 3))) & 1u) ? sx[r] * a.scale_log2 : -INFINITY;
+      tmax = fmaxf(tmax, sx[r]);
+    }
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+    // lazy running max (see the generic kernel)
+    const bool move = tmax > mrun + 8.f;
+    if (__any(move)) {
+      const float mnew = move ? tmax : mrun;
+      const float alpha = mrun == -INFINITY ? 0.f : exp2f(mrun - mnew);
+      lrun *= alpha;
+      mrun = mnew;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float al = __shfl(alpha, 8 * (r >> 2) + 4 * g2 + (r & 3));
+#pragma unroll
+        for (int nt = 0; nt < NTH; ++nt) o[nt][r] *= al;
+      }
+    }
+    float psum = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      sx[r] = sx[r] == -INFINITY ? 0.f : exp2f(sx[r] - mrun);
+      psum += sx[r];
+    }
+    psum += __shfl_xor(psum, 32);
+    lrun += psum;
+    bf16x8 pa[2];
+#pragma unroll
+    for (int uu = 0; uu < 2; ++uu)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) pa[uu][e] = (__bf16)sx[8 * uu + e];
+    // B operand (keys 16u + 8h + 4*g2 + 0..3 for slots 4h .. 4h+3, dim
+    // dh*HALF + nt*32 + l32) from two transposing reads
+    const bf16_raw* vb0 = tile + (4 * g2 + (i16 >> 2)) * KROW + dh * HALF + 16 * (G & 1) + 4 * (i16 & 3);
+    // fragments in batches of four (two output tiles x both key halves)
+#pragma unroll
+    for (int n2 = 0; n2 < NTH; n2 += 2) {
+      bf16x8 vf[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const bf16_raw* p0 = vb0 + (16 * (u & 1)) * KROW + (n2 + (u >> 1)) * 32;
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) s16x4*)DLC_LDS(p0));
+        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) s16x4*)DLC_LDS(p0 + 8 * KROW));
+        vf[u] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        o[n2 + (u >> 1)] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa[u & 1], vf[u], o[n2 + (u >> 1)], 0, 0, 0);
+      asm volatile("" ::: "memory");
+    }
+  };
+  for (int64_t it = 0; it < ntile; it += NST) {
+    tile_step(sK0, sK2, 0, it);
+    if (it + 1 < ntile) tile_step(sK1, sK0, 1, it + 1);
+    if (it + 2 < ntile) tile_step(sK2, sK1, 2, it + 2);
+  }
+
+  if (!active) return;
+  const int64_t slot0 = (bq * a.splits + split) * a.n_h;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int hr = 8 * (r >> 2) + 4 * g2 + (r & 3);
+    const float l = __shfl(lrun, hr);
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+    const int64_t h = hbase + hr;
+    if (h < a.n_h) {
+      float* op = a.o + (slot0 + h) * CD + dh * HALF + l32;
+#pragma unroll
+      for (int nt = 0; nt < NTH; ++nt) op[nt * 32] = o[nt][r] * inv;
+    }
+  }
+  if (dh == 0 && g2 == 0 && a.lse && hbase + l32 < a.n_h)
+    a.lse[slot0 + hbase + l32] = lrun > 0.f ? (mrun + log2f(lrun)) * kLn2 : -INFINITY;
+}
+
 // ------------------------------------------------------------------ combine
 
-__global__ void __launch_bounds__(256) combine_kernel(const float* op, const float* lp, int64_t splits,
+// One block per (query, head).  The split weights e^{lse_j - lse} are formed
+// once in LDS; each thread then owns 4 consecutive dims (c % 4 == 0) or one
+// dim and sums the splits with independent loads.
+constexpr int kMaxSplits = 256;
+
+__global__ void __launch_bounds__(128) combine_kernel(const float* op, const float* lp, int64_t splits,
                                                       int64_t n_h, int64_t c, float* out, float* lse) {
+  __shared__ float wsh[kMaxSplits];
+  __shared__ float red[2];
   const int64_t bh = blockIdx.x;  // bq * n_h + h
   const int64_t bq = bh / n_h, h = bh - bq * n_h;
-  float M = -INFINITY;
-  for (int64_t j = 0; j < splits; ++j) M = fmaxf(M, lp[(bq * splits + j) * n_h + h]);
-  float L = 0.f;
-  if (M != -INFINITY)
-    for (int64_t j = 0; j < splits; ++j) L += __expf(lp[(bq * splits + j) * n_h + h] - M);
-  const float invL = L > 0.f ? 1.f / L : 0.f;
-  for (int64_t d = threadIdx.x; d < c; d += blockDim.x) {
-    float acc = 0.f;
-    if (M != -INFINITY)
-      for (int64_t j = 0; j < splits; ++j) {
-        const float lj = lp[(bq * splits + j) * n_h + h];
-        if (lj != -INFINITY) acc = fmaf(__expf(lj - M), op[((bq * splits + j) * n_h + h) * c + d], acc);
-      }
-    out[bh * c + d] = acc * invL;
+  const int tid = threadIdx.x;
+  for (int j = tid; j < splits; j += blockDim.x) wsh[j] = lp[(bq * splits + j) * n_h + h];
+  __syncthreads();
+  if (tid < 64) {
+    float M = -INFINITY;
+    for (int j = tid; j < splits; j += 64) M = fmaxf(M, wsh[j]);
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+    float L = 0.f;
+    for (int j = tid; j < splits; j += 64) L += (M == -INFINITY) ? 0.f : __expf(wsh[j] - M);
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) L += __shfl_xor(L, off);
+    if (tid == 0) { red[0] = M; red[1] = L; }
   }
-  if (threadIdx.x == 0 && lse) lse[bh] = M == -INFINITY ? -INFINITY : M + __logf(L);
+  __syncthreads();
+  const float M = red[0], L = red[1];
+  for (int j = tid; j < splits; j += blockDim.x) wsh[j] = (M == -INFINITY) ? 0.f : __expf(wsh[j] - M) / L;
+  __syncthreads();
+  const float* base = op + (bq * splits * n_h + h) * c;
+  const int64_t sstride = n_h * c;
+  if ((c & 3) == 0) {
+    for (int64_t d = 4 * tid; d < c; d += 4 * blockDim.x) {
+      float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll 8
+      for (int64_t j = 0; j < splits; ++j) {
+        const float wj = wsh[j];
+        const float4 v = *reinterpret_cast<const float4*>(base + j * sstride + d);
+        acc.x = fmaf(wj, v.x, acc.x); acc.y = fmaf(wj, v.y, acc.y);
+        acc.z = fmaf(wj, v.z, acc.z); acc.w = fmaf(wj, v.w, acc.w);
+      }
+      *reinterpret_cast<float4*>(out + bh * c + d) = acc;
+    }
+  } else {
+    for (int64_t d = tid; d < c; d += blockDim.x) {
+      float acc = 0.f;
+#pragma unroll 8
+      for (int64_t j = 0; j < splits; ++j) acc = fmaf(wsh[j], base[j * sstride + d], acc);
+      out[bh * c + d] = acc;
+    }
+  }
+  if (tid == 0 && lse) lse[bh] = M == -INFINITY ? -INFINITY : M + __logf(L);
 }
 
 // ------------------------------------------------------------------ host
@@ -390,7 +703,9 @@ Plan plan(int dtype, int64_t BQ, int64_t n_h, int64_t c, int64_t nkeys) {
   int64_t s = ceil_div(kTargetWorkgroups, per_split);
   const int64_t smax = ceil_div(nkeys > 0 ? nkeys : 1, kMinKeysPerSplit);
   s = s < smax ? s : smax;
-  s = s < 1 ? 1 : s;
+  const int64_t smin = ceil_div(nkeys > 0 ? nkeys : 1, 4096);  // a split's rows fit in LDS
+  s = s < smin ? smin : s;
+  s = s < 1 ? 1 : (s > kMaxSplits ? kMaxSplits : s);
   p.splits = s;
   p.kps = ceil_div(nkeys > 0 ? nkeys : 1, s);
   if (p.mfma) p.kps = ceil_div(p.kps, 32) * 32;
@@ -436,7 +751,7 @@ int run_attend(const char* name, int dtype, AttArgs a, int64_t BQ, int64_t nkeys
     dim3 grid{(unsigned)(p.splits * p.head_groups), (unsigned)BQ, 1u};
     if (a.c == 128) hipLaunchKernelGGL((attend_mfma_kernel<128, GATHER>), grid, dim3(512), 0, s, a);
     if (a.c == 256) hipLaunchKernelGGL((attend_mfma_kernel<256, GATHER>), grid, dim3(512), 0, s, a);
-    if (a.c == 512) hipLaunchKernelGGL((attend_mfma_kernel<512, GATHER>), grid, dim3(512), 0, s, a);
+    if (a.c == 512) hipLaunchKernelGGL((attend512_kernel<GATHER>), grid, dim3(512), 0, s, a);
   } else {
     DLC_REQUIRE(a.n_h <= 65535, DLC_E_UNSUPPORTED, "%s: n_h > 65535 on the VALU path", name);
     dim3 grid{(unsigned)p.splits, (unsigned)a.n_h, (unsigned)BQ};
@@ -447,8 +762,8 @@ int run_attend(const char* name, int dtype, AttArgs a, int64_t BQ, int64_t nkeys
   }
   int rc = check_launch(name);
   if (rc || p.splits == 1) return rc;
-  hipLaunchKernelGGL(combine_kernel, dim3((unsigned)(BQ * a.n_h)), dim3(a.c < 256 ? unsigned(a.c) : 256u), 0, s,
-                     a.o, a.lse, p.splits, a.n_h, a.c, out, lse);
+  hipLaunchKernelGGL(combine_kernel, dim3((unsigned)(BQ * a.n_h)), dim3(128), 0, s, a.o, a.lse, p.splits, a.n_h,
+                     a.c, out, lse);
   return check_launch(name);
 }
 

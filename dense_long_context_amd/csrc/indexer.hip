@@ -36,13 +36,16 @@ struct IdxArgs {
   int64_t n_q, n_hI, cI, m, k, cap, t_max;
   float* scores;       // [BQ][score_ld]
   int64_t score_ld;
-  uint32_t* hist;      // [BQ][kBins]
-  uint32_t* cnt;       // [BQ][4]: selected, candidates
-  int32_t* sel;        // [BQ][k]
-  int32_t* cand;       // [BQ][cap]
+  uint32_t* hist;      // [BQ][kBins] first-digit histogram
+  uint32_t* ccnt;      // [BQ][max_chunks][2] per-chunk counts: selected, candidates
+  int32_t* sel;        // [BQ][cap] chunk c's selected entries start at c*keys_per_wg
+  int32_t* cand;       // [BQ][cap] chunk c's candidates start at c*keys_per_wg
+  int32_t* cand_idx;   // [BQ][cap] compacted candidates when they overflow LDS
+  uint32_t* cand_key;  // [BQ][cap] their score keys
   int32_t* idx;        // [BQ][k]
   int32_t* count;      // [BQ]
   int64_t keys_per_wg; // scores / filter chunk
+  int64_t max_chunks;
 };
 
 __device__ __forceinline__ int64_t visible(const IdxArgs& a, int64_t bq) {
@@ -195,63 +198,78 @@ __global__ void __launch_bounds__(256) scores_mfma_kernel(IdxArgs a) {
 
 // Finds the bin T with above(T) < need <= above(T) + h[T], where above(T)
 // counts the entries in bins > T.  Every thread of the block gets (T, above).
-// h is an LDS array of nbins (a multiple of blockDim.x); scratch holds
-// blockDim.x + 2 words.
+// h is an LDS array of nbins (a multiple of blockDim.x, blockDim.x a multiple
+// of 64 and at most 1024); scratch holds 16 + 2 words.  Each thread owns a
+// run of nbins/blockDim.x bins; a suffix scan of the per-thread totals (wave
+// shuffles, then the wave totals) locates the one thread whose run crosses
+// `need`, and that thread walks its own bins.
 __device__ void find_threshold(const uint32_t* h, int nbins, uint32_t need, uint32_t* scratch,
                                int* T_out, uint32_t* above_out) {
   const int per = nbins / blockDim.x;
   const int lo = threadIdx.x * per;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nwaves = blockDim.x >> 6;
   uint32_t mine = 0;
   for (int i = 0; i < per; ++i) mine += h[lo + i];
-  scratch[threadIdx.x] = mine;
-  if (threadIdx.x == 0) {  // defaults if no bin qualifies (inconsistent counts)
-    scratch[blockDim.x] = 0;
-    scratch[blockDim.x + 1] = 0;
+  // inclusive suffix sum within the wave (lanes above this one)
+  uint32_t suf = mine;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const uint32_t v = __shfl_down(suf, off);
+    if (lane + off < 64) suf += v;
+  }
+  if (lane == 0) scratch[wave] = suf;  // the wave's total
+  if (threadIdx.x == 0) {              // defaults if no bin qualifies (inconsistent counts)
+    scratch[16] = 0;
+    scratch[17] = 0;
   }
   __syncthreads();
-  if (threadIdx.x == 0) {
-    // suffix scan from the top thread down; blockDim.x <= 1024 so this is short
-    uint32_t run = 0;
-    for (int i = blockDim.x - 1; i >= 0; --i) {
-      const uint32_t v = scratch[i];
-      scratch[i] = run;  // entries in bins owned by higher threads
+  uint32_t higher = 0;
+  for (int w = wave + 1; w < nwaves; ++w) higher += scratch[w];
+  uint32_t run = higher + suf - mine;  // entries in bins owned by higher threads
+  if (run < need && run + mine >= need) {
+    for (int i = per - 1; i >= 0; --i) {
+      const uint32_t v = h[lo + i];
+      if (run < need && run + v >= need) {
+        scratch[16] = uint32_t(lo + i);
+        scratch[17] = run;
+      }
       run += v;
     }
   }
   __syncthreads();
-  uint32_t run = scratch[threadIdx.x];
+  *T_out = int(scratch[16]);
+  *above_out = scratch[17];
   __syncthreads();
-  for (int i = per - 1; i >= 0; --i) {
-    const uint32_t v = h[lo + i];
-    if (run < need && run + v >= need) {
-      scratch[blockDim.x] = uint32_t(lo + i);
-      scratch[blockDim.x + 1] = run;
-    }
-    run += v;
+}
+
+// Ordered compaction helper: returns this thread's position among the threads
+// of the block with pred set (in thread order) and, through *total, their
+// count.  wtot holds blockDim.x/64 words.  Ends with the block synchronised.
+__device__ __forceinline__ uint32_t block_rank(bool pred, uint32_t* wtot, uint32_t* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nwaves = blockDim.x >> 6;
+  const uint64_t mask = __ballot(pred);
+  if (lane == 0) wtot[wave] = uint32_t(__popcll(mask));
+  __syncthreads();
+  uint32_t before = 0, all = 0;
+  for (int w = 0; w < nwaves; ++w) {
+    const uint32_t x = wtot[w];
+    before += w < wave ? x : 0u;
+    all += x;
   }
   __syncthreads();
-  *T_out = int(scratch[blockDim.x]);
-  *above_out = scratch[blockDim.x + 1];
-  __syncthreads();
+  *total = all;
+  return before + uint32_t(__popcll(mask & ((uint64_t(1) << lane) - 1)));
 }
 
-// wave-aggregated append of `pred` entries to list[cnt] (slots past `limit` are dropped)
-__device__ __forceinline__ void wave_append(bool pred, int32_t value, uint32_t* counter, int32_t* list,
-                                            uint32_t limit) {
-  const uint64_t mask = __ballot(pred);
-  if (mask == 0) return;
-  const int lane = threadIdx.x & 63;
-  const int leader = __ffsll((unsigned long long)mask) - 1;
-  uint32_t base = 0;
-  if (lane == leader) base = atomicAdd(counter, uint32_t(__popcll(mask)));
-  base = __shfl(base, leader);
-  const uint32_t pos = base + uint32_t(__popcll(mask & ((uint64_t(1) << lane) - 1)));
-  if (pred && pos < limit) list[pos] = value;
-}
-
+// Every workgroup recomputes the threshold bin T of its query from the
+// first-digit histogram, then splits its own chunk of keys into "above T"
+// (selected for sure) and "in T" (candidates).  Both lists go to the chunk's
+// own segment, in ascending key order, and the two counts to the chunk's own
+// slot: no global atomics, and the result does not depend on scheduling.
 __global__ void __launch_bounds__(256) filter_kernel(IdxArgs a) {
   __shared__ uint32_t h[kBins];
-  __shared__ uint32_t scratch[256 + 2];
+  __shared__ uint32_t scratch[18];
+  __shared__ uint32_t wtot[4];
   const int64_t bq = blockIdx.y;
   const int64_t nvis = visible(a, bq);
   const int64_t keff = min(a.k, nvis);
@@ -265,35 +283,100 @@ __global__ void __launch_bounds__(256) filter_kernel(IdxArgs a) {
   find_threshold(h, kBins, uint32_t(keff), scratch, &T, &above);
 
   const float* sc = a.scores + bq * a.score_ld;
-  // whole waves iterate together so the ballots see every lane
+  int32_t* sel = a.sel + bq * a.cap + s0;
+  int32_t* cand = a.cand + bq * a.cap + s0;
+  uint32_t nsel = 0, ncand = 0;
   for (int64_t base = s0; base < s1; base += blockDim.x) {
     const int64_t s = base + threadIdx.x;
     int d = -1;
     if (s < s1) d = int(order_key(sc[s]) >> kShift1);
-    wave_append(d > T, int32_t(s), a.cnt + bq * 4 + 0, a.sel + bq * a.k, uint32_t(a.k));
-    wave_append(d == T, int32_t(s), a.cnt + bq * 4 + 1, a.cand + bq * a.cap, uint32_t(a.cap));
+    uint32_t t1, t2;
+    const uint32_t r1 = block_rank(d > T, wtot, &t1);
+    if (d > T) sel[nsel + r1] = int32_t(s);
+    const uint32_t r2 = block_rank(d == T, wtot, &t2);
+    if (d == T) cand[ncand + r2] = int32_t(s);
+    nsel += t1;
+    ncand += t2;
+  }
+  if (threadIdx.x == 0) {
+    a.ccnt[(bq * a.max_chunks + blockIdx.x) * 2 + 0] = nsel;
+    a.ccnt[(bq * a.max_chunks + blockIdx.x) * 2 + 1] = ncand;
   }
 }
 
 // ---------------------------------------------------------------- finish
 
+constexpr int kMaxChunks = 4096;
+constexpr int kLdsCand = 4096;
+
 // radix passes over the candidates' composite key: the low 21 bits of the score
 // key (the top 11 bits are T for all of them), then the bit-inverted index
 constexpr int kPasses = 5;
-__constant__ int kPassShift[kPasses] = {42, 32, 21, 10, 0};
-__constant__ int kPassBits[kPasses] = {11, 10, 11, 11, 10};
+__device__ __forceinline__ int pass_shift(int p) { return p == 0 ? 42 : p == 1 ? 32 : p == 2 ? 21 : p == 3 ? 10 : 0; }
+__device__ __forceinline__ int pass_bits(int p) { return (p == 1 || p == 4) ? 10 : 11; }
 
-__device__ __forceinline__ uint64_t cand_key(const float* sc, int32_t s) {
-  const uint64_t key = order_key(sc[s]) & 0x1fffffu;
-  return (key << 32) | uint64_t(0xffffffffu - uint32_t(s));
+__device__ __forceinline__ uint64_t cand_key(uint32_t key, int32_t s) {
+  return (uint64_t(key & 0x1fffffu) << 32) | uint64_t(0xffffffffu - uint32_t(s));
 }
 
+// block-wide exclusive scan of v[0 .. n) in place (n <= 4 * blockDim.x); returns the total
+__device__ uint32_t block_exclusive_scan(uint32_t* v, int n, uint32_t* wsum) {
+  const int per = 4;
+  const int lo = threadIdx.x * per;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nwaves = blockDim.x >> 6;
+  uint32_t loc[per];
+  uint32_t mine = 0;
+#pragma unroll
+  for (int i = 0; i < per; ++i) {
+    loc[i] = (lo + i < n) ? v[lo + i] : 0u;
+    mine += loc[i];
+  }
+  uint32_t inc = mine;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const uint32_t t = __shfl_up(inc, off);
+    if (lane >= off) inc += t;
+  }
+  if (lane == 63) wsum[wave] = inc;
+  __syncthreads();
+  uint32_t before = 0, total = 0;
+  for (int w = 0; w < nwaves; ++w) {
+    const uint32_t x = wsum[w];
+    if (w < wave) before += x;
+    total += x;
+  }
+  uint32_t run = before + inc - mine;
+#pragma unroll
+  for (int i = 0; i < per; ++i) {
+    if (lo + i < n) v[lo + i] = run;
+    run += loc[i];
+  }
+  __syncthreads();
+  return total;
+}
+
+// number of entries of the ascending list l[0 .. n) that are < x
+__device__ __forceinline__ uint32_t lower_bound(const int32_t* l, uint32_t n, int32_t x) {
+  uint32_t lo = 0, hi = n;
+  while (lo < hi) {
+    const uint32_t mid = (lo + hi) >> 1;
+    if (l[mid] < x) lo = mid + 1; else hi = mid;
+  }
+  return lo;
+}
+
+// One workgroup per query.  The "above T" lists of all chunks, in chunk order,
+// form one ascending list; radix passes over the candidates find the exact
+// k_eff-th composite key; the candidates at or above it are compacted in
+// order into a second ascending list; the two lists are merged by rank.
 __global__ void __launch_bounds__(1024) finish_kernel(IdxArgs a) {
-  extern __shared__ uint32_t fsm[];
-  uint32_t* h = fsm;                                    // kBins
-  uint32_t* scratch = h + kBins;                         // 1024 + 2
-  uint32_t* nsel_lds = scratch + 1024 + 2;               // 1
-  int32_t* buf = reinterpret_cast<int32_t*>(nsel_lds + 2);  // pow2 >= keff
+  __shared__ uint32_t h[kBins];
+  __shared__ uint32_t scratch[18];
+  __shared__ uint32_t wsum[16];
+  __shared__ uint32_t off_sel[kMaxChunks], off_cand[kMaxChunks];
+  __shared__ int32_t lsel[kMaxK], lc2[kMaxK];
+  __shared__ int32_t lc_idx[kLdsCand];
+  __shared__ uint32_t lc_key[kLdsCand];
   const int64_t bq = blockIdx.x;
   const int64_t nvis = visible(a, bq);
   const int64_t keff = min(a.k, nvis);
@@ -303,27 +386,54 @@ __global__ void __launch_bounds__(1024) finish_kernel(IdxArgs a) {
     for (int64_t j = threadIdx.x; j < a.k; j += blockDim.x) out[j] = j < nvis ? int32_t(j) : -1;
     return;
   }
-  const uint32_t n_sel = min(a.cnt[bq * 4 + 0], uint32_t(keff));
-  const uint32_t n_cand = min(a.cnt[bq * 4 + 1], uint32_t(a.cap));
-  const int32_t* sel = a.sel + bq * a.k;
-  const int32_t* cand = a.cand + bq * a.cap;
+  const int nch = int(ceil_div(nvis, a.keys_per_wg));
+  const uint32_t* cc = a.ccnt + bq * a.max_chunks * 2;
+  for (int c = threadIdx.x; c < nch; c += blockDim.x) {
+    off_sel[c] = cc[2 * c];
+    off_cand[c] = cc[2 * c + 1];
+  }
+  __syncthreads();
+  const uint32_t n_sel = min(block_exclusive_scan(off_sel, nch, wsum), uint32_t(keff));
+  const uint32_t n_cand = min(block_exclusive_scan(off_cand, nch, wsum), uint32_t(nvis));
   const float* sc = a.scores + bq * a.score_ld;
-  int P = 1;
-  while (P < keff) P <<= 1;
-  for (int j = threadIdx.x; j < P; j += blockDim.x) buf[j] = j < int(n_sel) ? sel[j] : 0x7fffffff;
-  if (threadIdx.x == 0) *nsel_lds = n_sel;
+  const bool in_lds = n_cand <= uint32_t(kLdsCand);
+  int32_t* cidx = in_lds ? lc_idx : a.cand_idx + bq * a.cap;
+  uint32_t* ckey = in_lds ? lc_key : a.cand_key + bq * a.cap;
+  // gather the chunks' lists: every thread takes independent entries and finds
+  // its chunk by binary search over the exclusive offsets
+  auto chunk_of = [&](const uint32_t* off, uint32_t i) {
+    int lo = 0, hi = nch - 1;  // largest c with off[c] <= i
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (off[mid] <= i) lo = mid; else hi = mid - 1;
+    }
+    return lo;
+  };
+  for (uint32_t i = threadIdx.x; i < n_sel; i += blockDim.x) {
+    const int c = chunk_of(off_sel, i);
+    lsel[i] = a.sel[bq * a.cap + int64_t(c) * a.keys_per_wg + (i - off_sel[c])];
+  }
+  for (uint32_t i = threadIdx.x; i < n_cand; i += blockDim.x) {
+    const int c = chunk_of(off_cand, i);
+    const int32_t sidx = a.cand[bq * a.cap + int64_t(c) * a.keys_per_wg + (i - off_cand[c])];
+    cidx[i] = sidx;
+    ckey[i] = order_key(sc[sidx]);
+  }
+  __threadfence_block();
   __syncthreads();
 
+  // the exact threshold: after the passes, the selected candidates are those
+  // whose composite key is >= thr
   uint32_t need = uint32_t(keff) - n_sel;
   uint64_t pval = 0, pmask = 0;
-  for (int pass = 0; pass < kPasses && need > 0; ++pass) {
-    const int shift = kPassShift[pass], bits = kPassBits[pass];
+  for (int pass = 0; pass < kPasses; ++pass) {
+    const int shift = pass_shift(pass), bits = pass_bits(pass);
     const uint32_t dmask = (1u << bits) - 1u;
     const int nb = 1 << bits;
     for (int i = threadIdx.x; i < kBins; i += blockDim.x) h[i] = 0;
     __syncthreads();
     for (uint32_t i = threadIdx.x; i < n_cand; i += blockDim.x) {
-      const uint64_t ck = cand_key(sc, cand[i]);
+      const uint64_t ck = cand_key(ckey[i], cidx[i]);
       if ((ck & pmask) == pval) atomicAdd(&h[(ck >> shift) & dmask], 1u);
     }
     __syncthreads();
@@ -331,56 +441,64 @@ __global__ void __launch_bounds__(1024) finish_kernel(IdxArgs a) {
     uint32_t above;
     find_threshold(h, nb < 1024 ? 1024 : nb, need, scratch, &D, &above);
     const bool take_all = (above + h[D] == need);
-    // select every candidate with a larger digit (and, if the bin D is exactly what
-    // is still needed, the whole bin D as well)
-    for (uint32_t i = threadIdx.x; i < n_cand; i += blockDim.x) {
-      const int32_t s = cand[i];
-      const uint64_t ck = cand_key(sc, s);
-      if ((ck & pmask) == pval) {
-        const uint32_t dg = uint32_t(ck >> shift) & dmask;
-        if (dg > uint32_t(D) || (take_all && dg == uint32_t(D))) {
-          const uint32_t pos = atomicAdd(nsel_lds, 1u);
-          if (pos < uint32_t(P)) buf[pos] = s;
-        }
-      }
-    }
-    __syncthreads();
-    need = take_all ? 0 : need - above;
     pval |= uint64_t(D) << shift;
     pmask |= uint64_t(dmask) << shift;
+    if (take_all) break;
+    need -= above;
   }
-  __syncthreads();
+  const uint64_t thr = pval;
 
-  // bitonic sort of buf[0 .. P) ascending (padding INT_MAX sinks to the end)
-  for (int size = 2; size <= P; size <<= 1) {
-    for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      for (int i = threadIdx.x; i < P / 2; i += blockDim.x) {
-        const int lo = 2 * stride * (i / stride) + (i % stride);
-        const int hi = lo + stride;
-        const bool asc = (lo & size) == 0;
-        const int32_t x = buf[lo], y = buf[hi];
-        if ((x > y) == asc) { buf[lo] = y; buf[hi] = x; }
-      }
-      __syncthreads();
-    }
+  // ordered compaction of the selected candidates
+  uint32_t n2 = 0;
+  for (uint32_t base = 0; base < n_cand; base += blockDim.x) {
+    const uint32_t i = base + threadIdx.x;
+    const bool take = i < n_cand && cand_key(ckey[i], cidx[i]) >= thr;
+    uint32_t tot;
+    const uint32_t r = block_rank(take, wsum, &tot);
+    if (take && n2 + r < uint32_t(kMaxK)) lc2[n2 + r] = cidx[i];
+    n2 += tot;
   }
-  for (int64_t j = threadIdx.x; j < a.k; j += blockDim.x) out[j] = j < keff ? buf[j] : -1;
+  n2 = min(n2, uint32_t(keff) - n_sel);
+  // merge two ascending lists by rank
+  for (uint32_t i = threadIdx.x; i < n_sel; i += blockDim.x) {
+    const int32_t x = lsel[i];
+    out[i + lower_bound(lc2, n2, x)] = x;
+  }
+  for (uint32_t j = threadIdx.x; j < n2; j += blockDim.x) {
+    const int32_t y = lc2[j];
+    out[j + lower_bound(lsel, n_sel, y)] = y;
+  }
+  for (int64_t j = n_sel + n2 + threadIdx.x; j < a.k; j += blockDim.x) out[j] = -1;
 }
 
 // ---------------------------------------------------------------- host
 
 struct WsLayout {
-  size_t scores, hist, cnt, sel, cand, total;
+  size_t scores, hist, ccnt, sel, cand, cand_idx, cand_key, total;
 };
+
+// keys per scores/filter workgroup: about 1024 workgroups over the batch, at
+// most kMaxChunks chunks per query
+int64_t keys_per_wg(int64_t BQ, int64_t vis_max) {
+  const int64_t tiles = ceil_div(vis_max, 16) * BQ;
+  int64_t tpw = tiles / (1024 * 4);
+  tpw = tpw < 1 ? 1 : (tpw > 16 ? 16 : tpw);
+  int64_t kpw = tpw * 64;
+  const int64_t floor_kpw = ceil_div(ceil_div(vis_max > 0 ? vis_max : 1, kMaxChunks), 64) * 64;
+  return kpw > floor_kpw ? kpw : floor_kpw;
+}
 
 WsLayout ws_layout(int64_t B, int64_t n_q, int64_t cap, int64_t k, bool own_scores) {
   const size_t BQ = size_t(B) * size_t(n_q);
+  (void)k;
   WsLayout L{};
   size_t off = 0;
-  L.hist = off;  off = align_up(off + BQ * kBins * 4, 256);
-  L.cnt = off;   off = align_up(off + BQ * 4 * 4, 256);
-  L.sel = off;   off = align_up(off + BQ * size_t(k) * 4, 256);
-  L.cand = off;  off = align_up(off + BQ * size_t(cap) * 4, 256);
+  L.hist = off;      off = align_up(off + BQ * kBins * 4, 256);
+  L.ccnt = off;      off = align_up(off + BQ * kMaxChunks * 2 * 4, 256);
+  L.sel = off;       off = align_up(off + BQ * size_t(cap) * 4, 256);
+  L.cand = off;      off = align_up(off + BQ * size_t(cap) * 4, 256);
+  L.cand_idx = off;  off = align_up(off + BQ * size_t(cap) * 4, 256);
+  L.cand_key = off;  off = align_up(off + BQ * size_t(cap) * 4, 256);
   L.scores = off;
   if (own_scores) off = align_up(off + BQ * size_t(cap) * 4, 256);
   L.total = off;
@@ -427,25 +545,23 @@ int csa_index_topk(int dtype, int64_t B, int64_t n_q, int64_t n_hI, int64_t cI, 
   a.scores = scores ? scores : reinterpret_cast<float*>(w + L.scores);
   a.score_ld = cap;
   a.hist = reinterpret_cast<uint32_t*>(w + L.hist);
-  a.cnt = reinterpret_cast<uint32_t*>(w + L.cnt);
+  a.ccnt = reinterpret_cast<uint32_t*>(w + L.ccnt);
   a.sel = reinterpret_cast<int32_t*>(w + L.sel);
   a.cand = reinterpret_cast<int32_t*>(w + L.cand);
+  a.cand_idx = reinterpret_cast<int32_t*>(w + L.cand_idx);
+  a.cand_key = reinterpret_cast<uint32_t*>(w + L.cand_key);
+  a.max_chunks = kMaxChunks;
   a.idx = idx; a.count = count;
   const int64_t BQ = B * n_q;
 
-  // hist and cnt are adjacent: one clear covers both
-  int rc = fill_u32(a.hist, 0, int64_t((L.sel - L.hist) / 4), s);
+  int rc = fill_u32(a.hist, 0, int64_t(BQ * kBins), s);
   if (rc) return rc;
 
   const int64_t vis_max = t_max / m;
   if (vis_max > 0) {
     const bool mfma = mfma_shape && aligned(qI, 16) && aligned(KI, 16);
     DLC_REQUIRE(mfma || n_hI * cI <= 8192, DLC_E_UNSUPPORTED, "csa_index_topk: MFMA shape needs 16-byte alignment");
-    // aim for about 1024 workgroups in flight over the whole batch
-    const int64_t tiles = ceil_div(vis_max, 16) * BQ;
-    int64_t tiles_per_wave = tiles / (1024 * 4);
-    tiles_per_wave = tiles_per_wave < 1 ? 1 : (tiles_per_wave > 16 ? 16 : tiles_per_wave);
-    a.keys_per_wg = tiles_per_wave * 4 * 16;
+    a.keys_per_wg = keys_per_wg(BQ, vis_max);
     const int64_t nchunks = ceil_div(vis_max, a.keys_per_wg);
     dim3 grid{(unsigned)nchunks, (unsigned)BQ, 1u};
     {
@@ -476,10 +592,8 @@ int csa_index_topk(int dtype, int64_t B, int64_t n_q, int64_t n_hI, int64_t cI, 
     hipLaunchKernelGGL(filter_kernel, grid, dim3(256), 0, s, a);
     if ((rc = check_launch("csa_index_topk/filter"))) return rc;
   }
-  int P = 1;
-  while (P < k) P <<= 1;
-  const size_t fsmem = (kBins + 1024 + 4) * 4 + size_t(P) * 4;
-  hipLaunchKernelGGL(finish_kernel, dim3((unsigned)BQ), dim3(1024), fsmem, s, a);
+  if (vis_max == 0) a.keys_per_wg = 64;
+  hipLaunchKernelGGL(finish_kernel, dim3((unsigned)BQ), dim3(1024), 0, s, a);
   return check_launch("csa_index_topk/finish");
 }
 
