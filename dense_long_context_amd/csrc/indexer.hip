@@ -110,8 +110,13 @@ __global__ void __launch_bounds__(256) scores_valu_kernel(IdxArgs a) {
 // head/key l%16 of the A/B operands and dims 8*(l/16) .. +7 of each 32-dim
 // step; the result holds key l%16 and heads 4*(l/16) .. +3.  The head sum is
 // finished with two cross-lane adds.  Queries stay in registers for the whole
-// pass; keys stream from HBM, the next tile's loads in flight while the
-// current tile is multiplied.
+// pass; keys stream from HBM with PF tiles per wave in flight (each wave's
+// loads for tile t+PF go out right after tile t's products).
+
+#ifndef DLC_INDEXER_PREFETCH
+#define DLC_INDEXER_PREFETCH 2
+#endif
+constexpr int PF = DLC_INDEXER_PREFETCH;  // key tiles in flight per wave
 
 template <int HT, int KT>
 __global__ void __launch_bounds__(256) scores_mfma_kernel(IdxArgs a) {
@@ -153,8 +158,8 @@ __global__ void __launch_bounds__(256) scores_mfma_kernel(IdxArgs a) {
   const int64_t b = bq / a.n_q;
   const bf16_raw* K = static_cast<const bf16_raw*>(a.KI) + b * a.cap * cI;
   const int64_t ntiles = (s1 - s0 + 15) / 16;
-  int64_t tile = wave;
-  uint4 cur[KT], nxt[KT];
+  // wave w takes tiles w, w+4, w+8, ...; a ring of PF tiles is in flight
+  uint4 ring[PF][KT];
   auto load_tile = [&](int64_t tl, uint4* dst) {
     int64_t row = s0 + tl * 16 + r16;
     row = row < s1 ? row : s1 - 1;  // rows past the end repeat the last visible row
@@ -162,34 +167,40 @@ __global__ void __launch_bounds__(256) scores_mfma_kernel(IdxArgs a) {
 #pragma unroll
     for (int kt = 0; kt < KT; ++kt) dst[kt] = *reinterpret_cast<const uint4*>(p + kt * 32);
   };
-  if (tile < ntiles) load_tile(tile, cur);
-  for (; tile < ntiles; tile += 4) {
-    if (tile + 4 < ntiles) load_tile(tile + 4, nxt);
-    f32x4 acc[HT];
 #pragma unroll
-    for (int ht = 0; ht < HT; ++ht) acc[ht] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int p = 0; p < PF; ++p)
+    if (wave + 4 * p < ntiles) load_tile(wave + 4 * p, ring[p]);
+  for (int64_t base = wave; base < ntiles; base += 4 * PF) {
 #pragma unroll
-    for (int kt = 0; kt < KT; ++kt) {
-      const bf16x8 kb = __builtin_bit_cast(bf16x8, cur[kt]);
+    for (int p = 0; p < PF; ++p) {
+      const int64_t tile = base + 4 * p;
+      if (tile < ntiles) {
+        f32x4 acc[HT];
 #pragma unroll
-      for (int ht = 0; ht < HT; ++ht)
-        acc[ht] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qf[ht][kt], kb, acc[ht], 0, 0, 0);
+        for (int ht = 0; ht < HT; ++ht) acc[ht] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kt = 0; kt < KT; ++kt) {
+          const bf16x8 kb = __builtin_bit_cast(bf16x8, ring[p][kt]);
+#pragma unroll
+          for (int ht = 0; ht < HT; ++ht)
+            acc[ht] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qf[ht][kt], kb, acc[ht], 0, 0, 0);
+        }
+        if (tile + 4 * PF < ntiles) load_tile(tile + 4 * PF, ring[p]);
+        float part = 0.f;
+#pragma unroll
+        for (int ht = 0; ht < HT; ++ht)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) part = fmaf(wv[ht][r], fmaxf(acc[ht][r], 0.f), part);
+        part += __shfl_xor(part, 16);
+        part += __shfl_xor(part, 32);
+        const int64_t s = s0 + tile * 16 + r16;
+        if (g == 0 && s < s1) {
+          const float score = canon_zero(part);
+          a.scores[bq * a.score_ld + s] = score;
+          atomicAdd(&hist[order_key(score) >> kShift1], 1u);
+        }
+      }
     }
-    float part = 0.f;
-#pragma unroll
-    for (int ht = 0; ht < HT; ++ht)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) part = fmaf(wv[ht][r], fmaxf(acc[ht][r], 0.f), part);
-    part += __shfl_xor(part, 16);
-    part += __shfl_xor(part, 32);
-    const int64_t s = s0 + tile * 16 + r16;
-    if (g == 0 && s < s1) {
-      const float score = canon_zero(part);
-      a.scores[bq * a.score_ld + s] = score;
-      atomicAdd(&hist[order_key(score) >> kShift1], 1u);
-    }
-#pragma unroll
-    for (int kt = 0; kt < KT; ++kt) cur[kt] = nxt[kt];
   }
   flush_hist(hist, a.hist + bq * kBins);
 }
