@@ -74,35 +74,61 @@ class HipEvents:
         self.hip.hipEventDestroy(e)
 
 
-def build_workload(cfg, dev, n_dec):
+STREAMS = ["aKV", "bKV", "aZ", "bZ", "IaKV", "IbKV", "IaZ", "IbZ", "KV", "Z"]
+
+
+def stream_layout(cfg):
+    """Column offset and width of each projected stream in the side-by-side buffer."""
+    width = {nm: (cfg.cI if nm.startswith("I") else cfg.c) for nm in STREAMS}
+    off, o = {}, 0
+    for nm in STREAMS:
+        off[nm] = o
+        o += width[nm]
+    return off, width, o
+
+
+def stream_weight(cfg, nm):
+    """W for stream ``nm``: [d][width] bf16 on the host, N(0, 1/d)."""
+    _, width, _ = stream_layout(cfg)
+    import synth
+    return synth.normal((cfg.d, width[nm]), synth.tensor_seed(cfg.seed, nm), cfg.weight_std, "bf16")
+
+
+def query_weight(cfg, nm):
+    """Query-side weights on the host: W^DQ [d][d_c], W^w [d][n_hI] (std 1/sqrt(d)), and
+    W^IUQ [d_c][n_hI*cI], W^UQ and W^UQ_hca [d_c][n_h*c] (std 1/sqrt(d_c))."""
+    import synth
+    shape = {"DQ": (cfg.d, cfg.d_c), "w": (cfg.d, cfg.n_hI), "IUQ": (cfg.d_c, cfg.n_hI * cfg.cI),
+             "UQ": (cfg.d_c, cfg.n_h * cfg.c), "UQ_hca": (cfg.d_c, cfg.n_h * cfg.c)}[nm]
+    std = cfg.weight_std if nm in ("DQ", "w") else cfg.d_c ** -0.5
+    return synth.normal(shape, synth.tensor_seed(cfg.seed, nm), std, "bf16")
+
+
+def hidden_rows(cfg, b, n_tot, r0, r1, dev):
+    """Rows [r0, r1) of sequence b's hidden states [n_tot][d] bf16, drawn on ``dev``."""
+    import synth
+    base = synth.tensor_seed(cfg.seed, "H") * 16 + b
+    return synth.normal_chunked_rows(n_tot, cfg.d, base, 1.0, "bf16", dev, r0, r1)
+
+
+def build_workload(cfg, dev, n_dec, n_sets=3):
     import torch
 
     import dense_long_context_amd as dlc
-    import synth
 
     B, d, c, cI, m, mp = cfg.B, cfg.d, cfg.c, cfg.cI, cfg.m, cfg.m_prime
     n_ctx = cfg.t                       # 2^20 context tokens
     n_tot = n_ctx + n_dec               # plus the decode tokens
-    std = cfg.weight_std
     t0 = time.perf_counter()
-    # weights (host draws, moved once); streams are laid out side by side
-    order = ["aKV", "bKV", "aZ", "bZ", "IaKV", "IbKV", "IaZ", "IbZ", "KV", "Z"]
-    width = {nm: (cI if nm.startswith("I") else c) for nm in order}
-    Wt = torch.cat([synth.normal((d, width[nm]), synth.tensor_seed(cfg.seed, nm), std, "bf16").t()
-                    for nm in order], 0).contiguous().to(dev)          # [3584][d]
-    off, o = {}, 0
-    for nm in order:
-        off[nm] = o
-        o += width[nm]
-    NS = o
+    off, width, NS = stream_layout(cfg)
+    Wt = torch.cat([stream_weight(cfg, nm).t() for nm in STREAMS], 0).contiguous().to(dev)  # [NS][d]
     S = torch.empty((B, n_tot, NS), dtype=torch.bfloat16, device=dev)
     H_dec = torch.empty((B, n_dec, d), dtype=torch.bfloat16, device=dev)  # hidden states of the decode tokens
     chunk = 1 << 16
     for b in range(B):
-        base = synth.tensor_seed(cfg.seed, "H") * 16 + b
         for r0 in range(0, n_tot, chunk):
             r1 = min(n_tot, r0 + chunk)
-            Hc = synth.normal_chunked_rows(n_tot, d, base, 1.0, "bf16", dev, r0, r1)
+            Hc = hidden_rows(cfg, b, n_tot, r0, r1, dev)
             dlc.dlc_project(Hc, Wt, out=S[b, r0:r1])
             if r0 <= n_ctx < r1:
                 H_dec[b] = Hc[n_ctx - r0:n_ctx - r0 + n_dec]
@@ -113,7 +139,7 @@ def build_workload(cfg, dev, n_dec):
     cap_csa, cap_hca = n_tot // m, n_tot // mp
     t1 = time.perf_counter()
     sets = []
-    for _ in range(3):
+    for _ in range(n_sets):
         Cc = torch.empty((B, cap_csa, c), dtype=torch.bfloat16, device=dev)
         KI = torch.empty((B, cap_csa, cI), dtype=torch.bfloat16, device=dev)
         Ch = torch.empty((B, cap_hca, c), dtype=torch.bfloat16, device=dev)
@@ -122,21 +148,19 @@ def build_workload(cfg, dev, n_dec):
         dlc.hca_compress(col("Z"), col("KV"), mp, Ch)
         sets.append((Cc, KI, Ch))
     torch.cuda.synchronize()
-    t_comp = (time.perf_counter() - t1) / 3
+    t_comp = (time.perf_counter() - t1) / n_sets
 
     # decode queries of tokens n_ctx .. n_tot-1 (projected once, stored per step)
-    def W(nm, rows, cols):
-        return synth.normal((rows, cols), synth.tensor_seed(cfg.seed, nm), std if nm in ("DQ", "w") else
-                            cfg.d_c ** -0.5, "bf16").t().contiguous().to(dev)
+    Wq = {nm: query_weight(cfg, nm).t().contiguous().to(dev) for nm in ("DQ", "w", "IUQ", "UQ", "UQ_hca")}
     h = H_dec.reshape(B * n_dec, d)
-    cQ = dlc.dlc_project(h, W("DQ", d, cfg.d_c))
-    qI = dlc.dlc_project(cQ, W("IUQ", cfg.d_c, cfg.n_hI * cI))
-    wI = dlc.dlc_project(h, W("w", d, cfg.n_hI), out_dtype=torch.float32)
-    q = dlc.dlc_project(cQ, W("UQ", cfg.d_c, cfg.n_h * c))
-    qh = dlc.dlc_project(cQ, W("UQ_hca", cfg.d_c, cfg.n_h * c))
+    cQ = dlc.dlc_project(h, Wq["DQ"])
+    qI = dlc.dlc_project(cQ, Wq["IUQ"])
+    wI = dlc.dlc_project(h, Wq["w"], out_dtype=torch.float32)
+    q = dlc.dlc_project(cQ, Wq["UQ"])
+    qh = dlc.dlc_project(cQ, Wq["UQ_hca"])
     per_step = lambda x, *shape: x.reshape(B, n_dec, *shape).transpose(0, 1).contiguous()  # noqa: E731
     Q = dict(qI=per_step(qI, 1, cfg.n_hI, cI), wI=per_step(wI, 1, cfg.n_hI), q=per_step(q, 1, cfg.n_h, c),
-             qh=per_step(qh, 1, cfg.n_h, c))
+             qh=per_step(qh, 1, cfg.n_h, c), cQ=per_step(cQ, 1, cfg.d_c))
     torch.cuda.synchronize()
     del H_dec
     return dict(S=S, col=col, sets=sets, Q=Q, n_ctx=n_ctx, n_tot=n_tot, cap_csa=cap_csa, cap_hca=cap_hca,
@@ -191,7 +215,7 @@ def make_steps(cfg, wl, dev, n_dec):
         calls.append((L.hca_attend, (BF, B, 1, n_h, c, mp, p(Q["qh"][s]), p(Ch), cap_hca, p(tt[s]), t, 0.0,
                                      p(o2), p(l2), p(ws_h), ws_h.numel(), stream)))
         steps.append((t, calls))
-    keep = (ws_i, ws_c, ws_h, idx, cnt, o1, l1, o2, l2, tt)
+    keep = dict(ws_i=ws_i, ws_c=ws_c, ws_h=ws_h, idx=idx, cnt=cnt, o_csa=o1, lse_csa=l1, o_hca=o2, lse_hca=l2, t=tt)
     return steps, keep
 
 

@@ -1,0 +1,417 @@
+"""Parity of the five workloads on the GPU against the fp64 oracle.
+
+* toy6: the six-token example of "DeepSeek-V4 Hybrid Attention: CSA and HCA
+  from Scratch" (The Running Example), once with the page's own hand-picked
+  weights (the device reproduces the printed values) and once with seeded
+  N(0,1) weights (the device matches the oracle's whole chain at 1e-5).
+* decode8k: one layer from bf16 hidden states (d=1024, 8192 context tokens,
+  query at t=8192), every stage checked against the oracle fed the device's
+  own stored inputs, plus the whole chain against the oracle's own chain.
+* csa128k: CSA decode at n_h=128, c=512, k=1024 over 32768 entries, B=8,
+  every query checked in full.
+* hca1m: dense HCA decode over 8192 entries of c=512, B=16, in full.
+* hybrid1m: the 2^20-token layer in the launch configuration the benchmark
+  times; sampled compressor entries (regenerated from their hidden rows),
+  sampled prefill queries, and sampled decode steps checked in full.
+
+Tolerances: stored bf16 results 8e-3 row-relative (one bf16 rounding of an
+fp32 result); attention outputs 2e-2 row-relative for bf16 inputs and 1e-5
+for fp32; lse absolute at the same bars; top-k sets exact up to the tie band
+of devtools.check_topk, widened by the scores' fp32 arithmetic bound.
+"""
+
+
+import numpy as np
+import pytest
+import torch
+
+import dense_long_context_amd as dlc
+import oracle as O
+import synth
+from devtools import DEV, assert_rows_close, check_topk, f64, need_gpu
+
+pytestmark = pytest.mark.gpu
+
+TOL_STORE = 8e-3
+TOL_ATT_BF16 = 2e-2
+
+
+def setup_module():
+    need_gpu()
+
+
+def _np(x):
+    return x.detach().cpu().to(torch.float64).numpy() if isinstance(x, torch.Tensor) else np.asarray(x)
+
+
+def _score_slack(qI, wI, KI):
+    """Bound on the fp32 accumulation error of the device scores (per entry)."""
+    q, w, K = f64(qI), f64(wI), f64(KI)
+    mag = np.abs(K) @ np.abs(q).T @ np.abs(w)
+    return 2e-6 * mag * (q.shape[1] + q.shape[0]) ** 0.5 + 1e-30
+
+
+def _check_index(qI, wI, KI, t, m, k, idx_row, count, scores_row=None, what=""):
+    """Scores (when given) within their arithmetic bound, and the top-k set."""
+    ref = O.index_scores(qI, wI, KI, t, m)
+    nv = len(ref)
+    slack = _score_slack(qI, wI, KI[:nv]) if nv else np.zeros(0)
+    if scores_row is not None:
+        assert np.all(np.abs(_np(scores_row)[:nv] - ref) <= slack), f"{what}: scores"
+    check_topk(_np(idx_row).astype(np.int64), int(count), ref, k, abs_slack=float(slack.max()) if nv else 0.0)
+    return ref
+
+
+def _check_attend(o, lse, o_ref, lse_ref, tol, what):
+    assert_rows_close(o, o_ref, tol, what)
+    l, lr = _np(lse), f64(lse_ref)
+    fin = np.isfinite(lr)
+    assert np.array_equal(np.isfinite(l), fin), f"{what}: lse finiteness"
+    if fin.any():
+        err = float(np.abs(l[fin] - lr[fin]).max())
+        assert err <= tol, f"{what}: lse error {err:.3e}"
+
+
+# ====================================================================== toy6
+
+def _toy_run(H, W, streams_dtype, m, mp, k, c, cI, KI_override=None):
+    """The chain of the toy on the device through the C ABI (fp32)."""
+    order = ["aKV", "bKV", "aZ", "bZ", "IaKV", "IbKV", "IaZ", "IbZ", "KV", "Z"]
+    Wt = torch.cat([W[nm].t() for nm in order], 0).contiguous().to(DEV)
+    Hd = H.to(DEV)
+    S = dlc.dlc_project(Hd, Wt)
+    col = {nm: S[None, :, c * i:c * i + c] for i, nm in enumerate(order)}
+    n = H.shape[0]
+    Cc = torch.zeros((1, n // m, c), device=DEV)
+    KI = torch.zeros((1, n // m, cI), device=DEV)
+    Ch = torch.zeros((1, n // mp, c), device=DEV)
+    dlc.csa_compress(col["aZ"], col["bZ"], col["aKV"], col["bKV"], m, Cc)
+    dlc.csa_compress(col["IaZ"], col["IbZ"], col["IaKV"], col["IbKV"], m, KI)
+    dlc.hca_compress(col["Z"], col["KV"], mp, Ch)
+    if KI_override is not None:
+        KI = torch.as_tensor(KI_override, dtype=torch.float32)[None].contiguous().to(DEV)
+    t = n - 1
+    h = Hd[t:t + 1]
+    cQ = dlc.dlc_project(h, W["DQ"].t().contiguous().to(DEV))
+    qI = dlc.dlc_project(cQ, W["IUQ"].t().contiguous().to(DEV)).reshape(1, 1, 1, cI)
+    wI = dlc.dlc_project(h, W["w"].t().contiguous().to(DEV)).reshape(1, 1, 1)
+    q = dlc.dlc_project(cQ, W["UQ"].t().contiguous().to(DEV)).reshape(1, 1, 1, c)
+    qh = dlc.dlc_project(cQ, W["UQ_hca"].t().contiguous().to(DEV)).reshape(1, 1, 1, c)
+    tt = torch.tensor([[t]], device=DEV)
+    scores = torch.full((1, 1, KI.shape[1]), float("nan"), device=DEV)
+    idx, cnt = dlc.csa_index_topk(qI, wI, KI, tt, t, m, k, scores=scores)
+    o_csa, lse_csa = dlc.csa_attend(q, Cc, idx, cnt)
+    o_hca, lse_hca = dlc.hca_attend(qh, Ch, tt, t, mp)
+    torch.cuda.synchronize()
+    scores = scores[:, :, :t // m]
+    return dict(Ccomp=Cc[0], KI=KI[0], Chca=Ch[0], scores=scores[0, 0], idx=idx[0, 0], cnt=cnt[0, 0],
+                o_csa=o_csa[0, 0], lse_csa=lse_csa[0, 0], o_hca=o_hca[0, 0], lse_hca=lse_hca[0, 0])
+
+
+def test_toy6_page_weights_reproduce_printed_values(golden):
+    """The page's hand-picked weights (HCA reuses W^aKV and W^aZ, the indexer keys
+    are the assumed [[0.5,0.5],[1,1]]): the device prints what the page prints."""
+    st, gw = golden["setup"], golden["weights"]
+    H = torch.tensor(st["H"], dtype=torch.float32)
+    m, mp, k, c, cI = st["m"], st["m_prime"], st["k"], st["c"], st["cI"]
+    W = {nm: torch.tensor(gw[nm], dtype=torch.float32) for nm in ("aKV", "bKV", "aZ", "bZ", "DQ", "IUQ", "w", "UQ")}
+    W["KV"], W["Z"], W["UQ_hca"] = W[gw["KV_hca_reuses"]], W[gw["Z_hca_reuses"]], W["UQ"]
+    for nm in ("IaKV", "IbKV", "IaZ", "IbZ"):       # unused: the keys are injected
+        W[nm] = torch.zeros((2, cI))
+    r = _toy_run(H, W, "f32", m, mp, k, c, cI, KI_override=golden["indexer"]["KI_assumed"])
+    P = 2.5e-3
+    np.testing.assert_allclose(_np(r["Ccomp"][0]), golden["csa_entries"]["C0"], atol=P)
+    np.testing.assert_allclose(_np(r["Ccomp"][1]), golden["csa_entries"]["C1"], atol=P)
+    np.testing.assert_allclose(_np(r["scores"]), golden["indexer"]["scores"], atol=P)
+    assert int(r["cnt"]) == 1 and _np(r["idx"])[0] == golden["indexer"]["top1"][0]
+    np.testing.assert_allclose(_np(r["o_csa"])[0], golden["csa_output"]["o"], atol=P)
+    np.testing.assert_allclose(_np(r["Chca"][0]), golden["hca"]["C0"], atol=P)
+    np.testing.assert_allclose(_np(r["Chca"][1]), golden["hca"]["C1"], atol=P)
+    np.testing.assert_allclose(_np(r["o_hca"])[0], golden["hca"]["o"], atol=P)
+
+
+def test_toy6_seeded_chain_matches_oracle():
+    """Config toy6: H as printed, every weight N(0,1) seed 0, query at t=5, fp32."""
+    cfg = synth.get_config("toy6")
+    H = synth.page_toy_hidden("f32")
+    d, c, cI = cfg.d, cfg.c, cfg.cI
+    W = {nm: synth.normal((d, c if not nm.startswith("I") else cI), synth.tensor_seed(cfg.seed, nm), dtype="f32")
+         for nm in ("aKV", "bKV", "aZ", "bZ", "IaKV", "IbKV", "IaZ", "IbZ", "KV", "Z")}
+    W["DQ"] = synth.normal((d, cfg.d_c), synth.tensor_seed(cfg.seed, "DQ"), dtype="f32")
+    W["IUQ"] = synth.normal((cfg.d_c, cfg.n_hI * cI), synth.tensor_seed(cfg.seed, "IUQ"), dtype="f32")
+    W["w"] = synth.normal((d, cfg.n_hI), synth.tensor_seed(cfg.seed, "w"), dtype="f32")
+    W["UQ"] = synth.normal((cfg.d_c, cfg.n_h * c), synth.tensor_seed(cfg.seed, "UQ"), dtype="f32")
+    W["UQ_hca"] = synth.normal((cfg.d_c, cfg.n_h * c), synth.tensor_seed(cfg.seed, "UQ_hca"), dtype="f32")
+    r = _toy_run(H, W, "f32", cfg.m, cfg.m_prime, cfg.k, c, cI)
+    ref = O.decode_chain(H, W, cfg.t, cfg.m, cfg.m_prime, cfg.k, cfg.n_h, c, cfg.n_hI, cI, dtype="f32")
+    for nm in ("Ccomp", "KI", "Chca"):
+        assert_rows_close(r[nm], ref[nm], 1e-5, nm)
+    check_topk(_np(r["idx"]).astype(np.int64), int(r["cnt"]), ref["scores"], cfg.k)
+    _check_attend(r["o_csa"][None], r["lse_csa"], ref["o_csa"], ref["lse_csa"], 1e-5, "toy6 CSA")
+    _check_attend(r["o_hca"][None], r["lse_hca"], ref["o_hca"], ref["lse_hca"], 1e-5, "toy6 HCA")
+
+
+# ================================================================== decode8k
+
+def test_decode8k_chain():
+    """Config decode8k: bf16 H [8193][1024] ~N(0,1), weights N(0, 1/fan-in), query t=8192."""
+    cfg = synth.get_config("decode8k")
+    d, c, cI, m, mp, k, t = cfg.d, cfg.c, cfg.cI, cfg.m, cfg.m_prime, cfg.k, cfg.t
+    n = t + 1
+    H = synth.normal((n, d), synth.tensor_seed(cfg.seed, "H"), dtype="bf16")
+    order = ["aKV", "bKV", "aZ", "bZ", "IaKV", "IbKV", "IaZ", "IbZ", "KV", "Z"]
+    width = {nm: (cI if nm.startswith("I") else c) for nm in order}
+    W = {nm: synth.normal((d, width[nm]), synth.tensor_seed(cfg.seed, nm), cfg.weight_std, "bf16") for nm in order}
+    up = cfg.d_c ** -0.5
+    W["DQ"] = synth.normal((d, cfg.d_c), synth.tensor_seed(cfg.seed, "DQ"), cfg.weight_std, "bf16")
+    W["w"] = synth.normal((d, cfg.n_hI), synth.tensor_seed(cfg.seed, "w"), cfg.weight_std, "bf16")
+    W["IUQ"] = synth.normal((cfg.d_c, cfg.n_hI * cI), synth.tensor_seed(cfg.seed, "IUQ"), up, "bf16")
+    W["UQ"] = synth.normal((cfg.d_c, cfg.n_h * c), synth.tensor_seed(cfg.seed, "UQ"), up, "bf16")
+    W["UQ_hca"] = synth.normal((cfg.d_c, cfg.n_h * c), synth.tensor_seed(cfg.seed, "UQ_hca"), up, "bf16")
+
+    # ---- device chain
+    Hd = H.to(DEV)
+    Wt = torch.cat([W[nm].t() for nm in order], 0).contiguous().to(DEV)
+    S = dlc.dlc_project(Hd[:t], Wt)[None]                       # context rows 0..t-1 -> [1][t][1024]
+    offs = np.cumsum([0] + [width[nm] for nm in order])
+    col = {nm: S[:, :, offs[i]:offs[i + 1]] for i, nm in enumerate(order)}
+    Cc = torch.empty((1, t // m, c), dtype=torch.bfloat16, device=DEV)
+    KI = torch.empty((1, t // m, cI), dtype=torch.bfloat16, device=DEV)
+    Ch = torch.empty((1, t // mp, c), dtype=torch.bfloat16, device=DEV)
+    dlc.csa_compress(col["aZ"], col["bZ"], col["aKV"], col["bKV"], m, Cc)
+    dlc.csa_compress(col["IaZ"], col["IbZ"], col["IaKV"], col["IbKV"], m, KI)
+    dlc.hca_compress(col["Z"], col["KV"], mp, Ch)
+    h = Hd[t:t + 1]
+    dv = lambda nm: W[nm].t().contiguous().to(DEV)  # noqa: E731
+    cQ = dlc.dlc_project(h, dv("DQ"))
+    qI = dlc.dlc_project(cQ, dv("IUQ")).reshape(1, 1, cfg.n_hI, cI)
+    wI = dlc.dlc_project(h, dv("w"), out_dtype=torch.float32).reshape(1, 1, cfg.n_hI)
+    q = dlc.dlc_project(cQ, dv("UQ")).reshape(1, 1, cfg.n_h, c)
+    qh = dlc.dlc_project(cQ, dv("UQ_hca")).reshape(1, 1, cfg.n_h, c)
+    tt = torch.tensor([[t]], device=DEV)
+    scores = torch.full((1, 1, t // m), float("nan"), device=DEV)
+    idx, cnt = dlc.csa_index_topk(qI, wI, KI, tt, t, m, k, scores=scores)
+    o_csa, lse_csa = dlc.csa_attend(q, Cc, idx, cnt)
+    o_hca, lse_hca = dlc.hca_attend(qh, Ch, tt, t, mp)
+    torch.cuda.synchronize()
+
+    # ---- stage-wise: the oracle fed the device's own stored inputs
+    Sh = _np(S[0])
+    ref_S = O.store_as(O.project(H[:t], np.hstack([f64(W[nm]) for nm in order])), "bf16")
+    assert_rows_close(Sh, ref_S, TOL_STORE, "projected streams")
+    g = {nm: Sh[:, offs[i]:offs[i + 1]] for i, nm in enumerate(order)}
+    assert_rows_close(Cc[0], O.csa_compress(g["aZ"], g["bZ"], g["aKV"], g["bKV"], m), TOL_STORE, "C^Comp")
+    assert_rows_close(KI[0], O.csa_compress(g["IaZ"], g["IbZ"], g["IaKV"], g["IbKV"], m), TOL_STORE, "K^I")
+    assert_rows_close(Ch[0], O.hca_compress(g["Z"], g["KV"], mp), TOL_STORE, "C^HCA")
+    assert_rows_close(cQ, O.store_as(O.project(H[t:t + 1], W["DQ"]), "bf16"), TOL_STORE, "c^Q")
+    assert_rows_close(qI[0, 0], O.store_as(O.split_heads(O.project(cQ.cpu(), W["IUQ"])[0], cfg.n_hI, cI), "bf16"),
+                      TOL_STORE, "q^I")
+    assert_rows_close(wI[0], O.project(H[t:t + 1], W["w"]), 1e-4, "w^I")
+    assert_rows_close(q[0, 0], O.store_as(O.split_heads(O.project(cQ.cpu(), W["UQ"])[0], cfg.n_h, c), "bf16"),
+                      TOL_STORE, "q")
+    _check_index(qI[0, 0].cpu(), wI[0, 0].cpu(), KI[0].cpu(), t, m, k, idx[0, 0].cpu(), cnt[0, 0].cpu(),
+                 scores[0, 0].cpu(), "decode8k")
+    sel = _np(idx[0, 0])[:int(cnt[0, 0])].astype(np.int64)
+    o_r, l_r = O.csa_attend(q[0, 0].cpu(), Cc[0].cpu(), sel)
+    _check_attend(o_csa[0, 0], lse_csa[0, 0], o_r, l_r, TOL_ATT_BF16, "decode8k CSA")
+    o_r, l_r = O.hca_attend(qh[0, 0].cpu(), Ch[0].cpu(), t, mp)
+    _check_attend(o_hca[0, 0], lse_hca[0, 0], o_r, l_r, TOL_ATT_BF16, "decode8k HCA")
+
+    # ---- the whole chain against the oracle's own chain (its own roundings)
+    ref = O.decode_chain(H, W, t, m, mp, k, cfg.n_h, c, cfg.n_hI, cI, dtype="bf16")
+    assert_rows_close(Cc[0], ref["Ccomp"], TOL_STORE, "chain C^Comp")
+    assert_rows_close(Ch[0], ref["Chca"], TOL_STORE, "chain C^HCA")
+    _check_attend(o_hca[0, 0], lse_hca[0, 0], ref["o_hca"], ref["lse_hca"], TOL_ATT_BF16, "chain HCA")
+    # a top-k decision may flip only within what two independent bf16 roundings of
+    # q^I and K^I can move a score: |dI_s| <= sum_h |w_h| 2^-7 sum_j |q_hj| |K_sj|
+    band = float((np.abs(ref["KI"]) @ np.abs(ref["qI"]).T @ np.abs(ref["wI"])).max()) * 2.0 ** -7
+    flips = check_topk(sel.tolist() + [-1] * (k - len(sel)), int(cnt[0, 0]), ref["scores"], k, abs_slack=band)
+    if flips == 0:
+        _check_attend(o_csa[0, 0], lse_csa[0, 0], ref["o_csa"], ref["lse_csa"], TOL_ATT_BF16, "chain CSA")
+
+
+# =================================================================== csa128k
+
+def test_csa128k_all_queries():
+    """Config csa128k: B=8, t=131072 (32768 entries), c=512, n_h=128, k=1024,
+    n_hI=64, cI=128; caches and queries ~N(0,1) bf16, w^I ~N(0,1) fp32."""
+    cfg = synth.get_config("csa128k")
+    B, c, cI, m, k, t = cfg.B, cfg.c, cfg.cI, cfg.m, cfg.k, cfg.t
+    nv = t // m
+    ts = synth.tensor_seed
+    Cc = synth.normal_chunked_rows(B * nv, c, ts(cfg.seed, "Ccomp"), 1.0, "bf16", DEV).reshape(B, nv, c)
+    KI = synth.normal_chunked_rows(B * nv, cI, ts(cfg.seed, "KI"), 1.0, "bf16", DEV).reshape(B, nv, cI)
+    q = synth.normal((B, 1, cfg.n_h, c), ts(cfg.seed, "q"), dtype="bf16", device=DEV)
+    qI = synth.normal((B, 1, cfg.n_hI, cI), ts(cfg.seed, "qI"), dtype="bf16", device=DEV)
+    wI = synth.normal((B, 1, cfg.n_hI), ts(cfg.seed, "wI"), dtype="f32", device=DEV)
+    tt = torch.full((B, 1), t, dtype=torch.int64, device=DEV)
+    scores = torch.full((B, 1, nv), float("nan"), device=DEV)
+    idx, cnt = dlc.csa_index_topk(qI, wI, KI, tt, t, m, k, scores=scores)
+    o, lse = dlc.csa_attend(q, Cc, idx, cnt)
+    torch.cuda.synchronize()
+    for b in range(B):
+        _check_index(qI[b, 0].cpu(), wI[b, 0].cpu(), KI[b].cpu(), t, m, k, idx[b, 0].cpu(), cnt[b, 0].cpu(),
+                     scores[b, 0].cpu(), f"csa128k b={b}")
+        sel = _np(idx[b, 0]).astype(np.int64)
+        o_r, l_r = O.csa_attend(q[b, 0].cpu(), Cc[b].cpu(), sel)
+        _check_attend(o[b, 0], lse[b, 0], o_r, l_r, TOL_ATT_BF16, f"csa128k b={b}")
+
+
+# ===================================================================== hca1m
+
+def test_hca1m_all_queries():
+    """Config hca1m: B=16, t=2^20, m'=128 -> 8192 entries of c=512 bf16, n_h=128."""
+    cfg = synth.get_config("hca1m")
+    B, c, mp, t = cfg.B, cfg.c, cfg.m_prime, cfg.t
+    nv = t // mp
+    ts = synth.tensor_seed
+    Ch = synth.normal_chunked_rows(B * nv, c, ts(cfg.seed, "Chca"), 1.0, "bf16", DEV).reshape(B, nv, c)
+    q = synth.normal((B, 1, cfg.n_h, c), ts(cfg.seed, "q"), dtype="bf16", device=DEV)
+    tt = torch.full((B, 1), t, dtype=torch.int64, device=DEV)
+    o, lse = dlc.hca_attend(q, Ch, tt, t, mp)
+    torch.cuda.synchronize()
+    for b in range(B):
+        o_r, l_r = O.hca_attend(q[b, 0].cpu(), Ch[b].cpu(), t, mp)
+        _check_attend(o[b, 0], lse[b, 0], o_r, l_r, TOL_ATT_BF16, f"hca1m b={b}")
+
+
+# ================================================================== hybrid1m
+
+@pytest.fixture(scope="module")
+def hybrid():
+    """The benchmark's own workload and pre-marshalled decode steps."""
+    import bench
+
+    cfg = synth.get_config("hybrid1m")
+    wl = bench.build_workload(cfg, torch.device(DEV), cfg.n_decode)
+    steps, keep = bench.make_steps(cfg, wl, torch.device(DEV), cfg.n_decode)
+    yield cfg, wl, steps, keep, bench
+    del steps, keep, wl
+    torch.cuda.empty_cache()
+
+
+def _hidden_f64(bench, cfg, wl, b, r0, r1):
+    return f64(bench.hidden_rows(cfg, b, wl["n_tot"], r0, r1, torch.device(DEV)).cpu())
+
+
+def test_hybrid1m_compressor_sample(hybrid):
+    """Sampled entries of all three caches of every sequence: the device streams
+    against the oracle's projection of the regenerated hidden rows, then each
+    entry against the oracle's compressor on the device's streams."""
+    cfg, wl, _, _, bench = hybrid
+    m, mp, c, cI = cfg.m, cfg.m_prime, cfg.c, cfg.cI
+    off, width, _ = bench.stream_layout(cfg)
+    Wall = np.hstack([f64(bench.stream_weight(cfg, nm)) for nm in bench.STREAMS])
+    Cc, KI, Ch = wl["sets"][0]
+    n_csa, n_hca = wl["n_tot"] // m, wl["n_tot"] // mp
+    csa_pick = [0, 1, 16383, 16384, 16385, 131071, n_csa - 2, n_csa - 1]
+    hca_pick = [0, 511, 512, 4095, n_hca - 1]
+    for b in range(cfg.B):
+        for i in csa_pick:
+            r0, r1 = max(0, m * (i - 1)), m * (i + 1)
+            S = f64(wl["S"][b, r0:r1].cpu())
+            ref_S = O.store_as(O.project(_hidden_f64(bench, cfg, wl, b, r0, r1), Wall), "bf16")
+            assert_rows_close(S, ref_S, TOL_STORE, f"streams b={b} rows {r0}..{r1}")
+            g = {nm: S[:, off[nm]:off[nm] + width[nm]] for nm in bench.STREAMS}
+            li = 0 if i == 0 else 1                         # the entry's index within the slice
+            ref_c = O.csa_compress(g["aZ"], g["bZ"], g["aKV"], g["bKV"], m, i_begin=li, i_end=li + 1)
+            ref_k = O.csa_compress(g["IaZ"], g["IbZ"], g["IaKV"], g["IbKV"], m, i_begin=li, i_end=li + 1)
+            assert_rows_close(Cc[b, i:i + 1], ref_c, TOL_STORE, f"C^Comp b={b} i={i}")
+            assert_rows_close(KI[b, i:i + 1], ref_k, TOL_STORE, f"K^I b={b} i={i}")
+        for i in hca_pick:
+            r0, r1 = mp * i, mp * (i + 1)
+            S = f64(wl["S"][b, r0:r1].cpu())
+            g = {nm: S[:, off[nm]:off[nm] + width[nm]] for nm in ("Z", "KV")}
+            assert_rows_close(Ch[b, i:i + 1], O.hca_compress(g["Z"], g["KV"], mp), TOL_STORE, f"C^HCA b={b} i={i}")
+    # the other cache sets hold the same values
+    for Cc2, KI2, Ch2 in wl["sets"][1:]:
+        assert torch.equal(Cc2, Cc) and torch.equal(KI2, KI) and torch.equal(Ch2, Ch)
+
+
+def test_hybrid1m_decode_steps(hybrid):
+    """Decode steps exactly as the benchmark launches them (pre-marshalled C-ABI
+    calls on the cache set of the step).  Entries a step compresses are poisoned
+    first, so the incremental compressors are checked too."""
+    cfg, wl, steps, keep, bench = hybrid
+    m, mp, k, n_dec = cfg.m, cfg.m_prime, cfg.k, cfg.n_decode
+    for s in (0, 3, 127, 255):
+        t, calls = steps[s]
+        Cc, KI, Ch = wl["sets"][s % 3]
+        saved = []
+        if (t + 1) % m == 0:
+            i = (t + 1) // m - 1
+            saved += [(Cc, i, Cc[:, i].clone()), (KI, i, KI[:, i].clone())]
+        if (t + 1) % mp == 0:
+            i = (t + 1) // mp - 1
+            saved += [(Ch, i, Ch[:, i].clone())]
+        for buf, i, _ in saved:
+            buf[:, i] = float("nan")
+        print(f"decode step s={s} t={t}: {len(calls)} calls", flush=True)
+        bench.run_steps(steps, s, 1, n_dec)
+        torch.cuda.synchronize()
+        for buf, i, want in saved:                          # the same value the full pass wrote
+            assert torch.equal(buf[:, i], want), f"incremental compress of entry {i} at t={t}"
+        Q = wl["Q"]
+        for b in range(cfg.B):
+            _check_index(Q["qI"][s][b, 0].cpu(), Q["wI"][s][b, 0].cpu(), KI[b, :t // m].cpu(), t, m, k,
+                         keep["idx"][b, 0].cpu(), keep["cnt"][b, 0].cpu(), None, f"step {s} b={b}")
+            sel = _np(keep["idx"][b, 0])[:int(keep["cnt"][b, 0])].astype(np.int64)
+            o_r, l_r = O.csa_attend(Q["q"][s][b, 0].cpu(), Cc[b].cpu(), sel)
+            _check_attend(keep["o_csa"][b, 0], keep["lse_csa"][b, 0], o_r, l_r, TOL_ATT_BF16, f"CSA step {s} b={b}")
+            o_r, l_r = O.hca_attend(Q["qh"][s][b, 0].cpu(), Ch[b, :t // mp].cpu(), t, mp)
+            _check_attend(keep["o_hca"][b, 0], keep["lse_hca"][b, 0], o_r, l_r, TOL_ATT_BF16, f"HCA step {s} b={b}")
+
+
+def test_hybrid1m_decode_queries(hybrid):
+    """The decode queries the benchmark projects, against the oracle's projection
+    of the regenerated hidden rows (c^Q from h_t, the heads from the device's c^Q)."""
+    cfg, wl, _, _, bench = hybrid
+    n_ctx = wl["n_ctx"]
+    Wq = {nm: f64(bench.query_weight(cfg, nm)) for nm in ("DQ", "w", "IUQ", "UQ", "UQ_hca")}
+    for s in (0, 255):
+        for b in range(cfg.B):
+            h = _hidden_f64(bench, cfg, wl, b, n_ctx + s, n_ctx + s + 1)
+            cQ = wl["Q"]["cQ"][s][b]
+            assert_rows_close(cQ, O.store_as(O.project(h, Wq["DQ"]), "bf16"), TOL_STORE, "c^Q")
+            cQd = f64(cQ.cpu())
+            assert_rows_close(wl["Q"]["wI"][s][b], O.project(h, Wq["w"]), 1e-4, "w^I")
+            for nm, key, nh, wdt in (("IUQ", "qI", cfg.n_hI, cfg.cI), ("UQ", "q", cfg.n_h, cfg.c),
+                                     ("UQ_hca", "qh", cfg.n_h, cfg.c)):
+                ref = O.store_as(O.split_heads(O.project(cQd, Wq[nm])[0], nh, wdt), "bf16")
+                assert_rows_close(wl["Q"][key][s][b, 0], ref, TOL_STORE, key)
+
+
+def test_hybrid1m_prefill_sample(hybrid):
+    """Chunked causal prefill: a sample of queries at t in [2^20-4096, 2^20) per
+    sequence, run as one multi-query call of each stage against the full caches."""
+    cfg, wl, _, _, bench = hybrid
+    B, m, mp, k, c, cI = cfg.B, cfg.m, cfg.m_prime, cfg.k, cfg.c, cfg.cI
+    n_ctx = wl["n_ctx"]
+    offs = [-4096, -4095, -4093, -2049, -129, -128, -1]
+    nq = len(offs)
+    Wq = {nm: bench.query_weight(cfg, nm).t().contiguous().to(DEV) for nm in ("DQ", "w", "IUQ", "UQ", "UQ_hca")}
+    h = torch.cat([torch.cat([bench.hidden_rows(cfg, b, wl["n_tot"], n_ctx + o, n_ctx + o + 1, torch.device(DEV))
+                              for o in offs]) for b in range(B)])          # [B*nq][d]
+    cQ = dlc.dlc_project(h, Wq["DQ"])
+    qI = dlc.dlc_project(cQ, Wq["IUQ"]).reshape(B, nq, cfg.n_hI, cI)
+    wI = dlc.dlc_project(h, Wq["w"], out_dtype=torch.float32).reshape(B, nq, cfg.n_hI)
+    q = dlc.dlc_project(cQ, Wq["UQ"]).reshape(B, nq, cfg.n_h, c)
+    qh = dlc.dlc_project(cQ, Wq["UQ_hca"]).reshape(B, nq, cfg.n_h, c)
+    tt = torch.tensor([[n_ctx + o for o in offs]] * B, dtype=torch.int64, device=DEV)
+    t_max = n_ctx - 1
+    Cc, KI, Ch = wl["sets"][0]
+    idx, cnt = dlc.csa_index_topk(qI, wI, KI, tt, t_max, m, k)
+    o1, l1 = dlc.csa_attend(q, Cc, idx, cnt)
+    o2, l2 = dlc.hca_attend(qh, Ch, tt, t_max, mp)
+    torch.cuda.synchronize()
+    for b in range(B):
+        KIb, Ccb, Chb = KI[b].cpu(), Cc[b].cpu(), Ch[b].cpu()
+        for j, o in enumerate(offs):
+            t = n_ctx + o
+            _check_index(qI[b, j].cpu(), wI[b, j].cpu(), KIb[:t // m], t, m, k, idx[b, j].cpu(), cnt[b, j].cpu(),
+                         None, f"prefill b={b} t={t}")
+            sel = _np(idx[b, j])[:int(cnt[b, j])].astype(np.int64)
+            o_r, l_r = O.csa_attend(q[b, j].cpu(), Ccb, sel)
+            _check_attend(o1[b, j], l1[b, j], o_r, l_r, TOL_ATT_BF16, f"prefill CSA b={b} t={t}")
+            o_r, l_r = O.hca_attend(qh[b, j].cpu(), Chb[:t // mp], t, mp)
+            _check_attend(o2[b, j], l2[b, j], o_r, l_r, TOL_ATT_BF16, f"prefill HCA b={b} t={t}")
