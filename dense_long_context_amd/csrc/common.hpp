@@ -9,7 +9,7 @@
 #include <cstdarg>
 #include <cstdio>
 
-#include "../../include/dlc.h"
+#include "dlc.h"
 
 namespace dlc {
 

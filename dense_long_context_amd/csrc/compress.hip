@@ -2,20 +2,25 @@
 //
 // "DeepSeek-V4 Hybrid Attention: CSA and HCA from Scratch", §4-§5 (CSA) and
 // §10 (HCA): every output column is its own softmax-weighted pooling of the
-// window's rows.  One thread owns one (entry, group of columns); a group is
-// one 16-byte vector (8 bf16 or 4 fp32 columns) on the fast path and one
-// column on the generic path.  Each stream row is read exactly once per entry
-// that uses it, with consecutive threads on consecutive columns, so a wave
-// reads whole rows.  The window is consumed in chunks of kChunk rows with an
-// online softmax: the running max moves once per chunk, so the pass costs one
-// exp per logit plus one per chunk, with no second pass over Z.
+// window's rows.  A thread owns one (entry, group of columns) - a group is one
+// 16-byte vector (8 bf16 or 4 fp32 columns) on the fast path and one column on
+// the generic path - or, for calls with few entries, one slice of that pair's
+// window rows.  Consecutive threads take consecutive column groups of the same
+// rows, so a wave reads whole row segments, and each stream row is read once
+// per entry that uses it.  The window is consumed in chunks of kChunk rows with
+// an online softmax: all loads of a chunk are in flight together, the running
+// max moves once per chunk, and the pass costs one exp per logit plus one per
+// chunk, with no second pass over Z.
 #include "common.hpp"
 
 namespace dlc {
 
 namespace {
 
-constexpr int kChunk = 8;
+#ifndef DLC_POOL_CHUNK
+#define DLC_POOL_CHUNK 4
+#endif
+constexpr int kChunk = DLC_POOL_CHUNK;
 constexpr float kLog2e = 1.4426950408889634f;
 
 struct PoolArgs {
@@ -50,73 +55,126 @@ __device__ __forceinline__ void load_bias(const float* bias, int64_t r, int64_t 
   }
 }
 
-// One window segment: rows row0 .. row0+m-1 of (Z, C) with bias rows 0 .. m-1.
+// Window row rho of entry i: rho < m is row m*i + rho of the a-streams (bias
+// row rho), m <= rho < 2m is row m*(i-1) + rho - m of the b-streams (bias row
+// rho - m).  The window is cut into chunks of kChunk rows.  A chunk's partial
+// softmax state is (max, sum, acc) with its weights taken against its own max;
+// all its loads are in flight together, so a chunk costs one memory round trip.
 template <typename T, int VEC>
-__device__ __forceinline__ void pool_segment(const T* Z, const T* C, const float* bias, int64_t row0,
-                                             const PoolArgs& a, int64_t j0, float* mx, float* sum,
-                                             float* acc) {
-  for (int64_t r0 = 0; r0 < a.m; r0 += kChunk) {
-    float l[kChunk][VEC];
-    const int rows = int(a.m - r0 < kChunk ? a.m - r0 : kChunk);
+__device__ __forceinline__ void chunk_partial(const PoolArgs& a, int64_t boff, int64_t i, int r0, int r1,
+                                              int64_t j0, float* mx, float* sum, float* acc) {
+  float l[kChunk][VEC], cv[kChunk][VEC];
+#pragma unroll
+  for (int rr = 0; rr < kChunk; ++rr) {
+    const int rho = r0 + rr;
+    if (rho < r1) {
+      const int seg = rho >= a.m ? 1 : 0;
+      const int64_t rb = seg ? rho - a.m : rho;  // row within the block (bias row)
+      const int64_t row = a.m * (i - seg) + rb;
+      const T* Z = static_cast<const T*>(a.Z[seg]) + boff + row * a.ld;
+      const T* C = static_cast<const T*>(a.C[seg]) + boff + row * a.ld;
+      float bv[VEC];
+      load_cols<T, VEC>(Z, j0, a.c, l[rr]);
+      load_cols<T, VEC>(C, j0, a.c, cv[rr]);
+      load_bias<VEC>(a.bias[seg], rb, a.c, j0, bv);
+#pragma unroll
+      for (int u = 0; u < VEC; ++u) l[rr][u] = (l[rr][u] + bv[u]) * kLog2e;
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < VEC; ++u) {
+    float cm = -INFINITY;
+#pragma unroll
+    for (int rr = 0; rr < kChunk; ++rr)
+      if (r0 + rr < r1) cm = fmaxf(cm, l[rr][u]);
+    float sm = 0.f, ac = 0.f;
+    // logits are finite: one v_exp_f32 each
 #pragma unroll
     for (int rr = 0; rr < kChunk; ++rr) {
-      if (rr < rows) {
-        float z[VEC], bv[VEC];
-        load_cols<T, VEC>(Z + (row0 + r0 + rr) * a.ld, j0, a.c, z);
-        load_bias<VEC>(bias, r0 + rr, a.c, j0, bv);
-#pragma unroll
-        for (int u = 0; u < VEC; ++u) l[rr][u] = (z[u] + bv[u]) * kLog2e;
+      if (r0 + rr < r1) {
+        const float w = __builtin_amdgcn_exp2f(l[rr][u] - cm);
+        sm += w;
+        ac = fmaf(w, cv[rr][u], ac);
       }
     }
-    // move the running max once for the whole chunk
-#pragma unroll
-    for (int u = 0; u < VEC; ++u) {
-      float cm = mx[u];
-#pragma unroll
-      for (int rr = 0; rr < kChunk; ++rr)
-        if (rr < rows) cm = fmaxf(cm, l[rr][u]);
-      if (cm > mx[u]) {
-        const float f = (mx[u] == -INFINITY) ? 0.f : exp2f(mx[u] - cm);
-        sum[u] *= f;
-        acc[u] *= f;
-        mx[u] = cm;
-      }
-    }
-#pragma unroll
-    for (int rr = 0; rr < kChunk; ++rr) {
-      if (rr < rows) {
-        float cv[VEC];
-        load_cols<T, VEC>(C + (row0 + r0 + rr) * a.ld, j0, a.c, cv);
-#pragma unroll
-        for (int u = 0; u < VEC; ++u) {
-          const float w = (l[rr][u] == -INFINITY) ? 0.f : exp2f(l[rr][u] - mx[u]);
-          sum[u] += w;
-          acc[u] = fmaf(w, cv[u], acc[u]);
-        }
-      }
-    }
+    mx[u] = cm;
+    sum[u] = sm;
+    acc[u] = ac;
   }
 }
 
-template <typename T, int VEC, bool OVERLAP>
+// state <- state (+) partial.  The same operations wherever two states meet,
+// so the result depends only on the chunk order, not on which lanes held them.
+template <int VEC>
+__device__ __forceinline__ void merge_state(float* mS, float* sS, float* aS, const float* mP, const float* sP,
+                                            const float* aP) {
+#pragma unroll
+  for (int u = 0; u < VEC; ++u) {
+    const float M = fmaxf(mS[u], mP[u]);
+    const float f1 = mS[u] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mS[u] - M);
+    const float f2 = mP[u] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mP[u] - M);
+    sS[u] = fmaf(sS[u], f1, sP[u] * f2);
+    aS[u] = fmaf(aS[u], f1, aP[u] * f2);
+    mS[u] = M;
+  }
+}
+
+// The entry's value is the left-to-right fold of its chunk partials.
+// R = 1: a thread owns one (entry, column group) and folds its chunks in turn.
+// R > 1 (calls with few entries): R adjacent lanes share one (entry, column
+// group), lane q computes chunk q, and lane 0 folds them in order through lane
+// shuffles - the same fold, so an entry has the same bits whichever way it was
+// computed (an incremental decode call reproduces the full pass exactly).
+// Thread t = ((e * col_groups + g) * R + q); consecutive column groups of the
+// same rows sit in consecutive lanes, so a wave reads whole row segments.
+template <typename T, int VEC, bool OVERLAP, int R>
 __global__ void __launch_bounds__(256) pool_kernel(PoolArgs a) {
-  const int64_t tid = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (tid >= a.n_entries * a.col_groups) return;
-  const int64_t e = tid / a.col_groups;
-  const int64_t j0 = (tid - e * a.col_groups) * VEC;
+  const int64_t t = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  const int q = int(t % R);
+  const int64_t eg = t / R;
+  const bool live = eg < a.n_entries * a.col_groups;
+  const int64_t e = live ? eg / a.col_groups : 0;
+  const int64_t j0 = (eg - e * a.col_groups) * VEC;
   const int64_t i = a.i_begin + e;
   const int64_t boff = int64_t(blockIdx.y) * a.batch_stride;
+  const int rows = int((OVERLAP && i > 0) ? 2 * a.m : a.m);  // i = 0 has no b-rows
 
   float mx[VEC], sum[VEC], acc[VEC];
+  if constexpr (R == 1) {
 #pragma unroll
-  for (int u = 0; u < VEC; ++u) { mx[u] = -INFINITY; sum[u] = 0.f; acc[u] = 0.f; }
-
-  pool_segment<T, VEC>(static_cast<const T*>(a.Z[0]) + boff, static_cast<const T*>(a.C[0]) + boff,
-                       a.bias[0], a.m * i, a, j0, mx, sum, acc);
-  if (OVERLAP && i > 0)
-    pool_segment<T, VEC>(static_cast<const T*>(a.Z[1]) + boff, static_cast<const T*>(a.C[1]) + boff,
-                         a.bias[1], a.m * (i - 1), a, j0, mx, sum, acc);
-
+    for (int u = 0; u < VEC; ++u) { mx[u] = -INFINITY; sum[u] = 0.f; acc[u] = 0.f; }
+    if (live) {
+      for (int r0 = 0; r0 < rows; r0 += kChunk) {
+        float pm[VEC], ps[VEC], pa[VEC];
+        chunk_partial<T, VEC>(a, boff, i, r0, min(rows, r0 + kChunk), j0, pm, ps, pa);
+        merge_state<VEC>(mx, sum, acc, pm, ps, pa);
+      }
+    }
+  } else {
+    float pm[VEC], ps[VEC], pa[VEC];
+    const int r0 = q * kChunk;
+    if (live && r0 < rows) {
+      chunk_partial<T, VEC>(a, boff, i, r0, min(rows, r0 + kChunk), j0, pm, ps, pa);
+    } else {
+#pragma unroll
+      for (int u = 0; u < VEC; ++u) { pm[u] = -INFINITY; ps[u] = 0.f; pa[u] = 0.f; }
+    }
+#pragma unroll
+    for (int u = 0; u < VEC; ++u) { mx[u] = -INFINITY; sum[u] = 0.f; acc[u] = 0.f; }
+    const int base = int(threadIdx.x & 63) & ~(R - 1);  // lane of chunk 0
+#pragma unroll 1
+    for (int k = 0; k < R; ++k) {
+      float km[VEC], ks[VEC], ka[VEC];
+#pragma unroll
+      for (int u = 0; u < VEC; ++u) {
+        km[u] = __shfl(pm[u], base + k);
+        ks[u] = __shfl(ps[u], base + k);
+        ka[u] = __shfl(pa[u], base + k);
+      }
+      merge_state<VEC>(mx, sum, acc, km, ks, ka);
+    }
+  }
+  if (!live || q != 0) return;
   float o[VEC];
 #pragma unroll
   for (int u = 0; u < VEC; ++u) o[u] = acc[u] / sum[u];
@@ -128,18 +186,35 @@ __global__ void __launch_bounds__(256) pool_kernel(PoolArgs a) {
   }
 }
 
-template <typename T, int VEC>
-int launch_pool(PoolArgs a, bool overlap, int64_t B, hipStream_t s) {
-  const int64_t threads = a.n_entries * a.col_groups;
+template <typename T, int VEC, int R>
+int launch_pool_r(PoolArgs a, bool overlap, int64_t B, hipStream_t s) {
+  const int64_t threads = a.n_entries * a.col_groups * R;
   const int64_t blocks = ceil_div(threads, 256);
   DLC_REQUIRE(blocks < (int64_t(1) << 31) && B <= 65535, DLC_E_UNSUPPORTED, "compress: grid too large");
   dim3 grid{(unsigned)blocks, (unsigned)B, 1u};
   StageTimer timer(DLC_STAGE_COMPRESS, s);
   if (overlap)
-    hipLaunchKernelGGL((pool_kernel<T, VEC, true>), grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL((pool_kernel<T, VEC, true, R>), grid, dim3(256), 0, s, a);
   else
-    hipLaunchKernelGGL((pool_kernel<T, VEC, false>), grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL((pool_kernel<T, VEC, false, R>), grid, dim3(256), 0, s, a);
   return check_launch("compress");
+}
+
+// fewer than this many (entry, column group) pairs over all sequences: split rows
+constexpr int64_t kSmallLaunch = 1 << 16;
+
+template <typename T, int VEC>
+int launch_pool(PoolArgs a, bool overlap, int64_t B, hipStream_t s) {
+  // a few entries: one lane per chunk of window rows, if the window has at most 32 chunks
+  const int64_t chunks = ceil_div((overlap ? 2 : 1) * a.m, int64_t(kChunk));
+  if (a.n_entries * a.col_groups * B < kSmallLaunch && chunks <= 32) {
+    if (chunks <= 2) return launch_pool_r<T, VEC, 2>(a, overlap, B, s);
+    if (chunks <= 4) return launch_pool_r<T, VEC, 4>(a, overlap, B, s);
+    if (chunks <= 8) return launch_pool_r<T, VEC, 8>(a, overlap, B, s);
+    if (chunks <= 16) return launch_pool_r<T, VEC, 16>(a, overlap, B, s);
+    return launch_pool_r<T, VEC, 32>(a, overlap, B, s);
+  }
+  return launch_pool_r<T, VEC, 1>(a, overlap, B, s);
 }
 
 int pool_dispatch(const char* name, int dtype, int64_t B, int64_t n, int64_t c, int64_t m,
