@@ -274,12 +274,90 @@ def cpu_baseline(cfg, budget_s=15.0):
         O.hca_attend(q, Ch, t, cfg.m_prime)
         done += 1
         el = time.perf_counter() - t0
-        if el >= budget_s or done >= 64:
+        if el >= budget_s or done >= 256:
             break
     return {"value": done / el, "unit": "decode query-tokens/s", "cores": int(threads), "kind": "oracle",
             "sample": f"{done} decode queries at t=2^20 (indexer over {nv} entries, top-{cfg.k}, CSA attention "
                       f"over the selected entries, HCA attention over {nh_v} entries), fp64 numpy, "
                       f"{el:.1f} s; the per-step compressor work (one entry every m tokens) is omitted"}
+
+
+PMC_COPY_BYTES = 1 << 30
+
+
+def pmc_probe():
+    """The decode-shaped indexer call (B = 4, 262208-entry caches in three
+    rotating sets, t = 2^20) six times, then a copy of PMC_COPY_BYTES (four
+    times the 256 MB last-level cache) three times: the program the FETCH_SIZE
+    / WRITE_SIZE counter runs profile."""
+    import torch
+
+    from dense_long_context_amd import binding
+    import synth
+    from synth import get_config
+
+    cfg = get_config("hybrid1m")
+    dev = torch.device("cuda:0")
+    B, cI, m, k, n_hI = cfg.B, cfg.cI, cfg.m, cfg.k, cfg.n_hI
+    cap = (cfg.t + cfg.n_decode) // m
+    sets = [synth.normal((B, cap, cI), 7000 + i, dtype="bf16", device=dev) for i in range(3)]
+    qI = synth.normal((B, 1, n_hI, cI), 7010, dtype="bf16", device=dev)
+    wI = synth.normal((B, 1, n_hI), 7011, dtype="f32", device=dev)
+    t = torch.full((B, 1), cfg.t, dtype=torch.int64, device=dev)
+    ws = torch.empty(binding.csa_index_topk_ws(B, 1, cap, k), dtype=torch.uint8, device=dev)
+    # the copy's source is written first, so that the indexer's 800 MB of key
+    # streams have pushed it out of the caches before it is copied
+    a = torch.ones(PMC_COPY_BYTES, dtype=torch.uint8, device=dev)
+    b = torch.empty_like(a)
+    for i in range(6):
+        binding.csa_index_topk(qI, wI, sets[i % 3], t, cfg.t, m, k, ws=ws)
+    for _ in range(3):
+        binding.dlc_copy(b, a)
+    torch.cuda.synchronize()
+    print(json.dumps({"pmc_probe": "done", "scores_bytes_per_launch": step_bytes(cfg, cfg.t)[1],
+                      "copy_bytes": PMC_COPY_BYTES}), flush=True)
+
+
+def _counter_kib(csv_path, kernel_part, counter):
+    """Per-dispatch values (KiB) of ``counter`` for kernels whose name contains
+    ``kernel_part``, from a rocprofv3 counter_collection CSV."""
+    import csv
+    per = {}
+    with open(csv_path) as f:
+        for r in csv.DictReader(f):
+            if kernel_part in r["Kernel_Name"] and r["Counter_Name"] == counter:
+                per[r["Dispatch_Id"]] = per.get(r["Dispatch_Id"], 0.0) + float(r["Counter_Value"])
+    return list(per.values())
+
+
+def ingest_pmc(fetch_csv, write_csv):
+    """HBM bytes per launch of the scores kernel: FETCH_SIZE and WRITE_SIZE, each
+    scaled by what the same counter reads for the copy kernel (which moves
+    PMC_COPY_BYTES each way)."""
+    from synth import get_config
+
+    cfg = get_config("hybrid1m")
+    f_sc = _counter_kib(fetch_csv, "scores_mfma_kernel", "FETCH_SIZE")
+    f_cp = _counter_kib(fetch_csv, "copy_kernel", "FETCH_SIZE")
+    w_sc = _counter_kib(write_csv, "scores_mfma_kernel", "WRITE_SIZE")
+    w_cp = _counter_kib(write_csv, "copy_kernel", "WRITE_SIZE")
+    if not (f_sc and f_cp and w_sc and w_cp):
+        raise SystemExit("counter CSVs lack the scores or copy kernel dispatches")
+    # the first launch of each cache set is cold; the profiled launches rotate 3 sets
+    fetch_factor = (sum(f_cp) / len(f_cp)) * 1024 / PMC_COPY_BYTES
+    write_factor = (sum(w_cp) / len(w_cp)) * 1024 / PMC_COPY_BYTES
+    fetch = (sum(f_sc) / len(f_sc)) * 1024 / fetch_factor
+    write = (sum(w_sc) / len(w_sc)) * 1024 / write_factor
+    out = {"kernel": SCORES_KERNEL, "workload": "hybrid1m decode indexer, B=4, 262144 visible entries",
+           "source_hash": source_hash(), "fetch_kib_per_dispatch": sum(f_sc) / len(f_sc),
+           "write_kib_per_dispatch": sum(w_sc) / len(w_sc), "copy_fetch_factor": fetch_factor,
+           "copy_write_factor": write_factor, "fetch_bytes_per_launch": int(fetch),
+           "write_bytes_per_launch": int(write), "hbm_bytes_per_launch": int(fetch + write),
+           "algorithmic_bytes_per_launch": step_bytes(cfg, cfg.t)[1], "dispatches": len(f_sc)}
+    os.makedirs(os.path.dirname(COUNTERS_FILE), exist_ok=True)
+    with open(COUNTERS_FILE, "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out))
 
 
 def main():
@@ -289,11 +367,23 @@ def main():
     ap.add_argument("--warmup", type=int, default=16)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--repeat", type=int, default=1, help="time the K steps this many times, report the best")
+    ap.add_argument("--pmc-probe", action="store_true",
+                    help="run only the indexer on the decode shapes plus a copy kernel of known size "
+                         "(the short program that rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE profile)")
+    ap.add_argument("--ingest-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write the HBM traffic of the scores kernel from two rocprofv3 counter CSVs")
     args = ap.parse_args()
+    if args.ingest_pmc:
+        ingest_pmc(*args.ingest_pmc)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py runs on one GPU only: the CSA/HCA hot path here is single-device "
               "(multi-GPU sharding is a design note, not part of this build).", file=sys.stderr)
         sys.exit(2)
+
+    if args.pmc_probe:
+        pmc_probe()
+        return
 
     import torch
 
@@ -313,30 +403,40 @@ def main():
     run_steps(steps, 0, args.warmup, n_dec)
     torch.cuda.synchronize()
     K = args.steps
-    best = None
-    for rep in range(args.repeat):
-        # live per-kernel timing of the dominant kernel (indexer scores) over the timed steps
-        evs = [(ev.create(), ev.create()) for _ in range(K)]
+
+    def timed(armed):
+        """K steps between a barrier-free pair of stream events.  armed: also
+        time every launch of the scores kernel with its own HIP events."""
+        evs = [(ev.create(), ev.create()) for _ in range(K)] if armed else []
         start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         start.record()
         for j in range(K):
             s = args.warmup + j
-            binding.dlc_timing_arm(binding.STAGE_INDEX_SCORES, evs[j][0], evs[j][1])
+            if armed:
+                binding.dlc_timing_arm(binding.STAGE_INDEX_SCORES, evs[j][0], evs[j][1])
             for fn, a in steps[s % n_dec][1]:
                 rc = fn(*a)
                 if rc != 0:
                     raise RuntimeError(binding.last_error())
         stop.record()
         torch.cuda.synchronize()
-        ms = start.elapsed_time(stop)
         k_ms = [ev.elapsed_ms(a, b) for a, b in evs]
         for a, b in evs:
             ev.destroy(a)
             ev.destroy(b)
+        return start.elapsed_time(stop), k_ms
+
+    # the step rate is taken without the per-kernel events (their records add
+    # gaps to the stream); the same K steps then run again with the scores
+    # kernel timed launch by launch
+    best = None
+    for rep in range(args.repeat):
+        ms, _ = timed(False)
+        ms_armed, k_ms = timed(True)
         if best is None or ms < best[0]:
-            best = (ms, k_ms)
-    ms, k_ms = best
+            best = (ms, k_ms, ms_armed)
+    ms, k_ms, ms_armed = best
     ts = [steps[(args.warmup + j) % n_dec][0] for j in range(K)]
     total_bytes = sum(step_bytes(cfg, t)[0] for t in ts)
     idx_bytes = sum(step_bytes(cfg, t)[1] for t in ts) / K
@@ -388,6 +488,7 @@ def main():
                      "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic,
                      "avg_launch_us": round(k_avg_ms * 1e3, 3),
                      "algorithmic_bytes_per_launch": int(idx_bytes)},
+        "ms_per_step_with_kernel_events": round(ms_armed / K, 5),
         "step_hbm_gbs": round(hbm_gbs, 1),
         "step_frac_of_peak": round(hbm_gbs / PEAK_HBM_GBS, 4),
         "copy_kernel_gbs": round(copy_gbs, 1),

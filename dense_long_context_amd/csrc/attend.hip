@@ -40,9 +40,6 @@ constexpr float kLn2 = 0.6931471805599453f;
 #define DLC_ATTEND_MIN_KEYS 64
 #endif
 constexpr int kMinKeysPerSplit = DLC_ATTEND_MIN_KEYS;
-#ifndef DLC_ATT_W4
-#define DLC_ATT_W4 0
-#endif
 constexpr int kTargetWorkgroups = DLC_ATTEND_TARGET_WGS;
 
 struct AttArgs {
@@ -407,10 +404,19 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_s_barrier();
 }
 
-constexpr int kW4TileBytes = 34816;   // 1024*31 + 16*t(31) + 1024, rounded up to 1 KB
+// LDS layout of a 32-key tile (gfx950 LDS: 64 banks of 4 bytes): key row r
+// starts at byte 1024*r + 16*t(r), t(4a+j) = 16a + a%4 + 4j.  Row starts then
+// differ mod 256 bytes so that
+//  * a ds_read_b128 of 16 consecutive rows at one 16-byte column (the Q.K^T A
+//    operand, 16 lanes per pass) touches 16 distinct 4-bank groups, and
+//  * a ds_read_b64_tr_b16 of 4 consecutive rows x 64 bytes (the P.V B operand,
+//    32 lanes per pass) touches 4 disjoint 16-bank groups;
+// both are conflict-free.  A row stays 1 KB contiguous, as one direct load
+// writes it.
+constexpr int kTileBytes = 34816;   // 1024*31 + 16*t(31) + 1024, rounded up to 1 KB
 constexpr int kMaxGatherKeys = 2048;  // keys per split whose rows sit in LDS
 
-__device__ __forceinline__ constexpr int w4_row_off(int r) {
+__device__ __forceinline__ constexpr int tile_row_off(int r) {
   return 1024 * r + 16 * (16 * (r >> 2) + ((r >> 2) & 3) + 4 * (r & 3));
 }
 
@@ -425,9 +431,9 @@ __global__ void __launch_bounds__(512) attend512_kernel(AttArgs a) {
   constexpr int HPG = 128;              // heads per workgroup: 4 slices of 32, each split over 2 waves
   // one array per stage: distinct objects let the compiler see that reads of
   // the current stage never alias the loads still landing in the others
-  __shared__ __attribute__((aligned(1024))) unsigned char sK0[kW4TileBytes];
-  __shared__ __attribute__((aligned(1024))) unsigned char sK1[kW4TileBytes];
-  __shared__ __attribute__((aligned(1024))) unsigned char sK2[kW4TileBytes];
+  __shared__ __attribute__((aligned(1024))) unsigned char sK0[kTileBytes];
+  __shared__ __attribute__((aligned(1024))) unsigned char sK1[kTileBytes];
+  __shared__ __attribute__((aligned(1024))) unsigned char sK2[kTileBytes];
   // partial S^T of every wave: lane-major, 16 values + 4 pad per lane so that
   // four 16-byte accesses per lane are free of bank conflicts
   constexpr int XROW = 20;
@@ -473,7 +479,7 @@ __global__ void __launch_bounds__(512) attend512_kernel(AttArgs a) {
       }
       gr = __builtin_amdgcn_readfirstlane(int(gr));
       const bf16_raw* src = gr >= 0 ? kv + gr * CD : g_zero_row;
-      const uint32_t lds_addr = (uint32_t)(uintptr_t)DLC_LDS(dst) + uint32_t(w4_row_off(row));
+      const uint32_t lds_addr = (uint32_t)(uintptr_t)DLC_LDS(dst) + uint32_t(tile_row_off(row));
       dma_row(src, uint32_t(lane) * 16u, lds_addr);
     }
   };
@@ -507,14 +513,14 @@ __global__ void __launch_bounds__(512) attend512_kernel(AttArgs a) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) o[nt][r] = 0.f;
   float mrun = -INFINITY, lrun = 0.f;
-  // per-lane LDS byte offsets within a tile (rows laid out by w4_row_off)
-  const uint32_t qk_off = uint32_t(w4_row_off(l32) + dh * 512 + 16 * g2);
+  // per-lane LDS byte offsets within a tile (rows laid out by tile_row_off)
+  const uint32_t qk_off = uint32_t(tile_row_off(l32) + dh * 512 + 16 * g2);
   uint32_t pv_off[2][2];
 #pragma unroll
   for (int u = 0; u < 2; ++u)
 #pragma unroll
     for (int h = 0; h < 2; ++h)
-      pv_off[u][h] = uint32_t(w4_row_off(16 * u + 8 * h + 4 * g2 + (i16 >> 2)) + dh * 512 + 32 * (G & 1) + 8 * (i16 & 3));
+      pv_off[u][h] = uint32_t(tile_row_off(16 * u + 8 * h + 4 * g2 + (i16 >> 2)) + dh * 512 + 32 * (G & 1) + 8 * (i16 & 3));
 
   auto tile_step = [&](const unsigned char* tile, unsigned char* next, int st, int64_t it) {
     wait_vmcnt(it + 1 < ntile ? RPW : 0);  // tile it has landed (tile it+1 may still fly)
@@ -664,272 +670,6 @@ __global__ void __launch_bounds__(512) attend512_kernel(AttArgs a) {
     a.lse[slot0 + hbase + l32] = lrun > 0.f ? (mrun + log2f(lrun)) * kLn2 : -INFINITY;
 }
 
-// ------------------------------------------------------------------ MFMA path, c = 512, four waves
-//
-// One wave per SIMD, each owning 32 heads over the whole of c, so no partial
-// S^T is exchanged between waves and the only barrier in the loop is the one
-// that hands a landed key tile to all four waves.  Per wave: Q^T for its 32
-// heads in 128 VGPRs, O (32 heads x 512 dims fp32) in 256 accumulators.
-// The loop is software-pipelined by one tile: iteration it runs Q.K^T of tile
-// it and P.V of tile it-1, so the softmax of tile it-1 has independent MFMA
-// work to hide under.  Tiles arrive by direct global->LDS loads, four stages,
-// two tiles in flight.
-//
-// LDS layout of a 32-key tile (gfx950 LDS: 64 banks of 4 bytes): key row r
-// starts at byte 1024*r + 16*t(r), t(4a+j) = 16a + a%4 + 4j.  Row starts then
-// differ mod 256 bytes so that
-//  * a ds_read_b128 of 16 consecutive rows at one 16-byte column (the Q.K^T
-//    A operand) touches 16 distinct 4-bank groups, and
-//  * a ds_read_b64_tr_b16 of 4 consecutive rows x 64 bytes (the P.V B
-//    operand, 32 lanes per pass) touches 4 disjoint 16-bank groups;
-// both are conflict-free.  A row is still 1 KB contiguous, as one direct load
-// writes it.
-
-__device__ __forceinline__ void wait_vmcnt_n(int n) {
-  if (n == 8)
-    __builtin_amdgcn_s_waitcnt(0x0F78);
-  else
-    __builtin_amdgcn_s_waitcnt(0x0F70);
-}
-
-template <bool GATHER>
-__global__ void __launch_bounds__(256) attend512w4_kernel(AttArgs a) {
-  constexpr int CD = 512, KS = 32, NT = 16;  // 16-dim Q.K^T steps; 32-dim output tiles
-  constexpr int NST = 4, RPW = 8, HPG = 128;
-  __shared__ __attribute__((aligned(1024))) unsigned char sT[NST * kW4TileBytes];
-  __shared__ int32_t sRow[GATHER ? kMaxGatherKeys : 1];
-
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int l32 = lane & 31, g2 = lane >> 5, G = lane >> 4, i16 = lane & 15;
-  const int64_t bq = blockIdx.y;
-  // XCD-aware order (see attend512_kernel)
-  const int64_t xcd = blockIdx.x & 7, rest = blockIdx.x >> 3;
-  const int64_t hg = rest % a.head_groups;
-  const int64_t split = (rest / a.head_groups) * 8 + xcd;
-  if (split >= a.splits) return;
-  const int64_t b = bq / a.n_q;
-  const int64_t nk = n_keys<GATHER>(a, bq);
-  const int64_t k0 = split * a.keys_per_split;
-  const int64_t k1 = min(nk, k0 + a.keys_per_split);
-  const int64_t hbase = hg * HPG + wave * 32;
-  const bool active = hbase < a.n_h;
-  const bf16_raw* kv = static_cast<const bf16_raw*>(a.kv) + b * a.cap * CD;
-  const int64_t ntile = k1 > k0 ? (k1 - k0 + 31) / 32 : 0;
-
-  if constexpr (GATHER) {
-    for (int64_t j = tid; j < k1 - k0; j += 256) sRow[j] = int32_t(key_row<true>(a, bq, k0 + j, k1));
-    __syncthreads();
-  }
-  // each wave moves rows RPW*wave .. +RPW-1 of a tile
-  auto issue = [&](int st, int64_t tl) {
-#pragma unroll
-    for (int r = 0; r < RPW; ++r) {
-      const int row = RPW * wave + r;
-      const int64_t j = tl * 32 + row;
-      int64_t gr;
-      if constexpr (GATHER) {
-        gr = (k0 + j < k1) ? sRow[j] : -1;
-      } else {
-        gr = (k0 + j < k1) ? k0 + j : -1;
-      }
-      gr = __builtin_amdgcn_readfirstlane(int(gr));
-      const bf16_raw* src = gr >= 0 ? kv + gr * CD : g_zero_row;
-      const uint32_t lds_addr = (uint32_t)(uintptr_t)DLC_LDS(sT) + uint32_t(st * kW4TileBytes + w4_row_off(row));
-      dma_row(src, uint32_t(lane) * 16u, lds_addr);
-    }
-  };
-  auto valid_mask = [&](int64_t tl) -> uint32_t {
-    const int64_t j = tl * 32 + l32;
-    bool v = k0 + j < k1;
-    if constexpr (GATHER) v = v && sRow[j] >= 0;
-    return uint32_t(__ballot(v) & 0xffffffffu);
-  };
-  // the first two tiles and Q are in flight together
-  if (ntile > 0) issue(0, 0);
-  if (ntile > 1) issue(1, 1);
-  // Q^T operand: lane holds head hbase + l32, dims 16*ks + 8*g2 .. +7
-  bf16x8 qf[KS];
-  {
-    // heads past n_h read head n_h-1: their S^T columns and outputs are never used
-    const int64_t h = min(hbase + l32, a.n_h - 1);
-    const bf16_raw* qp = static_cast<const bf16_raw*>(a.q) + (bq * a.n_h + h) * CD + g2 * 8;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) qf[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(qp + ks * 16));
-    // consume the Q loads here, so no wait for them is left inside the tile loop
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) asm volatile("" ::"v"(qf[ks]));
-  }
-  f32x16 o[NT];
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) o[nt][r] = 0.f;
-  float mrun = -INFINITY, lrun = 0.f;  // for head hbase + l32
-
-  // per-lane LDS byte offsets within a stage
-  const uint32_t qk_off = uint32_t(w4_row_off(l32) + 16 * g2);
-  uint32_t pv_off[2][2];
-#pragma unroll
-  for (int u = 0; u < 2; ++u)
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-      pv_off[u][h] = uint32_t(w4_row_off(16 * u + 8 * h + 4 * g2 + (i16 >> 2)) + 32 * (G & 1) + 8 * (i16 & 3));
-
-  f32x16 sp;  // S^T of the previous tile (scaled, masked logits once softmaxed)
-  uint32_t vprev = 0;
-  auto qk = [&](int st) {
-    f32x16 sx;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) sx[r] = 0.f;
-    const unsigned char* base = sT + st * kW4TileBytes + qk_off;
-    constexpr int QB = 2;
-    bf16x8 ka[QB], kb[QB];
-#pragma unroll
-    for (int u = 0; u < QB; ++u) ka[u] = *reinterpret_cast<const bf16x8*>(base + 32 * u);
-#pragma unroll
-    for (int k4 = 0; k4 < KS; k4 += QB) {
-      if (k4 + QB < KS) {
-#pragma unroll
-        for (int u = 0; u < QB; ++u) kb[u] = *reinterpret_cast<const bf16x8*>(base + 32 * (k4 + QB + u));
-      }
-      asm volatile("" ::: "memory");
-#pragma unroll
-      for (int u = 0; u < QB; ++u) sx = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[u], qf[k4 + u], sx, 0, 0, 0);
-#pragma unroll
-      for (int u = 0; u < QB; ++u) ka[u] = kb[u];
-    }
-    return sx;
-  };
-  auto pv = [&](int st, const bf16x8 (&pa)[2]) {
-    const unsigned char* base = sT + st * kW4TileBytes;
-    auto vfrag = [&](int nt, int u) {
-      const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (__attribute__((address_space(3))) s16x4*)DLC_LDS(base + pv_off[u][0] + 64 * nt));
-      const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (__attribute__((address_space(3))) s16x4*)DLC_LDS(base + pv_off[u][1] + 64 * nt));
-      return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-    };
-    bf16x8 va[2], vb[2];
-#pragma unroll
-    for (int u = 0; u < 2; ++u) va[u] = vfrag(0, u);
-#pragma unroll
-    for (int n1 = 0; n1 < NT; ++n1) {
-      if (n1 + 1 < NT) {
-#pragma unroll
-        for (int u = 0; u < 2; ++u) vb[u] = vfrag(n1 + 1, u);
-      }
-      asm volatile("" ::: "memory");
-#pragma unroll
-      for (int u = 0; u < 2; ++u) o[n1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa[u], va[u], o[n1], 0, 0, 0);
-#pragma unroll
-      for (int u = 0; u < 2; ++u) va[u] = vb[u];
-    }
-  };
-  // softmax of a finished S^T, in two parts.  prep: scaled, masked logits and
-  // their tile maximum; returns true when the running max must move by more
-  // than 8 (a factor 256) while O already holds mass, which needs O rescaled.
-  // Lazy running max: while it stays, p stays below 2^8 and the result is the
-  // same softmax.  The O rescale lives outside the tile loop, so the loop's
-  // register allocation never has to make room for it.
-  auto prep = [&](f32x16& sx, uint32_t vmask, float& tmax) -> bool {
-    tmax = -INFINITY;
-    const uint32_t vm = vmask >> (4 * g2);
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      sx[r] = ((vm >> (8 * (r >> 2) + (r & 3))) & 1u) ? sx[r] * a.scale_log2 : -INFINITY;
-      tmax = fmaxf(tmax, sx[r]);
-    }
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-    if (mrun == -INFINITY && tmax > -INFINITY) mrun = tmax;  // O is still zero
-    return __any(tmax > mrun + 8.f);
-  };
-  auto finish = [&](f32x16 sx, bf16x8 (&pa)[2]) {
-    const float mr = mrun == -INFINITY ? 0.f : mrun;  // a head with nothing valid yet: all p = 0
-    float psum = 0.f;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      sx[r] = exp2f(sx[r] - mr);  // exp2(-inf) = 0 for masked keys
-      psum += sx[r];
-    }
-    psum += __shfl_xor(psum, 32);
-    lrun += psum;
-#pragma unroll
-    for (int uu = 0; uu < 2; ++uu)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) pa[uu][e] = (__bf16)sx[8 * uu + e];
-  };
-
-  // Iteration it: softmax check of tile it-1, then (it < ntile) Q.K^T of tile
-  // it and P.V of tile it-1.  A needed rescale leaves the loop before anything
-  // else of that iteration ran; it resumes at the same it with the check done.
-  int64_t it = 0;
-  float tmax = -INFINITY;
-  bool prepped = false;
-  for (;;) {
-    bool rescale = false;
-    for (; it <= ntile; ++it) {
-      if (active && it > 0 && !prepped && prep(sp, vprev, tmax)) {
-        rescale = true;
-        break;
-      }
-      prepped = false;
-      if (it == ntile) break;
-      const int st = int(it & 3);
-      wait_vmcnt_n(it + 1 < ntile ? RPW : 0);  // this wave's rows of tile it have landed
-      lds_barrier();                           // ... every wave's; tile it-2's stage is free
-      if (it + 2 < ntile) issue(int((it + 2) & 3), it + 2);
-      const uint32_t vcur = valid_mask(it);
-      if (active) {
-        if (it > 0) {
-          bf16x8 pa[2];
-          finish(sp, pa);
-          sp = qk(st);
-          pv(int((it - 1) & 3), pa);
-        } else {
-          sp = qk(st);
-        }
-      }
-      vprev = vcur;
-    }
-    if (!rescale) break;
-    // the running max moves up to the tile maximum: O and l scale by alpha
-    const float mnew = fmaxf(mrun, tmax);
-    const float alpha = exp2f(mrun - mnew);
-    lrun *= alpha;
-    mrun = mnew;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const float al = __shfl(alpha, 8 * (r >> 2) + 4 * g2 + (r & 3));
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) o[nt][r] *= al;
-    }
-    prepped = true;
-  }
-  if (active && ntile > 0) {
-    bf16x8 pa[2];
-    finish(sp, pa);
-    pv(int((ntile - 1) & 3), pa);
-  }
-
-  if (!active) return;
-  const int64_t slot0 = (bq * a.splits + split) * a.n_h;
-#pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const int hr = 8 * (r >> 2) + 4 * g2 + (r & 3);
-    const float l = __shfl(lrun, hr);
-    const float inv = l > 0.f ? 1.f / l : 0.f;
-    const int64_t h = hbase + hr;
-    if (h < a.n_h) {
-      float* op = a.o + (slot0 + h) * CD + l32;
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) op[nt * 32] = o[nt][r] * inv;
-    }
-  }
-  if (g2 == 0 && a.lse && hbase + l32 < a.n_h)
-    a.lse[slot0 + hbase + l32] = lrun > 0.f ? (mrun + log2f(lrun)) * kLn2 : -INFINITY;
-}
-
 // ------------------------------------------------------------------ combine
 
 // One block per (query, head).  The split weights e^{lse_j - lse} are formed
@@ -1004,7 +744,7 @@ Plan plan(int dtype, int64_t BQ, int64_t n_h, int64_t c, int64_t nkeys) {
   int64_t s = ceil_div(kTargetWorkgroups, per_split);
   const int64_t smax = ceil_div(nkeys > 0 ? nkeys : 1, kMinKeysPerSplit);
   s = s < smax ? s : smax;
-  const int64_t smin = ceil_div(nkeys > 0 ? nkeys : 1, (c == 512 && DLC_ATT_W4) ? kMaxGatherKeys : 4096);  // a split's rows fit in LDS
+  const int64_t smin = ceil_div(nkeys > 0 ? nkeys : 1, c == 512 ? kMaxGatherKeys : 4096);  // a split's rows fit in LDS
   s = s < smin ? smin : s;
   s = s < 1 ? 1 : (s > kMaxSplits ? kMaxSplits : s);
   p.splits = s;
@@ -1052,11 +792,7 @@ int run_attend(const char* name, int dtype, AttArgs a, int64_t BQ, int64_t nkeys
     dim3 grid{(unsigned)(p.splits * p.head_groups), (unsigned)BQ, 1u};
     if (a.c == 128) hipLaunchKernelGGL((attend_mfma_kernel<128, GATHER>), grid, dim3(512), 0, s, a);
     if (a.c == 256) hipLaunchKernelGGL((attend_mfma_kernel<256, GATHER>), grid, dim3(512), 0, s, a);
-#if DLC_ATT_W4
-    if (a.c == 512) hipLaunchKernelGGL((attend512w4_kernel<GATHER>), grid, dim3(256), 0, s, a);
-#else
     if (a.c == 512) hipLaunchKernelGGL((attend512_kernel<GATHER>), grid, dim3(512), 0, s, a);
-#endif
   } else {
     DLC_REQUIRE(a.n_h <= 65535, DLC_E_UNSUPPORTED, "%s: n_h > 65535 on the VALU path", name);
     dim3 grid{(unsigned)p.splits, (unsigned)a.n_h, (unsigned)BQ};
