@@ -27,8 +27,12 @@
  *  - Device-side values (query positions t, top-k indices and counts) are
  *    clamped by the kernels to the ranges the host validated, so malformed
  *    device data yields wrong numbers, never an out-of-bounds access.
- *  - The calls hold no state and are reentrant; outputs are bitwise
- *    reproducible for identical inputs, shapes and device.
+ *  - The five calls and dlc_project hold no state and are reentrant (the
+ *    only state in the library is the per-thread timing hook of the
+ *    measurement section below).  Outputs are bitwise reproducible for
+ *    identical inputs, shapes and device; a compressed entry has the same
+ *    bits whether it was computed alone (i_end = i_begin + 1) or in a long
+ *    range.
  */
 #ifndef DLC_H
 #define DLC_H
