@@ -5,7 +5,7 @@
 // visible entries s < floor(t/m)).
 //
 // Pipeline per call (all on the caller's stream):
-//   1. clear      zero the first-digit histograms and the counters
+//   1. clear      zero the two digit histograms of every query
 //   2. scores     one pass over K^I: for bf16 with c^I % 32 == 0 the heads x keys
 //                 product runs on MFMA (v_mfma_f32_16x16x32_bf16) with the
 //                 queries held in registers; otherwise a VALU kernel.  Each
@@ -13,12 +13,15 @@
 //                 the order-preserving score key and adds its non-zero bins to
 //                 the query's histogram.
 //   3. filter     every workgroup finds the threshold bin T from that
-//                 histogram, appends entries above T to the selected list and
-//                 entries in T to the candidate list (wave-aggregated atomics).
-//   4. finish     one workgroup per query resolves the candidates with radix
-//                 passes over the remaining key bits and then the index (ties
-//                 go to the smaller index), sorts the k_eff winners ascending in
-//                 LDS and writes idx / count.
+//                 histogram and writes its chunk's entries above T (selected)
+//                 and in T (candidates, with their keys) to the chunk's own
+//                 segments in index order; the candidates' next 11 key bits go
+//                 into the query's second histogram.
+//   4. finish     one workgroup per query gathers the chunk lists, resolves the
+//                 candidates by radix passes over the remaining key bits and
+//                 then the index (ties go to the smaller index), starting from
+//                 the second histogram, and merges the two ascending lists into
+//                 idx / count.
 #include "common.hpp"
 
 namespace dlc {
@@ -36,10 +39,12 @@ struct IdxArgs {
   int64_t n_q, n_hI, cI, m, k, cap, t_max;
   float* scores;       // [BQ][score_ld]
   int64_t score_ld;
-  uint32_t* hist;      // [BQ][kBins] first-digit histogram
+  uint32_t* hist;      // [BQ][kBins] first-digit histogram (top 11 key bits)
+  uint32_t* hist2;     // [BQ][kBins] second digit (key bits 20..10) of the entries in bin T
   uint32_t* ccnt;      // [BQ][max_chunks][2] per-chunk counts: selected, candidates
   int32_t* sel;        // [BQ][cap] chunk c's selected entries start at c*keys_per_wg
   int32_t* cand;       // [BQ][cap] chunk c's candidates start at c*keys_per_wg
+  uint32_t* cand_kseg; // [BQ][cap] their score keys, same positions
   int32_t* cand_idx;   // [BQ][cap] compacted candidates when they overflow LDS
   uint32_t* cand_key;  // [BQ][cap] their score keys
   int32_t* idx;        // [BQ][k]
@@ -272,43 +277,106 @@ __device__ __forceinline__ uint32_t block_rank(bool pred, uint32_t* wtot, uint32
   return before + uint32_t(__popcll(mask & ((uint64_t(1) << lane) - 1)));
 }
 
+// Block-wide exclusive scan of one value per thread (blockDim.x = 256);
+// returns the block total.  wsum holds 4 words.  Ends synchronised.
+__device__ __forceinline__ uint32_t scan256(uint32_t v, uint32_t* wsum, uint32_t* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  uint32_t inc = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const uint32_t t = __shfl_up(inc, off);
+    if (lane >= off) inc += t;
+  }
+  if (lane == 63) wsum[wave] = inc;
+  __syncthreads();
+  uint32_t before = 0, all = 0;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const uint32_t x = wsum[w];
+    before += w < wave ? x : 0u;
+    all += x;
+  }
+  __syncthreads();
+  *total = all;
+  return before + inc - v;
+}
+
 // Every workgroup recomputes the threshold bin T of its query from the
 // first-digit histogram, then splits its own chunk of keys into "above T"
-// (selected for sure) and "in T" (candidates).  Both lists go to the chunk's
-// own segment, in ascending key order, and the two counts to the chunk's own
-// slot: no global atomics, and the result does not depend on scheduling.
+// (selected for sure) and "in T" (candidates, stored with their keys).  Thread
+// j takes entries 4j .. 4j+3 of each 1024-entry batch, so one scan of packed
+// counts orders both lists by index.  Both lists go to the chunk's own
+// segment and the two counts to the chunk's own slot: no global atomics for
+// the lists, and the result does not depend on scheduling.  The candidates'
+// second digit (key bits 20..10) is counted into the query's second
+// histogram, which is the first radix pass of the finish.
 __global__ void __launch_bounds__(256) filter_kernel(IdxArgs a) {
   __shared__ uint32_t h[kBins];
+  __shared__ uint32_t h2[kBins];
   __shared__ uint32_t scratch[18];
-  __shared__ uint32_t wtot[4];
+  __shared__ uint32_t wsum[4];
   const int64_t bq = blockIdx.y;
   const int64_t nvis = visible(a, bq);
   const int64_t keff = min(a.k, nvis);
   const int64_t s0 = int64_t(blockIdx.x) * a.keys_per_wg;
   if (keff == nvis || s0 >= nvis) return;  // keep-all and empty chunks need no filtering
   const int64_t s1 = min(nvis, s0 + a.keys_per_wg);
-  for (int i = threadIdx.x; i < kBins; i += blockDim.x) h[i] = a.hist[bq * kBins + i];
+  const float* sc = a.scores + bq * a.score_ld;
+  // the first batch of scores is in flight while the threshold is found
+  auto load4 = [&](int64_t base, float* v) {
+    const int64_t s = base + 4 * threadIdx.x;
+    if (s + 3 < s1 && (reinterpret_cast<uintptr_t>(sc + s) & 15) == 0) {
+      const float4 x = *reinterpret_cast<const float4*>(sc + s);
+      v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = s + e < s1 ? sc[s + e] : 0.f;
+    }
+  };
+  float v[4];
+  load4(s0, v);
+  for (int i = threadIdx.x; i < kBins; i += blockDim.x) {
+    h[i] = a.hist[bq * kBins + i];
+    h2[i] = 0;
+  }
   __syncthreads();
   int T;
   uint32_t above;
   find_threshold(h, kBins, uint32_t(keff), scratch, &T, &above);
 
-  const float* sc = a.scores + bq * a.score_ld;
   int32_t* sel = a.sel + bq * a.cap + s0;
   int32_t* cand = a.cand + bq * a.cap + s0;
+  uint32_t* ckey = a.cand_kseg + bq * a.cap + s0;
   uint32_t nsel = 0, ncand = 0;
-  for (int64_t base = s0; base < s1; base += blockDim.x) {
-    const int64_t s = base + threadIdx.x;
-    int d = -1;
-    if (s < s1) d = int(order_key(sc[s]) >> kShift1);
-    uint32_t t1, t2;
-    const uint32_t r1 = block_rank(d > T, wtot, &t1);
-    if (d > T) sel[nsel + r1] = int32_t(s);
-    const uint32_t r2 = block_rank(d == T, wtot, &t2);
-    if (d == T) cand[ncand + r2] = int32_t(s);
-    nsel += t1;
-    ncand += t2;
+  for (int64_t base = s0; base < s1; base += 4 * blockDim.x) {
+    if (base != s0) load4(base, v);
+    const int64_t sb = base + 4 * threadIdx.x;
+    uint32_t key[4], packed = 0;
+    int d[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      key[e] = order_key(v[e]);
+      d[e] = sb + e < s1 ? int(key[e] >> kShift1) : -1;
+      packed += d[e] > T ? 1u : 0u;
+      packed += d[e] == T ? 0x10000u : 0u;
+    }
+    uint32_t tot;
+    const uint32_t ex = scan256(packed, wsum, &tot);
+    uint32_t ps = nsel + (ex & 0xffffu), pc = ncand + (ex >> 16);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      if (d[e] > T) sel[ps++] = int32_t(sb + e);
+      if (d[e] == T) {
+        cand[pc] = int32_t(sb + e);
+        ckey[pc] = key[e];
+        ++pc;
+        atomicAdd(&h2[(key[e] >> 10) & 0x7ffu], 1u);
+      }
+    }
+    nsel += tot & 0xffffu;
+    ncand += tot >> 16;
   }
+  flush_hist(h2, a.hist2 + bq * kBins);
   if (threadIdx.x == 0) {
     a.ccnt[(bq * a.max_chunks + blockIdx.x) * 2 + 0] = nsel;
     a.ccnt[(bq * a.max_chunks + blockIdx.x) * 2 + 1] = ncand;
@@ -330,40 +398,55 @@ __device__ __forceinline__ uint64_t cand_key(uint32_t key, int32_t s) {
   return (uint64_t(key & 0x1fffffu) << 32) | uint64_t(0xffffffffu - uint32_t(s));
 }
 
-// block-wide exclusive scan of v[0 .. n) in place (n <= 4 * blockDim.x); returns the total
-__device__ uint32_t block_exclusive_scan(uint32_t* v, int n, uint32_t* wsum) {
-  const int per = 4;
-  const int lo = threadIdx.x * per;
+// Block-wide exclusive scans of two arrays v[0 .. n) and w[0 .. n) in place;
+// the totals come back through tv and tw.  Thread j owns the runs at
+// [j*per, (j+1)*per), per = ceil(n / blockDim.x); wsum holds 2*blockDim.x/64
+// words.  Ends synchronised.
+__device__ void block_exclusive_scan2(uint32_t* v, uint32_t* w, int n, uint32_t* wsum, uint32_t* tv,
+                                      uint32_t* tw) {
+  const int per = (n + int(blockDim.x) - 1) / int(blockDim.x);
+  const int lo = threadIdx.x * per, hi = min(n, lo + per);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nwaves = blockDim.x >> 6;
-  uint32_t loc[per];
-  uint32_t mine = 0;
-#pragma unroll
-  for (int i = 0; i < per; ++i) {
-    loc[i] = (lo + i < n) ? v[lo + i] : 0u;
-    mine += loc[i];
+  uint32_t mv = 0, mw = 0;
+  for (int i = lo; i < hi; ++i) {
+    mv += v[i];
+    mw += w[i];
   }
-  uint32_t inc = mine;
+  uint32_t iv = mv, iw = mw;
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) {
-    const uint32_t t = __shfl_up(inc, off);
-    if (lane >= off) inc += t;
+    const uint32_t a = __shfl_up(iv, off), b = __shfl_up(iw, off);
+    if (lane >= off) {
+      iv += a;
+      iw += b;
+    }
   }
-  if (lane == 63) wsum[wave] = inc;
-  __syncthreads();
-  uint32_t before = 0, total = 0;
-  for (int w = 0; w < nwaves; ++w) {
-    const uint32_t x = wsum[w];
-    if (w < wave) before += x;
-    total += x;
-  }
-  uint32_t run = before + inc - mine;
-#pragma unroll
-  for (int i = 0; i < per; ++i) {
-    if (lo + i < n) v[lo + i] = run;
-    run += loc[i];
+  if (lane == 63) {
+    wsum[wave] = iv;
+    wsum[nwaves + wave] = iw;
   }
   __syncthreads();
-  return total;
+  uint32_t bv = 0, bw = 0, sv = 0, sw = 0;
+  for (int k = 0; k < nwaves; ++k) {
+    const uint32_t x = wsum[k], y = wsum[nwaves + k];
+    if (k < wave) {
+      bv += x;
+      bw += y;
+    }
+    sv += x;
+    sw += y;
+  }
+  uint32_t rv = bv + iv - mv, rw = bw + iw - mw;
+  for (int i = lo; i < hi; ++i) {
+    const uint32_t x = v[i], y = w[i];
+    v[i] = rv;
+    w[i] = rw;
+    rv += x;
+    rw += y;
+  }
+  __syncthreads();
+  *tv = sv;
+  *tw = sw;
 }
 
 // number of entries of the ascending list l[0 .. n) that are < x
@@ -383,7 +466,7 @@ __device__ __forceinline__ uint32_t lower_bound(const int32_t* l, uint32_t n, in
 __global__ void __launch_bounds__(1024) finish_kernel(IdxArgs a) {
   __shared__ uint32_t h[kBins];
   __shared__ uint32_t scratch[18];
-  __shared__ uint32_t wsum[16];
+  __shared__ uint32_t wsum[32];
   __shared__ uint32_t off_sel[kMaxChunks], off_cand[kMaxChunks];
   __shared__ int32_t lsel[kMaxK], lc2[kMaxK];
   __shared__ int32_t lc_idx[kLdsCand];
@@ -404,9 +487,10 @@ __global__ void __launch_bounds__(1024) finish_kernel(IdxArgs a) {
     off_cand[c] = cc[2 * c + 1];
   }
   __syncthreads();
-  const uint32_t n_sel = min(block_exclusive_scan(off_sel, nch, wsum), uint32_t(keff));
-  const uint32_t n_cand = min(block_exclusive_scan(off_cand, nch, wsum), uint32_t(nvis));
-  const float* sc = a.scores + bq * a.score_ld;
+  uint32_t tsel, tcand;
+  block_exclusive_scan2(off_sel, off_cand, nch, wsum, &tsel, &tcand);
+  const uint32_t n_sel = min(tsel, uint32_t(keff));
+  const uint32_t n_cand = min(tcand, uint32_t(nvis));
   const bool in_lds = n_cand <= uint32_t(kLdsCand);
   int32_t* cidx = in_lds ? lc_idx : a.cand_idx + bq * a.cap;
   uint32_t* ckey = in_lds ? lc_key : a.cand_key + bq * a.cap;
@@ -420,15 +504,43 @@ __global__ void __launch_bounds__(1024) finish_kernel(IdxArgs a) {
     }
     return lo;
   };
-  for (uint32_t i = threadIdx.x; i < n_sel; i += blockDim.x) {
-    const int c = chunk_of(off_sel, i);
-    lsel[i] = a.sel[bq * a.cap + int64_t(c) * a.keys_per_wg + (i - off_sel[c])];
+  // four entries per thread per round, their loads in flight together
+  constexpr int G = 4;
+  for (uint32_t i0 = threadIdx.x; i0 < n_sel; i0 += G * blockDim.x) {
+    int32_t v[G];
+#pragma unroll
+    for (int u = 0; u < G; ++u) {
+      const uint32_t i = i0 + u * blockDim.x;
+      if (i < n_sel) {
+        const int c = chunk_of(off_sel, i);
+        v[u] = a.sel[bq * a.cap + int64_t(c) * a.keys_per_wg + (i - off_sel[c])];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < G; ++u)
+      if (i0 + u * blockDim.x < n_sel) lsel[i0 + u * blockDim.x] = v[u];
   }
-  for (uint32_t i = threadIdx.x; i < n_cand; i += blockDim.x) {
-    const int c = chunk_of(off_cand, i);
-    const int32_t sidx = a.cand[bq * a.cap + int64_t(c) * a.keys_per_wg + (i - off_cand[c])];
-    cidx[i] = sidx;
-    ckey[i] = order_key(sc[sidx]);
+  for (uint32_t i0 = threadIdx.x; i0 < n_cand; i0 += G * blockDim.x) {
+    int32_t vi[G];
+    uint32_t vk[G];
+#pragma unroll
+    for (int u = 0; u < G; ++u) {
+      const uint32_t i = i0 + u * blockDim.x;
+      if (i < n_cand) {
+        const int c = chunk_of(off_cand, i);
+        const int64_t at = bq * a.cap + int64_t(c) * a.keys_per_wg + (i - off_cand[c]);
+        vi[u] = a.cand[at];
+        vk[u] = a.cand_kseg[at];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < G; ++u) {
+      const uint32_t i = i0 + u * blockDim.x;
+      if (i < n_cand) {
+        cidx[i] = vi[u];
+        ckey[i] = vk[u];
+      }
+    }
   }
   __threadfence_block();
   __syncthreads();
@@ -441,13 +553,19 @@ __global__ void __launch_bounds__(1024) finish_kernel(IdxArgs a) {
     const int shift = pass_shift(pass), bits = pass_bits(pass);
     const uint32_t dmask = (1u << bits) - 1u;
     const int nb = 1 << bits;
-    for (int i = threadIdx.x; i < kBins; i += blockDim.x) h[i] = 0;
-    __syncthreads();
-    for (uint32_t i = threadIdx.x; i < n_cand; i += blockDim.x) {
-      const uint64_t ck = cand_key(ckey[i], cidx[i]);
-      if ((ck & pmask) == pval) atomicAdd(&h[(ck >> shift) & dmask], 1u);
+    if (pass == 0) {
+      // the filter already counted the candidates' first composite digit
+      for (int i = threadIdx.x; i < kBins; i += blockDim.x) h[i] = a.hist2[bq * kBins + i];
+      __syncthreads();
+    } else {
+      for (int i = threadIdx.x; i < kBins; i += blockDim.x) h[i] = 0;
+      __syncthreads();
+      for (uint32_t i = threadIdx.x; i < n_cand; i += blockDim.x) {
+        const uint64_t ck = cand_key(ckey[i], cidx[i]);
+        if ((ck & pmask) == pval) atomicAdd(&h[(ck >> shift) & dmask], 1u);
+      }
+      __syncthreads();
     }
-    __syncthreads();
     int D;
     uint32_t above;
     find_threshold(h, nb < 1024 ? 1024 : nb, need, scratch, &D, &above);
@@ -485,7 +603,7 @@ __global__ void __launch_bounds__(1024) finish_kernel(IdxArgs a) {
 // ---------------------------------------------------------------- host
 
 struct WsLayout {
-  size_t scores, hist, ccnt, sel, cand, cand_idx, cand_key, total;
+  size_t scores, hist, ccnt, sel, cand, cand_kseg, cand_idx, cand_key, total;
 };
 
 // keys per scores/filter workgroup: about 1024 workgroups over the batch, at
@@ -504,10 +622,11 @@ WsLayout ws_layout(int64_t B, int64_t n_q, int64_t cap, int64_t k, bool own_scor
   (void)k;
   WsLayout L{};
   size_t off = 0;
-  L.hist = off;      off = align_up(off + BQ * kBins * 4, 256);
+  L.hist = off;      off = align_up(off + BQ * kBins * 2 * 4, 256);  // hist, then hist2
   L.ccnt = off;      off = align_up(off + BQ * kMaxChunks * 2 * 4, 256);
   L.sel = off;       off = align_up(off + BQ * size_t(cap) * 4, 256);
   L.cand = off;      off = align_up(off + BQ * size_t(cap) * 4, 256);
+  L.cand_kseg = off; off = align_up(off + BQ * size_t(cap) * 4, 256);
   L.cand_idx = off;  off = align_up(off + BQ * size_t(cap) * 4, 256);
   L.cand_key = off;  off = align_up(off + BQ * size_t(cap) * 4, 256);
   L.scores = off;
@@ -556,16 +675,18 @@ int csa_index_topk(int dtype, int64_t B, int64_t n_q, int64_t n_hI, int64_t cI, 
   a.scores = scores ? scores : reinterpret_cast<float*>(w + L.scores);
   a.score_ld = cap;
   a.hist = reinterpret_cast<uint32_t*>(w + L.hist);
+  a.hist2 = a.hist + size_t(B * n_q) * kBins;
   a.ccnt = reinterpret_cast<uint32_t*>(w + L.ccnt);
   a.sel = reinterpret_cast<int32_t*>(w + L.sel);
   a.cand = reinterpret_cast<int32_t*>(w + L.cand);
+  a.cand_kseg = reinterpret_cast<uint32_t*>(w + L.cand_kseg);
   a.cand_idx = reinterpret_cast<int32_t*>(w + L.cand_idx);
   a.cand_key = reinterpret_cast<uint32_t*>(w + L.cand_key);
   a.max_chunks = kMaxChunks;
   a.idx = idx; a.count = count;
   const int64_t BQ = B * n_q;
 
-  int rc = fill_u32(a.hist, 0, int64_t(BQ * kBins), s);
+  int rc = fill_u32(a.hist, 0, int64_t(BQ * kBins * 2), s);
   if (rc) return rc;
 
   const int64_t vis_max = t_max / m;
