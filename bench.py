@@ -32,7 +32,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "decode query-tokens/s per CSA+HCA layer at 1M ctx; achieved HBM GB/s vs peak"
 PEAK_HBM_GBS = 8000.0
-SCORES_KERNEL = "scores_mfma_kernel<4, 4>"
+SCORES_KERNEL = "scores_mfma_kernel<4, 4, 4>"
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "indexer_scores_hybrid1m_counters.json")
 
 

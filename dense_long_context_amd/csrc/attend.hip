@@ -388,17 +388,6 @@ __device__ __forceinline__ void wait_vmcnt(int n) {
 }
 
 
-// One direct global->LDS load of a 1 KB row: lane i moves the 16 bytes at
-// row + lane_off (lane_off = 16*i) to LDS byte address lds_addr + 16*i.  The
-// row address and the LDS address are wave-uniform (SGPRs).  Issued through
-// asm so the compiler does not fold it into its own wait bookkeeping (it would
-// drain every tile in flight before each LDS read); the kernel waits for it
-// explicitly with wait_vmcnt.  The instruction writes no VGPR.
-__device__ __forceinline__ void dma_row(const void* row, uint32_t lane_off, uint32_t lds_addr) {
-  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(lane_off), "s"(row), "s"(lds_addr)
-               : "memory", "m0");
-}
-
 __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_s_waitcnt(0xC07F);  // LDS and scalar-memory counter only
   __builtin_amdgcn_s_barrier();
@@ -421,7 +410,6 @@ __device__ __forceinline__ constexpr int tile_row_off(int r) {
 }
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
-#define DLC_LDS(p) ((__attribute__((address_space(3))) void*)(p))
 
 template <bool GATHER>
 __global__ void __launch_bounds__(512) attend512_kernel(AttArgs a) {

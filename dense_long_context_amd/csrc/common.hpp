@@ -93,6 +93,28 @@ __device__ __forceinline__ uint32_t order_key(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// LDS pointer of a __shared__ object (address space 3)
+#define DLC_LDS(p) ((__attribute__((address_space(3))) void*)(p))
+
+// One direct global->LDS load (global_load_lds_dwordx4): every active lane i
+// moves the 16 bytes at base + lane_off to LDS byte address lds_addr + 16*i.
+// base and lds_addr are wave-uniform (SGPRs), lane_off a per-lane unsigned
+// byte offset.  Issued through asm so the compiler does not fold it into its
+// own wait bookkeeping (it would drain every load in flight before each LDS
+// read); the caller waits for it with an explicit s_waitcnt vmcnt.  The
+// instruction writes no VGPR.
+__device__ __forceinline__ void dma_row(const void* base, uint32_t lane_off, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(lane_off), "s"(base), "s"(lds_addr)
+               : "memory", "m0");
+}
+
+// s_waitcnt vmcnt(N) alone (expcnt and lgkmcnt left at their maxima)
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
+}
+
 // Records the caller's armed events around a stage's launches (see
 // dlc_timing_arm); a no-op unless armed.
 class StageTimer {

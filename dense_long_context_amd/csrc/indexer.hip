@@ -111,21 +111,27 @@ __global__ void __launch_bounds__(256) scores_valu_kernel(IdxArgs a) {
 // ---------------------------------------------------------------- scores (MFMA)
 //
 // One wave scores 16 keys per step: D[16 heads][16 keys] += Q[16 heads][32 dims]
-// x K^T[32 dims][16 keys] for every head tile and 32-dim step.  Lane l holds
-// head/key l%16 of the A/B operands and dims 8*(l/16) .. +7 of each 32-dim
-// step; the result holds key l%16 and heads 4*(l/16) .. +3.  The head sum is
-// finished with two cross-lane adds.  Queries stay in registers for the whole
-// pass; keys stream from HBM with PF tiles per wave in flight (each wave's
-// loads for tile t+PF go out right after tile t's products).
+// x K^T[32 dims][16 keys] (v_mfma_f32_16x16x32_bf16) for every head tile and
+// 32-dim step.  Lane l holds head/key l%16 of the A/B operands and dims
+// 8*(l/16) .. +7 of each 32-dim step; the result holds key l%16 and heads
+// 4*(l/16) .. +3, and the head sum is finished with two cross-lane adds.
+// Queries stay in registers for the whole pass.  Key tiles (16 keys,
+// 16*2*c^I bytes) arrive by direct global->LDS loads, one instruction moving
+// 1 KB of consecutive rows, so HBM sees whole lines.  Each wave streams its
+// own tiles through a ring of NS LDS stages with NS-1 tiles in flight, and
+// only it reads them, so the loop has no barrier.  Within a row, 16-byte chunk c is stored at slot
+// c ^ (row % chunks): the 16 rows that one ds_read_b128 pass reads at the
+// same chunk then fall on distinct banks (64 banks of 4 bytes).
 
-#ifndef DLC_INDEXER_PREFETCH
-#define DLC_INDEXER_PREFETCH 2
-#endif
-constexpr int PF = DLC_INDEXER_PREFETCH;  // key tiles in flight per wave
-
-template <int HT, int KT>
+template <int HT, int KT, int NS>
 __global__ void __launch_bounds__(256) scores_mfma_kernel(IdxArgs a) {
+  constexpr int ROWB = KT * 64;     // bytes per key row (2 * c^I)
+  constexpr int CPR = KT * 4;       // 16-byte chunks per row
+  constexpr int TILEB = 16 * ROWB;  // one tile: 16 keys
+  constexpr int RPI = 1024 / ROWB;  // rows per 1 KB load (KT loads per tile)
+  static_assert(RPI * KT == 16, "tile geometry");
   __shared__ uint32_t hist[kBins];
+  __shared__ __attribute__((aligned(1024))) unsigned char sK[4][NS][TILEB];
   const int64_t bq = blockIdx.y;
   const int64_t nvis = visible(a, bq);
   const int64_t s0 = int64_t(blockIdx.x) * a.keys_per_wg;
@@ -133,21 +139,48 @@ __global__ void __launch_bounds__(256) scores_mfma_kernel(IdxArgs a) {
   const int64_t s1 = min(nvis, s0 + a.keys_per_wg);
   for (int i = threadIdx.x; i < kBins; i += blockDim.x) hist[i] = 0;
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r16 = lane & 15, g = lane >> 4;
   const int cI = KT * 32;
 
-  // queries: A operand, rows = heads
+  const int64_t b = bq / a.n_q;
+  const bf16_raw* K = static_cast<const bf16_raw*>(a.KI) + b * a.cap * cI;
+  const int64_t ntiles = (s1 - s0 + 15) / 16;
+  // this wave's tiles: wave, wave+4, ... (the four waves stream one region together)
+  const int64_t my_tiles = ntiles > wave ? (ntiles - wave + 3) / 4 : 0;
+  // load j of a tile: lane -> row rho = j*RPI + lane/CPR, slot lane%CPR, which
+  // holds chunk slot ^ (rho % CPR) of that row; rows past the chunk's end
+  // repeat its last visible row
+  auto issue = [&](int64_t it, int st) {
+    const int64_t row0 = s0 + (wave + 4 * it) * 16;  // < s1
+    const bf16_raw* base = K + row0 * cI;
+#pragma unroll
+    for (int j = 0; j < KT; ++j) {
+      const int rho = j * RPI + lane / CPR;
+      const int chunk = (lane % CPR) ^ (rho % CPR);
+      const int64_t row = min(row0 + rho, s1 - 1);
+      const uint32_t off = uint32_t((row - row0) * ROWB + chunk * 16);
+      const uint32_t lds = (uint32_t)(uintptr_t)DLC_LDS(&sK[wave][st][0]) + uint32_t(j * 1024);
+      dma_row(base, off, lds);
+    }
+  };
+#pragma unroll
+  for (int p = 0; p < NS - 1; ++p)
+    if (p < my_tiles) issue(p, p);
+
+  // queries: A operand, rows = heads (loaded after the first tiles are in flight)
   bf16x8 qf[HT][KT];
   const bf16_raw* qg = static_cast<const bf16_raw*>(a.qI) + bq * a.n_hI * cI;
 #pragma unroll
   for (int ht = 0; ht < HT; ++ht) {
-    const int h = ht * 16 + r16;
+    // heads past n_hI read head n_hI-1 and are then zeroed (their weight is 0 too)
+    const bool pad = ht * 16 + r16 >= a.n_hI;
+    const int h = min(ht * 16 + r16, int(a.n_hI) - 1);
 #pragma unroll
     for (int kt = 0; kt < KT; ++kt) {
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (h < a.n_hI) v = *reinterpret_cast<const uint4*>(qg + h * cI + kt * 32 + g * 8);
-      qf[ht][kt] = __builtin_bit_cast(bf16x8, v);
+      const uint4 v = *reinterpret_cast<const uint4*>(qg + h * cI + kt * 32 + g * 8);
+      qf[ht][kt] = __builtin_bit_cast(bf16x8, pad ? make_uint4(0, 0, 0, 0) : v);
     }
   }
   float wv[HT][4];
@@ -158,53 +191,54 @@ __global__ void __launch_bounds__(256) scores_mfma_kernel(IdxArgs a) {
       const int h = ht * 16 + g * 4 + r;
       wv[ht][r] = h < a.n_hI ? a.wI[bq * a.n_hI + h] : 0.f;
     }
-  __syncthreads();
+#pragma unroll
+  for (int ht = 0; ht < HT; ++ht)
+#pragma unroll
+    for (int kt = 0; kt < KT; ++kt) asm volatile("" ::"v"(qf[ht][kt]));
+  __syncthreads();  // hist cleared (and the query loads, with every tile load before them, done)
 
-  const int64_t b = bq / a.n_q;
-  const bf16_raw* K = static_cast<const bf16_raw*>(a.KI) + b * a.cap * cI;
-  const int64_t ntiles = (s1 - s0 + 15) / 16;
-  // wave w takes tiles w, w+4, w+8, ...; a ring of PF tiles is in flight
-  uint4 ring[PF][KT];
-  auto load_tile = [&](int64_t tl, uint4* dst) {
-    int64_t row = s0 + tl * 16 + r16;
-    row = row < s1 ? row : s1 - 1;  // rows past the end repeat the last visible row
-    const bf16_raw* p = K + row * cI + g * 8;
+  for (int64_t it = 0; it < my_tiles; ++it) {
+    const int st = int(it % NS);
+    // the stage tile it+NS-1 goes to was read in iteration it-1, whose
+    // fragments have been consumed by its MFMAs
+    const int64_t nxt = it + NS - 1;
+    int after;  // tiles issued after tile it
+    if (nxt < my_tiles) {
+      issue(nxt, int(nxt % NS));
+      after = NS - 1;
+    } else {
+      after = int(my_tiles - 1 - it);
+    }
+    // tile it has landed once at most `after` tiles' loads are outstanding
+    if (after >= NS - 1) wait_vm<(NS - 1) * KT>();
+    else if (after == 2) wait_vm<2 * KT>();
+    else if (after == 1) wait_vm<KT>();
+    else wait_vm<0>();
+    asm volatile("" ::: "memory");
+    const unsigned char* tile = &sK[wave][st][0];
+    f32x4 acc[HT];
 #pragma unroll
-    for (int kt = 0; kt < KT; ++kt) dst[kt] = *reinterpret_cast<const uint4*>(p + kt * 32);
-  };
+    for (int ht = 0; ht < HT; ++ht) acc[ht] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int p = 0; p < PF; ++p)
-    if (wave + 4 * p < ntiles) load_tile(wave + 4 * p, ring[p]);
-  for (int64_t base = wave; base < ntiles; base += 4 * PF) {
+    for (int kt = 0; kt < KT; ++kt) {
+      const int slot = (4 * kt + g) ^ (r16 % CPR);
+      const bf16x8 kb = *reinterpret_cast<const bf16x8*>(tile + r16 * ROWB + slot * 16);
 #pragma unroll
-    for (int p = 0; p < PF; ++p) {
-      const int64_t tile = base + 4 * p;
-      if (tile < ntiles) {
-        f32x4 acc[HT];
+      for (int ht = 0; ht < HT; ++ht)
+        acc[ht] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qf[ht][kt], kb, acc[ht], 0, 0, 0);
+    }
+    float part = 0.f;
 #pragma unroll
-        for (int ht = 0; ht < HT; ++ht) acc[ht] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int ht = 0; ht < HT; ++ht)
 #pragma unroll
-        for (int kt = 0; kt < KT; ++kt) {
-          const bf16x8 kb = __builtin_bit_cast(bf16x8, ring[p][kt]);
-#pragma unroll
-          for (int ht = 0; ht < HT; ++ht)
-            acc[ht] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qf[ht][kt], kb, acc[ht], 0, 0, 0);
-        }
-        if (tile + 4 * PF < ntiles) load_tile(tile + 4 * PF, ring[p]);
-        float part = 0.f;
-#pragma unroll
-        for (int ht = 0; ht < HT; ++ht)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) part = fmaf(wv[ht][r], fmaxf(acc[ht][r], 0.f), part);
-        part += __shfl_xor(part, 16);
-        part += __shfl_xor(part, 32);
-        const int64_t s = s0 + tile * 16 + r16;
-        if (g == 0 && s < s1) {
-          const float score = canon_zero(part);
-          a.scores[bq * a.score_ld + s] = score;
-          atomicAdd(&hist[order_key(score) >> kShift1], 1u);
-        }
-      }
+      for (int r = 0; r < 4; ++r) part = fmaf(wv[ht][r], fmaxf(acc[ht][r], 0.f), part);
+    part += __shfl_xor(part, 16);
+    part += __shfl_xor(part, 32);
+    const int64_t s = s0 + (wave + 4 * it) * 16 + r16;
+    if (g == 0 && s < s1) {
+      const float score = canon_zero(part);
+      a.scores[bq * a.score_ld + s] = score;
+      atomicAdd(&hist[order_key(score) >> kShift1], 1u);
     }
   }
   flush_hist(hist, a.hist + bq * kBins);
@@ -606,14 +640,20 @@ struct WsLayout {
   size_t scores, hist, ccnt, sel, cand, cand_kseg, cand_idx, cand_key, total;
 };
 
-// keys per scores/filter workgroup: about 1024 workgroups over the batch, at
-// most kMaxChunks chunks per query
+// keys per scores/filter workgroup: a multiple of 64 chosen so that the whole
+// batch takes about kScoreWorkgroups workgroups - the number that are resident
+// at once (2 per CU for the scores kernel, whose key stages take 64 KB of
+// LDS), so there is no partial second round - and at most kMaxChunks chunks
+// per query
+#ifndef DLC_SCORES_WGS
+#define DLC_SCORES_WGS 512
+#endif
+constexpr int64_t kScoreWorkgroups = DLC_SCORES_WGS;
 int64_t keys_per_wg(int64_t BQ, int64_t vis_max) {
-  const int64_t tiles = ceil_div(vis_max, 16) * BQ;
-  int64_t tpw = tiles / (1024 * 4);
-  tpw = tpw < 1 ? 1 : (tpw > 16 ? 16 : tpw);
-  int64_t kpw = tpw * 64;
-  const int64_t floor_kpw = ceil_div(ceil_div(vis_max > 0 ? vis_max : 1, kMaxChunks), 64) * 64;
+  const int64_t vis = vis_max > 0 ? vis_max : 1;
+  int64_t kpw = ceil_div(ceil_div(vis * BQ, kScoreWorkgroups), 64) * 64;
+  kpw = kpw < 64 ? 64 : kpw;
+  const int64_t floor_kpw = ceil_div(ceil_div(vis, kMaxChunks), 64) * 64;
   return kpw > floor_kpw ? kpw : floor_kpw;
 }
 
@@ -701,7 +741,7 @@ int csa_index_topk(int dtype, int64_t B, int64_t n_q, int64_t n_hI, int64_t cI, 
     if (mfma) {
       const int HT = int(ceil_div(n_hI, 16)), KT = int(cI / 32);
 #define DLC_SCORES(ht, kt) \
-  if (HT == ht && KT == kt) hipLaunchKernelGGL((scores_mfma_kernel<ht, kt>), grid, dim3(256), 0, s, a);
+  if (HT == ht && KT == kt) hipLaunchKernelGGL((scores_mfma_kernel<ht, kt, 4>), grid, dim3(256), 0, s, a);
       DLC_SCORES(1, 1) DLC_SCORES(1, 2) DLC_SCORES(1, 4) DLC_SCORES(1, 8)
       DLC_SCORES(2, 1) DLC_SCORES(2, 2) DLC_SCORES(2, 4) DLC_SCORES(2, 8)
       DLC_SCORES(3, 1) DLC_SCORES(3, 2) DLC_SCORES(3, 4) DLC_SCORES(3, 8)
