@@ -28,7 +28,11 @@ Readings of points the pages leave open (each listed in the design notes):
 * top-k ties: larger score first, then smaller index; -0.0 equals +0.0;
 * nothing visible: output 0 and log-sum-exp -inf;
 * both attentions scale logits by 1/sqrt(c) ([Scratch] §8, applied to HCA
-  through the unified operator of §11); the indexer is unscaled (§6.4).
+  through the unified operator of §11); the indexer is unscaled (§6.4);
+* the sliding-window branch ([Evolution] §6.1-6.2, n_win = 128 per [Stack]
+  §4) covers the n_win most recent tokens including the query token itself,
+  uses the same scale, and is joined to the compressed branch as one
+  attention over both key sets (no entry is removed from either set).
 """
 
 from __future__ import annotations
@@ -54,6 +58,9 @@ __all__ = [
     "mqa_attend",
     "csa_attend",
     "hca_attend",
+    "window_positions",
+    "window_attend",
+    "merge_lse",
     "split_heads",
     "queries_from_hidden",
     "decode_chain",
@@ -271,6 +278,47 @@ def hca_attend(q, Chca, t: int, m_prime: int, scale=None):
     """Dense HCA attention over every visible HCA entry ([Scratch] §10)."""
     Chca = f64(Chca)
     return mqa_attend(q, Chca[:hca_visible(t, m_prime)], scale)
+
+
+# --------------------------------------------------------------------------
+# sliding-window branch ([Evolution] §6.1 and §6.2, "sliding window path";
+# [Stack] §4 gives n_win = 128 for V4-Pro)
+# --------------------------------------------------------------------------
+
+def window_positions(t: int, n_win: int) -> np.ndarray:
+    """Token positions of query t's sliding window: the n_win most recent
+    tokens up to and including t, i.e. max(0, t - n_win + 1) ... t.
+    ([Evolution] writes the same set 1-based as max(1, t-n_win+1) ... t.)"""
+    return np.arange(max(0, t - n_win + 1), t + 1, dtype=np.int64)
+
+
+def window_attend(q, Cwin, t: int, n_win: int, scale=None):
+    """Shared-KV MQA over the raw window entries c^window_p = h_p W^{window,KV}
+    for p in the window of t ([Evolution] §6.1).  Cwin is indexed by token
+    position: row p holds c^window_p."""
+    Cwin = f64(Cwin)
+    return mqa_attend(q, Cwin[window_positions(t, n_win)], scale)
+
+
+def merge_lse(o1, lse1, o2, lse2):
+    """Attention over the union of two disjoint key sets, from each part's
+    normalised output and log-sum-exp: the pages join the window entries to the
+    compressed ones by concatenation before one shared-KV MQA ([Evolution]
+    §6.1, §6.2); since softmax sums over keys, that MQA equals
+        lse = log(e^lse1 + e^lse2),  o = e^(lse1 - lse) o1 + e^(lse2 - lse) o2.
+    An empty part has lse = -inf and contributes nothing."""
+    o1, o2 = f64(o1), f64(o2)
+    l1, l2 = f64(lse1), f64(lse2)
+    m = np.maximum(l1, l2)
+    both_empty = ~np.isfinite(m)
+    ms = np.where(both_empty, 0.0, m)
+    w1 = np.where(np.isfinite(l1), np.exp(l1 - ms), 0.0)
+    w2 = np.where(np.isfinite(l2), np.exp(l2 - ms), 0.0)
+    tot = w1 + w2
+    safe = np.where(tot > 0, tot, 1.0)
+    o = (w1[..., None] * o1 + w2[..., None] * o2) / safe[..., None]
+    lse = np.where(both_empty, -np.inf, ms + np.log(safe))
+    return np.where(both_empty[..., None], 0.0, o), lse
 
 
 # --------------------------------------------------------------------------
