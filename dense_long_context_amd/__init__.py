@@ -19,4 +19,6 @@ from .binding import (  # noqa: F401
     last_error,
     lib,
     status_str,
+    window_attend,
+    window_attend_ws,
 )

@@ -42,12 +42,16 @@ SIGNATURES = {
     "hca_attend_ws": (_sz, [_i64, _i64, _i64, _i64, _i64]),
     "hca_attend": (_i32, [_i32, _i64, _i64, _i64, _i64, _i64, _vp, _vp, _i64, _vp, _i64, _f32, _vp,
                           _vp, _vp, _sz, _vp]),
+    "window_attend_ws": (_sz, [_i64, _i64, _i64, _i64, _i64]),
+    "window_attend": (_i32, [_i32, _i64, _i64, _i64, _i64, _i64, _vp, _vp, _i64, _vp, _i64, _f32, _vp, _vp,
+                             _vp, _vp, _vp, _sz, _vp]),
     "dlc_project": (_i32, [_i32, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _i32, _vp]),
     "dlc_timing_arm": (_i32, [_i32, _vp, _vp]),
     "dlc_copy": (_i32, [_vp, _vp, _sz, _vp]),
 }
 
 STAGE_INDEX_SCORES, STAGE_TOPK_SELECT, STAGE_CSA_ATTEND, STAGE_HCA_ATTEND, STAGE_COMPRESS = 1, 2, 3, 4, 5
+STAGE_WINDOW_ATTEND = 6
 
 
 class DlcError(RuntimeError):
@@ -228,6 +232,37 @@ def hca_attend(q, Chca, t, t_max, m_prime, scale=0.0, out=None, lse=None, ws=Non
     ws = _ws(hca_attend_ws(B, n_q, n_h, c, cap), dev, ws)
     _check("hca_attend", lib().hca_attend(
         _dt(q), B, n_q, n_h, c, m_prime, _p(q), _p(Chca), cap, _p(t), int(t_max), float(scale),
+        _p(out), _p(lse), _p(ws), ws.numel() * ws.element_size(), _stream(dev)))
+    return out, lse
+
+
+def window_attend_ws(B, n_q, n_h, c, n_win):
+    return lib().window_attend_ws(B, n_q, n_h, c, n_win)
+
+
+def window_attend(q, Cwin, t, t_max, n_win, o_in=None, lse_in=None, scale=0.0, out=None, lse=None, ws=None):
+    """Sliding-window branch over the ring Cwin [B][ring][c] (token p at row
+    p % ring, ring >= n_win), optionally joined to a compressed branch's
+    (o_in, lse_in) by their log-sum-exp.  Returns (out, lse); out may be o_in."""
+    B, n_q, n_h, c = q.shape
+    ring = Cwin.shape[1]
+    dev = q.device
+    _need(q.is_contiguous() and Cwin.is_contiguous() and t.is_contiguous(), "inputs must be contiguous")
+    _need(Cwin.shape[0] == B and Cwin.shape[2] == c and Cwin.dtype == q.dtype, "Cwin shape/dtype mismatch")
+    _need(t.dtype == torch.int64 and tuple(t.shape) == (B, n_q), "t must be int64 [B][n_q]")
+    _need((o_in is None) == (lse_in is None), "o_in and lse_in come together")
+    if o_in is not None:
+        _need(o_in.dtype == torch.float32 and tuple(o_in.shape) == (B, n_q, n_h, c) and o_in.is_contiguous(),
+              "o_in must be fp32 [B][n_q][n_h][c]")
+        _need(lse_in.dtype == torch.float32 and tuple(lse_in.shape) == (B, n_q, n_h) and lse_in.is_contiguous(),
+              "lse_in must be fp32 [B][n_q][n_h]")
+    if out is None:
+        out = torch.empty((B, n_q, n_h, c), dtype=torch.float32, device=dev)
+    if lse is None:
+        lse = torch.empty((B, n_q, n_h), dtype=torch.float32, device=dev)
+    ws = _ws(window_attend_ws(B, n_q, n_h, c, n_win), dev, ws)
+    _check("window_attend", lib().window_attend(
+        _dt(q), B, n_q, n_h, c, n_win, _p(q), _p(Cwin), ring, _p(t), int(t_max), float(scale), _p(o_in), _p(lse_in),
         _p(out), _p(lse), _p(ws), ws.numel() * ws.element_size(), _stream(dev)))
     return out, lse
 

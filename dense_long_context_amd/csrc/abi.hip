@@ -29,7 +29,7 @@ __global__ void fill_u32_kernel(uint32_t* p, uint32_t v, int64_t n) {
   for (; i < n; i += stride) p[i] = v;
 }
 
-constexpr int kStages = 6;
+constexpr int kStages = 7;
 static thread_local hipEvent_t g_armed[kStages][2] = {};
 
 StageTimer::StageTimer(int stage, hipStream_t s) : stage_(stage), s_(s) {

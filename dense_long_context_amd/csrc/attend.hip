@@ -42,39 +42,54 @@ constexpr float kLn2 = 0.6931471805599453f;
 constexpr int kMinKeysPerSplit = DLC_ATTEND_MIN_KEYS;
 constexpr int kTargetWorkgroups = DLC_ATTEND_TARGET_WGS;
 
+// which keys a query attends to
+constexpr int kDense = 0;   // entries s < min(floor(t/m'), cap)            (HCA)
+constexpr int kGather = 1;  // entries idx[0 .. count-1]                     (CSA)
+constexpr int kWindow = 2;  // tokens max(0, t-n_win+1) .. t of a ring of n_win rows
+
 struct AttArgs {
   const void* q;        // [BQ][n_h][c]
-  const void* kv;       // [B][cap][c]
+  const void* kv;       // [B][cap][c]; window: the ring of cap rows
   const int32_t* idx;   // gather: [BQ][k]
   const int32_t* count; // gather: [BQ]
-  const int64_t* t;     // contiguous: [BQ]
+  const int64_t* t;     // dense, window: [BQ]
   int64_t n_q, n_h, c, cap, k, m_prime, t_max;
+  int64_t n_win;        // window: tokens per window (<= cap)
   int64_t splits, keys_per_split, head_groups;
   float scale_log2;
   float* o;             // [BQ][splits][n_h][c] (splits == 1: the final output)
   float* lse;           // [BQ][splits][n_h] (may be nullptr when splits == 1)
 };
 
-template <bool GATHER>
+template <int MODE>
 __device__ __forceinline__ int64_t n_keys(const AttArgs& a, int64_t bq) {
-  if constexpr (GATHER) {
+  if constexpr (MODE == kGather) {
     int64_t n = a.count[bq];
     return n < 0 ? 0 : (n > a.k ? a.k : n);
   } else {
     int64_t t = a.t[bq];
     t = t < 0 ? 0 : (t > a.t_max ? a.t_max : t);
-    const int64_t v = t / a.m_prime;
-    return v < a.cap ? v : a.cap;
+    if constexpr (MODE == kWindow) {
+      return t + 1 < a.n_win ? t + 1 : a.n_win;
+    } else {
+      const int64_t v = t / a.m_prime;
+      return v < a.cap ? v : a.cap;
+    }
   }
 }
 
-// row of the j-th key of query bq, or -1 if that key is masked
-template <bool GATHER>
-__device__ __forceinline__ int64_t key_row(const AttArgs& a, int64_t bq, int64_t j, int64_t nk) {
-  if (j >= nk) return -1;
-  if constexpr (GATHER) {
+// row of the j-th key of query bq, or -1 if that key is masked (j >= lim);
+// nk is the query's key count (n_keys)
+template <int MODE>
+__device__ __forceinline__ int64_t key_row(const AttArgs& a, int64_t bq, int64_t j, int64_t lim, int64_t nk) {
+  if (j >= lim) return -1;
+  if constexpr (MODE == kGather) {
     const int64_t r = a.idx[bq * a.k + j];
     return (r >= 0 && r < a.cap) ? r : -1;
+  } else if constexpr (MODE == kWindow) {
+    int64_t t = a.t[bq];
+    t = t < 0 ? 0 : (t > a.t_max ? a.t_max : t);
+    return (t - nk + 1 + j) % a.cap;  // token position modulo the ring size
   } else {
     return j;
   }
@@ -82,12 +97,12 @@ __device__ __forceinline__ int64_t key_row(const AttArgs& a, int64_t bq, int64_t
 
 // ------------------------------------------------------------------ VALU path
 
-template <typename T, bool GATHER, int MAXD>
+template <typename T, int MODE, int MAXD>
 __global__ void __launch_bounds__(64) attend_valu_kernel(AttArgs a) {
   const int64_t split = blockIdx.x, h = blockIdx.y, bq = blockIdx.z;
   const int lane = threadIdx.x;
   const int64_t b = bq / a.n_q;
-  const int64_t nk = n_keys<GATHER>(a, bq);
+  const int64_t nk = n_keys<MODE>(a, bq);
   const int64_t k0 = split * a.keys_per_split;
   const int64_t k1 = min(nk, k0 + a.keys_per_split);
   const T* q = static_cast<const T*>(a.q) + (bq * a.n_h + h) * a.c;
@@ -102,7 +117,7 @@ __global__ void __launch_bounds__(64) attend_valu_kernel(AttArgs a) {
   }
   float mrun = -INFINITY, lrun = 0.f;
   for (int64_t j = k0; j < k1; ++j) {
-    const int64_t r = key_row<GATHER>(a, bq, j, nk);
+    const int64_t r = key_row<MODE>(a, bq, j, nk, nk);
     if (r < 0) continue;
     const T* row = kv + r * a.c;
     float cv[MAXD];
@@ -136,7 +151,7 @@ __global__ void __launch_bounds__(64) attend_valu_kernel(AttArgs a) {
 
 // ------------------------------------------------------------------ MFMA path
 
-template <int CD, bool GATHER>
+template <int CD, int MODE>
 __global__ void __launch_bounds__(512) attend_mfma_kernel(AttArgs a) {
   constexpr int HALF = CD / 2;
   constexpr int KSH = HALF / 16;  // 16-dim Q.K^T steps in one half of c
@@ -160,7 +175,7 @@ __global__ void __launch_bounds__(512) attend_mfma_kernel(AttArgs a) {
   const int64_t split = blockIdx.x / a.head_groups;
   const int64_t hg = blockIdx.x - split * a.head_groups;
   const int64_t b = bq / a.n_q;
-  const int64_t nk = n_keys<GATHER>(a, bq);
+  const int64_t nk = n_keys<MODE>(a, bq);
   const int64_t k0 = split * a.keys_per_split;
   const int64_t k1 = min(nk, k0 + a.keys_per_split);
   const int64_t hbase = hg * 128 + hp * 32;  // first head of this wave
@@ -202,7 +217,7 @@ __global__ void __launch_bounds__(512) attend_mfma_kernel(AttArgs a) {
         stv[i] = 0;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const int64_t r = key_row<GATHER>(a, bq, kbase + 4 * kq + j, k1);
+          const int64_t r = key_row<MODE>(a, bq, kbase + 4 * kq + j, k1, nk);
           stv[i] |= uint32_t(r >= 0) << j;
           stg[i][j] = r >= 0 ? *reinterpret_cast<const uint4*>(kv + r * CD + dg * 8) : make_uint4(0, 0, 0, 0);
         }
@@ -411,7 +426,7 @@ __device__ __forceinline__ constexpr int tile_row_off(int r) {
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 
-template <bool GATHER>
+template <int MODE>
 __global__ void __launch_bounds__(512) attend512_kernel(AttArgs a) {
   constexpr int CD = 512, HALF = 256, KSH = 16, NTH = 8;
   constexpr int NST = 3;                // tile stages, two tiles in flight
@@ -426,7 +441,7 @@ __global__ void __launch_bounds__(512) attend512_kernel(AttArgs a) {
   // four 16-byte accesses per lane are free of bank conflicts
   constexpr int XROW = 20;
   __shared__ __attribute__((aligned(16))) float sX[8 * 64 * XROW];
-  __shared__ int32_t sRow[GATHER ? kMaxGatherKeys : 1];
+  __shared__ int32_t sRow[MODE == kGather ? kMaxGatherKeys : 1];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: lets addresses live in SGPRs
@@ -441,7 +456,7 @@ __global__ void __launch_bounds__(512) attend512_kernel(AttArgs a) {
   const int64_t split = (rest / a.head_groups) * 8 + xcd;
   if (split >= a.splits) return;
   const int64_t b = bq / a.n_q;
-  const int64_t nk = n_keys<GATHER>(a, bq);
+  const int64_t nk = n_keys<MODE>(a, bq);
   const int64_t k0 = split * a.keys_per_split;
   const int64_t k1 = min(nk, k0 + a.keys_per_split);
   const int64_t hbase = hg * HPG + hp * 32;
@@ -449,8 +464,8 @@ __global__ void __launch_bounds__(512) attend512_kernel(AttArgs a) {
   const bf16_raw* kv = static_cast<const bf16_raw*>(a.kv) + b * a.cap * CD;
   const int64_t ntile = k1 > k0 ? (k1 - k0 + 31) / 32 : 0;
 
-  if constexpr (GATHER) {
-    for (int64_t j = tid; j < k1 - k0; j += 512) sRow[j] = int32_t(key_row<true>(a, bq, k0 + j, k1));
+  if constexpr (MODE == kGather) {
+    for (int64_t j = tid; j < k1 - k0; j += 512) sRow[j] = int32_t(key_row<kGather>(a, bq, k0 + j, k1, nk));
     __syncthreads();  // sRow ready for the tile loads
   }
   // each wave moves rows RPW*wave .. +RPW-1 of a tile: one 1 KB DMA load per row
@@ -460,10 +475,10 @@ __global__ void __launch_bounds__(512) attend512_kernel(AttArgs a) {
       const int row = RPW * wave + r;
       const int64_t j = tl * 32 + row;  // key position within the split
       int64_t gr;
-      if constexpr (GATHER) {
+      if constexpr (MODE == kGather) {
         gr = (k0 + j < k1) ? sRow[j] : -1;
       } else {
-        gr = (k0 + j < k1) ? k0 + j : -1;
+        gr = key_row<MODE>(a, bq, k0 + j, k1, nk);
       }
       gr = __builtin_amdgcn_readfirstlane(int(gr));
       const bf16_raw* src = gr >= 0 ? kv + gr * CD : g_zero_row;
@@ -475,7 +490,7 @@ __global__ void __launch_bounds__(512) attend512_kernel(AttArgs a) {
   auto valid_mask = [&](int64_t tl) -> uint32_t {
     const int64_t j = tl * 32 + l32;
     bool v = k0 + j < k1;
-    if constexpr (GATHER) v = v && sRow[j] >= 0;
+    if constexpr (MODE == kGather) v = v && sRow[j] >= 0;
     return uint32_t(__ballot(v) & 0xffffffffu);
   };
   // the first two tiles and Q are in flight together
@@ -662,35 +677,43 @@ __global__ void __launch_bounds__(512) attend512_kernel(AttArgs a) {
 
 // One block per (query, head).  The split weights e^{lse_j - lse} are formed
 // once in LDS; each thread then owns 4 consecutive dims (c % 4 == 0) or one
-// dim and sums the splits with independent loads.
+// dim and sums the splits with independent loads.  An optional extra part
+// (o_in, lse_in), laid out like the final output, joins as one more split:
+// the attention over the union of its keys and these (the window branch
+// joined to a compressed branch).  out may be o_in: every element is read and
+// written by the same thread, and lse_in is read before lse is written.
 constexpr int kMaxSplits = 256;
 
 __global__ void __launch_bounds__(128) combine_kernel(const float* op, const float* lp, int64_t splits,
-                                                      int64_t n_h, int64_t c, float* out, float* lse) {
-  __shared__ float wsh[kMaxSplits];
+                                                      int64_t n_h, int64_t c, float* out, float* lse,
+                                                      const float* o_in, const float* lse_in) {
+  __shared__ float wsh[kMaxSplits + 1];
   __shared__ float red[2];
   const int64_t bh = blockIdx.x;  // bq * n_h + h
   const int64_t bq = bh / n_h, h = bh - bq * n_h;
   const int tid = threadIdx.x;
+  const int parts = int(splits) + (o_in ? 1 : 0);
   for (int j = tid; j < splits; j += blockDim.x) wsh[j] = lp[(bq * splits + j) * n_h + h];
+  if (o_in && tid == 0) wsh[splits] = lse_in[bh];
   __syncthreads();
   if (tid < 64) {
     float M = -INFINITY;
-    for (int j = tid; j < splits; j += 64) M = fmaxf(M, wsh[j]);
+    for (int j = tid; j < parts; j += 64) M = fmaxf(M, wsh[j]);
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
     float L = 0.f;
-    for (int j = tid; j < splits; j += 64) L += (M == -INFINITY) ? 0.f : __expf(wsh[j] - M);
+    for (int j = tid; j < parts; j += 64) L += (M == -INFINITY) ? 0.f : __expf(wsh[j] - M);
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) L += __shfl_xor(L, off);
     if (tid == 0) { red[0] = M; red[1] = L; }
   }
   __syncthreads();
   const float M = red[0], L = red[1];
-  for (int j = tid; j < splits; j += blockDim.x) wsh[j] = (M == -INFINITY) ? 0.f : __expf(wsh[j] - M) / L;
+  for (int j = tid; j < parts; j += blockDim.x) wsh[j] = (M == -INFINITY) ? 0.f : __expf(wsh[j] - M) / L;
   __syncthreads();
   const float* base = op + (bq * splits * n_h + h) * c;
   const int64_t sstride = n_h * c;
+  const float w_in = o_in ? wsh[splits] : 0.f;
   if ((c & 3) == 0) {
     for (int64_t d = 4 * tid; d < c; d += 4 * blockDim.x) {
       float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -701,6 +724,11 @@ __global__ void __launch_bounds__(128) combine_kernel(const float* op, const flo
         acc.x = fmaf(wj, v.x, acc.x); acc.y = fmaf(wj, v.y, acc.y);
         acc.z = fmaf(wj, v.z, acc.z); acc.w = fmaf(wj, v.w, acc.w);
       }
+      if (o_in) {
+        const float4 v = *reinterpret_cast<const float4*>(o_in + bh * c + d);
+        acc.x = fmaf(w_in, v.x, acc.x); acc.y = fmaf(w_in, v.y, acc.y);
+        acc.z = fmaf(w_in, v.z, acc.z); acc.w = fmaf(w_in, v.w, acc.w);
+      }
       *reinterpret_cast<float4*>(out + bh * c + d) = acc;
     }
   } else {
@@ -708,6 +736,7 @@ __global__ void __launch_bounds__(128) combine_kernel(const float* op, const flo
       float acc = 0.f;
 #pragma unroll 8
       for (int64_t j = 0; j < splits; ++j) acc = fmaf(wsh[j], base[j * sstride + d], acc);
+      if (o_in) acc = fmaf(w_in, o_in[bh * c + d], acc);
       out[bh * c + d] = acc;
     }
   }
@@ -724,7 +753,7 @@ struct Plan {
   size_t o_off, l_off, total;
 };
 
-Plan plan(int dtype, int64_t BQ, int64_t n_h, int64_t c, int64_t nkeys) {
+Plan plan(int dtype, int64_t BQ, int64_t n_h, int64_t c, int64_t nkeys, bool merge = false) {
   Plan p{};
   p.mfma = mfma_ok(dtype, c);
   p.head_groups = p.mfma ? ceil_div(n_h, 128) : n_h;
@@ -740,7 +769,7 @@ Plan plan(int dtype, int64_t BQ, int64_t n_h, int64_t c, int64_t nkeys) {
   if (p.mfma) p.kps = ceil_div(p.kps, 32) * 32;
   p.o_off = 0;
   size_t off = 0;
-  if (s > 1) {
+  if (s > 1 || merge) {  // partials, combined afterwards
     off = align_up(size_t(BQ) * s * n_h * c * 4, 256);
     p.l_off = off;
     off = align_up(off + size_t(BQ) * s * n_h * 4, 256);
@@ -751,22 +780,25 @@ Plan plan(int dtype, int64_t BQ, int64_t n_h, int64_t c, int64_t nkeys) {
   return p;
 }
 
-size_t ws_bound(int64_t BQ, int64_t n_h, int64_t c, int64_t nkeys) {
-  const Plan a = plan(DLC_BF16, BQ, n_h, c, nkeys), b = plan(DLC_F32, BQ, n_h, c, nkeys);
+size_t ws_bound(int64_t BQ, int64_t n_h, int64_t c, int64_t nkeys, bool merge = false) {
+  const Plan a = plan(DLC_BF16, BQ, n_h, c, nkeys, merge), b = plan(DLC_F32, BQ, n_h, c, nkeys, merge);
   return a.total > b.total ? a.total : b.total;
 }
 
-template <bool GATHER>
+template <int MODE>
 int run_attend(const char* name, int dtype, AttArgs a, int64_t BQ, int64_t nkeys, float* out, float* lse,
-               void* ws, size_t ws_bytes, hipStream_t s) {
-  const Plan p = plan(dtype, BQ, a.n_h, a.c, nkeys);
+               void* ws, size_t ws_bytes, hipStream_t s, const float* o_in = nullptr,
+               const float* lse_in = nullptr) {
+  const bool merge = o_in != nullptr;
+  const Plan p = plan(dtype, BQ, a.n_h, a.c, nkeys, merge);
   DLC_REQUIRE(p.total == 0 || (ws != nullptr && ws_bytes >= p.total), DLC_E_WORKSPACE,
               "%s: workspace of %zu bytes needed, %zu given", name, p.total, ws_bytes);
   DLC_REQUIRE(ws == nullptr || aligned(ws, 256), DLC_E_WORKSPACE, "%s: workspace must be 256-byte aligned", name);
   a.splits = p.splits;
   a.keys_per_split = p.kps;
   a.head_groups = p.head_groups;
-  if (p.splits > 1) {
+  const bool partials = p.splits > 1 || merge;
+  if (partials) {
     a.o = reinterpret_cast<float*>(static_cast<char*>(ws) + p.o_off);
     a.lse = reinterpret_cast<float*>(static_cast<char*>(ws) + p.l_off);
   } else {
@@ -775,24 +807,25 @@ int run_attend(const char* name, int dtype, AttArgs a, int64_t BQ, int64_t nkeys
   }
   DLC_REQUIRE(BQ <= 65535 && p.splits * p.head_groups < (int64_t(1) << 31), DLC_E_UNSUPPORTED,
               "%s: grid too large", name);
-  StageTimer timer(GATHER ? DLC_STAGE_CSA_ATTEND : DLC_STAGE_HCA_ATTEND, s);
+  StageTimer timer(MODE == kGather ? DLC_STAGE_CSA_ATTEND : MODE == kDense ? DLC_STAGE_HCA_ATTEND
+                                                                             : DLC_STAGE_WINDOW_ATTEND, s);
   if (p.mfma) {
     dim3 grid{(unsigned)(p.splits * p.head_groups), (unsigned)BQ, 1u};
-    if (a.c == 128) hipLaunchKernelGGL((attend_mfma_kernel<128, GATHER>), grid, dim3(512), 0, s, a);
-    if (a.c == 256) hipLaunchKernelGGL((attend_mfma_kernel<256, GATHER>), grid, dim3(512), 0, s, a);
-    if (a.c == 512) hipLaunchKernelGGL((attend512_kernel<GATHER>), grid, dim3(512), 0, s, a);
+    if (a.c == 128) hipLaunchKernelGGL((attend_mfma_kernel<128, MODE>), grid, dim3(512), 0, s, a);
+    if (a.c == 256) hipLaunchKernelGGL((attend_mfma_kernel<256, MODE>), grid, dim3(512), 0, s, a);
+    if (a.c == 512) hipLaunchKernelGGL((attend512_kernel<MODE>), grid, dim3(512), 0, s, a);
   } else {
     DLC_REQUIRE(a.n_h <= 65535, DLC_E_UNSUPPORTED, "%s: n_h > 65535 on the VALU path", name);
     dim3 grid{(unsigned)p.splits, (unsigned)a.n_h, (unsigned)BQ};
     if (dtype == DLC_BF16)
-      hipLaunchKernelGGL((attend_valu_kernel<bf16_raw, GATHER, 16>), grid, dim3(64), 0, s, a);
+      hipLaunchKernelGGL((attend_valu_kernel<bf16_raw, MODE, 16>), grid, dim3(64), 0, s, a);
     else
-      hipLaunchKernelGGL((attend_valu_kernel<float, GATHER, 16>), grid, dim3(64), 0, s, a);
+      hipLaunchKernelGGL((attend_valu_kernel<float, MODE, 16>), grid, dim3(64), 0, s, a);
   }
   int rc = check_launch(name);
-  if (rc || p.splits == 1) return rc;
+  if (rc || !partials) return rc;
   hipLaunchKernelGGL(combine_kernel, dim3((unsigned)(BQ * a.n_h)), dim3(128), 0, s, a.o, a.lse, p.splits, a.n_h,
-                     a.c, out, lse);
+                     a.c, out, lse, o_in, lse_in);
   return check_launch(name);
 }
 
@@ -835,7 +868,7 @@ int csa_attend(int dtype, int64_t B, int64_t n_q, int64_t n_h, int64_t c, int64_
   a.q = q; a.kv = Ccomp; a.idx = idx; a.count = count;
   a.n_q = n_q; a.n_h = n_h; a.c = c; a.cap = cap; a.k = k;
   a.scale_log2 = (scale > 0.f ? scale : 1.f / std::sqrt(float(c))) * kLog2e;
-  return run_attend<true>("csa_attend", dtype, a, B * n_q, k, out, lse, ws, ws_bytes, as_stream(stream));
+  return run_attend<kGather>("csa_attend", dtype, a, B * n_q, k, out, lse, ws, ws_bytes, as_stream(stream));
 }
 
 int hca_attend(int dtype, int64_t B, int64_t n_q, int64_t n_h, int64_t c, int64_t m_prime, const void* q,
@@ -852,8 +885,34 @@ int hca_attend(int dtype, int64_t B, int64_t n_q, int64_t n_h, int64_t c, int64_
   a.q = q; a.kv = Chca; a.t = t;
   a.n_q = n_q; a.n_h = n_h; a.c = c; a.cap = cap; a.m_prime = m_prime; a.t_max = t_max;
   a.scale_log2 = (scale > 0.f ? scale : 1.f / std::sqrt(float(c))) * kLog2e;
-  return run_attend<false>("hca_attend", dtype, a, B * n_q, t_max / m_prime, out, lse, ws, ws_bytes,
+  return run_attend<kDense>("hca_attend", dtype, a, B * n_q, t_max / m_prime, out, lse, ws, ws_bytes,
                            as_stream(stream));
+}
+
+size_t window_attend_ws(int64_t B, int64_t n_q, int64_t n_h, int64_t c, int64_t n_win) {
+  if (B < 1 || n_q < 1 || n_h < 1 || c < 1 || n_win < 1) return 0;
+  return dlc::ws_bound(B * n_q, n_h, c, n_win, true);
+}
+
+int window_attend(int dtype, int64_t B, int64_t n_q, int64_t n_h, int64_t c, int64_t n_win, const void* q,
+                  const void* Cwin, int64_t ring, const int64_t* t, int64_t t_max, float scale, const float* o_in,
+                  const float* lse_in, float* out, float* lse, void* ws, size_t ws_bytes, void* stream) {
+  using namespace dlc;
+  int rc = common_checks("window_attend", dtype, B, n_q, n_h, c, q, Cwin, ring, out);
+  if (rc) return rc;
+  DLC_REQUIRE(n_win >= 1 && t_max >= 0, DLC_E_INVAL, "window_attend: need n_win >= 1 and t_max >= 0");
+  DLC_REQUIRE(ring >= n_win && Cwin != nullptr, DLC_E_SHAPE, "window_attend: ring (%lld) < n_win (%lld)",
+              (long long)ring, (long long)n_win);
+  DLC_REQUIRE(t != nullptr, DLC_E_INVAL, "window_attend: NULL t");
+  DLC_REQUIRE((o_in == nullptr) == (lse_in == nullptr), DLC_E_INVAL,
+              "window_attend: o_in and lse_in come together");
+  AttArgs a{};
+  a.q = q; a.kv = Cwin; a.t = t;
+  a.n_q = n_q; a.n_h = n_h; a.c = c; a.cap = ring; a.n_win = n_win; a.t_max = t_max; a.m_prime = 1;
+  a.scale_log2 = (scale > 0.f ? scale : 1.f / std::sqrt(float(c))) * kLog2e;
+  const int64_t nkeys = t_max + 1 < n_win ? t_max + 1 : n_win;
+  return run_attend<kWindow>("window_attend", dtype, a, B * n_q, nkeys, out, lse, ws, ws_bytes,
+                             as_stream(stream), o_in, lse_in);
 }
 
 }  // extern "C"

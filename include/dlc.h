@@ -167,6 +167,35 @@ int hca_attend(int dtype, int64_t B, int64_t n_q, int64_t n_h, int64_t c, int64_
                float scale, float* out, float* lse, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * window_attend - the sliding-window branch ("From MHA, GQA to MLA, DSA,
+ * HCA/CSA", §6.1 and §6.2, sliding window path): shared-KV attention of each
+ * query over the raw window entries c^window_p = h_p W^{window,KV} of the
+ * n_win most recent tokens p = max(0, t-n_win+1) .. t, with the same formula,
+ * scale and empty-case rule as csa_attend.  The pages join these entries to
+ * the compressed ones by concatenation before one attention; since softmax
+ * sums over keys, that equals merging the two parts' outputs by their
+ * log-sum-exp, which this call does when o_in is given.
+ *
+ *  Cwin    [B][ring][c] ring in dtype (ring >= n_win): the entry of token p
+ *          is row p % ring.  Decode: ring = n_win, the caller writes the new
+ *          token's row before the call.  Queries at several positions (a
+ *          prefill chunk ending at token T) need every window inside the
+ *          ring: ring >= n_win + (T - smallest t).
+ *  t,t_max as for hca_attend; only rows of tokens in the window are read
+ *  o_in, lse_in  optional fp32 [B][n_q][n_h][c] and [B][n_q][n_h]: the
+ *          compressed branch's output (csa_attend or hca_attend).  When given,
+ *          out / lse are the attention over both key sets; out may be o_in and
+ *          lse may be lse_in (in place).  Both NULL: the window part alone.
+ *  out     fp32 [B][n_q][n_h][c];  lse: fp32 [B][n_q][n_h] or NULL
+ *  ws      at least window_attend_ws(B, n_q, n_h, c, n_win) bytes, 256-byte aligned
+ */
+size_t window_attend_ws(int64_t B, int64_t n_q, int64_t n_h, int64_t c, int64_t n_win);
+int window_attend(int dtype, int64_t B, int64_t n_q, int64_t n_h, int64_t c, int64_t n_win,
+                  const void* q, const void* Cwin, int64_t ring, const int64_t* t, int64_t t_max, float scale,
+                  const float* o_in, const float* lse_in, float* out, float* lse,
+                  void* ws, size_t ws_bytes, void* stream);
+
+/*
  * dlc_project - dense projection out = A . W with fp32 accumulation, the
  * token projections that feed the compressor and the queries ([Scratch] §3:
  * C^a = H W^{aKV} and its siblings; §6.1-6.3 and §8: c^Q, q^I, w^I, q).
@@ -191,6 +220,7 @@ int dlc_project(int dtype, int64_t M, int64_t N, int64_t K, const void* A, int64
  *   DLC_STAGE_CSA_ATTEND    csa_attend (attention and combine kernels)
  *   DLC_STAGE_HCA_ATTEND    hca_attend (attention and combine kernels)
  *   DLC_STAGE_COMPRESS      csa_compress / hca_compress
+ *   DLC_STAGE_WINDOW_ATTEND window_attend (attention and merge kernels)
  *
  * dlc_copy - device-to-device copy kernel of `bytes` bytes (a multiple of
  * 16, both pointers 16-byte aligned); the reference for achievable HBM
@@ -201,7 +231,8 @@ enum {
   DLC_STAGE_TOPK_SELECT = 2,
   DLC_STAGE_CSA_ATTEND = 3,
   DLC_STAGE_HCA_ATTEND = 4,
-  DLC_STAGE_COMPRESS = 5
+  DLC_STAGE_COMPRESS = 5,
+  DLC_STAGE_WINDOW_ATTEND = 6
 };
 int dlc_timing_arm(int stage, void* ev_begin, void* ev_end);
 int dlc_copy(void* dst, const void* src, size_t bytes, void* stream);

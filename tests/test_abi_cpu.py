@@ -132,6 +132,23 @@ def test_attend_validation(L):
     assert L.hca_attend(BF16, 1, 1, 4, 128, 0, P, P, 4, P, 100, 0.0, P, None, None, 0, None) == E_INVAL
 
 
+def test_window_validation(L):
+    def win(**kw):
+        a = dict(dict(dtype=BF16, B=1, n_q=1, n_h=4, c=128, n_win=128, q=P, C=P, ring=128, t=P, t_max=10,
+                      o_in=None, lse_in=None, out=P, lse=None, ws=None, wsb=0), **kw)
+        return L.window_attend(a["dtype"], a["B"], a["n_q"], a["n_h"], a["c"], a["n_win"], a["q"], a["C"],
+                               a["ring"], a["t"], a["t_max"], 0.0, a["o_in"], a["lse_in"], a["out"], a["lse"],
+                               a["ws"], a["wsb"], None)
+    assert win(dtype=7) == E_DTYPE
+    assert win(n_win=0) == E_INVAL
+    assert win(t=None) == E_INVAL
+    assert win(ring=64) == E_SHAPE                       # ring smaller than the window
+    assert win(o_in=P) == E_INVAL                        # o_in without lse_in
+    assert win(o_in=P, lse_in=P) == E_WORKSPACE          # joining needs the partial buffers
+    assert L.window_attend_ws(4, 1, 128, 512, 128) > 0
+    assert L.window_attend_ws(4, 1, 128, 512, 0) == 0
+
+
 def test_project_validation(L):
     assert L.dlc_project(BF16, 4, 4, 0, P, 8, P, 8, P, 4, BF16, None) == E_INVAL
     assert L.dlc_project(BF16, 4, 4, 8, P, 4, P, 8, P, 4, BF16, None) == E_SHAPE

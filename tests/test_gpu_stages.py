@@ -265,3 +265,69 @@ def test_project(dtype, M, N, K, out_dtype):
     ref = O.project(A, W)
     tol = 1e-5 if out_dtype == "f32" else 8e-3
     assert_rows_close(out.cpu(), O.store_as(ref, out_dtype) if out_dtype == "bf16" else ref, tol, "project")
+
+
+# ------------------------------------------------------------ sliding window
+
+def _ring(B, ring, c, dtype, seed):
+    return synth.normal((B, ring, c), seed, dtype=dtype)
+
+
+def _window_ref(q, R, t, n_win):
+    """Oracle window attention of one query: the window's positions, their rows
+    read from the ring (token p at row p % ring)."""
+    pos = O.window_positions(int(t), n_win)
+    rows = f64(R)[pos % R.shape[0]]
+    return O.mqa_attend(q, rows)
+
+
+@pytest.mark.parametrize("dtype,B,n_q,n_h,c,n_win,ring,ts", [
+    ("f32", 1, 1, 3, 5, 4, 4, [2]),                                   # VALU path, partial window
+    ("f32", 2, 1, 2, 8, 4, 4, [10, 3]),                               # wrap-around
+    ("bf16", 2, 1, 16, 128, 128, 128, [300, 50]),                     # c = 128 MFMA path
+    ("bf16", 4, 1, 128, 512, 128, 128, [(1 << 20) + 5, (1 << 20) + 200, 127, 0]),  # V4-Pro shape, t = 0
+    ("bf16", 1, 3, 128, 512, 128, 130, [1000, 999, 998]),             # prefill chunk, ring > n_win
+])
+def test_window_attend(dtype, B, n_q, n_h, c, n_win, ring, ts):
+    seed = 900 + c + ring
+    q = synth.normal((B, n_q, n_h, c), seed, dtype=dtype)
+    R = _ring(B, ring, c, dtype, seed + 1)
+    t = torch.tensor(ts, dtype=torch.int64).reshape(B, n_q)
+    o, lse = dlc.window_attend(q.to(DEV), R.to(DEV), t.to(DEV), int(t.max()), n_win)
+    torch.cuda.synchronize()
+    for b in range(B):
+        for j in range(n_q):
+            o_r, l_r = _window_ref(q[b, j], R[b], t[b, j], n_win)
+            assert_rows_close(o[b, j], o_r, TOL_ATT[dtype], f"window b={b} q={j}")
+            assert np.abs(lse[b, j].cpu().numpy() - l_r).max() <= TOL_ATT[dtype]
+
+
+@pytest.mark.parametrize("dtype,B,n_h,c,k,cap,counts", [
+    ("bf16", 4, 128, 512, 1024, 262208, [1024, 1024, 7, 0]),  # V4-Pro shape; one empty compressed part
+    ("f32", 2, 4, 16, 8, 40, [5, 8]),
+])
+def test_window_joins_compressed_branch_in_place(dtype, B, n_h, c, k, cap, counts):
+    """csa_attend, then window_attend with the CSA output as o_in and out: the
+    attention over the union of the selected entries and the window."""
+    seed = 950 + c
+    n_win, ring = 128, 128
+    q = synth.normal((B, 1, n_h, c), seed, dtype=dtype)
+    Cc = synth.normal((B, cap, c), seed + 1, dtype=dtype)
+    R = _ring(B, ring, c, dtype, seed + 2)
+    g = torch.Generator().manual_seed(seed + 3)
+    idx = torch.full((B, 1, k), -1, dtype=torch.int32)
+    for b, n in enumerate(counts):
+        idx[b, 0, :n] = torch.sort(torch.randperm(cap, generator=g)[:n])[0].to(torch.int32)
+    cnt = torch.tensor(counts, dtype=torch.int32).reshape(B, 1)
+    t = torch.tensor([4 * cap + 3 + b for b in range(B)], dtype=torch.int64).reshape(B, 1)
+    qd, Rd = q.to(DEV), R.to(DEV)
+    o, lse = dlc.csa_attend(qd, Cc.to(DEV), idx.to(DEV), cnt.to(DEV))
+    dlc.window_attend(qd, Rd, t.to(DEV), int(t.max()), n_win, o_in=o, lse_in=lse, out=o, lse=lse)
+    torch.cuda.synchronize()
+    for b in range(B):
+        sel = idx[b, 0, :counts[b]].numpy().astype(np.int64)
+        o1, l1 = O.csa_attend(q[b, 0], Cc[b], sel)
+        o2, l2 = _window_ref(q[b, 0], R[b], t[b, 0], n_win)
+        o_r, l_r = O.merge_lse(o1, l1, o2, l2)
+        assert_rows_close(o[b, 0], o_r, TOL_ATT[dtype], f"joined b={b}")
+        assert np.abs(lse[b, 0].cpu().numpy() - l_r).max() <= TOL_ATT[dtype]
