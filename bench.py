@@ -104,6 +104,15 @@ def query_weight(cfg, nm):
     return synth.normal(shape, synth.tensor_seed(cfg.seed, nm), std, "bf16")
 
 
+N_WIN = 128  # sliding-window tokens per query (V4-Pro)
+
+
+def window_weight(cfg, nm):
+    """W^{window,KV} of the CSA layer ("win") or the HCA layer ("win_hca"): [d][c] bf16, N(0, 1/d)."""
+    import synth
+    return synth.normal((cfg.d, cfg.c), synth.tensor_seed(cfg.seed, nm), cfg.weight_std, "bf16")
+
+
 def hidden_rows(cfg, b, n_tot, r0, r1, dev):
     """Rows [r0, r1) of sequence b's hidden states [n_tot][d] bf16, drawn on ``dev``."""
     import synth
@@ -158,17 +167,33 @@ def build_workload(cfg, dev, n_dec, n_sets=3):
     wI = dlc.dlc_project(h, Wq["w"], out_dtype=torch.float32)
     q = dlc.dlc_project(cQ, Wq["UQ"])
     qh = dlc.dlc_project(cQ, Wq["UQ_hca"])
+    # sliding-window entries c^window_p = h_p W^{window,KV} of positions n_ctx-N_WIN .. n_tot-1, one ring per
+    # layer with ring = N_WIN + n_dec rows (token p at row p % ring), so every decode step's window is in it
+    ring = N_WIN + n_dec
+    lo = n_ctx - N_WIN
+    rings = {}
+    for nm in ("win", "win_hca"):
+        Ww = window_weight(cfg, nm).t().contiguous().to(dev)
+        R = torch.empty((B, ring, c), dtype=torch.bfloat16, device=dev)
+        for b in range(B):
+            hw = hidden_rows(cfg, b, n_tot, lo, n_tot, dev)
+            rows = dlc.dlc_project(hw, Ww)                        # positions lo .. n_tot-1
+            pos = torch.arange(lo, n_tot, device=dev) % ring
+            R[b, pos] = rows
+        rings[nm] = R
     per_step = lambda x, *shape: x.reshape(B, n_dec, *shape).transpose(0, 1).contiguous()  # noqa: E731
     Q = dict(qI=per_step(qI, 1, cfg.n_hI, cI), wI=per_step(wI, 1, cfg.n_hI), q=per_step(q, 1, cfg.n_h, c),
              qh=per_step(qh, 1, cfg.n_h, c), cQ=per_step(cQ, 1, cfg.d_c))
     torch.cuda.synchronize()
     del H_dec
-    return dict(S=S, col=col, sets=sets, Q=Q, n_ctx=n_ctx, n_tot=n_tot, cap_csa=cap_csa, cap_hca=cap_hca,
+    return dict(S=S, col=col, sets=sets, Q=Q, rings=rings, ring=ring, n_ctx=n_ctx, n_tot=n_tot, cap_csa=cap_csa,
+                cap_hca=cap_hca,
                 t_proj=t_proj, t_comp=t_comp, stream_bytes=S.numel() * 2)
 
 
-def make_steps(cfg, wl, dev, n_dec):
-    """Pre-marshal the C-ABI argument tuples of every decode step."""
+def make_steps(cfg, wl, dev, n_dec, window=False):
+    """Pre-marshal the C-ABI argument tuples of every decode step.  window: each
+    layer's sliding-window branch joins its attention output in place."""
     import torch
 
     import dense_long_context_amd as dlc
@@ -189,6 +214,7 @@ def make_steps(cfg, wl, dev, n_dec):
     o1 = torch.empty((B, 1, n_h, c), dtype=torch.float32, device=dev)
     l1 = torch.empty((B, 1, n_h), dtype=torch.float32, device=dev)
     o2, l2 = torch.empty_like(o1), torch.empty_like(l1)
+    ws_w = torch.empty(max(1, dlc.window_attend_ws(B, 1, n_h, c, N_WIN)), dtype=torch.uint8, device=dev)
     tt = torch.arange(wl["n_ctx"], wl["n_ctx"] + n_dec, dtype=torch.int64, device=dev)
     tt = tt[:, None, None].expand(n_dec, B, 1).contiguous()
     p = lambda x: x.data_ptr()  # noqa: E731
@@ -212,10 +238,19 @@ def make_steps(cfg, wl, dev, n_dec):
                                          p(tt[s]), t, p(idx), p(cnt), None, p(ws_i), ws_i.numel(), stream)))
         calls.append((L.csa_attend, (BF, B, 1, n_h, c, k, p(Q["q"][s]), p(Cc), cap_csa, p(idx), p(cnt), 0.0,
                                      p(o1), p(l1), p(ws_c), ws_c.numel(), stream)))
+        if window:
+            calls.append((L.window_attend, (BF, B, 1, n_h, c, N_WIN, p(Q["q"][s]), p(wl["rings"]["win"]), wl["ring"],
+                                            p(tt[s]), t, 0.0, p(o1), p(l1), p(o1), p(l1), p(ws_w), ws_w.numel(),
+                                            stream)))
         calls.append((L.hca_attend, (BF, B, 1, n_h, c, mp, p(Q["qh"][s]), p(Ch), cap_hca, p(tt[s]), t, 0.0,
                                      p(o2), p(l2), p(ws_h), ws_h.numel(), stream)))
+        if window:
+            calls.append((L.window_attend, (BF, B, 1, n_h, c, N_WIN, p(Q["qh"][s]), p(wl["rings"]["win_hca"]),
+                                            wl["ring"], p(tt[s]), t, 0.0, p(o2), p(l2), p(o2), p(l2), p(ws_w),
+                                            ws_w.numel(), stream)))
         steps.append((t, calls))
-    keep = dict(ws_i=ws_i, ws_c=ws_c, ws_h=ws_h, idx=idx, cnt=cnt, o_csa=o1, lse_csa=l1, o_hca=o2, lse_hca=l2, t=tt)
+    keep = dict(ws_i=ws_i, ws_c=ws_c, ws_h=ws_h, ws_w=ws_w, idx=idx, cnt=cnt, o_csa=o1, lse_csa=l1, o_hca=o2,
+                lse_hca=l2, t=tt)
     return steps, keep
 
 
@@ -437,6 +472,17 @@ def main():
         if best is None or ms < best[0]:
             best = (ms, k_ms, ms_armed)
     ms, k_ms, ms_armed = best
+    # the same steps with each layer's sliding-window branch joined in (reported beside the main line)
+    steps_w, keep_w = make_steps(cfg, wl, dev, n_dec, window=True)
+    run_steps(steps_w, 0, args.warmup, n_dec)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    run_steps(steps_w, args.warmup, K, n_dec)
+    e1.record()
+    torch.cuda.synchronize()
+    ms_win = e0.elapsed_time(e1)
+    del keep_w
     ts = [steps[(args.warmup + j) % n_dec][0] for j in range(K)]
     total_bytes = sum(step_bytes(cfg, t)[0] for t in ts)
     idx_bytes = sum(step_bytes(cfg, t)[1] for t in ts) / K
@@ -489,6 +535,8 @@ def main():
                      "avg_launch_us": round(k_avg_ms * 1e3, 3),
                      "algorithmic_bytes_per_launch": int(idx_bytes)},
         "ms_per_step_with_kernel_events": round(ms_armed / K, 5),
+        "with_sliding_window": {"value": round(cfg.B * K / (ms_win * 1e-3), 1), "ms_per_step": round(ms_win / K, 5),
+                                "n_win": N_WIN, "note": "each layer's 128-token window branch joined to its output"},
         "step_hbm_gbs": round(hbm_gbs, 1),
         "step_frac_of_peak": round(hbm_gbs / PEAK_HBM_GBS, 4),
         "copy_kernel_gbs": round(copy_gbs, 1),

@@ -80,4 +80,5 @@ TENSOR_IDS = dict(
     DQ=11, IUQ=12, w=13, UQ=14, UQ_hca=15,
     Ccomp=20, KI=21, Chca=22, q=23, qI=24, wI=25, q_hca=26,
     Ba=30, Bb=31, BIa=32, BIb=33, Bh=34,
+    win=16, win_hca=17,
 )

@@ -415,3 +415,42 @@ def test_hybrid1m_prefill_sample(hybrid):
             _check_attend(o1[b, j], l1[b, j], o_r, l_r, TOL_ATT_BF16, f"prefill CSA b={b} t={t}")
             o_r, l_r = O.hca_attend(qh[b, j].cpu(), Chb[:t // mp], t, mp)
             _check_attend(o2[b, j], l2[b, j], o_r, l_r, TOL_ATT_BF16, f"prefill HCA b={b} t={t}")
+
+
+def test_hybrid1m_decode_steps_with_window(hybrid):
+    """The benchmark's decode steps with each layer's sliding-window branch
+    joined in: the window rows against the oracle's projection of the
+    regenerated hidden rows, and the joined outputs against one attention over
+    the selected (or visible) entries and the window."""
+    cfg, wl, _, _, bench = hybrid
+    m, mp, n_dec, n_win = cfg.m, cfg.m_prime, cfg.n_decode, bench.N_WIN
+    steps, keep = bench.make_steps(cfg, wl, torch.device(DEV), n_dec, window=True)
+    ring = wl["ring"]
+    # window rows of a few positions
+    Ww = {nm: f64(bench.window_weight(cfg, nm)) for nm in ("win", "win_hca")}
+    for b in (0, cfg.B - 1):
+        for pos in (wl["n_ctx"] - n_win, wl["n_ctx"], wl["n_tot"] - 1):
+            h = _hidden_f64(bench, cfg, wl, b, pos, pos + 1)
+            for nm in ("win", "win_hca"):
+                got = wl["rings"][nm][b, pos % ring]
+                assert_rows_close(got[None], O.store_as(O.project(h, Ww[nm]), "bf16"), TOL_STORE, f"{nm} row {pos}")
+    Q = wl["Q"]
+    for s in (0, 200):
+        t, _ = steps[s]
+        print(f"decode step with window s={s} t={t}", flush=True)
+        bench.run_steps(steps, s, 1, n_dec)
+        torch.cuda.synchronize()
+        Cc, KI, Ch = wl["sets"][s % 3]
+        for b in range(cfg.B):
+            sel = _np(keep["idx"][b, 0])[:int(keep["cnt"][b, 0])].astype(np.int64)
+            pos = O.window_positions(t, n_win)
+            Rc = f64(wl["rings"]["win"][b].cpu())[pos % ring]
+            Rh = f64(wl["rings"]["win_hca"][b].cpu())[pos % ring]
+            o1, l1 = O.csa_attend(Q["q"][s][b, 0].cpu(), Cc[b].cpu(), sel)
+            o2, l2 = O.mqa_attend(Q["q"][s][b, 0].cpu(), Rc)
+            o_r, l_r = O.merge_lse(o1, l1, o2, l2)
+            _check_attend(keep["o_csa"][b, 0], keep["lse_csa"][b, 0], o_r, l_r, TOL_ATT_BF16, f"CSA+window s={s} b={b}")
+            o1, l1 = O.hca_attend(Q["qh"][s][b, 0].cpu(), Ch[b, :t // mp].cpu(), t, mp)
+            o2, l2 = O.mqa_attend(Q["qh"][s][b, 0].cpu(), Rh)
+            o_r, l_r = O.merge_lse(o1, l1, o2, l2)
+            _check_attend(keep["o_hca"][b, 0], keep["lse_hca"][b, 0], o_r, l_r, TOL_ATT_BF16, f"HCA+window s={s} b={b}")
