@@ -214,7 +214,9 @@ def make_steps(cfg, wl, dev, n_dec, window=False):
     o1 = torch.empty((B, 1, n_h, c), dtype=torch.float32, device=dev)
     l1 = torch.empty((B, 1, n_h), dtype=torch.float32, device=dev)
     o2, l2 = torch.empty_like(o1), torch.empty_like(l1)
-    ws_w = torch.empty(max(1, dlc.window_attend_ws(B, 1, n_h, c, N_WIN)), dtype=torch.uint8, device=dev)
+    ws_w = torch.empty(max(1, binding.lib().csa_attend_window_ws(B, 1, n_h, c, k, N_WIN),
+                           binding.lib().hca_attend_window_ws(B, 1, n_h, c, cap_hca, N_WIN)),
+                       dtype=torch.uint8, device=dev)
     tt = torch.arange(wl["n_ctx"], wl["n_ctx"] + n_dec, dtype=torch.int64, device=dev)
     tt = tt[:, None, None].expand(n_dec, B, 1).contiguous()
     p = lambda x: x.data_ptr()  # noqa: E731
@@ -236,18 +238,18 @@ def make_steps(cfg, wl, dev, n_dec, window=False):
                                            p(Ch), cap_hca, stream)))
         calls.append((L.csa_index_topk, (BF, B, 1, n_hI, cI, m, k, p(Q["qI"][s]), p(Q["wI"][s]), p(KI), cap_csa,
                                          p(tt[s]), t, p(idx), p(cnt), None, p(ws_i), ws_i.numel(), stream)))
-        calls.append((L.csa_attend, (BF, B, 1, n_h, c, k, p(Q["q"][s]), p(Cc), cap_csa, p(idx), p(cnt), 0.0,
-                                     p(o1), p(l1), p(ws_c), ws_c.numel(), stream)))
-        if window:
-            calls.append((L.window_attend, (BF, B, 1, n_h, c, N_WIN, p(Q["q"][s]), p(wl["rings"]["win"]), wl["ring"],
-                                            p(tt[s]), t, 0.0, p(o1), p(l1), p(o1), p(l1), p(ws_w), ws_w.numel(),
-                                            stream)))
-        calls.append((L.hca_attend, (BF, B, 1, n_h, c, mp, p(Q["qh"][s]), p(Ch), cap_hca, p(tt[s]), t, 0.0,
-                                     p(o2), p(l2), p(ws_h), ws_h.numel(), stream)))
-        if window:
-            calls.append((L.window_attend, (BF, B, 1, n_h, c, N_WIN, p(Q["qh"][s]), p(wl["rings"]["win_hca"]),
-                                            wl["ring"], p(tt[s]), t, 0.0, p(o2), p(l2), p(o2), p(l2), p(ws_w),
-                                            ws_w.numel(), stream)))
+        if window:  # each layer's attention with its sliding window joined in (one key list)
+            calls.append((L.csa_attend_window, (BF, B, 1, n_h, c, k, p(Q["q"][s]), p(Cc), cap_csa, p(idx), p(cnt),
+                                                p(wl["rings"]["win"]), wl["ring"], N_WIN, p(tt[s]), t, 0.0, p(o1),
+                                                p(l1), p(ws_w), ws_w.numel(), stream)))
+            calls.append((L.hca_attend_window, (BF, B, 1, n_h, c, mp, p(Q["qh"][s]), p(Ch), cap_hca, p(tt[s]), t,
+                                                p(wl["rings"]["win_hca"]), wl["ring"], N_WIN, 0.0, p(o2), p(l2),
+                                                p(ws_w), ws_w.numel(), stream)))
+        else:
+            calls.append((L.csa_attend, (BF, B, 1, n_h, c, k, p(Q["q"][s]), p(Cc), cap_csa, p(idx), p(cnt), 0.0,
+                                         p(o1), p(l1), p(ws_c), ws_c.numel(), stream)))
+            calls.append((L.hca_attend, (BF, B, 1, n_h, c, mp, p(Q["qh"][s]), p(Ch), cap_hca, p(tt[s]), t, 0.0,
+                                         p(o2), p(l2), p(ws_h), ws_h.numel(), stream)))
         steps.append((t, calls))
     keep = dict(ws_i=ws_i, ws_c=ws_c, ws_h=ws_h, ws_w=ws_w, idx=idx, cnt=cnt, o_csa=o1, lse_csa=l1, o_hca=o2,
                 lse_hca=l2, t=tt)
@@ -536,7 +538,8 @@ def main():
                      "algorithmic_bytes_per_launch": int(idx_bytes)},
         "ms_per_step_with_kernel_events": round(ms_armed / K, 5),
         "with_sliding_window": {"value": round(cfg.B * K / (ms_win * 1e-3), 1), "ms_per_step": round(ms_win / K, 5),
-                                "n_win": N_WIN, "note": "each layer's 128-token window branch joined to its output"},
+                                "n_win": N_WIN, "note": "csa_attend_window / hca_attend_window: each layer's "
+                                                        "128-token window joined to its compressed keys"},
         "step_hbm_gbs": round(hbm_gbs, 1),
         "step_frac_of_peak": round(hbm_gbs / PEAK_HBM_GBS, 4),
         "copy_kernel_gbs": round(copy_gbs, 1),

@@ -7,6 +7,7 @@ include/dlc.h); this package is its Python binding plus the in-tree build.
 from .binding import (  # noqa: F401
     DlcError,
     csa_attend,
+    csa_attend_window,
     csa_attend_ws,
     csa_compress,
     csa_index_topk,
@@ -14,6 +15,7 @@ from .binding import (  # noqa: F401
     default_scale,
     dlc_project,
     hca_attend,
+    hca_attend_window,
     hca_attend_ws,
     hca_compress,
     last_error,

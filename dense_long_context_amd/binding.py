@@ -45,6 +45,12 @@ SIGNATURES = {
     "window_attend_ws": (_sz, [_i64, _i64, _i64, _i64, _i64]),
     "window_attend": (_i32, [_i32, _i64, _i64, _i64, _i64, _i64, _vp, _vp, _i64, _vp, _i64, _f32, _vp, _vp,
                              _vp, _vp, _vp, _sz, _vp]),
+    "csa_attend_window_ws": (_sz, [_i64, _i64, _i64, _i64, _i64, _i64]),
+    "csa_attend_window": (_i32, [_i32, _i64, _i64, _i64, _i64, _i64, _vp, _vp, _i64, _vp, _vp, _vp, _i64, _i64,
+                                 _vp, _i64, _f32, _vp, _vp, _vp, _sz, _vp]),
+    "hca_attend_window_ws": (_sz, [_i64, _i64, _i64, _i64, _i64, _i64]),
+    "hca_attend_window": (_i32, [_i32, _i64, _i64, _i64, _i64, _i64, _vp, _vp, _i64, _vp, _i64, _vp, _i64, _i64,
+                                 _f32, _vp, _vp, _vp, _sz, _vp]),
     "dlc_project": (_i32, [_i32, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _i32, _vp]),
     "dlc_timing_arm": (_i32, [_i32, _vp, _vp]),
     "dlc_copy": (_i32, [_vp, _vp, _sz, _vp]),
@@ -264,6 +270,47 @@ def window_attend(q, Cwin, t, t_max, n_win, o_in=None, lse_in=None, scale=0.0, o
     _check("window_attend", lib().window_attend(
         _dt(q), B, n_q, n_h, c, n_win, _p(q), _p(Cwin), ring, _p(t), int(t_max), float(scale), _p(o_in), _p(lse_in),
         _p(out), _p(lse), _p(ws), ws.numel() * ws.element_size(), _stream(dev)))
+    return out, lse
+
+
+def csa_attend_window(q, Ccomp, idx, count, Cwin, t, t_max, n_win, scale=0.0, out=None, lse=None, ws=None):
+    """csa_attend joined with the sliding window of the ring Cwin [B][ring][c]."""
+    B, n_q, n_h, c = q.shape
+    k, ring = idx.shape[2], Cwin.shape[1]
+    dev = q.device
+    _need(all(x.is_contiguous() for x in (q, Ccomp, idx, count, Cwin, t)), "inputs must be contiguous")
+    _need(Ccomp.shape[0] == B and Ccomp.shape[2] == c and Ccomp.dtype == q.dtype, "Ccomp shape/dtype mismatch")
+    _need(Cwin.shape[0] == B and Cwin.shape[2] == c and Cwin.dtype == q.dtype, "Cwin shape/dtype mismatch")
+    _need(idx.dtype == torch.int32 and count.dtype == torch.int32, "idx/count must be int32")
+    _need(t.dtype == torch.int64 and tuple(t.shape) == (B, n_q), "t must be int64 [B][n_q]")
+    if out is None:
+        out = torch.empty((B, n_q, n_h, c), dtype=torch.float32, device=dev)
+    if lse is None:
+        lse = torch.empty((B, n_q, n_h), dtype=torch.float32, device=dev)
+    ws = _ws(lib().csa_attend_window_ws(B, n_q, n_h, c, k, n_win), dev, ws)
+    _check("csa_attend_window", lib().csa_attend_window(
+        _dt(q), B, n_q, n_h, c, k, _p(q), _p(Ccomp), Ccomp.shape[1], _p(idx), _p(count), _p(Cwin), ring, n_win,
+        _p(t), int(t_max), float(scale), _p(out), _p(lse), _p(ws), ws.numel() * ws.element_size(), _stream(dev)))
+    return out, lse
+
+
+def hca_attend_window(q, Chca, t, t_max, m_prime, Cwin, n_win, scale=0.0, out=None, lse=None, ws=None):
+    """hca_attend joined with the sliding window of the ring Cwin [B][ring][c]."""
+    B, n_q, n_h, c = q.shape
+    cap, ring = Chca.shape[1], Cwin.shape[1]
+    dev = q.device
+    _need(all(x.is_contiguous() for x in (q, Chca, Cwin, t)), "inputs must be contiguous")
+    _need(Chca.shape[0] == B and Chca.shape[2] == c and Chca.dtype == q.dtype, "Chca shape/dtype mismatch")
+    _need(Cwin.shape[0] == B and Cwin.shape[2] == c and Cwin.dtype == q.dtype, "Cwin shape/dtype mismatch")
+    _need(t.dtype == torch.int64 and tuple(t.shape) == (B, n_q), "t must be int64 [B][n_q]")
+    if out is None:
+        out = torch.empty((B, n_q, n_h, c), dtype=torch.float32, device=dev)
+    if lse is None:
+        lse = torch.empty((B, n_q, n_h), dtype=torch.float32, device=dev)
+    ws = _ws(lib().hca_attend_window_ws(B, n_q, n_h, c, cap, n_win), dev, ws)
+    _check("hca_attend_window", lib().hca_attend_window(
+        _dt(q), B, n_q, n_h, c, m_prime, _p(q), _p(Chca), cap, _p(t), int(t_max), _p(Cwin), ring, n_win,
+        float(scale), _p(out), _p(lse), _p(ws), ws.numel() * ws.element_size(), _stream(dev)))
     return out, lse
 
 

@@ -55,6 +55,11 @@ struct AttArgs {
   const int64_t* t;     // dense, window: [BQ]
   int64_t n_q, n_h, c, cap, k, m_prime, t_max;
   int64_t n_win;        // window: tokens per window (<= cap)
+  // optional sliding-window tail after the mode's own keys (the joined forms of
+  // csa_attend / hca_attend): tokens max(0,t-win_n+1) .. t of the ring win
+  const void* win;      // [B][win_ring][c] or nullptr
+  int64_t win_ring, win_n, win_tmax;
+  const int64_t* win_t; // [BQ]
   int64_t splits, keys_per_split, head_groups;
   float scale_log2;
   float* o;             // [BQ][splits][n_h][c] (splits == 1: the final output)
@@ -95,6 +100,34 @@ __device__ __forceinline__ int64_t key_row(const AttArgs& a, int64_t bq, int64_t
   }
 }
 
+// keys of the sliding-window tail of query bq (0 without one)
+__device__ __forceinline__ int64_t n_win_keys(const AttArgs& a, int64_t bq) {
+  if (a.win == nullptr) return 0;
+  int64_t t = a.win_t[bq];
+  t = t < 0 ? 0 : (t > a.win_tmax ? a.win_tmax : t);
+  return t + 1 < a.win_n ? t + 1 : a.win_n;
+}
+
+// Encoded source of key j of query bq (j < lim, else -1): r >= 0 is row r of
+// the mode's cache, -2 - r is row r of the window ring, -1 a masked key.  nkm
+// is the count of the mode's own keys, which come first.
+template <int MODE>
+__device__ __forceinline__ int64_t key_code(const AttArgs& a, int64_t bq, int64_t j, int64_t lim, int64_t nkm) {
+  if (j >= lim) return -1;
+  if (j < nkm) return key_row<MODE>(a, bq, j, nkm, nkm);
+  int64_t t = a.win_t[bq];
+  t = t < 0 ? 0 : (t > a.win_tmax ? a.win_tmax : t);
+  const int64_t nkw = t + 1 < a.win_n ? t + 1 : a.win_n;
+  return -2 - (t - nkw + 1 + (j - nkm)) % a.win_ring;
+}
+
+template <typename T>
+__device__ __forceinline__ const T* key_ptr(const AttArgs& a, int64_t b, int64_t code) {
+  if (code >= 0) return static_cast<const T*>(a.kv) + (b * a.cap + code) * a.c;
+  if (code <= -2) return static_cast<const T*>(a.win) + (b * a.win_ring + (-2 - code)) * a.c;
+  return nullptr;
+}
+
 // ------------------------------------------------------------------ VALU path
 
 template <typename T, int MODE, int MAXD>
@@ -102,11 +135,11 @@ __global__ void __launch_bounds__(64) attend_valu_kernel(AttArgs a) {
   const int64_t split = blockIdx.x, h = blockIdx.y, bq = blockIdx.z;
   const int lane = threadIdx.x;
   const int64_t b = bq / a.n_q;
-  const int64_t nk = n_keys<MODE>(a, bq);
+  const int64_t nkm = n_keys<MODE>(a, bq);
+  const int64_t nk = nkm + n_win_keys(a, bq);
   const int64_t k0 = split * a.keys_per_split;
   const int64_t k1 = min(nk, k0 + a.keys_per_split);
   const T* q = static_cast<const T*>(a.q) + (bq * a.n_h + h) * a.c;
-  const T* kv = static_cast<const T*>(a.kv) + b * a.cap * a.c;
 
   float qv[MAXD], acc[MAXD];
 #pragma unroll
@@ -117,9 +150,8 @@ __global__ void __launch_bounds__(64) attend_valu_kernel(AttArgs a) {
   }
   float mrun = -INFINITY, lrun = 0.f;
   for (int64_t j = k0; j < k1; ++j) {
-    const int64_t r = key_row<MODE>(a, bq, j, nk, nk);
-    if (r < 0) continue;
-    const T* row = kv + r * a.c;
+    const T* row = key_ptr<T>(a, b, key_code<MODE>(a, bq, j, nk, nkm));
+    if (row == nullptr) continue;
     float cv[MAXD];
     float dot = 0.f;
 #pragma unroll
@@ -175,12 +207,12 @@ __global__ void __launch_bounds__(512) attend_mfma_kernel(AttArgs a) {
   const int64_t split = blockIdx.x / a.head_groups;
   const int64_t hg = blockIdx.x - split * a.head_groups;
   const int64_t b = bq / a.n_q;
-  const int64_t nk = n_keys<MODE>(a, bq);
+  const int64_t nkm = n_keys<MODE>(a, bq);
+  const int64_t nk = nkm + n_win_keys(a, bq);
   const int64_t k0 = split * a.keys_per_split;
   const int64_t k1 = min(nk, k0 + a.keys_per_split);
   const int64_t hbase = hg * 128 + hp * 32;  // first head of this wave
   const bool active = hbase < a.n_h;
-  const bf16_raw* kv = static_cast<const bf16_raw*>(a.kv) + b * a.cap * CD;
 
   // Q^T operand over this wave's half of c: lane holds head hbase + l32,
   // dims dh*HALF + ks*16 + g2*8 .. +7
@@ -217,9 +249,9 @@ __global__ void __launch_bounds__(512) attend_mfma_kernel(AttArgs a) {
         stv[i] = 0;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const int64_t r = key_row<MODE>(a, bq, kbase + 4 * kq + j, k1, nk);
-          stv[i] |= uint32_t(r >= 0) << j;
-          stg[i][j] = r >= 0 ? *reinterpret_cast<const uint4*>(kv + r * CD + dg * 8) : make_uint4(0, 0, 0, 0);
+          const bf16_raw* row = key_ptr<bf16_raw>(a, b, key_code<MODE>(a, bq, kbase + 4 * kq + j, k1, nkm));
+          stv[i] |= uint32_t(row != nullptr) << j;
+          stg[i][j] = row ? *reinterpret_cast<const uint4*>(row + dg * 8) : make_uint4(0, 0, 0, 0);
         }
       }
     }
@@ -456,16 +488,16 @@ __global__ void __launch_bounds__(512) attend512_kernel(AttArgs a) {
   const int64_t split = (rest / a.head_groups) * 8 + xcd;
   if (split >= a.splits) return;
   const int64_t b = bq / a.n_q;
-  const int64_t nk = n_keys<MODE>(a, bq);
+  const int64_t nkm = n_keys<MODE>(a, bq);
+  const int64_t nk = nkm + n_win_keys(a, bq);
   const int64_t k0 = split * a.keys_per_split;
   const int64_t k1 = min(nk, k0 + a.keys_per_split);
   const int64_t hbase = hg * HPG + hp * 32;
   const bool active = hbase < a.n_h;
-  const bf16_raw* kv = static_cast<const bf16_raw*>(a.kv) + b * a.cap * CD;
   const int64_t ntile = k1 > k0 ? (k1 - k0 + 31) / 32 : 0;
 
   if constexpr (MODE == kGather) {
-    for (int64_t j = tid; j < k1 - k0; j += 512) sRow[j] = int32_t(key_row<kGather>(a, bq, k0 + j, k1, nk));
+    for (int64_t j = tid; j < k1 - k0; j += 512) sRow[j] = int32_t(key_code<kGather>(a, bq, k0 + j, k1, nkm));
     __syncthreads();  // sRow ready for the tile loads
   }
   // each wave moves rows RPW*wave .. +RPW-1 of a tile: one 1 KB DMA load per row
@@ -478,10 +510,11 @@ __global__ void __launch_bounds__(512) attend512_kernel(AttArgs a) {
       if constexpr (MODE == kGather) {
         gr = (k0 + j < k1) ? sRow[j] : -1;
       } else {
-        gr = key_row<MODE>(a, bq, k0 + j, k1, nk);
+        gr = key_code<MODE>(a, bq, k0 + j, k1, nkm);
       }
       gr = __builtin_amdgcn_readfirstlane(int(gr));
-      const bf16_raw* src = gr >= 0 ? kv + gr * CD : g_zero_row;
+      const bf16_raw* src = key_ptr<bf16_raw>(a, b, gr);
+      if (src == nullptr) src = g_zero_row;
       const uint32_t lds_addr = (uint32_t)(uintptr_t)DLC_LDS(dst) + uint32_t(tile_row_off(row));
       dma_row(src, uint32_t(lane) * 16u, lds_addr);
     }
@@ -490,7 +523,7 @@ __global__ void __launch_bounds__(512) attend512_kernel(AttArgs a) {
   auto valid_mask = [&](int64_t tl) -> uint32_t {
     const int64_t j = tl * 32 + l32;
     bool v = k0 + j < k1;
-    if constexpr (MODE == kGather) v = v && sRow[j] >= 0;
+    if constexpr (MODE == kGather) v = v && sRow[j] != -1;
     return uint32_t(__ballot(v) & 0xffffffffu);
   };
   // the first two tiles and Q are in flight together
@@ -841,6 +874,18 @@ int common_checks(const char* name, int dtype, int64_t B, int64_t n_q, int64_t n
   return DLC_OK;
 }
 
+// the joined forms: the mode's keys and the window's in one attention
+int window_tail(const char* name, AttArgs& a, const void* Cwin, int64_t ring, int64_t n_win, const int64_t* t,
+                int64_t t_max) {
+  DLC_REQUIRE(Cwin != nullptr && t != nullptr, DLC_E_INVAL, "%s: NULL window ring or t", name);
+  DLC_REQUIRE(n_win >= 1 && ring >= n_win && t_max >= 0, DLC_E_SHAPE,
+              "%s: need 1 <= n_win <= ring and t_max >= 0 (n_win=%lld ring=%lld)", name, (long long)n_win,
+              (long long)ring);
+  DLC_REQUIRE(!mfma_ok(DLC_BF16, a.c) || aligned(Cwin, 16), DLC_E_INVAL, "%s: ring must be 16-byte aligned", name);
+  a.win = Cwin; a.win_ring = ring; a.win_n = n_win; a.win_t = t; a.win_tmax = t_max;
+  return DLC_OK;
+}
+
 }  // namespace
 }  // namespace dlc
 
@@ -887,6 +932,54 @@ int hca_attend(int dtype, int64_t B, int64_t n_q, int64_t n_h, int64_t c, int64_
   a.scale_log2 = (scale > 0.f ? scale : 1.f / std::sqrt(float(c))) * kLog2e;
   return run_attend<kDense>("hca_attend", dtype, a, B * n_q, t_max / m_prime, out, lse, ws, ws_bytes,
                            as_stream(stream));
+}
+
+
+size_t csa_attend_window_ws(int64_t B, int64_t n_q, int64_t n_h, int64_t c, int64_t k, int64_t n_win) {
+  if (B < 1 || n_q < 1 || n_h < 1 || c < 1 || k < 1 || n_win < 1) return 0;
+  return dlc::ws_bound(B * n_q, n_h, c, k + n_win);
+}
+
+size_t hca_attend_window_ws(int64_t B, int64_t n_q, int64_t n_h, int64_t c, int64_t cap, int64_t n_win) {
+  if (B < 1 || n_q < 1 || n_h < 1 || c < 1 || cap < 0 || n_win < 1) return 0;
+  return dlc::ws_bound(B * n_q, n_h, c, cap + n_win);
+}
+
+int csa_attend_window(int dtype, int64_t B, int64_t n_q, int64_t n_h, int64_t c, int64_t k, const void* q,
+                      const void* Ccomp, int64_t cap, const int32_t* idx, const int32_t* count, const void* Cwin,
+                      int64_t ring, int64_t n_win, const int64_t* t, int64_t t_max, float scale, float* out,
+                      float* lse, void* ws, size_t ws_bytes, void* stream) {
+  using namespace dlc;
+  int rc = common_checks("csa_attend_window", dtype, B, n_q, n_h, c, q, Ccomp, cap, out);
+  if (rc) return rc;
+  DLC_REQUIRE(k >= 1, DLC_E_INVAL, "csa_attend_window: k must be >= 1");
+  DLC_REQUIRE(idx && count, DLC_E_INVAL, "csa_attend_window: NULL idx or count");
+  AttArgs a{};
+  a.q = q; a.kv = Ccomp; a.idx = idx; a.count = count;
+  a.n_q = n_q; a.n_h = n_h; a.c = c; a.cap = cap; a.k = k;
+  a.scale_log2 = (scale > 0.f ? scale : 1.f / std::sqrt(float(c))) * kLog2e;
+  if ((rc = window_tail("csa_attend_window", a, Cwin, ring, n_win, t, t_max))) return rc;
+  return run_attend<kGather>("csa_attend_window", dtype, a, B * n_q, k + n_win, out, lse, ws, ws_bytes,
+                             as_stream(stream));
+}
+
+int hca_attend_window(int dtype, int64_t B, int64_t n_q, int64_t n_h, int64_t c, int64_t m_prime, const void* q,
+                      const void* Chca, int64_t cap, const int64_t* t, int64_t t_max, const void* Cwin, int64_t ring,
+                      int64_t n_win, float scale, float* out, float* lse, void* ws, size_t ws_bytes, void* stream) {
+  using namespace dlc;
+  int rc = common_checks("hca_attend_window", dtype, B, n_q, n_h, c, q, Chca, cap, out);
+  if (rc) return rc;
+  DLC_REQUIRE(m_prime >= 1 && t_max >= 0, DLC_E_INVAL, "hca_attend_window: need m' >= 1 and t_max >= 0");
+  DLC_REQUIRE(t != nullptr, DLC_E_INVAL, "hca_attend_window: NULL t");
+  DLC_REQUIRE(t_max / m_prime <= cap, DLC_E_SHAPE, "hca_attend_window: floor(t_max/m')=%lld exceeds cap=%lld",
+              (long long)(t_max / m_prime), (long long)cap);
+  AttArgs a{};
+  a.q = q; a.kv = Chca; a.t = t;
+  a.n_q = n_q; a.n_h = n_h; a.c = c; a.cap = cap; a.m_prime = m_prime; a.t_max = t_max;
+  a.scale_log2 = (scale > 0.f ? scale : 1.f / std::sqrt(float(c))) * kLog2e;
+  if ((rc = window_tail("hca_attend_window", a, Cwin, ring, n_win, t, t_max))) return rc;
+  return run_attend<kDense>("hca_attend_window", dtype, a, B * n_q, t_max / m_prime + n_win, out, lse, ws,
+                            ws_bytes, as_stream(stream));
 }
 
 size_t window_attend_ws(int64_t B, int64_t n_q, int64_t n_h, int64_t c, int64_t n_win) {

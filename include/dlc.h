@@ -196,6 +196,28 @@ int window_attend(int dtype, int64_t B, int64_t n_q, int64_t n_h, int64_t c, int
                   void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * csa_attend_window / hca_attend_window - csa_attend and hca_attend with the
+ * layer's sliding-window branch joined in: one attention over the selected
+ * (CSA) or visible (HCA) compressed entries followed by the window entries of
+ * the ring, as the pages concatenate them (see window_attend).  The window
+ * keys are a tail of the same key list, so both sets share the splits and the
+ * combine; the result equals csa_attend (hca_attend) followed by window_attend
+ * with o_in, up to rounding.  Arguments as for csa_attend / hca_attend plus
+ * the ring Cwin [B][ring][c] (token p at row p % ring, ring >= n_win), n_win,
+ * and, for the CSA form, the query positions t / t_max that place the window.
+ */
+size_t csa_attend_window_ws(int64_t B, int64_t n_q, int64_t n_h, int64_t c, int64_t k, int64_t n_win);
+int csa_attend_window(int dtype, int64_t B, int64_t n_q, int64_t n_h, int64_t c, int64_t k,
+                      const void* q, const void* Ccomp, int64_t cap, const int32_t* idx, const int32_t* count,
+                      const void* Cwin, int64_t ring, int64_t n_win, const int64_t* t, int64_t t_max,
+                      float scale, float* out, float* lse, void* ws, size_t ws_bytes, void* stream);
+size_t hca_attend_window_ws(int64_t B, int64_t n_q, int64_t n_h, int64_t c, int64_t cap, int64_t n_win);
+int hca_attend_window(int dtype, int64_t B, int64_t n_q, int64_t n_h, int64_t c, int64_t m_prime,
+                      const void* q, const void* Chca, int64_t cap, const int64_t* t, int64_t t_max,
+                      const void* Cwin, int64_t ring, int64_t n_win, float scale, float* out, float* lse,
+                      void* ws, size_t ws_bytes, void* stream);
+
+/*
  * dlc_project - dense projection out = A . W with fp32 accumulation, the
  * token projections that feed the compressor and the queries ([Scratch] §3:
  * C^a = H W^{aKV} and its siblings; §6.1-6.3 and §8: c^Q, q^I, w^I, q).

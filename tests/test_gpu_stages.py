@@ -331,3 +331,56 @@ def test_window_joins_compressed_branch_in_place(dtype, B, n_h, c, k, cap, count
         o_r, l_r = O.merge_lse(o1, l1, o2, l2)
         assert_rows_close(o[b, 0], o_r, TOL_ATT[dtype], f"joined b={b}")
         assert np.abs(lse[b, 0].cpu().numpy() - l_r).max() <= TOL_ATT[dtype]
+
+
+@pytest.mark.parametrize("dtype,B,n_h,c,k,cap,counts,ring", [
+    ("bf16", 4, 128, 512, 1024, 262208, [1024, 1024, 7, 0], 128),  # V4-Pro shape; one empty compressed part
+    ("bf16", 2, 16, 128, 64, 2048, [64, 30], 200),                 # c = 128 MFMA path, ring > n_win
+    ("f32", 2, 4, 16, 8, 40, [5, 8], 128),                          # VALU path
+])
+def test_csa_attend_window(dtype, B, n_h, c, k, cap, counts, ring):
+    """One attention over the selected entries followed by the window: the
+    oracle's merge of the two parts (pinned to the concatenated attention)."""
+    seed = 970 + c
+    n_win = 128
+    q = synth.normal((B, 1, n_h, c), seed, dtype=dtype)
+    Cc = synth.normal((B, cap, c), seed + 1, dtype=dtype)
+    R = _ring(B, ring, c, dtype, seed + 2)
+    g = torch.Generator().manual_seed(seed + 3)
+    idx = torch.full((B, 1, k), -1, dtype=torch.int32)
+    for b, n in enumerate(counts):
+        idx[b, 0, :n] = torch.sort(torch.randperm(cap, generator=g)[:n])[0].to(torch.int32)
+    cnt = torch.tensor(counts, dtype=torch.int32).reshape(B, 1)
+    t = torch.tensor([4 * cap + 3 + 5 * b for b in range(B)], dtype=torch.int64).reshape(B, 1)
+    t[-1, 0] = 60                                                   # a window shorter than n_win
+    o, lse = dlc.csa_attend_window(q.to(DEV), Cc.to(DEV), idx.to(DEV), cnt.to(DEV), R.to(DEV), t.to(DEV),
+                                   int(t.max()), n_win)
+    torch.cuda.synchronize()
+    for b in range(B):
+        sel = idx[b, 0, :counts[b]].numpy().astype(np.int64)
+        o1, l1 = O.csa_attend(q[b, 0], Cc[b], sel)
+        o2, l2 = _window_ref(q[b, 0], R[b], t[b, 0], n_win)
+        o_r, l_r = O.merge_lse(o1, l1, o2, l2)
+        assert_rows_close(o[b, 0], o_r, TOL_ATT[dtype], f"csa+window b={b}")
+        assert np.abs(lse[b, 0].cpu().numpy() - l_r).max() <= TOL_ATT[dtype]
+
+
+@pytest.mark.parametrize("dtype,B,n_h,c,mp,cap,ts,ring", [
+    ("bf16", 4, 128, 512, 128, 8194, [(1 << 20) + 3, (1 << 20) + 130, 200, 5], 384),  # HCA empty for t < m'
+    ("f32", 2, 3, 8, 4, 30, [50, 2], 16),
+])
+def test_hca_attend_window(dtype, B, n_h, c, mp, cap, ts, ring):
+    seed = 990 + c
+    n_win = 128 if ring >= 128 else 16
+    q = synth.normal((B, 1, n_h, c), seed, dtype=dtype)
+    Ch = synth.normal((B, cap, c), seed + 1, dtype=dtype)
+    R = _ring(B, ring, c, dtype, seed + 2)
+    t = torch.tensor(ts, dtype=torch.int64).reshape(B, 1)
+    o, lse = dlc.hca_attend_window(q.to(DEV), Ch.to(DEV), t.to(DEV), int(t.max()), mp, R.to(DEV), n_win)
+    torch.cuda.synchronize()
+    for b in range(B):
+        o1, l1 = O.hca_attend(q[b, 0], Ch[b], int(t[b, 0]), mp)
+        o2, l2 = _window_ref(q[b, 0], R[b], t[b, 0], n_win)
+        o_r, l_r = O.merge_lse(o1, l1, o2, l2)
+        assert_rows_close(o[b, 0], o_r, TOL_ATT[dtype], f"hca+window b={b}")
+        assert np.abs(lse[b, 0].cpu().numpy() - l_r).max() <= TOL_ATT[dtype]
