@@ -404,25 +404,7 @@ __global__ void __launch_bounds__(512) attend_mfma_kernel(AttArgs a) {
     a.lse[slot0 + hbase + l32] = lrun > 0.f ? (mrun + log2f(lrun)) * kLn2 : -INFINITY;
 }
 
-// ------------------------------------------------------------------ MFMA path, c = 512
-//
-// The V4-Pro shape gets a kernel that keeps every 32-key tile in LDS exactly
-// once, row-major, and feeds both products from it:
-//  * tiles arrive by direct global->LDS loads (global_load_lds_dwordx4: one
-//    instruction moves one 1 KB key row), three stages deep with two tiles in
-//    flight; no registers hold staged data;
-//  * Q.K^T reads the A operand (key rows) with ds_read_b128;
-//  * P.V reads the B operand with ds_read_b64_tr_b16, the gfx950 transposing
-//    LDS read: in each 16-lane group, lane j receives element j%4 of the
-//    8-byte chunks addressed by lanes j/4, j/4+4, j/4+8, j/4+12.  Lane i of a
-//    group addresses key row base+i/4 at dims c0+4*(i%4), so lane j ends up
-//    with dim c0+j of keys base..base+3 - four consecutive keys of one dim,
-//    which is the packed-k layout the MFMA wants;
-//  * barriers are plain s_barrier after an LDS-only wait, so the tile loads in
-//    flight are never drained by a barrier; each tile is waited for with an
-//    explicit vmcnt that leaves the younger tile outstanding.
-// Wave w owns heads 32*(w/2) .. +31 and half w%2 of the 512 dims, as in the
-// generic kernel; the two halves' partial S^T are added through LDS.
+// ------------------------------------------------------------------ shared by the c = 512 kernel
 
 __device__ __align__(16) bf16_raw g_zero_row[512];  // masked keys load this row
 
@@ -440,49 +422,49 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_s_barrier();
 }
 
-// LDS layout of a 32-key tile (gfx950 LDS: 64 banks of 4 bytes): key row r
-// starts at byte 1024*r + 16*t(r), t(4a+j) = 16a + a%4 + 4j.  Row starts then
-// differ mod 256 bytes so that
-//  * a ds_read_b128 of 16 consecutive rows at one 16-byte column (the Q.K^T A
-//    operand, 16 lanes per pass) touches 16 distinct 4-bank groups, and
-//  * a ds_read_b64_tr_b16 of 4 consecutive rows x 64 bytes (the P.V B operand,
-//    32 lanes per pass) touches 4 disjoint 16-bank groups;
-// both are conflict-free.  A row stays 1 KB contiguous, as one direct load
-// writes it.
-constexpr int kTileBytes = 34816;   // 1024*31 + 16*t(31) + 1024, rounded up to 1 KB
+constexpr int kTileBytes = 34816;   // 32 rows of 1 KB at the offsets of h16_row_off, rounded up to 1 KB
 constexpr int kMaxGatherKeys = 2048;  // keys per split whose rows sit in LDS
-
-__device__ __forceinline__ constexpr int tile_row_off(int r) {
-  return 1024 * r + 16 * (16 * (r >> 2) + ((r >> 2) & 3) + 4 * (r & 3));
-}
-
 typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+// ------------------------------------------------------------------ MFMA path, c = 512, 16 heads per wave
+//
+// Eight waves, each owning 16 heads over all 512 dims, so no partial S^T is
+// exchanged and no softmax is computed twice.  Per 32-key tile and wave:
+//   S^T[16 keys][16 heads] = K[16 keys][32 dims] . Q^T[32 dims][16 heads]
+//     (v_mfma_f32_16x16x32_bf16, two 16-key halves x 16 dim steps),
+//   O[16 heads][16 dims] += P[16 heads][32 keys] . K[32 keys][16 dims]
+//     (32 output tiles).
+// Q (64 VGPRs) and O (128) stay in registers at two waves per SIMD.  The S^T
+// accumulator of lane l holds head l%16 and keys 4*(l/16) .. +3 of each half,
+// which is exactly the A operand P needs (its k-slots relabelled to those
+// keys); the B operand reads the same keys through ds_read_b64_tr_b16.  Tiles
+// arrive by direct global->LDS loads (dma_row), three stages in flight.
+//
+// LDS row layout of this kernel: row r starts at 1024*r + d(r) with
+// d(r) = 256*(r/8) + 32*(r%8) + 16*((r/8)%2), so that
+//  * the 16 rows of a ds_read_b128 pass (Q.K^T A operand) start on 16
+//    distinct 4-bank groups, and
+//  * the 8 rows x 32 bytes of a ds_read_b64_tr_b16 pass (P.V B operand,
+//    32 lanes) fall on 8 disjoint 8-bank groups.
+
+__device__ __forceinline__ constexpr int h16_row_off(int r) {
+  return 1024 * r + 256 * (r >> 3) + 32 * (r & 7) + 16 * ((r >> 3) & 1);
+}
+static_assert(h16_row_off(31) + 1024 <= kTileBytes, "tile layout");
 
 template <int MODE>
 __global__ void __launch_bounds__(512) attend512_kernel(AttArgs a) {
-  constexpr int CD = 512, HALF = 256, KSH = 16, NTH = 8;
-  constexpr int NST = 3;                // tile stages, two tiles in flight
-  constexpr int RPW = 4;                // key rows each wave moves per tile
-  constexpr int HPG = 128;              // heads per workgroup: 4 slices of 32, each split over 2 waves
-  // one array per stage: distinct objects let the compiler see that reads of
-  // the current stage never alias the loads still landing in the others
+  constexpr int CD = 512, KS = 16, NT = 32;  // 32-dim Q.K^T steps; 16-dim output tiles
+  constexpr int NST = 3, RPW = 4, HPG = 128;
   __shared__ __attribute__((aligned(1024))) unsigned char sK0[kTileBytes];
   __shared__ __attribute__((aligned(1024))) unsigned char sK1[kTileBytes];
   __shared__ __attribute__((aligned(1024))) unsigned char sK2[kTileBytes];
-  // partial S^T of every wave: lane-major, 16 values + 4 pad per lane so that
-  // four 16-byte accesses per lane are free of bank conflicts
-  constexpr int XROW = 20;
-  __shared__ __attribute__((aligned(16))) float sX[8 * 64 * XROW];
   __shared__ int32_t sRow[MODE == kGather ? kMaxGatherKeys : 1];
 
   const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: lets addresses live in SGPRs
-  const int l32 = lane & 31, g2 = lane >> 5, G = lane >> 4, i16 = lane & 15;
-  const int hp = wave >> 1, dh = wave & 1;  // head slice of 32, half of c
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int r16 = lane & 15, g = lane >> 4, i16 = lane & 15;
   const int64_t bq = blockIdx.y;
-  // XCD-aware order: workgroups are dealt round-robin to the 8 XCDs, so the
-  // head groups of one key split get ids that are equal mod 8 and share that
-  // XCD's L2 for the split's key rows
   const int64_t xcd = blockIdx.x & 7, rest = blockIdx.x >> 3;
   const int64_t hg = rest % a.head_groups;
   const int64_t split = (rest / a.head_groups) * 8 + xcd;
@@ -492,20 +474,19 @@ __global__ void __launch_bounds__(512) attend512_kernel(AttArgs a) {
   const int64_t nk = nkm + n_win_keys(a, bq);
   const int64_t k0 = split * a.keys_per_split;
   const int64_t k1 = min(nk, k0 + a.keys_per_split);
-  const int64_t hbase = hg * HPG + hp * 32;
+  const int64_t hbase = hg * HPG + wave * 16;
   const bool active = hbase < a.n_h;
   const int64_t ntile = k1 > k0 ? (k1 - k0 + 31) / 32 : 0;
 
   if constexpr (MODE == kGather) {
     for (int64_t j = tid; j < k1 - k0; j += 512) sRow[j] = int32_t(key_code<kGather>(a, bq, k0 + j, k1, nkm));
-    __syncthreads();  // sRow ready for the tile loads
+    __syncthreads();
   }
-  // each wave moves rows RPW*wave .. +RPW-1 of a tile: one 1 KB DMA load per row
-  auto issue = [&](unsigned char* dst, int st, int64_t tl) {
+  auto issue = [&](unsigned char* dst, int64_t tl) {
 #pragma unroll
     for (int r = 0; r < RPW; ++r) {
       const int row = RPW * wave + r;
-      const int64_t j = tl * 32 + row;  // key position within the split
+      const int64_t j = tl * 32 + row;
       int64_t gr;
       if constexpr (MODE == kGather) {
         gr = (k0 + j < k1) ? sRow[j] : -1;
@@ -515,195 +496,152 @@ __global__ void __launch_bounds__(512) attend512_kernel(AttArgs a) {
       gr = __builtin_amdgcn_readfirstlane(int(gr));
       const bf16_raw* src = key_ptr<bf16_raw>(a, b, gr);
       if (src == nullptr) src = g_zero_row;
-      const uint32_t lds_addr = (uint32_t)(uintptr_t)DLC_LDS(dst) + uint32_t(tile_row_off(row));
+      const uint32_t lds_addr = (uint32_t)(uintptr_t)DLC_LDS(dst) + uint32_t(h16_row_off(row));
       dma_row(src, uint32_t(lane) * 16u, lds_addr);
     }
   };
-  // bit j: key j of tile tl is valid (masked keys were loaded as zero rows)
   auto valid_mask = [&](int64_t tl) -> uint32_t {
-    const int64_t j = tl * 32 + l32;
+    const int64_t j = tl * 32 + (lane & 31);
     bool v = k0 + j < k1;
     if constexpr (MODE == kGather) v = v && sRow[j] != -1;
     return uint32_t(__ballot(v) & 0xffffffffu);
   };
-  // the first two tiles and Q are in flight together
-  if (ntile > 0) issue(sK0, 0, 0);
-  if (ntile > 1) issue(sK1, 1, 1);
-  // Q^T operand over this wave's half of c: lane holds head hbase + l32,
-  // dims dh*HALF + ks*16 + g2*8 .. +7; heads past n_h read head n_h-1 (their
-  // S^T columns and outputs are never used)
-  bf16x8 qf[KSH];
+  if (ntile > 0) issue(sK0, 0);
+  if (ntile > 1) issue(sK1, 1);
+  // Q^T operand: lane holds head hbase + r16, dims 32*ks + 8*g .. +7; heads
+  // past n_h read head n_h-1 (their columns and outputs are never used)
+  bf16x8 qf[KS];
   {
-    const int64_t h = min(hbase + l32, a.n_h - 1);
-    const bf16_raw* qp = static_cast<const bf16_raw*>(a.q) + (bq * a.n_h + h) * CD + dh * HALF + g2 * 8;
+    const int64_t h = min(hbase + r16, a.n_h - 1);
+    const bf16_raw* qp = static_cast<const bf16_raw*>(a.q) + (bq * a.n_h + h) * CD + g * 8;
 #pragma unroll
-    for (int ks = 0; ks < KSH; ++ks) qf[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(qp + ks * 16));
-    // consume the Q loads here (this also waits for the two tiles issued
-    // above), so no wait for them is left inside the tile loop
+    for (int ks = 0; ks < KS; ++ks) qf[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(qp + ks * 32));
 #pragma unroll
-    for (int ks = 0; ks < KSH; ++ks) asm volatile("" ::"v"(qf[ks]));
+    for (int ks = 0; ks < KS; ++ks) asm volatile("" ::"v"(qf[ks]));
   }
-  f32x16 o[NTH];
+  f32x4 o[NT];
 #pragma unroll
-  for (int nt = 0; nt < NTH; ++nt)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) o[nt][r] = 0.f;
-  float mrun = -INFINITY, lrun = 0.f;
-  // per-lane LDS byte offsets within a tile (rows laid out by tile_row_off)
-  const uint32_t qk_off = uint32_t(tile_row_off(l32) + dh * 512 + 16 * g2);
-  uint32_t pv_off[2][2];
-#pragma unroll
-  for (int u = 0; u < 2; ++u)
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-      pv_off[u][h] = uint32_t(tile_row_off(16 * u + 8 * h + 4 * g2 + (i16 >> 2)) + dh * 512 + 32 * (G & 1) + 8 * (i16 & 3));
+  for (int nt = 0; nt < NT; ++nt) o[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float mrun = -INFINITY, lrun = 0.f;  // for head hbase + r16
 
-  auto tile_step = [&](const unsigned char* tile, unsigned char* next, int st, int64_t it) {
-    wait_vmcnt(it + 1 < ntile ? RPW : 0);  // tile it has landed (tile it+1 may still fly)
-    lds_barrier();                         // ... for every wave; stage (it+2)%3 and sX are free
-    if (it + 2 < ntile) issue(next, (st + 2) % NST, it + 2);
-    f32x16 sx;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) sx[r] = 0.f;
-    if (active) {
-      // partial S^T = K . Q^T over this wave's half of c; the next batch of
-      // fragments is in flight while the current one feeds the MFMAs
-      const unsigned char* krow = tile + qk_off;
-      bf16x8 ka[4], kb[4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) ka[u] = *reinterpret_cast<const bf16x8*>(krow + 32 * u);
-#pragma unroll
-      for (int k4 = 0; k4 < KSH; k4 += 4) {
-        if (k4 + 4 < KSH) {
-#pragma unroll
-          for (int u = 0; u < 4; ++u) kb[u] = *reinterpret_cast<const bf16x8*>(krow + 32 * (k4 + 4 + u));
-        }
-        asm volatile("" ::: "memory");
-#pragma unroll
-        for (int u = 0; u < 4; ++u) sx = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[u], qf[k4 + u], sx, 0, 0, 0);
-#pragma unroll
-        for (int u = 0; u < 4; ++u) ka[u] = kb[u];
-      }
-      float4* xw = reinterpret_cast<float4*>(&sX[(wave * 64 + lane) * XROW]);
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4)
-        xw[q4] = make_float4(sx[4 * q4], sx[4 * q4 + 1], sx[4 * q4 + 2], sx[4 * q4 + 3]);
-    }
-    const uint32_t vmask = valid_mask(it);
+  // per-lane LDS offsets: Q.K^T A operand (row r16 of each half, chunk 4*ks + g)
+  const uint32_t qk_off0 = uint32_t(h16_row_off(r16) + 16 * g);
+  const uint32_t qk_off1 = uint32_t(h16_row_off(16 + r16) + 16 * g);
+  // P.V B operand: keys 4*g + i16/4 (+16 for the second half), dims 16*nt + 4*(i16%4)
+  const uint32_t pv_off0 = uint32_t(h16_row_off(4 * g + (i16 >> 2)) + 8 * (i16 & 3));
+  const uint32_t pv_off1 = uint32_t(h16_row_off(16 + 4 * g + (i16 >> 2)) + 8 * (i16 & 3));
+
+  auto tile_step = [&](const unsigned char* tile, unsigned char* next, int64_t it) {
+    wait_vmcnt(it + 1 < ntile ? RPW : 0);
     lds_barrier();
+    if (it + 2 < ntile) issue(next, it + 2);
+    const uint32_t vmask = valid_mask(it);
     if (!active) return;
-    // full S^T = both halves; lane holds head l32, keys kr(r) = 8*(r/4) + 4*g2 + r%4
-    // add the partner's half, eight values at a time (bounded register use)
-    {
-      const float4* xr = reinterpret_cast<const float4*>(&sX[((wave ^ 1) * 64 + lane) * XROW]);
+    // S^T of both 16-key halves, the next two fragments in flight
+    f32x4 s0 = f32x4{0.f, 0.f, 0.f, 0.f}, s1 = s0;
+    bf16x8 ka0 = *reinterpret_cast<const bf16x8*>(tile + qk_off0);
+    bf16x8 ka1 = *reinterpret_cast<const bf16x8*>(tile + qk_off1);
 #pragma unroll
-      for (int hq = 0; hq < 2; ++hq) {
-        const float4 v0 = xr[2 * hq], v1 = xr[2 * hq + 1];
-        const float ov[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int r = 8 * hq + e;
-          sx[r] = dh == 0 ? sx[r] + ov[e] : ov[e] + sx[r];
-        }
-        asm volatile("" ::: "memory");
+    for (int ks = 0; ks < KS; ++ks) {
+      bf16x8 kn0 = ka0, kn1 = ka1;
+      if (ks + 1 < KS) {
+        kn0 = *reinterpret_cast<const bf16x8*>(tile + qk_off0 + 64 * (ks + 1));
+        kn1 = *reinterpret_cast<const bf16x8*>(tile + qk_off1 + 64 * (ks + 1));
       }
+      s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka0, qf[ks], s0, 0, 0, 0);
+      s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka1, qf[ks], s1, 0, 0, 0);
+      ka0 = kn0;
+      ka1 = kn1;
+      asm volatile("" ::: "memory");
     }
+    // logits: lane holds head r16, keys 4g+e (s0) and 16+4g+e (s1)
+    float x[8];
     float tmax = -INFINITY;
-    if (vmask == 0xffffffffu) {  // a full tile (wave-uniform): no mask
+    const uint32_t vm = vmask >> (4 * g);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        sx[r] *= a.scale_log2;
-        tmax = fmaxf(tmax, sx[r]);
-      }
-    } else {
-      const uint32_t vm = vmask >> (4 * g2);  // key 8*(r/4) + 4*g2 + r%4 -> bit 8*(r/4) + r%4
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        sx[r] = ((vm >> (8 * (r >> 2) + (r & 3))) & 1u) ? sx[r] * a.scale_log2 : -INFINITY;
-        tmax = fmaxf(tmax, sx[r]);
-      }
+    for (int e = 0; e < 4; ++e) {
+      x[e] = ((vm >> e) & 1u) ? s0[e] * a.scale_log2 : -INFINITY;
+      x[4 + e] = ((vm >> (16 + e)) & 1u) ? s1[e] * a.scale_log2 : -INFINITY;
     }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) tmax = fmaxf(tmax, x[e]);
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
     tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-    // lazy running max (see the generic kernel)
+    // lazy running max: O is rescaled only when the max grows by more than 2^8
     const bool move = tmax > mrun + 8.f;
     if (__any(move)) {
       const float mnew = move ? tmax : mrun;
       const float alpha = mrun == -INFINITY ? 0.f : exp2f(mrun - mnew);
       lrun *= alpha;
       mrun = mnew;
+      // O rows are heads 4*g + e
+      float al[4];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float al = __shfl(alpha, 8 * (r >> 2) + 4 * g2 + (r & 3));
+      for (int e = 0; e < 4; ++e) al[e] = __shfl(alpha, 4 * g + e);
 #pragma unroll
-        for (int nt = 0; nt < NTH; ++nt) o[nt][r] *= al;
-      }
+      for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[nt][e] *= al[e];
     }
-    // v_exp_f32 directly: masked keys give exp2(-inf) = 0; a head with nothing
-    // valid yet has mrun = -inf, and exponentiates against 0 instead
     const float mr = mrun == -INFINITY ? 0.f : mrun;
     float psum = 0.f;
+    bf16x8 pa;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      sx[r] = __builtin_amdgcn_exp2f(sx[r] - mr);
-      psum += sx[r];
+    for (int e = 0; e < 8; ++e) {
+      const float p = __builtin_amdgcn_exp2f(x[e] - mr);
+      psum += p;
+      pa[e] = (__bf16)p;
     }
+    psum += __shfl_xor(psum, 16);
     psum += __shfl_xor(psum, 32);
     lrun += psum;
-    bf16x8 pa[2];
-#pragma unroll
-    for (int uu = 0; uu < 2; ++uu)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) pa[uu][e] = (__bf16)sx[8 * uu + e];
-    // B operand (keys 16u + 8h + 4*g2 + 0..3 for slots 4h .. 4h+3, dim
-    // dh*HALF + nt*32 + l32) from two transposing reads
-    auto vfrag = [&](int nt, int u) {
+    // P.V: B operand lane holds dim 16*nt + i16 of keys 4g..4g+3 and 16+4g..16+4g+3
+    auto vfrag = [&](int nt) {
       const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (__attribute__((address_space(3))) s16x4*)DLC_LDS(tile + pv_off[u][0] + 64 * nt));
+          (__attribute__((address_space(3))) s16x4*)DLC_LDS(tile + pv_off0 + 32 * nt));
       const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (__attribute__((address_space(3))) s16x4*)DLC_LDS(tile + pv_off[u][1] + 64 * nt));
+          (__attribute__((address_space(3))) s16x4*)DLC_LDS(tile + pv_off1 + 32 * nt));
       return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
     };
-    // fragments in batches of four (two output tiles x both key halves), the
-    // next batch in flight while the current one feeds the MFMAs
-    bf16x8 va[4], vb[4];
+    bf16x8 va[2], vb[2];
+    va[0] = vfrag(0);
+    va[1] = vfrag(1);
 #pragma unroll
-    for (int u = 0; u < 4; ++u) va[u] = vfrag(u >> 1, u & 1);
-#pragma unroll
-    for (int n2 = 0; n2 < NTH; n2 += 2) {
-      if (n2 + 2 < NTH) {
-#pragma unroll
-        for (int u = 0; u < 4; ++u) vb[u] = vfrag(n2 + 2 + (u >> 1), u & 1);
+    for (int n2 = 0; n2 < NT; n2 += 2) {
+      if (n2 + 2 < NT) {
+        vb[0] = vfrag(n2 + 2);
+        vb[1] = vfrag(n2 + 3);
       }
+      o[n2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, va[0], o[n2], 0, 0, 0);
+      o[n2 + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, va[1], o[n2 + 1], 0, 0, 0);
+      va[0] = vb[0];
+      va[1] = vb[1];
       asm volatile("" ::: "memory");
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
-        o[n2 + (u >> 1)] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa[u & 1], va[u], o[n2 + (u >> 1)], 0, 0, 0);
-#pragma unroll
-      for (int u = 0; u < 4; ++u) va[u] = vb[u];
     }
   };
   for (int64_t it = 0; it < ntile; it += NST) {
-    tile_step(sK0, sK2, 0, it);
-    if (it + 1 < ntile) tile_step(sK1, sK0, 1, it + 1);
-    if (it + 2 < ntile) tile_step(sK2, sK1, 2, it + 2);
+    tile_step(sK0, sK2, it);
+    if (it + 1 < ntile) tile_step(sK1, sK0, it + 1);
+    if (it + 2 < ntile) tile_step(sK2, sK1, it + 2);
   }
 
   if (!active) return;
+  // normalise and write: o[nt][e] is head 4*g + e, dim 16*nt + i16
   const int64_t slot0 = (bq * a.splits + split) * a.n_h;
 #pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const int hr = 8 * (r >> 2) + 4 * g2 + (r & 3);
+  for (int e = 0; e < 4; ++e) {
+    const int hr = 4 * g + e;
     const float l = __shfl(lrun, hr);
     const float inv = l > 0.f ? 1.f / l : 0.f;
     const int64_t h = hbase + hr;
     if (h < a.n_h) {
-      float* op = a.o + (slot0 + h) * CD + dh * HALF + l32;
+      float* op = a.o + (slot0 + h) * CD + i16;
 #pragma unroll
-      for (int nt = 0; nt < NTH; ++nt) op[nt * 32] = o[nt][r] * inv;
+      for (int nt = 0; nt < NT; ++nt) op[16 * nt] = o[nt][e] * inv;
     }
   }
-  if (dh == 0 && g2 == 0 && a.lse && hbase + l32 < a.n_h)
-    a.lse[slot0 + hbase + l32] = lrun > 0.f ? (mrun + log2f(lrun)) * kLn2 : -INFINITY;
+  if (g == 0 && a.lse && hbase + r16 < a.n_h)
+    a.lse[slot0 + hbase + r16] = lrun > 0.f ? (mrun + log2f(lrun)) * kLn2 : -INFINITY;
 }
 
 // ------------------------------------------------------------------ combine
