@@ -437,8 +437,14 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 // Q (64 VGPRs) and O (128) stay in registers at two waves per SIMD.  The S^T
 // accumulator of lane l holds head l%16 and keys 4*(l/16) .. +3 of each half,
 // which is exactly the A operand P needs (its k-slots relabelled to those
-// keys); the B operand reads the same keys through ds_read_b64_tr_b16.  Tiles
-// arrive by direct global->LDS loads (dma_row), three stages in flight.
+// keys); the B operand reads the same keys through ds_read_b64_tr_b16.
+//
+// Pipeline: tiles arrive by direct global->LDS loads (dma_row) into a ring of
+// four buffers, three tiles ahead.  Step i runs O += P_i . V_i interleaved
+// with S^T_{i+1} = K_{i+1} . Q^T (four MFMAs per 32-dim step, every LDS
+// operand read one step before its MFMA), then the softmax of tile i+1; the
+// per-head max and sum use row swaps (v_permlane16/32_swap) rather than LDS
+// permutes, which would queue behind the tile reads.
 //
 // LDS row layout of this kernel: row r starts at 1024*r + d(r) with
 // d(r) = 256*(r/8) + 32*(r%8) + 16*((r/8)%2), so that
@@ -452,13 +458,29 @@ __device__ __forceinline__ constexpr int h16_row_off(int r) {
 }
 static_assert(h16_row_off(31) + 1024 <= kTileBytes, "tile layout");
 
+// Lane reductions over the four lanes l%16 + 16*g (g = 0..3) that hold one
+// head: v_permlane16_swap / v_permlane32_swap exchange whole rows between two
+// copies of the value, so max/sum of the two results pairs every lane with
+// its partner 16 (then 32) lanes away.  Plain VALU, unlike ds_bpermute, which
+// queues behind the tile reads in the LDS pipe.
+__device__ __forceinline__ float head_max4(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float head_sum4(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 template <int MODE>
 __global__ void __launch_bounds__(512) attend512_kernel(AttArgs a) {
   constexpr int CD = 512, KS = 16, NT = 32;  // 32-dim Q.K^T steps; 16-dim output tiles
-  constexpr int NST = 3, RPW = 4, HPG = 128;
-  __shared__ __attribute__((aligned(1024))) unsigned char sK0[kTileBytes];
-  __shared__ __attribute__((aligned(1024))) unsigned char sK1[kTileBytes];
-  __shared__ __attribute__((aligned(1024))) unsigned char sK2[kTileBytes];
+  constexpr int NST = 4, RPW = 4, HPG = 128;
+  __shared__ __attribute__((aligned(1024))) unsigned char sK[NST * kTileBytes];
   __shared__ int32_t sRow[MODE == kGather ? kMaxGatherKeys : 1];
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -477,27 +499,47 @@ __global__ void __launch_bounds__(512) attend512_kernel(AttArgs a) {
   const int64_t hbase = hg * HPG + wave * 16;
   const bool active = hbase < a.n_h;
   const int64_t ntile = k1 > k0 ? (k1 - k0 + 31) / 32 : 0;
+  // positions behind the key codes, read once: ring slot of window key j is
+  // (mbase + j) mod cap (window mode), of tail key j >= nkm (wbase + j) mod win_ring
+  int64_t mbase = 0, wbase = 0;
+  if constexpr (MODE == kWindow) {
+    int64_t t = a.t[bq];
+    t = t < 0 ? 0 : (t > a.t_max ? a.t_max : t);
+    mbase = t - nkm + 1;
+  }
+  if (a.win != nullptr) {
+    int64_t t = a.win_t[bq];
+    t = t < 0 ? 0 : (t > a.win_tmax ? a.win_tmax : t);
+    wbase = t - (nk - nkm) + 1 - nkm;
+  }
+  const bf16_raw* zrow = g_zero_row;
+  asm volatile("" : "+s"(zrow));  // keep the masked-key source in SGPRs
 
   if constexpr (MODE == kGather) {
     for (int64_t j = tid; j < k1 - k0; j += 512) sRow[j] = int32_t(key_code<kGather>(a, bq, k0 + j, k1, nkm));
     __syncthreads();
   }
-  auto issue = [&](unsigned char* dst, int64_t tl) {
+  const uint32_t lds0 = (uint32_t)(uintptr_t)DLC_LDS(sK);
+  auto issue = [&](int64_t tl) {
+    const uint32_t buf = lds0 + uint32_t(tl & (NST - 1)) * kTileBytes;
 #pragma unroll
     for (int r = 0; r < RPW; ++r) {
       const int row = RPW * wave + r;
-      const int64_t j = tl * 32 + row;
-      int64_t gr;
+      const int64_t j = k0 + tl * 32 + row;
+      int64_t code;
       if constexpr (MODE == kGather) {
-        gr = (k0 + j < k1) ? sRow[j] : -1;
+        code = j < k1 ? sRow[j - k0] : -1;
+      } else if (j >= k1) {
+        code = -1;
+      } else if (j < nkm) {
+        code = MODE == kWindow ? (mbase + j) % a.cap : j;
       } else {
-        gr = key_code<MODE>(a, bq, k0 + j, k1, nkm);
+        code = -2 - (wbase + j) % a.win_ring;
       }
-      gr = __builtin_amdgcn_readfirstlane(int(gr));
-      const bf16_raw* src = key_ptr<bf16_raw>(a, b, gr);
-      if (src == nullptr) src = g_zero_row;
-      const uint32_t lds_addr = (uint32_t)(uintptr_t)DLC_LDS(dst) + uint32_t(h16_row_off(row));
-      dma_row(src, uint32_t(lane) * 16u, lds_addr);
+      code = __builtin_amdgcn_readfirstlane(int(code));
+      const bf16_raw* src = key_ptr<bf16_raw>(a, b, code);
+      if (src == nullptr) src = zrow;
+      dma_row(src, uint32_t(lane) * 16u, buf + uint32_t(h16_row_off(row)));
     }
   };
   auto valid_mask = [&](int64_t tl) -> uint32_t {
@@ -506,8 +548,11 @@ __global__ void __launch_bounds__(512) attend512_kernel(AttArgs a) {
     if constexpr (MODE == kGather) v = v && sRow[j] != -1;
     return uint32_t(__ballot(v) & 0xffffffffu);
   };
-  if (ntile > 0) issue(sK0, 0);
-  if (ntile > 1) issue(sK1, 1);
+  // tiles 0..2 in flight before the loop; tile i+3 is issued once every wave
+  // is past tile i-1 (the barrier of step i)
+  if (ntile > 0) issue(0);
+  if (ntile > 1) issue(1);
+  if (ntile > 2) issue(2);
   // Q^T operand: lane holds head hbase + r16, dims 32*ks + 8*g .. +7; heads
   // past n_h read head n_h-1 (their columns and outputs are never used)
   bf16x8 qf[KS];
@@ -516,9 +561,13 @@ __global__ void __launch_bounds__(512) attend512_kernel(AttArgs a) {
     const bf16_raw* qp = static_cast<const bf16_raw*>(a.q) + (bq * a.n_h + h) * CD + g * 8;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) qf[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(qp + ks * 32));
+    // wait for Q here, together with the first three tiles, so that no
+    // vector-memory wait for Q lands inside the tile loop (it would drain
+    // the tile loads in flight)
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) asm volatile("" ::"v"(qf[ks]));
   }
+
   f32x4 o[NT];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) o[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -530,43 +579,90 @@ __global__ void __launch_bounds__(512) attend512_kernel(AttArgs a) {
   // P.V B operand: keys 4*g + i16/4 (+16 for the second half), dims 16*nt + 4*(i16%4)
   const uint32_t pv_off0 = uint32_t(h16_row_off(4 * g + (i16 >> 2)) + 8 * (i16 & 3));
   const uint32_t pv_off1 = uint32_t(h16_row_off(16 + 4 * g + (i16 >> 2)) + 8 * (i16 & 3));
+  auto tile_ptr = [&](int64_t tl) { return sK + (tl & (NST - 1)) * kTileBytes; };
+  auto kfrag = [&](const unsigned char* tile, uint32_t off, int ks) {
+    return *reinterpret_cast<const bf16x8*>(tile + off + 64 * ks);
+  };
+  auto vfrag = [&](const unsigned char* tile, int nt) {
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) s16x4*)DLC_LDS(tile + pv_off0 + 32 * nt));
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) s16x4*)DLC_LDS(tile + pv_off1 + 32 * nt));
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  };
 
-  auto tile_step = [&](const unsigned char* tile, unsigned char* next, int64_t it) {
-    wait_vmcnt(it + 1 < ntile ? RPW : 0);
-    lds_barrier();
-    if (it + 2 < ntile) issue(next, it + 2);
-    const uint32_t vmask = valid_mask(it);
-    if (!active) return;
-    // S^T of both 16-key halves, the next two fragments in flight
-    f32x4 s0 = f32x4{0.f, 0.f, 0.f, 0.f}, s1 = s0;
-    bf16x8 ka0 = *reinterpret_cast<const bf16x8*>(tile + qk_off0);
-    bf16x8 ka1 = *reinterpret_cast<const bf16x8*>(tile + qk_off1);
+  // S^T of one tile alone (the first)
+  f32x4 s0, s1;
+  auto qk_only = [&](const unsigned char* tq) {
+    s0 = f32x4{0.f, 0.f, 0.f, 0.f};
+    s1 = s0;
+    bf16x8 ka0 = kfrag(tq, qk_off0, 0), ka1 = kfrag(tq, qk_off1, 0);
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      bf16x8 kn0 = ka0, kn1 = ka1;
+      bf16x8 kb0 = ka0, kb1 = ka1;
       if (ks + 1 < KS) {
-        kn0 = *reinterpret_cast<const bf16x8*>(tile + qk_off0 + 64 * (ks + 1));
-        kn1 = *reinterpret_cast<const bf16x8*>(tile + qk_off1 + 64 * (ks + 1));
+        kb0 = kfrag(tq, qk_off0, ks + 1);
+        kb1 = kfrag(tq, qk_off1, ks + 1);
       }
       s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka0, qf[ks], s0, 0, 0, 0);
       s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka1, qf[ks], s1, 0, 0, 0);
-      ka0 = kn0;
-      ka1 = kn1;
-      asm volatile("" ::: "memory");
+      ka0 = kb0;
+      ka1 = kb1;
+      __builtin_amdgcn_sched_barrier(0);
     }
-    // logits: lane holds head r16, keys 4g+e (s0) and 16+4g+e (s1)
+  };
+  // O += P . V of tile tp and, interleaved, S^T of tile tq: four MFMAs per
+  // step; each operand register is refilled for the next step right after
+  // the MFMA that reads it is issued
+  bf16x8 pa;
+  auto pv_qk = [&](const unsigned char* tp, const unsigned char* tq) {
+    s0 = f32x4{0.f, 0.f, 0.f, 0.f};
+    s1 = s0;
+    bf16x8 ka0 = kfrag(tq, qk_off0, 0), ka1 = kfrag(tq, qk_off1, 0);
+    bf16x8 va0 = vfrag(tp, 0), va1 = vfrag(tp, 1);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka0, qf[ks], s0, 0, 0, 0);
+      if (ks + 1 < KS) ka0 = kfrag(tq, qk_off0, ks + 1);
+      o[2 * ks] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, va0, o[2 * ks], 0, 0, 0);
+      if (ks + 1 < KS) va0 = vfrag(tp, 2 * ks + 2);
+      s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka1, qf[ks], s1, 0, 0, 0);
+      if (ks + 1 < KS) ka1 = kfrag(tq, qk_off1, ks + 1);
+      o[2 * ks + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, va1, o[2 * ks + 1], 0, 0, 0);
+      if (ks + 1 < KS) va1 = vfrag(tp, 2 * ks + 3);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  auto pv_only = [&](const unsigned char* tp) {
+    bf16x8 va0 = vfrag(tp, 0), va1 = vfrag(tp, 1);
+#pragma unroll
+    for (int n2 = 0; n2 < NT; n2 += 2) {
+      bf16x8 vb0 = va0, vb1 = va1;
+      if (n2 + 2 < NT) {
+        vb0 = vfrag(tp, n2 + 2);
+        vb1 = vfrag(tp, n2 + 3);
+      }
+      o[n2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, va0, o[n2], 0, 0, 0);
+      o[n2 + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, va1, o[n2 + 1], 0, 0, 0);
+      va0 = vb0;
+      va1 = vb1;
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  // softmax of S^T (keys masked by vmask) into pa, rescaling O if the running
+  // max grew; lane holds head r16, keys 4g+e (s0) and 16+4g+e (s1)
+  auto softmax = [&](uint32_t vmask) {
     float x[8];
-    float tmax = -INFINITY;
     const uint32_t vm = vmask >> (4 * g);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       x[e] = ((vm >> e) & 1u) ? s0[e] * a.scale_log2 : -INFINITY;
       x[4 + e] = ((vm >> (16 + e)) & 1u) ? s1[e] * a.scale_log2 : -INFINITY;
     }
+    float tmax = x[0];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) tmax = fmaxf(tmax, x[e]);
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+    for (int e = 1; e < 8; ++e) tmax = fmaxf(tmax, x[e]);
+    tmax = head_max4(tmax);
     // lazy running max: O is rescaled only when the max grows by more than 2^8
     const bool move = tmax > mrun + 8.f;
     if (__any(move)) {
@@ -585,45 +681,35 @@ __global__ void __launch_bounds__(512) attend512_kernel(AttArgs a) {
     }
     const float mr = mrun == -INFINITY ? 0.f : mrun;
     float psum = 0.f;
-    bf16x8 pa;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const float p = __builtin_amdgcn_exp2f(x[e] - mr);
       psum += p;
       pa[e] = (__bf16)p;
     }
-    psum += __shfl_xor(psum, 16);
-    psum += __shfl_xor(psum, 32);
-    lrun += psum;
-    // P.V: B operand lane holds dim 16*nt + i16 of keys 4g..4g+3 and 16+4g..16+4g+3
-    auto vfrag = [&](int nt) {
-      const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (__attribute__((address_space(3))) s16x4*)DLC_LDS(tile + pv_off0 + 32 * nt));
-      const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (__attribute__((address_space(3))) s16x4*)DLC_LDS(tile + pv_off1 + 32 * nt));
-      return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-    };
-    bf16x8 va[2], vb[2];
-    va[0] = vfrag(0);
-    va[1] = vfrag(1);
-#pragma unroll
-    for (int n2 = 0; n2 < NT; n2 += 2) {
-      if (n2 + 2 < NT) {
-        vb[0] = vfrag(n2 + 2);
-        vb[1] = vfrag(n2 + 3);
-      }
-      o[n2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, va[0], o[n2], 0, 0, 0);
-      o[n2 + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, va[1], o[n2 + 1], 0, 0, 0);
-      va[0] = vb[0];
-      va[1] = vb[1];
-      asm volatile("" ::: "memory");
-    }
+    lrun += head_sum4(psum);
   };
-  for (int64_t it = 0; it < ntile; it += NST) {
-    tile_step(sK0, sK2, it);
-    if (it + 1 < ntile) tile_step(sK1, sK0, it + 1);
-    if (it + 2 < ntile) tile_step(sK2, sK1, it + 2);
+
+  if (ntile > 0) {
+    wait_vm<0>();
+    lds_barrier();
+    const uint32_t vmask = valid_mask(0);
+    if (active) {
+      qk_only(tile_ptr(0));
+      softmax(vmask);
+    }
   }
+  for (int64_t it = 0; it + 1 < ntile; ++it) {
+    if (it + 2 < ntile) wait_vm<RPW>(); else wait_vm<0>();
+    lds_barrier();
+    if (it + 3 < ntile) issue(it + 3);
+    const uint32_t vmask = valid_mask(it + 1);
+    if (active) {
+      pv_qk(tile_ptr(it), tile_ptr(it + 1));
+      softmax(vmask);
+    }
+  }
+  if (ntile > 0 && active) pv_only(tile_ptr(ntile - 1));
 
   if (!active) return;
   // normalise and write: o[nt][e] is head 4*g + e, dim 16*nt + i16
