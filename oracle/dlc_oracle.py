@@ -32,7 +32,15 @@ Readings of points the pages leave open (each listed in the design notes):
 * the sliding-window branch ([Evolution] §6.1-6.2, n_win = 128 per [Stack]
   §4) covers the n_win most recent tokens including the query token itself,
   uses the same scale, and is joined to the compressed branch as one
-  attention over both key sets (no entry is removed from either set).
+  attention over both key sets (no entry is removed from either set);
+* the FP4 indexer ([Scratch] §6.4 and §12 say the indexer's products run in
+  FP4 without naming a format) uses the OCP microscaling MXFP4 format: E2M1
+  elements, one power-of-two (E8M0) scale per 32 consecutive elements of a
+  row, shared exponent floor(log2(block max |x|)) - 2, elements rounded to
+  the nearest E2M1 value with ties to the even code and saturated at 6; a
+  zero element is stored as +0.  Both q^I and K^I are quantized this way and
+  the score is the exact fp64 value of the formula on the dequantized
+  operands (w^I stays fp32).
 """
 
 from __future__ import annotations
@@ -68,6 +76,11 @@ __all__ = [
     "compressed_bytes_per_token_layer",
     "ledger",
     "indexer_flops_per_query",
+    "MXFP4_BLOCK",
+    "E2M1_MAGNITUDES",
+    "mxfp4_quantize",
+    "mxfp4_dequantize",
+    "index_scores_fp4",
 ]
 
 
@@ -238,6 +251,70 @@ def topk_select(scores, k: int) -> np.ndarray:
     k_eff = min(int(k), n)
     order = np.lexsort((np.arange(n), -s))  # last key is primary
     return np.sort(order[:k_eff]).astype(np.int64)
+
+
+# --------------------------------------------------------------------------
+# FP4 indexer ([Scratch] §6.4: the indexer's attention runs in FP4, which the
+# ReLU makes safe; §12: FP4 indexer FLOPs).  The format is the OCP MXFP4
+# reading stated in the module header.
+# --------------------------------------------------------------------------
+
+MXFP4_BLOCK = 32
+# magnitude of E2M1 codes 0..7 (sign in bit 3): 0, the subnormal 0.5, then
+# 1.x * 2^(e-1) for e = 1..3 with one mantissa bit
+E2M1_MAGNITUDES = (0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0)
+
+
+def mxfp4_quantize(x):
+    """MXFP4 quantization of the last axis in blocks of 32.
+
+    Returns (codes, shared): codes are integers 0..15 with the layout of x
+    (bit 3 the sign, bits 0..2 the E2M1 magnitude code), shared the block
+    exponents (x.shape[:-1] + (width/32,)), so that an element's value is
+    sign * E2M1_MAGNITUDES[code & 7] * 2**shared.
+
+    Per block: shared = floor(log2(max |x|)) - 2, the exponent that puts the
+    block maximum in [4, 8), E2M1's top binade; an all-zero block takes the
+    smallest E8M0 exponent, -127.  Each element x / 2**shared (exact: a power
+    of two) is rounded to the nearest E2M1 magnitude, a tie going to the even
+    code (even mantissa), and magnitudes above 6 become 6.
+    """
+    x = f64(x)
+    width = x.shape[-1]
+    if width % MXFP4_BLOCK:
+        raise ValueError("width must be a multiple of 32")
+    blocks = x.reshape(x.shape[:-1] + (width // MXFP4_BLOCK, MXFP4_BLOCK))
+    amax = np.abs(blocks).max(axis=-1)
+    _, e = np.frexp(amax)            # amax = f * 2**e with 0.5 <= f < 1
+    shared = np.where(amax > 0, (e - 1) - 2, -127)
+    shared = np.clip(shared, -127, 127).astype(np.int64)
+    y = blocks / np.ldexp(1.0, shared)[..., None]
+    grid = np.asarray(E2M1_MAGNITUDES)
+    dist = np.abs(np.abs(y)[..., None] - grid)
+    nearest = dist == dist.min(axis=-1, keepdims=True)
+    even = nearest & (np.arange(8) % 2 == 0)
+    mag_code = np.where(even.any(axis=-1), np.argmax(even, axis=-1), np.argmax(nearest, axis=-1))
+    negative = (y < 0) & (mag_code > 0)
+    codes = (mag_code + 8 * negative).reshape(x.shape)
+    return codes.astype(np.int64), shared
+
+
+def mxfp4_dequantize(codes, shared) -> np.ndarray:
+    """Values of MXFP4 codes with their block exponents (inverse of the grid map)."""
+    codes = np.asarray(codes, dtype=np.int64)
+    shared = np.asarray(shared, dtype=np.int64)
+    mag = np.asarray(E2M1_MAGNITUDES)[codes & 7]
+    val = np.where(codes & 8, -mag, mag)
+    scale = np.repeat(np.ldexp(1.0, shared), MXFP4_BLOCK, axis=-1)
+    return val * scale
+
+
+def index_scores_fp4(qI, wI, KI, t: int, m: int) -> np.ndarray:
+    """Indexer scores with q^I and K^I in MXFP4: the formula of index_scores
+    evaluated exactly on the dequantized operands ([Scratch] §6.4)."""
+    qd = mxfp4_dequantize(*mxfp4_quantize(qI))
+    kd = mxfp4_dequantize(*mxfp4_quantize(KI))
+    return index_scores(qd, wI, kd, t, m)
 
 
 # --------------------------------------------------------------------------
