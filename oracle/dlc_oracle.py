@@ -289,11 +289,15 @@ def mxfp4_quantize(x):
     shared = np.where(amax > 0, (e - 1) - 2, -127)
     shared = np.clip(shared, -127, 127).astype(np.int64)
     y = blocks / np.ldexp(1.0, shared)[..., None]
-    grid = np.asarray(E2M1_MAGNITUDES)
-    dist = np.abs(np.abs(y)[..., None] - grid)
-    nearest = dist == dist.min(axis=-1, keepdims=True)
-    even = nearest & (np.arange(8) % 2 == 0)
-    mag_code = np.where(even.any(axis=-1), np.argmax(even, axis=-1), np.argmax(nearest, axis=-1))
+    # nearest magnitude: scan the grid upwards, keeping the closest so far; an
+    # equal distance (a midpoint, between codes c-1 and c) goes to c if c is even
+    mag_code = np.zeros(y.shape, dtype=np.int64)
+    best = np.full(y.shape, np.inf)
+    for c, g in enumerate(E2M1_MAGNITUDES):
+        d = np.abs(np.abs(y) - g)
+        take = (d < best) | ((d == best) & (c % 2 == 0))
+        mag_code = np.where(take, c, mag_code)
+        best = np.where(take, d, best)
     negative = (y < 0) & (mag_code > 0)
     codes = (mag_code + 8 * negative).reshape(x.shape)
     return codes.astype(np.int64), shared
