@@ -11,6 +11,8 @@ from .binding import (  # noqa: F401
     csa_attend_ws,
     csa_compress,
     csa_index_topk,
+    csa_index_topk_fp4,
+    csa_index_topk_fp4_ws,
     csa_index_topk_ws,
     default_scale,
     dlc_project,
@@ -20,6 +22,7 @@ from .binding import (  # noqa: F401
     hca_compress,
     last_error,
     lib,
+    mxfp4_quantize,
     status_str,
     window_attend,
     window_attend_ws,

@@ -36,6 +36,10 @@ SIGNATURES = {
     "csa_index_topk_ws": (_sz, [_i64, _i64, _i64, _i64]),
     "csa_index_topk": (_i32, [_i32, _i64, _i64, _i64, _i64, _i64, _i64, _vp, _vp, _vp, _i64, _vp,
                               _i64, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "mxfp4_quantize": (_i32, [_i32, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp]),
+    "csa_index_topk_fp4_ws": (_sz, [_i64, _i64, _i64, _i64, _i64, _i64]),
+    "csa_index_topk_fp4": (_i32, [_i32, _i64, _i64, _i64, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _i64, _vp,
+                                  _i64, _vp, _vp, _vp, _vp, _sz, _vp]),
     "csa_attend_ws": (_sz, [_i64, _i64, _i64, _i64, _i64]),
     "csa_attend": (_i32, [_i32, _i64, _i64, _i64, _i64, _i64, _vp, _vp, _i64, _vp, _vp, _f32, _vp,
                           _vp, _vp, _sz, _vp]),
@@ -187,6 +191,55 @@ def csa_index_topk(qI, wI, KI, t, t_max, m, k, idx=None, count=None, scores=None
     ws = _ws(nb, dev, ws)
     _check("csa_index_topk", lib().csa_index_topk(
         _dt(qI), B, n_q, n_hI, cI, m, k, _p(qI), _p(wI), _p(KI), cap, _p(t), int(t_max), _p(idx),
+        _p(count), _p(scores), _p(ws), ws.numel() * ws.element_size(), _stream(dev)))
+    return idx, count
+
+
+def mxfp4_quantize(x, codes=None, scales=None):
+    """MXFP4 codes and E8M0 scales of the rows of x ([..., width], width % 32 == 0,
+    fp32 or bf16, contiguous).  Returns (codes uint8 [..., width/2],
+    scales uint8 [..., width/32]); see include/dlc.h for the format."""
+    _need(x.is_contiguous(), "x must be contiguous")
+    width = x.shape[-1]
+    rows = x.numel() // width if width else 0
+    dev = x.device
+    if codes is None:
+        codes = torch.empty(tuple(x.shape[:-1]) + (width // 2,), dtype=torch.uint8, device=dev)
+    if scales is None:
+        scales = torch.empty(tuple(x.shape[:-1]) + (width // 32,), dtype=torch.uint8, device=dev)
+    _need(codes.is_contiguous() and scales.is_contiguous(), "codes/scales must be contiguous")
+    _need(codes.numel() == rows * (width // 2) and scales.numel() == rows * (width // 32), "codes/scales size")
+    _check("mxfp4_quantize", lib().mxfp4_quantize(
+        _dt(x), 1, rows, width, _p(x), rows * width, _p(codes), rows * (width // 2), _p(scales),
+        rows * (width // 32), _stream(dev)))
+    return codes, scales
+
+
+def csa_index_topk_fp4_ws(B, n_q, n_hI, cI, cap, k):
+    return lib().csa_index_topk_fp4_ws(B, n_q, n_hI, cI, cap, k)
+
+
+def csa_index_topk_fp4(qI, wI, KIc, KIs, t, t_max, m, k, idx=None, count=None, scores=None, ws=None):
+    """FP4 (MXFP4) indexer scores and top-k.  qI [B][n_q][n_hI][cI] fp32/bf16 (quantized
+    inside), wI fp32 [B][n_q][n_hI], KIc uint8 [B][cap][cI/2] and KIs uint8 [B][cap][cI/32]
+    (mxfp4_quantize of the K^I cache), t int64 [B][n_q].  Returns (idx, count)."""
+    B, n_q, n_hI, cI = qI.shape
+    cap = KIc.shape[1]
+    dev = qI.device
+    for x, nm in ((qI, "qI"), (wI, "wI"), (KIc, "KIc"), (KIs, "KIs"), (t, "t")):
+        _need(x.is_contiguous(), f"{nm} must be contiguous")
+    _need(wI.dtype == torch.float32 and t.dtype == torch.int64, "wI must be fp32 and t int64")
+    _need(tuple(wI.shape) == (B, n_q, n_hI) and tuple(t.shape) == (B, n_q), "wI/t shape mismatch")
+    _need(KIc.dtype == torch.uint8 and KIs.dtype == torch.uint8, "KIc/KIs must be uint8")
+    _need(tuple(KIc.shape) == (B, cap, cI // 2) and tuple(KIs.shape) == (B, cap, cI // 32), "KIc/KIs shape")
+    if idx is None:
+        idx = torch.empty((B, n_q, k), dtype=torch.int32, device=dev)
+    if count is None:
+        count = torch.empty((B, n_q), dtype=torch.int32, device=dev)
+    nb = csa_index_topk_fp4_ws(B, n_q, n_hI, cI, cap, k)
+    ws = _ws(nb, dev, ws)
+    _check("csa_index_topk_fp4", lib().csa_index_topk_fp4(
+        _dt(qI), B, n_q, n_hI, cI, m, k, _p(qI), _p(wI), _p(KIc), _p(KIs), cap, _p(t), int(t_max), _p(idx),
         _p(count), _p(scores), _p(ws), ws.numel() * ws.element_size(), _stream(dev)))
     return idx, count
 

@@ -458,24 +458,6 @@ __device__ __forceinline__ constexpr int h16_row_off(int r) {
 }
 static_assert(h16_row_off(31) + 1024 <= kTileBytes, "tile layout");
 
-// Lane reductions over the four lanes l%16 + 16*g (g = 0..3) that hold one
-// head: v_permlane16_swap / v_permlane32_swap exchange whole rows between two
-// copies of the value, so max/sum of the two results pairs every lane with
-// its partner 16 (then 32) lanes away.  Plain VALU, unlike ds_bpermute, which
-// queues behind the tile reads in the LDS pipe.
-__device__ __forceinline__ float head_max4(float v) {
-  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
-  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
-}
-__device__ __forceinline__ float head_sum4(float v) {
-  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
-  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
-}
-
 template <int MODE>
 __global__ void __launch_bounds__(512) attend512_kernel(AttArgs a) {
   constexpr int CD = 512, KS = 16, NT = 32;  // 32-dim Q.K^T steps; 16-dim output tiles
@@ -662,7 +644,7 @@ __global__ void __launch_bounds__(512) attend512_kernel(AttArgs a) {
     float tmax = x[0];
 #pragma unroll
     for (int e = 1; e < 8; ++e) tmax = fmaxf(tmax, x[e]);
-    tmax = head_max4(tmax);
+    tmax = rows4_max(tmax);
     // lazy running max: O is rescaled only when the max grows by more than 2^8
     const bool move = tmax > mrun + 8.f;
     if (__any(move)) {
@@ -687,7 +669,7 @@ __global__ void __launch_bounds__(512) attend512_kernel(AttArgs a) {
       psum += p;
       pa[e] = (__bf16)p;
     }
-    lrun += head_sum4(psum);
+    lrun += rows4_sum(psum);
   };
 
   if (ntile > 0) {

@@ -93,6 +93,24 @@ __device__ __forceinline__ uint32_t order_key(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// Reductions over the four 16-lane rows of a wave (lanes l%16 + 16*r,
+// r = 0..3): v_permlane16_swap / v_permlane32_swap exchange whole rows between
+// two copies of the value, so combining the two results pairs every lane with
+// its partner 16 (then 32) lanes away.  Plain VALU, unlike ds_bpermute, which
+// queues behind LDS reads.  The sum adds (row0 + row1) + (row2 + row3).
+__device__ __forceinline__ float rows4_max(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float rows4_sum(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 // LDS pointer of a __shared__ object (address space 3)
 #define DLC_LDS(p) ((__attribute__((address_space(3))) void*)(p))
 
@@ -105,6 +123,13 @@ __device__ __forceinline__ uint32_t order_key(float f) {
 // instruction writes no VGPR.
 __device__ __forceinline__ void dma_row(const void* base, uint32_t lane_off, uint32_t lds_addr) {
   asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(lane_off), "s"(base), "s"(lds_addr)
+               : "memory", "m0");
+}
+
+// The same with 4 bytes per lane (global_load_lds_dword): active lane i moves
+// the dword at base + lane_off to LDS byte address lds_addr + 4*i.
+__device__ __forceinline__ void dma_dword(const void* base, uint32_t lane_off, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1" ::"v"(lane_off), "s"(base), "s"(lds_addr)
                : "memory", "m0");
 }
 

@@ -8,7 +8,9 @@
 //   1. clear      zero the two digit histograms of every query
 //   2. scores     one pass over K^I: for bf16 with c^I % 32 == 0 the heads x keys
 //                 product runs on MFMA (v_mfma_f32_16x16x32_bf16) with the
-//                 queries held in registers; otherwise a VALU kernel.  Each
+//                 queries held in registers; otherwise a VALU kernel; with
+//                 MXFP4 operands (csa_index_topk_fp4, §6.4's FP4 indexer) on
+//                 the block-scaled v_mfma_scale_f32_16x16x128_f8f6f4.  Each
 //                 workgroup also builds an LDS histogram of the top 11 bits of
 //                 the order-preserving score key and adds its non-zero bins to
 //                 the query's histogram.
@@ -34,7 +36,10 @@ constexpr int kMaxK = 8192;
 struct IdxArgs {
   const void* qI;      // [BQ][n_hI][cI]
   const float* wI;     // [BQ][n_hI]
-  const void* KI;      // [B][cap][cI]
+  const void* KI;      // [B][cap][cI] (FP4: [B][cap][cI/2] code bytes)
+  const uint8_t* k_scale;  // FP4: [B][cap][cI/32] E8M0 scale bytes
+  const uint8_t* q_code;   // FP4: [BQ][n_hI][cI/2] query code bytes
+  const uint8_t* q_scale;  // FP4: [BQ][n_hI][cI/32] query scale bytes
   const int64_t* t;    // [BQ]
   int64_t n_q, n_hI, cI, m, k, cap, t_max;
   float* scores;       // [BQ][score_ld]
@@ -232,8 +237,165 @@ __global__ void __launch_bounds__(256) scores_mfma_kernel(IdxArgs a) {
     for (int ht = 0; ht < HT; ++ht)
 #pragma unroll
       for (int r = 0; r < 4; ++r) part = fmaf(wv[ht][r], fmaxf(acc[ht][r], 0.f), part);
-    part += __shfl_xor(part, 16);
-    part += __shfl_xor(part, 32);
+    part = rows4_sum(part);
+    const int64_t s = s0 + (wave + 4 * it) * 16 + r16;
+    if (g == 0 && s < s1) {
+      const float score = canon_zero(part);
+      a.scores[bq * a.score_ld + s] = score;
+      atomicAdd(&hist[order_key(score) >> kShift1], 1u);
+    }
+  }
+  flush_hist(hist, a.hist + bq * kBins);
+}
+
+// ---------------------------------------------------------------- scores (FP4)
+//
+// MXFP4 operands on v_mfma_scale_f32_16x16x128_f8f6f4: D[16 heads][16 keys]
+// += Q[16 heads][128 dims] x K^T[128 dims][16 keys], each operand carrying one
+// E8M0 scale per 32 dims, so every product is exact and only the fp32 sums
+// round.  Lane l supplies head/key l%16 and the 32-dim block l/16 of each
+// 128-dim step: 16 code bytes and one scale byte.  The streaming is that of
+// the bf16 kernel: a 16-key tile (16 code rows of c^I/2 bytes, then their 16
+// scale rows of c^I/32 bytes) arrives by direct global->LDS loads into the
+// wave's own ring of NS stages, NS-1 tiles in flight, no barrier.  Within a
+// code row, 16-byte chunk c sits at slot c ^ ((row / RPB) % CPR) (RPB rows
+// per 256 bytes, CPR chunks per row), so the 16 rows of one ds_read_b128
+// pass fall on distinct banks.  The queries arrive quantized
+// (mxfp4_quantize, run on them just before).  Result layout and head sum as
+// in the bf16 kernel.
+
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+template <int CI, int NS>
+__global__ void __launch_bounds__(256) scores_fp4_kernel(IdxArgs a) {
+  constexpr int KB = CI / 32;               // scale bytes (32-dim blocks) per row
+  constexpr int ROWB = CI / 2;              // code bytes per row
+  constexpr int CPR = ROWB / 16;            // 16-byte chunks per code row
+  constexpr int RPB = 256 / ROWB;           // code rows per 256 bytes (the bank width)
+  constexpr int NJ = CI / 128;              // 128-dim MFMA steps = 1 KB code loads per tile
+  constexpr int CODEB = 16 * ROWB;          // code bytes of a tile
+  constexpr int STB = CODEB + 16 * KB;      // stage: codes, then scales
+  constexpr int SLANES = 16 * KB / 4;       // lanes of the scale load (4 bytes each)
+  constexpr int HT = 4;                     // head tiles: up to 64 heads
+  static_assert(CI == 128 || CI == 256, "c^I");
+  __shared__ uint32_t hist[kBins];
+  __shared__ __attribute__((aligned(16))) unsigned char sK[4][NS][STB];
+  const int64_t bq = blockIdx.y;
+  const int64_t nvis = visible(a, bq);
+  const int64_t s0 = int64_t(blockIdx.x) * a.keys_per_wg;
+  if (s0 >= nvis) return;
+  const int64_t s1 = min(nvis, s0 + a.keys_per_wg);
+  for (int i = threadIdx.x; i < kBins; i += blockDim.x) hist[i] = 0;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int r16 = lane & 15, g = lane >> 4;
+  const int64_t b = bq / a.n_q;
+  const uint8_t* Kc = static_cast<const uint8_t*>(a.KI) + b * a.cap * ROWB;
+  const uint8_t* Ks = a.k_scale + b * a.cap * KB;
+  const int64_t ntiles = (s1 - s0 + 15) / 16;
+  const int64_t my_tiles = ntiles > wave ? (ntiles - wave + 3) / 4 : 0;
+  // tile it of this wave: rows row0 .. row0+15, those past the chunk's end
+  // repeat its last visible row
+  auto issue = [&](int64_t it, int st) {
+    const int64_t row0 = s0 + (wave + 4 * it) * 16;  // < s1
+    const uint32_t lds = (uint32_t)(uintptr_t)DLC_LDS(&sK[wave][st][0]);
+#pragma unroll
+    for (int q = 0; q < NJ; ++q) {
+      const int pos = q * 1024 + 16 * lane;
+      const int rho = pos / ROWB, slot = (pos % ROWB) / 16;
+      const int chunk = slot ^ ((rho / RPB) % CPR);
+      const int64_t row = min(row0 + rho, s1 - 1);
+      dma_row(Kc + row0 * ROWB, uint32_t((row - row0) * ROWB + chunk * 16), lds + uint32_t(q * 1024));
+    }
+    if (lane < SLANES) {
+      const int rho = 4 * lane / KB;
+      const int64_t row = min(row0 + rho, s1 - 1);
+      dma_dword(Ks + row0 * KB, uint32_t((row - row0) * KB + (4 * lane) % KB), lds + uint32_t(CODEB));
+    }
+  };
+#pragma unroll
+  for (int p = 0; p < NS - 1; ++p)
+    if (p < my_tiles) issue(p, p);
+
+  // queries (A operand, rows = heads): head ht*16 + r16, block 4j + g; heads
+  // past n_hI take zero codes (their weight is 0 too)
+  i32x8 qa[HT][NJ];
+  int qs[HT][NJ];
+#pragma unroll
+  for (int ht = 0; ht < HT; ++ht) {
+    const int h = ht * 16 + r16;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const int blk = 4 * j + g;
+      uint4 c = make_uint4(0, 0, 0, 0);
+      int e8 = 127;
+      if (h < a.n_hI) {
+        c = *reinterpret_cast<const uint4*>(a.q_code + (bq * a.n_hI + h) * ROWB + blk * 16);
+        e8 = a.q_scale[(bq * a.n_hI + h) * KB + blk];
+      }
+      qa[ht][j] = i32x8{int(c.x), int(c.y), int(c.z), int(c.w), 0, 0, 0, 0};
+      qs[ht][j] = e8;
+    }
+  }
+  float wv[HT][4];
+#pragma unroll
+  for (int ht = 0; ht < HT; ++ht)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int h = ht * 16 + g * 4 + r;
+      wv[ht][r] = h < a.n_hI ? a.wI[bq * a.n_hI + h] : 0.f;
+    }
+  // wait for the query and weight loads (and with them the first tiles) here:
+  // a wait for them inside the loop would drain the tile loads in flight
+#pragma unroll
+  for (int ht = 0; ht < HT; ++ht) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) asm volatile("" ::"v"(wv[ht][r]));
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+      asm volatile("" ::"v"(qa[ht][j][0]), "v"(qa[ht][j][1]), "v"(qa[ht][j][2]), "v"(qa[ht][j][3]), "v"(qs[ht][j]));
+  }
+  __syncthreads();  // hist cleared
+
+  constexpr int LPT = NJ + 1;  // loads per tile and lane (the scale load counts for every lane)
+  for (int64_t it = 0; it < my_tiles; ++it) {
+    const int st = int(it % NS);
+    const int64_t nxt = it + NS - 1;
+    int after;  // tiles issued after tile it
+    if (nxt < my_tiles) {
+      issue(nxt, int(nxt % NS));
+      after = NS - 1;
+    } else {
+      after = int(my_tiles - 1 - it);
+    }
+    if (after >= NS - 1) wait_vm<(NS - 1) * LPT>();
+    else if (after == 2) wait_vm<2 * LPT>();
+    else if (after == 1) wait_vm<LPT>();
+    else wait_vm<0>();
+    asm volatile("" ::: "memory");
+    const unsigned char* tile = &sK[wave][st][0];
+    f32x4 acc[HT];
+#pragma unroll
+    for (int ht = 0; ht < HT; ++ht) acc[ht] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const int blk = 4 * j + g;
+      const int slot = blk ^ ((r16 / RPB) % CPR);
+      const uint4 k4 = *reinterpret_cast<const uint4*>(tile + r16 * ROWB + slot * 16);
+      const int ksc = tile[CODEB + r16 * KB + blk];
+      const i32x8 kb = i32x8{int(k4.x), int(k4.y), int(k4.z), int(k4.w), 0, 0, 0, 0};
+#pragma unroll
+      for (int ht = 0; ht < HT; ++ht)
+        acc[ht] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qa[ht][j], kb, acc[ht], 4, 4, 0, qs[ht][j], 0,
+                                                                   ksc);
+    }
+    float part = 0.f;
+#pragma unroll
+    for (int ht = 0; ht < HT; ++ht)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) part = fmaf(wv[ht][r], fmaxf(acc[ht][r], 0.f), part);
+    part = rows4_sum(part);
     const int64_t s = s0 + (wave + 4 * it) * 16 + r16;
     if (g == 0 && s < s1) {
       const float score = canon_zero(part);
@@ -649,6 +811,9 @@ struct WsLayout {
 #define DLC_SCORES_WGS 512
 #endif
 constexpr int64_t kScoreWorkgroups = DLC_SCORES_WGS;
+#ifndef DLC_FP4_NS
+#define DLC_FP4_NS 8  // LDS stages per wave in the FP4 scores kernel (NS-1 tiles in flight)
+#endif
 int64_t keys_per_wg(int64_t BQ, int64_t vis_max) {
   const int64_t vis = vis_max > 0 ? vis_max : 1;
   int64_t kpw = ceil_div(ceil_div(vis * BQ, kScoreWorkgroups), 64) * 64;
@@ -675,6 +840,50 @@ WsLayout ws_layout(int64_t B, int64_t n_q, int64_t cap, int64_t k, bool own_scor
   return L;
 }
 
+// IdxArgs pointers into the workspace
+void bind_ws(IdxArgs& a, const WsLayout& L, void* ws, float* scores, int64_t BQ, int64_t cap) {
+  char* w = static_cast<char*>(ws);
+  a.scores = scores ? scores : reinterpret_cast<float*>(w + L.scores);
+  a.score_ld = cap;
+  a.hist = reinterpret_cast<uint32_t*>(w + L.hist);
+  a.hist2 = a.hist + size_t(BQ) * kBins;
+  a.ccnt = reinterpret_cast<uint32_t*>(w + L.ccnt);
+  a.sel = reinterpret_cast<int32_t*>(w + L.sel);
+  a.cand = reinterpret_cast<int32_t*>(w + L.cand);
+  a.cand_kseg = reinterpret_cast<uint32_t*>(w + L.cand_kseg);
+  a.cand_idx = reinterpret_cast<int32_t*>(w + L.cand_idx);
+  a.cand_key = reinterpret_cast<uint32_t*>(w + L.cand_key);
+  a.max_chunks = kMaxChunks;
+}
+
+// threshold/filter and finish: scores (and the first histogram) -> idx, count
+int select_topk(IdxArgs& a, int64_t BQ, int64_t vis_max, hipStream_t s) {
+  int rc;
+  StageTimer timer(DLC_STAGE_TOPK_SELECT, s);
+  if (vis_max > 0) {
+    const int64_t nchunks = ceil_div(vis_max, a.keys_per_wg);
+    dim3 grid{(unsigned)nchunks, (unsigned)BQ, 1u};
+    hipLaunchKernelGGL(filter_kernel, grid, dim3(256), 0, s, a);
+    if ((rc = check_launch("csa_index_topk/filter"))) return rc;
+  }
+  if (vis_max == 0) a.keys_per_wg = 64;
+  hipLaunchKernelGGL(finish_kernel, dim3((unsigned)BQ), dim3(1024), 0, s, a);
+  return check_launch("csa_index_topk/finish");
+}
+
+// the FP4 call's workspace: the common layout, then the quantized queries
+struct Fp4Ws {
+  size_t code, scale, total;
+};
+Fp4Ws fp4_query_off(int64_t B, int64_t n_q, int64_t cap, int64_t k, int64_t n_hI, int64_t cI) {
+  const size_t rows = size_t(B) * size_t(n_q) * size_t(n_hI);
+  Fp4Ws w{};
+  w.code = ws_layout(B, n_q, cap, k, true).total;
+  w.scale = align_up(w.code + rows * size_t(cI / 2), 256);
+  w.total = align_up(w.scale + rows * size_t(cI / 32), 256);
+  return w;
+}
+
 }  // namespace
 }  // namespace dlc
 
@@ -683,6 +892,11 @@ extern "C" {
 size_t csa_index_topk_ws(int64_t B, int64_t n_q, int64_t cap, int64_t k) {
   if (B < 1 || n_q < 1 || cap < 0 || k < 1) return 0;
   return dlc::ws_layout(B, n_q, cap, k, true).total;
+}
+
+size_t csa_index_topk_fp4_ws(int64_t B, int64_t n_q, int64_t n_hI, int64_t cI, int64_t cap, int64_t k) {
+  if (B < 1 || n_q < 1 || n_hI < 1 || cI < 32 || cap < 0 || k < 1) return 0;
+  return dlc::fp4_query_off(B, n_q, cap, k, n_hI, cI).total;
 }
 
 int csa_index_topk(int dtype, int64_t B, int64_t n_q, int64_t n_hI, int64_t cI, int64_t m, int64_t k,
@@ -708,23 +922,12 @@ int csa_index_topk(int dtype, int64_t B, int64_t n_q, int64_t n_hI, int64_t cI, 
   DLC_REQUIRE(B * n_q <= 65535, DLC_E_UNSUPPORTED, "csa_index_topk: B*n_q > 65535");
 
   hipStream_t s = as_stream(stream);
-  char* w = static_cast<char*>(ws);
   IdxArgs a{};
   a.qI = qI; a.wI = wI; a.KI = KI; a.t = t;
   a.n_q = n_q; a.n_hI = n_hI; a.cI = cI; a.m = m; a.k = k; a.cap = cap; a.t_max = t_max;
-  a.scores = scores ? scores : reinterpret_cast<float*>(w + L.scores);
-  a.score_ld = cap;
-  a.hist = reinterpret_cast<uint32_t*>(w + L.hist);
-  a.hist2 = a.hist + size_t(B * n_q) * kBins;
-  a.ccnt = reinterpret_cast<uint32_t*>(w + L.ccnt);
-  a.sel = reinterpret_cast<int32_t*>(w + L.sel);
-  a.cand = reinterpret_cast<int32_t*>(w + L.cand);
-  a.cand_kseg = reinterpret_cast<uint32_t*>(w + L.cand_kseg);
-  a.cand_idx = reinterpret_cast<int32_t*>(w + L.cand_idx);
-  a.cand_key = reinterpret_cast<uint32_t*>(w + L.cand_key);
-  a.max_chunks = kMaxChunks;
-  a.idx = idx; a.count = count;
   const int64_t BQ = B * n_q;
+  bind_ws(a, L, ws, scores, BQ, cap);
+  a.idx = idx; a.count = count;
 
   int rc = fill_u32(a.hist, 0, int64_t(BQ * kBins * 2), s);
   if (rc) return rc;
@@ -757,16 +960,62 @@ int csa_index_topk(int dtype, int64_t B, int64_t n_q, int64_t n_hI, int64_t cI, 
     }
     if ((rc = check_launch("csa_index_topk/scores"))) return rc;
   }
-  StageTimer timer(DLC_STAGE_TOPK_SELECT, s);
+  return select_topk(a, BQ, vis_max, s);
+}
+
+int csa_index_topk_fp4(int dtype, int64_t B, int64_t n_q, int64_t n_hI, int64_t cI, int64_t m, int64_t k,
+                       const void* qI, const float* wI, const uint8_t* KIc, const uint8_t* KIs, int64_t cap,
+                       const int64_t* t, int64_t t_max, int32_t* idx, int32_t* count, float* scores, void* ws,
+                       size_t ws_bytes, void* stream) {
+  using namespace dlc;
+  DLC_REQUIRE(dtype == DLC_F32 || dtype == DLC_BF16, DLC_E_DTYPE, "csa_index_topk_fp4: unsupported dtype %d", dtype);
+  DLC_REQUIRE(B >= 1 && n_q >= 1 && n_hI >= 1 && m >= 1 && cap >= 0 && t_max >= 0, DLC_E_INVAL,
+              "csa_index_topk_fp4: need B, n_q, n_hI, m >= 1 and cap, t_max >= 0");
+  DLC_REQUIRE(cI == 128 || cI == 256, DLC_E_UNSUPPORTED, "csa_index_topk_fp4: cI=%lld not in {128, 256}",
+              (long long)cI);
+  DLC_REQUIRE(n_hI <= 64, DLC_E_UNSUPPORTED, "csa_index_topk_fp4: n_hI=%lld > 64", (long long)n_hI);
+  DLC_REQUIRE(k >= 1 && k <= kMaxK, DLC_E_UNSUPPORTED, "csa_index_topk_fp4: k=%lld outside [1, %d]", (long long)k,
+              kMaxK);
+  DLC_REQUIRE(t_max / m <= cap, DLC_E_SHAPE, "csa_index_topk_fp4: floor(t_max/m)=%lld exceeds cap=%lld",
+              (long long)(t_max / m), (long long)cap);
+  DLC_REQUIRE(cap < (int64_t(1) << 31), DLC_E_UNSUPPORTED, "csa_index_topk_fp4: cap must be < 2^31");
+  DLC_REQUIRE(qI && wI && t && idx && count && ((KIc && KIs) || cap == 0), DLC_E_INVAL,
+              "csa_index_topk_fp4: NULL argument");
+  DLC_REQUIRE(aligned(qI, 16) && (cap == 0 || aligned(KIc, 16)), DLC_E_INVAL,
+              "csa_index_topk_fp4: qI and KIc must be 16-byte aligned");
+  const WsLayout L = ws_layout(B, n_q, cap, k, true);
+  const Fp4Ws W = fp4_query_off(B, n_q, cap, k, n_hI, cI);
+  DLC_REQUIRE(ws != nullptr && ws_bytes >= W.total, DLC_E_WORKSPACE,
+              "csa_index_topk_fp4: workspace of %zu bytes needed, %zu given", W.total, ws_bytes);
+  DLC_REQUIRE(aligned(ws, 256), DLC_E_WORKSPACE, "csa_index_topk_fp4: workspace must be 256-byte aligned");
+  DLC_REQUIRE(B * n_q <= 65535, DLC_E_UNSUPPORTED, "csa_index_topk_fp4: B*n_q > 65535");
+
+  hipStream_t s = as_stream(stream);
+  IdxArgs a{};
+  a.qI = qI; a.wI = wI; a.KI = KIc; a.k_scale = KIs; a.t = t;
+  a.n_q = n_q; a.n_hI = n_hI; a.cI = cI; a.m = m; a.k = k; a.cap = cap; a.t_max = t_max;
+  const int64_t BQ = B * n_q;
+  bind_ws(a, L, ws, scores, BQ, cap);
+  a.idx = idx; a.count = count;
+  uint8_t* qc = static_cast<uint8_t*>(ws) + W.code;
+  uint8_t* qsc = static_cast<uint8_t*>(ws) + W.scale;
+  a.q_code = qc; a.q_scale = qsc;
+
+  int rc = fill_u32(a.hist, 0, int64_t(BQ * kBins * 2), s);
+  if (rc) return rc;
+  const int64_t vis_max = t_max / m;
   if (vis_max > 0) {
-    const int64_t nchunks = ceil_div(vis_max, a.keys_per_wg);
-    dim3 grid{(unsigned)nchunks, (unsigned)BQ, 1u};
-    hipLaunchKernelGGL(filter_kernel, grid, dim3(256), 0, s, a);
-    if ((rc = check_launch("csa_index_topk/filter"))) return rc;
+    const int64_t rows = BQ * n_hI;
+    if ((rc = mxfp4_quantize(dtype, 1, rows, cI, qI, rows * cI, qc, rows * cI / 2, qsc, rows * cI / 32, stream)))
+      return rc;
+    a.keys_per_wg = keys_per_wg(BQ, vis_max);
+    dim3 grid{(unsigned)ceil_div(vis_max, a.keys_per_wg), (unsigned)BQ, 1u};
+    StageTimer timer(DLC_STAGE_INDEX_SCORES, s);
+    if (cI == 128) hipLaunchKernelGGL((scores_fp4_kernel<128, DLC_FP4_NS>), grid, dim3(256), 0, s, a);
+    if (cI == 256) hipLaunchKernelGGL((scores_fp4_kernel<256, DLC_FP4_NS>), grid, dim3(256), 0, s, a);
+    if ((rc = check_launch("csa_index_topk_fp4/scores"))) return rc;
   }
-  if (vis_max == 0) a.keys_per_wg = 64;
-  hipLaunchKernelGGL(finish_kernel, dim3((unsigned)BQ), dim3(1024), 0, s, a);
-  return check_launch("csa_index_topk/finish");
+  return select_topk(a, BQ, vis_max, s);
 }
 
 }  // extern "C"

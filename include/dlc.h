@@ -134,6 +134,48 @@ int csa_index_topk(int dtype, int64_t B, int64_t n_q, int64_t n_hI, int64_t cI, 
                    void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * FP4 indexer ([Scratch] §6.4: the indexer's q . K products run in FP4;
+ * §12: indexer FLOPs "in FP4").  The pages name no FP4 format; these calls
+ * use OCP MXFP4: a row is cut into blocks of 32 elements, each block stores
+ * one E8M0 scale byte e + 127 with e = floor(log2(max |x|)) - 2 (-127 for an
+ * all-zero block) and 32 E2M1 codes (bit 3 sign, bits 0..2 the magnitude
+ * index into {0, 0.5, 1, 1.5, 2, 3, 4, 6}), each x / 2^e rounded to the
+ * nearest magnitude with ties to the even code, saturated at 6, zero stored
+ * as code 0.  Element 2i is the low nibble of code byte i.
+ *
+ * mxfp4_quantize - quantize rows of width `width` (a multiple of 32):
+ *  src     [B] batches of [rows][width] in dtype (DLC_F32 or DLC_BF16),
+ *          batch b at src + b*src_bstride elements; 16-byte aligned
+ *  codes   out [B] x [rows][width/2] bytes, batch b at codes + b*codes_bstride;
+ *          16-byte aligned
+ *  scales  out [B] x [rows][width/32] E8M0 bytes, batch b at
+ *          scales + b*scales_bstride
+ * Quantizing rows i_begin .. i_end-1 of a cache: pass src + i_begin*width,
+ * codes + i_begin*width/2, scales + i_begin*width/32 and rows = i_end-i_begin.
+ *
+ * csa_index_topk_fp4 - csa_index_topk with q^I and K^I in MXFP4: the scores
+ * are the formula of csa_index_topk on the dequantized operands, products
+ * exact and sums in fp32 (v_mfma_scale_f32_16x16x128_f8f6f4), w^I in fp32.
+ *  qI      [B][n_q][n_hI][cI] in dtype (DLC_F32 or DLC_BF16), quantized per
+ *          head row inside the call (the same rule); 16-byte aligned
+ *  KIc     [B][cap][cI/2] key code bytes (mxfp4_quantize of the K^I cache)
+ *  KIs     [B][cap][cI/32] key scale bytes
+ *  ws      workspace of at least csa_index_topk_fp4_ws(B, n_q, n_hI, cI,
+ *          cap, k) bytes, 256-byte aligned (it also holds the quantized
+ *          queries); its contents on entry do not matter
+ *  other arguments, outputs and ranking as for csa_index_topk.
+ * Limits: cI in {128, 256}, n_hI <= 64, 1 <= k <= 8192; KIc 16-byte
+ * aligned.
+ */
+int mxfp4_quantize(int dtype, int64_t B, int64_t rows, int64_t width, const void* src, int64_t src_bstride,
+                   uint8_t* codes, int64_t codes_bstride, uint8_t* scales, int64_t scales_bstride, void* stream);
+size_t csa_index_topk_fp4_ws(int64_t B, int64_t n_q, int64_t n_hI, int64_t cI, int64_t cap, int64_t k);
+int csa_index_topk_fp4(int dtype, int64_t B, int64_t n_q, int64_t n_hI, int64_t cI, int64_t m, int64_t k,
+                       const void* qI, const float* wI, const uint8_t* KIc, const uint8_t* KIs, int64_t cap,
+                       const int64_t* t, int64_t t_max, int32_t* idx, int32_t* count, float* scores,
+                       void* ws, size_t ws_bytes, void* stream);
+
+/*
  * csa_attend - shared-KV multi-query attention over the selected CSA
  * entries ([Scratch] §8): for every head h,
  *   o[h] = sum_s softmax_s(scale * q[h] . C^Comp[s]) * C^Comp[s],
@@ -237,8 +279,8 @@ int dlc_project(int dtype, int64_t M, int64_t N, int64_t K, const void* A, int64
  * the caller's HIP events `ev_begin` (before) and `ev_end` (after) on that
  * launch's stream, then disarms.  The events are hipEvent_t handles owned by
  * the caller; NULL events disarm the stage.  Stages:
- *   DLC_STAGE_INDEX_SCORES  the indexer score kernel of csa_index_topk
- *   DLC_STAGE_TOPK_SELECT   the threshold/filter and finish kernels of csa_index_topk
+ *   DLC_STAGE_INDEX_SCORES  the indexer score kernel of csa_index_topk (or _fp4)
+ *   DLC_STAGE_TOPK_SELECT   the threshold/filter and finish kernels of csa_index_topk (or _fp4)
  *   DLC_STAGE_CSA_ATTEND    csa_attend (attention and combine kernels)
  *   DLC_STAGE_HCA_ATTEND    hca_attend (attention and combine kernels)
  *   DLC_STAGE_COMPRESS      csa_compress / hca_compress

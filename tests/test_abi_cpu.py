@@ -104,6 +104,50 @@ def test_index_topk_validation(L, kw, status):
     assert _topk(L, **kw) == status
 
 
+def _topk_fp4(L, **kw):
+    a = dict(dtype=BF16, B=1, n_q=1, n_hI=4, cI=128, m=4, k=8, qI=P, wI=P, KIc=P, KIs=P, cap=16, t=P,
+             t_max=64, idx=P, count=P, scores=None, ws=P, ws_bytes=1 << 30)
+    a.update(kw)
+    return L.csa_index_topk_fp4(a["dtype"], a["B"], a["n_q"], a["n_hI"], a["cI"], a["m"], a["k"], a["qI"],
+                                a["wI"], a["KIc"], a["KIs"], a["cap"], a["t"], a["t_max"], a["idx"], a["count"],
+                                a["scores"], a["ws"], a["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dtype=3), E_DTYPE),
+    (dict(cI=64), E_UNSUPPORTED),
+    (dict(cI=96), E_UNSUPPORTED),
+    (dict(n_hI=65), E_UNSUPPORTED),
+    (dict(k=0), E_UNSUPPORTED),
+    (dict(m=0), E_INVAL),
+    (dict(t_max=68), E_SHAPE),          # floor(68/4) = 17 > cap
+    (dict(KIs=None), E_INVAL),
+    (dict(qI=P + 4), E_INVAL),          # misaligned query
+    (dict(ws_bytes=16), E_WORKSPACE),
+])
+def test_index_topk_fp4_validation(L, kw, status):
+    assert _topk_fp4(L, **kw) == status
+
+
+@pytest.mark.parametrize("args,status", [
+    ((BF16, 1, 4, 48, P, 192, P, 96, P, 6), E_SHAPE),      # width not a multiple of 32
+    ((7, 1, 4, 64, P, 256, P, 128, P, 8), E_DTYPE),
+    ((BF16, 1, 4, 64, None, 256, P, 128, P, 8), E_INVAL),
+    ((BF16, 2, 4, 64, P, 128, P, 128, P, 8), E_SHAPE),     # batch stride shorter than the rows
+    ((BF16, 1, 4, 64, P + 2, 256, P, 128, P, 8), E_INVAL),  # misaligned source
+    ((BF16, 1, 0, 64, None, 0, None, 0, None, 0), OK),      # no rows: nothing to do
+])
+def test_mxfp4_quantize_validation(L, args, status):
+    assert L.mxfp4_quantize(*args, None) == status
+
+
+def test_fp4_workspace_query(L):
+    base = L.csa_index_topk_ws(4, 1, 262144, 1024)
+    w = L.csa_index_topk_fp4_ws(4, 1, 64, 128, 262144, 1024)
+    assert w >= base + 4 * 64 * (64 + 4) and w % 256 == 0
+    assert L.csa_index_topk_fp4_ws(0, 1, 64, 128, 10, 1) == 0
+
+
 def test_workspace_queries(L):
     w1 = L.csa_index_topk_ws(4, 1, 262144, 1024)
     assert w1 > 262144 * 4 * 4
