@@ -33,6 +33,7 @@ sys.path.insert(0, ROOT)
 METRIC = "decode query-tokens/s per CSA+HCA layer at 1M ctx; achieved HBM GB/s vs peak"
 PEAK_HBM_GBS = 8000.0
 SCORES_KERNEL = "scores_mfma_kernel<4, 4, 4>"
+SCORES_KERNEL_FP4 = "scores_fp4_kernel<128, 4, 8>"
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "indexer_scores_hybrid1m_counters.json")
 
 
@@ -155,7 +156,8 @@ def build_workload(cfg, dev, n_dec, n_sets=3):
         dlc.csa_compress(col("aZ"), col("bZ"), col("aKV"), col("bKV"), m, Cc)
         dlc.csa_compress(col("IaZ"), col("IbZ"), col("IaKV"), col("IbKV"), m, KI)
         dlc.hca_compress(col("Z"), col("KV"), mp, Ch)
-        sets.append((Cc, KI, Ch))
+        KIc, KIs = dlc.mxfp4_quantize(KI)  # the FP4 indexer's key cache (MXFP4 codes + scales)
+        sets.append((Cc, KI, Ch, KIc, KIs))
     torch.cuda.synchronize()
     t_comp = (time.perf_counter() - t1) / n_sets
 
@@ -191,9 +193,11 @@ def build_workload(cfg, dev, n_dec, n_sets=3):
                 t_proj=t_proj, t_comp=t_comp, stream_bytes=S.numel() * 2)
 
 
-def make_steps(cfg, wl, dev, n_dec, window=False):
+def make_steps(cfg, wl, dev, n_dec, window=False, fp4=False):
     """Pre-marshal the C-ABI argument tuples of every decode step.  window: each
-    layer's sliding-window branch joins its attention output in place."""
+    layer's sliding-window branch joins its attention output in place.  fp4: the
+    indexer runs on the MXFP4 key cache (each new K^I entry is quantized as it
+    is written) through csa_index_topk_fp4."""
     import torch
 
     import dense_long_context_amd as dlc
@@ -206,7 +210,8 @@ def make_steps(cfg, wl, dev, n_dec, window=False):
     S, col = wl["S"], wl["col"]
     ld, bs = S.stride(1), S.stride(0)
     n_tot, cap_csa, cap_hca = wl["n_tot"], wl["cap_csa"], wl["cap_hca"]
-    ws_i = torch.empty(dlc.csa_index_topk_ws(B, 1, cap_csa, k), dtype=torch.uint8, device=dev)
+    ws_i = torch.empty(max(dlc.csa_index_topk_ws(B, 1, cap_csa, k),
+                           dlc.csa_index_topk_fp4_ws(B, 1, n_hI, cI, cap_csa, k)), dtype=torch.uint8, device=dev)
     ws_c = torch.empty(max(1, dlc.csa_attend_ws(B, 1, n_h, c, k)), dtype=torch.uint8, device=dev)
     ws_h = torch.empty(max(1, dlc.hca_attend_ws(B, 1, n_h, c, cap_hca)), dtype=torch.uint8, device=dev)
     idx = torch.empty((B, 1, k), dtype=torch.int32, device=dev)
@@ -224,7 +229,7 @@ def make_steps(cfg, wl, dev, n_dec, window=False):
     steps = []
     for s in range(n_dec):
         t = wl["n_ctx"] + s
-        Cc, KI, Ch = wl["sets"][s % 3]
+        Cc, KI, Ch, KIc, KIs = wl["sets"][s % 3]
         calls = []
         if (t + 1) % m == 0:
             i = (t + 1) // m - 1
@@ -232,12 +237,22 @@ def make_steps(cfg, wl, dev, n_dec, window=False):
                                            p(col("bKV")), ld, bs, None, None, i, i + 1, p(Cc), cap_csa, stream)))
             calls.append((L.csa_compress, (BF, B, n_tot, cI, m, p(col("IaZ")), p(col("IbZ")), p(col("IaKV")),
                                            p(col("IbKV")), ld, bs, None, None, i, i + 1, p(KI), cap_csa, stream)))
+            if fp4:
+                calls.append((L.mxfp4_quantize, (BF, B, 1, cI, p(KI) + i * cI * 2, cap_csa * cI,
+                                                 p(KIc) + i * cI // 2, cap_csa * cI // 2, p(KIs) + i * cI // 32,
+                                                 cap_csa * cI // 32, stream)))
         if (t + 1) % mp == 0:
             i = (t + 1) // mp - 1
             calls.append((L.hca_compress, (BF, B, n_tot, c, mp, p(col("Z")), p(col("KV")), ld, bs, None, i, i + 1,
                                            p(Ch), cap_hca, stream)))
-        calls.append((L.csa_index_topk, (BF, B, 1, n_hI, cI, m, k, p(Q["qI"][s]), p(Q["wI"][s]), p(KI), cap_csa,
-                                         p(tt[s]), t, p(idx), p(cnt), None, p(ws_i), ws_i.numel(), stream)))
+        if fp4:
+            calls.append((L.csa_index_topk_fp4, (BF, B, 1, n_hI, cI, m, k, p(Q["qI"][s]), p(Q["wI"][s]), p(KIc),
+                                                 p(KIs), cap_csa, p(tt[s]), t, p(idx), p(cnt), None, p(ws_i),
+                                                 ws_i.numel(), stream)))
+        else:
+            calls.append((L.csa_index_topk, (BF, B, 1, n_hI, cI, m, k, p(Q["qI"][s]), p(Q["wI"][s]), p(KI),
+                                             cap_csa, p(tt[s]), t, p(idx), p(cnt), None, p(ws_i), ws_i.numel(),
+                                             stream)))
         if window:  # each layer's attention with its sliding window joined in (one key list)
             calls.append((L.csa_attend_window, (BF, B, 1, n_h, c, k, p(Q["q"][s]), p(Cc), cap_csa, p(idx), p(cnt),
                                                 p(wl["rings"]["win"]), wl["ring"], N_WIN, p(tt[s]), t, 0.0, p(o1),
@@ -256,16 +271,21 @@ def make_steps(cfg, wl, dev, n_dec, window=False):
     return steps, keep
 
 
-def step_bytes(cfg, t):
-    """Algorithmic HBM bytes of one decode step (B queries at position t)."""
+def step_bytes(cfg, t, fp4=False):
+    """Algorithmic HBM bytes of one decode step (B queries at position t).  The
+    second value is the indexer scores kernel's share: every visible K^I row
+    (bf16, or MXFP4 codes + scales), the query and its head weights."""
     B, c, cI, m, mp, k, n_h, n_hI = cfg.B, cfg.c, cfg.cI, cfg.m, cfg.m_prime, cfg.k, cfg.n_h, cfg.n_hI
     v_csa, v_hca = t // m, t // mp
-    idx_b = v_csa * cI * 2 + n_hI * cI * 2 + n_hI * 4
+    row_i = cI // 2 + cI // 32 if fp4 else cI * 2
+    idx_b = v_csa * row_i + n_hI * row_i + n_hI * 4
     csa_b = min(k, v_csa) * c * 2 + n_h * c * 2 + n_h * c * 4 + n_h * 4
     hca_b = v_hca * c * 2 + n_h * c * 2 + n_h * c * 4 + n_h * 4
     comp = 0
     if (t + 1) % m == 0:
         comp += (4 * m * c * 2 + c * 2) + (4 * m * cI * 2 + cI * 2)
+        if fp4:
+            comp += cI * 2 + cI // 2 + cI // 32
     if (t + 1) % mp == 0:
         comp += 2 * mp * c * 2 + c * 2
     return B * (idx_b + csa_b + hca_b + comp), B * idx_b
@@ -441,7 +461,7 @@ def main():
     torch.cuda.synchronize()
     K = args.steps
 
-    def timed(armed):
+    def timed(armed, steps=steps):
         """K steps between a barrier-free pair of stream events.  armed: also
         time every launch of the scores kernel with its own HIP events."""
         evs = [(ev.create(), ev.create()) for _ in range(K)] if armed else []
@@ -485,6 +505,13 @@ def main():
     torch.cuda.synchronize()
     ms_win = e0.elapsed_time(e1)
     del keep_w
+    # the same steps with the FP4 (MXFP4) indexer (reported beside the main line)
+    steps_f, keep_f = make_steps(cfg, wl, dev, n_dec, fp4=True)
+    run_steps(steps_f, 0, args.warmup, n_dec)
+    torch.cuda.synchronize()
+    ms_f, _ = timed(False, steps_f)
+    _, kf_ms = timed(True, steps_f)
+    del keep_f
     ts = [steps[(args.warmup + j) % n_dec][0] for j in range(K)]
     total_bytes = sum(step_bytes(cfg, t)[0] for t in ts)
     idx_bytes = sum(step_bytes(cfg, t)[1] for t in ts) / K
@@ -492,6 +519,9 @@ def main():
     achieved = idx_bytes / (k_avg_ms * 1e-3) / 1e9
     ms_step = ms / K
     value = cfg.B * K / (ms * 1e-3)
+    idx_bytes_f = sum(step_bytes(cfg, t, fp4=True)[1] for t in ts) / K
+    kf_avg_ms = sum(kf_ms) / len(kf_ms)
+    achieved_f = idx_bytes_f / (kf_avg_ms * 1e-3) / 1e9
     hbm_gbs = total_bytes / (ms * 1e-3) / 1e9
 
     # copy-kernel reference for achievable bandwidth
@@ -540,6 +570,14 @@ def main():
         "with_sliding_window": {"value": round(cfg.B * K / (ms_win * 1e-3), 1), "ms_per_step": round(ms_win / K, 5),
                                 "n_win": N_WIN, "note": "csa_attend_window / hca_attend_window: each layer's "
                                                         "128-token window joined to its compressed keys"},
+        "with_fp4_indexer": {"value": round(cfg.B * K / (ms_f * 1e-3), 1), "ms_per_step": round(ms_f / K, 5),
+                             "scores_kernel": SCORES_KERNEL_FP4, "scores_avg_launch_us": round(kf_avg_ms * 1e3, 3),
+                             "scores_achieved_gbs": round(achieved_f, 1),
+                             "scores_frac": round(achieved_f / PEAK_HBM_GBS, 4),
+                             "scores_algorithmic_bytes_per_launch": int(idx_bytes_f),
+                             "note": "csa_index_topk_fp4 on the MXFP4 K^I cache (68 B per entry: 64 code bytes + "
+                                     "4 E8M0 scales); new entries quantized as they are written; the top-k set "
+                                     "differs from the bf16 indexer's by the FP4 rounding of the scores"},
         "step_hbm_gbs": round(hbm_gbs, 1),
         "step_frac_of_peak": round(hbm_gbs / PEAK_HBM_GBS, 4),
         "copy_kernel_gbs": round(copy_gbs, 1),

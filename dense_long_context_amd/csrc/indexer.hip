@@ -232,12 +232,15 @@ __global__ void __launch_bounds__(256) scores_mfma_kernel(IdxArgs a) {
       for (int ht = 0; ht < HT; ++ht)
         acc[ht] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qf[ht][kt], kb, acc[ht], 0, 0, 0);
     }
-    float part = 0.f;
+    // four independent partial sums (one per head row of the lane), then a tree
+    float ps[4];
 #pragma unroll
-    for (int ht = 0; ht < HT; ++ht)
+    for (int r = 0; r < 4; ++r) {
+      ps[r] = wv[0][r] * fmaxf(acc[0][r], 0.f);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) part = fmaf(wv[ht][r], fmaxf(acc[ht][r], 0.f), part);
-    part = rows4_sum(part);
+      for (int ht = 1; ht < HT; ++ht) ps[r] = fmaf(wv[ht][r], fmaxf(acc[ht][r], 0.f), ps[r]);
+    }
+    const float part = rows4_sum((ps[0] + ps[1]) + (ps[2] + ps[3]));
     const int64_t s = s0 + (wave + 4 * it) * 16 + r16;
     if (g == 0 && s < s1) {
       const float score = canon_zero(part);
@@ -266,8 +269,8 @@ __global__ void __launch_bounds__(256) scores_mfma_kernel(IdxArgs a) {
 
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 
-template <int CI, int NS>
-__global__ void __launch_bounds__(256) scores_fp4_kernel(IdxArgs a) {
+template <int CI, int NS, int NW>
+__global__ void __launch_bounds__(64 * NW) scores_fp4_kernel(IdxArgs a) {
   constexpr int KB = CI / 32;               // scale bytes (32-dim blocks) per row
   constexpr int ROWB = CI / 2;              // code bytes per row
   constexpr int CPR = ROWB / 16;            // 16-byte chunks per code row
@@ -279,7 +282,7 @@ __global__ void __launch_bounds__(256) scores_fp4_kernel(IdxArgs a) {
   constexpr int HT = 4;                     // head tiles: up to 64 heads
   static_assert(CI == 128 || CI == 256, "c^I");
   __shared__ uint32_t hist[kBins];
-  __shared__ __attribute__((aligned(16))) unsigned char sK[4][NS][STB];
+  __shared__ __attribute__((aligned(16))) unsigned char sK[NW][NS][STB];
   const int64_t bq = blockIdx.y;
   const int64_t nvis = visible(a, bq);
   const int64_t s0 = int64_t(blockIdx.x) * a.keys_per_wg;
@@ -294,11 +297,11 @@ __global__ void __launch_bounds__(256) scores_fp4_kernel(IdxArgs a) {
   const uint8_t* Kc = static_cast<const uint8_t*>(a.KI) + b * a.cap * ROWB;
   const uint8_t* Ks = a.k_scale + b * a.cap * KB;
   const int64_t ntiles = (s1 - s0 + 15) / 16;
-  const int64_t my_tiles = ntiles > wave ? (ntiles - wave + 3) / 4 : 0;
+  const int64_t my_tiles = ntiles > wave ? (ntiles - wave + NW - 1) / NW : 0;
   // tile it of this wave: rows row0 .. row0+15, those past the chunk's end
   // repeat its last visible row
   auto issue = [&](int64_t it, int st) {
-    const int64_t row0 = s0 + (wave + 4 * it) * 16;  // < s1
+    const int64_t row0 = s0 + (wave + NW * it) * 16;  // < s1
     const uint32_t lds = (uint32_t)(uintptr_t)DLC_LDS(&sK[wave][st][0]);
 #pragma unroll
     for (int q = 0; q < NJ; ++q) {
@@ -390,13 +393,16 @@ __global__ void __launch_bounds__(256) scores_fp4_kernel(IdxArgs a) {
         acc[ht] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qa[ht][j], kb, acc[ht], 4, 4, 0, qs[ht][j], 0,
                                                                    ksc);
     }
-    float part = 0.f;
+    // four independent partial sums (one per head row of the lane), then a tree
+    float ps[4];
 #pragma unroll
-    for (int ht = 0; ht < HT; ++ht)
+    for (int r = 0; r < 4; ++r) {
+      ps[r] = wv[0][r] * fmaxf(acc[0][r], 0.f);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) part = fmaf(wv[ht][r], fmaxf(acc[ht][r], 0.f), part);
-    part = rows4_sum(part);
-    const int64_t s = s0 + (wave + 4 * it) * 16 + r16;
+      for (int ht = 1; ht < HT; ++ht) ps[r] = fmaf(wv[ht][r], fmaxf(acc[ht][r], 0.f), ps[r]);
+    }
+    const float part = rows4_sum((ps[0] + ps[1]) + (ps[2] + ps[3]));
+    const int64_t s = s0 + (wave + NW * it) * 16 + r16;
     if (g == 0 && s < s1) {
       const float score = canon_zero(part);
       a.scores[bq * a.score_ld + s] = score;
@@ -812,7 +818,10 @@ struct WsLayout {
 #endif
 constexpr int64_t kScoreWorkgroups = DLC_SCORES_WGS;
 #ifndef DLC_FP4_NS
-#define DLC_FP4_NS 8  // LDS stages per wave in the FP4 scores kernel (NS-1 tiles in flight)
+#define DLC_FP4_NS 4  // LDS stages per wave in the FP4 scores kernel (NS-1 tiles in flight)
+#endif
+#ifndef DLC_FP4_NW
+#define DLC_FP4_NW 8  // waves per workgroup of the FP4 scores kernel
 #endif
 int64_t keys_per_wg(int64_t BQ, int64_t vis_max) {
   const int64_t vis = vis_max > 0 ? vis_max : 1;
@@ -1011,8 +1020,10 @@ int csa_index_topk_fp4(int dtype, int64_t B, int64_t n_q, int64_t n_hI, int64_t 
     a.keys_per_wg = keys_per_wg(BQ, vis_max);
     dim3 grid{(unsigned)ceil_div(vis_max, a.keys_per_wg), (unsigned)BQ, 1u};
     StageTimer timer(DLC_STAGE_INDEX_SCORES, s);
-    if (cI == 128) hipLaunchKernelGGL((scores_fp4_kernel<128, DLC_FP4_NS>), grid, dim3(256), 0, s, a);
-    if (cI == 256) hipLaunchKernelGGL((scores_fp4_kernel<256, DLC_FP4_NS>), grid, dim3(256), 0, s, a);
+    if (cI == 128)
+      hipLaunchKernelGGL((scores_fp4_kernel<128, DLC_FP4_NS, DLC_FP4_NW>), grid, dim3(64 * DLC_FP4_NW), 0, s, a);
+    if (cI == 256)
+      hipLaunchKernelGGL((scores_fp4_kernel<256, DLC_FP4_NS, DLC_FP4_NW>), grid, dim3(64 * DLC_FP4_NW), 0, s, a);
     if ((rc = check_launch("csa_index_topk_fp4/scores"))) return rc;
   }
   return select_topk(a, BQ, vis_max, s);

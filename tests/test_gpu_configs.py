@@ -302,7 +302,7 @@ def test_hybrid1m_compressor_sample(hybrid):
     m, mp, c, cI = cfg.m, cfg.m_prime, cfg.c, cfg.cI
     off, width, _ = bench.stream_layout(cfg)
     Wall = np.hstack([f64(bench.stream_weight(cfg, nm)) for nm in bench.STREAMS])
-    Cc, KI, Ch = wl["sets"][0]
+    Cc, KI, Ch = wl["sets"][0][:3]
     n_csa, n_hca = wl["n_tot"] // m, wl["n_tot"] // mp
     csa_pick = [0, 1, 16383, 16384, 16385, 131071, n_csa - 2, n_csa - 1]
     hca_pick = [0, 511, 512, 4095, n_hca - 1]
@@ -324,7 +324,7 @@ def test_hybrid1m_compressor_sample(hybrid):
             g = {nm: S[:, off[nm]:off[nm] + width[nm]] for nm in ("Z", "KV")}
             assert_rows_close(Ch[b, i:i + 1], O.hca_compress(g["Z"], g["KV"], mp), TOL_STORE, f"C^HCA b={b} i={i}")
     # the other cache sets hold the same values
-    for Cc2, KI2, Ch2 in wl["sets"][1:]:
+    for Cc2, KI2, Ch2, *_ in wl["sets"][1:]:
         assert torch.equal(Cc2, Cc) and torch.equal(KI2, KI) and torch.equal(Ch2, Ch)
 
 
@@ -336,7 +336,7 @@ def test_hybrid1m_decode_steps(hybrid):
     m, mp, k, n_dec = cfg.m, cfg.m_prime, cfg.k, cfg.n_decode
     for s in (0, 3, 127, 255):
         t, calls = steps[s]
-        Cc, KI, Ch = wl["sets"][s % 3]
+        Cc, KI, Ch = wl["sets"][s % 3][:3]
         saved = []
         if (t + 1) % m == 0:
             i = (t + 1) // m - 1
@@ -399,7 +399,7 @@ def test_hybrid1m_prefill_sample(hybrid):
     qh = dlc.dlc_project(cQ, Wq["UQ_hca"]).reshape(B, nq, cfg.n_h, c)
     tt = torch.tensor([[n_ctx + o for o in offs]] * B, dtype=torch.int64, device=DEV)
     t_max = n_ctx - 1
-    Cc, KI, Ch = wl["sets"][0]
+    Cc, KI, Ch = wl["sets"][0][:3]
     idx, cnt = dlc.csa_index_topk(qI, wI, KI, tt, t_max, m, k)
     o1, l1 = dlc.csa_attend(q, Cc, idx, cnt)
     o2, l2 = dlc.hca_attend(qh, Ch, tt, t_max, mp)
@@ -440,7 +440,7 @@ def test_hybrid1m_decode_steps_with_window(hybrid):
         print(f"decode step with window s={s} t={t}", flush=True)
         bench.run_steps(steps, s, 1, n_dec)
         torch.cuda.synchronize()
-        Cc, KI, Ch = wl["sets"][s % 3]
+        Cc, KI, Ch = wl["sets"][s % 3][:3]
         for b in range(cfg.B):
             sel = _np(keep["idx"][b, 0])[:int(keep["cnt"][b, 0])].astype(np.int64)
             pos = O.window_positions(t, n_win)
@@ -454,3 +454,44 @@ def test_hybrid1m_decode_steps_with_window(hybrid):
             o2, l2 = O.mqa_attend(Q["qh"][s][b, 0].cpu(), Rh)
             o_r, l_r = O.merge_lse(o1, l1, o2, l2)
             _check_attend(keep["o_hca"][b, 0], keep["lse_hca"][b, 0], o_r, l_r, TOL_ATT_BF16, f"HCA+window s={s} b={b}")
+
+
+def test_hybrid1m_decode_steps_fp4(hybrid):
+    """The benchmark's decode steps with the FP4 indexer: the MXFP4 key cache
+    (entries written by the full pass and, on compress steps, by the step
+    itself) bit-exact against the oracle's quantization of K^I, and the
+    selected set against the oracle's FP4 scores over all visible entries."""
+    cfg, wl, _, _, bench = hybrid
+    m, k, n_dec, cI = cfg.m, cfg.k, cfg.n_decode, cfg.cI
+    steps, keep = bench.make_steps(cfg, wl, torch.device(DEV), n_dec, fp4=True)
+    Q = wl["Q"]
+    for s in (3, 255):
+        t, _ = steps[s]
+        Cc, KI, Ch, KIc, KIs = wl["sets"][s % 3]
+        i = (t + 1) // m - 1 if (t + 1) % m == 0 else None
+        if i is not None:                                   # the step re-quantizes entry i
+            KIc[:, i] = 0
+            KIs[:, i] = 0
+        print(f"fp4 decode step s={s} t={t}", flush=True)
+        bench.run_steps(steps, s, 1, n_dec)
+        torch.cuda.synchronize()
+        nv = t // m
+        if i is not None:                                   # the entry this step wrote, all sequences
+            codes_i, shared_i = O.mxfp4_quantize(f64(KI[:, i].cpu()))
+            c_dev = KIc[:, i].cpu().numpy().astype(np.int64)
+            assert np.array_equal(np.stack([c_dev & 15, c_dev >> 4], axis=-1).reshape(cfg.B, cI), codes_i)
+            assert np.array_equal(KIs[:, i].cpu().numpy().astype(np.int64) - 127, shared_i)
+        for b in (0, cfg.B - 1):
+            K = f64(KI[b, :nv].cpu())
+            codes, shared = O.mxfp4_quantize(K)
+            c_dev = KIc[b, :nv].cpu().numpy().astype(np.int64)
+            got = np.stack([c_dev & 15, c_dev >> 4], axis=-1).reshape(nv, cI)
+            assert np.array_equal(got, codes), f"fp4 codes step {s} b={b}"
+            assert np.array_equal(KIs[b, :nv].cpu().numpy().astype(np.int64) - 127, shared), f"fp4 scales {s} b={b}"
+            qI, wI = Q["qI"][s][b, 0].cpu(), Q["wI"][s][b, 0].cpu()
+            qd = O.mxfp4_dequantize(*O.mxfp4_quantize(qI))
+            kd = O.mxfp4_dequantize(codes, shared)
+            ref = O.index_scores(qd, wI, kd, t, m)
+            slack = 2e-6 * (np.abs(kd) @ np.abs(qd).T @ np.abs(f64(wI))) * (cI + qd.shape[0]) ** 0.5 + 1e-30
+            check_topk(_np(keep["idx"][b, 0]).astype(np.int64), int(keep["cnt"][b, 0]), ref, k,
+                       abs_slack=float(slack.max()))
