@@ -32,6 +32,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "decode query-tokens/s per CSA+HCA layer at 1M ctx; achieved HBM GB/s vs peak"
 PEAK_HBM_GBS = 8000.0
+PEAK_BF16_TFLOPS = 2500.0  # dense bf16 MFMA
 SCORES_KERNEL = "scores_mfma_kernel<4, 4, 4>"
 SCORES_KERNEL_FP4 = "scores_fp4_kernel<128, 4, 8>"
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "indexer_scores_hybrid1m_counters.json")
@@ -271,6 +272,81 @@ def make_steps(cfg, wl, dev, n_dec, window=False, fp4=False):
     return steps, keep
 
 
+def prefill_pass(cfg, wl, dev, n_pref=4096, chunk=256, ev=None):
+    """The chunked causal prefill of config 5: queries at t = 2^20-n_pref .. 2^20-1
+    of every sequence, `chunk` per sequence per call, through csa_index_topk (which
+    runs query-tiled at this many queries), csa_attend and hca_attend.  Returns the
+    timings (ms) and the indexer's algorithmic FLOPs."""
+    import torch
+
+    import dense_long_context_amd as dlc
+    from dense_long_context_amd import binding
+
+    B, d, c, cI, m, mp, k, n_h, n_hI = cfg.B, cfg.d, cfg.c, cfg.cI, cfg.m, cfg.m_prime, cfg.k, cfg.n_h, cfg.n_hI
+    n_ctx, n_tot = wl["n_ctx"], wl["n_tot"]
+    Cc, KI, Ch = wl["sets"][0][:3]
+    Wq = {nm: query_weight(cfg, nm).t().contiguous().to(dev) for nm in ("DQ", "w", "IUQ", "UQ", "UQ_hca")}
+    chunks = []
+    for c0 in range(0, n_pref, chunk):
+        h = torch.cat([hidden_rows(cfg, b, n_tot, n_ctx - n_pref + c0, n_ctx - n_pref + c0 + chunk, dev)
+                       for b in range(B)])                                  # [B*chunk][d]
+        cQ = dlc.dlc_project(h, Wq["DQ"])
+        chunks.append(dict(
+            qI=dlc.dlc_project(cQ, Wq["IUQ"]).reshape(B, chunk, n_hI, cI),
+            wI=dlc.dlc_project(h, Wq["w"], out_dtype=torch.float32).reshape(B, chunk, n_hI),
+            q=dlc.dlc_project(cQ, Wq["UQ"]).reshape(B, chunk, n_h, c),
+            qh=dlc.dlc_project(cQ, Wq["UQ_hca"]).reshape(B, chunk, n_h, c),
+            t=torch.arange(n_ctx - n_pref + c0, n_ctx - n_pref + c0 + chunk, device=dev,
+                           dtype=torch.int64)[None].expand(B, chunk).contiguous()))
+        del h, cQ
+    ws_i = torch.empty(dlc.csa_index_topk_ws(B, chunk, wl["cap_csa"], k), dtype=torch.uint8, device=dev)
+    ws_c = torch.empty(max(1, dlc.csa_attend_ws(B, chunk, n_h, c, k)), dtype=torch.uint8, device=dev)
+    ws_h = torch.empty(max(1, dlc.hca_attend_ws(B, chunk, n_h, c, wl["cap_hca"])), dtype=torch.uint8, device=dev)
+    idx = torch.empty((B, chunk, k), dtype=torch.int32, device=dev)
+    cnt = torch.empty((B, chunk), dtype=torch.int32, device=dev)
+    o1 = torch.empty((B, chunk, n_h, c), dtype=torch.float32, device=dev)
+    l1 = torch.empty((B, chunk, n_h), dtype=torch.float32, device=dev)
+    o2, l2 = torch.empty_like(o1), torch.empty_like(l1)
+
+    def run(q, evs=None):
+        t_max = int(q["t"].max())
+        if evs is not None:
+            binding.dlc_timing_arm(binding.STAGE_INDEX_SCORES, evs[0], evs[1])
+        dlc.csa_index_topk(q["qI"], q["wI"], KI, q["t"], t_max, m, k, idx=idx, count=cnt, ws=ws_i)
+        if evs is not None:
+            binding.dlc_timing_arm(binding.STAGE_CSA_ATTEND, evs[2], evs[3])
+        dlc.csa_attend(q["q"], Cc, idx, cnt, out=o1, lse=l1, ws=ws_c)
+        if evs is not None:
+            binding.dlc_timing_arm(binding.STAGE_HCA_ATTEND, evs[4], evs[5])
+        dlc.hca_attend(q["qh"], Ch, q["t"], t_max, mp, out=o2, lse=l2, ws=ws_h)
+
+    run(chunks[0])
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for q in chunks:
+        run(q)
+    e1.record()
+    torch.cuda.synchronize()
+    total_ms = e0.elapsed_time(e1)
+    # a second pass with the scores kernel and the two attentions bracketed by HIP events
+    scores_ms, csa_ms, hca_ms = [], [], []
+    for q in chunks:
+        evs = [ev.create() for _ in range(6)]
+        run(q, evs)
+        torch.cuda.synchronize()
+        scores_ms.append(ev.elapsed_ms(evs[0], evs[1]))
+        csa_ms.append(ev.elapsed_ms(evs[2], evs[3]))
+        hca_ms.append(ev.elapsed_ms(evs[4], evs[5]))
+        for e in evs:
+            ev.destroy(e)
+    vis = sum((t // m) for t in range(n_ctx - n_pref, n_ctx)) * B
+    idx_flop = 2.0 * vis * n_hI * cI
+    hca_flop = 4.0 * sum((t // mp) for t in range(n_ctx - n_pref, n_ctx)) * B * n_h * c
+    return dict(total_ms=total_ms, scores_ms=sum(scores_ms), csa_ms=sum(csa_ms), hca_ms=sum(hca_ms),
+                idx_flop=idx_flop, hca_flop=hca_flop, n_pref=n_pref, chunk=chunk)
+
+
 def step_bytes(cfg, t, fp4=False):
     """Algorithmic HBM bytes of one decode step (B queries at position t).  The
     second value is the indexer scores kernel's share: every visible K^I row
@@ -423,6 +499,7 @@ def main():
     ap.add_argument("--steps", type=int, default=240)
     ap.add_argument("--warmup", type=int, default=16)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true", help="skip the chunked-prefill measurement")
     ap.add_argument("--repeat", type=int, default=1, help="time the K steps this many times, report the best")
     ap.add_argument("--pmc-probe", action="store_true",
                     help="run only the indexer on the decode shapes plus a copy kernel of known size "
@@ -584,6 +661,19 @@ def main():
         "setup": {"projection_s": round(wl["t_proj"], 3), "compress_ms_per_cache_set": round(wl["t_comp"] * 1e3, 2),
                   "compress_stream_gbs": round(wl["stream_bytes"] / wl["t_comp"] / 1e9, 1)},
     }
+    if not args.no_prefill:
+        log("chunked causal prefill of 4096 queries per sequence")
+        pf = prefill_pass(cfg, wl, dev, ev=ev)
+        result["prefill"] = {
+            "queries": cfg.B * pf["n_pref"], "chunk_per_sequence": pf["chunk"], "ms": round(pf["total_ms"], 3),
+            "query_tokens_per_s": round(cfg.B * pf["n_pref"] / (pf["total_ms"] * 1e-3), 1),
+            "indexer_scores_ms": round(pf["scores_ms"], 3),
+            "indexer_scores_tflops": round(pf["idx_flop"] / (pf["scores_ms"] * 1e-3) / 1e12, 1),
+            "indexer_scores_mfma_frac": round(pf["idx_flop"] / (pf["scores_ms"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "csa_attend_ms": round(pf["csa_ms"], 3), "hca_attend_ms": round(pf["hca_ms"], 3),
+            "hca_attend_tflops": round(pf["hca_flop"] / (pf["hca_ms"] * 1e-3) / 1e12, 1),
+            "note": "t = 2^20-4096 .. 2^20-1, causal against the full caches; the indexer runs query-tiled "
+                    "(scores_prefill_kernel, v_mfma_f32_32x32x16_bf16) at 256 queries per sequence per call"}
     if not args.no_cpu_baseline:
         log("timing the oracle on a bounded sample")
         result["cpu_baseline"] = cpu_baseline(cfg)

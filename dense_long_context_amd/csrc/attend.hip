@@ -417,10 +417,6 @@ __device__ __forceinline__ void wait_vmcnt(int n) {
 }
 
 
-__device__ __forceinline__ void lds_barrier() {
-  __builtin_amdgcn_s_waitcnt(0xC07F);  // LDS and scalar-memory counter only
-  __builtin_amdgcn_s_barrier();
-}
 
 constexpr int kTileBytes = 34816;   // 32 rows of 1 KB at the offsets of h16_row_off, rounded up to 1 KB
 constexpr int kMaxGatherKeys = 2048;  // keys per split whose rows sit in LDS

@@ -140,6 +140,14 @@ __device__ __forceinline__ void wait_vm() {
   __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
 }
 
+// Workgroup barrier that waits only for LDS and scalar-memory operations:
+// __syncthreads would also drain every vector-memory load in flight (the
+// direct global->LDS loads of the next tiles).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt and expcnt left at their maxima
+  __builtin_amdgcn_s_barrier();
+}
+
 // Records the caller's armed events around a stage's launches (see
 // dlc_timing_arm); a no-op unless armed.
 class StageTimer {

@@ -32,6 +32,12 @@ namespace {
 constexpr int kBins = 2048;      // first digit: top 11 bits of the key
 constexpr int kShift1 = 21;
 constexpr int kMaxK = 8192;
+#ifndef DLC_PREFILL_NB
+#define DLC_PREFILL_NB 2  // stages of the prefill scores kernel's query ring
+#endif
+#ifndef DLC_PREFILL_HPS
+#define DLC_PREFILL_HPS 2  // heads per stage of that ring
+#endif
 
 struct IdxArgs {
   const void* qI;      // [BQ][n_hI][cI]
@@ -409,6 +415,193 @@ __global__ void __launch_bounds__(64 * NW) scores_fp4_kernel(IdxArgs a) {
       atomicAdd(&hist[order_key(score) >> kShift1], 1u);
     }
   }
+  flush_hist(hist, a.hist + bq * kBins);
+}
+
+// ---------------------------------------------------------------- scores (prefill)
+//
+// Many queries of one sequence (a prefill chunk; [Scratch] §6.4's cost
+// paragraph: the indexer's term is quadratic in n).  Keys are now reused
+// across queries, so the product is a real GEMM: a workgroup scores a tile
+// of TQ = 64 queries x TK = 256 keys, looping over the heads:
+//   S_h[32 queries][32 keys] = Q_h[32][16] . K^T[16][32]  (v_mfma_f32_32x32x16_bf16,
+//   which on this part issues at about 1.7x the rate of the 16x16x32 form)
+//   score[q][s] += w[q][h] * ReLU(S_h[q][s])
+// Wave w owns queries 32*(w/4) .. +31 and keys 64*(w%4) .. +63 of the tile.
+// Its K^T operands (64 keys x 128 dims, 64 VGPRs) stay in registers for all
+// heads; each head's 64 x 128 query tile arrives by direct global->LDS loads
+// two heads at a time into a double buffer of 32 KB stages, one barrier per
+// stage; an odd head count is padded with a zero-weight copy of the last
+// head.  The ReLU-and-weight epilogue of each
+// head runs behind the next head's MFMAs.
+// Within a query row, 16-byte chunk c sits at slot c ^ (row % 16), so the 16
+// rows of one ds_read_b128 pass fall on distinct banks.  Only visible
+// entries are written; hist_kernel then builds the first-digit histogram
+// from the scores.  Grid: (key tiles, query tiles, B), key tiles fastest, so
+// the workgroups resident on an XCD share one query tile in its L2.
+
+template <int CI>
+__global__ void __launch_bounds__(512) scores_prefill_kernel(IdxArgs a) {
+  constexpr int KS = CI / 16;           // 16-dim steps of v_mfma_f32_32x32x16_bf16
+  constexpr int TQ = 64, TK = 256, NW = 8, NB = DLC_PREFILL_NB;
+  constexpr int QROWB = CI * 2;         // bytes of one query-head row
+  constexpr int QTILEB = TQ * QROWB;    // one head's query tile
+  constexpr int CPR = QROWB / 16;       // 16-byte chunks per row
+  constexpr int ROWS_PER_LOAD = 1024 / QROWB;
+  constexpr int LOADS_PER_HEAD = QTILEB / 1024 / NW;  // per wave
+  constexpr int HPS = DLC_PREFILL_HPS;                 // heads per stage (even)
+  constexpr int LPS = HPS * LOADS_PER_HEAD;           // per wave and stage
+  static_assert(CPR == 16 && LOADS_PER_HEAD >= 1, "tile geometry for c^I = 128");
+  static_assert(HPS % 2 == 0 && HPS <= 64, "heads per stage");
+  __shared__ __attribute__((aligned(1024))) unsigned char sQ[NB][HPS][QTILEB];
+  __shared__ float sW[64 + HPS][TQ];    // w[h][q]; rows n_hI .. stay 0 (head counts not a multiple of HPS)
+  __shared__ int64_t sVis[TQ];
+  __shared__ int64_t sMax;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int r32 = lane & 31, hi = lane >> 5;
+  const int64_t b = blockIdx.z;
+  const int64_t q0 = int64_t(blockIdx.y) * TQ;
+  const int64_t k0 = int64_t(blockIdx.x) * TK;
+  const int nq = int(min(int64_t(TQ), a.n_q - q0));
+  const int n_hI = int(a.n_hI);
+  const int ngroups = (n_hI + HPS - 1) / HPS;  // heads go in groups of HPS; a short last group is padded
+                                               // with zero-weight copies of the last head
+  if (tid == 0) sMax = 0;
+  __syncthreads();
+  if (tid < TQ) {
+    const int64_t v = tid < nq ? visible(a, b * a.n_q + q0 + tid) : 0;
+    sVis[tid] = v;
+    atomicMax(reinterpret_cast<unsigned long long*>(&sMax), (unsigned long long)v);
+  }
+  for (int i = tid; i < TQ * (64 + HPS); i += NW * 64) {
+    const int h = i / TQ, q = i % TQ;
+    sW[h][q] = (q < nq && h < n_hI) ? a.wI[(b * a.n_q + q0 + q) * n_hI + h] : 0.f;
+  }
+  __syncthreads();
+  if (k0 >= sMax) return;  // no query of the tile sees these keys
+
+  // the query tiles of head group p -> stage p % NB: load j of a wave covers
+  // rows ROWS_PER_LOAD*(wave*LOADS_PER_HEAD + j) ..; rows past the tile's
+  // queries repeat its last query, a head past n_hI repeats the last head
+  const bf16_raw* qbase = static_cast<const bf16_raw*>(a.qI) + (b * a.n_q + q0) * n_hI * CI;
+  const uint32_t lds0 = (uint32_t)(uintptr_t)DLC_LDS(&sQ[0][0][0]);
+  auto issue = [&](int p) {
+#pragma unroll
+    for (int u = 0; u < HPS; ++u) {
+      const bf16_raw* base = qbase + min(HPS * p + u, n_hI - 1) * CI;
+#pragma unroll
+      for (int j = 0; j < LOADS_PER_HEAD; ++j) {
+        const int ld = wave * LOADS_PER_HEAD + j;
+        const int row = ld * ROWS_PER_LOAD + lane / CPR;
+        const int chunk = (lane % CPR) ^ (row % CPR);
+        const int qr = min(row, nq - 1);
+        const uint32_t off = uint32_t(qr * n_hI * QROWB + chunk * 16);
+        dma_row(base, off, lds0 + uint32_t(((p % NB) * HPS + u) * QTILEB + ld * 1024));
+      }
+    }
+  };
+  const int npre = min(NB - 1, ngroups);
+  for (int p = 0; p < npre; ++p) issue(p);
+
+  // K^T operands (B, 16 dims x 32 keys per step) of this wave: key
+  // k0 + 64*(wave%4) + 32*j + r32, dims 16*ks + 8*hi .. +7
+  const bf16_raw* Kb = static_cast<const bf16_raw*>(a.KI) + b * a.cap * CI;
+  bf16x8 kf[2][KS];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int64_t key = min(k0 + 64 * (wave & 3) + 32 * j + r32, a.cap - 1);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      kf[j][ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(Kb + key * CI + 16 * ks + 8 * hi));
+  }
+  // wait for the key operands (and the first query tiles) once, outside the head loop
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) asm volatile("" ::"v"(kf[j][ks]));
+
+  f32x16 sc[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sc[j][r] = 0.f;
+  const int qw = 32 * (wave >> 2);  // the wave's first query row in the tile
+  const int qrow = qw + r32;        // the query row this lane supplies to the A operand
+
+  // one head's S^T tiles, and its epilogue: score += w[q][h] * ReLU(S_h)
+  auto head_mfma = [&](const unsigned char* tile, f32x16 (&S)[2]) {
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const int slot = (2 * ks + hi) ^ (qrow % CPR);
+      const bf16x8 qa = *reinterpret_cast<const bf16x8*>(tile + qrow * QROWB + slot * 16);
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        S[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf[j][ks], ks == 0 ? f32x16{} : S[j], 0, 0, 0);
+    }
+  };
+  // S[j] lane: key 32j + r32 of the wave's keys, queries qw + 8(r/4) + 4hi + r%4
+  auto head_epilogue = [&](int h, const f32x16 (&S)[2]) {
+    const float* wrow = &sW[h][qw + 4 * hi];
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+      const float4 w = *reinterpret_cast<const float4*>(wrow + 8 * r4);
+      const float wv[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) sc[j][4 * r4 + e] = fmaf(wv[e], fmaxf(S[j][4 * r4 + e], 0.f), sc[j][4 * r4 + e]);
+    }
+  };
+  // heads in groups of HPS (one barrier per group); the epilogue of each
+  // head runs behind the next head's MFMAs
+  f32x16 Sa[2], Sb[2];
+  for (int p = 0; p < ngroups; ++p) {
+    const int after = min(NB - 2, ngroups - 1 - p);  // groups issued after group p
+    if (after >= 2) wait_vm<2 * LPS>();
+    else if (after == 1) wait_vm<LPS>();
+    else wait_vm<0>();
+    lds_barrier();  // every wave is past group p-1: its stage takes group p+NB-1
+    if (p + NB - 1 < ngroups) issue(p + NB - 1);
+#pragma unroll
+    for (int u = 0; u < HPS; u += 2) {
+      const int h = HPS * p + u;
+      head_mfma(&sQ[p % NB][u][0], Sa);
+      if (h > 0) head_epilogue(h - 1, Sb);
+      head_mfma(&sQ[p % NB][u + 1][0], Sb);
+      head_epilogue(h, Sa);
+    }
+  }
+  if (ngroups > 0) head_epilogue(HPS * ngroups - 1, Sb);
+  // visible entries only
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int qr = qw + 8 * (r >> 2) + 4 * hi + (r & 3);
+    if (qr >= nq) continue;
+    const int64_t nv = sVis[qr];
+    float* out = a.scores + (b * a.n_q + q0 + qr) * a.score_ld;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int64_t key = k0 + 64 * (wave & 3) + 32 * j + r32;
+      if (key < nv) out[key] = canon_zero(sc[j][r]);
+    }
+  }
+}
+
+// first-digit histogram of the scores, chunk by chunk (the prefill path; the
+// other scores kernels build it as they go)
+__global__ void __launch_bounds__(256) hist_kernel(IdxArgs a) {
+  __shared__ uint32_t hist[kBins];
+  const int64_t bq = blockIdx.y;
+  const int64_t nvis = visible(a, bq);
+  const int64_t s0 = int64_t(blockIdx.x) * a.keys_per_wg;
+  if (s0 >= nvis) return;
+  const int64_t s1 = min(nvis, s0 + a.keys_per_wg);
+  for (int i = threadIdx.x; i < kBins; i += blockDim.x) hist[i] = 0;
+  __syncthreads();
+  const float* sc = a.scores + bq * a.score_ld;
+  for (int64_t s = s0 + threadIdx.x; s < s1; s += blockDim.x) atomicAdd(&hist[order_key(sc[s]) >> kShift1], 1u);
   flush_hist(hist, a.hist + bq * kBins);
 }
 
@@ -817,6 +1010,11 @@ struct WsLayout {
 #define DLC_SCORES_WGS 512
 #endif
 constexpr int64_t kScoreWorkgroups = DLC_SCORES_WGS;
+// queries per sequence from which the indexer runs query-tiled (prefill)
+#ifndef DLC_PREFILL_MIN_Q
+#define DLC_PREFILL_MIN_Q 64
+#endif
+constexpr int64_t kPrefillMinQueries = DLC_PREFILL_MIN_Q;
 #ifndef DLC_FP4_NS
 #define DLC_FP4_NS 4  // LDS stages per wave in the FP4 scores kernel (NS-1 tiles in flight)
 #endif
@@ -948,9 +1146,13 @@ int csa_index_topk(int dtype, int64_t B, int64_t n_q, int64_t n_hI, int64_t cI, 
     a.keys_per_wg = keys_per_wg(BQ, vis_max);
     const int64_t nchunks = ceil_div(vis_max, a.keys_per_wg);
     dim3 grid{(unsigned)nchunks, (unsigned)BQ, 1u};
+    const bool prefill = mfma && cI == 128 && n_q >= kPrefillMinQueries;
     {
     StageTimer timer(DLC_STAGE_INDEX_SCORES, s);
-    if (mfma) {
+    if (prefill) {
+      dim3 pgrid{(unsigned)ceil_div(vis_max, 256), (unsigned)ceil_div(n_q, 64), (unsigned)B};
+      hipLaunchKernelGGL((scores_prefill_kernel<128>), pgrid, dim3(512), 0, s, a);
+    } else if (mfma) {
       const int HT = int(ceil_div(n_hI, 16)), KT = int(cI / 32);
 #define DLC_SCORES(ht, kt) \
   if (HT == ht && KT == kt) hipLaunchKernelGGL((scores_mfma_kernel<ht, kt, 4>), grid, dim3(256), 0, s, a);
@@ -968,6 +1170,10 @@ int csa_index_topk(int dtype, int64_t B, int64_t n_q, int64_t n_hI, int64_t cI, 
     }
     }
     if ((rc = check_launch("csa_index_topk/scores"))) return rc;
+    if (prefill) {  // the first-digit histogram, which the other scores kernels build as they go
+      hipLaunchKernelGGL(hist_kernel, grid, dim3(256), 0, s, a);
+      if ((rc = check_launch("csa_index_topk/hist"))) return rc;
+    }
   }
   return select_topk(a, BQ, vis_max, s);
 }

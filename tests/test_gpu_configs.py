@@ -417,6 +417,43 @@ def test_hybrid1m_prefill_sample(hybrid):
             _check_attend(o2[b, j], l2[b, j], o_r, l_r, TOL_ATT_BF16, f"prefill HCA b={b} t={t}")
 
 
+def test_hybrid1m_prefill_chunk_query_tiled(hybrid):
+    """A 256-query chunk of the prefill per sequence (t = 2^20-4096 .. 2^20-3841),
+    as the benchmark calls it: the indexer runs query-tiled at this many queries.
+    The selected sets and both attention outputs of a sample of queries per
+    sequence (first, last and interior query tiles) against the oracle."""
+    cfg, wl, _, _, bench = hybrid
+    B, m, mp, k, c, cI = cfg.B, cfg.m, cfg.m_prime, cfg.k, cfg.c, cfg.cI
+    n_ctx, nq = wl["n_ctx"], 256
+    Wq = {nm: bench.query_weight(cfg, nm).t().contiguous().to(DEV) for nm in ("DQ", "w", "IUQ", "UQ", "UQ_hca")}
+    h = torch.cat([bench.hidden_rows(cfg, b, wl["n_tot"], n_ctx - 4096, n_ctx - 4096 + nq, torch.device(DEV))
+                   for b in range(B)])
+    cQ = dlc.dlc_project(h, Wq["DQ"])
+    qI = dlc.dlc_project(cQ, Wq["IUQ"]).reshape(B, nq, cfg.n_hI, cI)
+    wI = dlc.dlc_project(h, Wq["w"], out_dtype=torch.float32).reshape(B, nq, cfg.n_hI)
+    q = dlc.dlc_project(cQ, Wq["UQ"]).reshape(B, nq, cfg.n_h, c)
+    qh = dlc.dlc_project(cQ, Wq["UQ_hca"]).reshape(B, nq, cfg.n_h, c)
+    tt = torch.arange(n_ctx - 4096, n_ctx - 4096 + nq, dtype=torch.int64, device=DEV)[None].expand(B, nq).contiguous()
+    t_max = int(tt.max())
+    Cc, KI, Ch = wl["sets"][0][:3]
+    print(f"prefill chunk: {B}x{nq} queries", flush=True)
+    idx, cnt = dlc.csa_index_topk(qI, wI, KI, tt, t_max, m, k)
+    o1, l1 = dlc.csa_attend(q, Cc, idx, cnt)
+    o2, l2 = dlc.hca_attend(qh, Ch, tt, t_max, mp)
+    torch.cuda.synchronize()
+    for b in range(B):
+        KIb, Ccb, Chb = KI[b].cpu(), Cc[b].cpu(), Ch[b].cpu()
+        for j in ((0, 255), (63, 64), (100, 191))[b % 3]:
+            t = int(tt[b, j])
+            _check_index(qI[b, j].cpu(), wI[b, j].cpu(), KIb[:t // m], t, m, k, idx[b, j].cpu(), cnt[b, j].cpu(),
+                         None, f"prefill tiled b={b} j={j}")
+            sel = _np(idx[b, j])[:int(cnt[b, j])].astype(np.int64)
+            o_r, l_r = O.csa_attend(q[b, j].cpu(), Ccb, sel)
+            _check_attend(o1[b, j], l1[b, j], o_r, l_r, TOL_ATT_BF16, f"prefill tiled CSA b={b} j={j}")
+            o_r, l_r = O.hca_attend(qh[b, j].cpu(), Chb[:t // mp], t, mp)
+            _check_attend(o2[b, j], l2[b, j], o_r, l_r, TOL_ATT_BF16, f"prefill tiled HCA b={b} j={j}")
+
+
 def test_hybrid1m_decode_steps_with_window(hybrid):
     """The benchmark's decode steps with each layer's sliding-window branch
     joined in: the window rows against the oracle's projection of the

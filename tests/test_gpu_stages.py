@@ -134,6 +134,37 @@ def test_index_topk(dtype, B, n_q, n_hI, cI, m, k, cap, ts):
             check_topk(idx[b, j], cnt[b, j], ref, k, abs_slack=float(slack.max()) if nv else 0.0)
 
 
+@pytest.mark.parametrize("B,n_q,n_hI,m,k,cap,seed", [
+    (2, 100, 64, 4, 100, 3000, 1),      # two query tiles (64 + 36), mixed visibilities
+    (1, 64, 20, 2, 50, 700, 2),         # 20 heads, one full tile
+    (3, 70, 64, 4, 1024, 2000, 3),      # k >= visible for most queries
+])
+def test_index_topk_prefill(B, n_q, n_hI, m, k, cap, seed):
+    """Many queries per sequence: the query-tiled MFMA scores kernel and the
+    histogram pass, against the oracle for every query."""
+    cI = 128
+    qI = synth.normal((B, n_q, n_hI, cI), 700 + seed, dtype="bf16")
+    wI = synth.normal((B, n_q, n_hI), 701 + seed, dtype="f32")
+    KI = synth.normal((B, cap, cI), 702 + seed, dtype="bf16")
+    rng = np.random.default_rng(seed)
+    t = torch.from_numpy(rng.integers(0, m * cap + 1, size=(B, n_q))).to(torch.int64)
+    t[0, 0], t[0, 1] = 0, m * cap          # nothing visible / everything visible
+    t_max = int(t.max())
+    scores = torch.full((B, n_q, cap), float("nan"), dtype=torch.float32, device=DEV)
+    idx, cnt = dlc.csa_index_topk(qI.to(DEV), wI.to(DEV), KI.to(DEV), t.to(DEV), t_max, m, k, scores=scores)
+    torch.cuda.synchronize()
+    idx, cnt, sc = idx.cpu().numpy(), cnt.cpu().numpy(), scores.cpu().numpy()
+    for b in range(B):
+        for j in range(n_q):
+            tt = int(t[b, j])
+            ref = O.index_scores(qI[b, j], wI[b, j], KI[b], tt, m)
+            nv = len(ref)
+            slack = _score_slack(qI[b, j], wI[b, j], KI[b, :nv]) if nv else np.zeros(0)
+            assert np.all(np.abs(sc[b, j, :nv] - ref) <= slack), f"scores b={b} q={j}"
+            assert np.isnan(sc[b, j, nv:]).all(), f"entries past the visible range written b={b} q={j}"
+            check_topk(idx[b, j], cnt[b, j], ref, k, abs_slack=float(slack.max()) if nv else 0.0)
+
+
 def test_index_topk_ties_pick_smallest_indices():
     # every score equal (zero keys): the k smallest indices, in order
     B, cap, k = 1, 3000, 100
