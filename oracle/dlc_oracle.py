@@ -40,7 +40,15 @@ Readings of points the pages leave open (each listed in the design notes):
   the nearest E2M1 value with ties to the even code and saturated at 6; a
   zero element is stored as +0.  Both q^I and K^I are quantized this way and
   the score is the exact fp64 value of the formula on the dequantized
-  operands (w^I stays fp32).
+  operands (w^I stays fp32);
+* [Evolution] §6.2 derives the indexer key from the compressed KV entry,
+  k^I_u = c^comp_u W^I_k, and the indexer query from the hidden state,
+  q^I_{t,j} = h_t W^I_{q,j}; [Scratch] §6.2-6.4 instead compresses separate
+  indexer streams and up-projects c^Q.  Both derivations feed the same
+  scoring formula;
+* sink logits ([Scratch] §12 names them without a formula) are read as one
+  logit z_h per head that joins the softmax as an extra key whose value is
+  the zero vector: it takes probability mass and contributes nothing.
 """
 
 from __future__ import annotations
@@ -81,6 +89,10 @@ __all__ = [
     "mxfp4_quantize",
     "mxfp4_dequantize",
     "index_scores_fp4",
+    "evolution_indexer_keys",
+    "evolution_indexer_queries",
+    "mqa_attend_with_sink",
+    "apply_sink",
 ]
 
 
@@ -322,6 +334,22 @@ def index_scores_fp4(qI, wI, KI, t: int, m: int) -> np.ndarray:
 
 
 # --------------------------------------------------------------------------
+# the [Evolution] derivation of the indexer's inputs (§6.2)
+# --------------------------------------------------------------------------
+
+def evolution_indexer_keys(Ccomp, W_kI) -> np.ndarray:
+    """k^I_u = c^comp_u W^I_k: the indexer key of every compressed entry, a
+    projection of the entry itself ([Evolution] §6.2)."""
+    return project(Ccomp, W_kI)
+
+
+def evolution_indexer_queries(h_t, W_qI, n_hI: int, cI: int) -> np.ndarray:
+    """q^I_{t,j} = h_t W^I_{q,j} for the n_hI heads, side by side in W
+    ([Evolution] §6.2): rows [n_hI][cI]."""
+    return split_heads(project(h_t, W_qI), n_hI, cI)
+
+
+# --------------------------------------------------------------------------
 # shared-KV multi-query attention ([Scratch] §8, §10, §11)
 # --------------------------------------------------------------------------
 
@@ -379,6 +407,36 @@ def window_attend(q, Cwin, t: int, n_win: int, scale=None):
     position: row p holds c^window_p."""
     Cwin = f64(Cwin)
     return mqa_attend(q, Cwin[window_positions(t, n_win)], scale)
+
+
+def mqa_attend_with_sink(q, KV, z, scale=None):
+    """Shared-KV MQA with one sink logit per head: the softmax of head h runs
+    over the logits of the keys and z_h, and the sink's value is zero, so
+    o_h = sum_s p_s KV_s with p = softmax([q_h . KV_s * scale ..., z_h]) over
+    the keys only, and lse_h = log(sum_s exp(q_h . KV_s * scale) + exp(z_h)).
+    Written out directly from the definition (one extra logit, zero value)."""
+    q, KV, z = f64(q), f64(KV), f64(z)
+    nh, c = q.shape
+    if scale is None or scale <= 0:
+        scale = 1.0 / math.sqrt(c)
+    logits = np.concatenate([(q @ KV.T) * scale, z[:, None]], axis=1)   # [nh][N+1]
+    mx = logits.max(axis=1, keepdims=True)
+    e = np.exp(logits - mx)
+    tot = e.sum(axis=1, keepdims=True)
+    p = e / tot
+    values = np.concatenate([KV, np.zeros((1, c))], axis=0)             # the sink's value is 0
+    return p @ values, (mx + np.log(tot))[:, 0]
+
+
+def apply_sink(o, lse, z):
+    """The sink applied to a finished attention (o, lse) of one head set:
+    o' = o * e^lse / (e^lse + e^z), lse' = log(e^lse + e^z); an empty key set
+    (lse = -inf) gives o' = 0 and lse' = z."""
+    o, lse, z = f64(o), f64(lse), f64(z)
+    m = np.maximum(lse, z)
+    a = np.where(np.isfinite(lse), np.exp(lse - m), 0.0)
+    bz = np.exp(z - m)
+    return o * (a / (a + bz))[..., None], m + np.log(a + bz)
 
 
 def merge_lse(o1, lse1, o2, lse2):
