@@ -6,6 +6,7 @@ include/dlc.h); this package is its Python binding plus the in-tree build.
 
 from .binding import (  # noqa: F401
     DlcError,
+    attend_sink,
     csa_attend,
     csa_attend_window,
     csa_attend_ws,

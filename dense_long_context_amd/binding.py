@@ -55,6 +55,7 @@ SIGNATURES = {
     "hca_attend_window_ws": (_sz, [_i64, _i64, _i64, _i64, _i64, _i64]),
     "hca_attend_window": (_i32, [_i32, _i64, _i64, _i64, _i64, _i64, _vp, _vp, _i64, _vp, _i64, _vp, _i64, _i64,
                                  _f32, _vp, _vp, _vp, _sz, _vp]),
+    "attend_sink": (_i32, [_i64, _i64, _i64, _vp, _vp, _vp, _vp]),
     "dlc_project": (_i32, [_i32, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _i32, _vp]),
     "dlc_timing_arm": (_i32, [_i32, _vp, _vp]),
     "dlc_copy": (_i32, [_vp, _vp, _sz, _vp]),
@@ -382,6 +383,18 @@ def dlc_project(A, Wt, out=None, out_dtype=None):
         _dt(A), M, N, K, _p(A), _stride(A, 0, K), _p(Wt), _stride(Wt, 0, K), _p(out), _stride(out, 0, N), _dt(out),
         _stream(A.device)))
     return out
+
+
+def attend_sink(out, lse, z):
+    """Per-head sink logits z (fp32 [n_h]) applied in place to an attention's
+    fp32 output [..., n_h, c] and log-sum-exp [..., n_h]; returns (out, lse)."""
+    n_h, c = out.shape[-2], out.shape[-1]
+    rows = out.numel() // (n_h * c) if n_h * c else 0
+    _need(out.dtype == torch.float32 and lse.dtype == torch.float32 and z.dtype == torch.float32, "fp32 only")
+    _need(out.is_contiguous() and lse.is_contiguous() and z.is_contiguous(), "contiguous tensors only")
+    _need(lse.numel() == rows * n_h and z.numel() == n_h, "lse / z shape")
+    _check("attend_sink", lib().attend_sink(rows, n_h, c, _p(out), _p(lse), _p(z), _stream(out.device)))
+    return out, lse
 
 
 def dlc_timing_arm(stage, ev_begin, ev_end):

@@ -778,6 +778,32 @@ __global__ void __launch_bounds__(128) combine_kernel(const float* op, const flo
   if (tid == 0 && lse) lse[bh] = M == -INFINITY ? -INFINITY : M + __logf(L);
 }
 
+// ------------------------------------------------------------------ sink logits
+//
+// One logit z_h per head joins a finished attention's softmax as an extra
+// key with a zero value: o' = o * e^lse / (e^lse + e^z), lse' = log(e^lse +
+// e^z).  One block per (row, head); the factor is formed once, then the c
+// dims are scaled in place (float4 when c % 4 == 0).
+__global__ void __launch_bounds__(128) sink_kernel(float* o, float* lse, const float* z, int64_t n_h, int64_t c) {
+  const int64_t rh = blockIdx.x;  // row * n_h + head
+  const float l = lse[rh], zh = z[rh % n_h];
+  const float m = fmaxf(l, zh);
+  const float el = l == -INFINITY ? 0.f : expf(l - m), ez = expf(zh - m);
+  const float f = el / (el + ez);
+  float* op = o + rh * c;
+  if ((c & 3) == 0) {
+    for (int64_t d = threadIdx.x; d < c / 4; d += blockDim.x) {
+      float4 v = reinterpret_cast<float4*>(op)[d];
+      v.x *= f; v.y *= f; v.z *= f; v.w *= f;
+      reinterpret_cast<float4*>(op)[d] = v;
+    }
+  } else {
+    for (int64_t d = threadIdx.x; d < c; d += blockDim.x) op[d] *= f;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) lse[rh] = m + logf(el + ez);
+}
+
 // ------------------------------------------------------------------ host
 
 bool mfma_ok(int dtype, int64_t c) { return dtype == DLC_BF16 && (c == 128 || c == 256 || c == 512); }
@@ -1008,6 +1034,17 @@ int window_attend(int dtype, int64_t B, int64_t n_q, int64_t n_h, int64_t c, int
   const int64_t nkeys = t_max + 1 < n_win ? t_max + 1 : n_win;
   return run_attend<kWindow>("window_attend", dtype, a, B * n_q, nkeys, out, lse, ws, ws_bytes,
                              as_stream(stream), o_in, lse_in);
+}
+
+int attend_sink(int64_t rows, int64_t n_h, int64_t c, float* out, float* lse, const float* z, void* stream) {
+  using namespace dlc;
+  DLC_REQUIRE(rows >= 0 && n_h >= 1 && c >= 1, DLC_E_INVAL, "attend_sink: need rows >= 0, n_h >= 1, c >= 1");
+  if (rows == 0) return DLC_OK;
+  DLC_REQUIRE(out && lse && z, DLC_E_INVAL, "attend_sink: NULL argument");
+  DLC_REQUIRE(aligned(out, 16), DLC_E_INVAL, "attend_sink: out must be 16-byte aligned");
+  DLC_REQUIRE(rows * n_h < (int64_t(1) << 31), DLC_E_UNSUPPORTED, "attend_sink: rows*n_h too large");
+  hipLaunchKernelGGL(sink_kernel, dim3((unsigned)(rows * n_h)), dim3(128), 0, as_stream(stream), out, lse, z, n_h, c);
+  return check_launch("attend_sink");
 }
 
 }  // extern "C"

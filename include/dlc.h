@@ -260,6 +260,21 @@ int hca_attend_window(int dtype, int64_t B, int64_t n_q, int64_t n_h, int64_t c,
                       void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * attend_sink - per-head sink logits ([Scratch] §12 names them without a formula;
+ * the reading: one logit z_h per head joins the attention's softmax as an
+ * extra key whose value is the zero vector).  Applied in place to a finished
+ * attention (the output and log-sum-exp of csa_attend, hca_attend or their
+ * joined forms), which is exact:
+ *   o'[h]   = o[h] * e^lse[h] / (e^lse[h] + e^z[h])
+ *   lse'[h] = log(e^lse[h] + e^z[h])
+ * An empty key set (lse = -inf, o = 0) gives o' = 0 and lse' = z.
+ *  out  [rows][n_h][c] fp32, in place, 16-byte aligned (rows = B*n_q)
+ *  lse  [rows][n_h] fp32, in place
+ *  z    [n_h] fp32 sink logits (natural-log units, like lse)
+ */
+int attend_sink(int64_t rows, int64_t n_h, int64_t c, float* out, float* lse, const float* z, void* stream);
+
+/*
  * dlc_project - dense projection out = A . W with fp32 accumulation, the
  * token projections that feed the compressor and the queries ([Scratch] §3:
  * C^a = H W^{aKV} and its siblings; §6.1-6.3 and §8: c^Q, q^I, w^I, q).

@@ -141,6 +141,18 @@ def test_mxfp4_quantize_validation(L, args, status):
     assert L.mxfp4_quantize(*args, None) == status
 
 
+@pytest.mark.parametrize("args,status", [
+    ((1, 0, 8, P, P, P), E_INVAL),          # n_h = 0
+    ((1, 4, 0, P, P, P), E_INVAL),          # c = 0
+    ((1, 4, 8, None, P, P), E_INVAL),
+    ((1, 4, 8, P, P, None), E_INVAL),
+    ((1, 4, 8, P + 4, P, P), E_INVAL),      # misaligned output
+    ((0, 4, 8, None, None, None), OK),      # no rows: nothing to do
+])
+def test_attend_sink_validation(L, args, status):
+    assert L.attend_sink(*args, None) == status
+
+
 def test_fp4_workspace_query(L):
     base = L.csa_index_topk_ws(4, 1, 262144, 1024)
     w = L.csa_index_topk_fp4_ws(4, 1, 64, 128, 262144, 1024)
