@@ -40,6 +40,12 @@ constexpr float kLn2 = 0.6931471805599453f;
 #define DLC_ATTEND_MIN_KEYS 64
 #endif
 constexpr int kMinKeysPerSplit = DLC_ATTEND_MIN_KEYS;
+// split-K partial outputs of the c = 512 MFMA path in bf16 (halves their
+// write and the combine's read; the final output and lse stay fp32)
+#ifndef DLC_BF16_PARTIALS
+#define DLC_BF16_PARTIALS 1
+#endif
+constexpr bool kBf16Partials = DLC_BF16_PARTIALS != 0;
 constexpr int kTargetWorkgroups = DLC_ATTEND_TARGET_WGS;
 
 // which keys a query attends to
@@ -63,6 +69,7 @@ struct AttArgs {
   int64_t splits, keys_per_split, head_groups;
   float scale_log2;
   float* o;             // [BQ][splits][n_h][c] (splits == 1: the final output)
+  bf16_raw* ob;         // c = 512 MFMA path with partials: [BQ][splits][n_h][c] bf16 (o unused)
   float* lse;           // [BQ][splits][n_h] (may be nullptr when splits == 1)
 };
 
@@ -689,23 +696,48 @@ __global__ void __launch_bounds__(512) attend512_kernel(AttArgs a) {
   }
   if (ntile > 0 && active) pv_only(tile_ptr(ntile - 1));
 
-  if (!active) return;
   // normalise and write: o[nt][e] is head 4*g + e, dim 16*nt + i16
   const int64_t slot0 = (bq * a.splits + split) * a.n_h;
+  float inv[4];
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
-    const int hr = 4 * g + e;
-    const float l = __shfl(lrun, hr);
-    const float inv = l > 0.f ? 1.f / l : 0.f;
-    const int64_t h = hbase + hr;
+    const float l = __shfl(lrun, 4 * g + e);
+    inv[e] = l > 0.f ? 1.f / l : 0.f;
+  }
+  if (active && g == 0 && a.lse && hbase + r16 < a.n_h)
+    a.lse[slot0 + hbase + r16] = lrun > 0.f ? (mrun + log2f(lrun)) * kLn2 : -INFINITY;
+  if (a.ob != nullptr) {
+    // bf16 partials: each wave stages its 16 rows in LDS (rows 1040 bytes
+    // apart, so the 2-byte writes of the four row groups hit different
+    // banks), then writes every row as one 1 KB store of 16 bytes per lane
+    constexpr int RS = 1040;
+    __syncthreads();  // every wave is done with the tile ring
+    if (!active) return;
+    unsigned char* stage = sK + wave * 16 * RS;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        const __bf16 v = (__bf16)(o[nt][e] * inv[e]);
+        *reinterpret_cast<__bf16*>(stage + (4 * g + e) * RS + 2 * (16 * nt + i16)) = v;
+      }
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // the wave's own LDS writes (lgkmcnt(0))
+    for (int r = 0; r < 16 && hbase + r < a.n_h; ++r) {
+      const uint4 v = *reinterpret_cast<const uint4*>(stage + r * RS + 16 * lane);
+      *reinterpret_cast<uint4*>(a.ob + (slot0 + hbase + r) * CD + 8 * lane) = v;
+    }
+    return;
+  }
+  if (!active) return;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int64_t h = hbase + 4 * g + e;
     if (h < a.n_h) {
       float* op = a.o + (slot0 + h) * CD + i16;
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) op[16 * nt] = o[nt][e] * inv;
+      for (int nt = 0; nt < NT; ++nt) op[16 * nt] = o[nt][e] * inv[e];
     }
   }
-  if (g == 0 && a.lse && hbase + r16 < a.n_h)
-    a.lse[slot0 + hbase + r16] = lrun > 0.f ? (mrun + log2f(lrun)) * kLn2 : -INFINITY;
 }
 
 // ------------------------------------------------------------------ combine
@@ -719,7 +751,18 @@ __global__ void __launch_bounds__(512) attend512_kernel(AttArgs a) {
 // written by the same thread, and lse_in is read before lse is written.
 constexpr int kMaxSplits = 256;
 
-__global__ void __launch_bounds__(128) combine_kernel(const float* op, const float* lp, int64_t splits,
+// 4 consecutive partial values at p as floats
+__device__ __forceinline__ float4 load_part4(const float* p) { return *reinterpret_cast<const float4*>(p); }
+__device__ __forceinline__ float4 load_part4(const bf16_raw* p) {
+  const uint2 u = *reinterpret_cast<const uint2*>(p);
+  return make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u), __uint_as_float(u.y << 16),
+                     __uint_as_float(u.y & 0xffff0000u));
+}
+__device__ __forceinline__ float load_part1(const float* p) { return *p; }
+__device__ __forceinline__ float load_part1(const bf16_raw* p) { return __uint_as_float(uint32_t(*p) << 16); }
+
+template <typename PT>
+__global__ void __launch_bounds__(128) combine_kernel(const PT* op, const float* lp, int64_t splits,
                                                       int64_t n_h, int64_t c, float* out, float* lse,
                                                       const float* o_in, const float* lse_in) {
   __shared__ float wsh[kMaxSplits + 1];
@@ -746,7 +789,7 @@ __global__ void __launch_bounds__(128) combine_kernel(const float* op, const flo
   const float M = red[0], L = red[1];
   for (int j = tid; j < parts; j += blockDim.x) wsh[j] = (M == -INFINITY) ? 0.f : __expf(wsh[j] - M) / L;
   __syncthreads();
-  const float* base = op + (bq * splits * n_h + h) * c;
+  const PT* base = op + (bq * splits * n_h + h) * c;
   const int64_t sstride = n_h * c;
   const float w_in = o_in ? wsh[splits] : 0.f;
   if ((c & 3) == 0) {
@@ -755,7 +798,7 @@ __global__ void __launch_bounds__(128) combine_kernel(const float* op, const flo
 #pragma unroll 8
       for (int64_t j = 0; j < splits; ++j) {
         const float wj = wsh[j];
-        const float4 v = *reinterpret_cast<const float4*>(base + j * sstride + d);
+        const float4 v = load_part4(base + j * sstride + d);
         acc.x = fmaf(wj, v.x, acc.x); acc.y = fmaf(wj, v.y, acc.y);
         acc.z = fmaf(wj, v.z, acc.z); acc.w = fmaf(wj, v.w, acc.w);
       }
@@ -770,7 +813,7 @@ __global__ void __launch_bounds__(128) combine_kernel(const float* op, const flo
     for (int64_t d = tid; d < c; d += blockDim.x) {
       float acc = 0.f;
 #pragma unroll 8
-      for (int64_t j = 0; j < splits; ++j) acc = fmaf(wsh[j], base[j * sstride + d], acc);
+      for (int64_t j = 0; j < splits; ++j) acc = fmaf(wsh[j], load_part1(base + j * sstride + d), acc);
       if (o_in) acc = fmaf(w_in, o_in[bh * c + d], acc);
       out[bh * c + d] = acc;
     }
@@ -809,7 +852,7 @@ __global__ void __launch_bounds__(128) sink_kernel(float* o, float* lse, const f
 bool mfma_ok(int dtype, int64_t c) { return dtype == DLC_BF16 && (c == 128 || c == 256 || c == 512); }
 
 struct Plan {
-  bool mfma;
+  bool mfma, bf16_parts;  // bf16_parts: the partial outputs are stored in bf16
   int64_t splits, kps, head_groups;
   size_t o_off, l_off, total;
 };
@@ -830,8 +873,9 @@ Plan plan(int dtype, int64_t BQ, int64_t n_h, int64_t c, int64_t nkeys, bool mer
   if (p.mfma) p.kps = ceil_div(p.kps, 32) * 32;
   p.o_off = 0;
   size_t off = 0;
+  p.bf16_parts = p.mfma && c == 512 && kBf16Partials;
   if (s > 1 || merge) {  // partials, combined afterwards
-    off = align_up(size_t(BQ) * s * n_h * c * 4, 256);
+    off = align_up(size_t(BQ) * s * n_h * c * (p.bf16_parts ? 2 : 4), 256);
     p.l_off = off;
     off = align_up(off + size_t(BQ) * s * n_h * 4, 256);
   } else {
@@ -859,8 +903,10 @@ int run_attend(const char* name, int dtype, AttArgs a, int64_t BQ, int64_t nkeys
   a.keys_per_split = p.kps;
   a.head_groups = p.head_groups;
   const bool partials = p.splits > 1 || merge;
+  a.ob = nullptr;
   if (partials) {
     a.o = reinterpret_cast<float*>(static_cast<char*>(ws) + p.o_off);
+    if (p.bf16_parts) a.ob = reinterpret_cast<bf16_raw*>(static_cast<char*>(ws) + p.o_off);
     a.lse = reinterpret_cast<float*>(static_cast<char*>(ws) + p.l_off);
   } else {
     a.o = out;
@@ -885,8 +931,12 @@ int run_attend(const char* name, int dtype, AttArgs a, int64_t BQ, int64_t nkeys
   }
   int rc = check_launch(name);
   if (rc || !partials) return rc;
-  hipLaunchKernelGGL(combine_kernel, dim3((unsigned)(BQ * a.n_h)), dim3(128), 0, s, a.o, a.lse, p.splits, a.n_h,
-                     a.c, out, lse, o_in, lse_in);
+  if (p.bf16_parts)
+    hipLaunchKernelGGL(combine_kernel<bf16_raw>, dim3((unsigned)(BQ * a.n_h)), dim3(128), 0, s, a.ob, a.lse,
+                       p.splits, a.n_h, a.c, out, lse, o_in, lse_in);
+  else
+    hipLaunchKernelGGL(combine_kernel<float>, dim3((unsigned)(BQ * a.n_h)), dim3(128), 0, s, a.o, a.lse, p.splits,
+                       a.n_h, a.c, out, lse, o_in, lse_in);
   return check_launch(name);
 }
 
