@@ -9,19 +9,20 @@
 // partial output plus its log-sum-exp; a combine kernel merges the splits
 // exactly (o = sum_j e^{lse_j - lse} o_j, lse = log sum_j e^{lse_j}).
 //
-// MFMA path (bf16, c in {128, 256, 512}): a workgroup is 8 waves and covers
-// 128 heads.  All heads share each key row, so a 32-key tile is staged once in
-// LDS, row-major for Q.K^T and transposed for P.V.  Wave w owns heads
-// 32*(w/2) .. +31 and half w%2 of the c dimensions, and multiplies with
-// v_mfma_f32_32x32x16_bf16:
-//   S^T[32 keys][32 heads] = K[32 keys][half] . Q^T[half][32 heads]  (Q in registers)
-//   (the two halves' partial S^T are swapped through LDS and added)
-//   O[32 heads][half]     += P[32 heads][32 keys] . V[32 keys][half]
-// Splitting c between two waves keeps Q (64 VGPRs) and O (128 AGPRs) of a
-// wave in registers at two waves per SIMD.  The S^T accumulator already holds,
-// per lane, the 16 keys of one head that the P operand needs, so P never goes
-// through memory.  Tiles are double-buffered: the next tile's global loads are
-// in flight while the current one is used.
+// MFMA paths (bf16).  A workgroup is 8 waves and covers 128 heads; all heads
+// share each key row, so a 32-key tile is staged once in LDS, row-major for
+// Q.K^T and read transposed for P.V.
+//  * c in {128, 256} (attend_mfma_kernel): wave w owns heads 32*(w/2) .. +31
+//    and half w%2 of the c dimensions, with v_mfma_f32_32x32x16_bf16:
+//      S^T[32 keys][32 heads] = K[32 keys][half] . Q^T[half][32 heads]
+//      (the two halves' partial S^T are swapped through LDS and added)
+//      O[32 heads][half]     += P[32 heads][32 keys] . V[32 keys][half]
+//    The S^T accumulator already holds, per lane, the 16 keys of one head
+//    that the P operand needs, so P never goes through memory.  Tiles are
+//    double-buffered.
+//  * c = 512 (attend512_kernel): 16 heads per wave over all 512 dims, a
+//    four-buffer tile ring with P.V of one tile interleaved with Q.K^T of the
+//    next, and bf16 split-K partials (described at the kernel).
 // The VALU path covers fp32 and other shapes.
 #include "common.hpp"
 
@@ -414,16 +415,6 @@ __global__ void __launch_bounds__(512) attend_mfma_kernel(AttArgs a) {
 // ------------------------------------------------------------------ shared by the c = 512 kernel
 
 __device__ __align__(16) bf16_raw g_zero_row[512];  // masked keys load this row
-
-__device__ __forceinline__ void wait_vmcnt(int n) {
-  // s_waitcnt with only the vector-memory counter set
-  if (n == 4)
-    __builtin_amdgcn_s_waitcnt(0x0F74);
-  else
-    __builtin_amdgcn_s_waitcnt(0x0F70);
-}
-
-
 
 constexpr int kTileBytes = 34816;   // 32 rows of 1 KB at the offsets of h16_row_off, rounded up to 1 KB
 constexpr int kMaxGatherKeys = 2048;  // keys per split whose rows sit in LDS

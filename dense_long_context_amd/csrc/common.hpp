@@ -36,7 +36,6 @@ inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 typedef uint16_t bf16_raw;
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
