@@ -126,6 +126,10 @@ int hca_compress(int dtype, int64_t B, int64_t n, int64_t c, int64_t m_prime,
  *          256-byte aligned; its contents on entry do not matter
  * Limits: 1 <= k <= 8192; bf16 with c^I in {32, 64, 128, 256} and n_hI <= 64
  * (the MFMA shapes), otherwise n_hI*cI <= 8192.
+ * Many queries per sequence (a prefill chunk: bf16, c^I = 128, n_q >= 64)
+ * run query-tiled, each key row then serving 64 queries; the results are
+ * the same.  The workspace grows with B*n_q*cap (six 4-byte arrays per query
+ * and entry), so prefill callers pass their queries in chunks.
  */
 size_t csa_index_topk_ws(int64_t B, int64_t n_q, int64_t cap, int64_t k);
 int csa_index_topk(int dtype, int64_t B, int64_t n_q, int64_t n_hI, int64_t cI, int64_t m, int64_t k,
