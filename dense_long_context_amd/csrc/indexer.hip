@@ -589,6 +589,167 @@ __global__ void __launch_bounds__(512) scores_prefill_kernel(IdxArgs a) {
   }
 }
 
+// The same query tiling with MXFP4 operands (csa_index_topk_fp4 at many
+// queries): S_h[32 q][32 keys] on v_mfma_scale_f32_32x32x64_f8f6f4, lane l
+// supplying row/column l%32 and the 32-dim block l/32 of a 64-dim step (16
+// code bytes and its E8M0 scale byte).  The wave's key operands (64 keys x
+// c^I: codes and scales) stay in registers; HPS heads' query codes (64 rows
+// of c^I/2 bytes, chunk c at slot c ^ ((row/4) % 4)) and scales arrive per
+// stage by direct global->LDS loads, double-buffered.
+
+template <int CI>
+__global__ void __launch_bounds__(512) scores_prefill_fp4_kernel(IdxArgs a) {
+  constexpr int KB = CI / 32;           // scale bytes (32-dim blocks) per row
+  constexpr int ROWB = CI / 2;          // code bytes per row
+  constexpr int CPR = ROWB / 16;        // 16-byte chunks per code row
+  constexpr int NJ = CI / 64;           // 64-dim MFMA steps
+  constexpr int TQ = 64, TK = 256, NW = 8, NB = 2, HPS = 8;
+  constexpr int QCODEB = TQ * ROWB;     // one head's query codes (4 KB at c^I = 128)
+  constexpr int QSCB = TQ * KB;         // its scales (256 B)
+  constexpr int HEADB = QCODEB + QSCB;
+  constexpr int CODE_LOADS = QCODEB / 1024;  // 1 KB loads per head
+  static_assert(CI == 128 && CPR == 4 && KB == 4, "tile geometry for c^I = 128");
+  static_assert(HPS * (CODE_LOADS + 1) == 5 * NW, "one stage is five loads per wave");
+  __shared__ __attribute__((aligned(1024))) unsigned char sQ[NB][HPS][HEADB];
+  __shared__ float sW[64 + HPS][TQ];
+  __shared__ int64_t sVis[TQ];
+  __shared__ int64_t sMax;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int r32 = lane & 31, hi = lane >> 5;
+  const int64_t b = blockIdx.z;
+  const int64_t q0 = int64_t(blockIdx.y) * TQ;
+  const int64_t k0 = int64_t(blockIdx.x) * TK;
+  const int nq = int(min(int64_t(TQ), a.n_q - q0));
+  const int n_hI = int(a.n_hI);
+  const int ngroups = (n_hI + HPS - 1) / HPS;
+  if (tid == 0) sMax = 0;
+  __syncthreads();
+  if (tid < TQ) {
+    const int64_t v = tid < nq ? visible(a, b * a.n_q + q0 + tid) : 0;
+    sVis[tid] = v;
+    atomicMax(reinterpret_cast<unsigned long long*>(&sMax), (unsigned long long)v);
+  }
+  for (int i = tid; i < TQ * (64 + HPS); i += NW * 64) {
+    const int h = i / TQ, q = i % TQ;
+    sW[h][q] = (q < nq && h < n_hI) ? a.wI[(b * a.n_q + q0 + q) * n_hI + h] : 0.f;
+  }
+  __syncthreads();
+  if (k0 >= sMax) return;
+
+  // stage p holds heads HPS*p .. +HPS-1 (a head past n_hI repeats the last
+  // head, at zero weight); load u of wave w: head (5w+u)/5 ... laid out as
+  // HPS*(CODE_LOADS+1) loads spread over the waves, each either 1 KB of codes
+  // (16 query rows) or the head's 64 scale dwords
+  const uint8_t* qc = a.q_code + (b * a.n_q + q0) * n_hI * ROWB;
+  const uint8_t* qs = a.q_scale + (b * a.n_q + q0) * n_hI * KB;
+  const uint32_t lds0 = (uint32_t)(uintptr_t)DLC_LDS(&sQ[0][0][0]);
+  auto issue = [&](int p) {
+#pragma unroll
+    for (int u = 0; u < 5; ++u) {
+      const int ld = wave * 5 + u;                       // 0 .. HPS*(CODE_LOADS+1)-1
+      const int hh = ld / (CODE_LOADS + 1), part = ld % (CODE_LOADS + 1);
+      const int h = min(HPS * p + hh, n_hI - 1);
+      const uint32_t dst = lds0 + uint32_t(((p % NB) * HPS + hh) * HEADB);
+      if (part < CODE_LOADS) {
+        const int row = part * 16 + lane / CPR;
+        const int chunk = (lane % CPR) ^ ((row >> 2) & 3);
+        const int qr = min(row, nq - 1);
+        dma_row(qc + h * ROWB, uint32_t(qr * n_hI * ROWB + chunk * 16), dst + uint32_t(part * 1024));
+      } else {
+        const int qr = min(lane, nq - 1);
+        dma_dword(qs + h * KB, uint32_t(qr * n_hI * KB), dst + uint32_t(QCODEB));
+      }
+    }
+  };
+  const int npre = min(NB - 1, ngroups);
+  for (int p = 0; p < npre; ++p) issue(p);
+
+  // K^T operands: key k0 + 64*(wave%4) + 32*j + r32, block 2*ks + hi
+  const uint8_t* Kc = static_cast<const uint8_t*>(a.KI) + b * a.cap * ROWB;
+  const uint8_t* Ks = a.k_scale + b * a.cap * KB;
+  i32x8 kf[2][NJ];
+  int ksc[2][NJ];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int64_t key = min(k0 + 64 * (wave & 3) + 32 * j + r32, a.cap - 1);
+#pragma unroll
+    for (int ks = 0; ks < NJ; ++ks) {
+      const uint4 c = *reinterpret_cast<const uint4*>(Kc + key * ROWB + (2 * ks + hi) * 16);
+      kf[j][ks] = i32x8{int(c.x), int(c.y), int(c.z), int(c.w), 0, 0, 0, 0};
+      ksc[j][ks] = Ks[key * KB + 2 * ks + hi];
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int ks = 0; ks < NJ; ++ks)
+      asm volatile("" ::"v"(kf[j][ks][0]), "v"(kf[j][ks][1]), "v"(kf[j][ks][2]), "v"(kf[j][ks][3]),
+                   "v"(ksc[j][ks]));
+
+  f32x16 sc[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sc[j][r] = 0.f;
+  const int qw = 32 * (wave >> 2);
+  const int qrow = qw + r32;
+
+  auto head_mfma = [&](const unsigned char* hb, f32x16 (&S)[2]) {
+#pragma unroll
+    for (int ks = 0; ks < NJ; ++ks) {
+      const int slot = (2 * ks + hi) ^ ((qrow >> 2) & 3);
+      const uint4 c = *reinterpret_cast<const uint4*>(hb + qrow * ROWB + slot * 16);
+      const int qsc = hb[QCODEB + qrow * KB + 2 * ks + hi];
+      const i32x8 qa = i32x8{int(c.x), int(c.y), int(c.z), int(c.w), 0, 0, 0, 0};
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        S[j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(qa, kf[j][ks], ks == 0 ? f32x16{} : S[j], 4, 4, 0,
+                                                                qsc, 0, ksc[j][ks]);
+    }
+  };
+  auto head_epilogue = [&](int h, const f32x16 (&S)[2]) {
+    const float* wrow = &sW[h][qw + 4 * hi];
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+      const float4 w = *reinterpret_cast<const float4*>(wrow + 8 * r4);
+      const float wv[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) sc[j][4 * r4 + e] = fmaf(wv[e], fmaxf(S[j][4 * r4 + e], 0.f), sc[j][4 * r4 + e]);
+    }
+  };
+  f32x16 Sa[2], Sb[2];
+  for (int p = 0; p < ngroups; ++p) {
+    if (p + 1 < ngroups) wait_vm<5>(); else wait_vm<0>();
+    lds_barrier();
+    if (p + NB - 1 < ngroups) issue(p + NB - 1);
+#pragma unroll 1
+    for (int u = 0; u < HPS; u += 2) {
+      const int h = HPS * p + u;
+      head_mfma(&sQ[p % NB][u][0], Sa);
+      if (h > 0) head_epilogue(h - 1, Sb);
+      head_mfma(&sQ[p % NB][u + 1][0], Sb);
+      head_epilogue(h, Sa);
+    }
+  }
+  if (ngroups > 0) head_epilogue(HPS * ngroups - 1, Sb);
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int qr = qw + 8 * (r >> 2) + 4 * hi + (r & 3);
+    if (qr >= nq) continue;
+    const int64_t nv = sVis[qr];
+    float* out = a.scores + (b * a.n_q + q0 + qr) * a.score_ld;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int64_t key = k0 + 64 * (wave & 3) + 32 * j + r32;
+      if (key < nv) out[key] = canon_zero(sc[j][r]);
+    }
+  }
+}
+
 // first-digit histogram of the scores, chunk by chunk (the prefill path; the
 // other scores kernels build it as they go)
 __global__ void __launch_bounds__(256) hist_kernel(IdxArgs a) {
@@ -1226,11 +1387,20 @@ int csa_index_topk_fp4(int dtype, int64_t B, int64_t n_q, int64_t n_hI, int64_t 
     a.keys_per_wg = keys_per_wg(BQ, vis_max);
     dim3 grid{(unsigned)ceil_div(vis_max, a.keys_per_wg), (unsigned)BQ, 1u};
     StageTimer timer(DLC_STAGE_INDEX_SCORES, s);
-    if (cI == 128)
+    const bool prefill = cI == 128 && n_q >= kPrefillMinQueries;
+    if (prefill) {
+      dim3 pgrid{(unsigned)ceil_div(vis_max, 256), (unsigned)ceil_div(n_q, 64), (unsigned)B};
+      hipLaunchKernelGGL((scores_prefill_fp4_kernel<128>), pgrid, dim3(512), 0, s, a);
+    }
+    if (!prefill && cI == 128)
       hipLaunchKernelGGL((scores_fp4_kernel<128, DLC_FP4_NS, DLC_FP4_NW>), grid, dim3(64 * DLC_FP4_NW), 0, s, a);
-    if (cI == 256)
+    if (!prefill && cI == 256)
       hipLaunchKernelGGL((scores_fp4_kernel<256, DLC_FP4_NS, DLC_FP4_NW>), grid, dim3(64 * DLC_FP4_NW), 0, s, a);
     if ((rc = check_launch("csa_index_topk_fp4/scores"))) return rc;
+    if (prefill) {
+      hipLaunchKernelGGL(hist_kernel, grid, dim3(256), 0, s, a);
+      if ((rc = check_launch("csa_index_topk_fp4/hist"))) return rc;
+    }
   }
   return select_topk(a, BQ, vis_max, s);
 }

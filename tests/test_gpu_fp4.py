@@ -115,6 +115,40 @@ def test_index_topk_fp4(dtype, B, n_q, n_hI, cI, m, k, cap, ts):
             check_topk(idx[b, j], cnt[b, j], ref, k, abs_slack=float(slack.max()) if nv else 0.0)
 
 
+@pytest.mark.parametrize("B,n_q,n_hI,m,k,cap,seed", [
+    (2, 100, 64, 4, 100, 3000, 1),      # two query tiles (64 + 36), mixed visibilities
+    (1, 64, 20, 2, 50, 700, 2),         # 20 heads: a head group padded at zero weight
+])
+def test_index_topk_fp4_prefill(B, n_q, n_hI, m, k, cap, seed):
+    """Many queries per sequence: the query-tiled FP4 kernel (32x32x64 MXFP4
+    MFMA) against the oracle's FP4 scores, every query."""
+    cI = 128
+    qI = synth.normal((B, n_q, n_hI, cI), 950 + seed, dtype="bf16")
+    wI = synth.normal((B, n_q, n_hI), 951 + seed, dtype="f32")
+    KI = synth.normal((B, cap, cI), 952 + seed, dtype="bf16")
+    KIc, KIs = dlc.mxfp4_quantize(KI.to(DEV))
+    rng = np.random.default_rng(seed)
+    t = torch.from_numpy(rng.integers(0, m * cap + 1, size=(B, n_q))).to(torch.int64)
+    t[0, 0], t[0, 1] = 0, m * cap
+    t_max = int(t.max())
+    scores = torch.full((B, n_q, cap), float("nan"), dtype=torch.float32, device=DEV)
+    idx, cnt = dlc.csa_index_topk_fp4(qI.to(DEV), wI.to(DEV), KIc, KIs, t.to(DEV), t_max, m, k, scores=scores)
+    torch.cuda.synchronize()
+    idx, cnt, sc = idx.cpu().numpy(), cnt.cpu().numpy(), scores.cpu().numpy()
+    Kd = [O.mxfp4_dequantize(*O.mxfp4_quantize(KI[b])) for b in range(B)]
+    for b in range(B):
+        for j in range(n_q):
+            tt = int(t[b, j])
+            nv = tt // m
+            qd = O.mxfp4_dequantize(*O.mxfp4_quantize(qI[b, j]))
+            ref = O.index_scores(qd, wI[b, j], Kd[b], tt, m)
+            slack = (2e-6 * (np.abs(Kd[b][:nv]) @ np.abs(qd).T @ np.abs(f64(wI[b, j]))) * (cI + n_hI) ** 0.5
+                     + 1e-30) if nv else np.zeros(0)
+            assert np.all(np.abs(sc[b, j, :nv] - ref) <= slack), f"scores b={b} q={j}"
+            assert np.isnan(sc[b, j, nv:]).all(), f"entries past the visible range written b={b} q={j}"
+            check_topk(idx[b, j], cnt[b, j], ref, k, abs_slack=float(slack.max()) if nv else 0.0)
+
+
 def test_index_topk_fp4_ties_pick_smallest_indices():
     # zero keys: every score is 0, so the k smallest indices win, in order
     B, cap, k = 1, 3000, 100
