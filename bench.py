@@ -272,7 +272,7 @@ def make_steps(cfg, wl, dev, n_dec, window=False, fp4=False):
     return steps, keep
 
 
-def prefill_pass(cfg, wl, dev, n_pref=4096, chunk=256, ev=None):
+def prefill_pass(cfg, wl, dev, n_pref=4096, chunk=256, ev=None, fp4=False):
     """The chunked causal prefill of config 5: queries at t = 2^20-n_pref .. 2^20-1
     of every sequence, `chunk` per sequence per call, through csa_index_topk (which
     runs query-tiled at this many queries), csa_attend and hca_attend.  Returns the
@@ -284,7 +284,7 @@ def prefill_pass(cfg, wl, dev, n_pref=4096, chunk=256, ev=None):
 
     B, d, c, cI, m, mp, k, n_h, n_hI = cfg.B, cfg.d, cfg.c, cfg.cI, cfg.m, cfg.m_prime, cfg.k, cfg.n_h, cfg.n_hI
     n_ctx, n_tot = wl["n_ctx"], wl["n_tot"]
-    Cc, KI, Ch = wl["sets"][0][:3]
+    Cc, KI, Ch, KIc, KIs = wl["sets"][0]
     Wq = {nm: query_weight(cfg, nm).t().contiguous().to(dev) for nm in ("DQ", "w", "IUQ", "UQ", "UQ_hca")}
     chunks = []
     for c0 in range(0, n_pref, chunk):
@@ -299,7 +299,9 @@ def prefill_pass(cfg, wl, dev, n_pref=4096, chunk=256, ev=None):
             t=torch.arange(n_ctx - n_pref + c0, n_ctx - n_pref + c0 + chunk, device=dev,
                            dtype=torch.int64)[None].expand(B, chunk).contiguous()))
         del h, cQ
-    ws_i = torch.empty(dlc.csa_index_topk_ws(B, chunk, wl["cap_csa"], k), dtype=torch.uint8, device=dev)
+    ws_i = torch.empty(max(dlc.csa_index_topk_ws(B, chunk, wl["cap_csa"], k),
+                           dlc.csa_index_topk_fp4_ws(B, chunk, n_hI, cI, wl["cap_csa"], k)), dtype=torch.uint8,
+                       device=dev)
     ws_c = torch.empty(max(1, dlc.csa_attend_ws(B, chunk, n_h, c, k)), dtype=torch.uint8, device=dev)
     ws_h = torch.empty(max(1, dlc.hca_attend_ws(B, chunk, n_h, c, wl["cap_hca"])), dtype=torch.uint8, device=dev)
     idx = torch.empty((B, chunk, k), dtype=torch.int32, device=dev)
@@ -312,7 +314,10 @@ def prefill_pass(cfg, wl, dev, n_pref=4096, chunk=256, ev=None):
         t_max = int(q["t"].max())
         if evs is not None:
             binding.dlc_timing_arm(binding.STAGE_INDEX_SCORES, evs[0], evs[1])
-        dlc.csa_index_topk(q["qI"], q["wI"], KI, q["t"], t_max, m, k, idx=idx, count=cnt, ws=ws_i)
+        if fp4:
+            dlc.csa_index_topk_fp4(q["qI"], q["wI"], KIc, KIs, q["t"], t_max, m, k, idx=idx, count=cnt, ws=ws_i)
+        else:
+            dlc.csa_index_topk(q["qI"], q["wI"], KI, q["t"], t_max, m, k, idx=idx, count=cnt, ws=ws_i)
         if evs is not None:
             binding.dlc_timing_arm(binding.STAGE_CSA_ATTEND, evs[2], evs[3])
         dlc.csa_attend(q["q"], Cc, idx, cnt, out=o1, lse=l1, ws=ws_c)
@@ -674,6 +679,14 @@ def main():
             "hca_attend_tflops": round(pf["hca_flop"] / (pf["hca_ms"] * 1e-3) / 1e12, 1),
             "note": "t = 2^20-4096 .. 2^20-1, causal against the full caches; the indexer runs query-tiled "
                     "(scores_prefill_kernel, v_mfma_f32_32x32x16_bf16) at 256 queries per sequence per call"}
+        pf4 = prefill_pass(cfg, wl, dev, ev=ev, fp4=True)
+        result["prefill"]["with_fp4_indexer"] = {
+            "ms": round(pf4["total_ms"], 3),
+            "query_tokens_per_s": round(cfg.B * pf4["n_pref"] / (pf4["total_ms"] * 1e-3), 1),
+            "indexer_scores_ms": round(pf4["scores_ms"], 3),
+            "indexer_scores_tflops": round(pf4["idx_flop"] / (pf4["scores_ms"] * 1e-3) / 1e12, 1),
+            "note": "csa_index_topk_fp4 (scores_prefill_fp4_kernel, v_mfma_scale_f32_32x32x64_f8f6f4) on the "
+                    "MXFP4 key cache"}
     if not args.no_cpu_baseline:
         log("timing the oracle on a bounded sample")
         result["cpu_baseline"] = cpu_baseline(cfg)
