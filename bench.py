@@ -505,6 +505,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=16)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true", help="skip the chunked-prefill measurement")
+    ap.add_argument("--prefill-only", action="store_true",
+                    help="build the caches, run only the chunked prefill (bf16 and FP4 indexer) and print its JSON")
     ap.add_argument("--repeat", type=int, default=1, help="time the K steps this many times, report the best")
     ap.add_argument("--pmc-probe", action="store_true",
                     help="run only the indexer on the decode shapes plus a copy kernel of known size "
@@ -536,8 +538,17 @@ def main():
     log("building the 2^20-token caches (projection + compressors)")
     wl = build_workload(cfg, dev, n_dec)
     log(f"set-up: projection {wl['t_proj']:.2f} s, compressors {wl['t_comp']*1e3:.1f} ms per cache set")
-    steps, keep = make_steps(cfg, wl, dev, n_dec)
     ev = HipEvents()
+    if args.prefill_only:
+        out = {}
+        for name, fp4 in (("bf16_indexer", False), ("fp4_indexer", True)):
+            pf = prefill_pass(cfg, wl, dev, ev=ev, fp4=fp4)
+            out[name] = {"ms": round(pf["total_ms"], 3), "indexer_scores_ms": round(pf["scores_ms"], 3),
+                         "csa_attend_ms": round(pf["csa_ms"], 3), "hca_attend_ms": round(pf["hca_ms"], 3),
+                         "queries": cfg.B * pf["n_pref"]}
+        print(json.dumps({"prefill": out}), flush=True)
+        return
+    steps, keep = make_steps(cfg, wl, dev, n_dec)
 
     run_steps(steps, 0, args.warmup, n_dec)
     torch.cuda.synchronize()

@@ -848,7 +848,8 @@ struct Plan {
   size_t o_off, l_off, total;
 };
 
-Plan plan(int dtype, int64_t BQ, int64_t n_h, int64_t c, int64_t nkeys, bool merge = false) {
+// gather: the keys of a split are listed in LDS (kGather), which bounds a split's length
+Plan plan(int dtype, int64_t BQ, int64_t n_h, int64_t c, int64_t nkeys, bool merge = false, bool gather = true) {
   Plan p{};
   p.mfma = mfma_ok(dtype, c);
   p.head_groups = p.mfma ? ceil_div(n_h, 128) : n_h;
@@ -856,8 +857,10 @@ Plan plan(int dtype, int64_t BQ, int64_t n_h, int64_t c, int64_t nkeys, bool mer
   int64_t s = ceil_div(kTargetWorkgroups, per_split);
   const int64_t smax = ceil_div(nkeys > 0 ? nkeys : 1, kMinKeysPerSplit);
   s = s < smax ? s : smax;
-  const int64_t smin = ceil_div(nkeys > 0 ? nkeys : 1, c == 512 ? kMaxGatherKeys : 4096);  // a split's rows fit in LDS
-  s = s < smin ? smin : s;
+  if (gather) {  // a split's row list fits in LDS
+    const int64_t smin = ceil_div(nkeys > 0 ? nkeys : 1, c == 512 ? kMaxGatherKeys : 4096);
+    s = s < smin ? smin : s;
+  }
   s = s < 1 ? 1 : (s > kMaxSplits ? kMaxSplits : s);
   p.splits = s;
   p.kps = ceil_div(nkeys > 0 ? nkeys : 1, s);
@@ -886,7 +889,7 @@ int run_attend(const char* name, int dtype, AttArgs a, int64_t BQ, int64_t nkeys
                void* ws, size_t ws_bytes, hipStream_t s, const float* o_in = nullptr,
                const float* lse_in = nullptr) {
   const bool merge = o_in != nullptr;
-  const Plan p = plan(dtype, BQ, a.n_h, a.c, nkeys, merge);
+  const Plan p = plan(dtype, BQ, a.n_h, a.c, nkeys, merge, MODE == kGather);
   DLC_REQUIRE(p.total == 0 || (ws != nullptr && ws_bytes >= p.total), DLC_E_WORKSPACE,
               "%s: workspace of %zu bytes needed, %zu given", name, p.total, ws_bytes);
   DLC_REQUIRE(ws == nullptr || aligned(ws, 256), DLC_E_WORKSPACE, "%s: workspace must be 256-byte aligned", name);
