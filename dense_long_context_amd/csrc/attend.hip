@@ -698,24 +698,23 @@ __global__ void __launch_bounds__(512) attend512_kernel(AttArgs a) {
   if (active && g == 0 && a.lse && hbase + r16 < a.n_h)
     a.lse[slot0 + hbase + r16] = lrun > 0.f ? (mrun + log2f(lrun)) * kLn2 : -INFINITY;
   if (a.ob != nullptr) {
-    // bf16 partials: each wave stages its 16 rows in LDS (rows 1040 bytes
-    // apart, so the 2-byte writes of the four row groups hit different
-    // banks), then writes every row as one 1 KB store of 16 bytes per lane
-    constexpr int RS = 1040;
-    __syncthreads();  // every wave is done with the tile ring
+    // bf16 partials in fragment order, straight from the accumulators: the
+    // wave's block of 16 heads x 512 dims is 16 stores of 16 bytes per lane,
+    // store j of lane 16g + i16 holding heads 4g .. 4g+3 at dims 16nt + i16
+    // of nt = 2j (elements 0..3) and 2j+1 (4..7); blocks of 16 heads follow
+    // each other, n_h rounded up to 16 (combine_frag_kernel reads them)
     if (!active) return;
-    unsigned char* stage = sK + wave * 16 * RS;
+    const int64_t nh16 = (a.n_h + 15) & ~int64_t(15);
+    bf16_raw* dst = a.ob + ((bq * a.splits + split) * nh16 + hbase) * CD + 8 * lane;
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
+    for (int j = 0; j < NT / 2; ++j) {
+      bf16x8 v;
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-        const __bf16 v = (__bf16)(o[nt][e] * inv[e]);
-        *reinterpret_cast<__bf16*>(stage + (4 * g + e) * RS + 2 * (16 * nt + i16)) = v;
+      for (int e = 0; e < 4; ++e) {
+        v[e] = (__bf16)(o[2 * j][e] * inv[e]);
+        v[4 + e] = (__bf16)(o[2 * j + 1][e] * inv[e]);
       }
-    __builtin_amdgcn_s_waitcnt(0xC07F);  // the wave's own LDS writes (lgkmcnt(0))
-    for (int r = 0; r < 16 && hbase + r < a.n_h; ++r) {
-      const uint4 v = *reinterpret_cast<const uint4*>(stage + r * RS + 16 * lane);
-      *reinterpret_cast<uint4*>(a.ob + (slot0 + hbase + r) * CD + 8 * lane) = v;
+      *reinterpret_cast<bf16x8*>(dst + 512 * j) = v;
     }
     return;
   }
@@ -742,18 +741,7 @@ __global__ void __launch_bounds__(512) attend512_kernel(AttArgs a) {
 // written by the same thread, and lse_in is read before lse is written.
 constexpr int kMaxSplits = 256;
 
-// 4 consecutive partial values at p as floats
-__device__ __forceinline__ float4 load_part4(const float* p) { return *reinterpret_cast<const float4*>(p); }
-__device__ __forceinline__ float4 load_part4(const bf16_raw* p) {
-  const uint2 u = *reinterpret_cast<const uint2*>(p);
-  return make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u), __uint_as_float(u.y << 16),
-                     __uint_as_float(u.y & 0xffff0000u));
-}
-__device__ __forceinline__ float load_part1(const float* p) { return *p; }
-__device__ __forceinline__ float load_part1(const bf16_raw* p) { return __uint_as_float(uint32_t(*p) << 16); }
-
-template <typename PT>
-__global__ void __launch_bounds__(128) combine_kernel(const PT* op, const float* lp, int64_t splits,
+__global__ void __launch_bounds__(128) combine_kernel(const float* op, const float* lp, int64_t splits,
                                                       int64_t n_h, int64_t c, float* out, float* lse,
                                                       const float* o_in, const float* lse_in) {
   __shared__ float wsh[kMaxSplits + 1];
@@ -780,7 +768,7 @@ __global__ void __launch_bounds__(128) combine_kernel(const PT* op, const float*
   const float M = red[0], L = red[1];
   for (int j = tid; j < parts; j += blockDim.x) wsh[j] = (M == -INFINITY) ? 0.f : __expf(wsh[j] - M) / L;
   __syncthreads();
-  const PT* base = op + (bq * splits * n_h + h) * c;
+  const float* base = op + (bq * splits * n_h + h) * c;
   const int64_t sstride = n_h * c;
   const float w_in = o_in ? wsh[splits] : 0.f;
   if ((c & 3) == 0) {
@@ -789,7 +777,7 @@ __global__ void __launch_bounds__(128) combine_kernel(const PT* op, const float*
 #pragma unroll 8
       for (int64_t j = 0; j < splits; ++j) {
         const float wj = wsh[j];
-        const float4 v = load_part4(base + j * sstride + d);
+        const float4 v = *reinterpret_cast<const float4*>(base + j * sstride + d);
         acc.x = fmaf(wj, v.x, acc.x); acc.y = fmaf(wj, v.y, acc.y);
         acc.z = fmaf(wj, v.z, acc.z); acc.w = fmaf(wj, v.w, acc.w);
       }
@@ -804,12 +792,128 @@ __global__ void __launch_bounds__(128) combine_kernel(const PT* op, const float*
     for (int64_t d = tid; d < c; d += blockDim.x) {
       float acc = 0.f;
 #pragma unroll 8
-      for (int64_t j = 0; j < splits; ++j) acc = fmaf(wsh[j], load_part1(base + j * sstride + d), acc);
+      for (int64_t j = 0; j < splits; ++j) acc = fmaf(wsh[j], base[j * sstride + d], acc);
       if (o_in) acc = fmaf(w_in, o_in[bh * c + d], acc);
       out[bh * c + d] = acc;
     }
   }
   if (tid == 0 && lse) lse[bh] = M == -INFINITY ? -INFINITY : M + __logf(L);
+}
+
+// The bf16 partials of attend512_kernel, in its fragment order.  A block
+// covers one query, one block of 16 heads and JB of the 16 fragment stores j
+// (blockIdx.y picks which), with W waves per j; blockDim.x = 64 * JB * W.
+// Lane l of the waves of store j reads, for its share of the splits (every
+// W-th), the 16 bytes lane l stored as its store j - heads 4g .. 4g+3 (g =
+// l/16) at dims 16nt + l%16 of nt = 2j, 2j+1 - so a wave reads 1 KB of
+// consecutive bytes per split; the W sums meet in LDS.  The split weights of
+// the 16 heads are formed in LDS first.  The extra part (o_in, lse_in) joins
+// as in combine_kernel; the host then launches JB = 16 (one block per query
+// and head block), so that lse_in is read before lse is written in place.
+__global__ void __launch_bounds__(1024) combine_frag_kernel(const bf16_raw* op, const float* lp, int64_t splits,
+                                                            int64_t n_h, int W, float* out, float* lse,
+                                                            const float* o_in, const float* lse_in) {
+  constexpr int CD = 512;
+  __shared__ __attribute__((aligned(16))) float wsh[(kMaxSplits + 1) * 16];  // [part][head of the block]
+  __shared__ float mh[16], lh[16];
+  __shared__ float4 red[4 * 2 * 64];  // wave sums [wave][2][lane] (W > 1 only with JB = 1, W <= 4)
+  const int64_t nb = (n_h + 15) / 16;
+  const int64_t bq = blockIdx.x / nb, hb = (int64_t(blockIdx.x) - bq * nb) * 16;
+  const int tid = threadIdx.x, nthr = blockDim.x;
+  const int lane = tid & 63, wid = tid >> 6, wv = wid % W;
+  const int j = int(blockIdx.y) * (nthr / (64 * W)) + wid / W;
+  const int parts = int(splits) + (o_in ? 1 : 0);
+  // lse of every part for the block's heads (heads past n_h: -inf), four
+  // heads a thread, loaded together
+  for (int i = tid; i < parts * 4; i += nthr) {
+    const int p = i >> 2, e0 = 4 * (i & 3);
+    float v[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int64_t h = hb + e0 + e;
+      v[e] = -INFINITY;
+      if (h < n_h) v[e] = p < splits ? lp[(bq * splits + p) * n_h + h] : lse_in[bq * n_h + h];
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) wsh[p * 16 + e0 + e] = v[e];
+  }
+  __syncthreads();
+  {  // per head: max, sum and weights over the parts, nthr/16 threads a head
+     // (consecutive lanes of one wave)
+    const int tph = nthr >> 4, hh = tid / tph, q = tid % tph;
+    float M = -INFINITY;
+    for (int p = q; p < parts; p += tph) M = fmaxf(M, wsh[p * 16 + hh]);
+    for (int off = 1; off < tph; off <<= 1) M = fmaxf(M, __shfl_xor(M, off));
+    float L = 0.f;
+    if (M != -INFINITY)
+      for (int p = q; p < parts; p += tph) L += __expf(wsh[p * 16 + hh] - M);
+    for (int off = 1; off < tph; off <<= 1) L += __shfl_xor(L, off);
+    const float rl = M == -INFINITY ? 0.f : 1.f / L;
+    for (int p = q; p < parts; p += tph) wsh[p * 16 + hh] = M == -INFINITY ? 0.f : __expf(wsh[p * 16 + hh] - M) * rl;
+    if (q == 0) {
+      mh[hh] = M;
+      lh[hh] = L;
+    }
+  }
+  __syncthreads();
+  const int g = lane >> 4, i16 = lane & 15;
+  float acc[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) acc[k] = 0.f;
+  const int64_t sstride = nb * 16 * CD;
+  const bf16_raw* base = op + (bq * splits * nb * 16 + hb) * CD + 512 * j + 8 * lane;
+  // U loads issued together, then used (the compiler left to itself waits
+  // for each load before the next)
+  constexpr int U = 8;
+  for (int64_t p0 = wv; p0 < splits; p0 += U * W) {
+    uint4 u[U];
+#pragma unroll
+    for (int i = 0; i < U; ++i) {
+      const int64_t p = p0 + int64_t(i) * W;
+      u[i] = p < splits ? *reinterpret_cast<const uint4*>(base + p * sstride) : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < U; ++i) {
+      const int64_t p = p0 + int64_t(i) * W;
+      if (p < splits) {
+        const float4 w = *reinterpret_cast<const float4*>(&wsh[p * 16 + 4 * g]);
+        acc[0] = fmaf(w.x, __uint_as_float(u[i].x << 16), acc[0]);
+        acc[1] = fmaf(w.y, __uint_as_float(u[i].x & 0xffff0000u), acc[1]);
+        acc[2] = fmaf(w.z, __uint_as_float(u[i].y << 16), acc[2]);
+        acc[3] = fmaf(w.w, __uint_as_float(u[i].y & 0xffff0000u), acc[3]);
+        acc[4] = fmaf(w.x, __uint_as_float(u[i].z << 16), acc[4]);
+        acc[5] = fmaf(w.y, __uint_as_float(u[i].z & 0xffff0000u), acc[5]);
+        acc[6] = fmaf(w.z, __uint_as_float(u[i].w << 16), acc[6]);
+        acc[7] = fmaf(w.w, __uint_as_float(u[i].w & 0xffff0000u), acc[7]);
+      }
+    }
+  }
+  if (W > 1) {  // the other waves of store j hand their sums to its first wave
+    if (wv != 0) {
+      red[(wid * 2) * 64 + lane] = make_float4(acc[0], acc[1], acc[2], acc[3]);
+      red[(wid * 2 + 1) * 64 + lane] = make_float4(acc[4], acc[5], acc[6], acc[7]);
+    }
+    __syncthreads();
+    if (wv != 0) return;
+    for (int v = 1; v < W; ++v) {
+      const float4 a0 = red[((wid + v) * 2) * 64 + lane], a1 = red[((wid + v) * 2 + 1) * 64 + lane];
+      acc[0] += a0.x; acc[1] += a0.y; acc[2] += a0.z; acc[3] += a0.w;
+      acc[4] += a1.x; acc[5] += a1.y; acc[6] += a1.z; acc[7] += a1.w;
+    }
+  }
+  // element k: head hb + 4g + k%4, dim 16 (2j + k/4) + i16
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const int64_t h = hb + 4 * g + (k & 3);
+    if (h < n_h) {
+      const int64_t at = (bq * n_h + h) * CD + 16 * (2 * j + (k >> 2)) + i16;
+      float v = acc[k];
+      if (o_in) v = fmaf(wsh[int(splits) * 16 + 4 * g + (k & 3)], o_in[at], v);
+      out[at] = v;
+    }
+  }
+  if (lse && j == 0 && lane < 16 && hb + lane < n_h)
+    lse[bq * n_h + hb + lane] = mh[lane] == -INFINITY ? -INFINITY : mh[lane] + __logf(lh[lane]);
 }
 
 // ------------------------------------------------------------------ sink logits
@@ -869,7 +973,9 @@ Plan plan(int dtype, int64_t BQ, int64_t n_h, int64_t c, int64_t nkeys, bool mer
   size_t off = 0;
   p.bf16_parts = p.mfma && c == 512 && kBf16Partials;
   if (s > 1 || merge) {  // partials, combined afterwards
-    off = align_up(size_t(BQ) * s * n_h * c * (p.bf16_parts ? 2 : 4), 256);
+    // bf16 partials: blocks of 16 heads (n_h rounded up to 16)
+    const int64_t nh_parts = p.bf16_parts ? (n_h + 15) / 16 * 16 : n_h;
+    off = align_up(size_t(BQ) * s * nh_parts * c * (p.bf16_parts ? 2 : 4), 256);
     p.l_off = off;
     off = align_up(off + size_t(BQ) * s * n_h * 4, 256);
   } else {
@@ -925,12 +1031,17 @@ int run_attend(const char* name, int dtype, AttArgs a, int64_t BQ, int64_t nkeys
   }
   int rc = check_launch(name);
   if (rc || !partials) return rc;
-  if (p.bf16_parts)
-    hipLaunchKernelGGL(combine_kernel<bf16_raw>, dim3((unsigned)(BQ * a.n_h)), dim3(128), 0, s, a.ob, a.lse,
-                       p.splits, a.n_h, a.c, out, lse, o_in, lse_in);
-  else
-    hipLaunchKernelGGL(combine_kernel<float>, dim3((unsigned)(BQ * a.n_h)), dim3(128), 0, s, a.o, a.lse, p.splits,
-                       a.n_h, a.c, out, lse, o_in, lse_in);
+  if (p.bf16_parts) {
+    // merging: one block per query and head block (lse may be lse_in);
+    // else four waves per fragment store, sharing the splits
+    const unsigned jb = merge ? 16u : 1u, w = merge ? 1u : 4u;
+    const dim3 grid{(unsigned)(BQ * ((a.n_h + 15) / 16)), 16u / jb, 1u};
+    hipLaunchKernelGGL(combine_frag_kernel, grid, dim3(64 * jb * w), 0, s, a.ob, a.lse, p.splits, a.n_h, int(w),
+                       out, lse, o_in, lse_in);
+  } else {
+    hipLaunchKernelGGL(combine_kernel, dim3((unsigned)(BQ * a.n_h)), dim3(128), 0, s, a.o, a.lse, p.splits, a.n_h,
+                       a.c, out, lse, o_in, lse_in);
+  }
   return check_launch(name);
 }
 

@@ -224,6 +224,7 @@ def _random_selection(B, n_q, k, cap, seed, counts):
     ("bf16", 2, 2, 128, 512, 1024, 32768, [1024, 1000, 77, 0]),
     ("bf16", 1, 1, 48, 256, 300, 900, [299]),                # heads not a multiple of 32
     ("bf16", 1, 3, 128, 512, 40, 5000, [40, 33, 1]),
+    ("bf16", 2, 1, 40, 512, 300, 2000, [300, 129]),           # c = 512 split partials, last head block partial
 ])
 def test_csa_attend(dtype, B, n_q, n_h, c, k, cap, counts):
     seed = 700 + cap + k
@@ -261,6 +262,7 @@ def test_csa_attend_ignores_invalid_indices():
     ("bf16", 1, 1, 16, 128, 128, 64, [8192]),                # decode-8k shape
     ("bf16", 3, 1, 128, 512, 128, 700, [700 * 128, 3 * 128 + 5, 100]),
     ("bf16", 2, 2, 40, 256, 16, 513, [513 * 16, 16 * 500 + 3, 31, 16 * 64]),
+    ("bf16", 2, 1, 24, 512, 128, 3000, [3000 * 128, 128 * 777 + 5]),  # c = 512, 24 heads: one partial head block
 ])
 def test_hca_attend(dtype, B, n_q, n_h, c, mp, cap, ts):
     seed = 900 + cap
@@ -335,6 +337,7 @@ def test_window_attend(dtype, B, n_q, n_h, c, n_win, ring, ts):
 
 @pytest.mark.parametrize("dtype,B,n_h,c,k,cap,counts", [
     ("bf16", 4, 128, 512, 1024, 262208, [1024, 1024, 7, 0]),  # V4-Pro shape; one empty compressed part
+    ("bf16", 2, 40, 512, 200, 3000, [200, 64]),              # c = 512, 40 heads: the merge with a partial head block
     ("f32", 2, 4, 16, 8, 40, [5, 8]),
 ])
 def test_window_joins_compressed_branch_in_place(dtype, B, n_h, c, k, cap, counts):
