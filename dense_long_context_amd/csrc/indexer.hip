@@ -814,6 +814,47 @@ __device__ void find_threshold(const uint32_t* h, int nbins, uint32_t need, uint
   __syncthreads();
 }
 
+// The same search over a histogram the threads hold in registers: thread i
+// owns bins PER*i .. PER*i + PER-1, given in v (nbins = PER * blockDim.x).
+template <int PER>
+__device__ void find_threshold_regs(const uint32_t (&v)[PER], uint32_t need, uint32_t* scratch, int* T_out,
+                                    uint32_t* above_out) {
+  const int lo = threadIdx.x * PER;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nwaves = blockDim.x >> 6;
+  uint32_t mine = 0;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) mine += v[i];
+  uint32_t suf = mine;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const uint32_t x = __shfl_down(suf, off);
+    if (lane + off < 64) suf += x;
+  }
+  if (lane == 0) scratch[wave] = suf;
+  if (threadIdx.x == 0) {
+    scratch[16] = 0;
+    scratch[17] = 0;
+  }
+  __syncthreads();
+  uint32_t higher = 0;
+  for (int w = wave + 1; w < nwaves; ++w) higher += scratch[w];
+  uint32_t run = higher + suf - mine;
+  if (run < need && run + mine >= need) {
+#pragma unroll
+    for (int i = PER - 1; i >= 0; --i) {
+      if (run < need && run + v[i] >= need) {
+        scratch[16] = uint32_t(lo + i);
+        scratch[17] = run;
+      }
+      run += v[i];
+    }
+  }
+  __syncthreads();
+  *T_out = int(scratch[16]);
+  *above_out = scratch[17];
+  __syncthreads();
+}
+
 // Ordered compaction helper: returns this thread's position among the threads
 // of the block with pred set (in thread order) and, through *total, their
 // count.  wtot holds blockDim.x/64 words.  Ends with the block synchronised.
@@ -867,7 +908,7 @@ __device__ __forceinline__ uint32_t scan256(uint32_t v, uint32_t* wsum, uint32_t
 // second digit (key bits 20..10) is counted into the query's second
 // histogram, which is the first radix pass of the finish.
 __global__ void __launch_bounds__(256) filter_kernel(IdxArgs a) {
-  __shared__ uint32_t h[kBins];
+  static_assert(kBins == 8 * 256, "filter_kernel: eight first-digit bins per thread");
   __shared__ uint32_t h2[kBins];
   __shared__ uint32_t scratch[18];
   __shared__ uint32_t wsum[4];
@@ -891,14 +932,18 @@ __global__ void __launch_bounds__(256) filter_kernel(IdxArgs a) {
   };
   float v[4];
   load4(s0, v);
-  for (int i = threadIdx.x; i < kBins; i += blockDim.x) {
-    h[i] = a.hist[bq * kBins + i];
-    h2[i] = 0;
+  // thread j holds first-digit bins 8j .. 8j+7 (two 16-byte loads)
+  uint32_t hv[8];
+  {
+    const uint4* hp = reinterpret_cast<const uint4*>(a.hist + bq * kBins) + 2 * threadIdx.x;
+    const uint4 x = hp[0], y = hp[1];
+    hv[0] = x.x; hv[1] = x.y; hv[2] = x.z; hv[3] = x.w;
+    hv[4] = y.x; hv[5] = y.y; hv[6] = y.z; hv[7] = y.w;
   }
-  __syncthreads();
+  for (int i = threadIdx.x; i < kBins; i += blockDim.x) h2[i] = 0;
   int T;
   uint32_t above;
-  find_threshold(h, kBins, uint32_t(keff), scratch, &T, &above);
+  find_threshold_regs<8>(hv, uint32_t(keff), scratch, &T, &above);  // also orders the h2 clear
 
   int32_t* sel = a.sel + bq * a.cap + s0;
   int32_t* cand = a.cand + bq * a.cap + s0;
@@ -1037,10 +1082,23 @@ __global__ void __launch_bounds__(1024) finish_kernel(IdxArgs a) {
     return;
   }
   const int nch = int(ceil_div(nvis, a.keys_per_wg));
-  const uint32_t* cc = a.ccnt + bq * a.max_chunks * 2;
-  for (int c = threadIdx.x; c < nch; c += blockDim.x) {
-    off_sel[c] = cc[2 * c];
-    off_cand[c] = cc[2 * c + 1];
+  const uint2* cc = reinterpret_cast<const uint2*>(a.ccnt + bq * a.max_chunks * 2);
+  // the chunk counts and the candidates' first composite digit (counted by
+  // the filter; pass 0 below) load together
+  static_assert(kBins % 2 == 0, "bins in pairs");
+  const uint2* h2g = reinterpret_cast<const uint2*>(a.hist2 + bq * kBins);
+  for (int i = threadIdx.x; i < kBins / 2 || i < nch; i += blockDim.x) {
+    uint2 x = make_uint2(0, 0), y = make_uint2(0, 0);
+    if (i < nch) x = cc[i];
+    if (i < kBins / 2) y = h2g[i];
+    if (i < nch) {
+      off_sel[i] = x.x;
+      off_cand[i] = x.y;
+    }
+    if (i < kBins / 2) {
+      h[2 * i] = y.x;
+      h[2 * i + 1] = y.y;
+    }
   }
   __syncthreads();
   uint32_t tsel, tcand;
@@ -1060,28 +1118,20 @@ __global__ void __launch_bounds__(1024) finish_kernel(IdxArgs a) {
     }
     return lo;
   };
-  // four entries per thread per round, their loads in flight together
+  // both lists in one sweep, four entries of each per thread per round, all
+  // their loads in flight together
   constexpr int G = 4;
-  for (uint32_t i0 = threadIdx.x; i0 < n_sel; i0 += G * blockDim.x) {
-    int32_t v[G];
+  const uint32_t n_both = n_sel > n_cand ? n_sel : n_cand;
+  for (uint32_t i0 = threadIdx.x; i0 < n_both; i0 += G * blockDim.x) {
+    int32_t vs[G], vi[G];
+    uint32_t vk[G];
 #pragma unroll
     for (int u = 0; u < G; ++u) {
       const uint32_t i = i0 + u * blockDim.x;
       if (i < n_sel) {
         const int c = chunk_of(off_sel, i);
-        v[u] = a.sel[bq * a.cap + int64_t(c) * a.keys_per_wg + (i - off_sel[c])];
+        vs[u] = a.sel[bq * a.cap + int64_t(c) * a.keys_per_wg + (i - off_sel[c])];
       }
-    }
-#pragma unroll
-    for (int u = 0; u < G; ++u)
-      if (i0 + u * blockDim.x < n_sel) lsel[i0 + u * blockDim.x] = v[u];
-  }
-  for (uint32_t i0 = threadIdx.x; i0 < n_cand; i0 += G * blockDim.x) {
-    int32_t vi[G];
-    uint32_t vk[G];
-#pragma unroll
-    for (int u = 0; u < G; ++u) {
-      const uint32_t i = i0 + u * blockDim.x;
       if (i < n_cand) {
         const int c = chunk_of(off_cand, i);
         const int64_t at = bq * a.cap + int64_t(c) * a.keys_per_wg + (i - off_cand[c]);
@@ -1092,6 +1142,7 @@ __global__ void __launch_bounds__(1024) finish_kernel(IdxArgs a) {
 #pragma unroll
     for (int u = 0; u < G; ++u) {
       const uint32_t i = i0 + u * blockDim.x;
+      if (i < n_sel) lsel[i] = vs[u];
       if (i < n_cand) {
         cidx[i] = vi[u];
         ckey[i] = vk[u];
@@ -1110,9 +1161,8 @@ __global__ void __launch_bounds__(1024) finish_kernel(IdxArgs a) {
     const uint32_t dmask = (1u << bits) - 1u;
     const int nb = 1 << bits;
     if (pass == 0) {
-      // the filter already counted the candidates' first composite digit
-      for (int i = threadIdx.x; i < kBins; i += blockDim.x) h[i] = a.hist2[bq * kBins + i];
-      __syncthreads();
+      // the filter already counted the candidates' first composite digit (h,
+      // loaded with the chunk counts)
     } else {
       for (int i = threadIdx.x; i < kBins; i += blockDim.x) h[i] = 0;
       __syncthreads();
