@@ -126,13 +126,20 @@ __global__ void __launch_bounds__(256) scores_valu_kernel(IdxArgs a) {
 // 32-dim step.  Lane l holds head/key l%16 of the A/B operands and dims
 // 8*(l/16) .. +7 of each 32-dim step; the result holds key l%16 and heads
 // 4*(l/16) .. +3, and the head sum is finished with two cross-lane adds.
-// Queries stay in registers for the whole pass.  Key tiles (16 keys,
+// Queries stay in registers for the whole pass; they arrive once per
+// workgroup, wave w moving heads 16w .. 16w+15 into the last stage of its
+// ring, from where every wave reads its operands.  Key tiles (16 keys,
 // 16*2*c^I bytes) arrive by direct global->LDS loads, one instruction moving
 // 1 KB of consecutive rows, so HBM sees whole lines.  Each wave streams its
 // own tiles through a ring of NS LDS stages with NS-1 tiles in flight, and
 // only it reads them, so the loop has no barrier.  Within a row, 16-byte chunk c is stored at slot
 // c ^ (row % chunks): the 16 rows that one ds_read_b128 pass reads at the
 // same chunk then fall on distinct banks (64 banks of 4 bytes).
+// The scores of kScoreBuf tiles collect in LDS and go out together: vmcnt
+// counts stores too, so a store per tile between the tile loads would make
+// every wait for a tile also wait for part of the next one.
+
+constexpr int kScoreBuf = 32;  // tiles whose scores a wave collects before storing them
 
 template <int HT, int KT, int NS>
 __global__ void __launch_bounds__(256) scores_mfma_kernel(IdxArgs a) {
@@ -141,8 +148,10 @@ __global__ void __launch_bounds__(256) scores_mfma_kernel(IdxArgs a) {
   constexpr int TILEB = 16 * ROWB;  // one tile: 16 keys
   constexpr int RPI = 1024 / ROWB;  // rows per 1 KB load (KT loads per tile)
   static_assert(RPI * KT == 16, "tile geometry");
+  static_assert(HT <= 4, "one 16-head block of queries per wave");
   __shared__ uint32_t hist[kBins];
   __shared__ __attribute__((aligned(1024))) unsigned char sK[4][NS][TILEB];
+  __shared__ float sS[4][kScoreBuf * 16];
   const int64_t bq = blockIdx.y;
   const int64_t nvis = visible(a, bq);
   const int64_t s0 = int64_t(blockIdx.x) * a.keys_per_wg;
@@ -176,24 +185,21 @@ __global__ void __launch_bounds__(256) scores_mfma_kernel(IdxArgs a) {
       dma_row(base, off, lds);
     }
   };
+  // queries: wave w < HT moves heads 16w .. 16w+15 (rows past n_hI repeat
+  // head n_hI-1) into the last stage of its ring, rows in order
+  if (wave < HT) {
+    const bf16_raw* qg = static_cast<const bf16_raw*>(a.qI) + bq * a.n_hI * cI;
+#pragma unroll
+    for (int j = 0; j < KT; ++j) {
+      const int h = min(wave * 16 + j * RPI + lane / CPR, int(a.n_hI) - 1);
+      const uint32_t off = uint32_t(h * ROWB + (lane % CPR) * 16);
+      const uint32_t lds = (uint32_t)(uintptr_t)DLC_LDS(&sK[wave][NS - 1][0]) + uint32_t(j * 1024);
+      dma_row(qg, off, lds);
+    }
+  }
 #pragma unroll
   for (int p = 0; p < NS - 1; ++p)
     if (p < my_tiles) issue(p, p);
-
-  // queries: A operand, rows = heads (loaded after the first tiles are in flight)
-  bf16x8 qf[HT][KT];
-  const bf16_raw* qg = static_cast<const bf16_raw*>(a.qI) + bq * a.n_hI * cI;
-#pragma unroll
-  for (int ht = 0; ht < HT; ++ht) {
-    // heads past n_hI read head n_hI-1 and are then zeroed (their weight is 0 too)
-    const bool pad = ht * 16 + r16 >= a.n_hI;
-    const int h = min(ht * 16 + r16, int(a.n_hI) - 1);
-#pragma unroll
-    for (int kt = 0; kt < KT; ++kt) {
-      const uint4 v = *reinterpret_cast<const uint4*>(qg + h * cI + kt * 32 + g * 8);
-      qf[ht][kt] = __builtin_bit_cast(bf16x8, pad ? make_uint4(0, 0, 0, 0) : v);
-    }
-  }
   float wv[HT][4];
 #pragma unroll
   for (int ht = 0; ht < HT; ++ht)
@@ -205,8 +211,26 @@ __global__ void __launch_bounds__(256) scores_mfma_kernel(IdxArgs a) {
 #pragma unroll
   for (int ht = 0; ht < HT; ++ht)
 #pragma unroll
+    for (int r = 0; r < 4; ++r) asm volatile("" ::"v"(wv[ht][r]));
+  wait_vm<0>();     // the query block and the first tiles
+  __syncthreads();  // every wave's query rows landed; hist cleared
+  // A operand, rows = heads: head ht*16 + r16 from wave ht's block; heads past
+  // n_hI are zeroed (their weight is 0 too)
+  bf16x8 qf[HT][KT];
+#pragma unroll
+  for (int ht = 0; ht < HT; ++ht) {
+    const bool pad = ht * 16 + r16 >= a.n_hI;
+#pragma unroll
+    for (int kt = 0; kt < KT; ++kt) {
+      const uint4 v = *reinterpret_cast<const uint4*>(&sK[ht][NS - 1][r16 * ROWB + kt * 64 + g * 16]);
+      qf[ht][kt] = __builtin_bit_cast(bf16x8, pad ? make_uint4(0, 0, 0, 0) : v);
+    }
+  }
+#pragma unroll
+  for (int ht = 0; ht < HT; ++ht)
+#pragma unroll
     for (int kt = 0; kt < KT; ++kt) asm volatile("" ::"v"(qf[ht][kt]));
-  __syncthreads();  // hist cleared (and the query loads, with every tile load before them, done)
+  __syncthreads();  // every wave holds its operands: the last stages may take tiles
 
   for (int64_t it = 0; it < my_tiles; ++it) {
     const int st = int(it % NS);
@@ -248,10 +272,24 @@ __global__ void __launch_bounds__(256) scores_mfma_kernel(IdxArgs a) {
     }
     const float part = rows4_sum((ps[0] + ps[1]) + (ps[2] + ps[3]));
     const int64_t s = s0 + (wave + 4 * it) * 16 + r16;
-    if (g == 0 && s < s1) {
+    const int slot = int(it % kScoreBuf);
+    if (g == 0) {
       const float score = canon_zero(part);
-      a.scores[bq * a.score_ld + s] = score;
-      atomicAdd(&hist[order_key(score) >> kShift1], 1u);
+      sS[wave][slot * 16 + r16] = score;
+      if (s < s1) atomicAdd(&hist[order_key(score) >> kShift1], 1u);
+    }
+    if (slot == kScoreBuf - 1 || it + 1 == my_tiles) {
+      // the wave's buffered tiles it-slot .. it, 16 scores each (the LDS
+      // accesses of one wave run in order)
+      asm volatile("" ::: "memory");
+      const int64_t t0 = it - slot;
+#pragma unroll
+      for (int q = 0; q < kScoreBuf / 4; ++q) {
+        const int idx = q * 64 + lane, tl = idx >> 4;
+        const int64_t sk = s0 + (wave + 4 * (t0 + tl)) * 16 + (idx & 15);
+        if (tl <= slot && sk < s1) a.scores[bq * a.score_ld + sk] = sS[wave][idx];
+      }
+      asm volatile("" ::: "memory");
     }
   }
   flush_hist(hist, a.hist + bq * kBins);
@@ -270,8 +308,8 @@ __global__ void __launch_bounds__(256) scores_mfma_kernel(IdxArgs a) {
 // code row, 16-byte chunk c sits at slot c ^ ((row / RPB) % CPR) (RPB rows
 // per 256 bytes, CPR chunks per row), so the 16 rows of one ds_read_b128
 // pass fall on distinct banks.  The queries arrive quantized
-// (mxfp4_quantize, run on them just before).  Result layout and head sum as
-// in the bf16 kernel.
+// (mxfp4_quantize, run on them just before).  Result layout, head sum and
+// the buffered score stores as in the bf16 kernel.
 
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 
@@ -289,6 +327,7 @@ __global__ void __launch_bounds__(64 * NW) scores_fp4_kernel(IdxArgs a) {
   static_assert(CI == 128 || CI == 256, "c^I");
   __shared__ uint32_t hist[kBins];
   __shared__ __attribute__((aligned(16))) unsigned char sK[NW][NS][STB];
+  __shared__ float sS[NW][kScoreBuf * 16];
   const int64_t bq = blockIdx.y;
   const int64_t nvis = visible(a, bq);
   const int64_t s0 = int64_t(blockIdx.x) * a.keys_per_wg;
@@ -409,10 +448,22 @@ __global__ void __launch_bounds__(64 * NW) scores_fp4_kernel(IdxArgs a) {
     }
     const float part = rows4_sum((ps[0] + ps[1]) + (ps[2] + ps[3]));
     const int64_t s = s0 + (wave + NW * it) * 16 + r16;
-    if (g == 0 && s < s1) {
+    const int slot = int(it % kScoreBuf);
+    if (g == 0) {
       const float score = canon_zero(part);
-      a.scores[bq * a.score_ld + s] = score;
-      atomicAdd(&hist[order_key(score) >> kShift1], 1u);
+      sS[wave][slot * 16 + r16] = score;
+      if (s < s1) atomicAdd(&hist[order_key(score) >> kShift1], 1u);
+    }
+    if (slot == kScoreBuf - 1 || it + 1 == my_tiles) {
+      asm volatile("" ::: "memory");
+      const int64_t t0 = it - slot;
+#pragma unroll
+      for (int q = 0; q < kScoreBuf / 4; ++q) {
+        const int idx = q * 64 + lane, tl = idx >> 4;
+        const int64_t sk = s0 + (wave + NW * (t0 + tl)) * 16 + (idx & 15);
+        if (tl <= slot && sk < s1) a.scores[bq * a.score_ld + sk] = sS[wave][idx];
+      }
+      asm volatile("" ::: "memory");
     }
   }
   flush_hist(hist, a.hist + bq * kBins);
