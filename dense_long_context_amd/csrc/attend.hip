@@ -810,9 +810,10 @@ __global__ void __launch_bounds__(128) combine_kernel(const float* op, const flo
 // the 16 heads are formed in LDS first.  The extra part (o_in, lse_in) joins
 // as in combine_kernel; the host then launches JB = 16 (one block per query
 // and head block), so that lse_in is read before lse is written in place.
-__global__ void __launch_bounds__(1024) combine_frag_kernel(const bf16_raw* op, const float* lp, int64_t splits,
-                                                            int64_t n_h, int W, float* out, float* lse,
-                                                            const float* o_in, const float* lse_in) {
+template <int NT, int U>  // block size; partials a wave has in flight
+__global__ void __launch_bounds__(NT) combine_frag_kernel(const bf16_raw* op, const float* lp, int64_t splits,
+                                                          int64_t n_h, int W, float* out, float* lse,
+                                                          const float* o_in, const float* lse_in) {
   constexpr int CD = 512;
   __shared__ __attribute__((aligned(16))) float wsh[(kMaxSplits + 1) * 16];  // [part][head of the block]
   __shared__ float mh[16], lh[16];
@@ -823,19 +824,46 @@ __global__ void __launch_bounds__(1024) combine_frag_kernel(const bf16_raw* op, 
   const int lane = tid & 63, wid = tid >> 6, wv = wid % W;
   const int j = int(blockIdx.y) * (nthr / (64 * W)) + wid / W;
   const int parts = int(splits) + (o_in ? 1 : 0);
+  const int g = lane >> 4, i16 = lane & 15;
+  const int64_t sstride = nb * 16 * CD;
+  const bf16_raw* base = op + (bq * splits * nb * 16 + hb) * CD + 512 * j + 8 * lane;
   // lse of every part for the block's heads (heads past n_h: -inf), four
-  // heads a thread, loaded together
-  for (int i = tid; i < parts * 4; i += nthr) {
-    const int p = i >> 2, e0 = 4 * (i & 3);
-    float v[4];
+  // heads a thread; the first round is loaded before the partials of the
+  // first batch, which do not depend on the weights and stay in flight while
+  // the weights are formed
+  // (every load below is unconditional, from a clamped address, with the
+  // result dropped when out of range: loads under branches make the
+  // compiler wait for them early)
+  auto lse_load = [&](int i, float* v) {
+    const int p = min(i >> 2, parts - 1), e0 = 4 * (i & 3);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const int64_t h = hb + e0 + e;
-      v[e] = -INFINITY;
-      if (h < n_h) v[e] = p < splits ? lp[(bq * splits + p) * n_h + h] : lse_in[bq * n_h + h];
+      const int64_t h = hb + e0 + e, hc = h < n_h ? h : n_h - 1;
+      const float* src = p < splits ? lp + (bq * splits + p) * n_h + hc : lse_in + bq * n_h + hc;
+      const float x = *src;
+      v[e] = h < n_h ? x : -INFINITY;
     }
+  };
+  float lv[4];
+  lse_load(tid, lv);
+  asm volatile("" ::: "memory");  // these loads first, so that their wait leaves the partials in flight
+  uint4 u[U];
+  const int64_t wstep = int64_t(W) * sstride;
+  {
+    const bf16_raw* pp = base + wv * sstride;
+    const bf16_raw* plast = base + (splits - 1) * sstride;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) wsh[p * 16 + e0 + e] = v[e];
+    for (int i = 0; i < U; ++i, pp += wstep) u[i] = *reinterpret_cast<const uint4*>(wv + i * W < splits ? pp : plast);
+  }
+  if (tid < parts * 4) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) wsh[(tid >> 2) * 16 + 4 * (tid & 3) + e] = lv[e];
+  }
+  for (int i = tid + nthr; i < parts * 4; i += nthr) {
+    float v[4];
+    lse_load(i, v);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) wsh[(i >> 2) * 16 + 4 * (i & 3) + e] = v[e];
   }
   __syncthreads();
   {  // per head: max, sum and weights over the parts, nthr/16 threads a head
@@ -856,36 +884,35 @@ __global__ void __launch_bounds__(1024) combine_frag_kernel(const bf16_raw* op, 
     }
   }
   __syncthreads();
-  const int g = lane >> 4, i16 = lane & 15;
   float acc[8];
 #pragma unroll
   for (int k = 0; k < 8; ++k) acc[k] = 0.f;
-  const int64_t sstride = nb * 16 * CD;
-  const bf16_raw* base = op + (bq * splits * nb * 16 + hb) * CD + 512 * j + 8 * lane;
-  // U loads issued together, then used (the compiler left to itself waits
-  // for each load before the next)
-  constexpr int U = 8;
-  for (int64_t p0 = wv; p0 < splits; p0 += U * W) {
-    uint4 u[U];
+  auto accumulate = [&](const uint4& x, int64_t p) {
+    const float4 w = *reinterpret_cast<const float4*>(&wsh[p * 16 + 4 * g]);
+    acc[0] = fmaf(w.x, __uint_as_float(x.x << 16), acc[0]);
+    acc[1] = fmaf(w.y, __uint_as_float(x.x & 0xffff0000u), acc[1]);
+    acc[2] = fmaf(w.z, __uint_as_float(x.y << 16), acc[2]);
+    acc[3] = fmaf(w.w, __uint_as_float(x.y & 0xffff0000u), acc[3]);
+    acc[4] = fmaf(w.x, __uint_as_float(x.z << 16), acc[4]);
+    acc[5] = fmaf(w.y, __uint_as_float(x.z & 0xffff0000u), acc[5]);
+    acc[6] = fmaf(w.z, __uint_as_float(x.w << 16), acc[6]);
+    acc[7] = fmaf(w.w, __uint_as_float(x.w & 0xffff0000u), acc[7]);
+  };
+#pragma unroll
+  for (int i = 0; i < U; ++i) {
+    const int64_t p = wv + int64_t(i) * W;
+    if (p < splits) accumulate(u[i], p);
+  }
+  // further batches (more than U * W splits), U loads issued together
+  for (int64_t p0 = wv + int64_t(U) * W; p0 < splits; p0 += int64_t(U) * W) {
+    const bf16_raw* pp = base + p0 * sstride;
+    const bf16_raw* plast = base + (splits - 1) * sstride;
+#pragma unroll
+    for (int i = 0; i < U; ++i, pp += wstep) u[i] = *reinterpret_cast<const uint4*>(p0 + i * W < splits ? pp : plast);
 #pragma unroll
     for (int i = 0; i < U; ++i) {
       const int64_t p = p0 + int64_t(i) * W;
-      u[i] = p < splits ? *reinterpret_cast<const uint4*>(base + p * sstride) : make_uint4(0, 0, 0, 0);
-    }
-#pragma unroll
-    for (int i = 0; i < U; ++i) {
-      const int64_t p = p0 + int64_t(i) * W;
-      if (p < splits) {
-        const float4 w = *reinterpret_cast<const float4*>(&wsh[p * 16 + 4 * g]);
-        acc[0] = fmaf(w.x, __uint_as_float(u[i].x << 16), acc[0]);
-        acc[1] = fmaf(w.y, __uint_as_float(u[i].x & 0xffff0000u), acc[1]);
-        acc[2] = fmaf(w.z, __uint_as_float(u[i].y << 16), acc[2]);
-        acc[3] = fmaf(w.w, __uint_as_float(u[i].y & 0xffff0000u), acc[3]);
-        acc[4] = fmaf(w.x, __uint_as_float(u[i].z << 16), acc[4]);
-        acc[5] = fmaf(w.y, __uint_as_float(u[i].z & 0xffff0000u), acc[5]);
-        acc[6] = fmaf(w.z, __uint_as_float(u[i].w << 16), acc[6]);
-        acc[7] = fmaf(w.w, __uint_as_float(u[i].w & 0xffff0000u), acc[7]);
-      }
+      if (p < splits) accumulate(u[i], p);
     }
   }
   if (W > 1) {  // the other waves of store j hand their sums to its first wave
@@ -1034,10 +1061,13 @@ int run_attend(const char* name, int dtype, AttArgs a, int64_t BQ, int64_t nkeys
   if (p.bf16_parts) {
     // merging: one block per query and head block (lse may be lse_in);
     // else four waves per fragment store, sharing the splits
-    const unsigned jb = merge ? 16u : 1u, w = merge ? 1u : 4u;
-    const dim3 grid{(unsigned)(BQ * ((a.n_h + 15) / 16)), 16u / jb, 1u};
-    hipLaunchKernelGGL(combine_frag_kernel, grid, dim3(64 * jb * w), 0, s, a.ob, a.lse, p.splits, a.n_h, int(w),
-                       out, lse, o_in, lse_in);
+    const unsigned nb = (unsigned)(BQ * ((a.n_h + 15) / 16));
+    if (merge)
+      hipLaunchKernelGGL((combine_frag_kernel<1024, 4>), dim3(nb, 1u, 1u), dim3(1024), 0, s, a.ob, a.lse, p.splits,
+                         a.n_h, 1, out, lse, o_in, lse_in);
+    else
+      hipLaunchKernelGGL((combine_frag_kernel<256, 16>), dim3(nb, 16u, 1u), dim3(256), 0, s, a.ob, a.lse, p.splits,
+                         a.n_h, 4, out, lse, o_in, lse_in);
   } else {
     hipLaunchKernelGGL(combine_kernel, dim3((unsigned)(BQ * a.n_h)), dim3(128), 0, s, a.o, a.lse, p.splits, a.n_h,
                        a.c, out, lse, o_in, lse_in);
