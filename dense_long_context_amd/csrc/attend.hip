@@ -49,6 +49,7 @@ constexpr int kMinKeysPerSplit = DLC_ATTEND_MIN_KEYS;
 constexpr bool kBf16Partials = DLC_BF16_PARTIALS != 0;
 constexpr int kTargetWorkgroups = DLC_ATTEND_TARGET_WGS;
 
+
 // which keys a query attends to
 constexpr int kDense = 0;   // entries s < min(floor(t/m'), cap)            (HCA)
 constexpr int kGather = 1;  // entries idx[0 .. count-1]                     (CSA)
@@ -452,10 +453,11 @@ __device__ __forceinline__ constexpr int h16_row_off(int r) {
 }
 static_assert(h16_row_off(31) + 1024 <= kTileBytes, "tile layout");
 
-template <int MODE>
-__global__ void __launch_bounds__(512) attend512_kernel(AttArgs a) {
+template <int MODE, int NW>  // NW waves: 16*NW heads per workgroup
+__global__ void __launch_bounds__(64 * NW) attend512_kernel(AttArgs a) {
   constexpr int CD = 512, KS = 16, NT = 32;  // 32-dim Q.K^T steps; 16-dim output tiles
-  constexpr int NST = 4, RPW = 4, HPG = 128;
+  constexpr int NST = 4, RPW = 32 / NW, HPG = 16 * NW;
+  static_assert(NW == 4 || NW == 8, "4 or 8 waves");
   __shared__ __attribute__((aligned(1024))) unsigned char sK[NST * kTileBytes];
   __shared__ int32_t sRow[MODE == kGather ? kMaxGatherKeys : 1];
 
@@ -492,7 +494,7 @@ __global__ void __launch_bounds__(512) attend512_kernel(AttArgs a) {
   asm volatile("" : "+s"(zrow));  // keep the masked-key source in SGPRs
 
   if constexpr (MODE == kGather) {
-    for (int64_t j = tid; j < k1 - k0; j += 512) sRow[j] = int32_t(key_code<kGather>(a, bq, k0 + j, k1, nkm));
+    for (int64_t j = tid; j < k1 - k0; j += 64 * NW) sRow[j] = int32_t(key_code<kGather>(a, bq, k0 + j, k1, nkm));
     __syncthreads();
   }
   const uint32_t lds0 = (uint32_t)(uintptr_t)DLC_LDS(sK);
@@ -975,6 +977,7 @@ bool mfma_ok(int dtype, int64_t c) { return dtype == DLC_BF16 && (c == 128 || c 
 
 struct Plan {
   bool mfma, bf16_parts;  // bf16_parts: the partial outputs are stored in bf16
+  int64_t heads;          // heads per workgroup (MFMA paths)
   int64_t splits, kps, head_groups;
   size_t o_off, l_off, total;
 };
@@ -983,16 +986,31 @@ struct Plan {
 Plan plan(int dtype, int64_t BQ, int64_t n_h, int64_t c, int64_t nkeys, bool merge = false, bool gather = true) {
   Plan p{};
   p.mfma = mfma_ok(dtype, c);
-  p.head_groups = p.mfma ? ceil_div(n_h, 128) : n_h;
-  const int64_t per_split = p.mfma ? BQ * p.head_groups : BQ * n_h;
-  int64_t s = ceil_div(kTargetWorkgroups, per_split);
-  const int64_t smax = ceil_div(nkeys > 0 ? nkeys : 1, kMinKeysPerSplit);
-  s = s < smax ? s : smax;
-  if (gather) {  // a split's row list fits in LDS
-    const int64_t smin = ceil_div(nkeys > 0 ? nkeys : 1, c == 512 ? kMaxGatherKeys : 4096);
-    s = s < smin ? smin : s;
+  const int64_t nk1 = nkeys > 0 ? nkeys : 1;
+  auto split_count = [&](int64_t per_split) {
+    int64_t s = ceil_div(kTargetWorkgroups, per_split);
+    const int64_t smax = ceil_div(nk1, kMinKeysPerSplit);
+    s = s < smax ? s : smax;
+    if (gather) {  // a split's row list fits in LDS
+      const int64_t smin = ceil_div(nk1, c == 512 ? kMaxGatherKeys : 4096);
+      s = s < smin ? smin : s;
+    }
+    return s < 1 ? 1 : (s > kMaxSplits ? kMaxSplits : s);
+  };
+  // c = 512: 128 heads (8 waves) per workgroup, or 64 (4 waves) when the
+  // minimum split length leaves the 128-head grid under half the target and
+  // the smaller groups add workgroups
+  p.heads = p.mfma ? 128 : 1;
+  p.head_groups = p.mfma ? ceil_div(n_h, p.heads) : n_h;
+  int64_t s = split_count(p.mfma ? BQ * p.head_groups : BQ * n_h);
+  if (p.mfma && c == 512 && n_h > 64 && 2 * BQ * p.head_groups * s < kTargetWorkgroups) {
+    const int64_t hg64 = ceil_div(n_h, 64), s64 = split_count(BQ * hg64);
+    if (hg64 * s64 > p.head_groups * s) {
+      p.heads = 64;
+      p.head_groups = hg64;
+      s = s64;
+    }
   }
-  s = s < 1 ? 1 : (s > kMaxSplits ? kMaxSplits : s);
   p.splits = s;
   p.kps = ceil_div(nkeys > 0 ? nkeys : 1, s);
   if (p.mfma) p.kps = ceil_div(p.kps, 32) * 32;
@@ -1047,7 +1065,15 @@ int run_attend(const char* name, int dtype, AttArgs a, int64_t BQ, int64_t nkeys
     dim3 grid{(unsigned)(p.splits * p.head_groups), (unsigned)BQ, 1u};
     if (a.c == 128) hipLaunchKernelGGL((attend_mfma_kernel<128, MODE>), grid, dim3(512), 0, s, a);
     if (a.c == 256) hipLaunchKernelGGL((attend_mfma_kernel<256, MODE>), grid, dim3(512), 0, s, a);
-    if (a.c == 512) hipLaunchKernelGGL((attend512_kernel<MODE>), grid, dim3(512), 0, s, a);
+    if (a.c == 512) {
+      // block x = 8 * (chunk * head_groups + hg) + xcd runs split 8 * chunk +
+      // xcd of head group hg: whole chunks of 8 splits for every head group
+      const dim3 grid8{(unsigned)(ceil_div(p.splits, 8) * 8 * p.head_groups), (unsigned)BQ, 1u};
+      if (p.heads == 64)
+        hipLaunchKernelGGL((attend512_kernel<MODE, 4>), grid8, dim3(256), 0, s, a);
+      else
+        hipLaunchKernelGGL((attend512_kernel<MODE, 8>), grid8, dim3(512), 0, s, a);
+    }
   } else {
     DLC_REQUIRE(a.n_h <= 65535, DLC_E_UNSUPPORTED, "%s: n_h > 65535 on the VALU path", name);
     dim3 grid{(unsigned)p.splits, (unsigned)a.n_h, (unsigned)BQ};

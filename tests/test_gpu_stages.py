@@ -225,6 +225,11 @@ def _random_selection(B, n_q, k, cap, seed, counts):
     ("bf16", 1, 1, 48, 256, 300, 900, [299]),                # heads not a multiple of 32
     ("bf16", 1, 3, 128, 512, 40, 5000, [40, 33, 1]),
     ("bf16", 2, 1, 40, 512, 300, 2000, [300, 129]),           # c = 512 split partials, last head block partial
+    # several head groups and a split count that is not a multiple of 8 (the
+    # c = 512 grid runs splits in chunks of 8 per head group): 64-head groups
+    # (4 groups, 5 splits), then 128-head groups (2 groups, 5 splits)
+    ("bf16", 1, 1, 256, 512, 300, 2000, [300]),
+    ("bf16", 4, 4, 256, 512, 300, 3000, [300, 299, 1, 0, 300, 150, 64, 65, 300, 300, 33, 257, 300, 2, 100, 200]),
 ])
 def test_csa_attend(dtype, B, n_q, n_h, c, k, cap, counts):
     seed = 700 + cap + k
