@@ -131,8 +131,10 @@ __global__ void __launch_bounds__(256) scores_valu_kernel(IdxArgs a) {
 // ring, from where every wave reads its operands.  Key tiles (16 keys,
 // 16*2*c^I bytes) arrive by direct global->LDS loads, one instruction moving
 // 1 KB of consecutive rows, so HBM sees whole lines.  Each wave streams its
-// own tiles through a ring of NS LDS stages with NS-1 tiles in flight, and
-// only it reads them, so the loop has no barrier.  Within a row, 16-byte chunk c is stored at slot
+// own tiles through a ring of NS LDS stages, and only it reads them, so the
+// loop has no barrier.  A tile's operands are read into registers first and
+// its stage refilled right away, so NS tiles are in flight during the
+// compute.  Within a row, 16-byte chunk c is stored at slot
 // c ^ (row % chunks): the 16 rows that one ds_read_b128 pass reads at the
 // same chunk then fall on distinct banks (64 banks of 4 bytes).
 // The scores of kScoreBuf tiles collect in LDS and go out together: vmcnt
@@ -153,11 +155,12 @@ __global__ void __launch_bounds__(256) scores_mfma_kernel(IdxArgs a) {
   __shared__ __attribute__((aligned(1024))) unsigned char sK[4][NS][TILEB];
   __shared__ float sS[4][kScoreBuf * 16];
   const int64_t bq = blockIdx.y;
-  const int64_t nvis = visible(a, bq);
   const int64_t s0 = int64_t(blockIdx.x) * a.keys_per_wg;
-  if (s0 >= nvis) return;
-  const int64_t s1 = min(nvis, s0 + a.keys_per_wg);
-  for (int i = threadIdx.x; i < kBins; i += blockDim.x) hist[i] = 0;
+  // The grid covers floor(t_max/m) <= cap entries, so rows below s1l exist
+  // whatever this query's t: the first tiles go out by that bound, before
+  // t has been read (rows past the query's own visible end are loaded and
+  // scored but neither stored nor counted).
+  const int64_t s1l = min(min(a.t_max / a.m, a.cap), s0 + a.keys_per_wg);
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -166,20 +169,22 @@ __global__ void __launch_bounds__(256) scores_mfma_kernel(IdxArgs a) {
 
   const int64_t b = bq / a.n_q;
   const bf16_raw* K = static_cast<const bf16_raw*>(a.KI) + b * a.cap * cI;
-  const int64_t ntiles = (s1 - s0 + 15) / 16;
   // this wave's tiles: wave, wave+4, ... (the four waves stream one region together)
-  const int64_t my_tiles = ntiles > wave ? (ntiles - wave + 3) / 4 : 0;
+  auto tiles_of_wave = [&](int64_t end) {
+    const int64_t nt = (end - s0 + 15) / 16;
+    return nt > wave ? (nt - wave + 3) / 4 : int64_t(0);
+  };
   // load j of a tile: lane -> row rho = j*RPI + lane/CPR, slot lane%CPR, which
-  // holds chunk slot ^ (rho % CPR) of that row; rows past the chunk's end
-  // repeat its last visible row
+  // holds chunk slot ^ (rho % CPR) of that row; rows past s1l repeat row
+  // s1l - 1
   auto issue = [&](int64_t it, int st) {
-    const int64_t row0 = s0 + (wave + 4 * it) * 16;  // < s1
+    const int64_t row0 = s0 + (wave + 4 * it) * 16;  // < s1l
     const bf16_raw* base = K + row0 * cI;
 #pragma unroll
     for (int j = 0; j < KT; ++j) {
       const int rho = j * RPI + lane / CPR;
       const int chunk = (lane % CPR) ^ (rho % CPR);
-      const int64_t row = min(row0 + rho, s1 - 1);
+      const int64_t row = min(row0 + rho, s1l - 1);
       const uint32_t off = uint32_t((row - row0) * ROWB + chunk * 16);
       const uint32_t lds = (uint32_t)(uintptr_t)DLC_LDS(&sK[wave][st][0]) + uint32_t(j * 1024);
       dma_row(base, off, lds);
@@ -197,9 +202,20 @@ __global__ void __launch_bounds__(256) scores_mfma_kernel(IdxArgs a) {
       dma_row(qg, off, lds);
     }
   }
+  {
+    const int64_t first = tiles_of_wave(s1l);
 #pragma unroll
-  for (int p = 0; p < NS - 1; ++p)
-    if (p < my_tiles) issue(p, p);
+    for (int p = 0; p < NS - 1; ++p)
+      if (p < first) issue(p, p);
+  }
+  const int64_t nvis = visible(a, bq);
+  if (s0 >= nvis) {  // nothing of this chunk is visible to the query (the whole workgroup)
+    wait_vm<0>();
+    return;
+  }
+  const int64_t s1 = min(nvis, s0 + a.keys_per_wg);
+  const int64_t my_tiles = tiles_of_wave(s1);  // <= the tiles issued by s1l
+  for (int i = threadIdx.x; i < kBins; i += blockDim.x) hist[i] = 0;
   float wv[HT][4];
 #pragma unroll
   for (int ht = 0; ht < HT; ++ht)
@@ -231,37 +247,41 @@ __global__ void __launch_bounds__(256) scores_mfma_kernel(IdxArgs a) {
 #pragma unroll
     for (int kt = 0; kt < KT; ++kt) asm volatile("" ::"v"(qf[ht][kt]));
   __syncthreads();  // every wave holds its operands: the last stages may take tiles
+  if (NS - 1 < my_tiles) issue(NS - 1, NS - 1);
 
   for (int64_t it = 0; it < my_tiles; ++it) {
     const int st = int(it % NS);
-    // the stage tile it+NS-1 goes to was read in iteration it-1, whose
-    // fragments have been consumed by its MFMAs
-    const int64_t nxt = it + NS - 1;
-    int after;  // tiles issued after tile it
-    if (nxt < my_tiles) {
-      issue(nxt, int(nxt % NS));
-      after = NS - 1;
-    } else {
-      after = int(my_tiles - 1 - it);
-    }
-    // tile it has landed once at most `after` tiles' loads are outstanding
-    if (after >= NS - 1) wait_vm<(NS - 1) * KT>();
+    // tiles it+1 .. it+NS-1 (those that exist) were issued after tile it;
+    // tile it has landed once at most their loads are outstanding (tiles
+    // issued by s1l past my_tiles only make the wait longer)
+    const int64_t rest = my_tiles - 1 - it;
+    const int after = rest < NS - 1 ? int(rest) : NS - 1;
+    static_assert(NS == 4, "the waits below enumerate three tiles in flight");
+    if (after == 3) wait_vm<3 * KT>();
     else if (after == 2) wait_vm<2 * KT>();
     else if (after == 1) wait_vm<KT>();
     else wait_vm<0>();
     asm volatile("" ::: "memory");
+    // the tile's operands into registers; the stage then takes tile it+NS,
+    // so NS tiles stay in flight while this one is computed
     const unsigned char* tile = &sK[wave][st][0];
+    bf16x8 kb[KT];
+#pragma unroll
+    for (int kt = 0; kt < KT; ++kt) {
+      const int slot = (4 * kt + g) ^ (r16 % CPR);
+      kb[kt] = *reinterpret_cast<const bf16x8*>(tile + r16 * ROWB + slot * 16);
+    }
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the reads are done
+    asm volatile("" ::: "memory");
+    if (it + NS < my_tiles) issue(it + NS, st);
     f32x4 acc[HT];
 #pragma unroll
     for (int ht = 0; ht < HT; ++ht) acc[ht] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int kt = 0; kt < KT; ++kt) {
-      const int slot = (4 * kt + g) ^ (r16 % CPR);
-      const bf16x8 kb = *reinterpret_cast<const bf16x8*>(tile + r16 * ROWB + slot * 16);
+    for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
       for (int ht = 0; ht < HT; ++ht)
-        acc[ht] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qf[ht][kt], kb, acc[ht], 0, 0, 0);
-    }
+        acc[ht] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qf[ht][kt], kb[kt], acc[ht], 0, 0, 0);
     // four independent partial sums (one per head row of the lane), then a tree
     float ps[4];
 #pragma unroll
@@ -292,6 +312,7 @@ __global__ void __launch_bounds__(256) scores_mfma_kernel(IdxArgs a) {
       asm volatile("" ::: "memory");
     }
   }
+  wait_vm<0>();  // tiles issued by s1l that no iteration waited for
   flush_hist(hist, a.hist + bq * kBins);
 }
 
@@ -329,11 +350,10 @@ __global__ void __launch_bounds__(64 * NW) scores_fp4_kernel(IdxArgs a) {
   __shared__ __attribute__((aligned(16))) unsigned char sK[NW][NS][STB];
   __shared__ float sS[NW][kScoreBuf * 16];
   const int64_t bq = blockIdx.y;
-  const int64_t nvis = visible(a, bq);
   const int64_t s0 = int64_t(blockIdx.x) * a.keys_per_wg;
-  if (s0 >= nvis) return;
-  const int64_t s1 = min(nvis, s0 + a.keys_per_wg);
-  for (int i = threadIdx.x; i < kBins; i += blockDim.x) hist[i] = 0;
+  // rows below s1l exist whatever this query's t (as in the bf16 kernel):
+  // the first tiles go out before t has been read
+  const int64_t s1l = min(min(a.t_max / a.m, a.cap), s0 + a.keys_per_wg);
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -341,30 +361,42 @@ __global__ void __launch_bounds__(64 * NW) scores_fp4_kernel(IdxArgs a) {
   const int64_t b = bq / a.n_q;
   const uint8_t* Kc = static_cast<const uint8_t*>(a.KI) + b * a.cap * ROWB;
   const uint8_t* Ks = a.k_scale + b * a.cap * KB;
-  const int64_t ntiles = (s1 - s0 + 15) / 16;
-  const int64_t my_tiles = ntiles > wave ? (ntiles - wave + NW - 1) / NW : 0;
-  // tile it of this wave: rows row0 .. row0+15, those past the chunk's end
-  // repeat its last visible row
+  auto tiles_of_wave = [&](int64_t end) {
+    const int64_t nt = (end - s0 + 15) / 16;
+    return nt > wave ? (nt - wave + NW - 1) / NW : int64_t(0);
+  };
+  // tile it of this wave: rows row0 .. row0+15 (rows past s1l repeat row s1l - 1)
   auto issue = [&](int64_t it, int st) {
-    const int64_t row0 = s0 + (wave + NW * it) * 16;  // < s1
+    const int64_t row0 = s0 + (wave + NW * it) * 16;  // < s1l
     const uint32_t lds = (uint32_t)(uintptr_t)DLC_LDS(&sK[wave][st][0]);
 #pragma unroll
     for (int q = 0; q < NJ; ++q) {
       const int pos = q * 1024 + 16 * lane;
       const int rho = pos / ROWB, slot = (pos % ROWB) / 16;
       const int chunk = slot ^ ((rho / RPB) % CPR);
-      const int64_t row = min(row0 + rho, s1 - 1);
+      const int64_t row = min(row0 + rho, s1l - 1);
       dma_row(Kc + row0 * ROWB, uint32_t((row - row0) * ROWB + chunk * 16), lds + uint32_t(q * 1024));
     }
     if (lane < SLANES) {
       const int rho = 4 * lane / KB;
-      const int64_t row = min(row0 + rho, s1 - 1);
+      const int64_t row = min(row0 + rho, s1l - 1);
       dma_dword(Ks + row0 * KB, uint32_t((row - row0) * KB + (4 * lane) % KB), lds + uint32_t(CODEB));
     }
   };
+  {
+    const int64_t first = tiles_of_wave(s1l);
 #pragma unroll
-  for (int p = 0; p < NS - 1; ++p)
-    if (p < my_tiles) issue(p, p);
+    for (int p = 0; p < NS - 1; ++p)
+      if (p < first) issue(p, p);
+  }
+  const int64_t nvis = visible(a, bq);
+  if (s0 >= nvis) {  // nothing of this chunk is visible to the query (the whole workgroup)
+    wait_vm<0>();
+    return;
+  }
+  const int64_t s1 = min(nvis, s0 + a.keys_per_wg);  // this query's end of the chunk
+  const int64_t my_tiles = tiles_of_wave(s1);         // <= the tiles issued by s1l
+  for (int i = threadIdx.x; i < kBins; i += blockDim.x) hist[i] = 0;
 
   // queries (A operand, rows = heads): head ht*16 + r16, block 4j + g; heads
   // past n_hI take zero codes (their weight is 0 too)
@@ -466,6 +498,7 @@ __global__ void __launch_bounds__(64 * NW) scores_fp4_kernel(IdxArgs a) {
       asm volatile("" ::: "memory");
     }
   }
+  wait_vm<0>();  // tiles issued by s1l that no iteration waited for
   flush_hist(hist, a.hist + bq * kBins);
 }
 
