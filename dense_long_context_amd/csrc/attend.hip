@@ -465,9 +465,21 @@ __global__ void __launch_bounds__(64 * NW) attend512_kernel(AttArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r16 = lane & 15, g = lane >> 4, i16 = lane & 15;
   const int64_t bq = blockIdx.y;
-  const int64_t xcd = blockIdx.x & 7, rest = blockIdx.x >> 3;
-  const int64_t hg = rest % a.head_groups;
-  const int64_t split = (rest / a.head_groups) * 8 + xcd;
+  // block x -> (split, head group hg).  With several head groups and at
+  // least 8 splits, x = 8 * (chunk * head_groups + hg) + xcd runs split
+  // 8 * chunk + xcd (the grid rounded to whole chunks), so the head groups
+  // of a split are dispatched to one XCD and share its L2; otherwise x =
+  // split * head_groups + hg (with one head group, consecutive splits go to
+  // consecutive XCDs)
+  int64_t hg, split;
+  if (a.head_groups > 1 && a.splits >= 8) {
+    const int64_t xcd = blockIdx.x & 7, rest = blockIdx.x >> 3;
+    hg = rest % a.head_groups;
+    split = (rest / a.head_groups) * 8 + xcd;
+  } else {
+    split = blockIdx.x / a.head_groups;
+    hg = blockIdx.x - split * a.head_groups;
+  }
   if (split >= a.splits) return;
   const int64_t b = bq / a.n_q;
   const int64_t nkm = n_keys<MODE>(a, bq);
@@ -1066,9 +1078,11 @@ int run_attend(const char* name, int dtype, AttArgs a, int64_t BQ, int64_t nkeys
     if (a.c == 128) hipLaunchKernelGGL((attend_mfma_kernel<128, MODE>), grid, dim3(512), 0, s, a);
     if (a.c == 256) hipLaunchKernelGGL((attend_mfma_kernel<256, MODE>), grid, dim3(512), 0, s, a);
     if (a.c == 512) {
-      // block x = 8 * (chunk * head_groups + hg) + xcd runs split 8 * chunk +
-      // xcd of head group hg: whole chunks of 8 splits for every head group
-      const dim3 grid8{(unsigned)(ceil_div(p.splits, 8) * 8 * p.head_groups), (unsigned)BQ, 1u};
+      // several head groups and >= 8 splits: whole chunks of 8 splits for
+      // every head group (the kernel's block mapping)
+      const int64_t gx = p.head_groups > 1 && p.splits >= 8 ? ceil_div(p.splits, 8) * 8 * p.head_groups
+                                                             : p.splits * p.head_groups;
+      const dim3 grid8{(unsigned)gx, (unsigned)BQ, 1u};
       if (p.heads == 64)
         hipLaunchKernelGGL((attend512_kernel<MODE, 4>), grid8, dim3(256), 0, s, a);
       else
