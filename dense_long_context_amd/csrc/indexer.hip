@@ -73,6 +73,13 @@ __device__ __forceinline__ int64_t visible(const IdxArgs& a, int64_t bq) {
 
 __device__ __forceinline__ float canon_zero(float s) { return s == 0.f ? 0.f : s; }
 
+// ReLU of an MFMA result in one instruction: v_med3_f32(x, 0, 3e38) is x for
+// 0 <= x <= 3e38 and 0 below (a signed zero may come out as -0, which the
+// final canon_zero maps to +0).  fmaxf(x, 0), or a median with +inf (which
+// the compiler folds into that max), costs two: the compiler first
+// canonicalises x for the IEEE max.
+__device__ __forceinline__ float relu(float x) { return __builtin_amdgcn_fmed3f(x, 0.f, 3.0e38f); }
+
 // LDS histogram of the first digit -> the query's global histogram
 __device__ __forceinline__ void flush_hist(uint32_t* lds, uint32_t* global) {
   __syncthreads();
@@ -286,9 +293,9 @@ __global__ void __launch_bounds__(256) scores_mfma_kernel(IdxArgs a) {
     float ps[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      ps[r] = wv[0][r] * fmaxf(acc[0][r], 0.f);
+      ps[r] = wv[0][r] * relu(acc[0][r]);
 #pragma unroll
-      for (int ht = 1; ht < HT; ++ht) ps[r] = fmaf(wv[ht][r], fmaxf(acc[ht][r], 0.f), ps[r]);
+      for (int ht = 1; ht < HT; ++ht) ps[r] = fmaf(wv[ht][r], relu(acc[ht][r]), ps[r]);
     }
     const float part = rows4_sum((ps[0] + ps[1]) + (ps[2] + ps[3]));
     const int64_t s = s0 + (wave + 4 * it) * 16 + r16;
@@ -474,9 +481,9 @@ __global__ void __launch_bounds__(64 * NW) scores_fp4_kernel(IdxArgs a) {
     float ps[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      ps[r] = wv[0][r] * fmaxf(acc[0][r], 0.f);
+      ps[r] = wv[0][r] * relu(acc[0][r]);
 #pragma unroll
-      for (int ht = 1; ht < HT; ++ht) ps[r] = fmaf(wv[ht][r], fmaxf(acc[ht][r], 0.f), ps[r]);
+      for (int ht = 1; ht < HT; ++ht) ps[r] = fmaf(wv[ht][r], relu(acc[ht][r]), ps[r]);
     }
     const float part = rows4_sum((ps[0] + ps[1]) + (ps[2] + ps[3]));
     const int64_t s = s0 + (wave + NW * it) * 16 + r16;
@@ -635,7 +642,7 @@ __global__ void __launch_bounds__(512) scores_prefill_kernel(IdxArgs a) {
 #pragma unroll
       for (int e = 0; e < 4; ++e)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) sc[j][4 * r4 + e] = fmaf(wv[e], fmaxf(S[j][4 * r4 + e], 0.f), sc[j][4 * r4 + e]);
+        for (int j = 0; j < 2; ++j) sc[j][4 * r4 + e] = fmaf(wv[e], relu(S[j][4 * r4 + e]), sc[j][4 * r4 + e]);
     }
   };
   // heads in groups of HPS (one barrier per group); the epilogue of each
@@ -802,7 +809,7 @@ __global__ void __launch_bounds__(512) scores_prefill_fp4_kernel(IdxArgs a) {
 #pragma unroll
       for (int e = 0; e < 4; ++e)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) sc[j][4 * r4 + e] = fmaf(wv[e], fmaxf(S[j][4 * r4 + e], 0.f), sc[j][4 * r4 + e]);
+        for (int j = 0; j < 2; ++j) sc[j][4 * r4 + e] = fmaf(wv[e], relu(S[j][4 * r4 + e]), sc[j][4 * r4 + e]);
     }
   };
   f32x16 Sa[2], Sb[2];
