@@ -25,6 +25,7 @@
 //                 the second histogram, and merges the two ascending lists into
 //                 idx / count.
 #include "common.hpp"
+#include "mxfp4.hpp"
 
 namespace dlc {
 namespace {
@@ -507,6 +508,29 @@ __global__ void __launch_bounds__(64 * NW) scores_fp4_kernel(IdxArgs a) {
   }
   wait_vm<0>();  // tiles issued by s1l that no iteration waited for
   flush_hist(hist, a.hist + bq * kBins);
+}
+
+// The FP4 call's preparation in one launch: blocks below fill_blocks clear
+// the histograms; the others quantize the queries, one 32-element block per
+// thread, with the encoding of mxfp4_quantize (codes [rows][c^I/2], scales
+// [rows][c^I/32]).
+template <typename T>
+__global__ void __launch_bounds__(256) prep_fp4_kernel(uint32_t* hist, int64_t nhist, int fill_blocks, const T* q,
+                                                       int64_t qblocks, int64_t bpr, uint8_t* codes,
+                                                       uint8_t* scales) {
+  if (int(blockIdx.x) < fill_blocks) {
+    for (int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x; i < nhist; i += int64_t(fill_blocks) * 256) hist[i] = 0;
+    return;
+  }
+  const int64_t i = int64_t(blockIdx.x - fill_blocks) * 256 + threadIdx.x;
+  if (i >= qblocks) return;
+  const int64_t r = i / bpr, j = i % bpr;
+  float v[32];
+  load32<T>(q + (r * bpr + j) * 32, v);
+  uint32_t e8;
+  const uint4 c = mxfp4_encode32(v, e8);
+  *reinterpret_cast<uint4*>(codes + (r * bpr + j) * 16) = c;
+  scales[r * bpr + j] = uint8_t(e8);
 }
 
 // ---------------------------------------------------------------- scores (prefill)
@@ -1518,13 +1542,19 @@ int csa_index_topk_fp4(int dtype, int64_t B, int64_t n_q, int64_t n_hI, int64_t 
   uint8_t* qsc = static_cast<uint8_t*>(ws) + W.scale;
   a.q_code = qc; a.q_scale = qsc;
 
-  int rc = fill_u32(a.hist, 0, int64_t(BQ * kBins * 2), s);
-  if (rc) return rc;
+  int rc;
   const int64_t vis_max = t_max / m;
-  if (vis_max > 0) {
-    const int64_t rows = BQ * n_hI;
-    if ((rc = mxfp4_quantize(dtype, 1, rows, cI, qI, rows * cI, qc, rows * cI / 2, qsc, rows * cI / 32, stream)))
-      return rc;
+  if (vis_max > 0) {  // histograms cleared and queries quantized by one launch
+    const int64_t nhist = BQ * kBins * 2, qblocks = BQ * n_hI * (cI / 32);
+    const int fill_blocks = int(std::min<int64_t>(ceil_div(nhist, 1024), 256));
+    const dim3 pgrid{unsigned(fill_blocks + ceil_div(qblocks, 256)), 1u, 1u};
+    if (dtype == DLC_BF16)
+      hipLaunchKernelGGL(prep_fp4_kernel<bf16_raw>, pgrid, dim3(256), 0, s, a.hist, nhist, fill_blocks,
+                         static_cast<const bf16_raw*>(qI), qblocks, cI / 32, qc, qsc);
+    else
+      hipLaunchKernelGGL(prep_fp4_kernel<float>, pgrid, dim3(256), 0, s, a.hist, nhist, fill_blocks,
+                         static_cast<const float*>(qI), qblocks, cI / 32, qc, qsc);
+    if ((rc = check_launch("csa_index_topk_fp4/prep"))) return rc;
     a.keys_per_wg = keys_per_wg(BQ, vis_max);
     dim3 grid{(unsigned)ceil_div(vis_max, a.keys_per_wg), (unsigned)BQ, 1u};
     StageTimer timer(DLC_STAGE_INDEX_SCORES, s);
@@ -1542,6 +1572,8 @@ int csa_index_topk_fp4(int dtype, int64_t B, int64_t n_q, int64_t n_hI, int64_t 
       hipLaunchKernelGGL(hist_kernel, grid, dim3(256), 0, s, a);
       if ((rc = check_launch("csa_index_topk_fp4/hist"))) return rc;
     }
+  } else if ((rc = fill_u32(a.hist, 0, int64_t(BQ * kBins * 2), s))) {
+    return rc;
   }
   return select_topk(a, BQ, vis_max, s);
 }
