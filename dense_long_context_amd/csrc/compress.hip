@@ -21,6 +21,12 @@ namespace {
 #define DLC_POOL_CHUNK 4
 #endif
 constexpr int kChunk = DLC_POOL_CHUNK;
+// CSA entries per thread on the full-pass path (a window of 2m rows is only
+// two chunks: one entry alone is too little work for a wave's start-up)
+#ifndef DLC_POOL_EPT
+#define DLC_POOL_EPT 2
+#endif
+constexpr int64_t kEntriesPerThread = DLC_POOL_EPT;
 constexpr float kLog2e = 1.4426950408889634f;
 
 struct PoolArgs {
@@ -31,6 +37,7 @@ struct PoolArgs {
   int64_t c, m;          // width, window rows per segment (m or m')
   int64_t i_begin, n_entries;
   int64_t col_groups;
+  int64_t ept;           // entries per thread (R = 1 path): consecutive entries, folded in turn
   void* out;
   int64_t cap;
 };
@@ -130,65 +137,80 @@ __device__ __forceinline__ void merge_state(float* mS, float* sS, float* aS, con
 template <typename T, int VEC, bool OVERLAP, int R>
 __global__ void __launch_bounds__(256) pool_kernel(PoolArgs a) {
   const int64_t t = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
-  const int q = int(t % R);
-  const int64_t eg = t / R;
-  const bool live = eg < a.n_entries * a.col_groups;
-  const int64_t e = live ? eg / a.col_groups : 0;
-  const int64_t j0 = (eg - e * a.col_groups) * VEC;
-  const int64_t i = a.i_begin + e;
   const int64_t boff = int64_t(blockIdx.y) * a.batch_stride;
-  const int rows = int((OVERLAP && i > 0) ? 2 * a.m : a.m);  // i = 0 has no b-rows
-
-  float mx[VEC], sum[VEC], acc[VEC];
-  if constexpr (R == 1) {
+  auto store = [&](int64_t i, int64_t j0, const float* acc, const float* sum) {
+    float o[VEC];
 #pragma unroll
-    for (int u = 0; u < VEC; ++u) { mx[u] = -INFINITY; sum[u] = 0.f; acc[u] = 0.f; }
-    if (live) {
+    for (int u = 0; u < VEC; ++u) o[u] = acc[u] / sum[u];
+    T* out = static_cast<T*>(a.out) + (int64_t(blockIdx.y) * a.cap + i) * a.c + j0;
+    if constexpr (VEC == 1) {
+      Fmt<T>::store(out, o[0]);
+    } else {
+      Fmt<T>::store_vec(out, o);
+    }
+  };
+  if constexpr (R == 1) {
+    // thread (entry group, column group): entries ept*g .. ept*g + ept-1 in
+    // turn (a wave still covers one entry's column groups at a time)
+    const int64_t groups = ceil_div(a.n_entries, a.ept);
+    if (t >= groups * a.col_groups) return;
+    const int64_t eg = t / a.col_groups;
+    const int64_t j0 = (t - eg * a.col_groups) * VEC;
+    for (int64_t e = eg * a.ept; e < min(a.n_entries, (eg + 1) * a.ept); ++e) {
+      const int64_t i = a.i_begin + e;
+      const int rows = int((OVERLAP && i > 0) ? 2 * a.m : a.m);  // i = 0 has no b-rows
+      float mx[VEC], sum[VEC], acc[VEC];
+#pragma unroll
+      for (int u = 0; u < VEC; ++u) { mx[u] = -INFINITY; sum[u] = 0.f; acc[u] = 0.f; }
       for (int r0 = 0; r0 < rows; r0 += kChunk) {
         float pm[VEC], ps[VEC], pa[VEC];
         chunk_partial<T, VEC>(a, boff, i, r0, min(rows, r0 + kChunk), j0, pm, ps, pa);
         merge_state<VEC>(mx, sum, acc, pm, ps, pa);
       }
+      store(i, j0, acc, sum);
     }
   } else {
-    float pm[VEC], ps[VEC], pa[VEC];
-    const int r0 = q * kChunk;
-    if (live && r0 < rows) {
-      chunk_partial<T, VEC>(a, boff, i, r0, min(rows, r0 + kChunk), j0, pm, ps, pa);
-    } else {
+    const int q = int(t % R);
+    const int64_t eg = t / R;
+    const bool live = eg < a.n_entries * a.col_groups;
+    const int64_t e = live ? eg / a.col_groups : 0;
+    const int64_t j0 = (eg - e * a.col_groups) * VEC;
+    const int64_t i = a.i_begin + e;
+    const int rows = int((OVERLAP && i > 0) ? 2 * a.m : a.m);  // i = 0 has no b-rows
+    float mx[VEC], sum[VEC], acc[VEC];
+    {
+      float pm[VEC], ps[VEC], pa[VEC];
+      const int r0 = q * kChunk;
+      if (live && r0 < rows) {
+        chunk_partial<T, VEC>(a, boff, i, r0, min(rows, r0 + kChunk), j0, pm, ps, pa);
+      } else {
 #pragma unroll
-      for (int u = 0; u < VEC; ++u) { pm[u] = -INFINITY; ps[u] = 0.f; pa[u] = 0.f; }
-    }
-#pragma unroll
-    for (int u = 0; u < VEC; ++u) { mx[u] = -INFINITY; sum[u] = 0.f; acc[u] = 0.f; }
-    const int base = int(threadIdx.x & 63) & ~(R - 1);  // lane of chunk 0
-#pragma unroll 1
-    for (int k = 0; k < R; ++k) {
-      float km[VEC], ks[VEC], ka[VEC];
-#pragma unroll
-      for (int u = 0; u < VEC; ++u) {
-        km[u] = __shfl(pm[u], base + k);
-        ks[u] = __shfl(ps[u], base + k);
-        ka[u] = __shfl(pa[u], base + k);
+        for (int u = 0; u < VEC; ++u) { pm[u] = -INFINITY; ps[u] = 0.f; pa[u] = 0.f; }
       }
-      merge_state<VEC>(mx, sum, acc, km, ks, ka);
-    }
-  }
-  if (!live || q != 0) return;
-  float o[VEC];
 #pragma unroll
-  for (int u = 0; u < VEC; ++u) o[u] = acc[u] / sum[u];
-  T* out = static_cast<T*>(a.out) + (int64_t(blockIdx.y) * a.cap + i) * a.c + j0;
-  if constexpr (VEC == 1) {
-    Fmt<T>::store(out, o[0]);
-  } else {
-    Fmt<T>::store_vec(out, o);
+      for (int u = 0; u < VEC; ++u) { mx[u] = -INFINITY; sum[u] = 0.f; acc[u] = 0.f; }
+      const int base = int(threadIdx.x & 63) & ~(R - 1);  // lane of chunk 0
+#pragma unroll 1
+      for (int k = 0; k < R; ++k) {
+        float km[VEC], ks[VEC], ka[VEC];
+#pragma unroll
+        for (int u = 0; u < VEC; ++u) {
+          km[u] = __shfl(pm[u], base + k);
+          ks[u] = __shfl(ps[u], base + k);
+          ka[u] = __shfl(pa[u], base + k);
+        }
+        merge_state<VEC>(mx, sum, acc, km, ks, ka);
+      }
+    }
+    if (!live || q != 0) return;
+    store(i, j0, acc, sum);
   }
 }
 
 template <typename T, int VEC, int R>
 int launch_pool_r(PoolArgs a, bool overlap, int64_t B, hipStream_t s) {
-  const int64_t threads = a.n_entries * a.col_groups * R;
+  a.ept = R == 1 && overlap ? kEntriesPerThread : 1;
+  const int64_t threads = (R == 1 ? ceil_div(a.n_entries, a.ept) : a.n_entries) * a.col_groups * R;
   const int64_t blocks = ceil_div(threads, 256);
   DLC_REQUIRE(blocks < (int64_t(1) << 31) && B <= 65535, DLC_E_UNSUPPORTED, "compress: grid too large");
   dim3 grid{(unsigned)blocks, (unsigned)B, 1u};
