@@ -22,7 +22,10 @@
 //    double-buffered.
 //  * c = 512 (attend512_kernel): 16 heads per wave over all 512 dims, a
 //    four-buffer tile ring with P.V of one tile interleaved with Q.K^T of the
-//    next, and bf16 split-K partials (described at the kernel).
+//    next, and bf16 split-K partials written in MFMA fragment order
+//    (described at the kernel, merged by combine_frag_kernel).  A workgroup
+//    is 8 waves (128 heads), or 4 waves (64 heads) when the minimum split
+//    length leaves the 128-head grid under half the target.
 // The VALU path covers fp32 and other shapes.
 #include "common.hpp"
 
