@@ -877,7 +877,34 @@ __global__ void __launch_bounds__(256) hist_kernel(IdxArgs a) {
   for (int i = threadIdx.x; i < kBins; i += blockDim.x) hist[i] = 0;
   __syncthreads();
   const float* sc = a.scores + bq * a.score_ld;
-  for (int64_t s = s0 + threadIdx.x; s < s1; s += blockDim.x) atomicAdd(&hist[order_key(sc[s]) >> kShift1], 1u);
+  // 16 scores a thread per round (four 16-byte loads in flight together;
+  // one at a time, the loop was load-latency bound); the scalar head and
+  // tail of a misaligned or ragged chunk one by one
+  auto count = [&](float x) { atomicAdd(&hist[order_key(x) >> kShift1], 1u); };
+  // first 16-byte aligned score at or after s0
+  int64_t a0 = s0 + int64_t(((16u - uint32_t(reinterpret_cast<uintptr_t>(sc + s0) & 15u)) & 15u) / 4u);
+  if (a0 > s1) a0 = s1;
+  for (int64_t s = s0 + threadIdx.x; s < a0; s += blockDim.x) count(sc[s]);
+  const int64_t nv4 = (s1 - a0) / 4;
+  const float4* p4 = reinterpret_cast<const float4*>(sc + a0);
+  for (int64_t v0 = threadIdx.x; v0 < nv4; v0 += 4 * blockDim.x) {
+    float4 x[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int64_t v = v0 + u * blockDim.x;
+      x[u] = p4[v < nv4 ? v : nv4 - 1];
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      if (v0 + u * blockDim.x < nv4) {
+        count(x[u].x);
+        count(x[u].y);
+        count(x[u].z);
+        count(x[u].w);
+      }
+    }
+  }
+  for (int64_t s = a0 + nv4 * 4 + threadIdx.x; s < s1; s += blockDim.x) count(sc[s]);
   flush_hist(hist, a.hist + bq * kBins);
 }
 
@@ -1034,7 +1061,7 @@ __global__ void __launch_bounds__(256) filter_kernel(IdxArgs a) {
   if (keff == nvis || s0 >= nvis) return;  // keep-all and empty chunks need no filtering
   const int64_t s1 = min(nvis, s0 + a.keys_per_wg);
   const float* sc = a.scores + bq * a.score_ld;
-  // the first batch of scores is in flight while the threshold is found
+  // the first batches of scores are in flight while the threshold is found
   auto load4 = [&](int64_t base, float* v) {
     const int64_t s = base + 4 * threadIdx.x;
     if (s + 3 < s1 && (reinterpret_cast<uintptr_t>(sc + s) & 15) == 0) {
@@ -1045,8 +1072,12 @@ __global__ void __launch_bounds__(256) filter_kernel(IdxArgs a) {
       for (int e = 0; e < 4; ++e) v[e] = s + e < s1 ? sc[s + e] : 0.f;
     }
   };
-  float v[4];
-  load4(s0, v);
+  // a ring of FD batches in registers: batch i+FD is loaded as batch i is
+  // used (one batch at a time, the loop was load-latency bound)
+  constexpr int FD = 4;
+  float vb[FD][4];
+#pragma unroll
+  for (int d = 0; d < FD; ++d) load4(s0 + int64_t(d) * 4 * blockDim.x, vb[d]);
   // thread j holds first-digit bins 8j .. 8j+7 (two 16-byte loads)
   uint32_t hv[8];
   {
@@ -1064,33 +1095,42 @@ __global__ void __launch_bounds__(256) filter_kernel(IdxArgs a) {
   int32_t* cand = a.cand + bq * a.cap + s0;
   uint32_t* ckey = a.cand_kseg + bq * a.cap + s0;
   uint32_t nsel = 0, ncand = 0;
-  for (int64_t base = s0; base < s1; base += 4 * blockDim.x) {
-    if (base != s0) load4(base, v);
-    const int64_t sb = base + 4 * threadIdx.x;
-    uint32_t key[4], packed = 0;
-    int d[4];
+  const int64_t step = 4 * int64_t(blockDim.x);
+  for (int64_t round = s0; round < s1; round += FD * step) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      key[e] = order_key(v[e]);
-      d[e] = sb + e < s1 ? int(key[e] >> kShift1) : -1;
-      packed += d[e] > T ? 1u : 0u;
-      packed += d[e] == T ? 0x10000u : 0u;
-    }
-    uint32_t tot;
-    const uint32_t ex = scan256(packed, wsum, &tot);
-    uint32_t ps = nsel + (ex & 0xffffu), pc = ncand + (ex >> 16);
+    for (int dd = 0; dd < FD; ++dd) {
+      const int64_t base = round + dd * step;
+      if (base >= s1) break;  // uniform
+      float v[4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      if (d[e] > T) sel[ps++] = int32_t(sb + e);
-      if (d[e] == T) {
-        cand[pc] = int32_t(sb + e);
-        ckey[pc] = key[e];
-        ++pc;
-        atomicAdd(&h2[(key[e] >> 10) & 0x7ffu], 1u);
+      for (int e = 0; e < 4; ++e) v[e] = vb[dd][e];
+      load4(base + FD * step, vb[dd]);  // past s1: zeros, no access
+      const int64_t sb = base + 4 * threadIdx.x;
+      uint32_t key[4], packed = 0;
+      int d[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        key[e] = order_key(v[e]);
+        d[e] = sb + e < s1 ? int(key[e] >> kShift1) : -1;
+        packed += d[e] > T ? 1u : 0u;
+        packed += d[e] == T ? 0x10000u : 0u;
       }
+      uint32_t tot;
+      const uint32_t ex = scan256(packed, wsum, &tot);
+      uint32_t ps = nsel + (ex & 0xffffu), pc = ncand + (ex >> 16);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if (d[e] > T) sel[ps++] = int32_t(sb + e);
+        if (d[e] == T) {
+          cand[pc] = int32_t(sb + e);
+          ckey[pc] = key[e];
+          ++pc;
+          atomicAdd(&h2[(key[e] >> 10) & 0x7ffu], 1u);
+        }
+      }
+      nsel += tot & 0xffffu;
+      ncand += tot >> 16;
     }
-    nsel += tot & 0xffffu;
-    ncand += tot >> 16;
   }
   flush_hist(h2, a.hist2 + bq * kBins);
   if (threadIdx.x == 0) {
