@@ -1376,6 +1376,9 @@ struct WsLayout {
 #define DLC_SCORES_WGS 512
 #endif
 constexpr int64_t kScoreWorkgroups = DLC_SCORES_WGS;
+// query-tiled (prefill) calls: the chunks of the histogram and filter
+// kernels, sized for eight 256-thread workgroups per CU
+constexpr int64_t kSelectWorkgroups = 2048;
 // queries per sequence from which the indexer runs query-tiled (prefill)
 #ifndef DLC_PREFILL_MIN_Q
 #define DLC_PREFILL_MIN_Q 64
@@ -1387,9 +1390,12 @@ constexpr int64_t kPrefillMinQueries = DLC_PREFILL_MIN_Q;
 #ifndef DLC_FP4_NW
 #define DLC_FP4_NW 8  // waves per workgroup of the FP4 scores kernel
 #endif
-int64_t keys_per_wg(int64_t BQ, int64_t vis_max) {
+// wgs: the workgroups the batch should take (kScoreWorkgroups for the
+// decode scores kernel, which shares its chunks with the selection;
+// kSelectWorkgroups when only the histogram and filter kernels use them)
+int64_t keys_per_wg(int64_t BQ, int64_t vis_max, int64_t wgs = kScoreWorkgroups) {
   const int64_t vis = vis_max > 0 ? vis_max : 1;
-  int64_t kpw = ceil_div(ceil_div(vis * BQ, kScoreWorkgroups), 64) * 64;
+  int64_t kpw = ceil_div(ceil_div(vis * BQ, wgs), 64) * 64;
   kpw = kpw < 64 ? 64 : kpw;
   const int64_t floor_kpw = ceil_div(ceil_div(vis, kMaxChunks), 64) * 64;
   return kpw > floor_kpw ? kpw : floor_kpw;
@@ -1509,10 +1515,10 @@ int csa_index_topk(int dtype, int64_t B, int64_t n_q, int64_t n_hI, int64_t cI, 
   if (vis_max > 0) {
     const bool mfma = mfma_shape && aligned(qI, 16) && aligned(KI, 16);
     DLC_REQUIRE(mfma || n_hI * cI <= 8192, DLC_E_UNSUPPORTED, "csa_index_topk: MFMA shape needs 16-byte alignment");
-    a.keys_per_wg = keys_per_wg(BQ, vis_max);
+    const bool prefill = mfma && cI == 128 && n_q >= kPrefillMinQueries;
+    a.keys_per_wg = keys_per_wg(BQ, vis_max, prefill ? kSelectWorkgroups : kScoreWorkgroups);
     const int64_t nchunks = ceil_div(vis_max, a.keys_per_wg);
     dim3 grid{(unsigned)nchunks, (unsigned)BQ, 1u};
-    const bool prefill = mfma && cI == 128 && n_q >= kPrefillMinQueries;
     {
     StageTimer timer(DLC_STAGE_INDEX_SCORES, s);
     if (prefill) {
@@ -1595,10 +1601,10 @@ int csa_index_topk_fp4(int dtype, int64_t B, int64_t n_q, int64_t n_hI, int64_t 
       hipLaunchKernelGGL(prep_fp4_kernel<float>, pgrid, dim3(256), 0, s, a.hist, nhist, fill_blocks,
                          static_cast<const float*>(qI), qblocks, cI / 32, qc, qsc);
     if ((rc = check_launch("csa_index_topk_fp4/prep"))) return rc;
-    a.keys_per_wg = keys_per_wg(BQ, vis_max);
+    const bool prefill = cI == 128 && n_q >= kPrefillMinQueries;
+    a.keys_per_wg = keys_per_wg(BQ, vis_max, prefill ? kSelectWorkgroups : kScoreWorkgroups);
     dim3 grid{(unsigned)ceil_div(vis_max, a.keys_per_wg), (unsigned)BQ, 1u};
     StageTimer timer(DLC_STAGE_INDEX_SCORES, s);
-    const bool prefill = cI == 128 && n_q >= kPrefillMinQueries;
     if (prefill) {
       dim3 pgrid{(unsigned)ceil_div(vis_max, 256), (unsigned)ceil_div(n_q, 64), (unsigned)B};
       hipLaunchKernelGGL((scores_prefill_fp4_kernel<128>), pgrid, dim3(512), 0, s, a);
