@@ -97,6 +97,24 @@ __device__ __forceinline__ uint32_t order_key(float f) {
 // two copies of the value, so combining the two results pairs every lane with
 // its partner 16 (then 32) lanes away.  Plain VALU, unlike ds_bpermute, which
 // queues behind LDS reads.  The sum adds (row0 + row1) + (row2 + row3).
+// Inclusive prefix sum over the 64 lanes of a wave in six DPP adds: row_shr
+// 1, 2, 4, 8 within each 16-lane row, then row_bcast:15 (row r's last lane
+// into row r+1, rows 1 and 3) and row_bcast:31 (lane 31 into rows 2 and 3).
+// Lanes without a source add the old value 0.  The whole wave must be active.
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
+  v += uint32_t(__builtin_amdgcn_update_dpp(0, int(v), 0x111, 0xf, 0xf, false));  // row_shr:1
+  v += uint32_t(__builtin_amdgcn_update_dpp(0, int(v), 0x112, 0xf, 0xf, false));  // row_shr:2
+  v += uint32_t(__builtin_amdgcn_update_dpp(0, int(v), 0x114, 0xf, 0xf, false));  // row_shr:4
+  v += uint32_t(__builtin_amdgcn_update_dpp(0, int(v), 0x118, 0xf, 0xf, false));  // row_shr:8
+  v += uint32_t(__builtin_amdgcn_update_dpp(0, int(v), 0x142, 0xa, 0xf, false));  // row_bcast:15
+  v += uint32_t(__builtin_amdgcn_update_dpp(0, int(v), 0x143, 0xc, 0xf, false));  // row_bcast:31
+  return v;
+}
+// the wave's total of an inclusive scan (lane 63)
+__device__ __forceinline__ uint32_t wave_total(uint32_t incl) {
+  return uint32_t(__builtin_amdgcn_readlane(int(incl), 63));
+}
+
 __device__ __forceinline__ float rows4_max(float v) {
   const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
   v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));

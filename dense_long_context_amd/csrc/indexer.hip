@@ -924,13 +924,9 @@ __device__ void find_threshold(const uint32_t* h, int nbins, uint32_t need, uint
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nwaves = blockDim.x >> 6;
   uint32_t mine = 0;
   for (int i = 0; i < per; ++i) mine += h[lo + i];
-  // inclusive suffix sum within the wave (lanes above this one)
-  uint32_t suf = mine;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const uint32_t v = __shfl_down(suf, off);
-    if (lane + off < 64) suf += v;
-  }
+  // inclusive suffix sum within the wave (this lane and those above it)
+  const uint32_t pre = wave_incl_scan(mine);
+  const uint32_t suf = wave_total(pre) - pre + mine;
   if (lane == 0) scratch[wave] = suf;  // the wave's total
   if (threadIdx.x == 0) {              // defaults if no bin qualifies (inconsistent counts)
     scratch[16] = 0;
@@ -966,12 +962,8 @@ __device__ void find_threshold_regs(const uint32_t (&v)[PER], uint32_t need, uin
   uint32_t mine = 0;
 #pragma unroll
   for (int i = 0; i < PER; ++i) mine += v[i];
-  uint32_t suf = mine;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const uint32_t x = __shfl_down(suf, off);
-    if (lane + off < 64) suf += x;
-  }
+  const uint32_t pre = wave_incl_scan(mine);
+  const uint32_t suf = wave_total(pre) - pre + mine;
   if (lane == 0) scratch[wave] = suf;
   if (threadIdx.x == 0) {
     scratch[16] = 0;
@@ -1020,12 +1012,7 @@ __device__ __forceinline__ uint32_t block_rank(bool pred, uint32_t* wtot, uint32
 // returns the block total.  wsum holds 4 words.  Ends synchronised.
 __device__ __forceinline__ uint32_t scan256(uint32_t v, uint32_t* wsum, uint32_t* total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  uint32_t inc = v;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const uint32_t t = __shfl_up(inc, off);
-    if (lane >= off) inc += t;
-  }
+  const uint32_t inc = wave_incl_scan(v);
   if (lane == 63) wsum[wave] = inc;
   __syncthreads();
   uint32_t before = 0, all = 0;
@@ -1168,15 +1155,7 @@ __device__ void block_exclusive_scan2(uint32_t* v, uint32_t* w, int n, uint32_t*
     mv += v[i];
     mw += w[i];
   }
-  uint32_t iv = mv, iw = mw;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const uint32_t a = __shfl_up(iv, off), b = __shfl_up(iw, off);
-    if (lane >= off) {
-      iv += a;
-      iw += b;
-    }
-  }
+  const uint32_t iv = wave_incl_scan(mv), iw = wave_incl_scan(mw);
   if (lane == 63) {
     wsum[wave] = iv;
     wsum[nwaves + wave] = iw;
