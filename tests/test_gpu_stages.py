@@ -138,6 +138,7 @@ def test_index_topk(dtype, B, n_q, n_hI, cI, m, k, cap, ts):
     (2, 100, 64, 4, 100, 3000, 1),      # two query tiles (64 + 36), mixed visibilities
     (1, 64, 20, 2, 50, 700, 2),         # 20 heads, one full tile
     (3, 70, 64, 4, 1024, 2000, 3),      # k >= visible for most queries
+    (2, 66, 64, 4, 200, 1001, 4),       # cap % 4 != 0: score rows not 16-byte aligned (scalar head and tail)
 ])
 def test_index_topk_prefill(B, n_q, n_hI, m, k, cap, seed):
     """Many queries per sequence: the query-tiled MFMA scores kernel and the
