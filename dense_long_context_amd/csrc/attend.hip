@@ -25,7 +25,10 @@
 //    next, and bf16 split-K partials written in MFMA fragment order
 //    (described at the kernel, merged by combine_frag_kernel).  A workgroup
 //    is 8 waves (128 heads), or 4 waves (64 heads) when the minimum split
-//    length leaves the 128-head grid under half the target.
+//    length leaves the 128-head grid under half the target.  Over dense keys
+//    (HCA) the 8-wave kernel runs in its HD form: the softmax stays per head,
+//    P is exchanged through LDS and each wave owns a 64-dim slice of O for
+//    every head, so the LDS reads per tile drop from 64 KB to 44 KB a wave.
 // The VALU path covers fp32 and other shapes.
 #include "common.hpp"
 
@@ -51,6 +54,16 @@ constexpr int kMinKeysPerSplit = DLC_ATTEND_MIN_KEYS;
 #endif
 constexpr bool kBf16Partials = DLC_BF16_PARTIALS != 0;
 constexpr int kTargetWorkgroups = DLC_ATTEND_TARGET_WGS;
+// the HD form of the c = 512 kernel for dense keys (eight waves; with the
+// window's ring arithmetic it would spill a register), for splits of at
+// least kHdMinKeys keys: its two extra barriers and the per-tile flag reads
+// are a fixed cost that a short (decode) split does not win back
+#ifndef DLC_ATTEND_HD
+#define DLC_ATTEND_HD 1
+#endif
+constexpr bool kHeadsDims = DLC_ATTEND_HD != 0;
+constexpr int64_t kHdMinKeys = 1024;
+
 
 
 // which keys a query attends to
@@ -456,13 +469,29 @@ __device__ __forceinline__ constexpr int h16_row_off(int r) {
 }
 static_assert(h16_row_off(31) + 1024 <= kTileBytes, "tile layout");
 
-template <int MODE, int NW>  // NW waves: 16*NW heads per workgroup
+// HD (heads / dims) form, eight waves: S^T and the softmax stay per head
+// (wave w, heads 16w .. 16w+15), but the P.V product is split by output
+// dims: wave w owns O[all 128 heads][dims 64w .. 64w+63].  Each wave puts its
+// P fragment (16 bytes per lane, already in the A-operand layout) into LDS
+// and every wave reads the eight fragments back, so per tile and wave the
+// LDS delivers the 32 KB key tile once (for S^T), a 4 KB slice of it (V)
+// and 8 KB of P, instead of the whole tile twice.  A running max that moves
+// is published as per-head factors alpha with a flag per wave; the owners of
+// the O slices apply them before adding the tile.  Double-buffered P,
+// alpha and flags need no barrier beyond the one per tile.
+template <int MODE, int NW, bool HD = false>  // NW waves: 16*NW heads per workgroup
 __global__ void __launch_bounds__(64 * NW) attend512_kernel(AttArgs a) {
   constexpr int CD = 512, KS = 16, NT = 32;  // 32-dim Q.K^T steps; 16-dim output tiles
   constexpr int NST = 4, RPW = 32 / NW, HPG = 16 * NW;
   static_assert(NW == 4 || NW == 8, "4 or 8 waves");
+  static_assert(!HD || (NW == 8 && MODE != kGather), "the HD form: eight waves, no gather list (LDS)");
   __shared__ __attribute__((aligned(1024))) unsigned char sK[NST * kTileBytes];
   __shared__ int32_t sRow[MODE == kGather ? kMaxGatherKeys : 1];
+  constexpr int PB = HD ? 2 : 1;
+  __shared__ __attribute__((aligned(16))) bf16x8 sP[PB][HD ? 8 : 1][64];  // [buffer][head block][lane]
+  __shared__ __attribute__((aligned(16))) float sAlpha[PB][HD ? 128 : 4];
+  __shared__ __attribute__((aligned(16))) int32_t sMove[PB][8];
+  __shared__ __attribute__((aligned(16))) float sL[HD ? 128 : 4];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -490,7 +519,9 @@ __global__ void __launch_bounds__(64 * NW) attend512_kernel(AttArgs a) {
   const int64_t k0 = split * a.keys_per_split;
   const int64_t k1 = min(nk, k0 + a.keys_per_split);
   const int64_t hbase = hg * HPG + wave * 16;
-  const bool active = hbase < a.n_h;
+  // HD: every wave computes S^T (heads past n_h use head n_h-1), since every
+  // wave's P block feeds all of them
+  const bool active = HD || hbase < a.n_h;
   const int64_t ntile = k1 > k0 ? (k1 - k0 + 31) / 32 : 0;
   // positions behind the key codes, read once: ring slot of window key j is
   // (mbase + j) mod cap (window mode), of tail key j >= nkm (wbase + j) mod win_ring
@@ -608,6 +639,77 @@ __global__ void __launch_bounds__(64 * NW) attend512_kernel(AttArgs a) {
   // step; each operand register is refilled for the next step right after
   // the MFMA that reads it is issued
   bf16x8 pa;
+  // HD: O[16 heads of block hb][dims 64*wave + 16*n] is o[4*hb + n]; the
+  // tile's P blocks come from buffer pb; first the rescale that any wave's
+  // softmax published for this tile
+  auto hd_rescale = [&](int pb) {
+    const int4 m0 = *reinterpret_cast<const int4*>(&sMove[pb][0]);
+    const int4 m1 = *reinterpret_cast<const int4*>(&sMove[pb][4]);
+    if ((m0.x | m0.y | m0.z | m0.w | m1.x | m1.y | m1.z | m1.w) != 0) {
+#pragma unroll
+      for (int hb = 0; hb < 8; ++hb) {
+        const float4 al = *reinterpret_cast<const float4*>(&sAlpha[pb][16 * hb + 4 * g]);
+#pragma unroll
+        for (int n = 0; n < 4; ++n) {
+          o[4 * hb + n][0] *= al.x;
+          o[4 * hb + n][1] *= al.y;
+          o[4 * hb + n][2] *= al.z;
+          o[4 * hb + n][3] *= al.w;
+        }
+      }
+    }
+  };
+  auto hd_pv_qk = [&](const unsigned char* tp, const unsigned char* tq, int pb) {
+    hd_rescale(pb);
+    s0 = f32x4{0.f, 0.f, 0.f, 0.f};
+    s1 = s0;
+    bf16x8 vb[4];
+#pragma unroll
+    for (int n = 0; n < 4; ++n) vb[n] = vfrag(tp, 4 * wave + n);
+    bf16x8 ka0 = kfrag(tq, qk_off0, 0), ka1 = kfrag(tq, qk_off1, 0);
+    bf16x8 pc;
+    // step pair (2hb, 2hb+1) adds head block hb's four output tiles; P block
+    // hb is read two S^T MFMAs ahead of its first use (registers are too
+    // tight for a second P buffer), so even steps issue both S^T MFMAs first
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const int hb = ks >> 1;
+      if ((ks & 1) == 0) {
+        pc = sP[pb][hb][lane];
+        s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka0, qf[ks], s0, 0, 0, 0);
+        if (ks + 1 < KS) ka0 = kfrag(tq, qk_off0, ks + 1);
+        s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka1, qf[ks], s1, 0, 0, 0);
+        if (ks + 1 < KS) ka1 = kfrag(tq, qk_off1, ks + 1);
+        o[4 * hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pc, vb[0], o[4 * hb], 0, 0, 0);
+        o[4 * hb + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pc, vb[1], o[4 * hb + 1], 0, 0, 0);
+      } else {
+        s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka0, qf[ks], s0, 0, 0, 0);
+        if (ks + 1 < KS) ka0 = kfrag(tq, qk_off0, ks + 1);
+        o[4 * hb + 2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pc, vb[2], o[4 * hb + 2], 0, 0, 0);
+        s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka1, qf[ks], s1, 0, 0, 0);
+        if (ks + 1 < KS) ka1 = kfrag(tq, qk_off1, ks + 1);
+        o[4 * hb + 3] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pc, vb[3], o[4 * hb + 3], 0, 0, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  auto hd_pv_only = [&](const unsigned char* tp, int pb) {
+    hd_rescale(pb);
+    bf16x8 vb[4];
+#pragma unroll
+    for (int n = 0; n < 4; ++n) vb[n] = vfrag(tp, 4 * wave + n);
+    bf16x8 pc = sP[pb][0][lane];
+#pragma unroll
+    for (int hb = 0; hb < 8; ++hb) {
+      bf16x8 pn = pc;
+      if (hb + 1 < 8) pn = sP[pb][hb + 1][lane];
+#pragma unroll
+      for (int n = 0; n < 4; ++n)
+        o[4 * hb + n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pc, vb[n], o[4 * hb + n], 0, 0, 0);
+      pc = pn;
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
   auto pv_qk = [&](const unsigned char* tp, const unsigned char* tq) {
     s0 = f32x4{0.f, 0.f, 0.f, 0.f};
     s1 = s0;
@@ -643,8 +745,9 @@ __global__ void __launch_bounds__(64 * NW) attend512_kernel(AttArgs a) {
     }
   };
   // softmax of S^T (keys masked by vmask) into pa, rescaling O if the running
-  // max grew; lane holds head r16, keys 4g+e (s0) and 16+4g+e (s1)
-  auto softmax = [&](uint32_t vmask) {
+  // max grew; lane holds head r16, keys 4g+e (s0) and 16+4g+e (s1).  HD: the
+  // factors, the flag and P go to LDS buffer pb instead
+  auto softmax = [&](uint32_t vmask, int pb) {
     float x[8];
     const uint32_t vm = vmask >> (4 * g);
 #pragma unroll
@@ -658,7 +761,18 @@ __global__ void __launch_bounds__(64 * NW) attend512_kernel(AttArgs a) {
     tmax = rows4_max(tmax);
     // lazy running max: O is rescaled only when the max grows by more than 2^8
     const bool move = tmax > mrun + 8.f;
-    if (__any(move)) {
+    const bool any_move = __any(move);
+    if constexpr (HD) {
+      float alpha = 1.f;
+      if (any_move) {
+        const float mnew = move ? tmax : mrun;
+        alpha = mrun == -INFINITY ? 0.f : exp2f(mrun - mnew);
+        lrun *= alpha;
+        mrun = mnew;
+      }
+      if (g == 0) sAlpha[pb][16 * wave + r16] = alpha;
+      if (lane == 0) sMove[pb][wave] = any_move ? 1 : 0;
+    } else if (any_move) {
       const float mnew = move ? tmax : mrun;
       const float alpha = mrun == -INFINITY ? 0.f : exp2f(mrun - mnew);
       lrun *= alpha;
@@ -681,6 +795,7 @@ __global__ void __launch_bounds__(64 * NW) attend512_kernel(AttArgs a) {
       pa[e] = (__bf16)p;
     }
     lrun += rows4_sum(psum);
+    if constexpr (HD) sP[pb][wave][lane] = pa;
   };
 
   if (ntile > 0) {
@@ -689,7 +804,7 @@ __global__ void __launch_bounds__(64 * NW) attend512_kernel(AttArgs a) {
     const uint32_t vmask = valid_mask(0);
     if (active) {
       qk_only(tile_ptr(0));
-      softmax(vmask);
+      softmax(vmask, 0);
     }
   }
   for (int64_t it = 0; it + 1 < ntile; ++it) {
@@ -697,15 +812,75 @@ __global__ void __launch_bounds__(64 * NW) attend512_kernel(AttArgs a) {
     lds_barrier();
     if (it + 3 < ntile) issue(it + 3);
     const uint32_t vmask = valid_mask(it + 1);
-    if (active) {
+    if constexpr (HD) {
+      hd_pv_qk(tile_ptr(it), tile_ptr(it + 1), int(it & 1));
+      softmax(vmask, int((it + 1) & 1));
+    } else if (active) {
       pv_qk(tile_ptr(it), tile_ptr(it + 1));
-      softmax(vmask);
+      softmax(vmask, 0);
     }
   }
-  if (ntile > 0 && active) pv_only(tile_ptr(ntile - 1));
+  if constexpr (HD) {
+    if (ntile > 0) {
+      lds_barrier();  // the last tile's P blocks, from every wave
+      hd_pv_only(tile_ptr(ntile - 1), int((ntile - 1) & 1));
+    }
+  } else if (ntile > 0 && active) {
+    pv_only(tile_ptr(ntile - 1));
+  }
 
-  // normalise and write: o[nt][e] is head 4*g + e, dim 16*nt + i16
   const int64_t slot0 = (bq * a.splits + split) * a.n_h;
+  if constexpr (HD) {
+    // every head's sum, from the wave that owns its softmax, to the owners
+    // of the O slices; o[4*hb + n][e] is head 16*hb + 4*g + e of the
+    // workgroup, dim 64*wave + 16*n + i16
+    if (g == 0) sL[16 * wave + r16] = lrun;
+    if (g == 0 && a.lse && hbase + r16 < a.n_h)
+      a.lse[slot0 + hbase + r16] = lrun > 0.f ? (mrun + log2f(lrun)) * kLn2 : -INFINITY;
+    lds_barrier();
+    const int64_t h0 = hg * HPG;
+    if (a.ob != nullptr) {
+      // fragment order (as below): head block hb's stores j = 2*wave and
+      // 2*wave+1 hold dims 16nt + i16 of nt = 2j, 2j+1
+      const int64_t nh16 = (a.n_h + 15) & ~int64_t(15);
+      bf16_raw* dst0 = a.ob + ((bq * a.splits + split) * nh16 + h0) * CD + 8 * lane;
+#pragma unroll
+      for (int hb = 0; hb < 8; ++hb) {
+        if (h0 + 16 * hb >= a.n_h) break;
+        const float4 l4 = *reinterpret_cast<const float4*>(&sL[16 * hb + 4 * g]);
+        const float inv[4] = {l4.x > 0.f ? 1.f / l4.x : 0.f, l4.y > 0.f ? 1.f / l4.y : 0.f,
+                              l4.z > 0.f ? 1.f / l4.z : 0.f, l4.w > 0.f ? 1.f / l4.w : 0.f};
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) {
+          bf16x8 v;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            v[e] = (__bf16)(o[4 * hb + 2 * jj][e] * inv[e]);
+            v[4 + e] = (__bf16)(o[4 * hb + 2 * jj + 1][e] * inv[e]);
+          }
+          *reinterpret_cast<bf16x8*>(dst0 + int64_t(16 * hb) * CD + 512 * (2 * wave + jj)) = v;
+        }
+      }
+      return;
+    }
+#pragma unroll
+    for (int hb = 0; hb < 8; ++hb) {
+      const float4 l4 = *reinterpret_cast<const float4*>(&sL[16 * hb + 4 * g]);
+      const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int64_t h = h0 + 16 * hb + 4 * g + e;
+        if (h < a.n_h) {
+          const float inv = lv[e] > 0.f ? 1.f / lv[e] : 0.f;
+          float* op = a.o + (slot0 + h) * CD + 64 * wave + i16;
+#pragma unroll
+          for (int n = 0; n < 4; ++n) op[16 * n] = o[4 * hb + n][e] * inv;
+        }
+      }
+    }
+    return;
+  }
+  // normalise and write: o[nt][e] is head 4*g + e, dim 16*nt + i16
   float inv[4];
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
@@ -1088,6 +1263,8 @@ int run_attend(const char* name, int dtype, AttArgs a, int64_t BQ, int64_t nkeys
       const dim3 grid8{(unsigned)gx, (unsigned)BQ, 1u};
       if (p.heads == 64)
         hipLaunchKernelGGL((attend512_kernel<MODE, 4>), grid8, dim3(256), 0, s, a);
+      else if (MODE == kDense && kHeadsDims && p.kps >= kHdMinKeys)
+        hipLaunchKernelGGL((attend512_kernel<MODE, 8, MODE == kDense>), grid8, dim3(512), 0, s, a);
       else
         hipLaunchKernelGGL((attend512_kernel<MODE, 8>), grid8, dim3(512), 0, s, a);
     }

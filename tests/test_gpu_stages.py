@@ -288,6 +288,52 @@ def test_hca_attend(dtype, B, n_q, n_h, c, mp, cap, ts):
             assert np.abs(f64(lse[b, j]) - l_ref).max() <= 1e-3 + 1e-5 * np.abs(l_ref).max()
 
 
+@pytest.mark.parametrize("n_q,n_h,mp,cap,seed,sample", [
+    (256, 120, 16, 1100, 1, (0, 1, 2, 77, 128, 255)),  # one split per query (fp32 output), a partial head block
+    (16, 128, 4, 16400, 2, (0, 1, 9)),                  # 16 splits of 1056 keys: bf16 partials, empty splits, combine
+])
+def test_hca_attend_long_splits(n_q, n_h, mp, cap, seed, sample):
+    """Splits of at least 1024 keys run the c = 512 kernel in its HD form (the
+    softmax per head, P exchanged through LDS, O split by dims): sampled
+    queries against the oracle, with an empty query, a full one and ragged
+    key counts."""
+    c = 512
+    q = synth.normal((1, n_q, n_h, c), 1700 + seed, dtype="bf16")
+    C = synth.normal((1, cap, c), 1710 + seed, dtype="bf16")
+    rng = np.random.default_rng(seed)
+    t = torch.from_numpy(rng.integers(1024 * mp, cap * mp + 1, size=(1, n_q))).to(torch.int64)
+    t[0, 0], t[0, 1] = mp - 1, cap * mp  # no key; every key
+    out, lse = dlc.hca_attend(q.to(DEV), C.to(DEV), t.to(DEV), int(t.max()), mp)
+    torch.cuda.synchronize()
+    out, lse = out.cpu(), lse.cpu()
+    for j in sample:
+        o_ref, l_ref = O.hca_attend(q[0, j], C[0], int(t[0, j]), mp)
+        if not np.isfinite(l_ref).any():
+            assert (out[0, j] == 0).all() and torch.isneginf(lse[0, j]).all()
+            continue
+        assert_rows_close(out[0, j], o_ref, TOL_ATT["bf16"], f"hca long splits q={j}")
+        assert np.abs(f64(lse[0, j]) - l_ref).max() <= 1e-3 + 1e-5 * np.abs(l_ref).max()
+
+
+def test_hca_attend_window_long_splits():
+    """The window branch joined to HCA with 256 consecutive queries of one
+    sequence (one split of >= 1024 keys each: the HD form with the window's
+    keys as the tail of the key list)."""
+    n_q, n_h, c, mp, cap, ring, n_win = 256, 128, 512, 16, 1100, 512, 128
+    q = synth.normal((1, n_q, n_h, c), 1750, dtype="bf16")
+    Ch = synth.normal((1, cap, c), 1751, dtype="bf16")
+    R = _ring(1, ring, c, "bf16", 1752)
+    t = (cap * mp - n_q + torch.arange(n_q, dtype=torch.int64)).reshape(1, n_q)
+    o, lse = dlc.hca_attend_window(q.to(DEV), Ch.to(DEV), t.to(DEV), int(t.max()), mp, R.to(DEV), n_win)
+    torch.cuda.synchronize()
+    for j in (0, 100, 255):
+        o1, l1 = O.hca_attend(q[0, j], Ch[0], int(t[0, j]), mp)
+        o2, l2 = _window_ref(q[0, j], R[0], t[0, j], n_win)
+        o_r, l_r = O.merge_lse(o1, l1, o2, l2)
+        assert_rows_close(o[0, j], o_r, TOL_ATT["bf16"], f"hca+window long splits q={j}")
+        assert np.abs(lse[0, j].cpu().numpy() - l_r).max() <= TOL_ATT["bf16"]
+
+
 # --------------------------------------------------------------- projection
 
 @pytest.mark.parametrize("dtype,M,N,K,out_dtype", [
