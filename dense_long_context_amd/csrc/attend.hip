@@ -62,7 +62,10 @@ constexpr int kTargetWorkgroups = DLC_ATTEND_TARGET_WGS;
 #define DLC_ATTEND_HD 1
 #endif
 constexpr bool kHeadsDims = DLC_ATTEND_HD != 0;
-constexpr int64_t kHdMinKeys = 1024;
+#ifndef DLC_HD_MIN_KEYS
+#define DLC_HD_MIN_KEYS 1024
+#endif
+constexpr int64_t kHdMinKeys = DLC_HD_MIN_KEYS;
 
 
 
