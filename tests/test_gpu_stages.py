@@ -112,6 +112,7 @@ def _score_slack(qI, wI, KI):
     ("bf16", 1, 2, 16, 32, 4, 1024, 1500, [6000, 4100]),    # k >= visible for one query
     ("bf16", 2, 1, 20, 64, 2, 300, 4000, [8000, 7777]),     # head padding (20 -> 32)
     ("bf16", 1, 1, 64, 256, 4, 16, 600, [2400]),
+    ("bf16", 1, 2, 64, 128, 4, 8192, 20000, [80000, 40003]),  # the largest k the ABI takes
 ])
 def test_index_topk(dtype, B, n_q, n_hI, cI, m, k, cap, ts):
     seed = 500 + cap
@@ -231,6 +232,8 @@ def _random_selection(B, n_q, k, cap, seed, counts):
     # (4 groups, 5 splits), then 128-head groups (2 groups, 5 splits)
     ("bf16", 1, 1, 256, 512, 300, 2000, [300]),
     ("bf16", 4, 4, 256, 512, 300, 3000, [300, 299, 1, 0, 300, 150, 64, 65, 300, 300, 33, 257, 300, 2, 100, 200]),
+    # the largest k: more gathered keys than one split holds in LDS (2048)
+    ("bf16", 1, 2, 128, 512, 8192, 9000, [8192, 5000]),
 ])
 def test_csa_attend(dtype, B, n_q, n_h, c, k, cap, counts):
     seed = 700 + cap + k
