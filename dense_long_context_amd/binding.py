@@ -126,8 +126,30 @@ def _need(cond, msg):
         raise ValueError(msg)
 
 
+def _on_device(dev, **named):
+    """Every named tensor (None is skipped) is a tensor on the CUDA device
+    ``dev``: the kernels dereference these pointers, so a host tensor or one
+    on another device must never reach them."""
+    _need(isinstance(dev, torch.device) and dev.type == "cuda", f"inputs must be on a CUDA device, not {dev}")
+    for nm, x in named.items():
+        if x is None:
+            continue
+        _need(isinstance(x, torch.Tensor), f"{nm} must be a torch tensor")
+        _need(x.device == dev, f"{nm} is on {x.device}; every tensor of the call must be on {dev}")
+
+
+def _exact(x, nm, dtype, shape):
+    """An output or side input the C ABI reads as a dense array of ``shape``."""
+    if x is None:
+        return
+    _need(x.dtype == dtype, f"{nm} must be {dtype}, got {x.dtype}")
+    _need(tuple(x.shape) == tuple(shape), f"{nm} must have shape {tuple(shape)}, got {tuple(x.shape)}")
+    _need(x.is_contiguous(), f"{nm} must be contiguous")
+
+
 def _ws(nbytes, dev, ws):
     if ws is not None:
+        _need(ws.is_contiguous(), "ws must be contiguous")
         return ws
     return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=dev)
 
@@ -140,11 +162,16 @@ def csa_compress(Za, Zb, Ca, Cb, m, out, i_begin=0, i_end=None, Ba=None, Bb=None
     Streams are [B][rows][c] tensors (views with a row stride are fine) that
     share one stride pattern; ``n`` is the number of valid rows (default: all).
     """
+    _on_device(Za.device, Za=Za, Zb=Zb, Ca=Ca, Cb=Cb, out=out, Ba=Ba, Bb=Bb)
     B, rows, c = Za.shape
     for x in (Zb, Ca, Cb):
         _need(x.shape == Za.shape and x.stride() == Za.stride() and x.dtype == Za.dtype,
               "the four streams must share shape, strides and dtype")
     _need(Za.stride(2) == 1, "stream rows must be contiguous")
+    _need(out.dtype == Za.dtype and out.dim() == 3 and out.shape[0] == B and out.shape[2] == c and out.is_contiguous(),
+          "out must be a contiguous [B][cap][c] tensor in the streams' dtype")
+    _exact(Ba, "Ba", torch.float32, (m, c))
+    _exact(Bb, "Bb", torch.float32, (m, c))
     n = rows if n is None else n
     i_end = n // m if i_end is None else i_end
     _check("csa_compress", lib().csa_compress(
@@ -155,10 +182,14 @@ def csa_compress(Za, Zb, Ca, Cb, m, out, i_begin=0, i_end=None, Ba=None, Bb=None
 
 def hca_compress(Z, Cs, m_prime, out, i_begin=0, i_end=None, bias=None, n=None):
     """Compress HCA entries [i_begin, i_end) into ``out`` [B][cap][c]."""
+    _on_device(Z.device, Z=Z, C=Cs, out=out, bias=bias)
     B, rows, c = Z.shape
     _need(Cs.shape == Z.shape and Cs.stride() == Z.stride() and Cs.dtype == Z.dtype,
           "Z and C must share shape, strides and dtype")
     _need(Z.stride(2) == 1, "stream rows must be contiguous")
+    _need(out.dtype == Z.dtype and out.dim() == 3 and out.shape[0] == B and out.shape[2] == c and out.is_contiguous(),
+          "out must be a contiguous [B][cap][c] tensor in the streams' dtype")
+    _exact(bias, "bias", torch.float32, (m_prime, c))
     n = rows if n is None else n
     i_end = n // m_prime if i_end is None else i_end
     _check("hca_compress", lib().hca_compress(
@@ -176,14 +207,19 @@ def csa_index_topk_ws(B, n_q, cap, k):
 def csa_index_topk(qI, wI, KI, t, t_max, m, k, idx=None, count=None, scores=None, ws=None):
     """Indexer scores and top-k.  qI [B][n_q][n_hI][cI], wI fp32 [B][n_q][n_hI],
     KI [B][cap][cI], t int64 [B][n_q] on the device.  Returns (idx, count)."""
+    dev = qI.device
+    _on_device(dev, qI=qI, wI=wI, KI=KI, t=t, idx=idx, count=count, scores=scores, ws=ws)
     B, n_q, n_hI, cI = qI.shape
     cap = KI.shape[1]
-    dev = qI.device
     for x, nm in ((qI, "qI"), (wI, "wI"), (KI, "KI"), (t, "t")):
         _need(x.is_contiguous(), f"{nm} must be contiguous")
     _need(wI.dtype == torch.float32 and t.dtype == torch.int64, "wI must be fp32 and t int64")
     _need(tuple(wI.shape) == (B, n_q, n_hI) and tuple(t.shape) == (B, n_q), "wI/t shape mismatch")
-    _need(KI.shape[0] == B and KI.shape[2] == cI and KI.dtype == qI.dtype, "KI shape/dtype mismatch")
+    _need(KI.dim() == 3 and KI.shape[0] == B and KI.shape[2] == cI and KI.dtype == qI.dtype,
+          "KI shape/dtype mismatch")
+    _exact(idx, "idx", torch.int32, (B, n_q, k))
+    _exact(count, "count", torch.int32, (B, n_q))
+    _exact(scores, "scores", torch.float32, (B, n_q, cap))
     if idx is None:
         idx = torch.empty((B, n_q, k), dtype=torch.int32, device=dev)
     if count is None:
@@ -200,6 +236,7 @@ def mxfp4_quantize(x, codes=None, scales=None):
     """MXFP4 codes and E8M0 scales of the rows of x ([..., width], width % 32 == 0,
     fp32 or bf16, contiguous).  Returns (codes uint8 [..., width/2],
     scales uint8 [..., width/32]); see include/dlc.h for the format."""
+    _on_device(x.device, x=x, codes=codes, scales=scales)
     _need(x.is_contiguous(), "x must be contiguous")
     width = x.shape[-1]
     rows = x.numel() // width if width else 0
@@ -209,6 +246,7 @@ def mxfp4_quantize(x, codes=None, scales=None):
     if scales is None:
         scales = torch.empty(tuple(x.shape[:-1]) + (width // 32,), dtype=torch.uint8, device=dev)
     _need(codes.is_contiguous() and scales.is_contiguous(), "codes/scales must be contiguous")
+    _need(codes.dtype == torch.uint8 and scales.dtype == torch.uint8, "codes/scales must be uint8")
     _need(codes.numel() == rows * (width // 2) and scales.numel() == rows * (width // 32), "codes/scales size")
     _check("mxfp4_quantize", lib().mxfp4_quantize(
         _dt(x), 1, rows, width, _p(x), rows * width, _p(codes), rows * (width // 2), _p(scales),
@@ -224,9 +262,13 @@ def csa_index_topk_fp4(qI, wI, KIc, KIs, t, t_max, m, k, idx=None, count=None, s
     """FP4 (MXFP4) indexer scores and top-k.  qI [B][n_q][n_hI][cI] fp32/bf16 (quantized
     inside), wI fp32 [B][n_q][n_hI], KIc uint8 [B][cap][cI/2] and KIs uint8 [B][cap][cI/32]
     (mxfp4_quantize of the K^I cache), t int64 [B][n_q].  Returns (idx, count)."""
+    dev = qI.device
+    _on_device(dev, qI=qI, wI=wI, KIc=KIc, KIs=KIs, t=t, idx=idx, count=count, scores=scores, ws=ws)
     B, n_q, n_hI, cI = qI.shape
     cap = KIc.shape[1]
-    dev = qI.device
+    _exact(idx, "idx", torch.int32, (B, n_q, k))
+    _exact(count, "count", torch.int32, (B, n_q))
+    _exact(scores, "scores", torch.float32, (B, n_q, cap))
     for x, nm in ((qI, "qI"), (wI, "wI"), (KIc, "KIc"), (KIs, "KIs"), (t, "t")):
         _need(x.is_contiguous(), f"{nm} must be contiguous")
     _need(wI.dtype == torch.float32 and t.dtype == torch.int64, "wI must be fp32 and t int64")
@@ -259,13 +301,18 @@ def csa_attend(q, Ccomp, idx, count, scale=0.0, out=None, lse=None, ws=None):
     """Shared-KV MQA over the selected CSA entries.  q [B][n_q][n_h][c];
     Ccomp [B][cap][c]; idx int32 [B][n_q][k]; count int32 [B][n_q].
     Returns (out fp32 [B][n_q][n_h][c], lse fp32 [B][n_q][n_h])."""
+    dev = q.device
+    _on_device(dev, q=q, Ccomp=Ccomp, idx=idx, count=count, out=out, lse=lse, ws=ws)
     B, n_q, n_h, c = q.shape
     k = idx.shape[2]
-    dev = q.device
     _need(q.is_contiguous() and Ccomp.is_contiguous() and idx.is_contiguous() and count.is_contiguous(),
           "inputs must be contiguous")
-    _need(Ccomp.shape[0] == B and Ccomp.shape[2] == c and Ccomp.dtype == q.dtype, "Ccomp shape/dtype mismatch")
-    _need(idx.dtype == torch.int32 and count.dtype == torch.int32, "idx/count must be int32")
+    _need(Ccomp.dim() == 3 and Ccomp.shape[0] == B and Ccomp.shape[2] == c and Ccomp.dtype == q.dtype,
+          "Ccomp shape/dtype mismatch")
+    _exact(idx, "idx", torch.int32, (B, n_q, k))
+    _exact(count, "count", torch.int32, (B, n_q))
+    _exact(out, "out", torch.float32, (B, n_q, n_h, c))
+    _exact(lse, "lse", torch.float32, (B, n_q, n_h))
     if out is None:
         out = torch.empty((B, n_q, n_h, c), dtype=torch.float32, device=dev)
     if lse is None:
@@ -279,12 +326,16 @@ def csa_attend(q, Ccomp, idx, count, scale=0.0, out=None, lse=None, ws=None):
 
 def hca_attend(q, Chca, t, t_max, m_prime, scale=0.0, out=None, lse=None, ws=None):
     """Dense shared-KV MQA over the visible HCA entries.  Returns (out, lse)."""
+    dev = q.device
+    _on_device(dev, q=q, Chca=Chca, t=t, out=out, lse=lse, ws=ws)
     B, n_q, n_h, c = q.shape
     cap = Chca.shape[1]
-    dev = q.device
     _need(q.is_contiguous() and Chca.is_contiguous() and t.is_contiguous(), "inputs must be contiguous")
-    _need(Chca.shape[0] == B and Chca.shape[2] == c and Chca.dtype == q.dtype, "Chca shape/dtype mismatch")
+    _need(Chca.dim() == 3 and Chca.shape[0] == B and Chca.shape[2] == c and Chca.dtype == q.dtype,
+          "Chca shape/dtype mismatch")
     _need(t.dtype == torch.int64 and tuple(t.shape) == (B, n_q), "t must be int64 [B][n_q]")
+    _exact(out, "out", torch.float32, (B, n_q, n_h, c))
+    _exact(lse, "lse", torch.float32, (B, n_q, n_h))
     if out is None:
         out = torch.empty((B, n_q, n_h, c), dtype=torch.float32, device=dev)
     if lse is None:
@@ -304,9 +355,12 @@ def window_attend(q, Cwin, t, t_max, n_win, o_in=None, lse_in=None, scale=0.0, o
     """Sliding-window branch over the ring Cwin [B][ring][c] (token p at row
     p % ring, ring >= n_win), optionally joined to a compressed branch's
     (o_in, lse_in) by their log-sum-exp.  Returns (out, lse); out may be o_in."""
+    dev = q.device
+    _on_device(dev, q=q, Cwin=Cwin, t=t, o_in=o_in, lse_in=lse_in, out=out, lse=lse, ws=ws)
     B, n_q, n_h, c = q.shape
     ring = Cwin.shape[1]
-    dev = q.device
+    _exact(out, "out", torch.float32, (B, n_q, n_h, c))
+    _exact(lse, "lse", torch.float32, (B, n_q, n_h))
     _need(q.is_contiguous() and Cwin.is_contiguous() and t.is_contiguous(), "inputs must be contiguous")
     _need(Cwin.shape[0] == B and Cwin.shape[2] == c and Cwin.dtype == q.dtype, "Cwin shape/dtype mismatch")
     _need(t.dtype == torch.int64 and tuple(t.shape) == (B, n_q), "t must be int64 [B][n_q]")
@@ -329,9 +383,14 @@ def window_attend(q, Cwin, t, t_max, n_win, o_in=None, lse_in=None, scale=0.0, o
 
 def csa_attend_window(q, Ccomp, idx, count, Cwin, t, t_max, n_win, scale=0.0, out=None, lse=None, ws=None):
     """csa_attend joined with the sliding window of the ring Cwin [B][ring][c]."""
+    dev = q.device
+    _on_device(dev, q=q, Ccomp=Ccomp, idx=idx, count=count, Cwin=Cwin, t=t, out=out, lse=lse, ws=ws)
     B, n_q, n_h, c = q.shape
     k, ring = idx.shape[2], Cwin.shape[1]
-    dev = q.device
+    _exact(idx, "idx", torch.int32, (B, n_q, k))
+    _exact(count, "count", torch.int32, (B, n_q))
+    _exact(out, "out", torch.float32, (B, n_q, n_h, c))
+    _exact(lse, "lse", torch.float32, (B, n_q, n_h))
     _need(all(x.is_contiguous() for x in (q, Ccomp, idx, count, Cwin, t)), "inputs must be contiguous")
     _need(Ccomp.shape[0] == B and Ccomp.shape[2] == c and Ccomp.dtype == q.dtype, "Ccomp shape/dtype mismatch")
     _need(Cwin.shape[0] == B and Cwin.shape[2] == c and Cwin.dtype == q.dtype, "Cwin shape/dtype mismatch")
@@ -350,9 +409,12 @@ def csa_attend_window(q, Ccomp, idx, count, Cwin, t, t_max, n_win, scale=0.0, ou
 
 def hca_attend_window(q, Chca, t, t_max, m_prime, Cwin, n_win, scale=0.0, out=None, lse=None, ws=None):
     """hca_attend joined with the sliding window of the ring Cwin [B][ring][c]."""
+    dev = q.device
+    _on_device(dev, q=q, Chca=Chca, t=t, Cwin=Cwin, out=out, lse=lse, ws=ws)
     B, n_q, n_h, c = q.shape
     cap, ring = Chca.shape[1], Cwin.shape[1]
-    dev = q.device
+    _exact(out, "out", torch.float32, (B, n_q, n_h, c))
+    _exact(lse, "lse", torch.float32, (B, n_q, n_h))
     _need(all(x.is_contiguous() for x in (q, Chca, Cwin, t)), "inputs must be contiguous")
     _need(Chca.shape[0] == B and Chca.shape[2] == c and Chca.dtype == q.dtype, "Chca shape/dtype mismatch")
     _need(Cwin.shape[0] == B and Cwin.shape[2] == c and Cwin.dtype == q.dtype, "Cwin shape/dtype mismatch")
@@ -372,13 +434,15 @@ def hca_attend_window(q, Chca, t, t_max, m_prime, Cwin, n_win, scale=0.0, out=No
 
 def dlc_project(A, Wt, out=None, out_dtype=None):
     """out[M][N] = A[M][K] . W with W given transposed as Wt [N][K]; fp32 accumulation."""
+    _on_device(A.device, A=A, Wt=Wt, out=out)
     M, K = A.shape
     N = Wt.shape[0]
-    _need(Wt.shape[1] == K and Wt.dtype == A.dtype, "Wt must be [N][K] in A's dtype")
+    _need(Wt.dim() == 2 and Wt.shape[1] == K and Wt.dtype == A.dtype, "Wt must be [N][K] in A's dtype")
     _need(A.stride(1) == 1 and Wt.stride(1) == 1, "rows must be contiguous")
     if out is None:
         out = torch.empty((M, N), dtype=out_dtype or A.dtype, device=A.device)
     _need(out.stride(1) == 1 and tuple(out.shape) == (M, N), "out must be [M][N] with contiguous rows")
+    _need(out.dtype in (torch.float32, A.dtype), "out must be fp32 or A's dtype")
     _check("dlc_project", lib().dlc_project(
         _dt(A), M, N, K, _p(A), _stride(A, 0, K), _p(Wt), _stride(Wt, 0, K), _p(out), _stride(out, 0, N), _dt(out),
         _stream(A.device)))
@@ -388,6 +452,7 @@ def dlc_project(A, Wt, out=None, out_dtype=None):
 def attend_sink(out, lse, z):
     """Per-head sink logits z (fp32 [n_h]) applied in place to an attention's
     fp32 output [..., n_h, c] and log-sum-exp [..., n_h]; returns (out, lse)."""
+    _on_device(out.device, out=out, lse=lse, z=z)
     n_h, c = out.shape[-2], out.shape[-1]
     rows = out.numel() // (n_h * c) if n_h * c else 0
     _need(out.dtype == torch.float32 and lse.dtype == torch.float32 and z.dtype == torch.float32, "fp32 only")
@@ -404,6 +469,8 @@ def dlc_timing_arm(stage, ev_begin, ev_end):
 
 def dlc_copy(dst, src):
     """Copy kernel (bandwidth reference): dst[:] = src[:] for equal-size device tensors."""
+    _on_device(src.device, dst=dst, src=src)
+    _need(dst.is_contiguous() and src.is_contiguous(), "dst and src must be contiguous")
     nb = src.numel() * src.element_size()
     _need(dst.numel() * dst.element_size() == nb, "size mismatch")
     _check("dlc_copy", lib().dlc_copy(_p(dst), _p(src), nb, _stream(src.device)))

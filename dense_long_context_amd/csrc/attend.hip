@@ -1252,6 +1252,10 @@ int run_attend(const char* name, int dtype, AttArgs a, int64_t BQ, int64_t nkeys
   }
   DLC_REQUIRE(BQ <= 65535 && p.splits * p.head_groups < (int64_t(1) << 31), DLC_E_UNSUPPORTED,
               "%s: grid too large", name);
+  // the c = 512 kernel lists a split's gathered rows in LDS (kMaxGatherKeys)
+  DLC_REQUIRE(!(MODE == kGather && p.mfma && a.c == 512) || p.kps <= kMaxGatherKeys, DLC_E_UNSUPPORTED,
+              "%s: %lld gathered keys per query exceed %lld (%d splits of %d)", name, (long long)nkeys,
+              (long long)kMaxSplits * kMaxGatherKeys, kMaxSplits, kMaxGatherKeys);
   StageTimer timer(MODE == kGather ? DLC_STAGE_CSA_ATTEND : MODE == kDense ? DLC_STAGE_HCA_ATTEND
                                                                              : DLC_STAGE_WINDOW_ATTEND, s);
   if (p.mfma) {

@@ -95,11 +95,15 @@ __device__ __forceinline__ void chunk_partial(const PoolArgs& a, int64_t boff, i
     for (int rr = 0; rr < kChunk; ++rr)
       if (r0 + rr < r1) cm = fmaxf(cm, l[rr][u]);
     float sm = 0.f, ac = 0.f;
-    // logits are finite: one v_exp_f32 each
+    // one v_exp_f32 per logit.  A -inf logit (the page's padding) gets weight
+    // exp2(-inf) = 0; a chunk whose logits are all -inf keeps max -inf and
+    // weights 0 (taking its max as the reference would give -inf - -inf = NaN),
+    // so it adds nothing when merged.
+    const float cref = cm == -INFINITY ? 0.f : cm;
 #pragma unroll
     for (int rr = 0; rr < kChunk; ++rr) {
       if (r0 + rr < r1) {
-        const float w = __builtin_amdgcn_exp2f(l[rr][u] - cm);
+        const float w = __builtin_amdgcn_exp2f(l[rr][u] - cref);
         sm += w;
         ac = fmaf(w, cv[rr][u], ac);
       }

@@ -70,7 +70,9 @@ const char* dlc_last_error(void);
  *   Z^a[m*i + r][j] + B^a[r][j]        (r < m, current block)
  *   Z^b[m*(i-1) + r][j] + B^b[r][j]    (r < m, previous block; absent for i = 0)
  * then C^Comp[i][j] = sum of the weights times the matching C^a / C^b values.
- * The missing b-rows of entry 0 (the page pads them with -inf) get weight 0.
+ * The missing b-rows of entry 0 (the page pads them with -inf) get weight 0,
+ * and so does any row whose logit Z + B is -inf (a -inf bias masks its row
+ * position); a column whose logits are all -inf has no softmax and gives NaN.
  * The same call builds the indexer-key cache K^IComp from the indexer's own
  * four streams at width c := c^I ([Scratch] §6.4).
  *
@@ -194,6 +196,9 @@ int csa_index_topk_fp4(int dtype, int64_t B, int64_t n_q, int64_t n_hI, int64_t 
  *  out       fp32 [B][n_q][n_h][c];  lse: fp32 [B][n_q][n_h] or NULL
  *  ws        at least csa_attend_ws(B, n_q, n_h, c, k) bytes, 256-byte aligned
  * An empty selection gives o = 0 and lse = -inf.
+ * Limit: bf16 with c = 512 lists each split's rows in LDS, so k (plus n_win
+ * for csa_attend_window) is at most 256 * 2048 = 524288; beyond that the call
+ * returns DLC_E_UNSUPPORTED.
  */
 size_t csa_attend_ws(int64_t B, int64_t n_q, int64_t n_h, int64_t c, int64_t k);
 int csa_attend(int dtype, int64_t B, int64_t n_q, int64_t n_h, int64_t c, int64_t k,

@@ -217,3 +217,44 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(binding, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(ImportError):
         binding.lib()
+
+
+def test_attend_gather_limit(L):
+    """csa_attend's c = 512 kernel lists a split's gathered rows in LDS: more
+    keys than 256 splits x 2048 rows is refused, not run."""
+    big = 256 * 2048 + 1
+    rc = L.csa_attend(BF16, 1, 1, 128, 512, big, P, P, 1 << 20, P, P, 0.0, P, None, P, 1 << 40, None)
+    assert rc == E_UNSUPPORTED
+    assert "gathered keys" in binding.last_error()
+    rc = L.csa_attend_window(BF16, 1, 1, 128, 512, big - 128, P, P, 1 << 20, P, P, P, 256, 129, P, 10, 0.0, P,
+                             None, P, 1 << 40, None)
+    assert rc == E_UNSUPPORTED
+
+
+def test_binding_rejects_host_tensors():
+    """Tensors the kernels would dereference must be on the CUDA device: a host
+    tensor is refused by the binding before any call reaches the library."""
+    import torch
+
+    import dense_long_context_amd as dlc
+
+    bf = torch.bfloat16
+    qI, wI = torch.zeros((1, 1, 4, 64), dtype=bf), torch.zeros((1, 1, 4))
+    KI, t = torch.zeros((1, 16, 64), dtype=bf), torch.tensor([[64]])
+    q, C = torch.zeros((1, 1, 4, 128), dtype=bf), torch.zeros((1, 16, 128), dtype=bf)
+    idx, cnt = torch.zeros((1, 1, 8), dtype=torch.int32), torch.zeros((1, 1), dtype=torch.int32)
+    S = torch.zeros((1, 16, 8), dtype=bf)
+    calls = [
+        lambda: dlc.csa_index_topk(qI, wI, KI, t, 64, 4, 8),
+        lambda: dlc.csa_attend(q, C, idx, cnt),
+        lambda: dlc.hca_attend(q, C, t, 64, 4),
+        lambda: dlc.window_attend(q, C, t, 64, 16),
+        lambda: dlc.csa_compress(S, S, S, S, 4, torch.zeros((1, 4, 8), dtype=bf)),
+        lambda: dlc.hca_compress(S, S, 4, torch.zeros((1, 4, 8), dtype=bf)),
+        lambda: dlc.dlc_project(torch.zeros((4, 8), dtype=bf), torch.zeros((4, 8), dtype=bf)),
+        lambda: dlc.mxfp4_quantize(torch.zeros((4, 64), dtype=bf)),
+        lambda: dlc.attend_sink(torch.zeros((1, 4, 8)), torch.zeros((1, 4)), torch.zeros(4)),
+    ]
+    for f in calls:
+        with pytest.raises(ValueError, match="CUDA device"):
+            f()

@@ -14,7 +14,7 @@ import torch
 import dense_long_context_amd as dlc
 import oracle as O
 import synth
-from devtools import DEV, check_topk, f64, need_gpu
+from devtools import DEV, FlipTally, check_scores, check_topk, f64, need_gpu, score_bound
 
 pytestmark = pytest.mark.gpu
 
@@ -79,12 +79,9 @@ def test_mxfp4_quantize_cache_ranges_and_batches():
     assert np.array_equal(got_e, ref_e) and np.array_equal(got_c, ref_c)
 
 
-def _slack_fp4(qI, wI, KI):
-    """fp32 accumulation bound of the device scores on the dequantized operands"""
-    q = O.mxfp4_dequantize(*O.mxfp4_quantize(qI))
-    K = O.mxfp4_dequantize(*O.mxfp4_quantize(KI))
-    mag = np.abs(K) @ np.abs(q).T @ np.abs(f64(wI))
-    return 2e-6 * mag * (q.shape[1] + q.shape[0]) ** 0.5 + 1e-30
+def _bound_fp4(qI, wI, KI):
+    """fp32 bound of the device scores, on the dequantized operands"""
+    return score_bound(O.mxfp4_dequantize(*O.mxfp4_quantize(qI)), wI, O.mxfp4_dequantize(*O.mxfp4_quantize(KI)))
 
 
 @pytest.mark.parametrize("dtype,B,n_q,n_hI,cI,m,k,cap,ts", [
@@ -105,14 +102,16 @@ def test_index_topk_fp4(dtype, B, n_q, n_hI, cI, m, k, cap, ts):
     idx, cnt = dlc.csa_index_topk_fp4(qI.to(DEV), wI.to(DEV), KIc, KIs, t.to(DEV), t_max, m, k, scores=scores)
     torch.cuda.synchronize()
     idx, cnt, sc = idx.cpu().numpy(), cnt.cpu().numpy(), scores.cpu().numpy()
+    tally = FlipTally(f"index_topk_fp4 cap={cap}")
     for b in range(B):
         for j in range(n_q):
             tt = int(t[b, j])
             ref = O.index_scores_fp4(qI[b, j], wI[b, j], KI[b], tt, m)
             nv = len(ref)
-            slack = _slack_fp4(qI[b, j], wI[b, j], KI[b, :nv]) if nv else np.zeros(0)
-            assert np.all(np.abs(sc[b, j, :nv] - ref) <= slack), f"scores b={b} q={j}"
-            check_topk(idx[b, j], cnt[b, j], ref, k, abs_slack=float(slack.max()) if nv else 0.0)
+            if nv:
+                check_scores(sc[b, j, :nv], ref, _bound_fp4(qI[b, j], wI[b, j], KI[b, :nv]), f"scores b={b} q={j}")
+            tally.add(check_topk(idx[b, j], cnt[b, j], ref, k, dev_scores=sc[b, j, :nv]))
+    tally.report()
 
 
 @pytest.mark.parametrize("B,n_q,n_hI,m,k,cap,seed", [
@@ -137,17 +136,17 @@ def test_index_topk_fp4_prefill(B, n_q, n_hI, m, k, cap, seed):
     torch.cuda.synchronize()
     idx, cnt, sc = idx.cpu().numpy(), cnt.cpu().numpy(), scores.cpu().numpy()
     Kd = [O.mxfp4_dequantize(*O.mxfp4_quantize(KI[b])) for b in range(B)]
+    tally = FlipTally(f"index_topk_fp4 prefill seed={seed}")
     for b in range(B):
         for j in range(n_q):
             tt = int(t[b, j])
             nv = tt // m
             qd = O.mxfp4_dequantize(*O.mxfp4_quantize(qI[b, j]))
             ref = O.index_scores(qd, wI[b, j], Kd[b], tt, m)
-            slack = (2e-6 * (np.abs(Kd[b][:nv]) @ np.abs(qd).T @ np.abs(f64(wI[b, j]))) * (cI + n_hI) ** 0.5
-                     + 1e-30) if nv else np.zeros(0)
-            assert np.all(np.abs(sc[b, j, :nv] - ref) <= slack), f"scores b={b} q={j}"
+            check_scores(sc[b, j, :nv], ref, score_bound(qd, wI[b, j], Kd[b][:nv]), f"scores b={b} q={j}")
             assert np.isnan(sc[b, j, nv:]).all(), f"entries past the visible range written b={b} q={j}"
-            check_topk(idx[b, j], cnt[b, j], ref, k, abs_slack=float(slack.max()) if nv else 0.0)
+            tally.add(check_topk(idx[b, j], cnt[b, j], ref, k, dev_scores=sc[b, j, :nv]))
+    tally.report()
 
 
 def test_index_topk_fp4_ties_pick_smallest_indices():

@@ -5,7 +5,9 @@ the degenerate cases (nothing visible, k >= visible, ties, masked indices).
 Tolerances (derived in the design notes): fp32 outputs 1e-5 row-relative;
 bf16-stored outputs 8e-3 row-relative (one bf16 rounding of an fp32 result);
 fp32 attention outputs from bf16 inputs 2e-2 row-relative (north-star bar);
-top-k per the tie rule in devtools.check_topk.
+top-k per the tie rule in devtools.check_topk (the benchmark spec's band: ties within
+1e-4 relative at the k-th score), and exactly the selection rule applied to the
+device's own fp32 scores; scores within their fp32 bound (devtools.score_bound).
 """
 
 import math
@@ -17,7 +19,7 @@ import torch
 import dense_long_context_amd as dlc
 import oracle as O
 import synth
-from devtools import DEV, assert_rows_close, check_topk, f64, need_gpu
+from devtools import DEV, FlipTally, assert_rows_close, check_scores, check_topk, f64, need_gpu, score_bound
 
 pytestmark = pytest.mark.gpu
 
@@ -95,14 +97,57 @@ def test_hca_compress(dtype, B, n, c, mp, bias):
         assert_rows_close(got[b], O.store_as(ref, dtype), TOL_STORE[dtype], f"hca b={b}")
 
 
+@pytest.mark.parametrize("dtype,c,m,n", [
+    ("bf16", 128, 4, 515),      # few entries: the lanes-per-chunk path
+    ("bf16", 128, 4, 16400),    # full-pass path (one thread per entry pair and column group)
+    ("f32", 12, 4, 44003),
+    ("bf16", 64, 2, 301),
+])
+def test_compress_neg_inf_logits(dtype, c, m, n):
+    """-inf logits, the page's padding device ("DeepSeek-V4 Hybrid Attention:
+    CSA and HCA from Scratch", §4, block i = 0): a fully masked b-block (every
+    b-row bias -inf, so a whole chunk of -inf logits) leaves the a-rows' softmax
+    alone, scattered -inf biases drop their rows, and an HCA block whose first
+    rows are all -inf pools over the rest."""
+    B = 2
+    seed = 4242 + c + n
+    (Za, Zb, Ca, Cb), full = _streams(B, n, c, dtype, seed, scale=2.0)
+    dfull = full.to(DEV)
+    g = np.random.default_rng(seed)
+    Ba = synth.normal((m, c), seed + 1, dtype="f32")
+    mask = g.random((m, c)) < 0.3
+    mask[0] = False                                   # every column keeps at least one a-row
+    Ba[torch.from_numpy(mask)] = float("-inf")
+    Bb_all = torch.full((m, c), float("-inf"))
+    Bb_some = synth.normal((m, c), seed + 2, dtype="f32")
+    Bb_some[torch.from_numpy(g.random((m, c)) < 0.5)] = float("-inf")
+    cap = n // m
+    for Bb, nm in ((Bb_all, "b-block masked"), (Bb_some, "scattered")):
+        out = torch.full((B, cap, c), 7.0, dtype=TD[dtype], device=DEV)
+        dlc.csa_compress(dfull[0], dfull[1], dfull[2], dfull[3], m, out, 0, cap, Ba.to(DEV), Bb.to(DEV))
+        torch.cuda.synchronize()
+        got = out.cpu()
+        assert torch.isfinite(got.float()).all(), f"csa {nm}: non-finite entries"
+        for b in range(B):
+            ref = O.csa_compress(Za[b], Zb[b], Ca[b], Cb[b], m, Ba, Bb)
+            assert_rows_close(got[b], O.store_as(ref, dtype), TOL_STORE[dtype], f"csa {nm} b={b}")
+    # HCA: the first chunk of rows of every block fully masked, plus scattered -inf
+    mp = 16
+    Bh = synth.normal((mp, c), seed + 3, dtype="f32")
+    Bh[:4] = float("-inf")
+    Bh[4:][torch.from_numpy(g.random((mp - 4, c)) < 0.4)] = float("-inf")
+    Bh[mp - 1] = 0.0                                   # every column keeps one row
+    out = torch.empty((B, n // mp, c), dtype=TD[dtype], device=DEV)
+    dlc.hca_compress(dfull[0], dfull[2], mp, out, bias=Bh.to(DEV))
+    torch.cuda.synchronize()
+    got = out.cpu()
+    assert torch.isfinite(got.float()).all(), "hca: non-finite entries"
+    for b in range(B):
+        ref = O.hca_compress(Za[b], Ca[b], mp, Bh)
+        assert_rows_close(got[b], O.store_as(ref, dtype), TOL_STORE[dtype], f"hca -inf b={b}")
+
+
 # ------------------------------------------------------------ indexer, top-k
-
-def _score_slack(qI, wI, KI):
-    """fp32-accumulation error bound of the device scores, per entry."""
-    q, w, K = f64(qI), f64(wI), f64(KI)
-    mag = np.abs(K) @ np.abs(q).T @ np.abs(w)
-    return 2e-6 * mag * (q.shape[1] + q.shape[0]) ** 0.5 + 1e-30
-
 
 @pytest.mark.parametrize("dtype,B,n_q,n_hI,cI,m,k,cap,ts", [
     ("f32", 1, 1, 1, 2, 2, 1, 3, [5]),                      # worked-example shape
@@ -125,14 +170,15 @@ def test_index_topk(dtype, B, n_q, n_hI, cI, m, k, cap, ts):
     idx, cnt = dlc.csa_index_topk(qI.to(DEV), wI.to(DEV), KI.to(DEV), t.to(DEV), t_max, m, k, scores=scores)
     torch.cuda.synchronize()
     idx, cnt, sc = idx.cpu().numpy(), cnt.cpu().numpy(), scores.cpu().numpy()
+    tally = FlipTally(f"index_topk {dtype} cap={cap}")
     for b in range(B):
         for j in range(n_q):
             tt = int(t[b, j])
             ref = O.index_scores(qI[b, j], wI[b, j], KI[b], tt, m)
             nv = len(ref)
-            slack = _score_slack(qI[b, j], wI[b, j], KI[b, :nv])
-            assert np.all(np.abs(sc[b, j, :nv] - ref) <= slack), f"scores b={b} q={j}"
-            check_topk(idx[b, j], cnt[b, j], ref, k, abs_slack=float(slack.max()) if nv else 0.0)
+            check_scores(sc[b, j, :nv], ref, score_bound(qI[b, j], wI[b, j], KI[b, :nv]), f"scores b={b} q={j}")
+            tally.add(check_topk(idx[b, j], cnt[b, j], ref, k, dev_scores=sc[b, j, :nv]))
+    tally.report()
 
 
 @pytest.mark.parametrize("B,n_q,n_hI,m,k,cap,seed", [
@@ -156,15 +202,16 @@ def test_index_topk_prefill(B, n_q, n_hI, m, k, cap, seed):
     idx, cnt = dlc.csa_index_topk(qI.to(DEV), wI.to(DEV), KI.to(DEV), t.to(DEV), t_max, m, k, scores=scores)
     torch.cuda.synchronize()
     idx, cnt, sc = idx.cpu().numpy(), cnt.cpu().numpy(), scores.cpu().numpy()
+    tally = FlipTally(f"index_topk prefill seed={seed}")
     for b in range(B):
         for j in range(n_q):
             tt = int(t[b, j])
             ref = O.index_scores(qI[b, j], wI[b, j], KI[b], tt, m)
             nv = len(ref)
-            slack = _score_slack(qI[b, j], wI[b, j], KI[b, :nv]) if nv else np.zeros(0)
-            assert np.all(np.abs(sc[b, j, :nv] - ref) <= slack), f"scores b={b} q={j}"
+            check_scores(sc[b, j, :nv], ref, score_bound(qI[b, j], wI[b, j], KI[b, :nv]), f"scores b={b} q={j}")
             assert np.isnan(sc[b, j, nv:]).all(), f"entries past the visible range written b={b} q={j}"
-            check_topk(idx[b, j], cnt[b, j], ref, k, abs_slack=float(slack.max()) if nv else 0.0)
+            tally.add(check_topk(idx[b, j], cnt[b, j], ref, k, dev_scores=sc[b, j, :nv]))
+    tally.report()
 
 
 def test_index_topk_ties_pick_smallest_indices():

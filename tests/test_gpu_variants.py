@@ -91,6 +91,4 @@ def test_evolution_indexer_inputs():
         assert_rows_close(qI[b, 0].cpu(), qI_ref, 8e-3, f"queries b={b}")
         tt = int(t[b, 0])
         ref = O.index_scores(qI[b, 0].cpu(), w[b, 0], KI[b].cpu(), tt, m)
-        qd, Kd = f64(qI[b, 0].cpu()), f64(KI[b, :len(ref)].cpu())
-        slack = 2e-6 * (np.abs(Kd) @ np.abs(qd).T @ np.abs(f64(w[b, 0]))) * (cI + n_hI) ** 0.5 + 1e-30
-        check_topk(idx[b, 0].cpu().numpy().astype(np.int64), int(cnt[b, 0]), ref, k, abs_slack=float(slack.max()))
+        check_topk(idx[b, 0].cpu().numpy().astype(np.int64), int(cnt[b, 0]), ref, k)
