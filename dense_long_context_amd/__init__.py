@@ -8,6 +8,7 @@ from .binding import (  # noqa: F401
     DlcError,
     attend_sink,
     csa_attend,
+    csa_attend_noalloc,
     csa_attend_window,
     csa_attend_ws,
     csa_compress,

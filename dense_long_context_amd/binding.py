@@ -43,6 +43,8 @@ SIGNATURES = {
     "csa_attend_ws": (_sz, [_i64, _i64, _i64, _i64, _i64]),
     "csa_attend": (_i32, [_i32, _i64, _i64, _i64, _i64, _i64, _vp, _vp, _i64, _vp, _vp, _f32, _vp,
                           _vp, _vp, _sz, _vp]),
+    "csa_attend_noalloc": (_i32, [_i32, _i64, _i64, _i64, _i64, _i64, _vp, _vp, _i64, _vp, _vp, _f32, _vp,
+                                  _vp, _vp]),
     "hca_attend_ws": (_sz, [_i64, _i64, _i64, _i64, _i64]),
     "hca_attend": (_i32, [_i32, _i64, _i64, _i64, _i64, _i64, _vp, _vp, _i64, _vp, _i64, _f32, _vp,
                           _vp, _vp, _sz, _vp]),
@@ -321,6 +323,29 @@ def csa_attend(q, Ccomp, idx, count, scale=0.0, out=None, lse=None, ws=None):
     _check("csa_attend", lib().csa_attend(
         _dt(q), B, n_q, n_h, c, k, _p(q), _p(Ccomp), Ccomp.shape[1], _p(idx), _p(count), float(scale),
         _p(out), _p(lse), _p(ws), ws.numel() * ws.element_size(), _stream(dev)))
+    return out, lse
+
+
+def csa_attend_noalloc(q, Ccomp, idx, count, out, lse, scale=0.0):
+    """csa_attend without a workspace: the library's static scratch array holds
+    the split partials (see include/dlc.h for its size limit).  ``out`` fp32
+    [B][n_q][n_h][c] and ``lse`` fp32 [B][n_q][n_h] are the caller's; nothing
+    is allocated on this path."""
+    dev = q.device
+    _on_device(dev, q=q, Ccomp=Ccomp, idx=idx, count=count, out=out, lse=lse)
+    B, n_q, n_h, c = q.shape
+    k = idx.shape[2]
+    _need(q.is_contiguous() and Ccomp.is_contiguous(), "inputs must be contiguous")
+    _need(Ccomp.dim() == 3 and Ccomp.shape[0] == B and Ccomp.shape[2] == c and Ccomp.dtype == q.dtype,
+          "Ccomp shape/dtype mismatch")
+    _exact(idx, "idx", torch.int32, (B, n_q, k))
+    _exact(count, "count", torch.int32, (B, n_q))
+    _need(out is not None and lse is not None, "out and lse are required")
+    _exact(out, "out", torch.float32, (B, n_q, n_h, c))
+    _exact(lse, "lse", torch.float32, (B, n_q, n_h))
+    _check("csa_attend_noalloc", lib().csa_attend_noalloc(
+        _dt(q), B, n_q, n_h, c, k, _p(q), _p(Ccomp), Ccomp.shape[1], _p(idx), _p(count), float(scale),
+        _p(out), _p(lse), _stream(dev)))
     return out, lse
 
 

@@ -32,6 +32,8 @@
 // The VALU path covers fp32 and other shapes.
 #include "common.hpp"
 
+#include <mutex>
+
 namespace dlc {
 namespace {
 
@@ -1326,7 +1328,70 @@ int window_tail(const char* name, AttArgs& a, const void* Cwin, int64_t ring, in
   return DLC_OK;
 }
 
+// csa_attend with its caller-checked arguments; ws is the workspace (or the
+// scratch array of csa_attend_noalloc)
+int csa_attend_impl(const char* name, int dtype, int64_t B, int64_t n_q, int64_t n_h, int64_t c, int64_t k,
+                    const void* q, const void* Ccomp, int64_t cap, const int32_t* idx, const int32_t* count,
+                    float scale, float* out, float* lse, void* ws, size_t ws_bytes, hipStream_t s) {
+  AttArgs a{};
+  a.q = q; a.kv = Ccomp; a.idx = idx; a.count = count;
+  a.n_q = n_q; a.n_h = n_h; a.c = c; a.cap = cap; a.k = k;
+  a.scale_log2 = (scale > 0.f ? scale : 1.f / std::sqrt(float(c))) * kLog2e;
+  return run_attend<kGather>(name, dtype, a, B * n_q, k, out, lse, ws, ws_bytes, s);
+}
+
+int csa_attend_checks(const char* name, int dtype, int64_t B, int64_t n_q, int64_t n_h, int64_t c, int64_t k,
+                      const void* q, const void* Ccomp, int64_t cap, const int32_t* idx, const int32_t* count,
+                      const float* out) {
+  int rc = common_checks(name, dtype, B, n_q, n_h, c, q, Ccomp, cap, out);
+  if (rc) return rc;
+  DLC_REQUIRE(k >= 1, DLC_E_INVAL, "%s: k must be >= 1", name);
+  DLC_REQUIRE(idx && count, DLC_E_INVAL, "%s: NULL idx or count", name);
+  return DLC_OK;
+}
+
 }  // namespace
+
+// ------------------------------------------------------------------ allocation-free entry point
+//
+// csa_attend_noalloc keeps its split partials in this file-scope device array
+// instead of a caller workspace.  Every device the library runs on holds its
+// own copy at its own address until the process ends.  Host code never uses
+// the array's name as a device address: the address is taken once per device
+// with hipGetSymbolAddress (that device current) and kept in g_scratch_ptr.
+constexpr size_t kScratchBytes = size_t(32) << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// the scratch array's address on the device of stream s
+int scratch_for_stream(const char* name, hipStream_t s, void** out) {
+  int dev = -1;
+  hipError_t e = hipStreamGetDevice(s, &dev);
+  if (e != hipSuccess) return fail(DLC_E_HIP, "%s: hipStreamGetDevice: %s", name, hipGetErrorString(e));
+  DLC_REQUIRE(dev >= 0 && dev < kMaxDevices, DLC_E_UNSUPPORTED, "%s: device %d out of range", name, dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    int cur = -1;
+    e = hipGetDevice(&cur);
+    if (e != hipSuccess) return fail(DLC_E_HIP, "%s: hipGetDevice: %s", name, hipGetErrorString(e));
+    if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess)
+      return fail(DLC_E_HIP, "%s: hipSetDevice: %s", name, hipGetErrorString(e));
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (cur != dev) (void)hipSetDevice(cur);
+    if (e != hipSuccess || p == nullptr)
+      return fail(DLC_E_HIP, "%s: hipGetSymbolAddress: %s", name, hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return DLC_OK;
+}
+}  // namespace
+
 }  // namespace dlc
 
 extern "C" {
@@ -1345,15 +1410,28 @@ int csa_attend(int dtype, int64_t B, int64_t n_q, int64_t n_h, int64_t c, int64_
                const void* Ccomp, int64_t cap, const int32_t* idx, const int32_t* count, float scale, float* out,
                float* lse, void* ws, size_t ws_bytes, void* stream) {
   using namespace dlc;
-  int rc = common_checks("csa_attend", dtype, B, n_q, n_h, c, q, Ccomp, cap, out);
+  int rc = csa_attend_checks("csa_attend", dtype, B, n_q, n_h, c, k, q, Ccomp, cap, idx, count, out);
   if (rc) return rc;
-  DLC_REQUIRE(k >= 1, DLC_E_INVAL, "csa_attend: k must be >= 1");
-  DLC_REQUIRE(idx && count, DLC_E_INVAL, "csa_attend: NULL idx or count");
-  AttArgs a{};
-  a.q = q; a.kv = Ccomp; a.idx = idx; a.count = count;
-  a.n_q = n_q; a.n_h = n_h; a.c = c; a.cap = cap; a.k = k;
-  a.scale_log2 = (scale > 0.f ? scale : 1.f / std::sqrt(float(c))) * kLog2e;
-  return run_attend<kGather>("csa_attend", dtype, a, B * n_q, k, out, lse, ws, ws_bytes, as_stream(stream));
+  return csa_attend_impl("csa_attend", dtype, B, n_q, n_h, c, k, q, Ccomp, cap, idx, count, scale, out, lse, ws,
+                         ws_bytes, as_stream(stream));
+}
+
+int csa_attend_noalloc(int dtype, int64_t B, int64_t n_q, int64_t n_h, int64_t c, int64_t k, const void* q,
+                       const void* Ccomp, int64_t cap, const int32_t* idx, const int32_t* count, float scale,
+                       float* out, float* lse, void* stream) {
+  using namespace dlc;
+  const char* name = "csa_attend_noalloc";
+  int rc = csa_attend_checks(name, dtype, B, n_q, n_h, c, k, q, Ccomp, cap, idx, count, out);
+  if (rc) return rc;
+  const size_t need = csa_attend_ws(B, n_q, n_h, c, k);
+  DLC_REQUIRE(need <= kScratchBytes, DLC_E_UNSUPPORTED,
+              "%s: this shape needs %zu bytes of scratch, more than the %zu-byte static scratch array", name, need,
+              kScratchBytes);
+  void* ws = nullptr;
+  hipStream_t s = as_stream(stream);
+  if (need > 0 && (rc = scratch_for_stream(name, s, &ws))) return rc;
+  return csa_attend_impl(name, dtype, B, n_q, n_h, c, k, q, Ccomp, cap, idx, count, scale, out, lse, ws,
+                         need > 0 ? kScratchBytes : 0, s);
 }
 
 int hca_attend(int dtype, int64_t B, int64_t n_q, int64_t n_h, int64_t c, int64_t m_prime, const void* q,

@@ -206,6 +206,23 @@ int csa_attend(int dtype, int64_t B, int64_t n_q, int64_t n_h, int64_t c, int64_
                float scale, float* out, float* lse, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * csa_attend_noalloc - csa_attend for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): the same arguments without the workspace, the same
+ * kernels and bit-identical results.  Its split-K partials live in a static
+ * device array of 32 MiB (33554432 bytes) that every device the library runs
+ * on holds until the process ends; a shape whose csa_attend_ws(B, n_q, n_h, c,
+ * k) exceeds that returns DLC_E_UNSUPPORTED before anything is enqueued.  The
+ * call allocates and frees nothing.  All calls on one device share that
+ * device's array: calls that overlap on one device (concurrent streams or
+ * host threads) race and must be serialised by the caller.  Nothing in the
+ * array needs to start at zero; each call writes every byte it reads.
+ */
+int csa_attend_noalloc(int dtype, int64_t B, int64_t n_q, int64_t n_h, int64_t c, int64_t k,
+                       const void* q, const void* Ccomp, int64_t cap, const int32_t* idx, const int32_t* count,
+                       float scale, float* out, float* lse, void* stream);
+
+/*
  * hca_attend - dense shared-KV attention over every visible HCA entry
  * s < min(floor(t/m'), cap) ([Scratch] §10 and the unified operator of §11,
  * whose top-k is a no-op for HCA).  Same formula, layouts and empty-case
