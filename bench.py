@@ -188,9 +188,8 @@ def build_workload(cfg, dev, n_dec, n_sets=3):
     Q = dict(qI=per_step(qI, 1, cfg.n_hI, cI), wI=per_step(wI, 1, cfg.n_hI), q=per_step(q, 1, cfg.n_h, c),
              qh=per_step(qh, 1, cfg.n_h, c), cQ=per_step(cQ, 1, cfg.d_c))
     torch.cuda.synchronize()
-    del H_dec
     return dict(S=S, col=col, sets=sets, Q=Q, rings=rings, ring=ring, n_ctx=n_ctx, n_tot=n_tot, cap_csa=cap_csa,
-                cap_hca=cap_hca,
+                cap_hca=cap_hca, H_dec=H_dec, Wq=Wq,
                 t_proj=t_proj, t_comp=t_comp, stream_bytes=S.numel() * 2)
 
 
@@ -372,6 +371,151 @@ def step_bytes(cfg, t, fp4=False):
     return B * (idx_b + csa_b + hca_b + comp), B * idx_b
 
 
+def percentiles(ms):
+    import numpy as np
+    a = np.asarray(ms, dtype=np.float64)
+    return {"p10": round(float(np.percentile(a, 10)), 5), "median": round(float(np.median(a)), 5),
+            "p90": round(float(np.percentile(a, 90)), 5)}
+
+
+def timed_calls(fn, n, warmup=3):
+    """fn(i) enqueues one step; returns (mean ms over n steps from one event pair,
+    per-step ms from a second pass with an event pair around every step)."""
+    import torch
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(n):
+        fn(i)
+    e1.record()
+    torch.cuda.synchronize()
+    mean_ms = e0.elapsed_time(e1) / n
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    for i in range(n):
+        evs[i][0].record()
+        fn(i)
+        evs[i][1].record()
+    torch.cuda.synchronize()
+    return mean_ms, [a.elapsed_time(b) for a, b in evs]
+
+
+def stage_configs(dev, n, n_sets=3):
+    """Configs csa128k (csa_index_topk + csa_attend, B = 8 queries at t = 131072
+    over 32768 entries) and hca1m (hca_attend, B = 16 queries at t = 2^20 over
+    8192 entries), inputs ~N(0,1) drawn as the configs state, n_sets cache sets
+    rotating per step so the caches stream from HBM."""
+    import torch
+
+    import dense_long_context_amd as dlc
+    import synth
+    from synth import get_config
+
+    out = {}
+    # ---- csa128k
+    cfg = get_config("csa128k")
+    B, c, cI, m, k, t, n_h, n_hI = cfg.B, cfg.c, cfg.cI, cfg.m, cfg.k, cfg.t, cfg.n_h, cfg.n_hI
+    nv = t // m
+    ts = synth.tensor_seed
+    sets = []
+    for i in range(n_sets):
+        Cc = synth.normal_chunked_rows(B * nv, c, ts(cfg.seed, "Ccomp") + 100 * i, 1.0, "bf16", dev).reshape(B, nv, c)
+        KI = synth.normal_chunked_rows(B * nv, cI, ts(cfg.seed, "KI") + 100 * i, 1.0, "bf16", dev).reshape(B, nv, cI)
+        sets.append((Cc, KI))
+    q = synth.normal((B, 1, n_h, c), ts(cfg.seed, "q"), dtype="bf16", device=dev)
+    qI = synth.normal((B, 1, n_hI, cI), ts(cfg.seed, "qI"), dtype="bf16", device=dev)
+    wI = synth.normal((B, 1, n_hI), ts(cfg.seed, "wI"), dtype="f32", device=dev)
+    tt = torch.full((B, 1), t, dtype=torch.int64, device=dev)
+    idx = torch.empty((B, 1, k), dtype=torch.int32, device=dev)
+    cnt = torch.empty((B, 1), dtype=torch.int32, device=dev)
+    o = torch.empty((B, 1, n_h, c), device=dev)
+    lse = torch.empty((B, 1, n_h), device=dev)
+    ws_i = torch.zeros(dlc.csa_index_topk_ws(B, 1, nv, k), dtype=torch.uint8, device=dev)
+    ws_c = torch.empty(max(1, dlc.csa_attend_ws(B, 1, n_h, c, k)), dtype=torch.uint8, device=dev)
+
+    def csa_step(i):
+        Cc, KI = sets[i % n_sets]
+        dlc.csa_index_topk(qI, wI, KI, tt, t, m, k, idx=idx, count=cnt, ws=ws_i)
+        dlc.csa_attend(q, Cc, idx, cnt, out=o, lse=lse, ws=ws_c)
+    mean_ms, per = timed_calls(csa_step, n)
+    byts = B * (nv * cI * 2 + n_hI * cI * 2 + 4 * n_hI + min(k, nv) * c * 2 + n_h * c * 2 + 4 * n_h * c + 4 * n_h)
+    out["csa128k"] = {"workload": "csa128k decode: csa_index_topk + csa_attend, B=8 queries at t=131072 "
+                                  "(32768 entries), k=1024, n_h=128, c=512, n_hI=64, cI=128",
+                      "query_tokens_per_s": round(B / (mean_ms * 1e-3), 1), "ms_per_step": round(mean_ms, 5),
+                      "ms_per_step_events": percentiles(per),
+                      "algorithmic_bytes_per_step": int(byts),
+                      "hbm_gbs": round(byts / (mean_ms * 1e-3) / 1e9, 1),
+                      "frac_of_8tbs": round(byts / (mean_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+    del sets, ws_i, ws_c
+    torch.cuda.empty_cache()
+    # ---- hca1m
+    cfg = get_config("hca1m")
+    B, c, mp, t, n_h = cfg.B, cfg.c, cfg.m_prime, cfg.t, cfg.n_h
+    nv = t // mp
+    caches = [synth.normal_chunked_rows(B * nv, c, ts(cfg.seed, "Chca") + 100 * i, 1.0, "bf16", dev).reshape(B, nv, c)
+              for i in range(n_sets)]
+    q = synth.normal((B, 1, n_h, c), ts(cfg.seed, "q"), dtype="bf16", device=dev)
+    tt = torch.full((B, 1), t, dtype=torch.int64, device=dev)
+    o = torch.empty((B, 1, n_h, c), device=dev)
+    lse = torch.empty((B, 1, n_h), device=dev)
+    ws_h = torch.empty(max(1, dlc.hca_attend_ws(B, 1, n_h, c, nv)), dtype=torch.uint8, device=dev)
+
+    def hca_step(i):
+        dlc.hca_attend(q, caches[i % n_sets], tt, t, mp, out=o, lse=lse, ws=ws_h)
+    mean_ms, per = timed_calls(hca_step, n)
+    byts = B * (nv * c * 2 + n_h * c * 2 + 4 * n_h * c + 4 * n_h)
+    flop = B * 4.0 * nv * n_h * c
+    out["hca1m"] = {"workload": "hca1m decode: hca_attend, B=16 queries at t=2^20 over 8192 entries, n_h=128, c=512",
+                    "query_tokens_per_s": round(B / (mean_ms * 1e-3), 1), "ms_per_step": round(mean_ms, 5),
+                    "ms_per_step_events": percentiles(per),
+                    "algorithmic_bytes_per_step": int(byts), "algorithmic_flop_per_step": int(flop),
+                    "hbm_gbs": round(byts / (mean_ms * 1e-3) / 1e9, 1),
+                    "frac_of_8tbs": round(byts / (mean_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                    "tflops": round(flop / (mean_ms * 1e-3) / 1e12, 1),
+                    "mfma_frac": round(flop / (mean_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                    "bound_note": "at 8 TB/s the 140.5 MB take 17.6 us, at 2.5 PFLOP/s the 34.4 GFLOP 13.7 us: "
+                                  "even HBM-bound at peak the MFMA fraction is at most 0.78"}
+    del caches, ws_h
+    torch.cuda.empty_cache()
+    return out
+
+
+def query_projections(cfg, wl, n):
+    """The decode queries' projections of one step (B tokens): c^Q = h W^DQ,
+    q^I = c^Q W^IUQ, w^I = h W^w, q = c^Q W^UQ and the HCA q, all dlc_project."""
+    import torch
+
+    import dense_long_context_amd as dlc
+
+    B, d = cfg.B, cfg.d
+    H = wl["H_dec"]                      # [B][n_dec][d]
+    Wq = wl["Wq"]
+    n_dec = H.shape[1]
+    hs = [H[:, s].contiguous() for s in range(min(n, n_dec))]
+    cQ = torch.empty((B, cfg.d_c), dtype=torch.bfloat16, device=H.device)
+    qI = torch.empty((B, cfg.n_hI * cfg.cI), dtype=torch.bfloat16, device=H.device)
+    wI = torch.empty((B, cfg.n_hI), dtype=torch.float32, device=H.device)
+    q = torch.empty((B, cfg.n_h * cfg.c), dtype=torch.bfloat16, device=H.device)
+    qh = torch.empty_like(q)
+
+    def step(i):
+        h = hs[i % len(hs)]
+        dlc.dlc_project(h, Wq["DQ"], out=cQ)
+        dlc.dlc_project(cQ, Wq["IUQ"], out=qI)
+        dlc.dlc_project(h, Wq["w"], out=wI)
+        dlc.dlc_project(cQ, Wq["UQ"], out=q)
+        dlc.dlc_project(cQ, Wq["UQ_hca"], out=qh)
+    mean_ms, per = timed_calls(step, n)
+    wbytes = 2 * (d * cfg.d_c + cfg.d_c * cfg.n_hI * cfg.cI + d * cfg.n_hI + 2 * cfg.d_c * cfg.n_h * cfg.c)
+    flop = 2.0 * B * (d * cfg.d_c + cfg.d_c * cfg.n_hI * cfg.cI + d * cfg.n_hI + 2 * cfg.d_c * cfg.n_h * cfg.c)
+    return {"ms_per_step": round(mean_ms, 5), "ms_per_step_events": percentiles(per),
+            "weight_bytes_per_step": int(wbytes), "weight_gbs": round(wbytes / (mean_ms * 1e-3) / 1e9, 1),
+            "tflops": round(flop / (mean_ms * 1e-3) / 1e12, 2),
+            "note": "dlc_project x5 for the B decode tokens of a step (c^Q, q^I, w^I, q, HCA q); weight-read "
+                    "bound at this batch; outside the compressed-attention step and its value"}
+
+
 def run_steps(steps, s0, n, n_dec):
     for j in range(s0, s0 + n):
         for fn, args in steps[j % n_dec][1]:
@@ -381,43 +525,69 @@ def run_steps(steps, s0, n, n_dec):
                 raise RuntimeError(f"{fn.__name__} failed: {binding.last_error()}")
 
 
-def cpu_baseline(cfg, budget_s=15.0):
-    """The oracle, as it stands, on a bounded sample of the same decode step:
-    the indexer over 2^18 entries, top-k, CSA attention over the k selected
-    entries and HCA attention over 8192 entries, for one query at a time.
-    Inputs are drawn by synth with the workload's shapes and distributions."""
-    import numpy as np
-
-    import oracle as O
-    import synth
-
+def blas_info():
+    """Threads and library of the BLAS numpy runs on, and the host's core counts."""
+    info = {"cpu_count": os.cpu_count(), "affinity": len(os.sched_getaffinity(0))}
     try:
         from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        blas = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        if blas:
+            info["blas"] = f"{blas[0].get('internal_api')} {blas[0].get('version')}"
+            info["threads"] = int(max(i.get("num_threads", 1) for i in blas))
     except Exception:  # pragma: no cover
-        threads = os.cpu_count()
-    t = cfg.t
-    nv, nh_v = t // cfg.m, t // cfg.m_prime
-    KI = O.f64(synth.normal((nv, cfg.cI), 9001, dtype="bf16"))
-    Cc = O.f64(synth.normal((nv, cfg.c), 9002, dtype="bf16"))
-    Ch = O.f64(synth.normal((nh_v, cfg.c), 9003, dtype="bf16"))
-    done, t0 = 0, time.perf_counter()
-    while True:
-        qI = synth.normal((cfg.n_hI, cfg.cI), 9100 + done, dtype="bf16")
-        wI = synth.normal((cfg.n_hI,), 9200 + done, dtype="f32")
-        q = synth.normal((cfg.n_h, cfg.c), 9300 + done, dtype="bf16")
-        sc = O.index_scores(qI, wI, KI, t, cfg.m)
-        sel = O.topk_select(sc, cfg.k)
-        O.csa_attend(q, Cc, sel)
-        O.hca_attend(q, Ch, t, cfg.m_prime)
+        pass
+    info.setdefault("threads", info["affinity"])
+    return info
+
+
+def cpu_baseline(cfg, wl, steps, s_first, n_steps, budget_s=15.0):
+    """The oracle, as it stands, on a bounded sample of the GPU line's own
+    decode steps: the same query rows (copied to the host) against the same
+    caches (sequences 0 and 1; every cache set holds the same values), one
+    query at a time: indexer scores over all visible entries, top-k, CSA
+    attention over the rows the oracle selects, HCA attention over every
+    visible entry.  Only the oracle calls are timed."""
+    import numpy as np
+    import torch
+
+    import oracle as O
+
+    m, mp, k = cfg.m, cfg.m_prime, cfg.k
+    Cc, KI, Ch = wl["sets"][0][:3]
+    Q = wl["Q"]
+    host = {}
+    for b in (0, 1):
+        host[b] = (KI[b].cpu(), Cc[b].cpu(), Ch[b].cpu())
+    done, spent = 0, 0.0
+    n_dec = len(steps)
+    j = 0
+    while spent < budget_s and j < 4 * n_steps:
+        s = (s_first + j // 2) % n_dec
+        b = j % 2
+        t = steps[s][0]
+        KIh, Cch, Chh = host[b]
+        qI, wI = Q["qI"][s][b, 0].cpu(), Q["wI"][s][b, 0].cpu()
+        q, qh = Q["q"][s][b, 0].cpu(), Q["qh"][s][b, 0].cpu()
+        t0 = time.perf_counter()
+        sc = O.index_scores(qI, wI, KIh[:t // m], t, m)
+        sel = O.topk_select(sc, k)
+        t1 = time.perf_counter()
+        rows = Cch[torch.as_tensor(sel)]                    # the selected entries (host gather, untimed)
+        t2 = time.perf_counter()
+        O.csa_attend(q, rows, np.arange(len(sel)))
+        O.hca_attend(qh, Chh, t, mp)
+        t3 = time.perf_counter()
+        spent += (t1 - t0) + (t3 - t2)
         done += 1
-        el = time.perf_counter() - t0
-        if el >= budget_s or done >= 256:
-            break
-    return {"value": done / el, "unit": "decode query-tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{done} decode queries at t=2^20 (indexer over {nv} entries, top-{cfg.k}, CSA attention "
-                      f"over the selected entries, HCA attention over {nh_v} entries), fp64 numpy, "
-                      f"{el:.1f} s; the per-step compressor work (one entry every m tokens) is omitted"}
+        j += 1
+    bi = blas_info()
+    return {"value": done / spent, "unit": "decode query-tokens/s", "cores": int(bi["threads"]), "kind": "oracle",
+            "host": bi,
+            "sample": f"{done} decode queries of the timed steps (sequences 0 and 1, t = {steps[s_first][0]} ..): "
+                      f"indexer over all floor(t/m) entries, top-{k}, CSA attention over the selected entries, "
+                      f"HCA attention over floor(t/m') entries; fp64 numpy on the GPU line's own query rows and "
+                      f"caches, {spent:.1f} s of oracle time; the per-step compressor work (one entry every m "
+                      f"tokens) is left out"}
 
 
 PMC_COPY_BYTES = 1 << 30
@@ -505,6 +675,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=16)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true", help="skip the chunked-prefill measurement")
+    ap.add_argument("--no-configs", action="store_true", help="skip the csa128k and hca1m lines")
     ap.add_argument("--prefill-only", action="store_true",
                     help="build the caches, run only the chunked prefill (bf16 and FP4 indexer) and print its JSON")
     ap.add_argument("--repeat", type=int, default=1, help="time the K steps this many times, report the best")
@@ -587,6 +758,8 @@ def main():
         if best is None or ms < best[0]:
             best = (ms, k_ms, ms_armed)
     ms, k_ms, ms_armed = best
+    # per-step spread: the same steps once more with an event pair around each
+    _, step_ms = timed_calls(lambda j: run_steps(steps, args.warmup + j, 1, n_dec), K, warmup=0)
     # the same steps with each layer's sliding-window branch joined in (reported beside the main line)
     steps_w, keep_w = make_steps(cfg, wl, dev, n_dec, window=True)
     run_steps(steps_w, 0, args.warmup, n_dec)
@@ -659,6 +832,7 @@ def main():
                      "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic,
                      "avg_launch_us": round(k_avg_ms * 1e3, 3),
                      "algorithmic_bytes_per_launch": int(idx_bytes)},
+        "ms_per_step_events": percentiles(step_ms),
         "ms_per_step_with_kernel_events": round(ms_armed / K, 5),
         "with_sliding_window": {"value": round(cfg.B * K / (ms_win * 1e-3), 1), "ms_per_step": round(ms_win / K, 5),
                                 "n_win": N_WIN, "note": "csa_attend_window / hca_attend_window: each layer's "
@@ -677,6 +851,11 @@ def main():
         "setup": {"projection_s": round(wl["t_proj"], 3), "compress_ms_per_cache_set": round(wl["t_comp"] * 1e3, 2),
                   "compress_stream_gbs": round(wl["stream_bytes"] / wl["t_comp"] / 1e9, 1)},
     }
+    log("decode query projections")
+    result["query_projection"] = query_projections(cfg, wl, K)
+    if not args.no_configs:
+        log("configs csa128k and hca1m")
+        result["configs"] = stage_configs(dev, max(K, 20))
     if not args.no_prefill:
         log("chunked causal prefill of 4096 queries per sequence")
         pf = prefill_pass(cfg, wl, dev, ev=ev)
@@ -700,7 +879,7 @@ def main():
                     "MXFP4 key cache"}
     if not args.no_cpu_baseline:
         log("timing the oracle on a bounded sample")
-        result["cpu_baseline"] = cpu_baseline(cfg)
+        result["cpu_baseline"] = cpu_baseline(cfg, wl, steps, args.warmup, K)
     else:
         result["cpu_baseline"] = None
     del keep
