@@ -136,15 +136,21 @@ def build_workload(cfg, dev, n_dec, n_sets=3):
     S = torch.empty((B, n_tot, NS), dtype=torch.bfloat16, device=dev)
     H_dec = torch.empty((B, n_dec, d), dtype=torch.bfloat16, device=dev)  # hidden states of the decode tokens
     chunk = 1 << 16
+    evs = []
     for b in range(B):
         for r0 in range(0, n_tot, chunk):
             r1 = min(n_tot, r0 + chunk)
             Hc = hidden_rows(cfg, b, n_tot, r0, r1, dev)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
             dlc.dlc_project(Hc, Wt, out=S[b, r0:r1])
+            e1.record()
+            evs.append((e0, e1))
             if r0 <= n_ctx < r1:
                 H_dec[b] = Hc[n_ctx - r0:n_ctx - r0 + n_dec]
     torch.cuda.synchronize()
     t_proj = time.perf_counter() - t0
+    t_proj_kernel = sum(a.elapsed_time(b) for a, b in evs) / 1e3
     col = lambda nm: S[:, :, off[nm]:off[nm] + width[nm]]  # noqa: E731
 
     cap_csa, cap_hca = n_tot // m, n_tot // mp
@@ -190,7 +196,60 @@ def build_workload(cfg, dev, n_dec, n_sets=3):
     torch.cuda.synchronize()
     return dict(S=S, col=col, sets=sets, Q=Q, rings=rings, ring=ring, n_ctx=n_ctx, n_tot=n_tot, cap_csa=cap_csa,
                 cap_hca=cap_hca, H_dec=H_dec, Wq=Wq,
-                t_proj=t_proj, t_comp=t_comp, stream_bytes=S.numel() * 2)
+                t_proj=t_proj, t_proj_kernel=t_proj_kernel, t_comp=t_comp, stream_bytes=S.numel() * 2)
+
+
+def fused_setup(cfg, wl, dev):
+    """The three caches of the workload again, straight from the hidden rows by
+    csa_project_compress (C^Comp and K^I) and hca_project_compress (C^HCA),
+    chunk by chunk of rows as the two-pass build projects them; returns the
+    summed kernel time (HIP events) and whether every cache equals the
+    two-pass build's bit for bit."""
+    import torch
+
+    import dense_long_context_amd as dlc
+    from dense_long_context_amd import binding
+
+    L = binding.lib()
+    B, d, c, cI, m, mp = cfg.B, cfg.d, cfg.c, cfg.cI, cfg.m, cfg.m_prime
+    n_tot = wl["n_tot"]
+    Wt = {nm: stream_weight(cfg, nm).t().contiguous().to(dev) for nm in STREAMS}
+    Cc0, KI0, Ch0 = wl["sets"][0][:3]
+    Cc, KI, Ch = torch.empty_like(Cc0), torch.empty_like(KI0), torch.empty_like(Ch0)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    chunk = 1 << 16
+    assert chunk % mp == 0 and chunk % m == 0
+    evs = []
+    for b in range(B):
+        for r0 in range(0, n_tot, chunk):
+            r1 = min(n_tot, r0 + chunk)
+            h0 = max(0, r0 - m)  # CSA entries of this chunk also pool the block before it
+            Hc = hidden_rows(cfg, b, n_tot, h0, r1, dev)
+            rows = r1 - h0
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            # rows h0 .. r1-1 as the call's sequence: its entry i is entry h0/m + i
+            # of the cache; the first is skipped when it needs the rows before h0
+            for out, nm, width in ((Cc, "", c), (KI, "I", cI)):
+                i0 = 0 if h0 == 0 else 1
+                rc = L.csa_project_compress(
+                    binding.DLC_BF16, 1, rows, d, width, m, Hc.data_ptr(), d, rows * d,
+                    Wt[nm + "aZ"].data_ptr(), Wt[nm + "bZ"].data_ptr(), Wt[nm + "aKV"].data_ptr(),
+                    Wt[nm + "bKV"].data_ptr(), d, None, None, i0, rows // m,
+                    out.data_ptr() + (b * out.shape[1] + h0 // m) * width * 2, out.shape[1] - h0 // m, stream)
+                assert rc == 0, binding.last_error()
+            Hh = Hc[r0 - h0:]
+            rc = L.hca_project_compress(
+                binding.DLC_BF16, 1, r1 - r0, d, c, mp, Hh.data_ptr(), d, (r1 - r0) * d, Wt["Z"].data_ptr(),
+                Wt["KV"].data_ptr(), d, None, 0, (r1 - r0) // mp,
+                Ch.data_ptr() + (b * Ch.shape[1] + r0 // mp) * c * 2, Ch.shape[1] - r0 // mp, stream)
+            assert rc == 0, binding.last_error()
+            e1.record()
+            evs.append((e0, e1))
+    torch.cuda.synchronize()
+    t = sum(a.elapsed_time(b) for a, b in evs) / 1e3
+    same = all(torch.equal(x, y) for x, y in ((Cc, Cc0), (KI, KI0), (Ch, Ch0)))
+    return t, same
 
 
 def make_steps(cfg, wl, dev, n_dec, window=False, fp4=False):
@@ -210,7 +269,7 @@ def make_steps(cfg, wl, dev, n_dec, window=False, fp4=False):
     S, col = wl["S"], wl["col"]
     ld, bs = S.stride(1), S.stride(0)
     n_tot, cap_csa, cap_hca = wl["n_tot"], wl["cap_csa"], wl["cap_hca"]
-    ws_i = torch.empty(max(dlc.csa_index_topk_ws(B, 1, cap_csa, k),
+    ws_i = torch.zeros(max(dlc.csa_index_topk_ws(B, 1, cap_csa, k),
                            dlc.csa_index_topk_fp4_ws(B, 1, n_hI, cI, cap_csa, k)), dtype=torch.uint8, device=dev)
     ws_c = torch.empty(max(1, dlc.csa_attend_ws(B, 1, n_h, c, k)), dtype=torch.uint8, device=dev)
     ws_h = torch.empty(max(1, dlc.hca_attend_ws(B, 1, n_h, c, cap_hca)), dtype=torch.uint8, device=dev)
@@ -298,7 +357,7 @@ def prefill_pass(cfg, wl, dev, n_pref=4096, chunk=256, ev=None, fp4=False):
             t=torch.arange(n_ctx - n_pref + c0, n_ctx - n_pref + c0 + chunk, device=dev,
                            dtype=torch.int64)[None].expand(B, chunk).contiguous()))
         del h, cQ
-    ws_i = torch.empty(max(dlc.csa_index_topk_ws(B, chunk, wl["cap_csa"], k),
+    ws_i = torch.zeros(max(dlc.csa_index_topk_ws(B, chunk, wl["cap_csa"], k),
                            dlc.csa_index_topk_fp4_ws(B, chunk, n_hI, cI, wl["cap_csa"], k)), dtype=torch.uint8,
                        device=dev)
     ws_c = torch.empty(max(1, dlc.csa_attend_ws(B, chunk, n_h, c, k)), dtype=torch.uint8, device=dev)
@@ -676,6 +735,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true", help="skip the chunked-prefill measurement")
     ap.add_argument("--no-configs", action="store_true", help="skip the csa128k and hca1m lines")
+    ap.add_argument("--no-fused", action="store_true", help="skip the fused projection + pooling set-up pass")
     ap.add_argument("--prefill-only", action="store_true",
                     help="build the caches, run only the chunked prefill (bf16 and FP4 indexer) and print its JSON")
     ap.add_argument("--repeat", type=int, default=1, help="time the K steps this many times, report the best")
@@ -851,6 +911,17 @@ def main():
         "setup": {"projection_s": round(wl["t_proj"], 3), "compress_ms_per_cache_set": round(wl["t_comp"] * 1e3, 2),
                   "compress_stream_gbs": round(wl["stream_bytes"] / wl["t_comp"] / 1e9, 1)},
     }
+    if not args.no_fused:
+        log("fused projection + pooling pass")
+        t_fused, same = fused_setup(cfg, wl, dev)
+        flops = 2.0 * cfg.B * wl["n_tot"] * cfg.d * stream_layout(cfg)[2]
+        result["setup"].update({
+            "projection_kernel_s": round(wl["t_proj_kernel"], 3),
+            "projection_tflops": round(flops / wl["t_proj_kernel"] / 1e12, 1),
+            "two_pass_kernel_s": round(wl["t_proj_kernel"] + wl["t_comp"], 3),
+            "fused_kernel_s": round(t_fused, 3),
+            "fused_equals_two_pass": bool(same),
+        })
     log("decode query projections")
     result["query_projection"] = query_projections(cfg, wl, K)
     if not args.no_configs:

@@ -12,6 +12,7 @@ from .binding import (  # noqa: F401
     csa_attend_window,
     csa_attend_ws,
     csa_compress,
+    csa_project_compress,
     csa_index_topk,
     csa_index_topk_fp4,
     csa_index_topk_fp4_ws,
@@ -22,6 +23,7 @@ from .binding import (  # noqa: F401
     hca_attend_window,
     hca_attend_ws,
     hca_compress,
+    hca_project_compress,
     last_error,
     lib,
     mxfp4_quantize,

@@ -33,6 +33,10 @@ SIGNATURES = {
                             _i64, _i64, _vp, _i64, _vp]),
     "hca_compress": (_i32, [_i32, _i64, _i64, _i64, _i64, _vp, _vp, _i64, _i64, _vp, _i64, _i64,
                             _vp, _i64, _vp]),
+    "csa_project_compress": (_i32, [_i32, _i64, _i64, _i64, _i64, _i64, _vp, _i64, _i64, _vp, _vp, _vp, _vp,
+                                    _i64, _vp, _vp, _i64, _i64, _vp, _i64, _vp]),
+    "hca_project_compress": (_i32, [_i32, _i64, _i64, _i64, _i64, _i64, _vp, _i64, _i64, _vp, _vp, _i64, _vp,
+                                    _i64, _i64, _vp, _i64, _vp]),
     "csa_index_topk_ws": (_sz, [_i64, _i64, _i64, _i64]),
     "csa_index_topk": (_i32, [_i32, _i64, _i64, _i64, _i64, _i64, _i64, _vp, _vp, _vp, _i64, _vp,
                               _i64, _vp, _vp, _vp, _vp, _sz, _vp]),
@@ -197,6 +201,54 @@ def hca_compress(Z, Cs, m_prime, out, i_begin=0, i_end=None, bias=None, n=None):
     _check("hca_compress", lib().hca_compress(
         _dt(Z), B, n, c, m_prime, _p(Z), _p(Cs), _stride(Z, 1, c), _stride(Z, 0, rows * c), _p(bias), i_begin, i_end,
         _p(out), out.shape[1], _stream(Z.device)))
+    return out
+
+
+def _fused_inputs(H, Wts, out, c):
+    """Shape and layout checks shared by the fused projection + pooling calls:
+    H [B][rows][d] bf16 with contiguous rows, each Wt [c][d] (rows contiguous,
+    one leading dimension for all), out [B][cap][c] bf16 contiguous."""
+    _need(H.dim() == 3 and H.dtype == torch.bfloat16 and H.stride(2) == 1,
+          "H must be a bf16 [B][rows][d] tensor with contiguous rows")
+    B, rows, d = H.shape
+    for W in Wts:
+        _need(W.dim() == 2 and tuple(W.shape) == (c, d) and W.dtype == torch.bfloat16 and W.stride(1) == 1
+              and W.stride(0) == Wts[0].stride(0), "weights must be bf16 [c][d] with one row stride")
+    _need(out.dtype == torch.bfloat16 and out.dim() == 3 and out.shape[0] == B and out.shape[2] == c
+          and out.is_contiguous(), "out must be a contiguous bf16 [B][cap][c] tensor")
+    return B, rows, d
+
+
+def csa_project_compress(H, WtZa, WtZb, WtCa, WtCb, m, out, i_begin=0, i_end=None, Ba=None, Bb=None, n=None):
+    """CSA entries [i_begin, i_end) straight from hidden rows H [B][rows][d]:
+    the four stream projections (weights transposed, [c][d]) and the pooling in
+    one pass, equal to dlc_project of each stream followed by csa_compress."""
+    Wts = (WtZa, WtZb, WtCa, WtCb)
+    _on_device(H.device, H=H, WtZa=WtZa, WtZb=WtZb, WtCa=WtCa, WtCb=WtCb, out=out, Ba=Ba, Bb=Bb)
+    c = out.shape[-1]
+    B, rows, d = _fused_inputs(H, Wts, out, c)
+    _exact(Ba, "Ba", torch.float32, (m, c))
+    _exact(Bb, "Bb", torch.float32, (m, c))
+    n = rows if n is None else n
+    i_end = n // m if i_end is None else i_end
+    _check("csa_project_compress", lib().csa_project_compress(
+        DLC_BF16, B, n, d, c, m, _p(H), _stride(H, 1, d), _stride(H, 0, rows * d), _p(WtZa), _p(WtZb), _p(WtCa),
+        _p(WtCb), _stride(WtZa, 0, d), _p(Ba), _p(Bb), i_begin, i_end, _p(out), out.shape[1], _stream(H.device)))
+    return out
+
+
+def hca_project_compress(H, WtZ, WtC, m_prime, out, i_begin=0, i_end=None, bias=None, n=None):
+    """HCA entries [i_begin, i_end) straight from hidden rows H [B][rows][d]
+    (weights transposed, [c][d]), equal to dlc_project then hca_compress."""
+    _on_device(H.device, H=H, WtZ=WtZ, WtC=WtC, out=out, bias=bias)
+    c = out.shape[-1]
+    B, rows, d = _fused_inputs(H, (WtZ, WtC), out, c)
+    _exact(bias, "bias", torch.float32, (m_prime, c))
+    n = rows if n is None else n
+    i_end = n // m_prime if i_end is None else i_end
+    _check("hca_project_compress", lib().hca_project_compress(
+        DLC_BF16, B, n, d, c, m_prime, _p(H), _stride(H, 1, d), _stride(H, 0, rows * d), _p(WtZ), _p(WtC),
+        _stride(WtZ, 0, d), _p(bias), i_begin, i_end, _p(out), out.shape[1], _stream(H.device)))
     return out
 
 

@@ -11,23 +11,19 @@
 // an online softmax: all loads of a chunk are in flight together, the running
 // max moves once per chunk, and the pass costs one exp per logit plus one per
 // chunk, with no second pass over Z.
-#include "common.hpp"
+#include "pool_math.hpp"
 
 namespace dlc {
 
 namespace {
 
-#ifndef DLC_POOL_CHUNK
-#define DLC_POOL_CHUNK 4
-#endif
-constexpr int kChunk = DLC_POOL_CHUNK;
+constexpr int kChunk = kPoolChunk;
 // CSA entries per thread on the full-pass path (a window of 2m rows is only
 // two chunks: one entry alone is too little work for a wave's start-up)
 #ifndef DLC_POOL_EPT
 #define DLC_POOL_EPT 2
 #endif
 constexpr int64_t kEntriesPerThread = DLC_POOL_EPT;
-constexpr float kLog2e = 1.4426950408889634f;
 
 struct PoolArgs {
   const void* Z[2];      // [0]: a-stream (HCA: its only stream), [1]: b-stream
@@ -85,49 +81,10 @@ __device__ __forceinline__ void chunk_partial(const PoolArgs& a, int64_t boff, i
       load_cols<T, VEC>(C, j0, a.c, cv[rr]);
       load_bias<VEC>(a.bias[seg], rb, a.c, j0, bv);
 #pragma unroll
-      for (int u = 0; u < VEC; ++u) l[rr][u] = (l[rr][u] + bv[u]) * kLog2e;
+      for (int u = 0; u < VEC; ++u) l[rr][u] = pool_logit(l[rr][u], bv[u]);
     }
   }
-#pragma unroll
-  for (int u = 0; u < VEC; ++u) {
-    float cm = -INFINITY;
-#pragma unroll
-    for (int rr = 0; rr < kChunk; ++rr)
-      if (r0 + rr < r1) cm = fmaxf(cm, l[rr][u]);
-    float sm = 0.f, ac = 0.f;
-    // one v_exp_f32 per logit.  A -inf logit (the page's padding) gets weight
-    // exp2(-inf) = 0; a chunk whose logits are all -inf keeps max -inf and
-    // weights 0 (taking its max as the reference would give -inf - -inf = NaN),
-    // so it adds nothing when merged.
-    const float cref = cm == -INFINITY ? 0.f : cm;
-#pragma unroll
-    for (int rr = 0; rr < kChunk; ++rr) {
-      if (r0 + rr < r1) {
-        const float w = __builtin_amdgcn_exp2f(l[rr][u] - cref);
-        sm += w;
-        ac = fmaf(w, cv[rr][u], ac);
-      }
-    }
-    mx[u] = cm;
-    sum[u] = sm;
-    acc[u] = ac;
-  }
-}
-
-// state <- state (+) partial.  The same operations wherever two states meet,
-// so the result depends only on the chunk order, not on which lanes held them.
-template <int VEC>
-__device__ __forceinline__ void merge_state(float* mS, float* sS, float* aS, const float* mP, const float* sP,
-                                            const float* aP) {
-#pragma unroll
-  for (int u = 0; u < VEC; ++u) {
-    const float M = fmaxf(mS[u], mP[u]);
-    const float f1 = mS[u] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mS[u] - M);
-    const float f2 = mP[u] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mP[u] - M);
-    sS[u] = fmaf(sS[u], f1, sP[u] * f2);
-    aS[u] = fmaf(aS[u], f1, aP[u] * f2);
-    mS[u] = M;
-  }
+  chunk_fold<VEC>(l, cv, r1 - r0, mx, sum, acc);
 }
 
 // The entry's value is the left-to-right fold of its chunk partials.
@@ -145,7 +102,7 @@ __global__ void __launch_bounds__(256) pool_kernel(PoolArgs a) {
   auto store = [&](int64_t i, int64_t j0, const float* acc, const float* sum) {
     float o[VEC];
 #pragma unroll
-    for (int u = 0; u < VEC; ++u) o[u] = acc[u] / sum[u];
+    for (int u = 0; u < VEC; ++u) o[u] = pool_value(acc[u], sum[u]);
     T* out = static_cast<T*>(a.out) + (int64_t(blockIdx.y) * a.cap + i) * a.c + j0;
     if constexpr (VEC == 1) {
       Fmt<T>::store(out, o[0]);

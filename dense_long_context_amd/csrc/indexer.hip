@@ -5,25 +5,25 @@
 // visible entries s < floor(t/m)).
 //
 // Pipeline per call (all on the caller's stream):
-//   1. clear      zero the two digit histograms of every query
-//   2. scores     one pass over K^I: for bf16 with c^I % 32 == 0 the heads x keys
+//   1. scores     one pass over K^I: for bf16 with c^I % 32 == 0 the heads x keys
 //                 product runs on MFMA (v_mfma_f32_16x16x32_bf16) with the
 //                 queries held in registers; otherwise a VALU kernel; with
 //                 MXFP4 operands (csa_index_topk_fp4, §6.4's FP4 indexer) on
 //                 the block-scaled v_mfma_scale_f32_16x16x128_f8f6f4.  Each
 //                 workgroup also builds an LDS histogram of the top 11 bits of
 //                 the order-preserving score key and adds its non-zero bins to
-//                 the query's histogram.
-//   3. filter     every workgroup finds the threshold bin T from that
+//                 the query's histogram (which the previous call's selection
+//                 left at zero).
+//   2. select     every workgroup finds the threshold bin T from that
 //                 histogram and writes its chunk's entries above T (selected)
 //                 and in T (candidates, with their keys) to the chunk's own
 //                 segments in index order; the candidates' next 11 key bits go
-//                 into the query's second histogram.
-//   4. finish     one workgroup per query gathers the chunk lists, resolves the
-//                 candidates by radix passes over the remaining key bits and
-//                 then the index (ties go to the smaller index), starting from
-//                 the second histogram, and merges the two ascending lists into
-//                 idx / count.
+//                 into the query's second histogram.  The last workgroup of a
+//                 query resolves the candidates by radix passes over the
+//                 remaining key bits and then the index (ties go to the
+//                 smaller index), starting from the second histogram, and
+//                 writes the selected and chosen entries to their slots of
+//                 idx in ascending order.
 #include "common.hpp"
 #include "mxfp4.hpp"
 
@@ -33,6 +33,7 @@ namespace {
 constexpr int kBins = 2048;      // first digit: top 11 bits of the key
 constexpr int kShift1 = 21;
 constexpr int kMaxK = 8192;
+constexpr int kTicketStride = 32;  // words between the queries' arrival counters (one 128-byte line each)
 #ifndef DLC_PREFILL_NB
 #define DLC_PREFILL_NB 2  // stages of the prefill scores kernel's query ring
 #endif
@@ -57,8 +58,12 @@ struct IdxArgs {
   int32_t* sel;        // [BQ][cap] chunk c's selected entries start at c*keys_per_wg
   int32_t* cand;       // [BQ][cap] chunk c's candidates start at c*keys_per_wg
   uint32_t* cand_kseg; // [BQ][cap] their score keys, same positions
-  int32_t* cand_idx;   // [BQ][cap] compacted candidates when they overflow LDS
+  uint32_t* cand_srk;  // [BQ][cap] selected entries of the chunk before each candidate, same positions
+  uint32_t* ticket;    // [BQ][kTicketStride] selection workgroups of the query that have finished
+  int32_t* cand_idx;   // [BQ][cap] the query's candidates gathered, when they overflow LDS
   uint32_t* cand_key;  // [BQ][cap] their score keys
+  uint32_t* cand_srk2; // [BQ][cap] their selected-entry counts
+  int32_t* chosen;     // [BQ][k] the chosen candidates, when they overflow LDS
   int32_t* idx;        // [BQ][k]
   int32_t* count;      // [BQ]
   int64_t keys_per_wg; // scores / filter chunk
@@ -90,6 +95,16 @@ __device__ __forceinline__ void flush_hist(uint32_t* lds, uint32_t* global) {
   }
 }
 
+// The selection kernel that follows a scores kernel needs the query's second
+// histogram and arrival counter at zero: the first workgroup of each query
+// in the scores kernel clears them.
+__device__ __forceinline__ void clear_select_state(const IdxArgs& a, int64_t bq) {
+  if (blockIdx.x != 0) return;
+  uint4* h2 = reinterpret_cast<uint4*>(a.hist2 + bq * kBins);
+  for (int i = threadIdx.x; i < kBins / 4; i += blockDim.x) h2[i] = make_uint4(0, 0, 0, 0);
+  if (threadIdx.x == 0) a.ticket[bq * kTicketStride] = 0;
+}
+
 // ---------------------------------------------------------------- scores (VALU)
 
 template <typename T>
@@ -99,6 +114,7 @@ __global__ void __launch_bounds__(256) scores_valu_kernel(IdxArgs a) {
   float* q = smem + kBins;                // [n_hI][cI]
   float* w = q + a.n_hI * a.cI;           // [n_hI]
   const int64_t bq = blockIdx.y;
+  clear_select_state(a, bq);
   const int64_t nvis = visible(a, bq);
   const int64_t s0 = int64_t(blockIdx.x) * a.keys_per_wg;
   if (s0 >= nvis) return;
@@ -163,6 +179,7 @@ __global__ void __launch_bounds__(256) scores_mfma_kernel(IdxArgs a) {
   __shared__ __attribute__((aligned(1024))) unsigned char sK[4][NS][TILEB];
   __shared__ float sS[4][kScoreBuf * 16];
   const int64_t bq = blockIdx.y;
+  clear_select_state(a, bq);
   const int64_t s0 = int64_t(blockIdx.x) * a.keys_per_wg;
   // The grid covers floor(t_max/m) <= cap entries, so rows below s1l exist
   // whatever this query's t: the first tiles go out by that bound, before
@@ -870,6 +887,7 @@ __global__ void __launch_bounds__(512) scores_prefill_fp4_kernel(IdxArgs a) {
 __global__ void __launch_bounds__(256) hist_kernel(IdxArgs a) {
   __shared__ uint32_t hist[kBins];
   const int64_t bq = blockIdx.y;
+  clear_select_state(a, bq);
   const int64_t nvis = visible(a, bq);
   const int64_t s0 = int64_t(blockIdx.x) * a.keys_per_wg;
   if (s0 >= nvis) return;
@@ -911,52 +929,16 @@ __global__ void __launch_bounds__(256) hist_kernel(IdxArgs a) {
 // ---------------------------------------------------------------- threshold
 
 // Finds the bin T with above(T) < need <= above(T) + h[T], where above(T)
-// counts the entries in bins > T.  Every thread of the block gets (T, above).
-// h is an LDS array of nbins (a multiple of blockDim.x, blockDim.x a multiple
-// of 64 and at most 1024); scratch holds 16 + 2 words.  Each thread owns a
-// run of nbins/blockDim.x bins; a suffix scan of the per-thread totals (wave
-// shuffles, then the wave totals) locates the one thread whose run crosses
+// counts the entries in bins > T, over a histogram the threads hold in
+// registers: thread i owns bins PER*i .. PER*i + PER-1, given in v (nbins =
+// PER * blockDim.x, blockDim.x a multiple of 64 and at most 1024).  Every
+// thread gets (T, above), h[T] and, in *total_out, the sum of all bins.
+// scratch holds 16 + 3 words.  A suffix scan of the per-thread totals (within the
+// wave, then over the wave totals) locates the one thread whose run crosses
 // `need`, and that thread walks its own bins.
-__device__ void find_threshold(const uint32_t* h, int nbins, uint32_t need, uint32_t* scratch,
-                               int* T_out, uint32_t* above_out) {
-  const int per = nbins / blockDim.x;
-  const int lo = threadIdx.x * per;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nwaves = blockDim.x >> 6;
-  uint32_t mine = 0;
-  for (int i = 0; i < per; ++i) mine += h[lo + i];
-  // inclusive suffix sum within the wave (this lane and those above it)
-  const uint32_t pre = wave_incl_scan(mine);
-  const uint32_t suf = wave_total(pre) - pre + mine;
-  if (lane == 0) scratch[wave] = suf;  // the wave's total
-  if (threadIdx.x == 0) {              // defaults if no bin qualifies (inconsistent counts)
-    scratch[16] = 0;
-    scratch[17] = 0;
-  }
-  __syncthreads();
-  uint32_t higher = 0;
-  for (int w = wave + 1; w < nwaves; ++w) higher += scratch[w];
-  uint32_t run = higher + suf - mine;  // entries in bins owned by higher threads
-  if (run < need && run + mine >= need) {
-    for (int i = per - 1; i >= 0; --i) {
-      const uint32_t v = h[lo + i];
-      if (run < need && run + v >= need) {
-        scratch[16] = uint32_t(lo + i);
-        scratch[17] = run;
-      }
-      run += v;
-    }
-  }
-  __syncthreads();
-  *T_out = int(scratch[16]);
-  *above_out = scratch[17];
-  __syncthreads();
-}
-
-// The same search over a histogram the threads hold in registers: thread i
-// owns bins PER*i .. PER*i + PER-1, given in v (nbins = PER * blockDim.x).
 template <int PER>
 __device__ void find_threshold_regs(const uint32_t (&v)[PER], uint32_t need, uint32_t* scratch, int* T_out,
-                                    uint32_t* above_out) {
+                                    uint32_t* above_out, uint32_t* total_out, uint32_t* count_out = nullptr) {
   const int lo = threadIdx.x * PER;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nwaves = blockDim.x >> 6;
   uint32_t mine = 0;
@@ -968,10 +950,16 @@ __device__ void find_threshold_regs(const uint32_t (&v)[PER], uint32_t need, uin
   if (threadIdx.x == 0) {
     scratch[16] = 0;
     scratch[17] = 0;
+    scratch[18] = 0;
   }
   __syncthreads();
-  uint32_t higher = 0;
-  for (int w = wave + 1; w < nwaves; ++w) higher += scratch[w];
+  uint32_t higher = 0, all = 0;
+  for (int w = 0; w < nwaves; ++w) {
+    const uint32_t x = scratch[w];
+    higher += w > wave ? x : 0u;
+    all += x;
+  }
+  *total_out = all;
   uint32_t run = higher + suf - mine;
   if (run < need && run + mine >= need) {
 #pragma unroll
@@ -979,45 +967,29 @@ __device__ void find_threshold_regs(const uint32_t (&v)[PER], uint32_t need, uin
       if (run < need && run + v[i] >= need) {
         scratch[16] = uint32_t(lo + i);
         scratch[17] = run;
+        scratch[18] = v[i];
       }
       run += v[i];
     }
   }
   __syncthreads();
   *T_out = int(scratch[16]);
+  if (count_out) *count_out = scratch[18];
   *above_out = scratch[17];
   __syncthreads();
 }
 
-// Ordered compaction helper: returns this thread's position among the threads
-// of the block with pred set (in thread order) and, through *total, their
-// count.  wtot holds blockDim.x/64 words.  Ends with the block synchronised.
-__device__ __forceinline__ uint32_t block_rank(bool pred, uint32_t* wtot, uint32_t* total) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nwaves = blockDim.x >> 6;
-  const uint64_t mask = __ballot(pred);
-  if (lane == 0) wtot[wave] = uint32_t(__popcll(mask));
-  __syncthreads();
-  uint32_t before = 0, all = 0;
-  for (int w = 0; w < nwaves; ++w) {
-    const uint32_t x = wtot[w];
-    before += w < wave ? x : 0u;
-    all += x;
-  }
-  __syncthreads();
-  *total = all;
-  return before + uint32_t(__popcll(mask & ((uint64_t(1) << lane) - 1)));
-}
-
-// Block-wide exclusive scan of one value per thread (blockDim.x = 256);
-// returns the block total.  wsum holds 4 words.  Ends synchronised.
-__device__ __forceinline__ uint32_t scan256(uint32_t v, uint32_t* wsum, uint32_t* total) {
+// Block-wide exclusive scan of one value per thread (NW waves); returns the
+// block total.  wsum holds NW words.  Ends synchronised.
+template <int NW>
+__device__ __forceinline__ uint32_t scan_block(uint32_t v, uint32_t* wsum, uint32_t* total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const uint32_t inc = wave_incl_scan(v);
   if (lane == 63) wsum[wave] = inc;
   __syncthreads();
   uint32_t before = 0, all = 0;
 #pragma unroll
-  for (int w = 0; w < 4; ++w) {
+  for (int w = 0; w < NW; ++w) {
     const uint32_t x = wsum[w];
     before += w < wave ? x : 0u;
     all += x;
@@ -1027,109 +999,41 @@ __device__ __forceinline__ uint32_t scan256(uint32_t v, uint32_t* wsum, uint32_t
   return before + inc - v;
 }
 
-// Every workgroup recomputes the threshold bin T of its query from the
-// first-digit histogram, then splits its own chunk of keys into "above T"
-// (selected for sure) and "in T" (candidates, stored with their keys).  Thread
-// j takes entries 4j .. 4j+3 of each 1024-entry batch, so one scan of packed
-// counts orders both lists by index.  Both lists go to the chunk's own
-// segment and the two counts to the chunk's own slot: no global atomics for
-// the lists, and the result does not depend on scheduling.  The candidates'
-// second digit (key bits 20..10) is counted into the query's second
-// histogram, which is the first radix pass of the finish.
-__global__ void __launch_bounds__(256) filter_kernel(IdxArgs a) {
-  static_assert(kBins == 8 * 256, "filter_kernel: eight first-digit bins per thread");
-  __shared__ uint32_t h2[kBins];
-  __shared__ uint32_t scratch[18];
-  __shared__ uint32_t wsum[4];
-  const int64_t bq = blockIdx.y;
-  const int64_t nvis = visible(a, bq);
-  const int64_t keff = min(a.k, nvis);
-  const int64_t s0 = int64_t(blockIdx.x) * a.keys_per_wg;
-  if (keff == nvis || s0 >= nvis) return;  // keep-all and empty chunks need no filtering
-  const int64_t s1 = min(nvis, s0 + a.keys_per_wg);
-  const float* sc = a.scores + bq * a.score_ld;
-  // the first batches of scores are in flight while the threshold is found
-  auto load4 = [&](int64_t base, float* v) {
-    const int64_t s = base + 4 * threadIdx.x;
-    if (s + 3 < s1 && (reinterpret_cast<uintptr_t>(sc + s) & 15) == 0) {
-      const float4 x = *reinterpret_cast<const float4*>(sc + s);
-      v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w;
-    } else {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) v[e] = s + e < s1 ? sc[s + e] : 0.f;
-    }
-  };
-  // a ring of FD batches in registers: batch i+FD is loaded as batch i is
-  // used (one batch at a time, the loop was load-latency bound)
-  constexpr int FD = 4;
-  float vb[FD][4];
-#pragma unroll
-  for (int d = 0; d < FD; ++d) load4(s0 + int64_t(d) * 4 * blockDim.x, vb[d]);
-  // thread j holds first-digit bins 8j .. 8j+7 (two 16-byte loads)
-  uint32_t hv[8];
-  {
-    const uint4* hp = reinterpret_cast<const uint4*>(a.hist + bq * kBins) + 2 * threadIdx.x;
-    const uint4 x = hp[0], y = hp[1];
-    hv[0] = x.x; hv[1] = x.y; hv[2] = x.z; hv[3] = x.w;
-    hv[4] = y.x; hv[5] = y.y; hv[6] = y.z; hv[7] = y.w;
-  }
-  for (int i = threadIdx.x; i < kBins; i += blockDim.x) h2[i] = 0;
-  int T;
-  uint32_t above;
-  find_threshold_regs<8>(hv, uint32_t(keff), scratch, &T, &above);  // also orders the h2 clear
-
-  int32_t* sel = a.sel + bq * a.cap + s0;
-  int32_t* cand = a.cand + bq * a.cap + s0;
-  uint32_t* ckey = a.cand_kseg + bq * a.cap + s0;
-  uint32_t nsel = 0, ncand = 0;
-  const int64_t step = 4 * int64_t(blockDim.x);
-  for (int64_t round = s0; round < s1; round += FD * step) {
-#pragma unroll
-    for (int dd = 0; dd < FD; ++dd) {
-      const int64_t base = round + dd * step;
-      if (base >= s1) break;  // uniform
-      float v[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) v[e] = vb[dd][e];
-      load4(base + FD * step, vb[dd]);  // past s1: zeros, no access
-      const int64_t sb = base + 4 * threadIdx.x;
-      uint32_t key[4], packed = 0;
-      int d[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        key[e] = order_key(v[e]);
-        d[e] = sb + e < s1 ? int(key[e] >> kShift1) : -1;
-        packed += d[e] > T ? 1u : 0u;
-        packed += d[e] == T ? 0x10000u : 0u;
-      }
-      uint32_t tot;
-      const uint32_t ex = scan256(packed, wsum, &tot);
-      uint32_t ps = nsel + (ex & 0xffffu), pc = ncand + (ex >> 16);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        if (d[e] > T) sel[ps++] = int32_t(sb + e);
-        if (d[e] == T) {
-          cand[pc] = int32_t(sb + e);
-          ckey[pc] = key[e];
-          ++pc;
-          atomicAdd(&h2[(key[e] >> 10) & 0x7ffu], 1u);
-        }
-      }
-      nsel += tot & 0xffffu;
-      ncand += tot >> 16;
-    }
-  }
-  flush_hist(h2, a.hist2 + bq * kBins);
-  if (threadIdx.x == 0) {
-    a.ccnt[(bq * a.max_chunks + blockIdx.x) * 2 + 0] = nsel;
-    a.ccnt[(bq * a.max_chunks + blockIdx.x) * 2 + 1] = ncand;
-  }
-}
-
-// ---------------------------------------------------------------- finish
-
-constexpr int kMaxChunks = 4096;
-constexpr int kLdsCand = 4096;
+// ---------------------------------------------------------------- selection
+//
+// One kernel after the scores: a workgroup per chunk of keys_per_wg entries
+// filters its chunk, and the last workgroup of a query to finish resolves
+// the query's threshold exactly and writes idx / count.
+//
+// Filter (every workgroup).  The threshold bin T of the query comes from the
+// first-digit histogram: above(T) < k_eff <= above(T) + h[T].  The chunk's
+// entries above T (selected for sure) and in T (candidates, stored with
+// their keys and with the number of the chunk's selected entries before
+// them) go to the chunk's own segments in index order: thread j takes
+// entries 4j .. 4j+3 of each batch of 4*kSelThreads, so one scan of packed
+// counts orders both lists.  The candidates' second digit (key bits 20..10) is
+// counted into the query's second histogram.
+//
+// Finish (the last workgroup of the query; an arrival counter per query,
+// cleared by the scores kernel of the same call).  After the exclusive scans
+// of the chunk counts, radix passes over the candidates' composite key (the
+// low 21 key bits, then the bit-inverted index) find the exact k_eff-th
+// entry, starting from the second histogram.  The chosen candidates are
+// those at or above it, and their output slots follow from the counts:
+// chosen candidate j (in index order) goes to j + (selected entries before
+// its chunk) + (selected entries of its chunk before it); selected entry i
+// goes to i + (chosen candidates below it), a binary search over the chosen
+// list.  The finishing workgroup then clears the query's first-digit
+// histogram, so that the next call's scores kernel finds it zero.  A
+// histogram that did not start at zero (a workspace that no call of the
+// library has cleared) shows as a bin above the visible count or a total
+// other than it; the filter then counts the query's scores again itself.
+constexpr int kMaxChunks = 1024;  // chunks per query (keys_per_wg keeps to it)
+constexpr int kFinCand = 4096;    // candidates the finishing workgroup holds in LDS (more: the workspace)
+constexpr int kFinChosen = 2048;  // chosen candidates it holds in LDS (more: the workspace)
+constexpr int kSelThreads = 512;
+constexpr int kSelWaves = kSelThreads / 64;
+constexpr int kBpt = kBins / kSelThreads;  // first-digit bins per thread
 
 // radix passes over the candidates' composite key: the low 21 bits of the score
 // key (the top 11 bits are T for all of them), then the bit-inverted index
@@ -1141,15 +1045,14 @@ __device__ __forceinline__ uint64_t cand_key(uint32_t key, int32_t s) {
   return (uint64_t(key & 0x1fffffu) << 32) | uint64_t(0xffffffffu - uint32_t(s));
 }
 
-// Block-wide exclusive scans of two arrays v[0 .. n) and w[0 .. n) in place;
-// the totals come back through tv and tw.  Thread j owns the runs at
-// [j*per, (j+1)*per), per = ceil(n / blockDim.x); wsum holds 2*blockDim.x/64
-// words.  Ends synchronised.
-__device__ void block_exclusive_scan2(uint32_t* v, uint32_t* w, int n, uint32_t* wsum, uint32_t* tv,
-                                      uint32_t* tw) {
-  const int per = (n + int(blockDim.x) - 1) / int(blockDim.x);
+// Exclusive scans of v[0 .. n) and w[0 .. n) in place (kSelThreads threads);
+// the totals come back through tv and tw.  Thread j owns the run [j*per,
+// (j+1)*per), per = ceil(n / kSelThreads); wsum holds 2*kSelWaves words.
+// Ends synchronised.
+__device__ void scan_runs2(uint32_t* v, uint32_t* w, int n, uint32_t* wsum, uint32_t* tv, uint32_t* tw) {
+  const int per = (n + kSelThreads - 1) / kSelThreads;
   const int lo = threadIdx.x * per, hi = min(n, lo + per);
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nwaves = blockDim.x >> 6;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   uint32_t mv = 0, mw = 0;
   for (int i = lo; i < hi; ++i) {
     mv += v[i];
@@ -1158,16 +1061,15 @@ __device__ void block_exclusive_scan2(uint32_t* v, uint32_t* w, int n, uint32_t*
   const uint32_t iv = wave_incl_scan(mv), iw = wave_incl_scan(mw);
   if (lane == 63) {
     wsum[wave] = iv;
-    wsum[nwaves + wave] = iw;
+    wsum[kSelWaves + wave] = iw;
   }
   __syncthreads();
   uint32_t bv = 0, bw = 0, sv = 0, sw = 0;
-  for (int k = 0; k < nwaves; ++k) {
-    const uint32_t x = wsum[k], y = wsum[nwaves + k];
-    if (k < wave) {
-      bv += x;
-      bw += y;
-    }
+#pragma unroll
+  for (int k = 0; k < kSelWaves; ++k) {
+    const uint32_t x = wsum[k], y = wsum[kSelWaves + k];
+    bv += k < wave ? x : 0u;
+    bw += k < wave ? y : 0u;
     sv += x;
     sw += y;
   }
@@ -1184,166 +1086,384 @@ __device__ void block_exclusive_scan2(uint32_t* v, uint32_t* w, int n, uint32_t*
   *tw = sw;
 }
 
-// number of entries of the ascending list l[0 .. n) that are < x
-__device__ __forceinline__ uint32_t lower_bound(const int32_t* l, uint32_t n, int32_t x) {
-  uint32_t lo = 0, hi = n;
-  while (lo < hi) {
-    const uint32_t mid = (lo + hi) >> 1;
-    if (l[mid] < x) lo = mid + 1; else hi = mid;
+// Binary searches of G keys at once: the same number of halving steps for
+// every key and lane (n is uniform), so the G reads of a step are in flight
+// together.
+// r[u] = the number of entries of the ascending list l[0 .. n) below x[u]
+template <int G>
+__device__ __forceinline__ void lower_bounds(const int32_t* l, uint32_t n, const int32_t (&x)[G], uint32_t (&r)[G]) {
+  uint32_t base[G];
+#pragma unroll
+  for (int u = 0; u < G; ++u) base[u] = 0;
+  uint32_t len = n;
+  while (len > 1) {
+    const uint32_t half = len >> 1;
+#pragma unroll
+    for (int u = 0; u < G; ++u) base[u] = l[base[u] + half] < x[u] ? base[u] + half : base[u];
+    len -= half;
   }
-  return lo;
+#pragma unroll
+  for (int u = 0; u < G; ++u) r[u] = base[u] + ((n > 0 && l[base[u]] < x[u]) ? 1u : 0u);
+}
+// c[u] = the largest chunk c < n with off[c] <= i[u] (off ascending, off[0] = 0)
+template <int G>
+__device__ __forceinline__ void chunks_of(const uint32_t* off, int n, const uint32_t (&i)[G], int (&c)[G]) {
+#pragma unroll
+  for (int u = 0; u < G; ++u) c[u] = 0;
+  int len = n;
+  while (len > 1) {
+    const int half = len >> 1;
+#pragma unroll
+    for (int u = 0; u < G; ++u) c[u] = off[c[u] + half] <= i[u] ? c[u] + half : c[u];
+    len -= half;
+  }
 }
 
-// One workgroup per query.  The "above T" lists of all chunks, in chunk order,
-// form one ascending list; radix passes over the candidates find the exact
-// k_eff-th composite key; the candidates at or above it are compacted in
-// order into a second ascending list; the two lists are merged by rank.
-__global__ void __launch_bounds__(1024) finish_kernel(IdxArgs a) {
-  __shared__ uint32_t h[kBins];
-  __shared__ uint32_t scratch[18];
-  __shared__ uint32_t wsum[32];
-  __shared__ uint32_t off_sel[kMaxChunks], off_cand[kMaxChunks];
-  __shared__ int32_t lsel[kMaxK], lc2[kMaxK];
-  __shared__ int32_t lc_idx[kLdsCand];
-  __shared__ uint32_t lc_key[kLdsCand];
-  const int64_t bq = blockIdx.x;
-  const int64_t nvis = visible(a, bq);
-  const int64_t keff = min(a.k, nvis);
+// thresholds over an LDS histogram of PER*kSelThreads bins; *count gets h[T] (read
+// before the search's last barrier, so h may be overwritten after it)
+template <int PER>
+__device__ __forceinline__ void find_in_lds(const uint32_t* h, uint32_t need, uint32_t* scratch, int* T,
+                                            uint32_t* above, uint32_t* count) {
+  uint32_t v[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) v[i] = h[PER * threadIdx.x + i];
+  uint32_t total;
+  find_threshold_regs<PER>(v, need, scratch, T, above, &total, count);
+}
+
+// Values that cross workgroups inside the selection kernel (the chunk lists,
+// counts and the second histogram) are written and read with agent-scope
+// atomic accesses, which this chip performs at the point of coherence of
+// all its L2 caches (global_store / global_load with sc1): once a wave's
+// stores have completed (vmcnt 0), another workgroup's atomic loads see
+// them, with no L2 write-back or invalidation, whichever XCD it runs on.
+template <typename T>
+__device__ __forceinline__ void st_agent(T* p, T v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+template <typename T>
+__device__ __forceinline__ T ld_agent(const T* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+struct FinishLds {
+  uint32_t off_sel[kMaxChunks], off_cand[kMaxChunks];
+  int32_t c_idx[kFinCand];
+  uint32_t c_key[kFinCand], c_srk[kFinCand];
+  int32_t chosen[kFinChosen];
+};
+
+__device__ void finish_query(const IdxArgs& a, int64_t bq, int64_t nvis, int64_t keff, uint32_t* h, FinishLds& L,
+                             uint32_t* scratch, uint32_t* wsum) {
+  const int tid = threadIdx.x;
+  const int64_t kpw = a.keys_per_wg;
+  const int nch = int(ceil_div(nvis, kpw));
   int32_t* out = a.idx + bq * a.k;
-  if (threadIdx.x == 0) a.count[bq] = int32_t(keff);
-  if (keff == nvis) {
-    for (int64_t j = threadIdx.x; j < a.k; j += blockDim.x) out[j] = j < nvis ? int32_t(j) : -1;
-    return;
-  }
-  const int nch = int(ceil_div(nvis, a.keys_per_wg));
-  const uint2* cc = reinterpret_cast<const uint2*>(a.ccnt + bq * a.max_chunks * 2);
-  // the chunk counts and the candidates' first composite digit (counted by
-  // the filter; pass 0 below) load together
-  static_assert(kBins % 2 == 0, "bins in pairs");
-  const uint2* h2g = reinterpret_cast<const uint2*>(a.hist2 + bq * kBins);
-  for (int i = threadIdx.x; i < kBins / 2 || i < nch; i += blockDim.x) {
-    uint2 x = make_uint2(0, 0), y = make_uint2(0, 0);
-    if (i < nch) x = cc[i];
-    if (i < kBins / 2) y = h2g[i];
-    if (i < nch) {
-      off_sel[i] = x.x;
-      off_cand[i] = x.y;
+  // the chunk counts and the candidates' second digit (pass 0 below)
+  const uint32_t* cc = a.ccnt + bq * a.max_chunks * 2;
+  const uint32_t* h2g = a.hist2 + bq * kBins;
+  {
+    uint32_t y[kBpt];
+#pragma unroll
+    for (int u = 0; u < kBpt; ++u) y[u] = ld_agent(h2g + tid + u * kSelThreads);
+    for (int i = tid; i < nch; i += kSelThreads) {
+      L.off_sel[i] = ld_agent(cc + 2 * i);
+      L.off_cand[i] = ld_agent(cc + 2 * i + 1);
     }
-    if (i < kBins / 2) {
-      h[2 * i] = y.x;
-      h[2 * i + 1] = y.y;
-    }
+#pragma unroll
+    for (int u = 0; u < kBpt; ++u) h[tid + u * kSelThreads] = y[u];
   }
   __syncthreads();
   uint32_t tsel, tcand;
-  block_exclusive_scan2(off_sel, off_cand, nch, wsum, &tsel, &tcand);
+  scan_runs2(L.off_sel, L.off_cand, nch, wsum, &tsel, &tcand);
   const uint32_t n_sel = min(tsel, uint32_t(keff));
   const uint32_t n_cand = min(tcand, uint32_t(nvis));
-  const bool in_lds = n_cand <= uint32_t(kLdsCand);
-  int32_t* cidx = in_lds ? lc_idx : a.cand_idx + bq * a.cap;
-  uint32_t* ckey = in_lds ? lc_key : a.cand_key + bq * a.cap;
-  // gather the chunks' lists: every thread takes independent entries and finds
-  // its chunk by binary search over the exclusive offsets
-  auto chunk_of = [&](const uint32_t* off, uint32_t i) {
-    int lo = 0, hi = nch - 1;  // largest c with off[c] <= i
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (off[mid] <= i) lo = mid; else hi = mid - 1;
-    }
-    return lo;
-  };
-  // both lists in one sweep, four entries of each per thread per round, all
-  // their loads in flight together
+  const uint32_t need0 = uint32_t(keff) - n_sel;
+  const bool cand_lds = n_cand <= uint32_t(kFinCand);
+  int32_t* ci = cand_lds ? L.c_idx : a.cand_idx + bq * a.cap;
+  uint32_t* ck = cand_lds ? L.c_key : a.cand_key + bq * a.cap;
+  uint32_t* cs = cand_lds ? L.c_srk : a.cand_srk2 + bq * a.cap;
+  int32_t* chosen = need0 <= uint32_t(kFinChosen) ? L.chosen : a.chosen + bq * a.k;
+  const int32_t* selg = a.sel + bq * a.cap;
+  const int64_t cbase = bq * a.cap;
+
+  // the first 1024 selected entries, loaded with the candidates
   constexpr int G = 4;
-  const uint32_t n_both = n_sel > n_cand ? n_sel : n_cand;
-  for (uint32_t i0 = threadIdx.x; i0 < n_both; i0 += G * blockDim.x) {
-    int32_t vs[G], vi[G];
-    uint32_t vk[G];
+  int32_t sv[G];
+  {
+    uint32_t si[G];
+    int sc[G];
 #pragma unroll
-    for (int u = 0; u < G; ++u) {
-      const uint32_t i = i0 + u * blockDim.x;
-      if (i < n_sel) {
-        const int c = chunk_of(off_sel, i);
-        vs[u] = a.sel[bq * a.cap + int64_t(c) * a.keys_per_wg + (i - off_sel[c])];
-      }
-      if (i < n_cand) {
-        const int c = chunk_of(off_cand, i);
-        const int64_t at = bq * a.cap + int64_t(c) * a.keys_per_wg + (i - off_cand[c]);
-        vi[u] = a.cand[at];
-        vk[u] = a.cand_kseg[at];
+    for (int u = 0; u < G; ++u) si[u] = tid + u * kSelThreads;
+    chunks_of<G>(L.off_sel, nch, si, sc);
+#pragma unroll
+    for (int u = 0; u < G; ++u)
+      sv[u] = si[u] < n_sel ? ld_agent(selg + int64_t(sc[u]) * kpw + (si[u] - L.off_sel[sc[u]])) : 0;
+  }
+  // eight candidates a thread per round, their loads in flight together
+  constexpr int GC = 8;
+  for (uint32_t i0 = tid; i0 < n_cand; i0 += GC * kSelThreads) {
+    int32_t vi[GC];
+    uint32_t vk[GC], vs[GC], ii[GC];
+    int cc[GC];
+#pragma unroll
+    for (int u = 0; u < GC; ++u) ii[u] = i0 + u * kSelThreads;
+    chunks_of<GC>(L.off_cand, nch, ii, cc);
+#pragma unroll
+    for (int u = 0; u < GC; ++u) {
+      if (ii[u] < n_cand) {
+        const int64_t at = cbase + int64_t(cc[u]) * kpw + (ii[u] - L.off_cand[cc[u]]);
+        vi[u] = ld_agent(a.cand + at);
+        vk[u] = ld_agent(a.cand_kseg + at);
+        vs[u] = ld_agent(a.cand_srk + at);
       }
     }
 #pragma unroll
-    for (int u = 0; u < G; ++u) {
-      const uint32_t i = i0 + u * blockDim.x;
-      if (i < n_sel) lsel[i] = vs[u];
+    for (int u = 0; u < GC; ++u) {
+      const uint32_t i = i0 + u * kSelThreads;
       if (i < n_cand) {
-        cidx[i] = vi[u];
-        ckey[i] = vk[u];
+        ci[i] = vi[u];
+        ck[i] = vk[u];
+        cs[i] = vs[u];
       }
     }
   }
   __threadfence_block();
   __syncthreads();
 
-  // the exact threshold: after the passes, the selected candidates are those
-  // whose composite key is >= thr
-  uint32_t need = uint32_t(keff) - n_sel;
+  // the exact threshold: the chosen candidates are those whose composite key
+  // is >= thr
+  uint32_t need = need0;
   uint64_t pval = 0, pmask = 0;
-  for (int pass = 0; pass < kPasses; ++pass) {
+  for (int pass = 0; pass < kPasses && need > 0; ++pass) {
     const int shift = pass_shift(pass), bits = pass_bits(pass);
     const uint32_t dmask = (1u << bits) - 1u;
-    const int nb = 1 << bits;
-    if (pass == 0) {
-      // the filter already counted the candidates' first composite digit (h,
-      // loaded with the chunk counts)
-    } else {
-      for (int i = threadIdx.x; i < kBins; i += blockDim.x) h[i] = 0;
+    if (pass > 0) {
+      for (int i = tid; i < kBins; i += kSelThreads) h[i] = 0;
       __syncthreads();
-      for (uint32_t i = threadIdx.x; i < n_cand; i += blockDim.x) {
-        const uint64_t ck = cand_key(ckey[i], cidx[i]);
-        if ((ck & pmask) == pval) atomicAdd(&h[(ck >> shift) & dmask], 1u);
+      for (uint32_t i = tid; i < n_cand; i += kSelThreads) {
+        const uint64_t key = cand_key(ck[i], ci[i]);
+        if ((key & pmask) == pval) atomicAdd(&h[(key >> shift) & dmask], 1u);
       }
       __syncthreads();
     }
     int D;
-    uint32_t above;
-    find_threshold(h, nb < 1024 ? 1024 : nb, need, scratch, &D, &above);
-    const bool take_all = (above + h[D] == need);
+    uint32_t above, hD;
+    if (bits == 11) find_in_lds<kBpt>(h, need, scratch, &D, &above, &hD);
+    else find_in_lds<kBpt / 2>(h, need, scratch, &D, &above, &hD);
+    const bool take_all = above + hD == need;
     pval |= uint64_t(D) << shift;
     pmask |= uint64_t(dmask) << shift;
     if (take_all) break;
     need -= above;
   }
   const uint64_t thr = pval;
+  // need0 == 0: no candidate is chosen (thr stays above every key)
+  const bool none = need0 == 0;
 
-  // ordered compaction of the selected candidates
-  uint32_t n2 = 0;
-  for (uint32_t base = 0; base < n_cand; base += blockDim.x) {
-    const uint32_t i = base + threadIdx.x;
-    const bool take = i < n_cand && cand_key(ckey[i], cidx[i]) >= thr;
+  // chosen candidates in index order: thread j counts its run, one scan
+  // gives the ranks; each goes straight to its output slot
+  {
+    const uint32_t per = (n_cand + kSelThreads - 1) / kSelThreads;
+    const uint32_t lo = tid * per, hi = min(n_cand, lo + per);
+    uint32_t mine = 0;
+    if (!none)
+      for (uint32_t i = lo; i < hi; ++i) mine += cand_key(ck[i], ci[i]) >= thr ? 1u : 0u;
     uint32_t tot;
-    const uint32_t r = block_rank(take, wsum, &tot);
-    if (take && n2 + r < uint32_t(kMaxK)) lc2[n2 + r] = cidx[i];
-    n2 += tot;
+    uint32_t j = scan_block<kSelWaves>(mine, wsum, &tot);
+    if (!none) {
+      for (uint32_t i = lo; i < hi; ++i) {
+        if (cand_key(ck[i], ci[i]) < thr) continue;
+        if (j < need0) {
+          const int32_t y = ci[i];
+          const int c = int(uint32_t(y) / uint32_t(kpw));
+          chosen[j] = y;
+          out[j + L.off_sel[c] + cs[i]] = y;
+        }
+        ++j;
+      }
+    }
   }
-  n2 = min(n2, uint32_t(keff) - n_sel);
-  // merge two ascending lists by rank
-  for (uint32_t i = threadIdx.x; i < n_sel; i += blockDim.x) {
-    const int32_t x = lsel[i];
-    out[i + lower_bound(lc2, n2, x)] = x;
+  __threadfence_block();
+  __syncthreads();
+  const uint32_t n2 = need0;
+  // selected entries: slot i + (chosen entries below)
+  {
+    uint32_t r[G];
+    lower_bounds<G>(chosen, n2, sv, r);
+#pragma unroll
+    for (int u = 0; u < G; ++u) {
+      const uint32_t i = tid + u * kSelThreads;
+      if (i < n_sel) out[i + r[u]] = sv[u];
+    }
   }
-  for (uint32_t j = threadIdx.x; j < n2; j += blockDim.x) {
-    const int32_t y = lc2[j];
-    out[j + lower_bound(lsel, n_sel, y)] = y;
+  for (uint32_t i0 = tid + G * kSelThreads; i0 < n_sel; i0 += G * kSelThreads) {
+    uint32_t si[G], r[G];
+    int sc[G];
+    int32_t x[G];
+#pragma unroll
+    for (int u = 0; u < G; ++u) si[u] = i0 + u * kSelThreads;
+    chunks_of<G>(L.off_sel, nch, si, sc);
+#pragma unroll
+    for (int u = 0; u < G; ++u)
+      x[u] = si[u] < n_sel ? ld_agent(selg + int64_t(sc[u]) * kpw + (si[u] - L.off_sel[sc[u]])) : 0;
+    lower_bounds<G>(chosen, n2, x, r);
+#pragma unroll
+    for (int u = 0; u < G; ++u)
+      if (si[u] < n_sel) out[si[u] + r[u]] = x[u];
   }
-  for (int64_t j = n_sel + n2 + threadIdx.x; j < a.k; j += blockDim.x) out[j] = -1;
+  for (int64_t j = keff + tid; j < a.k; j += kSelThreads) out[j] = -1;
+  if (tid == 0) a.count[bq] = int32_t(keff);
+  // the first-digit histogram back to zero for the next call
+  uint4* hg = reinterpret_cast<uint4*>(a.hist + bq * kBins);
+  for (int i = tid; i < kBins / 4; i += kSelThreads) hg[i] = make_uint4(0, 0, 0, 0);
+}
+
+__global__ void __launch_bounds__(kSelThreads) select_kernel(IdxArgs a) {
+  static_assert(kBins == kBpt * kSelThreads && kBpt % 4 == 0, "select_kernel: whole 16-byte runs of bins per thread");
+  __shared__ uint32_t h2[kBins];
+  __shared__ uint32_t scratch[19];
+  __shared__ uint32_t wsum[2 * kSelWaves];
+  __shared__ uint32_t s_last;
+  __shared__ FinishLds L;
+  const int tid = threadIdx.x;
+  const int64_t bq = blockIdx.y;
+  const int64_t nvis = visible(a, bq);
+  const int64_t keff = min(a.k, nvis);
+  const int64_t s0 = int64_t(blockIdx.x) * a.keys_per_wg;
+  if (keff == nvis) {  // keep all (or nothing visible): the first workgroup writes the result
+    if (blockIdx.x == 0) {
+      int32_t* out = a.idx + bq * a.k;
+      for (int64_t j = tid; j < a.k; j += kSelThreads) out[j] = j < nvis ? int32_t(j) : -1;
+      if (tid == 0) a.count[bq] = int32_t(keff);
+      uint4* hg = reinterpret_cast<uint4*>(a.hist + bq * kBins);
+      for (int i = tid; i < kBins / 4; i += kSelThreads) hg[i] = make_uint4(0, 0, 0, 0);
+    }
+    return;
+  }
+  if (s0 >= nvis) return;
+  const int64_t s1 = min(nvis, s0 + a.keys_per_wg);
+  const float* sc = a.scores + bq * a.score_ld;
+  // the first batches of scores are in flight while the threshold is found
+  auto load4 = [&](int64_t base, float* v) {
+    const int64_t s = base + 4 * tid;
+    if (s + 3 < s1 && (reinterpret_cast<uintptr_t>(sc + s) & 15) == 0) {
+      const float4 x = *reinterpret_cast<const float4*>(sc + s);
+      v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = s + e < s1 ? sc[s + e] : 0.f;
+    }
+  };
+  // a ring of FD batches in registers: batch i+FD is loaded as batch i is used
+  constexpr int FD = 2;
+  float vb[FD][4];
+#pragma unroll
+  for (int d = 0; d < FD; ++d) load4(s0 + int64_t(d) * 4 * kSelThreads, vb[d]);
+  // thread j holds first-digit bins kBpt*j .. kBpt*j + kBpt-1 (16-byte loads)
+  uint32_t hv[kBpt];
+  {
+    const uint4* hp = reinterpret_cast<const uint4*>(a.hist + bq * kBins) + (kBpt / 4) * tid;
+#pragma unroll
+    for (int q = 0; q < kBpt / 4; ++q) {
+      const uint4 x = hp[q];
+      hv[4 * q] = x.x; hv[4 * q + 1] = x.y; hv[4 * q + 2] = x.z; hv[4 * q + 3] = x.w;
+    }
+  }
+  for (int i = tid; i < kBins; i += kSelThreads) h2[i] = 0;
+  int T;
+  uint32_t above, total;
+  bool over = false;
+#pragma unroll
+  for (int e = 0; e < kBpt; ++e) over = over || hv[e] > uint32_t(nvis);
+  over = __syncthreads_or(over);
+  find_threshold_regs<kBpt>(hv, uint32_t(keff), scratch, &T, &above, &total);  // also orders the h2 clear
+  if (over || total != uint32_t(nvis)) {
+    // the histogram did not start at zero (no bin of a clean one exceeds the
+    // visible count, and the bins sum to it): count the query's scores again
+    for (int64_t s = tid; s < nvis; s += kSelThreads) atomicAdd(&h2[order_key(sc[s]) >> kShift1], 1u);
+    __syncthreads();
+#pragma unroll
+    for (int e = 0; e < kBpt; ++e) hv[e] = h2[kBpt * tid + e];
+    __syncthreads();
+    for (int i = tid; i < kBins; i += kSelThreads) h2[i] = 0;
+    find_threshold_regs<kBpt>(hv, uint32_t(keff), scratch, &T, &above, &total);
+  }
+
+  int32_t* sel = a.sel + bq * a.cap + s0;
+  int32_t* cand = a.cand + bq * a.cap + s0;
+  uint32_t* ckey = a.cand_kseg + bq * a.cap + s0;
+  uint32_t* csrk = a.cand_srk + bq * a.cap + s0;
+  uint32_t nsel = 0, ncand = 0;
+  const int64_t step = 4 * int64_t(kSelThreads);
+  for (int64_t round = s0; round < s1; round += FD * step) {
+#pragma unroll
+    for (int dd = 0; dd < FD; ++dd) {
+      const int64_t base = round + dd * step;
+      if (base >= s1) break;  // uniform
+      float v[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = vb[dd][e];
+      load4(base + FD * step, vb[dd]);  // past s1: zeros, no access
+      const int64_t sb = base + 4 * tid;
+      uint32_t key[4], packed = 0;
+      int d[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        key[e] = order_key(v[e]);
+        d[e] = sb + e < s1 ? int(key[e] >> kShift1) : -1;
+        packed += d[e] > T ? 1u : 0u;
+        packed += d[e] == T ? 0x10000u : 0u;
+      }
+      uint32_t tot;
+      const uint32_t ex = scan_block<kSelWaves>(packed, wsum, &tot);
+      uint32_t ps = nsel + (ex & 0xffffu), pc = ncand + (ex >> 16);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if (d[e] > T) st_agent(sel + ps++, int32_t(sb + e));
+        if (d[e] == T) {
+          st_agent(cand + pc, int32_t(sb + e));
+          st_agent(ckey + pc, key[e]);
+          st_agent(csrk + pc, ps);  // the chunk's selected entries before this one
+          ++pc;
+          atomicAdd(&h2[(key[e] >> 10) & 0x7ffu], 1u);
+        }
+      }
+      nsel += tot & 0xffffu;
+      ncand += tot >> 16;
+    }
+  }
+  flush_hist(h2, a.hist2 + bq * kBins);
+  if (tid == 0) {
+    st_agent(a.ccnt + (bq * a.max_chunks + blockIdx.x) * 2 + 0, nsel);
+    st_agent(a.ccnt + (bq * a.max_chunks + blockIdx.x) * 2 + 1, ncand);
+  }
+  // arrive once every wave's lists, counts and histogram adds have completed
+  // (agent-scope stores and atomics: complete means visible to every
+  // workgroup); the last workgroup of the query finishes it
+  wait_vm<0>();
+  __syncthreads();
+  if (tid == 0) {
+    const uint32_t nch = uint32_t(ceil_div(nvis, a.keys_per_wg));
+    s_last = __hip_atomic_fetch_add(&a.ticket[bq * kTicketStride], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == nch - 1 ? 1u
+                                                                                                         : 0u;
+  }
+  __syncthreads();
+  if (s_last == 0) return;
+  finish_query(a, bq, nvis, keff, h2, L, scratch, wsum);
+}
+
+// no entry is visible to any query (floor(t_max/m) = 0)
+__global__ void __launch_bounds__(256) select_none_kernel(int32_t* idx, int32_t* count, int64_t BQ, int64_t k) {
+  const int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  if (i < BQ * k) idx[i] = -1;
+  if (i < BQ) count[i] = 0;
 }
 
 // ---------------------------------------------------------------- host
 
 struct WsLayout {
-  size_t scores, hist, ccnt, sel, cand, cand_kseg, cand_idx, cand_key, total;
+  size_t scores, hist, ccnt, sel, cand, cand_kseg, cand_srk, cand_idx, cand_key, cand_srk2, chosen, total;
 };
 
 // keys per scores/filter workgroup: a multiple of 64 chosen so that the whole
@@ -1376,22 +1496,24 @@ int64_t keys_per_wg(int64_t BQ, int64_t vis_max, int64_t wgs = kScoreWorkgroups)
   const int64_t vis = vis_max > 0 ? vis_max : 1;
   int64_t kpw = ceil_div(ceil_div(vis * BQ, wgs), 64) * 64;
   kpw = kpw < 64 ? 64 : kpw;
-  const int64_t floor_kpw = ceil_div(ceil_div(vis, kMaxChunks), 64) * 64;
+  const int64_t floor_kpw = ceil_div(ceil_div(vis, kMaxChunks), 64) * 64;  // at most kMaxChunks chunks
   return kpw > floor_kpw ? kpw : floor_kpw;
 }
 
 WsLayout ws_layout(int64_t B, int64_t n_q, int64_t cap, int64_t k, bool own_scores) {
   const size_t BQ = size_t(B) * size_t(n_q);
-  (void)k;
   WsLayout L{};
   size_t off = 0;
-  L.hist = off;      off = align_up(off + BQ * kBins * 2 * 4, 256);  // hist, then hist2
+  L.hist = off;      off = align_up(off + BQ * (kBins * 2 + kTicketStride) * 4, 256);  // hist, hist2, tickets
   L.ccnt = off;      off = align_up(off + BQ * kMaxChunks * 2 * 4, 256);
   L.sel = off;       off = align_up(off + BQ * size_t(cap) * 4, 256);
   L.cand = off;      off = align_up(off + BQ * size_t(cap) * 4, 256);
   L.cand_kseg = off; off = align_up(off + BQ * size_t(cap) * 4, 256);
+  L.cand_srk = off;  off = align_up(off + BQ * size_t(cap) * 4, 256);
   L.cand_idx = off;  off = align_up(off + BQ * size_t(cap) * 4, 256);
   L.cand_key = off;  off = align_up(off + BQ * size_t(cap) * 4, 256);
+  L.cand_srk2 = off; off = align_up(off + BQ * size_t(cap) * 4, 256);
+  L.chosen = off;    off = align_up(off + BQ * size_t(k) * 4, 256);
   L.scores = off;
   if (own_scores) off = align_up(off + BQ * size_t(cap) * 4, 256);
   L.total = off;
@@ -1405,28 +1527,30 @@ void bind_ws(IdxArgs& a, const WsLayout& L, void* ws, float* scores, int64_t BQ,
   a.score_ld = cap;
   a.hist = reinterpret_cast<uint32_t*>(w + L.hist);
   a.hist2 = a.hist + size_t(BQ) * kBins;
+  a.ticket = a.hist2 + size_t(BQ) * kBins;
   a.ccnt = reinterpret_cast<uint32_t*>(w + L.ccnt);
   a.sel = reinterpret_cast<int32_t*>(w + L.sel);
   a.cand = reinterpret_cast<int32_t*>(w + L.cand);
   a.cand_kseg = reinterpret_cast<uint32_t*>(w + L.cand_kseg);
+  a.cand_srk = reinterpret_cast<uint32_t*>(w + L.cand_srk);
   a.cand_idx = reinterpret_cast<int32_t*>(w + L.cand_idx);
   a.cand_key = reinterpret_cast<uint32_t*>(w + L.cand_key);
+  a.cand_srk2 = reinterpret_cast<uint32_t*>(w + L.cand_srk2);
+  a.chosen = reinterpret_cast<int32_t*>(w + L.chosen);
   a.max_chunks = kMaxChunks;
 }
 
-// threshold/filter and finish: scores (and the first histogram) -> idx, count
+// the selection: scores (and the first histogram) -> idx, count
 int select_topk(IdxArgs& a, int64_t BQ, int64_t vis_max, hipStream_t s) {
-  int rc;
   StageTimer timer(DLC_STAGE_TOPK_SELECT, s);
-  if (vis_max > 0) {
-    const int64_t nchunks = ceil_div(vis_max, a.keys_per_wg);
-    dim3 grid{(unsigned)nchunks, (unsigned)BQ, 1u};
-    hipLaunchKernelGGL(filter_kernel, grid, dim3(256), 0, s, a);
-    if ((rc = check_launch("csa_index_topk/filter"))) return rc;
+  if (vis_max == 0) {
+    hipLaunchKernelGGL(select_none_kernel, dim3((unsigned)ceil_div(BQ * a.k, 256)), dim3(256), 0, s, a.idx, a.count,
+                       BQ, a.k);
+    return check_launch("csa_index_topk/select");
   }
-  if (vis_max == 0) a.keys_per_wg = 64;
-  hipLaunchKernelGGL(finish_kernel, dim3((unsigned)BQ), dim3(1024), 0, s, a);
-  return check_launch("csa_index_topk/finish");
+  const int64_t nchunks = ceil_div(vis_max, a.keys_per_wg);
+  hipLaunchKernelGGL(select_kernel, dim3((unsigned)nchunks, (unsigned)BQ, 1u), dim3(kSelThreads), 0, s, a);
+  return check_launch("csa_index_topk/select");
 }
 
 // the FP4 call's workspace: the common layout, then the quantized queries
@@ -1487,9 +1611,7 @@ int csa_index_topk(int dtype, int64_t B, int64_t n_q, int64_t n_hI, int64_t cI, 
   bind_ws(a, L, ws, scores, BQ, cap);
   a.idx = idx; a.count = count;
 
-  int rc = fill_u32(a.hist, 0, int64_t(BQ * kBins * 2), s);
-  if (rc) return rc;
-
+  int rc;
   const int64_t vis_max = t_max / m;
   if (vis_max > 0) {
     const bool mfma = mfma_shape && aligned(qI, 16) && aligned(KI, 16);
@@ -1569,8 +1691,8 @@ int csa_index_topk_fp4(int dtype, int64_t B, int64_t n_q, int64_t n_hI, int64_t 
 
   int rc;
   const int64_t vis_max = t_max / m;
-  if (vis_max > 0) {  // histograms cleared and queries quantized by one launch
-    const int64_t nhist = BQ * kBins * 2, qblocks = BQ * n_hI * (cI / 32);
+  if (vis_max > 0) {  // histograms and tickets cleared and queries quantized by one launch
+    const int64_t nhist = BQ * (kBins * 2 + kTicketStride), qblocks = BQ * n_hI * (cI / 32);
     const int fill_blocks = int(std::min<int64_t>(ceil_div(nhist, 1024), 256));
     const dim3 pgrid{unsigned(fill_blocks + ceil_div(qblocks, 256)), 1u, 1u};
     if (dtype == DLC_BF16)
@@ -1597,8 +1719,6 @@ int csa_index_topk_fp4(int dtype, int64_t B, int64_t n_q, int64_t n_hI, int64_t 
       hipLaunchKernelGGL(hist_kernel, grid, dim3(256), 0, s, a);
       if ((rc = check_launch("csa_index_topk_fp4/hist"))) return rc;
     }
-  } else if ((rc = fill_u32(a.hist, 0, int64_t(BQ * kBins * 2), s))) {
-    return rc;
   }
   return select_topk(a, BQ, vis_max, s);
 }

@@ -3,12 +3,10 @@
 // "DeepSeek-V4 Hybrid Attention: CSA and HCA from Scratch", §3 (C^a = H W^{aKV}
 // and the other stream projections), §6.1-6.3 and §8 (c^Q, q^I, w^I, q).
 //
-// bf16 path: 128x128 output tile per workgroup of 4 waves (2x2, 64x64 each),
-// 32-deep K steps staged through LDS with padded rows, v_mfma_f32_32x32x16_bf16,
-// fp32 accumulation; the next K step's global loads are in flight during the
-// current step's MFMAs.  Both operands are K-contiguous, so global loads are
-// whole 16-byte vectors along rows.  Other dtypes and shapes use a VALU kernel.
-#include "common.hpp"
+// bf16 path: one 128x128 output tile per workgroup, the tile product of
+// gemm128.hpp (v_mfma_f32_32x32x16_bf16, fp32 accumulation).  Other dtypes and
+// shapes use a VALU kernel.
+#include "gemm128.hpp"
 
 namespace dlc {
 namespace {
@@ -36,12 +34,10 @@ __global__ void __launch_bounds__(256) project_valu_kernel(ProjArgs a) {
     static_cast<float*>(a.out)[mrow * a.ldo + n] = acc;
 }
 
-constexpr int TM = 128, TN = 128, TK = 32;
-constexpr int LROW = TK + 8;  // padded LDS row (bf16): 80 bytes
+constexpr int TM = kGemmTile, TN = kGemmTile;
 
 __global__ void __launch_bounds__(256) project_mfma_kernel(ProjArgs a) {
-  __shared__ __attribute__((aligned(16))) bf16_raw sA[2][TM * LROW];
-  __shared__ __attribute__((aligned(16))) bf16_raw sB[2][TN * LROW];
+  __shared__ __attribute__((aligned(16))) GemmSmem sm;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int l32 = lane & 31, g2 = lane >> 5;
   const int wm = wave >> 1, wn = wave & 1;
@@ -51,63 +47,16 @@ __global__ void __launch_bounds__(256) project_mfma_kernel(ProjArgs a) {
   const int64_t n0 = (int64_t(blockIdx.x) % tiles_n) * TN;
   const bf16_raw* A = static_cast<const bf16_raw*>(a.A);
   const bf16_raw* W = static_cast<const bf16_raw*>(a.W);
-
-  // staging: 128 rows x 32 k = 512 16-byte vectors per operand, 2 per thread
-  uint4 ra[2], rb[2];
-  auto gload = [&](int64_t k0) {
+  const bf16_raw* arow[2];
+  const bf16_raw* brow[2];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int v = tid + 256 * i;
-      const int row = v >> 2, kc = (v & 3) * 8;
-      const int64_t gk = k0 + kc;
-      const int64_t gm = m0 + row, gn = n0 + row;
-      ra[i] = (gm < a.M && gk < a.K) ? *reinterpret_cast<const uint4*>(A + gm * a.lda + gk) : make_uint4(0, 0, 0, 0);
-      rb[i] = (gn < a.N && gk < a.K) ? *reinterpret_cast<const uint4*>(W + gn * a.ldw + gk) : make_uint4(0, 0, 0, 0);
-    }
-  };
-  auto swrite = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int v = tid + 256 * i;
-      const int row = v >> 2, kc = (v & 3) * 8;
-      *reinterpret_cast<uint4*>(&sA[buf][row * LROW + kc]) = ra[i];
-      *reinterpret_cast<uint4*>(&sB[buf][row * LROW + kc]) = rb[i];
-    }
-  };
-
-  f32x16 acc[2][2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-
-  const int64_t nk = ceil_div(a.K, TK);
-  gload(0);
-  swrite(0);
-  __syncthreads();
-  for (int64_t kt = 0; kt < nk; ++kt) {
-    const int buf = int(kt & 1);
-    if (kt + 1 < nk) gload((kt + 1) * TK);
-#pragma unroll
-    for (int ks = 0; ks < TK / 16; ++ks) {
-      bf16x8 af[2], bfr[2];
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-        af[i] = *reinterpret_cast<const bf16x8*>(&sA[buf][(wm * 64 + i * 32 + l32) * LROW + ks * 16 + g2 * 8]);
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-        bfr[j] = *reinterpret_cast<const bf16x8*>(&sB[buf][(wn * 64 + j * 32 + l32) * LROW + ks * 16 + g2 * 8]);
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
-    }
-    if (kt + 1 < nk) swrite(buf ^ 1);
-    __syncthreads();
+  for (int i = 0; i < 2; ++i) {
+    const int row = (tid + 256 * i) >> 2;
+    arow[i] = m0 + row < a.M ? A + (m0 + row) * a.lda : nullptr;
+    brow[i] = n0 + row < a.N ? W + (n0 + row) * a.ldw : nullptr;
   }
+  f32x16 acc[2][2];
+  gemm128(sm, arow, brow, a.K, acc);
   // D: lane holds column l32, rows 8*(r/4) + 4*g2 + r%4
 #pragma unroll
   for (int i = 0; i < 2; ++i)

@@ -105,6 +105,40 @@ int hca_compress(int dtype, int64_t B, int64_t n, int64_t c, int64_t m_prime,
                  void* Chca, int64_t cap, void* stream);
 
 /*
+ * csa_project_compress / hca_project_compress - the compressor's stream
+ * projections ([Scratch] §3: Z^a = H W^{aZ}, C^a = H W^{aKV}, and the b- and
+ * HCA streams alike) and its pooling (§4-§5, §10) in one pass: the projected
+ * streams are never written.  The result equals dlc_project of each stream
+ * (stored in bf16) followed by csa_compress / hca_compress with the same
+ * biases and entry range, bit for bit.
+ *
+ *  dtype          DLC_BF16 (hidden rows, weights and output)
+ *  B, n, d        sequences, valid rows per sequence, hidden width (d % 8 == 0)
+ *  H              hidden rows: row r of sequence b at H + b*h_bstride + r*ldh
+ *                 (ldh >= d; ldh, h_bstride multiples of 8; 16-byte aligned)
+ *  Wt*            per stream the weight transposed, [c][ldw] (channel j is
+ *                 row j, its d weights contiguous; ldw >= d, ldw % 8 == 0,
+ *                 16-byte aligned): csa takes Z^a, Z^b, C^a, C^b; hca Z, C
+ *  c              width: a multiple of 32 (csa) or 64 (hca)
+ *  m, m_prime     ratio: a divisor of 128 (csa: below 128)
+ *  Ba, Bb, Bias   fp32 [m][c] positional biases, or NULL for zeros
+ *  i_begin,i_end  0 <= i_begin <= i_end <= n/m; entries outside are untouched
+ *  Ccomp/Chca,cap output [B][cap][c] bf16 (cap >= i_end)
+ * Each workgroup projects a 128-row tile of every stream for one group of
+ * channels and pools it in place; a CSA tile completes 128/m - 1 entries (one
+ * block is shared with the next tile and projected twice).
+ */
+int csa_project_compress(int dtype, int64_t B, int64_t n, int64_t d, int64_t c, int64_t m,
+                         const void* H, int64_t ldh, int64_t h_bstride,
+                         const void* WtZa, const void* WtZb, const void* WtCa, const void* WtCb,
+                         int64_t ldw, const float* Ba, const float* Bb, int64_t i_begin,
+                         int64_t i_end, void* Ccomp, int64_t cap, void* stream);
+int hca_project_compress(int dtype, int64_t B, int64_t n, int64_t d, int64_t c, int64_t m_prime,
+                         const void* H, int64_t ldh, int64_t h_bstride, const void* WtZ,
+                         const void* WtC, int64_t ldw, const float* Bias, int64_t i_begin,
+                         int64_t i_end, void* Chca, int64_t cap, void* stream);
+
+/*
  * csa_index_topk - lightning-indexer scores and top-k ([Scratch] §6.4, §7).
  *
  * For query (b, q) at position t = t[b][q], over the visible entries
@@ -125,13 +159,20 @@ int hca_compress(int dtype, int64_t B, int64_t n, int64_t c, int64_t m_prime,
  *  scores  optional out fp32 [B][n_q][cap]: I[s] for visible s (others
  *          untouched), or NULL
  *  ws      workspace of at least csa_index_topk_ws(B, n_q, cap, k) bytes,
- *          256-byte aligned; its contents on entry do not matter
+ *          256-byte aligned; its contents on entry do not matter for the
+ *          result.  Each call leaves the first-digit histograms at its
+ *          start (B*n_q*2048 words) at zero for the next call on the same
+ *          workspace; a workspace that does not start that way (a new
+ *          allocation, or one used for something else in between) is
+ *          detected, and the call then counts the histograms again from
+ *          the scores, which costs it one more pass over them.  Calls that
+ *          share a workspace must not overlap.
  * Limits: 1 <= k <= 8192; bf16 with c^I in {32, 64, 128, 256} and n_hI <= 64
  * (the MFMA shapes), otherwise n_hI*cI <= 8192.
  * Many queries per sequence (a prefill chunk: bf16, c^I = 128, n_q >= 64)
  * run query-tiled, each key row then serving 64 queries; the results are
- * the same.  The workspace grows with B*n_q*cap (six 4-byte arrays per query
- * and entry), so prefill callers pass their queries in chunks.
+ * the same.  The workspace grows with B*n_q*cap (eight 4-byte arrays per
+ * query and entry), so prefill callers pass their queries in chunks.
  */
 size_t csa_index_topk_ws(int64_t B, int64_t n_q, int64_t cap, int64_t k);
 int csa_index_topk(int dtype, int64_t B, int64_t n_q, int64_t n_hI, int64_t cI, int64_t m, int64_t k,

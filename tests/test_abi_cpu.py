@@ -205,6 +205,48 @@ def test_window_validation(L):
     assert L.window_attend_ws(4, 1, 128, 512, 0) == 0
 
 
+def _csa_fused(L, **kw):
+    a = dict(dtype=BF16, B=1, n=256, d=64, c=64, m=4, H=P, ldh=64, hbs=256 * 64, W=P, ldw=64, Ba=None, Bb=None,
+             i0=0, i1=64, out=P, cap=64)
+    a.update(kw)
+    return L.csa_project_compress(a["dtype"], a["B"], a["n"], a["d"], a["c"], a["m"], a["H"], a["ldh"], a["hbs"],
+                                  a["W"], a["W"], a["W"], a["W"], a["ldw"], a["Ba"], a["Bb"], a["i0"], a["i1"],
+                                  a["out"], a["cap"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dtype=F32), E_UNSUPPORTED),  # the fused pass is bf16 only
+    (dict(m=0), E_INVAL),
+    (dict(H=None), E_INVAL),
+    (dict(W=None), E_INVAL),
+    (dict(c=48), E_UNSUPPORTED),       # channels come in groups of 32
+    (dict(m=3), E_UNSUPPORTED),        # the ratio must divide the 128-row tile
+    (dict(m=128, i1=2), E_UNSUPPORTED),  # CSA needs a tile of more than one block
+    (dict(d=60, ldh=64, ldw=64), E_UNSUPPORTED),  # K rows in whole 16-byte vectors
+    (dict(ldh=32), E_SHAPE),           # ldh < d
+    (dict(B=2, hbs=64), E_SHAPE),      # sequences overlap
+    (dict(i1=65), E_SHAPE),            # i_end > n/m
+    (dict(cap=63), E_SHAPE),
+    (dict(i0=5, i1=5), OK),            # empty range: nothing launched
+])
+def test_project_compress_validation(L, kw, status):
+    assert _csa_fused(L, **kw) == status
+    if status:
+        assert binding.last_error().startswith("csa_project_compress")
+
+
+def test_hca_project_compress_validation(L):
+    args = lambda **kw: dict(dict(c=128, m=128, i1=2, cap=2), **kw)  # noqa: E731
+    fused = lambda a: L.hca_project_compress(BF16, 1, 256, 64, a["c"], a["m"], P, 64, 256 * 64, P, P, 64,  # noqa: E731
+                                             None, 0, a["i1"], P, a["cap"], None)
+    assert fused(args(c=96)) == E_UNSUPPORTED   # channels come in groups of 64
+    assert fused(args(m=256, i1=1)) == E_UNSUPPORTED
+    assert fused(args(i1=3)) == E_SHAPE
+    assert fused(args(i1=0)) == OK
+    assert L.hca_project_compress(BF16, 1, 256, 64, 128, 128, P, 64, 256 * 64, P, None, 64, None, 0, 2, P, 2,
+                                  None) == E_INVAL
+
+
 def test_project_validation(L):
     assert L.dlc_project(BF16, 4, 4, 0, P, 8, P, 8, P, 4, BF16, None) == E_INVAL
     assert L.dlc_project(BF16, 4, 4, 8, P, 4, P, 8, P, 4, BF16, None) == E_SHAPE

@@ -158,6 +158,7 @@ def test_compress_neg_inf_logits(dtype, c, m, n):
     ("bf16", 2, 1, 20, 64, 2, 300, 4000, [8000, 7777]),     # head padding (20 -> 32)
     ("bf16", 1, 1, 64, 256, 4, 16, 600, [2400]),
     ("bf16", 1, 2, 64, 128, 4, 8192, 20000, [80000, 40003]),  # the largest k the ABI takes
+    ("bf16", 1, 1, 64, 128, 4, 2048, 200000, [800000]),     # 447 chunks of 448 entries
 ])
 def test_index_topk(dtype, B, n_q, n_hI, cI, m, k, cap, ts):
     seed = 500 + cap
@@ -240,6 +241,37 @@ def test_index_topk_duplicate_rows_break_ties_by_index():
     idx, cnt = dlc.csa_index_topk(qI.to(DEV), wI.to(DEV), KI.to(DEV), t.to(DEV), 4 * cap, 4, k)
     assert int(cnt[0, 0]) == k
     assert idx[0, 0].cpu().tolist() == ties[:k]
+
+
+def test_index_topk_workspace_reuse():
+    """One workspace through several calls: garbage on entry (the selection
+    then counts the first-digit histogram again from the scores), then the
+    state each call leaves behind, for two queries and for one.  Every result
+    against the oracle, a repeated call bit-identical, and the histogram area
+    (the first B*n_q*2048 words) zero after every call."""
+    n_hI, cI, m, k, cap = 64, 128, 4, 512, 30000
+    qI = synth.normal((2, 1, n_hI, cI), 41, dtype="bf16")
+    wI = synth.normal((2, 1, n_hI), 42, dtype="f32")
+    KI = synth.normal((2, cap, cI), 43, dtype="bf16")
+    ws = torch.full((dlc.csa_index_topk_ws(2, 1, cap, k),), 0xA5, dtype=torch.uint8, device=DEV)
+    ws[: 2 * 2048 * 4].view(torch.float32).fill_(float("nan"))  # rows of equal words: their sum wraps to 0
+    tally = FlipTally("index_topk workspace reuse")
+    runs = []
+    for B, ts in ((2, [120000, 90001]), (2, [120000, 90001]), (1, [50003]), (2, [7, 119999])):
+        t = torch.tensor(ts, dtype=torch.int64).reshape(B, 1)
+        scores = torch.empty((B, 1, cap), dtype=torch.float32, device=DEV)
+        idx, cnt = dlc.csa_index_topk(qI[:B].to(DEV), wI[:B].to(DEV), KI[:B].to(DEV), t.to(DEV), int(t.max()), m, k,
+                                      scores=scores, ws=ws)
+        torch.cuda.synchronize()
+        assert not ws[: B * 2048 * 4].any(), "histogram area not cleared"
+        runs.append(idx.cpu())
+        for b in range(B):
+            ref = O.index_scores(qI[b, 0], wI[b, 0], KI[b], ts[b], m)
+            nv = len(ref)
+            tally.add(check_topk(idx[b, 0].cpu().numpy(), int(cnt[b, 0]), ref, k,
+                                 dev_scores=scores[b, 0, :nv].cpu().numpy()))
+    assert torch.equal(runs[0], runs[1])
+    tally.report()
 
 
 def test_index_topk_nothing_visible():
