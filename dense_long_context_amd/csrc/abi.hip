@@ -31,12 +31,16 @@ __global__ void fill_u32_kernel(uint32_t* p, uint32_t v, int64_t n) {
 
 constexpr int kStages = 7;
 static thread_local hipEvent_t g_armed[kStages][2] = {};
+static thread_local int g_depth[kStages] = {};
 
+// Timers of one stage may nest (a call that runs the stage range by range
+// times the whole of it): only the outermost records its events.
 StageTimer::StageTimer(int stage, hipStream_t s) : stage_(stage), s_(s) {
-  if (g_armed[stage_][0]) (void)hipEventRecord(g_armed[stage_][0], s_);
+  if (g_depth[stage_]++ == 0 && g_armed[stage_][0]) (void)hipEventRecord(g_armed[stage_][0], s_);
 }
 
 StageTimer::~StageTimer() {
+  if (--g_depth[stage_] > 0) return;
   if (g_armed[stage_][1]) (void)hipEventRecord(g_armed[stage_][1], s_);
   g_armed[stage_][0] = g_armed[stage_][1] = nullptr;
 }

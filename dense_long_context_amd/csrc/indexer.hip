@@ -68,16 +68,34 @@ struct IdxArgs {
   int32_t* count;      // [BQ]
   int64_t keys_per_wg; // scores / filter chunk
   int64_t max_chunks;
+  // a range of the cache (the streaming prefill): entries key_begin ..
+  // key_begin + cap - 1 of every sequence, KI (and k_scale) pointing at
+  // entry key_begin of sequence 0, sequences key_bstride entries apart;
+  // entry numbers inside the kernels are relative to key_begin
+  int64_t key_begin, key_bstride;
 };
 
+// entries of the range visible to query bq: s < floor(t/m), from key_begin
 __device__ __forceinline__ int64_t visible(const IdxArgs& a, int64_t bq) {
   int64_t t = a.t[bq];
   t = t < 0 ? 0 : (t > a.t_max ? a.t_max : t);
-  int64_t v = t / a.m;
+  int64_t v = t / a.m - a.key_begin;
+  v = v < 0 ? 0 : v;
   return v < a.cap ? v : a.cap;
 }
 
+// the range's entries visible to the query with the largest t (t_max)
+__device__ __forceinline__ int64_t visible_max(const IdxArgs& a) {
+  const int64_t v = a.t_max / a.m - a.key_begin;
+  return v < 0 ? 0 : (v < a.cap ? v : a.cap);
+}
+
 __device__ __forceinline__ float canon_zero(float s) { return s == 0.f ? 0.f : s; }
+
+// the score behind an order_key (zeros come back as +0)
+__device__ __forceinline__ float key_score(uint32_t key) {
+  return __uint_as_float((key & 0x80000000u) ? (key & 0x7fffffffu) : ~key);
+}
 
 // ReLU of an MFMA result in one instruction: v_med3_f32(x, 0, 3e38) is x for
 // 0 <= x <= 3e38 and 0 below (a signed zero may come out as -0, which the
@@ -127,7 +145,7 @@ __global__ void __launch_bounds__(256) scores_valu_kernel(IdxArgs a) {
   __syncthreads();
 
   const int64_t b = bq / a.n_q;
-  const T* K = static_cast<const T*>(a.KI) + b * a.cap * a.cI;
+  const T* K = static_cast<const T*>(a.KI) + b * a.key_bstride * a.cI;
   for (int64_t s = s0 + threadIdx.x; s < s1; s += blockDim.x) {
     const T* ks = K + s * a.cI;
     float score = 0.f;
@@ -185,7 +203,7 @@ __global__ void __launch_bounds__(256) scores_mfma_kernel(IdxArgs a) {
   // whatever this query's t: the first tiles go out by that bound, before
   // t has been read (rows past the query's own visible end are loaded and
   // scored but neither stored nor counted).
-  const int64_t s1l = min(min(a.t_max / a.m, a.cap), s0 + a.keys_per_wg);
+  const int64_t s1l = min(visible_max(a), s0 + a.keys_per_wg);
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -193,7 +211,7 @@ __global__ void __launch_bounds__(256) scores_mfma_kernel(IdxArgs a) {
   const int cI = KT * 32;
 
   const int64_t b = bq / a.n_q;
-  const bf16_raw* K = static_cast<const bf16_raw*>(a.KI) + b * a.cap * cI;
+  const bf16_raw* K = static_cast<const bf16_raw*>(a.KI) + b * a.key_bstride * cI;
   // this wave's tiles: wave, wave+4, ... (the four waves stream one region together)
   auto tiles_of_wave = [&](int64_t end) {
     const int64_t nt = (end - s0 + 15) / 16;
@@ -375,17 +393,18 @@ __global__ void __launch_bounds__(64 * NW) scores_fp4_kernel(IdxArgs a) {
   __shared__ __attribute__((aligned(16))) unsigned char sK[NW][NS][STB];
   __shared__ float sS[NW][kScoreBuf * 16];
   const int64_t bq = blockIdx.y;
+  clear_select_state(a, bq);
   const int64_t s0 = int64_t(blockIdx.x) * a.keys_per_wg;
   // rows below s1l exist whatever this query's t (as in the bf16 kernel):
   // the first tiles go out before t has been read
-  const int64_t s1l = min(min(a.t_max / a.m, a.cap), s0 + a.keys_per_wg);
+  const int64_t s1l = min(visible_max(a), s0 + a.keys_per_wg);
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r16 = lane & 15, g = lane >> 4;
   const int64_t b = bq / a.n_q;
-  const uint8_t* Kc = static_cast<const uint8_t*>(a.KI) + b * a.cap * ROWB;
-  const uint8_t* Ks = a.k_scale + b * a.cap * KB;
+  const uint8_t* Kc = static_cast<const uint8_t*>(a.KI) + b * a.key_bstride * ROWB;
+  const uint8_t* Ks = a.k_scale + b * a.key_bstride * KB;
   auto tiles_of_wave = [&](int64_t end) {
     const int64_t nt = (end - s0 + 15) / 16;
     return nt > wave ? (nt - wave + NW - 1) / NW : int64_t(0);
@@ -639,7 +658,7 @@ __global__ void __launch_bounds__(512) scores_prefill_kernel(IdxArgs a) {
 
   // K^T operands (B, 16 dims x 32 keys per step) of this wave: key
   // k0 + 64*(wave%4) + 32*j + r32, dims 16*ks + 8*hi .. +7
-  const bf16_raw* Kb = static_cast<const bf16_raw*>(a.KI) + b * a.cap * CI;
+  const bf16_raw* Kb = static_cast<const bf16_raw*>(a.KI) + b * a.key_bstride * CI;
   bf16x8 kf[2][KS];
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
@@ -799,8 +818,8 @@ __global__ void __launch_bounds__(512) scores_prefill_fp4_kernel(IdxArgs a) {
   for (int p = 0; p < npre; ++p) issue(p);
 
   // K^T operands: key k0 + 64*(wave%4) + 32*j + r32, block 2*ks + hi
-  const uint8_t* Kc = static_cast<const uint8_t*>(a.KI) + b * a.cap * ROWB;
-  const uint8_t* Ks = a.k_scale + b * a.cap * KB;
+  const uint8_t* Kc = static_cast<const uint8_t*>(a.KI) + b * a.key_bstride * ROWB;
+  const uint8_t* Ks = a.k_scale + b * a.key_bstride * KB;
   i32x8 kf[2][NJ];
   int ksc[2][NJ];
 #pragma unroll
@@ -1460,6 +1479,107 @@ __global__ void __launch_bounds__(256) select_none_kernel(int32_t* idx, int32_t*
   if (i < BQ) count[i] = 0;
 }
 
+// ---------------------------------------------------------------- merge (streaming prefill)
+//
+// Query-tiled calls run the cache in ranges of kStreamKeys entries, so the
+// workspace holds one range's scores and lists, not the whole cache's.  Each
+// range gets its own top-k by the kernels above (entry numbers relative to
+// the range); this kernel folds it into the query's running top-k: the k
+// best of (running, range) under the selection's order (score descending,
+// then index ascending) are the k best of the union, since every entry left
+// out of either part has k better ones in that part.  One workgroup per
+// query: the candidates (running entries first, then the range's, so in
+// ascending index order) are staged in LDS, radix passes over the composite
+// key (score key, then the bit-inverted index) find the k_eff-th, and the
+// chosen ones are written in index order with their scores.
+struct MergeArgs {
+  const int32_t* in_idx;   // [BQ][k] running top-k (entry numbers), or nullptr before the first range
+  const float* in_sc;      // [BQ][k] their scores
+  const int32_t* in_cnt;   // [BQ]
+  const int32_t* part_idx; // [BQ][k] the range's top-k, relative to key_begin
+  const int32_t* part_cnt; // [BQ]
+  const float* part_sc;    // the range's scores, row bq at part_sc + bq*score_ld, relative entries
+  int64_t score_ld, key_begin, k;
+  int32_t* out_idx;        // [BQ][k], -1 after the count
+  float* out_sc;           // [BQ][k] or nullptr (the last range)
+  int32_t* out_cnt;        // [BQ]
+};
+
+__global__ void __launch_bounds__(256) merge_topk_kernel(MergeArgs a) {
+  extern __shared__ uint32_t mlds[];  // [2k] entries, then [2k] score keys
+  __shared__ uint32_t h[kBins];
+  __shared__ uint32_t scratch[19];
+  __shared__ uint32_t wsum[4];
+  const int tid = threadIdx.x;
+  const int64_t bq = blockIdx.x, k = a.k;
+  int32_t* ent = reinterpret_cast<int32_t*>(mlds);
+  uint32_t* key = mlds + 2 * k;
+  const int64_t n_in = a.in_idx ? min(max(int64_t(a.in_cnt[bq]), int64_t(0)), k) : 0;
+  const int64_t n_p = min(max(int64_t(a.part_cnt[bq]), int64_t(0)), k);
+  const uint32_t n = uint32_t(n_in + n_p), keff = uint32_t(min(int64_t(n), k));
+  for (uint32_t j = tid; j < n; j += 256) {
+    int32_t e;
+    float sc;
+    if (j < n_in) {
+      e = a.in_idx[bq * k + j];
+      sc = a.in_sc[bq * k + j];
+    } else {
+      const int32_t r = a.part_idx[bq * k + (j - n_in)];
+      e = int32_t(a.key_begin + r);
+      sc = a.part_sc[bq * a.score_ld + r];
+    }
+    ent[j] = e;
+    key[j] = order_key(sc);
+  }
+  __syncthreads();
+  auto composite = [&](uint32_t j) { return (uint64_t(key[j]) << 32) | uint64_t(0xffffffffu - uint32_t(ent[j])); };
+  // the exact k_eff-th composite key (all are distinct), when some are left out
+  uint64_t thr = 0;
+  if (n > keff) {
+    uint32_t need = keff;
+    uint64_t pval = 0, pmask = 0;
+    for (int pass = 0; pass < 6 && need > 0; ++pass) {
+      const int shift = pass == 0 ? 53 : pass == 1 ? 42 : pass == 2 ? 32 : pass == 3 ? 21 : pass == 4 ? 10 : 0;
+      const int bits = (pass == 2 || pass == 5) ? 10 : 11;
+      const uint32_t dmask = (1u << bits) - 1u;
+      for (int i = tid; i < kBins; i += 256) h[i] = 0;
+      __syncthreads();
+      for (uint32_t j = tid; j < n; j += 256) {
+        const uint64_t c = composite(j);
+        if ((c & pmask) == pval) atomicAdd(&h[(c >> shift) & dmask], 1u);
+      }
+      __syncthreads();
+      uint32_t v[8], above, hD, total;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] = h[8 * tid + i];
+      int D;
+      find_threshold_regs<8>(v, need, scratch, &D, &above, &total, &hD);
+      pval |= uint64_t(D) << shift;
+      pmask |= uint64_t(dmask) << shift;
+      if (above + hD == need) break;
+      need -= above;
+    }
+    thr = pval;
+  }
+  // chosen candidates in index order: thread j counts its run, one scan ranks them
+  const uint32_t per = (n + 255) / 256;
+  const uint32_t lo = tid * per, hi = min(n, lo + per);
+  uint32_t mine = 0;
+  for (uint32_t j = lo; j < hi; ++j) mine += composite(j) >= thr ? 1u : 0u;
+  uint32_t tot;
+  uint32_t r = scan_block<4>(mine, wsum, &tot);
+  for (uint32_t j = lo; j < hi; ++j) {
+    if (composite(j) < thr) continue;
+    if (r < keff) {
+      a.out_idx[bq * k + r] = ent[j];
+      if (a.out_sc) a.out_sc[bq * k + r] = key_score(key[j]);
+    }
+    ++r;
+  }
+  for (int64_t j = keff + tid; j < k; j += 256) a.out_idx[bq * k + j] = -1;
+  if (tid == 0) a.out_cnt[bq] = int32_t(keff);
+}
+
 // ---------------------------------------------------------------- host
 
 struct WsLayout {
@@ -1553,6 +1673,41 @@ int select_topk(IdxArgs& a, int64_t BQ, int64_t vis_max, hipStream_t s) {
   return check_launch("csa_index_topk/select");
 }
 
+// Query-tiled calls (n_q >= kPrefillMinQueries) run the cache in ranges of
+// kStreamKeys entries and fold each range's top-k into a running one
+// (merge_topk_kernel), so their workspace grows with n_q, not with n_q * cap.
+#ifndef DLC_STREAM_KEYS
+#define DLC_STREAM_KEYS 32768
+#endif
+constexpr int64_t kStreamKeys = DLC_STREAM_KEYS;
+bool streaming(int64_t n_q) { return n_q >= kPrefillMinQueries; }
+
+// a call's workspace: the arrays of one range (of the whole cache when not
+// streaming), then the two running top-k buffers and the range's top-k
+struct CallWs {
+  WsLayout L;
+  int64_t range;
+  size_t run_idx[2], run_sc[2], run_cnt[2], part_idx, part_cnt, total;
+};
+CallWs call_ws(int64_t B, int64_t n_q, int64_t cap, int64_t k, bool own_scores) {
+  CallWs w{};
+  const size_t BQ = size_t(B) * size_t(n_q);
+  w.range = streaming(n_q) ? std::min(cap, kStreamKeys) : cap;
+  w.L = ws_layout(B, n_q, w.range, k, own_scores);
+  size_t off = w.L.total;
+  if (streaming(n_q)) {
+    for (int i = 0; i < 2; ++i) {
+      w.run_idx[i] = off; off = align_up(off + BQ * size_t(k) * 4, 256);
+      w.run_sc[i] = off;  off = align_up(off + BQ * size_t(k) * 4, 256);
+      w.run_cnt[i] = off; off = align_up(off + BQ * 4, 256);
+    }
+    w.part_idx = off; off = align_up(off + BQ * size_t(k) * 4, 256);
+    w.part_cnt = off; off = align_up(off + BQ * 4, 256);
+  }
+  w.total = off;
+  return w;
+}
+
 // the FP4 call's workspace: the common layout, then the quantized queries
 struct Fp4Ws {
   size_t code, scale, total;
@@ -1560,10 +1715,88 @@ struct Fp4Ws {
 Fp4Ws fp4_query_off(int64_t B, int64_t n_q, int64_t cap, int64_t k, int64_t n_hI, int64_t cI) {
   const size_t rows = size_t(B) * size_t(n_q) * size_t(n_hI);
   Fp4Ws w{};
-  w.code = ws_layout(B, n_q, cap, k, true).total;
+  w.code = call_ws(B, n_q, cap, k, true).total;
   w.scale = align_up(w.code + rows * size_t(cI / 2), 256);
   w.total = align_up(w.scale + rows * size_t(cI / 32), 256);
   return w;
+}
+
+// entries of the range a.key_begin .. a.key_begin + a.cap - 1 visible to the
+// query with the largest t
+int64_t host_visible_max(const IdxArgs& a) {
+  const int64_t v = a.t_max / a.m - a.key_begin;
+  return v < 0 ? 0 : (v < a.cap ? v : a.cap);
+}
+
+// The call over the whole cache, or range by range.  a carries the inputs;
+// range(a) runs scores and selection over the range set in a (key_begin,
+// cap, KI, k_scale, scores, idx, count); key_row / scale_row are the bytes
+// of one cache entry (and of its scales).
+template <typename Range>
+int run_call(IdxArgs& a, const CallWs& w, void* ws, float* scores, int64_t BQ, int64_t cap, int32_t* idx,
+             int32_t* count, size_t key_row, size_t scale_row, hipStream_t s, Range range) {
+  const void* KI0 = a.KI;
+  const uint8_t* KS0 = a.k_scale;
+  a.key_bstride = cap;
+  if (!streaming(a.n_q)) {
+    a.key_begin = 0;
+    a.cap = cap;
+    bind_ws(a, w.L, ws, scores, BQ, cap);
+    a.idx = idx;
+    a.count = count;
+    return range(a);
+  }
+  const int64_t vis_total = std::min(a.t_max / a.m, cap);
+  if (vis_total == 0) {
+    a.idx = idx;
+    a.count = count;
+    return select_topk(a, BQ, 0, s);
+  }
+  char* wb = static_cast<char*>(ws);
+  const size_t mlds = size_t(2) * size_t(a.k) * 8;
+  if (mlds > 65536) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&merge_topk_kernel),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, int(mlds));
+    if (e != hipSuccess) return fail(DLC_E_HIP, "csa_index_topk: hipFuncSetAttribute: %s", hipGetErrorString(e));
+  }
+  int cur = 0, rc;
+  // the scores stage of a streaming call is the whole indexer: every range's
+  // scores, selection and merge
+  StageTimer timer(DLC_STAGE_INDEX_SCORES, s);
+  for (int64_t r0 = 0; r0 < vis_total; r0 += w.range) {
+    a.key_begin = r0;
+    a.cap = std::min(w.range, cap - r0);
+    a.KI = static_cast<const char*>(KI0) + size_t(r0) * key_row;
+    if (KS0) a.k_scale = KS0 + size_t(r0) * scale_row;
+    bind_ws(a, w.L, ws, scores ? scores + r0 : nullptr, BQ, w.range);
+    if (scores) a.score_ld = cap;
+    a.idx = reinterpret_cast<int32_t*>(wb + w.part_idx);
+    a.count = reinterpret_cast<int32_t*>(wb + w.part_cnt);
+    if ((rc = range(a))) return rc;
+    const bool last = r0 + w.range >= vis_total;
+    MergeArgs m{};
+    if (r0 > 0) {
+      m.in_idx = reinterpret_cast<const int32_t*>(wb + w.run_idx[cur]);
+      m.in_sc = reinterpret_cast<const float*>(wb + w.run_sc[cur]);
+      m.in_cnt = reinterpret_cast<const int32_t*>(wb + w.run_cnt[cur]);
+    }
+    m.part_idx = a.idx;
+    m.part_cnt = a.count;
+    m.part_sc = a.scores;
+    m.score_ld = a.score_ld;
+    m.key_begin = r0;
+    m.k = a.k;
+    m.out_idx = last ? idx : reinterpret_cast<int32_t*>(wb + w.run_idx[cur ^ 1]);
+    m.out_sc = last ? nullptr : reinterpret_cast<float*>(wb + w.run_sc[cur ^ 1]);
+    m.out_cnt = last ? count : reinterpret_cast<int32_t*>(wb + w.run_cnt[cur ^ 1]);
+    {
+      StageTimer timer(DLC_STAGE_TOPK_SELECT, s);
+      hipLaunchKernelGGL(merge_topk_kernel, dim3((unsigned)BQ), dim3(256), mlds, s, m);
+    }
+    if ((rc = check_launch("csa_index_topk/merge"))) return rc;
+    cur ^= 1;
+  }
+  return DLC_OK;
 }
 
 }  // namespace
@@ -1573,7 +1806,7 @@ extern "C" {
 
 size_t csa_index_topk_ws(int64_t B, int64_t n_q, int64_t cap, int64_t k) {
   if (B < 1 || n_q < 1 || cap < 0 || k < 1) return 0;
-  return dlc::ws_layout(B, n_q, cap, k, true).total;
+  return dlc::call_ws(B, n_q, cap, k, true).total;
 }
 
 size_t csa_index_topk_fp4_ws(int64_t B, int64_t n_q, int64_t n_hI, int64_t cI, int64_t cap, int64_t k) {
@@ -1597,58 +1830,59 @@ int csa_index_topk(int dtype, int64_t B, int64_t n_q, int64_t n_hI, int64_t cI, 
               (long long)(t_max / m), (long long)cap);
   DLC_REQUIRE(cap < (int64_t(1) << 31), DLC_E_UNSUPPORTED, "csa_index_topk: cap must be < 2^31");
   DLC_REQUIRE(qI && wI && t && idx && count && (KI || cap == 0), DLC_E_INVAL, "csa_index_topk: NULL argument");
-  const WsLayout L = ws_layout(B, n_q, cap, k, scores == nullptr);
-  DLC_REQUIRE(ws != nullptr && ws_bytes >= L.total, DLC_E_WORKSPACE,
-              "csa_index_topk: workspace of %zu bytes needed, %zu given", L.total, ws_bytes);
+  const CallWs W = call_ws(B, n_q, cap, k, scores == nullptr);
+  DLC_REQUIRE(ws != nullptr && ws_bytes >= W.total, DLC_E_WORKSPACE,
+              "csa_index_topk: workspace of %zu bytes needed, %zu given", W.total, ws_bytes);
   DLC_REQUIRE(aligned(ws, 256), DLC_E_WORKSPACE, "csa_index_topk: workspace must be 256-byte aligned");
   DLC_REQUIRE(B * n_q <= 65535, DLC_E_UNSUPPORTED, "csa_index_topk: B*n_q > 65535");
+  const bool mfma = mfma_shape && aligned(qI, 16) && (cap == 0 || aligned(KI, 16));
+  DLC_REQUIRE(mfma || n_hI * cI <= 8192, DLC_E_UNSUPPORTED, "csa_index_topk: MFMA shape needs 16-byte alignment");
 
   hipStream_t s = as_stream(stream);
   IdxArgs a{};
   a.qI = qI; a.wI = wI; a.KI = KI; a.t = t;
-  a.n_q = n_q; a.n_hI = n_hI; a.cI = cI; a.m = m; a.k = k; a.cap = cap; a.t_max = t_max;
+  a.n_q = n_q; a.n_hI = n_hI; a.cI = cI; a.m = m; a.k = k; a.t_max = t_max;
   const int64_t BQ = B * n_q;
-  bind_ws(a, L, ws, scores, BQ, cap);
-  a.idx = idx; a.count = count;
-
-  int rc;
-  const int64_t vis_max = t_max / m;
-  if (vis_max > 0) {
-    const bool mfma = mfma_shape && aligned(qI, 16) && aligned(KI, 16);
-    DLC_REQUIRE(mfma || n_hI * cI <= 8192, DLC_E_UNSUPPORTED, "csa_index_topk: MFMA shape needs 16-byte alignment");
-    const bool prefill = mfma && cI == 128 && n_q >= kPrefillMinQueries;
-    a.keys_per_wg = keys_per_wg(BQ, vis_max, prefill ? kSelectWorkgroups : kScoreWorkgroups);
-    const int64_t nchunks = ceil_div(vis_max, a.keys_per_wg);
-    dim3 grid{(unsigned)nchunks, (unsigned)BQ, 1u};
-    {
-    StageTimer timer(DLC_STAGE_INDEX_SCORES, s);
-    if (prefill) {
-      dim3 pgrid{(unsigned)ceil_div(vis_max, 256), (unsigned)ceil_div(n_q, 64), (unsigned)B};
-      hipLaunchKernelGGL((scores_prefill_kernel<128>), pgrid, dim3(512), 0, s, a);
-    } else if (mfma) {
-      const int HT = int(ceil_div(n_hI, 16)), KT = int(cI / 32);
+  const size_t esz = dtype == DLC_BF16 ? 2 : 4;
+  const bool prefill = mfma && cI == 128 && n_q >= kPrefillMinQueries;
+  auto range = [&](IdxArgs& r) -> int {
+    int rc;
+    const int64_t vis_max = host_visible_max(r);
+    if (vis_max > 0) {
+      r.keys_per_wg = keys_per_wg(BQ, vis_max, prefill ? kSelectWorkgroups : kScoreWorkgroups);
+      const int64_t nchunks = ceil_div(vis_max, r.keys_per_wg);
+      dim3 grid{(unsigned)nchunks, (unsigned)BQ, 1u};
+      {
+      StageTimer timer(DLC_STAGE_INDEX_SCORES, s);
+      if (prefill) {
+        dim3 pgrid{(unsigned)ceil_div(vis_max, 256), (unsigned)ceil_div(n_q, 64), (unsigned)B};
+        hipLaunchKernelGGL((scores_prefill_kernel<128>), pgrid, dim3(512), 0, s, r);
+      } else if (mfma) {
+        const int HT = int(ceil_div(n_hI, 16)), KT = int(cI / 32);
 #define DLC_SCORES(ht, kt) \
-  if (HT == ht && KT == kt) hipLaunchKernelGGL((scores_mfma_kernel<ht, kt, 4>), grid, dim3(256), 0, s, a);
-      DLC_SCORES(1, 1) DLC_SCORES(1, 2) DLC_SCORES(1, 4) DLC_SCORES(1, 8)
-      DLC_SCORES(2, 1) DLC_SCORES(2, 2) DLC_SCORES(2, 4) DLC_SCORES(2, 8)
-      DLC_SCORES(3, 1) DLC_SCORES(3, 2) DLC_SCORES(3, 4) DLC_SCORES(3, 8)
-      DLC_SCORES(4, 1) DLC_SCORES(4, 2) DLC_SCORES(4, 4) DLC_SCORES(4, 8)
+  if (HT == ht && KT == kt) hipLaunchKernelGGL((scores_mfma_kernel<ht, kt, 4>), grid, dim3(256), 0, s, r);
+        DLC_SCORES(1, 1) DLC_SCORES(1, 2) DLC_SCORES(1, 4) DLC_SCORES(1, 8)
+        DLC_SCORES(2, 1) DLC_SCORES(2, 2) DLC_SCORES(2, 4) DLC_SCORES(2, 8)
+        DLC_SCORES(3, 1) DLC_SCORES(3, 2) DLC_SCORES(3, 4) DLC_SCORES(3, 8)
+        DLC_SCORES(4, 1) DLC_SCORES(4, 2) DLC_SCORES(4, 4) DLC_SCORES(4, 8)
 #undef DLC_SCORES
-    } else {
-      const size_t smem = (kBins + n_hI * cI + n_hI) * 4;
-      if (dtype == DLC_BF16)
-        hipLaunchKernelGGL((scores_valu_kernel<bf16_raw>), grid, dim3(256), smem, s, a);
-      else
-        hipLaunchKernelGGL((scores_valu_kernel<float>), grid, dim3(256), smem, s, a);
+      } else {
+        const size_t smem = (kBins + n_hI * cI + n_hI) * 4;
+        if (dtype == DLC_BF16)
+          hipLaunchKernelGGL((scores_valu_kernel<bf16_raw>), grid, dim3(256), smem, s, r);
+        else
+          hipLaunchKernelGGL((scores_valu_kernel<float>), grid, dim3(256), smem, s, r);
+      }
+      }
+      if ((rc = check_launch("csa_index_topk/scores"))) return rc;
+      if (prefill) {  // the first-digit histogram, which the other scores kernels build as they go
+        hipLaunchKernelGGL(hist_kernel, grid, dim3(256), 0, s, r);
+        if ((rc = check_launch("csa_index_topk/hist"))) return rc;
+      }
     }
-    }
-    if ((rc = check_launch("csa_index_topk/scores"))) return rc;
-    if (prefill) {  // the first-digit histogram, which the other scores kernels build as they go
-      hipLaunchKernelGGL(hist_kernel, grid, dim3(256), 0, s, a);
-      if ((rc = check_launch("csa_index_topk/hist"))) return rc;
-    }
-  }
-  return select_topk(a, BQ, vis_max, s);
+    return select_topk(r, BQ, vis_max, s);
+  };
+  return run_call(a, W, ws, scores, BQ, cap, idx, count, size_t(cI) * esz, 0, s, range);
 }
 
 int csa_index_topk_fp4(int dtype, int64_t B, int64_t n_q, int64_t n_hI, int64_t cI, int64_t m, int64_t k,
@@ -1671,7 +1905,7 @@ int csa_index_topk_fp4(int dtype, int64_t B, int64_t n_q, int64_t n_hI, int64_t 
               "csa_index_topk_fp4: NULL argument");
   DLC_REQUIRE(aligned(qI, 16) && (cap == 0 || aligned(KIc, 16)), DLC_E_INVAL,
               "csa_index_topk_fp4: qI and KIc must be 16-byte aligned");
-  const WsLayout L = ws_layout(B, n_q, cap, k, true);
+  const CallWs CW = call_ws(B, n_q, cap, k, true);
   const Fp4Ws W = fp4_query_off(B, n_q, cap, k, n_hI, cI);
   DLC_REQUIRE(ws != nullptr && ws_bytes >= W.total, DLC_E_WORKSPACE,
               "csa_index_topk_fp4: workspace of %zu bytes needed, %zu given", W.total, ws_bytes);
@@ -1681,46 +1915,53 @@ int csa_index_topk_fp4(int dtype, int64_t B, int64_t n_q, int64_t n_hI, int64_t 
   hipStream_t s = as_stream(stream);
   IdxArgs a{};
   a.qI = qI; a.wI = wI; a.KI = KIc; a.k_scale = KIs; a.t = t;
-  a.n_q = n_q; a.n_hI = n_hI; a.cI = cI; a.m = m; a.k = k; a.cap = cap; a.t_max = t_max;
+  a.n_q = n_q; a.n_hI = n_hI; a.cI = cI; a.m = m; a.k = k; a.t_max = t_max;
   const int64_t BQ = B * n_q;
-  bind_ws(a, L, ws, scores, BQ, cap);
-  a.idx = idx; a.count = count;
   uint8_t* qc = static_cast<uint8_t*>(ws) + W.code;
   uint8_t* qsc = static_cast<uint8_t*>(ws) + W.scale;
   a.q_code = qc; a.q_scale = qsc;
 
   int rc;
-  const int64_t vis_max = t_max / m;
-  if (vis_max > 0) {  // histograms and tickets cleared and queries quantized by one launch
+  if (t_max / m > 0) {  // histograms and tickets cleared and queries quantized by one launch
+    uint32_t* hist = reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + CW.L.hist);
     const int64_t nhist = BQ * (kBins * 2 + kTicketStride), qblocks = BQ * n_hI * (cI / 32);
     const int fill_blocks = int(std::min<int64_t>(ceil_div(nhist, 1024), 256));
     const dim3 pgrid{unsigned(fill_blocks + ceil_div(qblocks, 256)), 1u, 1u};
     if (dtype == DLC_BF16)
-      hipLaunchKernelGGL(prep_fp4_kernel<bf16_raw>, pgrid, dim3(256), 0, s, a.hist, nhist, fill_blocks,
+      hipLaunchKernelGGL(prep_fp4_kernel<bf16_raw>, pgrid, dim3(256), 0, s, hist, nhist, fill_blocks,
                          static_cast<const bf16_raw*>(qI), qblocks, cI / 32, qc, qsc);
     else
-      hipLaunchKernelGGL(prep_fp4_kernel<float>, pgrid, dim3(256), 0, s, a.hist, nhist, fill_blocks,
+      hipLaunchKernelGGL(prep_fp4_kernel<float>, pgrid, dim3(256), 0, s, hist, nhist, fill_blocks,
                          static_cast<const float*>(qI), qblocks, cI / 32, qc, qsc);
     if ((rc = check_launch("csa_index_topk_fp4/prep"))) return rc;
-    const bool prefill = cI == 128 && n_q >= kPrefillMinQueries;
-    a.keys_per_wg = keys_per_wg(BQ, vis_max, prefill ? kSelectWorkgroups : kScoreWorkgroups);
-    dim3 grid{(unsigned)ceil_div(vis_max, a.keys_per_wg), (unsigned)BQ, 1u};
-    StageTimer timer(DLC_STAGE_INDEX_SCORES, s);
-    if (prefill) {
-      dim3 pgrid{(unsigned)ceil_div(vis_max, 256), (unsigned)ceil_div(n_q, 64), (unsigned)B};
-      hipLaunchKernelGGL((scores_prefill_fp4_kernel<128>), pgrid, dim3(512), 0, s, a);
-    }
-    if (!prefill && cI == 128)
-      hipLaunchKernelGGL((scores_fp4_kernel<128, DLC_FP4_NS, DLC_FP4_NW>), grid, dim3(64 * DLC_FP4_NW), 0, s, a);
-    if (!prefill && cI == 256)
-      hipLaunchKernelGGL((scores_fp4_kernel<256, DLC_FP4_NS, DLC_FP4_NW>), grid, dim3(64 * DLC_FP4_NW), 0, s, a);
-    if ((rc = check_launch("csa_index_topk_fp4/scores"))) return rc;
-    if (prefill) {
-      hipLaunchKernelGGL(hist_kernel, grid, dim3(256), 0, s, a);
-      if ((rc = check_launch("csa_index_topk_fp4/hist"))) return rc;
-    }
   }
-  return select_topk(a, BQ, vis_max, s);
+  const bool prefill = cI == 128 && n_q >= kPrefillMinQueries;
+  auto range = [&](IdxArgs& r) -> int {
+    int rc2;
+    const int64_t vis_max = host_visible_max(r);
+    if (vis_max > 0) {
+      r.keys_per_wg = keys_per_wg(BQ, vis_max, prefill ? kSelectWorkgroups : kScoreWorkgroups);
+      dim3 grid{(unsigned)ceil_div(vis_max, r.keys_per_wg), (unsigned)BQ, 1u};
+      {
+      StageTimer timer(DLC_STAGE_INDEX_SCORES, s);
+      if (prefill) {
+        dim3 pgrid{(unsigned)ceil_div(vis_max, 256), (unsigned)ceil_div(n_q, 64), (unsigned)B};
+        hipLaunchKernelGGL((scores_prefill_fp4_kernel<128>), pgrid, dim3(512), 0, s, r);
+      }
+      if (!prefill && cI == 128)
+        hipLaunchKernelGGL((scores_fp4_kernel<128, DLC_FP4_NS, DLC_FP4_NW>), grid, dim3(64 * DLC_FP4_NW), 0, s, r);
+      if (!prefill && cI == 256)
+        hipLaunchKernelGGL((scores_fp4_kernel<256, DLC_FP4_NS, DLC_FP4_NW>), grid, dim3(64 * DLC_FP4_NW), 0, s, r);
+      }
+      if ((rc2 = check_launch("csa_index_topk_fp4/scores"))) return rc2;
+      if (prefill) {
+        hipLaunchKernelGGL(hist_kernel, grid, dim3(256), 0, s, r);
+        if ((rc2 = check_launch("csa_index_topk_fp4/hist"))) return rc2;
+      }
+    }
+    return select_topk(r, BQ, vis_max, s);
+  };
+  return run_call(a, CW, ws, scores, BQ, cap, idx, count, size_t(cI / 2), size_t(cI / 32), s, range);
 }
 
 }  // extern "C"

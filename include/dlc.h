@@ -169,10 +169,12 @@ int hca_project_compress(int dtype, int64_t B, int64_t n, int64_t d, int64_t c, 
  *          share a workspace must not overlap.
  * Limits: 1 <= k <= 8192; bf16 with c^I in {32, 64, 128, 256} and n_hI <= 64
  * (the MFMA shapes), otherwise n_hI*cI <= 8192.
- * Many queries per sequence (a prefill chunk: bf16, c^I = 128, n_q >= 64)
- * run query-tiled, each key row then serving 64 queries; the results are
- * the same.  The workspace grows with B*n_q*cap (eight 4-byte arrays per
- * query and entry), so prefill callers pass their queries in chunks.
+ * Many queries per sequence (a prefill chunk, n_q >= 64) run query-tiled
+ * (bf16, c^I = 128: each key row then serves 64 queries) and stream the
+ * cache in ranges of 32768 entries, each range's top-k folded into a running
+ * top-k; the results are the same.  Their workspace grows with B*n_q*k and
+ * B*n_q*32768, not with cap; a decode call (n_q < 64) keeps eight 4-byte
+ * arrays per query and entry.
  */
 size_t csa_index_topk_ws(int64_t B, int64_t n_q, int64_t cap, int64_t k);
 int csa_index_topk(int dtype, int64_t B, int64_t n_q, int64_t n_hI, int64_t cI, int64_t m, int64_t k,
@@ -361,11 +363,13 @@ int dlc_project(int dtype, int64_t M, int64_t N, int64_t K, const void* A, int64
  * the caller's HIP events `ev_begin` (before) and `ev_end` (after) on that
  * launch's stream, then disarms.  The events are hipEvent_t handles owned by
  * the caller; NULL events disarm the stage.  Stages:
- *   DLC_STAGE_INDEX_SCORES  the indexer score kernel of csa_index_topk (or _fp4)
- *   DLC_STAGE_TOPK_SELECT   the threshold/filter and finish kernels of csa_index_topk (or _fp4)
+ *   DLC_STAGE_INDEX_SCORES  the indexer score kernel of csa_index_topk (or _fp4); for a
+ *                           query-tiled call (n_q >= 64), which runs the cache range by
+ *                           range, the whole indexer: every range's scores, selection and merge
+ *   DLC_STAGE_TOPK_SELECT   the selection kernel of csa_index_topk (or _fp4)
  *   DLC_STAGE_CSA_ATTEND    csa_attend (attention and combine kernels)
  *   DLC_STAGE_HCA_ATTEND    hca_attend (attention and combine kernels)
- *   DLC_STAGE_COMPRESS      csa_compress / hca_compress
+ *   DLC_STAGE_COMPRESS      csa_compress / hca_compress and the fused calls
  *   DLC_STAGE_WINDOW_ATTEND window_attend (attention and merge kernels)
  *
  * dlc_copy - device-to-device copy kernel of `bytes` bytes (a multiple of

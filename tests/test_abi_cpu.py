@@ -171,6 +171,18 @@ def test_workspace_queries(L):
     assert L.hca_attend_ws(16, 1, 128, 512, 16384) >= big
 
 
+def test_prefill_workspace_does_not_grow_with_the_cache(L):
+    """Query-tiled calls (64 or more queries a sequence) run the cache in
+    ranges: their workspace depends on the queries and k, not on cap; decode
+    calls keep one array per entry."""
+    sizes = [L.csa_index_topk_ws(4, 256, cap, 1024) for cap in (40000, 262144, 1 << 20, (1 << 22) + 3)]
+    assert len(set(sizes)) == 1, sizes
+    assert L.csa_index_topk_ws(4, 256, 20000, 1024) <= sizes[0]  # a cache shorter than one range
+    fp4 = [L.csa_index_topk_fp4_ws(4, 256, 64, 128, cap, 1024) for cap in (40000, 1 << 20)]
+    assert fp4[0] == fp4[1]
+    assert L.csa_index_topk_ws(4, 1, 1 << 20, 1024) > L.csa_index_topk_ws(4, 1, 1 << 18, 1024)
+
+
 def test_attend_validation(L):
     args = lambda **kw: dict(dict(dtype=BF16, B=1, n_q=1, n_h=4, c=128, k=8, q=P, C=P, cap=16, idx=P,  # noqa
                                   count=P, out=P, lse=None, ws=None, wsb=0), **kw)

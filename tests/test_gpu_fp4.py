@@ -118,6 +118,7 @@ def test_index_topk_fp4(dtype, B, n_q, n_hI, cI, m, k, cap, ts):
     (2, 100, 64, 4, 100, 3000, 1),      # two query tiles (64 + 36), mixed visibilities
     (1, 64, 20, 2, 50, 700, 2),         # 20 heads: a head group padded at zero weight
     (2, 66, 64, 4, 200, 1001, 4),       # cap % 4 != 0: score rows not 16-byte aligned
+    (1, 64, 64, 4, 700, 66000, 5),      # three ranges of 32768 entries folded into a running top-k
 ])
 def test_index_topk_fp4_prefill(B, n_q, n_hI, m, k, cap, seed):
     """Many queries per sequence: the query-tiled FP4 kernel (32x32x64 MXFP4
