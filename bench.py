@@ -742,6 +742,8 @@ def main():
     ap.add_argument("--pmc-probe", action="store_true",
                     help="run only the indexer on the decode shapes plus a copy kernel of known size "
                          "(the short program that rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE profile)")
+    ap.add_argument("--configs-only", action="store_true",
+                    help="run only the csa128k and hca1m lines (the program their rocprofv3 profiles run)")
     ap.add_argument("--ingest-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write the HBM traffic of the scores kernel from two rocprofv3 counter CSVs")
     args = ap.parse_args()
@@ -755,6 +757,10 @@ def main():
 
     if args.pmc_probe:
         pmc_probe()
+        return
+    if args.configs_only:
+        import torch
+        print(json.dumps({"configs": stage_configs(torch.device("cuda:0"), max(args.steps, 20))}), flush=True)
         return
 
     import torch
