@@ -655,8 +655,9 @@ PMC_COPY_BYTES = 1 << 30
 def pmc_probe():
     """The decode-shaped indexer call (B = 4, 262208-entry caches in three
     rotating sets, t = 2^20) six times, then a copy of PMC_COPY_BYTES (four
-    times the 256 MB last-level cache) three times: the program the FETCH_SIZE
-    / WRITE_SIZE counter runs profile."""
+    times the 256 MB last-level cache) three times and a read of another
+    PMC_COPY_BYTES in the scores kernel's load form (dlc_read) three times: the
+    program the FETCH_SIZE / WRITE_SIZE counter runs profile."""
     import torch
 
     from dense_long_context_amd import binding
@@ -675,11 +676,14 @@ def pmc_probe():
     # the copy's source is written first, so that the indexer's 800 MB of key
     # streams have pushed it out of the caches before it is copied
     a = torch.ones(PMC_COPY_BYTES, dtype=torch.uint8, device=dev)
+    r = torch.ones(PMC_COPY_BYTES, dtype=torch.uint8, device=dev)
     b = torch.empty_like(a)
     for i in range(6):
         binding.csa_index_topk(qI, wI, sets[i % 3], t, cfg.t, m, k, ws=ws)
     for _ in range(3):
         binding.dlc_copy(b, a)
+    for _ in range(3):
+        binding.dlc_read(r)
     torch.cuda.synchronize()
     print(json.dumps({"pmc_probe": "done", "scores_bytes_per_launch": step_bytes(cfg, cfg.t)[1],
                       "copy_bytes": PMC_COPY_BYTES}), flush=True)
@@ -698,26 +702,30 @@ def _counter_kib(csv_path, kernel_part, counter):
 
 
 def ingest_pmc(fetch_csv, write_csv):
-    """HBM bytes per launch of the scores kernel: FETCH_SIZE and WRITE_SIZE, each
-    scaled by what the same counter reads for the copy kernel (which moves
-    PMC_COPY_BYTES each way)."""
+    """HBM bytes per launch of the scores kernel: FETCH_SIZE scaled by what the
+    counter reads for the read kernel (PMC_COPY_BYTES loaded the way the scores
+    kernel loads its keys, 1 KB per wave instruction straight to LDS), and
+    WRITE_SIZE scaled by what it reads for the copy kernel's plain stores."""
     from synth import get_config
 
     cfg = get_config("hybrid1m")
     f_sc = _counter_kib(fetch_csv, "scores_mfma_kernel", "FETCH_SIZE")
     f_cp = _counter_kib(fetch_csv, "copy_kernel", "FETCH_SIZE")
+    f_rd = _counter_kib(fetch_csv, "read_lds_kernel", "FETCH_SIZE")
     w_sc = _counter_kib(write_csv, "scores_mfma_kernel", "WRITE_SIZE")
     w_cp = _counter_kib(write_csv, "copy_kernel", "WRITE_SIZE")
-    if not (f_sc and f_cp and w_sc and w_cp):
-        raise SystemExit("counter CSVs lack the scores or copy kernel dispatches")
+    if not (f_sc and f_cp and f_rd and w_sc and w_cp):
+        raise SystemExit("counter CSVs lack the scores, copy or read kernel dispatches")
     # the first launch of each cache set is cold; the profiled launches rotate 3 sets
-    fetch_factor = (sum(f_cp) / len(f_cp)) * 1024 / PMC_COPY_BYTES
+    copy_fetch_factor = (sum(f_cp) / len(f_cp)) * 1024 / PMC_COPY_BYTES
+    fetch_factor = (sum(f_rd) / len(f_rd)) * 1024 / PMC_COPY_BYTES
     write_factor = (sum(w_cp) / len(w_cp)) * 1024 / PMC_COPY_BYTES
     fetch = (sum(f_sc) / len(f_sc)) * 1024 / fetch_factor
     write = (sum(w_sc) / len(w_sc)) * 1024 / write_factor
     out = {"kernel": SCORES_KERNEL, "workload": "hybrid1m decode indexer, B=4, 262144 visible entries",
            "source_hash": source_hash(), "fetch_kib_per_dispatch": sum(f_sc) / len(f_sc),
-           "write_kib_per_dispatch": sum(w_sc) / len(w_sc), "copy_fetch_factor": fetch_factor,
+           "write_kib_per_dispatch": sum(w_sc) / len(w_sc), "read_fetch_factor": fetch_factor,
+           "copy_fetch_factor": copy_fetch_factor,
            "copy_write_factor": write_factor, "fetch_bytes_per_launch": int(fetch),
            "write_bytes_per_launch": int(write), "hbm_bytes_per_launch": int(fetch + write),
            "algorithmic_bytes_per_launch": step_bytes(cfg, cfg.t)[1], "dispatches": len(f_sc)}

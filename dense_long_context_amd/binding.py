@@ -65,6 +65,7 @@ SIGNATURES = {
     "dlc_project": (_i32, [_i32, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _i32, _vp]),
     "dlc_timing_arm": (_i32, [_i32, _vp, _vp]),
     "dlc_copy": (_i32, [_vp, _vp, _sz, _vp]),
+    "dlc_read": (_i32, [_vp, _sz, _vp]),
 }
 
 STAGE_INDEX_SCORES, STAGE_TOPK_SELECT, STAGE_CSA_ATTEND, STAGE_HCA_ATTEND, STAGE_COMPRESS = 1, 2, 3, 4, 5
@@ -552,6 +553,14 @@ def dlc_copy(dst, src):
     _need(dst.numel() * dst.element_size() == nb, "size mismatch")
     _check("dlc_copy", lib().dlc_copy(_p(dst), _p(src), nb, _stream(src.device)))
     return dst
+
+
+def dlc_read(src):
+    """Read-only kernel over a contiguous device tensor (size a multiple of 1 KB):
+    the calibration reference for read counters; returns nothing."""
+    _on_device(src.device, src=src)
+    _need(src.is_contiguous(), "src must be contiguous")
+    _check("dlc_read", lib().dlc_read(_p(src), src.numel() * src.element_size(), _stream(src.device)))
 
 
 def default_scale(c: int) -> float:

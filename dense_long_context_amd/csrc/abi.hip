@@ -67,6 +67,27 @@ __global__ void __launch_bounds__(256) copy_kernel(const u32x4* __restrict__ src
   }
 }
 
+// Read-only bandwidth reference in the load form of the indexer's key stream:
+// each wave moves 1 KB per global_load_lds_dwordx4 straight into LDS (no
+// register write), up to eight in flight in a ring of 1 KB slots, and every
+// 1 KB of the source is loaded once.  Nothing is written; the counters of
+// this kernel calibrate the read counters of the kernels that load the
+// same way.
+__global__ void __launch_bounds__(256) read_lds_kernel(const unsigned char* src, int64_t n_kb) {
+  constexpr int kSlots = 8;
+  __shared__ __attribute__((aligned(1024))) unsigned char ring[4][kSlots][1024];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const uint32_t lds = (uint32_t)(uintptr_t)DLC_LDS(&ring[wave][0][0]);
+  const int64_t stride = int64_t(gridDim.x) * 4;
+  int k = 0;
+  for (int64_t i = int64_t(blockIdx.x) * 4 + wave; i < n_kb; i += stride, ++k) {
+    if (k >= kSlots) wait_vm<kSlots - 1>();  // the load that last used this slot has landed
+    dma_row(src + i * 1024, uint32_t(lane) * 16u, lds + uint32_t(k % kSlots) * 1024u);
+  }
+  wait_vm<0>();
+}
+
 int fill_u32(uint32_t* p, uint32_t v, int64_t n, hipStream_t s) {
   if (n <= 0) return DLC_OK;
   int64_t blocks = ceil_div(n, 256);
@@ -114,6 +135,19 @@ int dlc_copy(void* dst, const void* src, size_t bytes, void* stream) {
   hipLaunchKernelGGL(copy_kernel, dim3((unsigned)blocks), dim3(256), 0, as_stream(stream),
                      static_cast<const u32x4*>(src), static_cast<u32x4*>(dst), n);
   return check_launch("dlc_copy");
+}
+
+int dlc_read(const void* src, size_t bytes, void* stream) {
+  using namespace dlc;
+  DLC_REQUIRE(src, DLC_E_INVAL, "dlc_read: NULL pointer");
+  DLC_REQUIRE(bytes % 1024 == 0 && aligned(src, 16), DLC_E_INVAL,
+              "dlc_read: size must be a multiple of 1024 and the pointer 16-byte aligned");
+  const int64_t n_kb = int64_t(bytes / 1024);
+  if (n_kb == 0) return DLC_OK;
+  const int64_t blocks = std::min<int64_t>(ceil_div(n_kb, 4 * 32), 2048);
+  hipLaunchKernelGGL(read_lds_kernel, dim3((unsigned)blocks), dim3(256), 0, as_stream(stream),
+                     static_cast<const unsigned char*>(src), n_kb);
+  return check_launch("dlc_read");
 }
 
 }  // extern "C"

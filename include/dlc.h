@@ -386,6 +386,14 @@ enum {
 };
 int dlc_timing_arm(int stage, void* ev_begin, void* ev_end);
 int dlc_copy(void* dst, const void* src, size_t bytes, void* stream);
+/*
+ * dlc_read - read-only kernel over `bytes` bytes (a multiple of 1024, src
+ * 16-byte aligned) in the load form of the indexer's key stream (1 KB per
+ * wave instruction, straight to LDS); each byte is loaded once and nothing
+ * is written.  The reference that calibrates the read counters of kernels
+ * that load that way.
+ */
+int dlc_read(const void* src, size_t bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -259,6 +259,13 @@ def test_hca_project_compress_validation(L):
                                   None) == E_INVAL
 
 
+def test_bandwidth_references_validation(L):
+    assert L.dlc_copy(P, P, 1000, None) == E_INVAL        # not a multiple of 16 bytes
+    assert L.dlc_read(P, 1000, None) == E_INVAL           # not a multiple of 1 KB
+    assert L.dlc_read(None, 1024, None) == E_INVAL
+    assert L.dlc_read(P, 0, None) == OK
+
+
 def test_project_validation(L):
     assert L.dlc_project(BF16, 4, 4, 0, P, 8, P, 8, P, 4, BF16, None) == E_INVAL
     assert L.dlc_project(BF16, 4, 4, 8, P, 4, P, 8, P, 4, BF16, None) == E_SHAPE
