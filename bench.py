@@ -33,7 +33,7 @@ sys.path.insert(0, ROOT)
 METRIC = "decode query-tokens/s per CSA+HCA layer at 1M ctx; achieved HBM GB/s vs peak"
 PEAK_HBM_GBS = 8000.0
 PEAK_BF16_TFLOPS = 2500.0  # dense bf16 MFMA
-SCORES_KERNEL = "scores_mfma_kernel<4, 4, 4>"
+SCORES_KERNEL = "scores_reg_kernel<4, 4, 3>"
 SCORES_KERNEL_FP4 = "scores_fp4_kernel<128, 4, 8>"
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "indexer_scores_hybrid1m_counters.json")
 
@@ -656,8 +656,8 @@ def pmc_probe():
     """The decode-shaped indexer call (B = 4, 262208-entry caches in three
     rotating sets, t = 2^20) six times, then a copy of PMC_COPY_BYTES (four
     times the 256 MB last-level cache) three times and a read of another
-    PMC_COPY_BYTES in the scores kernel's load form (dlc_read) three times: the
-    program the FETCH_SIZE / WRITE_SIZE counter runs profile."""
+    PMC_COPY_BYTES in the scores kernel's load form (dlc_read, tile form) three
+    times: the program the FETCH_SIZE / WRITE_SIZE counter runs profile."""
     import torch
 
     from dense_long_context_amd import binding
@@ -683,7 +683,7 @@ def pmc_probe():
     for _ in range(3):
         binding.dlc_copy(b, a)
     for _ in range(3):
-        binding.dlc_read(r)
+        binding.dlc_read(r, binding.READ_TILES)
     torch.cuda.synchronize()
     print(json.dumps({"pmc_probe": "done", "scores_bytes_per_launch": step_bytes(cfg, cfg.t)[1],
                       "copy_bytes": PMC_COPY_BYTES}), flush=True)
@@ -704,15 +704,15 @@ def _counter_kib(csv_path, kernel_part, counter):
 def ingest_pmc(fetch_csv, write_csv):
     """HBM bytes per launch of the scores kernel: FETCH_SIZE scaled by what the
     counter reads for the read kernel (PMC_COPY_BYTES loaded the way the scores
-    kernel loads its keys, 1 KB per wave instruction straight to LDS), and
-    WRITE_SIZE scaled by what it reads for the copy kernel's plain stores."""
+    kernel loads its keys: 16-byte register loads in the MFMA operand pattern),
+    and WRITE_SIZE scaled by what it reads for the copy kernel's plain stores."""
     from synth import get_config
 
     cfg = get_config("hybrid1m")
-    f_sc = _counter_kib(fetch_csv, "scores_mfma_kernel", "FETCH_SIZE")
+    f_sc = _counter_kib(fetch_csv, "scores_reg_kernel", "FETCH_SIZE")
     f_cp = _counter_kib(fetch_csv, "copy_kernel", "FETCH_SIZE")
-    f_rd = _counter_kib(fetch_csv, "read_lds_kernel", "FETCH_SIZE")
-    w_sc = _counter_kib(write_csv, "scores_mfma_kernel", "WRITE_SIZE")
+    f_rd = _counter_kib(fetch_csv, "read_tiles_kernel", "FETCH_SIZE")
+    w_sc = _counter_kib(write_csv, "scores_reg_kernel", "WRITE_SIZE")
     w_cp = _counter_kib(write_csv, "copy_kernel", "WRITE_SIZE")
     if not (f_sc and f_cp and f_rd and w_sc and w_cp):
         raise SystemExit("counter CSVs lack the scores, copy or read kernel dispatches")

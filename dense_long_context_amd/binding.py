@@ -65,7 +65,7 @@ SIGNATURES = {
     "dlc_project": (_i32, [_i32, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _i32, _vp]),
     "dlc_timing_arm": (_i32, [_i32, _vp, _vp]),
     "dlc_copy": (_i32, [_vp, _vp, _sz, _vp]),
-    "dlc_read": (_i32, [_vp, _sz, _vp]),
+    "dlc_read": (_i32, [_vp, _sz, _i32, _vp]),
 }
 
 STAGE_INDEX_SCORES, STAGE_TOPK_SELECT, STAGE_CSA_ATTEND, STAGE_HCA_ATTEND, STAGE_COMPRESS = 1, 2, 3, 4, 5
@@ -555,12 +555,17 @@ def dlc_copy(dst, src):
     return dst
 
 
-def dlc_read(src):
-    """Read-only kernel over a contiguous device tensor (size a multiple of 1 KB):
-    the calibration reference for read counters; returns nothing."""
+READ_LDS, READ_TILES = 0, 1  # load forms of dlc_read
+
+
+def dlc_read(src, form=READ_TILES):
+    """Read-only kernel over a contiguous device tensor in one load form (the
+    calibration reference for read counters): READ_TILES (size a multiple of
+    4 KB, the bf16 indexer's form) or READ_LDS (a multiple of 1 KB, the FP4
+    indexer's form); returns nothing."""
     _on_device(src.device, src=src)
     _need(src.is_contiguous(), "src must be contiguous")
-    _check("dlc_read", lib().dlc_read(_p(src), src.numel() * src.element_size(), _stream(src.device)))
+    _check("dlc_read", lib().dlc_read(_p(src), src.numel() * src.element_size(), int(form), _stream(src.device)))
 
 
 def default_scale(c: int) -> float:

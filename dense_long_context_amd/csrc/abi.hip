@@ -67,12 +67,12 @@ __global__ void __launch_bounds__(256) copy_kernel(const u32x4* __restrict__ src
   }
 }
 
-// Read-only bandwidth reference in the load form of the indexer's key stream:
-// each wave moves 1 KB per global_load_lds_dwordx4 straight into LDS (no
-// register write), up to eight in flight in a ring of 1 KB slots, and every
-// 1 KB of the source is loaded once.  Nothing is written; the counters of
-// this kernel calibrate the read counters of the kernels that load the
-// same way.
+// Read-only bandwidth references, one per load form; nothing is written, and
+// the counters of each calibrate the read counters of the kernels that load
+// the same way.  Direct-to-LDS form (the FP4 indexer's key stream): each wave
+// moves 1 KB per global_load_lds_dwordx4 straight into LDS (no register
+// write), up to eight in flight in a ring of 1 KB slots, and every 1 KB of
+// the source is loaded once.
 __global__ void __launch_bounds__(256) read_lds_kernel(const unsigned char* src, int64_t n_kb) {
   constexpr int kSlots = 8;
   __shared__ __attribute__((aligned(1024))) unsigned char ring[4][kSlots][1024];
@@ -86,6 +86,26 @@ __global__ void __launch_bounds__(256) read_lds_kernel(const unsigned char* src,
     dma_row(src + i * 1024, uint32_t(lane) * 16u, lds + uint32_t(k % kSlots) * 1024u);
   }
   wait_vm<0>();
+}
+
+// Register form in the bf16 indexer's MFMA operand pattern: the source is
+// 16-row tiles of 256-byte rows; for each of its tiles (tiles interleaved
+// over the grid's waves) lane l loads the 16 bytes at row l%16, byte
+// 64*kt + 16*(l/16), for kt = 0..3, so one instruction covers 64 bytes of
+// each of 16 rows.  The loaded words are folded together and handed to an
+// empty asm statement, which keeps the loads without storing anything.
+__global__ void __launch_bounds__(256) read_tiles_kernel(const unsigned char* src, int64_t n_tiles) {
+  const int lane = threadIdx.x & 63, r16 = lane & 15, g = lane >> 4;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t stride = int64_t(gridDim.x) * 4;
+  u32x4 acc = {0u, 0u, 0u, 0u};
+#pragma unroll 3
+  for (int64_t t = int64_t(blockIdx.x) * 4 + wave; t < n_tiles; t += stride) {
+    const unsigned char* row = src + (t * 16 + r16) * 256 + 16 * g;
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) acc ^= *reinterpret_cast<const u32x4*>(row + 64 * kt);
+  }
+  asm volatile("" ::"v"(acc.x), "v"(acc.y), "v"(acc.z), "v"(acc.w));
 }
 
 int fill_u32(uint32_t* p, uint32_t v, int64_t n, hipStream_t s) {
@@ -137,16 +157,24 @@ int dlc_copy(void* dst, const void* src, size_t bytes, void* stream) {
   return check_launch("dlc_copy");
 }
 
-int dlc_read(const void* src, size_t bytes, void* stream) {
+int dlc_read(const void* src, size_t bytes, int form, void* stream) {
   using namespace dlc;
   DLC_REQUIRE(src, DLC_E_INVAL, "dlc_read: NULL pointer");
-  DLC_REQUIRE(bytes % 1024 == 0 && aligned(src, 16), DLC_E_INVAL,
-              "dlc_read: size must be a multiple of 1024 and the pointer 16-byte aligned");
-  const int64_t n_kb = int64_t(bytes / 1024);
-  if (n_kb == 0) return DLC_OK;
-  const int64_t blocks = std::min<int64_t>(ceil_div(n_kb, 4 * 32), 2048);
-  hipLaunchKernelGGL(read_lds_kernel, dim3((unsigned)blocks), dim3(256), 0, as_stream(stream),
-                     static_cast<const unsigned char*>(src), n_kb);
+  DLC_REQUIRE(form == DLC_READ_LDS || form == DLC_READ_TILES, DLC_E_INVAL, "dlc_read: unknown form %d", form);
+  const size_t unit = form == DLC_READ_LDS ? 1024 : 4096;
+  DLC_REQUIRE(bytes % unit == 0 && aligned(src, 16), DLC_E_INVAL,
+              "dlc_read: size must be a multiple of %zu and the pointer 16-byte aligned", unit);
+  const int64_t n = int64_t(bytes / unit);
+  if (n == 0) return DLC_OK;
+  if (form == DLC_READ_LDS) {
+    const int64_t blocks = std::min<int64_t>(ceil_div(n, 4 * 32), 2048);
+    hipLaunchKernelGGL(read_lds_kernel, dim3((unsigned)blocks), dim3(256), 0, as_stream(stream),
+                       static_cast<const unsigned char*>(src), n);
+  } else {
+    const int64_t blocks = std::min<int64_t>(ceil_div(n, 4), 768);
+    hipLaunchKernelGGL(read_tiles_kernel, dim3((unsigned)blocks), dim3(256), 0, as_stream(stream),
+                       static_cast<const unsigned char*>(src), n);
+  }
   return check_launch("dlc_read");
 }
 

@@ -168,96 +168,91 @@ __global__ void __launch_bounds__(256) scores_valu_kernel(IdxArgs a) {
 // 32-dim step.  Lane l holds head/key l%16 of the A/B operands and dims
 // 8*(l/16) .. +7 of each 32-dim step; the result holds key l%16 and heads
 // 4*(l/16) .. +3, and the head sum is finished with two cross-lane adds.
-// Queries stay in registers for the whole pass; they arrive once per
-// workgroup, wave w moving heads 16w .. 16w+15 into the last stage of its
-// ring, from where every wave reads its operands.  Key tiles (16 keys,
-// 16*2*c^I bytes) arrive by direct global->LDS loads, one instruction moving
-// 1 KB of consecutive rows, so HBM sees whole lines.  Each wave streams its
-// own tiles through a ring of NS LDS stages, and only it reads them, so the
-// loop has no barrier.  A tile's operands are read into registers first and
-// its stage refilled right away, so NS tiles are in flight during the
-// compute.  Within a row, 16-byte chunk c is stored at slot
-// c ^ (row % chunks): the 16 rows that one ds_read_b128 pass reads at the
-// same chunk then fall on distinct banks (64 banks of 4 bytes).
-// The scores of kScoreBuf tiles collect in LDS and go out together: vmcnt
-// counts stores too, so a store per tile between the tile loads would make
-// every wait for a tile also wait for part of the next one.
+// Queries stay in registers for the whole pass.
+// The FP4 kernel below collects the scores of kScoreBuf tiles in LDS and
+// stores them together, since its key tiles arrive by direct-to-LDS loads
+// whose waits would otherwise also cover each score store.
 
 constexpr int kScoreBuf = 32;  // tiles whose scores a wave collects before storing them
+#ifndef DLC_SCORES_U
+#define DLC_SCORES_U 3  // key tiles in flight per wave in the register-load scores kernel
+#endif
+#ifndef DLC_SCORES_OCC
+#define DLC_SCORES_OCC 3  // waves per SIMD the register-load scores kernel is compiled for
+#endif
+#ifndef DLC_SCORES_RWGS
+#define DLC_SCORES_RWGS 768  // its workgroups per call (three per CU, one round)
+#endif
 
-template <int HT, int KT, int NS>
-__global__ void __launch_bounds__(256) scores_mfma_kernel(IdxArgs a) {
+// The bf16 kernel loads the key operands straight into registers: each
+// lane loads, per 16-key tile, the four 16-byte pieces of its key row that
+// its K^T operand needs (row r16 of the tile, bytes 64*kt + 16*g), so one
+// load instruction covers 64 bytes of 16 rows and the tile never passes
+// through LDS (on this part the register form streams faster than the
+// direct-to-LDS one).  The G = gridDim.x workgroups of a query take its tiles
+// interleaved, wave v of workgroup x taking tiles (it*G + x)*4 + v, so at any
+// moment the whole grid reads one narrow window of each key cache, as a
+// grid-strided copy does, rather than G far-apart streams.  Each wave keeps
+// U tiles in flight (U * 16 VGPRs): the loop is unrolled by U so each tile's
+// registers are named statically, a tile's registers are refilled with the
+// wave's tile U steps on as soon as its MFMAs have read them, and every load
+// is unconditional (rows clamp to the last row any query of the batch sees)
+// with no early exit inside a group of U, so every path into the loop head
+// carries the same loads in flight and the waits before each tile count only
+// the tiles behind it.  Queries arrive through LDS once per workgroup; each
+// tile's 16 scores go out as one 64-byte store.
+template <int HT, int KT, int U>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DLC_SCORES_OCC)))
+scores_reg_kernel(IdxArgs a) {
   constexpr int ROWB = KT * 64;     // bytes per key row (2 * c^I)
   constexpr int CPR = KT * 4;       // 16-byte chunks per row
-  constexpr int TILEB = 16 * ROWB;  // one tile: 16 keys
-  constexpr int RPI = 1024 / ROWB;  // rows per 1 KB load (KT loads per tile)
+  constexpr int RPI = 1024 / ROWB;  // rows per 1 KB query load
   static_assert(RPI * KT == 16, "tile geometry");
-  static_assert(HT <= 4, "one 16-head block of queries per wave");
+  static_assert(HT <= 4, "one 16-head block of queries per staging wave");
   __shared__ uint32_t hist[kBins];
-  __shared__ __attribute__((aligned(1024))) unsigned char sK[4][NS][TILEB];
-  __shared__ float sS[4][kScoreBuf * 16];
+  __shared__ __attribute__((aligned(1024))) unsigned char sQ[HT][16 * ROWB];
   const int64_t bq = blockIdx.y;
   clear_select_state(a, bq);
-  const int64_t s0 = int64_t(blockIdx.x) * a.keys_per_wg;
-  // The grid covers floor(t_max/m) <= cap entries, so rows below s1l exist
-  // whatever this query's t: the first tiles go out by that bound, before
-  // t has been read (rows past the query's own visible end are loaded and
-  // scored but neither stored nor counted).
-  const int64_t s1l = min(visible_max(a), s0 + a.keys_per_wg);
+  const int64_t vmax = visible_max(a);  // rows below vmax exist whatever this query's t
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r16 = lane & 15, g = lane >> 4;
   const int cI = KT * 32;
+  const int64_t step = int64_t(gridDim.x) * 4;      // tiles between a wave's consecutive tiles
+  const int64_t first = int64_t(blockIdx.x) * 4 + wave;
 
   const int64_t b = bq / a.n_q;
   const bf16_raw* K = static_cast<const bf16_raw*>(a.KI) + b * a.key_bstride * cI;
-  // this wave's tiles: wave, wave+4, ... (the four waves stream one region together)
-  auto tiles_of_wave = [&](int64_t end) {
-    const int64_t nt = (end - s0 + 15) / 16;
-    return nt > wave ? (nt - wave + 3) / 4 : int64_t(0);
-  };
-  // load j of a tile: lane -> row rho = j*RPI + lane/CPR, slot lane%CPR, which
-  // holds chunk slot ^ (rho % CPR) of that row; rows past s1l repeat row
-  // s1l - 1
-  auto issue = [&](int64_t it, int st) {
-    const int64_t row0 = s0 + (wave + 4 * it) * 16;  // < s1l
-    const bf16_raw* base = K + row0 * cI;
+  // this lane's pieces of the wave's tile it
+  auto load = [&](int64_t it, uint4 (&dst)[KT]) {
+    const int64_t row = min((first + it * step) * 16 + r16, vmax - 1);
+    const bf16_raw* p = K + row * cI + 8 * g;
 #pragma unroll
-    for (int j = 0; j < KT; ++j) {
-      const int rho = j * RPI + lane / CPR;
-      const int chunk = (lane % CPR) ^ (rho % CPR);
-      const int64_t row = min(row0 + rho, s1l - 1);
-      const uint32_t off = uint32_t((row - row0) * ROWB + chunk * 16);
-      const uint32_t lds = (uint32_t)(uintptr_t)DLC_LDS(&sK[wave][st][0]) + uint32_t(j * 1024);
-      dma_row(base, off, lds);
-    }
+    for (int kt = 0; kt < KT; ++kt) dst[kt] = *reinterpret_cast<const uint4*>(p + 32 * kt);
   };
   // queries: wave w < HT moves heads 16w .. 16w+15 (rows past n_hI repeat
-  // head n_hI-1) into the last stage of its ring, rows in order
+  // head n_hI-1) into its block of sQ, rows in order
   if (wave < HT) {
     const bf16_raw* qg = static_cast<const bf16_raw*>(a.qI) + bq * a.n_hI * cI;
 #pragma unroll
     for (int j = 0; j < KT; ++j) {
       const int h = min(wave * 16 + j * RPI + lane / CPR, int(a.n_hI) - 1);
       const uint32_t off = uint32_t(h * ROWB + (lane % CPR) * 16);
-      const uint32_t lds = (uint32_t)(uintptr_t)DLC_LDS(&sK[wave][NS - 1][0]) + uint32_t(j * 1024);
+      const uint32_t lds = (uint32_t)(uintptr_t)DLC_LDS(&sQ[wave][0]) + uint32_t(j * 1024);
       dma_row(qg, off, lds);
     }
   }
-  {
-    const int64_t first = tiles_of_wave(s1l);
+  uint4 kb[U][KT];
 #pragma unroll
-    for (int p = 0; p < NS - 1; ++p)
-      if (p < first) issue(p, p);
-  }
+  for (int u = 0; u < U; ++u) load(u, kb[u]);
   const int64_t nvis = visible(a, bq);
-  if (s0 >= nvis) {  // nothing of this chunk is visible to the query (the whole workgroup)
-    wait_vm<0>();
+  const int64_t n_tiles = (nvis + 15) / 16;
+  if (int64_t(blockIdx.x) * 64 >= nvis) {  // no wave of this workgroup has a visible tile
+    __builtin_amdgcn_s_waitcnt(0);
     return;
   }
-  const int64_t s1 = min(nvis, s0 + a.keys_per_wg);
-  const int64_t my_tiles = tiles_of_wave(s1);  // <= the tiles issued by s1l
+  const int64_t my_tiles = n_tiles > first ? (n_tiles - first + step - 1) / step : 0;
   for (int i = threadIdx.x; i < kBins; i += blockDim.x) hist[i] = 0;
   float wv[HT][4];
 #pragma unroll
@@ -267,95 +262,53 @@ __global__ void __launch_bounds__(256) scores_mfma_kernel(IdxArgs a) {
       const int h = ht * 16 + g * 4 + r;
       wv[ht][r] = h < a.n_hI ? a.wI[bq * a.n_hI + h] : 0.f;
     }
-#pragma unroll
-  for (int ht = 0; ht < HT; ++ht)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) asm volatile("" ::"v"(wv[ht][r]));
-  wait_vm<0>();     // the query block and the first tiles
+  wait_vm<0>();     // the query block (and the first tiles)
   __syncthreads();  // every wave's query rows landed; hist cleared
-  // A operand, rows = heads: head ht*16 + r16 from wave ht's block; heads past
-  // n_hI are zeroed (their weight is 0 too)
   bf16x8 qf[HT][KT];
 #pragma unroll
   for (int ht = 0; ht < HT; ++ht) {
     const bool pad = ht * 16 + r16 >= a.n_hI;
 #pragma unroll
     for (int kt = 0; kt < KT; ++kt) {
-      const uint4 v = *reinterpret_cast<const uint4*>(&sK[ht][NS - 1][r16 * ROWB + kt * 64 + g * 16]);
+      const uint4 v = *reinterpret_cast<const uint4*>(&sQ[ht][r16 * ROWB + kt * 64 + g * 16]);
       qf[ht][kt] = __builtin_bit_cast(bf16x8, pad ? make_uint4(0, 0, 0, 0) : v);
     }
   }
-#pragma unroll
-  for (int ht = 0; ht < HT; ++ht)
-#pragma unroll
-    for (int kt = 0; kt < KT; ++kt) asm volatile("" ::"v"(qf[ht][kt]));
-  __syncthreads();  // every wave holds its operands: the last stages may take tiles
-  if (NS - 1 < my_tiles) issue(NS - 1, NS - 1);
+  float* srow = a.scores + bq * a.score_ld;
 
-  for (int64_t it = 0; it < my_tiles; ++it) {
-    const int st = int(it % NS);
-    // tiles it+1 .. it+NS-1 (those that exist) were issued after tile it;
-    // tile it has landed once at most their loads are outstanding (tiles
-    // issued by s1l past my_tiles only make the wait longer)
-    const int64_t rest = my_tiles - 1 - it;
-    const int after = rest < NS - 1 ? int(rest) : NS - 1;
-    static_assert(NS == 4, "the waits below enumerate three tiles in flight");
-    if (after == 3) wait_vm<3 * KT>();
-    else if (after == 2) wait_vm<2 * KT>();
-    else if (after == 1) wait_vm<KT>();
-    else wait_vm<0>();
-    asm volatile("" ::: "memory");
-    // the tile's operands into registers; the stage then takes tile it+NS,
-    // so NS tiles stay in flight while this one is computed
-    const unsigned char* tile = &sK[wave][st][0];
-    bf16x8 kb[KT];
+  // whole groups of U tiles: the up to U-1 tiles past my_tiles in the last
+  // group lie at or past nvis, so their stores and counts are masked off
+  for (int64_t it0 = 0; it0 < my_tiles; it0 += U) {
 #pragma unroll
-    for (int kt = 0; kt < KT; ++kt) {
-      const int slot = (4 * kt + g) ^ (r16 % CPR);
-      kb[kt] = *reinterpret_cast<const bf16x8*>(tile + r16 * ROWB + slot * 16);
-    }
-    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the reads are done
-    asm volatile("" ::: "memory");
-    if (it + NS < my_tiles) issue(it + NS, st);
-    f32x4 acc[HT];
+    for (int u = 0; u < U; ++u) {
+      const int64_t it = it0 + u;
+      f32x4 acc[HT];
 #pragma unroll
-    for (int ht = 0; ht < HT; ++ht) acc[ht] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int ht = 0; ht < HT; ++ht) acc[ht] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int kt = 0; kt < KT; ++kt)
+      for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
-      for (int ht = 0; ht < HT; ++ht)
-        acc[ht] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qf[ht][kt], kb[kt], acc[ht], 0, 0, 0);
-    // four independent partial sums (one per head row of the lane), then a tree
-    float ps[4];
+        for (int ht = 0; ht < HT; ++ht)
+          acc[ht] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qf[ht][kt], __builtin_bit_cast(bf16x8, kb[u][kt]),
+                                                            acc[ht], 0, 0, 0);
+      load(it + U, kb[u]);
+      float ps[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      ps[r] = wv[0][r] * relu(acc[0][r]);
+      for (int r = 0; r < 4; ++r) {
+        ps[r] = wv[0][r] * relu(acc[0][r]);
 #pragma unroll
-      for (int ht = 1; ht < HT; ++ht) ps[r] = fmaf(wv[ht][r], relu(acc[ht][r]), ps[r]);
-    }
-    const float part = rows4_sum((ps[0] + ps[1]) + (ps[2] + ps[3]));
-    const int64_t s = s0 + (wave + 4 * it) * 16 + r16;
-    const int slot = int(it % kScoreBuf);
-    if (g == 0) {
-      const float score = canon_zero(part);
-      sS[wave][slot * 16 + r16] = score;
-      if (s < s1) atomicAdd(&hist[order_key(score) >> kShift1], 1u);
-    }
-    if (slot == kScoreBuf - 1 || it + 1 == my_tiles) {
-      // the wave's buffered tiles it-slot .. it, 16 scores each (the LDS
-      // accesses of one wave run in order)
-      asm volatile("" ::: "memory");
-      const int64_t t0 = it - slot;
-#pragma unroll
-      for (int q = 0; q < kScoreBuf / 4; ++q) {
-        const int idx = q * 64 + lane, tl = idx >> 4;
-        const int64_t sk = s0 + (wave + 4 * (t0 + tl)) * 16 + (idx & 15);
-        if (tl <= slot && sk < s1) a.scores[bq * a.score_ld + sk] = sS[wave][idx];
+        for (int ht = 1; ht < HT; ++ht) ps[r] = fmaf(wv[ht][r], relu(acc[ht][r]), ps[r]);
       }
-      asm volatile("" ::: "memory");
+      const float part = rows4_sum((ps[0] + ps[1]) + (ps[2] + ps[3]));
+      const int64_t s = (first + it * step) * 16 + r16;
+      if (g == 0 && s < nvis) {
+        const float score = canon_zero(part);
+        srow[s] = score;
+        atomicAdd(&hist[order_key(score) >> kShift1], 1u);
+      }
     }
   }
-  wait_vm<0>();  // tiles issued by s1l that no iteration waited for
+  __builtin_amdgcn_s_waitcnt(0);  // the tiles loaded past the end
   flush_hist(hist, a.hist + bq * kBins);
 }
 
@@ -1586,15 +1539,17 @@ struct WsLayout {
   size_t scores, hist, ccnt, sel, cand, cand_kseg, cand_srk, cand_idx, cand_key, cand_srk2, chosen, total;
 };
 
-// keys per scores/filter workgroup: a multiple of 64 chosen so that the whole
-// batch takes about kScoreWorkgroups workgroups - the number that are resident
-// at once (2 per CU for the scores kernel, whose key stages take 64 KB of
-// LDS), so there is no partial second round - and at most kMaxChunks chunks
-// per query
+// keys per selection (and FP4 scores) workgroup: a multiple of 64 chosen so
+// that the whole batch takes about kScoreWorkgroups workgroups - the number
+// that are resident at once (2 per CU for the FP4 scores kernel, whose key
+// stages take 64 KB of LDS), so there is no partial second round - and at most
+// kMaxChunks chunks per query.  The bf16 scores kernel sizes its own grid
+// (kScoreRegWorkgroups, its tiles interleaved over the workgroups of a query).
 #ifndef DLC_SCORES_WGS
 #define DLC_SCORES_WGS 512
 #endif
 constexpr int64_t kScoreWorkgroups = DLC_SCORES_WGS;
+constexpr int64_t kScoreRegWorkgroups = DLC_SCORES_RWGS;
 // query-tiled (prefill) calls: the chunks of the histogram and filter
 // kernels, sized for eight 256-thread workgroups per CU
 constexpr int64_t kSelectWorkgroups = 2048;
@@ -1859,8 +1814,12 @@ int csa_index_topk(int dtype, int64_t B, int64_t n_q, int64_t n_hI, int64_t cI, 
         hipLaunchKernelGGL((scores_prefill_kernel<128>), pgrid, dim3(512), 0, s, r);
       } else if (mfma) {
         const int HT = int(ceil_div(n_hI, 16)), KT = int(cI / 32);
+        // G workgroups per query, about kScoreRegWorkgroups in all, 64 keys each at least
+        const IdxArgs& rs = r;
+        const int64_t G = std::max<int64_t>(1, std::min(ceil_div(kScoreRegWorkgroups, BQ), ceil_div(vis_max, 64)));
+        const dim3 sgrid{(unsigned)G, (unsigned)BQ, 1u};
 #define DLC_SCORES(ht, kt) \
-  if (HT == ht && KT == kt) hipLaunchKernelGGL((scores_mfma_kernel<ht, kt, 4>), grid, dim3(256), 0, s, r);
+  if (HT == ht && KT == kt) hipLaunchKernelGGL((scores_reg_kernel<ht, kt, DLC_SCORES_U>), sgrid, dim3(256), 0, s, rs);
         DLC_SCORES(1, 1) DLC_SCORES(1, 2) DLC_SCORES(1, 4) DLC_SCORES(1, 8)
         DLC_SCORES(2, 1) DLC_SCORES(2, 2) DLC_SCORES(2, 4) DLC_SCORES(2, 8)
         DLC_SCORES(3, 1) DLC_SCORES(3, 2) DLC_SCORES(3, 4) DLC_SCORES(3, 8)

@@ -386,14 +386,21 @@ enum {
 };
 int dlc_timing_arm(int stage, void* ev_begin, void* ev_end);
 int dlc_copy(void* dst, const void* src, size_t bytes, void* stream);
+/* load forms of dlc_read */
+#define DLC_READ_LDS 0   /* 1 KB per wave instruction straight to LDS (global_load_lds_dwordx4) */
+#define DLC_READ_TILES 1 /* 16-byte register loads in the bf16 indexer's MFMA operand pattern */
 /*
- * dlc_read - read-only kernel over `bytes` bytes (a multiple of 1024, src
- * 16-byte aligned) in the load form of the indexer's key stream (1 KB per
- * wave instruction, straight to LDS); each byte is loaded once and nothing
- * is written.  The reference that calibrates the read counters of kernels
- * that load that way.
+ * dlc_read - read-only kernel over `bytes` bytes of device memory at src
+ * (16-byte aligned); each byte is loaded once and nothing is written.  The
+ * reference that calibrates the read counters of kernels that load the same
+ * way.  form DLC_READ_LDS: the FP4 indexer's key-stream form (bytes a
+ * multiple of 1024).  form DLC_READ_TILES: the bf16 indexer's form (bytes a
+ * multiple of 4096, read as 16-row tiles of 256-byte rows, lane l of a wave
+ * loading row l%16 at byte 64*kt + 16*(l/16) for kt = 0..3).  Returns
+ * DLC_E_INVAL for a NULL or misaligned src, a size that is not a multiple of
+ * the form's unit or an unknown form.
  */
-int dlc_read(const void* src, size_t bytes, void* stream);
+int dlc_read(const void* src, size_t bytes, int form, void* stream);
 
 #ifdef __cplusplus
 }

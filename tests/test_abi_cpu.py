@@ -261,9 +261,12 @@ def test_hca_project_compress_validation(L):
 
 def test_bandwidth_references_validation(L):
     assert L.dlc_copy(P, P, 1000, None) == E_INVAL        # not a multiple of 16 bytes
-    assert L.dlc_read(P, 1000, None) == E_INVAL           # not a multiple of 1 KB
-    assert L.dlc_read(None, 1024, None) == E_INVAL
-    assert L.dlc_read(P, 0, None) == OK
+    assert L.dlc_read(P, 1000, 0, None) == E_INVAL        # direct-to-LDS form: not a multiple of 1 KB
+    assert L.dlc_read(P, 1024, 1, None) == E_INVAL        # tile form: not a multiple of 4 KB
+    assert L.dlc_read(P, 4096, 2, None) == E_INVAL        # no such form
+    assert L.dlc_read(None, 1024, 0, None) == E_INVAL
+    assert L.dlc_read(P, 0, 0, None) == OK
+    assert L.dlc_read(P, 0, 1, None) == OK
 
 
 def test_project_validation(L):
