@@ -1193,12 +1193,12 @@ Plan plan(int dtype, int64_t BQ, int64_t n_h, int64_t c, int64_t nkeys, bool mer
     return s < 1 ? 1 : (s > kMaxSplits ? kMaxSplits : s);
   };
   // c = 512: 128 heads (8 waves) per workgroup, or 64 (4 waves) when the
-  // minimum split length leaves the 128-head grid under half the target and
-  // the smaller groups add workgroups
+  // minimum split length leaves the 128-head grid at or under half the target
+  // and the smaller groups add workgroups
   p.heads = p.mfma ? 128 : 1;
   p.head_groups = p.mfma ? ceil_div(n_h, p.heads) : n_h;
   int64_t s = split_count(p.mfma ? BQ * p.head_groups : BQ * n_h);
-  if (p.mfma && c == 512 && n_h > 64 && 2 * BQ * p.head_groups * s < kTargetWorkgroups) {
+  if (p.mfma && c == 512 && n_h > 64 && 2 * BQ * p.head_groups * s <= kTargetWorkgroups) {
     const int64_t hg64 = ceil_div(n_h, 64), s64 = split_count(BQ * hg64);
     if (hg64 * s64 > p.head_groups * s) {
       p.heads = 64;

@@ -200,9 +200,12 @@ constexpr int kScoreBuf = 32;  // tiles whose scores a wave collects before stor
 // with no early exit inside a group of U, so every path into the loop head
 // carries the same loads in flight and the waits before each tile count only
 // the tiles behind it.  Queries arrive through LDS once per workgroup; each
-// tile's 16 scores go out as one 64-byte store.
+// tile's 16 scores go out as one 64-byte store.  Registers: the query block
+// takes 4*HT*KT VGPRs and the tiles in flight 4*U*KT; c^I = 256 (KT = 8)
+// keeps two tiles in flight at two waves per SIMD, the narrower rows three
+// at DLC_SCORES_OCC waves per SIMD.
 template <int HT, int KT, int U>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DLC_SCORES_OCC)))
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KT >= 8 ? 2 : DLC_SCORES_OCC)))
 scores_reg_kernel(IdxArgs a) {
   constexpr int ROWB = KT * 64;     // bytes per key row (2 * c^I)
   constexpr int CPR = KT * 4;       // 16-byte chunks per row
@@ -1819,7 +1822,8 @@ int csa_index_topk(int dtype, int64_t B, int64_t n_q, int64_t n_hI, int64_t cI, 
         const int64_t G = std::max<int64_t>(1, std::min(ceil_div(kScoreRegWorkgroups, BQ), ceil_div(vis_max, 64)));
         const dim3 sgrid{(unsigned)G, (unsigned)BQ, 1u};
 #define DLC_SCORES(ht, kt) \
-  if (HT == ht && KT == kt) hipLaunchKernelGGL((scores_reg_kernel<ht, kt, DLC_SCORES_U>), sgrid, dim3(256), 0, s, rs);
+  if (HT == ht && KT == kt)                                                                              \
+    hipLaunchKernelGGL((scores_reg_kernel<ht, kt, kt >= 8 ? 2 : DLC_SCORES_U>), sgrid, dim3(256), 0, s, rs);
         DLC_SCORES(1, 1) DLC_SCORES(1, 2) DLC_SCORES(1, 4) DLC_SCORES(1, 8)
         DLC_SCORES(2, 1) DLC_SCORES(2, 2) DLC_SCORES(2, 4) DLC_SCORES(2, 8)
         DLC_SCORES(3, 1) DLC_SCORES(3, 2) DLC_SCORES(3, 4) DLC_SCORES(3, 8)
