@@ -182,20 +182,24 @@ def test_index_topk(dtype, B, n_q, n_hI, cI, m, k, cap, ts):
     tally.report()
 
 
-@pytest.mark.parametrize("B,n_q,n_hI,m,k,cap,seed", [
-    (2, 100, 64, 4, 100, 3000, 1),      # two query tiles (64 + 36), mixed visibilities
-    (1, 64, 20, 2, 50, 700, 2),         # 20 heads, one full tile
-    (3, 70, 64, 4, 1024, 2000, 3),      # k >= visible for most queries
-    (2, 66, 64, 4, 200, 1001, 4),       # cap % 4 != 0: score rows not 16-byte aligned (scalar head and tail)
-    (1, 64, 64, 4, 512, 70001, 5),      # three ranges of 32768 entries folded into a running top-k
-    (1, 64, 32, 4, 8192, 36000, 6),     # the largest k across two ranges
+@pytest.mark.parametrize("B,n_q,n_hI,cI,m,k,cap,seed", [
+    (2, 100, 64, 128, 4, 100, 3000, 1),      # two query tiles (64 + 36), mixed visibilities
+    (1, 64, 20, 128, 2, 50, 700, 2),         # 20 heads, one full tile
+    (3, 70, 64, 128, 4, 1024, 2000, 3),      # k >= visible for most queries
+    (2, 66, 64, 128, 4, 200, 1001, 4),       # cap % 4 != 0: score rows not 16-byte aligned (scalar head and tail)
+    (1, 64, 64, 128, 4, 512, 70001, 5),      # three ranges of 32768 entries folded into a running top-k
+    (1, 64, 32, 128, 4, 8192, 36000, 6),     # the largest k across two ranges
+    # c^I other than 128: the per-query MFMA scores kernel runs range by range
+    # (its rows counted from each range's first entry)
+    (1, 64, 64, 64, 4, 300, 40000, 7),
+    (1, 64, 32, 256, 4, 100, 33000, 8),      # c^I = 256: two tiles in flight per wave
 ])
-def test_index_topk_prefill(B, n_q, n_hI, m, k, cap, seed):
+def test_index_topk_prefill(B, n_q, n_hI, cI, m, k, cap, seed):
     """Many queries per sequence: the query-tiled MFMA scores kernel and the
-    histogram pass, against the oracle for every query.  These calls run the
-    cache in ranges of 32768 entries, each range's top-k folded into a
-    running one, so a cache past 32768 entries crosses ranges."""
-    cI = 128
+    histogram pass (c^I = 128), or the per-query MFMA scores kernel (other
+    widths), against the oracle for every query.  These calls run the cache
+    in ranges of 32768 entries, each range's top-k folded into a running one,
+    so a cache past 32768 entries crosses ranges."""
     qI = synth.normal((B, n_q, n_hI, cI), 700 + seed, dtype="bf16")
     wI = synth.normal((B, n_q, n_hI), 701 + seed, dtype="f32")
     KI = synth.normal((B, cap, cI), 702 + seed, dtype="bf16")
