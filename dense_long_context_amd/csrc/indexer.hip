@@ -1542,12 +1542,13 @@ struct WsLayout {
   size_t scores, hist, ccnt, sel, cand, cand_kseg, cand_srk, cand_idx, cand_key, cand_srk2, chosen, total;
 };
 
-// keys per selection (and FP4 scores) workgroup: a multiple of 64 chosen so
-// that the whole batch takes about kScoreWorkgroups workgroups - the number
-// that are resident at once (2 per CU for the FP4 scores kernel, whose key
-// stages take 64 KB of LDS), so there is no partial second round - and at most
-// kMaxChunks chunks per query.  The bf16 scores kernel sizes its own grid
-// (kScoreRegWorkgroups, its tiles interleaved over the workgroups of a query).
+// keys per workgroup of the FP4 (and VALU) scores kernels: a multiple of 64
+// chosen so that the whole batch takes about kScoreWorkgroups workgroups - the
+// number that are resident at once (2 per CU for the FP4 scores kernel, whose
+// key stages take 64 KB of LDS), so there is no partial second round - and at
+// most kMaxChunks chunks per query.  The bf16 scores kernel sizes its own grid
+// (kScoreRegWorkgroups, its tiles interleaved over the workgroups of a query),
+// and the selection its own chunks (kSelectDecodeWorkgroups).
 #ifndef DLC_SCORES_WGS
 #define DLC_SCORES_WGS 512
 #endif
@@ -1556,6 +1557,13 @@ constexpr int64_t kScoreRegWorkgroups = DLC_SCORES_RWGS;
 // query-tiled (prefill) calls: the chunks of the histogram and filter
 // kernels, sized for eight 256-thread workgroups per CU
 constexpr int64_t kSelectWorkgroups = 2048;
+// per-query (decode) calls: the chunks of the selection kernel, which need
+// not be the scores kernel's.  Fewer, longer chunks leave the workgroup that
+// finishes a query fewer chunk lists to walk.
+#ifndef DLC_SELECT_WGS
+#define DLC_SELECT_WGS 256
+#endif
+constexpr int64_t kSelectDecodeWorkgroups = DLC_SELECT_WGS;
 // queries per sequence from which the indexer runs query-tiled (prefill)
 #ifndef DLC_PREFILL_MIN_Q
 #define DLC_PREFILL_MIN_Q 64
@@ -1567,9 +1575,9 @@ constexpr int64_t kPrefillMinQueries = DLC_PREFILL_MIN_Q;
 #ifndef DLC_FP4_NW
 #define DLC_FP4_NW 8  // waves per workgroup of the FP4 scores kernel
 #endif
-// wgs: the workgroups the batch should take (kScoreWorkgroups for the
-// decode scores kernel, which shares its chunks with the selection;
-// kSelectWorkgroups when only the histogram and filter kernels use them)
+// wgs: the workgroups the batch should take (kScoreWorkgroups for the FP4
+// and VALU scores kernels, kSelectDecodeWorkgroups for the decode selection,
+// kSelectWorkgroups for the query-tiled histogram and filter kernels)
 int64_t keys_per_wg(int64_t BQ, int64_t vis_max, int64_t wgs = kScoreWorkgroups) {
   const int64_t vis = vis_max > 0 ? vis_max : 1;
   int64_t kpw = ceil_div(ceil_div(vis * BQ, wgs), 64) * 64;
@@ -1843,6 +1851,7 @@ int csa_index_topk(int dtype, int64_t B, int64_t n_q, int64_t n_hI, int64_t cI, 
         if ((rc = check_launch("csa_index_topk/hist"))) return rc;
       }
     }
+    if (vis_max > 0 && !prefill) r.keys_per_wg = keys_per_wg(BQ, vis_max, kSelectDecodeWorkgroups);
     return select_topk(r, BQ, vis_max, s);
   };
   return run_call(a, W, ws, scores, BQ, cap, idx, count, size_t(cI) * esz, 0, s, range);
@@ -1922,6 +1931,7 @@ int csa_index_topk_fp4(int dtype, int64_t B, int64_t n_q, int64_t n_hI, int64_t 
         if ((rc2 = check_launch("csa_index_topk_fp4/hist"))) return rc2;
       }
     }
+    if (vis_max > 0 && !prefill) r.keys_per_wg = keys_per_wg(BQ, vis_max, kSelectDecodeWorkgroups);
     return select_topk(r, BQ, vis_max, s);
   };
   return run_call(a, CW, ws, scores, BQ, cap, idx, count, size_t(cI / 2), size_t(cI / 32), s, range);
