@@ -577,11 +577,12 @@ __global__ void __launch_bounds__(64 * NW) attend512_kernel(AttArgs a) {
     if constexpr (MODE == kGather) v = v && sRow[j] != -1;
     return uint32_t(__ballot(v) & 0xffffffffu);
   };
-  // tiles 0..2 in flight before the loop; tile i+3 is issued once every wave
-  // is past tile i-1 (the barrier of step i)
+  // tile 0 and Q first, waited for together; then tiles 1 and 2, so that the
+  // first tile's compute starts as soon as its own rows are in (waiting for
+  // three tiles of every workgroup at once put the whole first burst of the
+  // call in front of it); tile i+3 is issued once every wave is past tile
+  // i-1 (the barrier of step i)
   if (ntile > 0) issue(0);
-  if (ntile > 1) issue(1);
-  if (ntile > 2) issue(2);
   // Q^T operand: lane holds head hbase + r16, dims 32*ks + 8*g .. +7; heads
   // past n_h read head n_h-1 (their columns and outputs are never used)
   bf16x8 qf[KS];
@@ -590,12 +591,14 @@ __global__ void __launch_bounds__(64 * NW) attend512_kernel(AttArgs a) {
     const bf16_raw* qp = static_cast<const bf16_raw*>(a.q) + (bq * a.n_h + h) * CD + g * 8;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) qf[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(qp + ks * 32));
-    // wait for Q here, together with the first three tiles, so that no
-    // vector-memory wait for Q lands inside the tile loop (it would drain
-    // the tile loads in flight)
+    // wait for Q here, so that no vector-memory wait for it lands inside the
+    // tile loop (it would drain the tile loads in flight)
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) asm volatile("" ::"v"(qf[ks]));
   }
+  wait_vm<0>();  // tile 0 and Q
+  if (ntile > 1) issue(1);
+  if (ntile > 2) issue(2);
 
   f32x4 o[NT];
 #pragma unroll
@@ -804,8 +807,7 @@ __global__ void __launch_bounds__(64 * NW) attend512_kernel(AttArgs a) {
   };
 
   if (ntile > 0) {
-    wait_vm<0>();
-    lds_barrier();
+    lds_barrier();  // tile 0 (waited for above) from every wave
     const uint32_t vmask = valid_mask(0);
     if (active) {
       qk_only(tile_ptr(0));
