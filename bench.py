@@ -878,6 +878,26 @@ def main():
     copy_gbs = 2 * (1 << 30) * 10 / (e0.elapsed_time(e1) * 1e-3) / 1e9
     del a, b
 
+    # read-only reference: dlc_read in the scores kernel's own load form over
+    # the same number of bytes, three rotating buffers (past the last-level
+    # cache), one HIP event pair per launch as for the scores kernel
+    nb = (int(idx_bytes) + 4095) // 4096 * 4096
+    rbufs = [torch.empty(nb, dtype=torch.uint8, device=dev) for _ in range(3)]
+    for i in range(3):
+        binding.dlc_read(rbufs[i], binding.READ_TILES)
+    torch.cuda.synchronize()
+    read_ms = []
+    for i in range(30):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        binding.dlc_read(rbufs[i % 3], binding.READ_TILES)
+        e1.record()
+        torch.cuda.synchronize()
+        read_ms.append(e0.elapsed_time(e1))
+    read_avg_ms = sum(read_ms) / len(read_ms)
+    read_gbs = nb / (read_avg_ms * 1e-3) / 1e9
+    del rbufs
+
     traffic = None
     if os.path.exists(COUNTERS_FILE):
         with open(COUNTERS_FILE) as f:
@@ -905,7 +925,12 @@ def main():
         "roofline": {"kernel": SCORES_KERNEL, "bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic,
                      "avg_launch_us": round(k_avg_ms * 1e3, 3),
-                     "algorithmic_bytes_per_launch": int(idx_bytes)},
+                     "algorithmic_bytes_per_launch": int(idx_bytes),
+                     "read_reference": {"kernel": "dlc_read (tile form)", "bytes": nb,
+                                        "avg_launch_us": round(read_avg_ms * 1e3, 3), "gbs": round(read_gbs, 1),
+                                        "kernel_frac_of_it": round(achieved / read_gbs, 4),
+                                        "note": "a read of the same bytes in the scores kernel's load form, "
+                                                "nothing else, timed the same way"}},
         "ms_per_step_events": percentiles(step_ms),
         "ms_per_step_with_kernel_events": round(ms_armed / K, 5),
         "with_sliding_window": {"value": round(cfg.B * K / (ms_win * 1e-3), 1), "ms_per_step": round(ms_win / K, 5),
