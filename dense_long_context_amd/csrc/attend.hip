@@ -584,9 +584,26 @@ __global__ void __launch_bounds__(64 * NW) attend512_kernel(AttArgs a) {
   // i-1 (the barrier of step i)
   if (ntile > 0) issue(0);
   // Q^T operand: lane holds head hbase + r16, dims 32*ks + 8*g .. +7; heads
-  // past n_h read head n_h-1 (their columns and outputs are never used)
+  // past n_h read head n_h-1 (their columns and outputs are never used).
+  // Loaded straight into that layout, every instruction touches 64 bytes of
+  // 16 rows, which the memory pipeline serves slowly; so the first QW waves
+  // move their 16 rows whole (1 KB a direct-to-LDS instruction) into ring
+  // buffers 1.. (free until tiles 1 and 2 are issued below), rows 1040 bytes
+  // apart so that a ds_read_b128 pass over 16 rows hits 16 distinct bank
+  // groups, and read the operand from there; the other waves (whose rows
+  // would not fit) load it directly.
+  constexpr int QROW = 1040, QW = (NST - 1) * kTileBytes / (16 * QROW) < NW ? (NST - 1) * kTileBytes / (16 * QROW) : NW;
+  static_assert(QW >= 1, "Q staging");
+  const bool q_lds = wave < QW;
+  const uint32_t qst = lds0 + uint32_t(kTileBytes) + uint32_t(wave * 16 * QROW);
   bf16x8 qf[KS];
-  {
+  if (q_lds) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int64_t h = min(hbase + r, a.n_h - 1);
+      dma_row(static_cast<const bf16_raw*>(a.q) + (bq * a.n_h + h) * CD, uint32_t(lane) * 16u, qst + uint32_t(r * QROW));
+    }
+  } else {
     const int64_t h = min(hbase + r16, a.n_h - 1);
     const bf16_raw* qp = static_cast<const bf16_raw*>(a.q) + (bq * a.n_h + h) * CD + g * 8;
 #pragma unroll
@@ -597,6 +614,13 @@ __global__ void __launch_bounds__(64 * NW) attend512_kernel(AttArgs a) {
     for (int ks = 0; ks < KS; ++ks) asm volatile("" ::"v"(qf[ks]));
   }
   wait_vm<0>();  // tile 0 and Q
+  lds_barrier();  // every wave's tile-0 rows and staged Q rows
+  if (q_lds) {
+    const unsigned char* qs = sK + kTileBytes + wave * 16 * QROW + r16 * QROW + 16 * g;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) qf[ks] = *reinterpret_cast<const bf16x8*>(qs + 64 * ks);
+  }
+  lds_barrier();  // the staged rows are read before tiles 1 and 2 overwrite them
   if (ntile > 1) issue(1);
   if (ntile > 2) issue(2);
 
@@ -807,8 +831,7 @@ __global__ void __launch_bounds__(64 * NW) attend512_kernel(AttArgs a) {
   };
 
   if (ntile > 0) {
-    lds_barrier();  // tile 0 (waited for above) from every wave
-    const uint32_t vmask = valid_mask(0);
+    const uint32_t vmask = valid_mask(0);  // tile 0 is in LDS for every wave (the barriers above)
     if (active) {
       qk_only(tile_ptr(0));
       softmax(vmask, 0);
