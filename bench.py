@@ -34,7 +34,7 @@ METRIC = "decode query-tokens/s per CSA+HCA layer at 1M ctx; achieved HBM GB/s v
 PEAK_HBM_GBS = 8000.0
 PEAK_BF16_TFLOPS = 2500.0  # dense bf16 MFMA
 SCORES_KERNEL = "scores_reg_kernel<4, 4, 3>"
-SCORES_KERNEL_FP4 = "scores_fp4_kernel<128, 4, 8>"
+SCORES_KERNEL_FP4 = "scores_fp4_reg_kernel<128, 3>"
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "indexer_scores_hybrid1m_counters.json")
 
 

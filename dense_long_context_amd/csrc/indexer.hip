@@ -321,8 +321,10 @@ scores_reg_kernel(IdxArgs a) {
 // += Q[16 heads][128 dims] x K^T[128 dims][16 keys], each operand carrying one
 // E8M0 scale per 32 dims, so every product is exact and only the fp32 sums
 // round.  Lane l supplies head/key l%16 and the 32-dim block l/16 of each
-// 128-dim step: 16 code bytes and one scale byte.  The streaming is that of
-// the bf16 kernel: a 16-key tile (16 code rows of c^I/2 bytes, then their 16
+// 128-dim step: 16 code bytes and one scale byte.  Two kernels: the
+// register-load one below (scores_fp4_reg_kernel) runs whenever the scale
+// array is 4-byte aligned; this one, which stages tiles through LDS, takes
+// the rest.  Here a 16-key tile (16 code rows of c^I/2 bytes, then their 16
 // scale rows of c^I/32 bytes) arrives by direct global->LDS loads into the
 // wave's own ring of NS stages, NS-1 tiles in flight, no barrier.  Within a
 // code row, 16-byte chunk c sits at slot c ^ ((row / RPB) % CPR) (RPB rows
@@ -506,6 +508,132 @@ __global__ void __launch_bounds__(64 * NW) scores_fp4_kernel(IdxArgs a) {
 // the histograms; the others quantize the queries, one 32-element block per
 // thread, with the encoding of mxfp4_quantize (codes [rows][c^I/2], scales
 // [rows][c^I/32]).
+// The same MXFP4 product with the key operands loaded straight into
+// registers, in the bf16 register kernel's scheme (tiles interleaved over
+// the G workgroups of a query, U tiles in flight per wave, every load
+// unconditional with rows clamped to the last row the batch may see, whole
+// groups of U tiles).  A 16-key tile is 16 code rows of c^I/2 bytes, and
+// lane l's operand for 128-dim step j is the 16 bytes of row l%16 at
+// 16*(4j + l/16): at c^I = 128 one 16-byte load per lane reads the whole
+// 1 KB tile.  Its scale byte (row l%16, block 4j + l/16) comes from one
+// 4-byte load of the row's scales.  Tiles are small (1 KB at c^I = 128), so
+// three in flight per wave, at 768 workgroups, is the measured best: more
+// tiles a wave or more workgroups leave each wave too few tiles for its
+// start-up and its last, partly wasted group.
+template <int CI, int U>
+__global__ void __launch_bounds__(256) scores_fp4_reg_kernel(IdxArgs a) {
+  constexpr int KB = CI / 32;    // scale bytes (32-dim blocks) per row
+  constexpr int ROWB = CI / 2;   // code bytes per row
+  constexpr int NJ = CI / 128;   // 128-dim MFMA steps
+  constexpr int HT = 4;          // head tiles: up to 64 heads
+  static_assert(CI == 128 || CI == 256, "c^I");
+  __shared__ uint32_t hist[kBins];
+  const int64_t bq = blockIdx.y;
+  clear_select_state(a, bq);
+  const int64_t vmax = visible_max(a);  // rows below vmax exist whatever this query's t
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int r16 = lane & 15, g = lane >> 4;
+  const int64_t step = int64_t(gridDim.x) * 4;
+  const int64_t first = int64_t(blockIdx.x) * 4 + wave;
+  const int64_t b = bq / a.n_q;
+  const uint8_t* Kc = static_cast<const uint8_t*>(a.KI) + b * a.key_bstride * ROWB;
+  const uint8_t* Ks = a.k_scale + b * a.key_bstride * KB;
+  // codes of step j, and the 4-byte word holding the row's scales of blocks
+  // 4j .. 4j+3 (this lane's is byte g of it; Ks is 4-byte aligned)
+  auto load = [&](int64_t it, uint4 (&kc)[NJ], uint32_t (&ks)[NJ]) {
+    const int64_t row = min((first + it * step) * 16 + r16, vmax - 1);
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      kc[j] = *reinterpret_cast<const uint4*>(Kc + row * ROWB + (4 * j + g) * 16);
+      ks[j] = *reinterpret_cast<const uint32_t*>(Ks + row * KB + 4 * j);
+    }
+  };
+  uint4 kc[U][NJ];
+  uint32_t ksc[U][NJ];
+#pragma unroll
+  for (int u = 0; u < U; ++u) load(u, kc[u], ksc[u]);
+  const int64_t nvis = visible(a, bq);
+  const int64_t n_tiles = (nvis + 15) / 16;
+  if (int64_t(blockIdx.x) * 64 >= nvis) {  // no wave of this workgroup has a visible tile
+    __builtin_amdgcn_s_waitcnt(0);
+    return;
+  }
+  const int64_t my_tiles = n_tiles > first ? (n_tiles - first + step - 1) / step : 0;
+  for (int i = threadIdx.x; i < kBins; i += blockDim.x) hist[i] = 0;
+  // queries (A operand, rows = heads): head ht*16 + r16, block 4j + g; heads
+  // past n_hI take zero codes (their weight is 0 too)
+  i32x8 qa[HT][NJ];
+  int qs[HT][NJ];
+#pragma unroll
+  for (int ht = 0; ht < HT; ++ht) {
+    const int h = min(ht * 16 + r16, int(a.n_hI) - 1);
+    const bool pad = ht * 16 + r16 >= a.n_hI;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const int blk = 4 * j + g;
+      const uint4 c = *reinterpret_cast<const uint4*>(a.q_code + (bq * a.n_hI + h) * ROWB + blk * 16);
+      const int e8 = a.q_scale[(bq * a.n_hI + h) * KB + blk];
+      qa[ht][j] = pad ? i32x8{0, 0, 0, 0, 0, 0, 0, 0} : i32x8{int(c.x), int(c.y), int(c.z), int(c.w), 0, 0, 0, 0};
+      qs[ht][j] = pad ? 127 : e8;
+    }
+  }
+  float wv[HT][4];
+#pragma unroll
+  for (int ht = 0; ht < HT; ++ht)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int h = ht * 16 + g * 4 + r;
+      wv[ht][r] = h < a.n_hI ? a.wI[bq * a.n_hI + h] : 0.f;
+    }
+  wait_vm<0>();     // the query, the weights and the first tiles
+  __syncthreads();  // hist cleared
+  float* srow = a.scores + bq * a.score_ld;
+
+  // whole groups of U tiles: the tiles past my_tiles in the last group lie at
+  // or past nvis, so their stores and counts are masked off
+  for (int64_t it0 = 0; it0 < my_tiles; it0 += U) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t it = it0 + u;
+      f32x4 acc[HT];
+#pragma unroll
+      for (int ht = 0; ht < HT; ++ht) acc[ht] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        const i32x8 kb = i32x8{int(kc[u][j].x), int(kc[u][j].y), int(kc[u][j].z), int(kc[u][j].w), 0, 0, 0, 0};
+        // byte g of the scale word, taken apart only here: the empty asm keeps
+        // the compiler from doing it (and so waiting for every tile in
+        // flight) at the loop head
+        uint32_t w = ksc[u][j];
+        asm volatile("" : "+v"(w));
+        const int sc = int((w >> (8 * g)) & 0xffu);
+#pragma unroll
+        for (int ht = 0; ht < HT; ++ht)
+          acc[ht] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qa[ht][j], kb, acc[ht], 4, 4, 0, qs[ht][j], 0, sc);
+      }
+      load(it + U, kc[u], ksc[u]);
+      float ps[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        ps[r] = wv[0][r] * relu(acc[0][r]);
+#pragma unroll
+        for (int ht = 1; ht < HT; ++ht) ps[r] = fmaf(wv[ht][r], relu(acc[ht][r]), ps[r]);
+      }
+      const float part = rows4_sum((ps[0] + ps[1]) + (ps[2] + ps[3]));
+      const int64_t s = (first + it * step) * 16 + r16;
+      if (g == 0 && s < nvis) {
+        const float score = canon_zero(part);
+        srow[s] = score;
+        atomicAdd(&hist[order_key(score) >> kShift1], 1u);
+      }
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0);  // the tiles loaded past the end
+  flush_hist(hist, a.hist + bq * kBins);
+}
+
 template <typename T>
 __global__ void __launch_bounds__(256) prep_fp4_kernel(uint32_t* hist, int64_t nhist, int fill_blocks, const T* q,
                                                        int64_t qblocks, int64_t bpr, uint8_t* codes,
@@ -1575,6 +1703,13 @@ constexpr int64_t kPrefillMinQueries = DLC_PREFILL_MIN_Q;
 #ifndef DLC_FP4_NW
 #define DLC_FP4_NW 8  // waves per workgroup of the FP4 scores kernel
 #endif
+#ifndef DLC_FP4_U
+#define DLC_FP4_U 3  // key tiles in flight per wave in the FP4 register-load kernel
+#endif
+#ifndef DLC_FP4_RWGS
+#define DLC_FP4_RWGS 768  // its workgroups per call
+#endif
+constexpr int64_t kFp4RegWorkgroups = DLC_FP4_RWGS;
 // wgs: the workgroups the batch should take (kScoreWorkgroups for the FP4
 // and VALU scores kernels, kSelectDecodeWorkgroups for the decode selection,
 // kSelectWorkgroups for the query-tiled histogram and filter kernels)
@@ -1920,9 +2055,17 @@ int csa_index_topk_fp4(int dtype, int64_t B, int64_t n_q, int64_t n_hI, int64_t 
         dim3 pgrid{(unsigned)ceil_div(vis_max, 256), (unsigned)ceil_div(n_q, 64), (unsigned)B};
         hipLaunchKernelGGL((scores_prefill_fp4_kernel<128>), pgrid, dim3(512), 0, s, r);
       }
-      if (!prefill && cI == 128)
+      // the register-load kernel on its own grid, as the bf16 one
+      const int64_t G = std::max<int64_t>(1, std::min(ceil_div(kFp4RegWorkgroups, BQ), ceil_div(vis_max, 64)));
+      const dim3 sgrid{(unsigned)G, (unsigned)BQ, 1u};
+      const bool reg = aligned(r.k_scale, 4);  // else the LDS-staged kernel
+      if (!prefill && reg && cI == 128)
+        hipLaunchKernelGGL((scores_fp4_reg_kernel<128, DLC_FP4_U>), sgrid, dim3(256), 0, s, r);
+      if (!prefill && reg && cI == 256)
+        hipLaunchKernelGGL((scores_fp4_reg_kernel<256, DLC_FP4_U>), sgrid, dim3(256), 0, s, r);
+      if (!prefill && !reg && cI == 128)
         hipLaunchKernelGGL((scores_fp4_kernel<128, DLC_FP4_NS, DLC_FP4_NW>), grid, dim3(64 * DLC_FP4_NW), 0, s, r);
-      if (!prefill && cI == 256)
+      if (!prefill && !reg && cI == 256)
         hipLaunchKernelGGL((scores_fp4_kernel<256, DLC_FP4_NS, DLC_FP4_NW>), grid, dim3(64 * DLC_FP4_NW), 0, s, r);
       }
       if ((rc2 = check_launch("csa_index_topk_fp4/scores"))) return rc2;
