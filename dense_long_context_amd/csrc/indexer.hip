@@ -169,11 +169,7 @@ __global__ void __launch_bounds__(256) scores_valu_kernel(IdxArgs a) {
 // 8*(l/16) .. +7 of each 32-dim step; the result holds key l%16 and heads
 // 4*(l/16) .. +3, and the head sum is finished with two cross-lane adds.
 // Queries stay in registers for the whole pass.
-// The FP4 kernel below collects the scores of kScoreBuf tiles in LDS and
-// stores them together, since its key tiles arrive by direct-to-LDS loads
-// whose waits would otherwise also cover each score store.
 
-constexpr int kScoreBuf = 32;  // tiles whose scores a wave collects before storing them
 #ifndef DLC_SCORES_U
 #define DLC_SCORES_U 3  // key tiles in flight per wave in the register-load scores kernel
 #endif
@@ -321,195 +317,14 @@ scores_reg_kernel(IdxArgs a) {
 // += Q[16 heads][128 dims] x K^T[128 dims][16 keys], each operand carrying one
 // E8M0 scale per 32 dims, so every product is exact and only the fp32 sums
 // round.  Lane l supplies head/key l%16 and the 32-dim block l/16 of each
-// 128-dim step: 16 code bytes and one scale byte.  Two kernels: the
-// register-load one below (scores_fp4_reg_kernel) runs whenever the scale
-// array is 4-byte aligned; this one, which stages tiles through LDS, takes
-// the rest.  Here a 16-key tile (16 code rows of c^I/2 bytes, then their 16
-// scale rows of c^I/32 bytes) arrives by direct global->LDS loads into the
-// wave's own ring of NS stages, NS-1 tiles in flight, no barrier.  Within a
-// code row, 16-byte chunk c sits at slot c ^ ((row / RPB) % CPR) (RPB rows
-// per 256 bytes, CPR chunks per row), so the 16 rows of one ds_read_b128
-// pass fall on distinct banks.  The queries arrive quantized
-// (mxfp4_quantize, run on them just before).  Result layout, head sum and
-// the buffered score stores as in the bf16 kernel.
+// 128-dim step: 16 code bytes and one scale byte.  The queries arrive
+// quantized (prep_fp4_kernel, run on them just before).  Result layout and
+// head sum as in the bf16 kernel.
 
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 
-template <int CI, int NS, int NW>
-__global__ void __launch_bounds__(64 * NW) scores_fp4_kernel(IdxArgs a) {
-  constexpr int KB = CI / 32;               // scale bytes (32-dim blocks) per row
-  constexpr int ROWB = CI / 2;              // code bytes per row
-  constexpr int CPR = ROWB / 16;            // 16-byte chunks per code row
-  constexpr int RPB = 256 / ROWB;           // code rows per 256 bytes (the bank width)
-  constexpr int NJ = CI / 128;              // 128-dim MFMA steps = 1 KB code loads per tile
-  constexpr int CODEB = 16 * ROWB;          // code bytes of a tile
-  constexpr int STB = CODEB + 16 * KB;      // stage: codes, then scales
-  constexpr int SLANES = 16 * KB / 4;       // lanes of the scale load (4 bytes each)
-  constexpr int HT = 4;                     // head tiles: up to 64 heads
-  static_assert(CI == 128 || CI == 256, "c^I");
-  __shared__ uint32_t hist[kBins];
-  __shared__ __attribute__((aligned(16))) unsigned char sK[NW][NS][STB];
-  __shared__ float sS[NW][kScoreBuf * 16];
-  const int64_t bq = blockIdx.y;
-  clear_select_state(a, bq);
-  const int64_t s0 = int64_t(blockIdx.x) * a.keys_per_wg;
-  // rows below s1l exist whatever this query's t (as in the bf16 kernel):
-  // the first tiles go out before t has been read
-  const int64_t s1l = min(visible_max(a), s0 + a.keys_per_wg);
-
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int r16 = lane & 15, g = lane >> 4;
-  const int64_t b = bq / a.n_q;
-  const uint8_t* Kc = static_cast<const uint8_t*>(a.KI) + b * a.key_bstride * ROWB;
-  const uint8_t* Ks = a.k_scale + b * a.key_bstride * KB;
-  auto tiles_of_wave = [&](int64_t end) {
-    const int64_t nt = (end - s0 + 15) / 16;
-    return nt > wave ? (nt - wave + NW - 1) / NW : int64_t(0);
-  };
-  // tile it of this wave: rows row0 .. row0+15 (rows past s1l repeat row s1l - 1)
-  auto issue = [&](int64_t it, int st) {
-    const int64_t row0 = s0 + (wave + NW * it) * 16;  // < s1l
-    const uint32_t lds = (uint32_t)(uintptr_t)DLC_LDS(&sK[wave][st][0]);
-#pragma unroll
-    for (int q = 0; q < NJ; ++q) {
-      const int pos = q * 1024 + 16 * lane;
-      const int rho = pos / ROWB, slot = (pos % ROWB) / 16;
-      const int chunk = slot ^ ((rho / RPB) % CPR);
-      const int64_t row = min(row0 + rho, s1l - 1);
-      dma_row(Kc + row0 * ROWB, uint32_t((row - row0) * ROWB + chunk * 16), lds + uint32_t(q * 1024));
-    }
-    if (lane < SLANES) {
-      const int rho = 4 * lane / KB;
-      const int64_t row = min(row0 + rho, s1l - 1);
-      dma_dword(Ks + row0 * KB, uint32_t((row - row0) * KB + (4 * lane) % KB), lds + uint32_t(CODEB));
-    }
-  };
-  {
-    const int64_t first = tiles_of_wave(s1l);
-#pragma unroll
-    for (int p = 0; p < NS - 1; ++p)
-      if (p < first) issue(p, p);
-  }
-  const int64_t nvis = visible(a, bq);
-  if (s0 >= nvis) {  // nothing of this chunk is visible to the query (the whole workgroup)
-    wait_vm<0>();
-    return;
-  }
-  const int64_t s1 = min(nvis, s0 + a.keys_per_wg);  // this query's end of the chunk
-  const int64_t my_tiles = tiles_of_wave(s1);         // <= the tiles issued by s1l
-  for (int i = threadIdx.x; i < kBins; i += blockDim.x) hist[i] = 0;
-
-  // queries (A operand, rows = heads): head ht*16 + r16, block 4j + g; heads
-  // past n_hI take zero codes (their weight is 0 too)
-  i32x8 qa[HT][NJ];
-  int qs[HT][NJ];
-#pragma unroll
-  for (int ht = 0; ht < HT; ++ht) {
-    const int h = ht * 16 + r16;
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-      const int blk = 4 * j + g;
-      uint4 c = make_uint4(0, 0, 0, 0);
-      int e8 = 127;
-      if (h < a.n_hI) {
-        c = *reinterpret_cast<const uint4*>(a.q_code + (bq * a.n_hI + h) * ROWB + blk * 16);
-        e8 = a.q_scale[(bq * a.n_hI + h) * KB + blk];
-      }
-      qa[ht][j] = i32x8{int(c.x), int(c.y), int(c.z), int(c.w), 0, 0, 0, 0};
-      qs[ht][j] = e8;
-    }
-  }
-  float wv[HT][4];
-#pragma unroll
-  for (int ht = 0; ht < HT; ++ht)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int h = ht * 16 + g * 4 + r;
-      wv[ht][r] = h < a.n_hI ? a.wI[bq * a.n_hI + h] : 0.f;
-    }
-  // wait for the query and weight loads (and with them the first tiles) here:
-  // a wait for them inside the loop would drain the tile loads in flight
-#pragma unroll
-  for (int ht = 0; ht < HT; ++ht) {
-#pragma unroll
-    for (int r = 0; r < 4; ++r) asm volatile("" ::"v"(wv[ht][r]));
-#pragma unroll
-    for (int j = 0; j < NJ; ++j)
-      asm volatile("" ::"v"(qa[ht][j][0]), "v"(qa[ht][j][1]), "v"(qa[ht][j][2]), "v"(qa[ht][j][3]), "v"(qs[ht][j]));
-  }
-  __syncthreads();  // hist cleared
-
-  constexpr int LPT = NJ + 1;  // loads per tile and lane (the scale load counts for every lane)
-  for (int64_t it = 0; it < my_tiles; ++it) {
-    const int st = int(it % NS);
-    const int64_t nxt = it + NS - 1;
-    int after;  // tiles issued after tile it
-    if (nxt < my_tiles) {
-      issue(nxt, int(nxt % NS));
-      after = NS - 1;
-    } else {
-      after = int(my_tiles - 1 - it);
-    }
-    if (after >= NS - 1) wait_vm<(NS - 1) * LPT>();
-    else if (after == 2) wait_vm<2 * LPT>();
-    else if (after == 1) wait_vm<LPT>();
-    else wait_vm<0>();
-    asm volatile("" ::: "memory");
-    const unsigned char* tile = &sK[wave][st][0];
-    f32x4 acc[HT];
-#pragma unroll
-    for (int ht = 0; ht < HT; ++ht) acc[ht] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-      const int blk = 4 * j + g;
-      const int slot = blk ^ ((r16 / RPB) % CPR);
-      const uint4 k4 = *reinterpret_cast<const uint4*>(tile + r16 * ROWB + slot * 16);
-      const int ksc = tile[CODEB + r16 * KB + blk];
-      const i32x8 kb = i32x8{int(k4.x), int(k4.y), int(k4.z), int(k4.w), 0, 0, 0, 0};
-#pragma unroll
-      for (int ht = 0; ht < HT; ++ht)
-        acc[ht] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qa[ht][j], kb, acc[ht], 4, 4, 0, qs[ht][j], 0,
-                                                                   ksc);
-    }
-    // four independent partial sums (one per head row of the lane), then a tree
-    float ps[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      ps[r] = wv[0][r] * relu(acc[0][r]);
-#pragma unroll
-      for (int ht = 1; ht < HT; ++ht) ps[r] = fmaf(wv[ht][r], relu(acc[ht][r]), ps[r]);
-    }
-    const float part = rows4_sum((ps[0] + ps[1]) + (ps[2] + ps[3]));
-    const int64_t s = s0 + (wave + NW * it) * 16 + r16;
-    const int slot = int(it % kScoreBuf);
-    if (g == 0) {
-      const float score = canon_zero(part);
-      sS[wave][slot * 16 + r16] = score;
-      if (s < s1) atomicAdd(&hist[order_key(score) >> kShift1], 1u);
-    }
-    if (slot == kScoreBuf - 1 || it + 1 == my_tiles) {
-      asm volatile("" ::: "memory");
-      const int64_t t0 = it - slot;
-#pragma unroll
-      for (int q = 0; q < kScoreBuf / 4; ++q) {
-        const int idx = q * 64 + lane, tl = idx >> 4;
-        const int64_t sk = s0 + (wave + NW * (t0 + tl)) * 16 + (idx & 15);
-        if (tl <= slot && sk < s1) a.scores[bq * a.score_ld + sk] = sS[wave][idx];
-      }
-      asm volatile("" ::: "memory");
-    }
-  }
-  wait_vm<0>();  // tiles issued by s1l that no iteration waited for
-  flush_hist(hist, a.hist + bq * kBins);
-}
-
-// The FP4 call's preparation in one launch: blocks below fill_blocks clear
-// the histograms; the others quantize the queries, one 32-element block per
-// thread, with the encoding of mxfp4_quantize (codes [rows][c^I/2], scales
-// [rows][c^I/32]).
-// The same MXFP4 product with the key operands loaded straight into
-// registers, in the bf16 register kernel's scheme (tiles interleaved over
+// The decode kernel loads the key operands straight into registers, in the
+// bf16 register kernel's scheme (tiles interleaved over
 // the G workgroups of a query, U tiles in flight per wave, every load
 // unconditional with rows clamped to the last row the batch may see, whole
 // groups of U tiles).  A 16-key tile is 16 code rows of c^I/2 bytes, and
@@ -1670,13 +1485,12 @@ struct WsLayout {
   size_t scores, hist, ccnt, sel, cand, cand_kseg, cand_srk, cand_idx, cand_key, cand_srk2, chosen, total;
 };
 
-// keys per workgroup of the FP4 (and VALU) scores kernels: a multiple of 64
-// chosen so that the whole batch takes about kScoreWorkgroups workgroups - the
-// number that are resident at once (2 per CU for the FP4 scores kernel, whose
-// key stages take 64 KB of LDS), so there is no partial second round - and at
-// most kMaxChunks chunks per query.  The bf16 scores kernel sizes its own grid
-// (kScoreRegWorkgroups, its tiles interleaved over the workgroups of a query),
-// and the selection its own chunks (kSelectDecodeWorkgroups).
+// keys per workgroup of the VALU scores kernel: a multiple of 64 chosen so
+// that the whole batch takes about kScoreWorkgroups workgroups, and at most
+// kMaxChunks chunks per query.  The MFMA scores kernels size their own grids
+// (kScoreRegWorkgroups, kFp4RegWorkgroups: tiles interleaved over the
+// workgroups of a query), and the selection its own chunks
+// (kSelectDecodeWorkgroups).
 #ifndef DLC_SCORES_WGS
 #define DLC_SCORES_WGS 512
 #endif
@@ -1697,12 +1511,6 @@ constexpr int64_t kSelectDecodeWorkgroups = DLC_SELECT_WGS;
 #define DLC_PREFILL_MIN_Q 64
 #endif
 constexpr int64_t kPrefillMinQueries = DLC_PREFILL_MIN_Q;
-#ifndef DLC_FP4_NS
-#define DLC_FP4_NS 4  // LDS stages per wave in the FP4 scores kernel (NS-1 tiles in flight)
-#endif
-#ifndef DLC_FP4_NW
-#define DLC_FP4_NW 8  // waves per workgroup of the FP4 scores kernel
-#endif
 #ifndef DLC_FP4_U
 #define DLC_FP4_U 3  // key tiles in flight per wave in the FP4 register-load kernel
 #endif
@@ -1710,8 +1518,8 @@ constexpr int64_t kPrefillMinQueries = DLC_PREFILL_MIN_Q;
 #define DLC_FP4_RWGS 768  // its workgroups per call
 #endif
 constexpr int64_t kFp4RegWorkgroups = DLC_FP4_RWGS;
-// wgs: the workgroups the batch should take (kScoreWorkgroups for the FP4
-// and VALU scores kernels, kSelectDecodeWorkgroups for the decode selection,
+// wgs: the workgroups the batch should take (kScoreWorkgroups for the VALU
+// scores kernel, kSelectDecodeWorkgroups for the decode selection,
 // kSelectWorkgroups for the query-tiled histogram and filter kernels)
 int64_t keys_per_wg(int64_t BQ, int64_t vis_max, int64_t wgs = kScoreWorkgroups) {
   const int64_t vis = vis_max > 0 ? vis_max : 1;
@@ -2010,8 +1818,8 @@ int csa_index_topk_fp4(int dtype, int64_t B, int64_t n_q, int64_t n_hI, int64_t 
   DLC_REQUIRE(cap < (int64_t(1) << 31), DLC_E_UNSUPPORTED, "csa_index_topk_fp4: cap must be < 2^31");
   DLC_REQUIRE(qI && wI && t && idx && count && ((KIc && KIs) || cap == 0), DLC_E_INVAL,
               "csa_index_topk_fp4: NULL argument");
-  DLC_REQUIRE(aligned(qI, 16) && (cap == 0 || aligned(KIc, 16)), DLC_E_INVAL,
-              "csa_index_topk_fp4: qI and KIc must be 16-byte aligned");
+  DLC_REQUIRE(aligned(qI, 16) && (cap == 0 || (aligned(KIc, 16) && aligned(KIs, 4))), DLC_E_INVAL,
+              "csa_index_topk_fp4: qI and KIc must be 16-byte aligned, KIs 4-byte aligned");
   const CallWs CW = call_ws(B, n_q, cap, k, true);
   const Fp4Ws W = fp4_query_off(B, n_q, cap, k, n_hI, cI);
   DLC_REQUIRE(ws != nullptr && ws_bytes >= W.total, DLC_E_WORKSPACE,
@@ -2058,15 +1866,10 @@ int csa_index_topk_fp4(int dtype, int64_t B, int64_t n_q, int64_t n_hI, int64_t 
       // the register-load kernel on its own grid, as the bf16 one
       const int64_t G = std::max<int64_t>(1, std::min(ceil_div(kFp4RegWorkgroups, BQ), ceil_div(vis_max, 64)));
       const dim3 sgrid{(unsigned)G, (unsigned)BQ, 1u};
-      const bool reg = aligned(r.k_scale, 4);  // else the LDS-staged kernel
-      if (!prefill && reg && cI == 128)
+      if (!prefill && cI == 128)
         hipLaunchKernelGGL((scores_fp4_reg_kernel<128, DLC_FP4_U>), sgrid, dim3(256), 0, s, r);
-      if (!prefill && reg && cI == 256)
+      if (!prefill && cI == 256)
         hipLaunchKernelGGL((scores_fp4_reg_kernel<256, DLC_FP4_U>), sgrid, dim3(256), 0, s, r);
-      if (!prefill && !reg && cI == 128)
-        hipLaunchKernelGGL((scores_fp4_kernel<128, DLC_FP4_NS, DLC_FP4_NW>), grid, dim3(64 * DLC_FP4_NW), 0, s, r);
-      if (!prefill && !reg && cI == 256)
-        hipLaunchKernelGGL((scores_fp4_kernel<256, DLC_FP4_NS, DLC_FP4_NW>), grid, dim3(64 * DLC_FP4_NW), 0, s, r);
       }
       if ((rc2 = check_launch("csa_index_topk_fp4/scores"))) return rc2;
       if (prefill) {

@@ -208,13 +208,13 @@ int csa_index_topk(int dtype, int64_t B, int64_t n_q, int64_t n_hI, int64_t cI, 
  *  qI      [B][n_q][n_hI][cI] in dtype (DLC_F32 or DLC_BF16), quantized per
  *          head row inside the call (the same rule); 16-byte aligned
  *  KIc     [B][cap][cI/2] key code bytes (mxfp4_quantize of the K^I cache)
- *  KIs     [B][cap][cI/32] key scale bytes
+ *  KIs     [B][cap][cI/32] key scale bytes; 4-byte aligned
  *  ws      workspace of at least csa_index_topk_fp4_ws(B, n_q, n_hI, cI,
  *          cap, k) bytes, 256-byte aligned (it also holds the quantized
  *          queries); its contents on entry do not matter
  *  other arguments, outputs and ranking as for csa_index_topk.
  * Limits: cI in {128, 256}, n_hI <= 64, 1 <= k <= 8192; KIc 16-byte
- * aligned.
+ * aligned, KIs 4-byte aligned (DLC_E_INVAL otherwise).
  */
 int mxfp4_quantize(int dtype, int64_t B, int64_t rows, int64_t width, const void* src, int64_t src_bstride,
                    uint8_t* codes, int64_t codes_bstride, uint8_t* scales, int64_t scales_bstride, void* stream);

@@ -123,6 +123,7 @@ def _topk_fp4(L, **kw):
     (dict(t_max=68), E_SHAPE),          # floor(68/4) = 17 > cap
     (dict(KIs=None), E_INVAL),
     (dict(qI=P + 4), E_INVAL),          # misaligned query
+    (dict(KIs=P + 2), E_INVAL),         # misaligned key scales
     (dict(ws_bytes=16), E_WORKSPACE),
 ])
 def test_index_topk_fp4_validation(L, kw, status):
