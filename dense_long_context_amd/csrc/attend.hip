@@ -1320,8 +1320,18 @@ int run_attend(const char* name, int dtype, AttArgs a, int64_t BQ, int64_t nkeys
       hipLaunchKernelGGL((combine_frag_kernel<1024, 4>), dim3(nb, 1u, 1u), dim3(1024), 0, s, a.ob, a.lse, p.splits,
                          a.n_h, 1, out, lse, o_in, lse_in);
     else
-      hipLaunchKernelGGL((combine_frag_kernel<256, 16>), dim3(nb, 16u, 1u), dim3(256), 0, s, a.ob, a.lse, p.splits,
-                         a.n_h, 4, out, lse, o_in, lse_in);
+      // each of the four waves of a store loads its share of the splits at once:
+      // as many loads in flight as it has splits, up to 16 (fewer registers
+      // for short split lists, so more blocks resident)
+      if (p.splits <= 16)
+        hipLaunchKernelGGL((combine_frag_kernel<256, 4>), dim3(nb, 16u, 1u), dim3(256), 0, s, a.ob, a.lse, p.splits,
+                           a.n_h, 4, out, lse, o_in, lse_in);
+      else if (p.splits <= 32)
+        hipLaunchKernelGGL((combine_frag_kernel<256, 8>), dim3(nb, 16u, 1u), dim3(256), 0, s, a.ob, a.lse, p.splits,
+                           a.n_h, 4, out, lse, o_in, lse_in);
+      else
+        hipLaunchKernelGGL((combine_frag_kernel<256, 16>), dim3(nb, 16u, 1u), dim3(256), 0, s, a.ob, a.lse, p.splits,
+                           a.n_h, 4, out, lse, o_in, lse_in);
   } else {
     hipLaunchKernelGGL(combine_kernel, dim3((unsigned)(BQ * a.n_h)), dim3(128), 0, s, a.o, a.lse, p.splits, a.n_h,
                        a.c, out, lse, o_in, lse_in);
