@@ -880,7 +880,8 @@ def main():
 
     # read-only reference: dlc_read in the scores kernel's own load form over
     # the same number of bytes, three rotating buffers (past the last-level
-    # cache), one HIP event pair per launch as for the scores kernel
+    # cache), one HIP event pair per launch bound to the kernel's dispatch, as
+    # for the scores kernel
     nb = (int(idx_bytes) + 4095) // 4096 * 4096
     rbufs = [torch.empty(nb, dtype=torch.uint8, device=dev) for _ in range(3)]
     for i in range(3):
@@ -888,12 +889,13 @@ def main():
     torch.cuda.synchronize()
     read_ms = []
     for i in range(30):
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
+        e0, e1 = ev.create(), ev.create()
+        binding.dlc_timing_arm(binding.STAGE_READ, e0, e1)
         binding.dlc_read(rbufs[i % 3], binding.READ_TILES)
-        e1.record()
         torch.cuda.synchronize()
-        read_ms.append(e0.elapsed_time(e1))
+        read_ms.append(ev.elapsed_ms(e0, e1))
+        ev.destroy(e0)
+        ev.destroy(e1)
     read_avg_ms = sum(read_ms) / len(read_ms)
     read_gbs = nb / (read_avg_ms * 1e-3) / 1e9
     del rbufs

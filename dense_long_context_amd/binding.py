@@ -70,6 +70,7 @@ SIGNATURES = {
 
 STAGE_INDEX_SCORES, STAGE_TOPK_SELECT, STAGE_CSA_ATTEND, STAGE_HCA_ATTEND, STAGE_COMPRESS = 1, 2, 3, 4, 5
 STAGE_WINDOW_ATTEND = 6
+STAGE_READ = 7
 
 
 class DlcError(RuntimeError):

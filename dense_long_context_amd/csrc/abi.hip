@@ -29,7 +29,7 @@ __global__ void fill_u32_kernel(uint32_t* p, uint32_t v, int64_t n) {
   for (; i < n; i += stride) p[i] = v;
 }
 
-constexpr int kStages = 7;
+constexpr int kStages = 8;
 static thread_local hipEvent_t g_armed[kStages][2] = {};
 static thread_local int g_depth[kStages] = {};
 
@@ -43,6 +43,15 @@ StageTimer::~StageTimer() {
   if (--g_depth[stage_] > 0) return;
   if (g_armed[stage_][1]) (void)hipEventRecord(g_armed[stage_][1], s_);
   g_armed[stage_][0] = g_armed[stage_][1] = nullptr;
+}
+
+bool take_stage_events(int stage, hipEvent_t* begin, hipEvent_t* end) {
+  *begin = *end = nullptr;
+  if (g_depth[stage] > 0 || !g_armed[stage][0] || !g_armed[stage][1]) return false;
+  *begin = g_armed[stage][0];
+  *end = g_armed[stage][1];
+  g_armed[stage][0] = g_armed[stage][1] = nullptr;
+  return true;
 }
 
 // Bandwidth reference: each block moves 32 KB per round (eight 16-byte
@@ -166,14 +175,16 @@ int dlc_read(const void* src, size_t bytes, int form, void* stream) {
               "dlc_read: size must be a multiple of %zu and the pointer 16-byte aligned", unit);
   const int64_t n = int64_t(bytes / unit);
   if (n == 0) return DLC_OK;
+  hipEvent_t evb, eve;
+  take_stage_events(DLC_STAGE_READ, &evb, &eve);
   if (form == DLC_READ_LDS) {
     const int64_t blocks = std::min<int64_t>(ceil_div(n, 4 * 32), 2048);
-    hipLaunchKernelGGL(read_lds_kernel, dim3((unsigned)blocks), dim3(256), 0, as_stream(stream),
-                       static_cast<const unsigned char*>(src), n);
+    hipExtLaunchKernelGGL(read_lds_kernel, dim3((unsigned)blocks), dim3(256), 0, as_stream(stream), evb, eve, 0u,
+                          static_cast<const unsigned char*>(src), n);
   } else {
     const int64_t blocks = std::min<int64_t>(ceil_div(n, 4), 768);
-    hipLaunchKernelGGL(read_tiles_kernel, dim3((unsigned)blocks), dim3(256), 0, as_stream(stream),
-                       static_cast<const unsigned char*>(src), n);
+    hipExtLaunchKernelGGL(read_tiles_kernel, dim3((unsigned)blocks), dim3(256), 0, as_stream(stream), evb, eve, 0u,
+                          static_cast<const unsigned char*>(src), n);
   }
   return check_launch("dlc_read");
 }

@@ -1,6 +1,7 @@
 // Shared device helpers and host-side validation for the gfx950 kernels.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <stddef.h>
@@ -175,6 +176,14 @@ class StageTimer {
   int stage_;
   hipStream_t s_;
 };
+
+// For a stage that is a single kernel launch: hands over the armed events of
+// `stage` (and disarms it) so that the caller binds them to that kernel's own
+// dispatch (hipExtLaunchKernelGGL).  They then time the kernel alone, where
+// events recorded around the launch also take in its dispatch latency.
+// Returns false, events null, when the stage is not armed or one of its
+// timers is open.
+bool take_stage_events(int stage, hipEvent_t* begin, hipEvent_t* end);
 
 // fill kernel: clears workspace on the stream (no memset nodes, so the calls
 // stay safe to capture in a graph)

@@ -1762,6 +1762,9 @@ int csa_index_topk(int dtype, int64_t B, int64_t n_q, int64_t n_hI, int64_t cI, 
       const int64_t nchunks = ceil_div(vis_max, r.keys_per_wg);
       dim3 grid{(unsigned)nchunks, (unsigned)BQ, 1u};
       {
+      // the decode scores kernel is one launch: the armed events go on its dispatch
+      hipEvent_t evb = nullptr, eve = nullptr;
+      if (!prefill && mfma) take_stage_events(DLC_STAGE_INDEX_SCORES, &evb, &eve);
       StageTimer timer(DLC_STAGE_INDEX_SCORES, s);
       if (prefill) {
         dim3 pgrid{(unsigned)ceil_div(vis_max, 256), (unsigned)ceil_div(n_q, 64), (unsigned)B};
@@ -1774,7 +1777,8 @@ int csa_index_topk(int dtype, int64_t B, int64_t n_q, int64_t n_hI, int64_t cI, 
         const dim3 sgrid{(unsigned)G, (unsigned)BQ, 1u};
 #define DLC_SCORES(ht, kt) \
   if (HT == ht && KT == kt)                                                                              \
-    hipLaunchKernelGGL((scores_reg_kernel<ht, kt, kt >= 8 ? 2 : DLC_SCORES_U>), sgrid, dim3(256), 0, s, rs);
+    hipExtLaunchKernelGGL((scores_reg_kernel<ht, kt, kt >= 8 ? 2 : DLC_SCORES_U>), sgrid, dim3(256), 0, s, evb, \
+                          eve, 0u, rs);
         DLC_SCORES(1, 1) DLC_SCORES(1, 2) DLC_SCORES(1, 4) DLC_SCORES(1, 8)
         DLC_SCORES(2, 1) DLC_SCORES(2, 2) DLC_SCORES(2, 4) DLC_SCORES(2, 8)
         DLC_SCORES(3, 1) DLC_SCORES(3, 2) DLC_SCORES(3, 4) DLC_SCORES(3, 8)
@@ -1858,6 +1862,8 @@ int csa_index_topk_fp4(int dtype, int64_t B, int64_t n_q, int64_t n_hI, int64_t 
       r.keys_per_wg = keys_per_wg(BQ, vis_max, prefill ? kSelectWorkgroups : kScoreWorkgroups);
       dim3 grid{(unsigned)ceil_div(vis_max, r.keys_per_wg), (unsigned)BQ, 1u};
       {
+      hipEvent_t evb = nullptr, eve = nullptr;
+      if (!prefill && (cI == 128 || cI == 256)) take_stage_events(DLC_STAGE_INDEX_SCORES, &evb, &eve);
       StageTimer timer(DLC_STAGE_INDEX_SCORES, s);
       if (prefill) {
         dim3 pgrid{(unsigned)ceil_div(vis_max, 256), (unsigned)ceil_div(n_q, 64), (unsigned)B};
@@ -1867,9 +1873,9 @@ int csa_index_topk_fp4(int dtype, int64_t B, int64_t n_q, int64_t n_hI, int64_t 
       const int64_t G = std::max<int64_t>(1, std::min(ceil_div(kFp4RegWorkgroups, BQ), ceil_div(vis_max, 64)));
       const dim3 sgrid{(unsigned)G, (unsigned)BQ, 1u};
       if (!prefill && cI == 128)
-        hipLaunchKernelGGL((scores_fp4_reg_kernel<128, DLC_FP4_U>), sgrid, dim3(256), 0, s, r);
+        hipExtLaunchKernelGGL((scores_fp4_reg_kernel<128, DLC_FP4_U>), sgrid, dim3(256), 0, s, evb, eve, 0u, r);
       if (!prefill && cI == 256)
-        hipLaunchKernelGGL((scores_fp4_reg_kernel<256, DLC_FP4_U>), sgrid, dim3(256), 0, s, r);
+        hipExtLaunchKernelGGL((scores_fp4_reg_kernel<256, DLC_FP4_U>), sgrid, dim3(256), 0, s, evb, eve, 0u, r);
       }
       if ((rc2 = check_launch("csa_index_topk_fp4/scores"))) return rc2;
       if (prefill) {

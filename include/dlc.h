@@ -361,16 +361,22 @@ int dlc_project(int dtype, int64_t M, int64_t N, int64_t K, const void* A, int64
  *
  * dlc_timing_arm - the next launch of `stage` on the calling thread records
  * the caller's HIP events `ev_begin` (before) and `ev_end` (after) on that
- * launch's stream, then disarms.  The events are hipEvent_t handles owned by
- * the caller; NULL events disarm the stage.  Stages:
- *   DLC_STAGE_INDEX_SCORES  the indexer score kernel of csa_index_topk (or _fp4); for a
- *                           query-tiled call (n_q >= 64), which runs the cache range by
- *                           range, the whole indexer: every range's scores, selection and merge
+ * launch's stream, then disarms.  Where the stage is one kernel (marked
+ * [kernel] below) the events are bound to that kernel's own dispatch
+ * (hipExtLaunchKernel) and time the kernel alone; elsewhere they are
+ * recorded around the stage's launches and also take in their dispatch
+ * latency.  The events are hipEvent_t handles owned by the caller; NULL
+ * events disarm the stage.  Stages:
+ *   DLC_STAGE_INDEX_SCORES  the indexer score kernel of csa_index_topk (or _fp4) [kernel];
+ *                           for a query-tiled call (n_q >= 64), which runs the cache range
+ *                           by range, the whole indexer: every range's scores, selection
+ *                           and merge
  *   DLC_STAGE_TOPK_SELECT   the selection kernel of csa_index_topk (or _fp4)
  *   DLC_STAGE_CSA_ATTEND    csa_attend (attention and combine kernels)
  *   DLC_STAGE_HCA_ATTEND    hca_attend (attention and combine kernels)
  *   DLC_STAGE_COMPRESS      csa_compress / hca_compress and the fused calls
  *   DLC_STAGE_WINDOW_ATTEND window_attend (attention and merge kernels)
+ *   DLC_STAGE_READ          the kernel of dlc_read [kernel]
  *
  * dlc_copy - device-to-device copy kernel of `bytes` bytes (a multiple of
  * 16, both pointers 16-byte aligned); the reference for achievable HBM
@@ -382,7 +388,8 @@ enum {
   DLC_STAGE_CSA_ATTEND = 3,
   DLC_STAGE_HCA_ATTEND = 4,
   DLC_STAGE_COMPRESS = 5,
-  DLC_STAGE_WINDOW_ATTEND = 6
+  DLC_STAGE_WINDOW_ATTEND = 6,
+  DLC_STAGE_READ = 7
 };
 int dlc_timing_arm(int stage, void* ev_begin, void* ev_end);
 int dlc_copy(void* dst, const void* src, size_t bytes, void* stream);

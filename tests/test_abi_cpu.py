@@ -270,6 +270,13 @@ def test_bandwidth_references_validation(L):
     assert L.dlc_read(P, 0, 1, None) == OK
 
 
+def test_timing_arm_stages(L):
+    for stage in range(1, 8):  # DLC_STAGE_INDEX_SCORES .. DLC_STAGE_READ
+        assert L.dlc_timing_arm(stage, None, None) == OK  # NULL events: disarmed
+    assert L.dlc_timing_arm(0, None, None) == E_INVAL
+    assert L.dlc_timing_arm(8, None, None) == E_INVAL
+
+
 def test_project_validation(L):
     assert L.dlc_project(BF16, 4, 4, 0, P, 8, P, 8, P, 4, BF16, None) == E_INVAL
     assert L.dlc_project(BF16, 4, 4, 8, P, 4, P, 8, P, 4, BF16, None) == E_SHAPE
