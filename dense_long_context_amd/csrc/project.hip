@@ -4,8 +4,10 @@
 // and the other stream projections), §6.1-6.3 and §8 (c^Q, q^I, w^I, q).
 //
 // bf16 path: one 128x128 output tile per workgroup, the tile product of
-// gemm128.hpp (v_mfma_f32_32x32x16_bf16, fp32 accumulation).  Other dtypes and
-// shapes use a VALU kernel.
+// gemm128.hpp (v_mfma_f32_32x32x16_bf16, fp32 accumulation).  At M <= 16 rows
+// (a decode step's tokens) the weights dominate the traffic and a 128-row
+// tile would leave most of the chip idle, so project_rows_kernel streams the
+// weight rows instead.  Other dtypes and shapes use a VALU kernel.
 #include "gemm128.hpp"
 
 namespace dlc {
@@ -77,6 +79,89 @@ __global__ void __launch_bounds__(256) project_mfma_kernel(ProjArgs a) {
     }
 }
 
+// Row-vector path (M <= 16): a wave computes D[16 n][16 m] = Wt[n0 .. n0+15][K]
+// . A[M rows][K]^T with v_mfma_f32_16x16x32_bf16, the weight rows as the A
+// operand.  In each 32-deep step s, lane l loads 16 bytes of weight row
+// n0 + l%16 and of activation row l%16 (zero from row M on) at k = 32s +
+// 8(l/16): one load instruction reads 64 contiguous bytes of 16 weight rows.
+// The KW waves that share a 16-column tile take its steps interleaved (wave
+// w of the tile: steps w, w + KW, ...), U steps in flight; their partial sums
+// meet in LDS and are added in wave order, so the bits do not depend on
+// timing.  Steps past K are loaded from a clamped address and masked.
+constexpr int kRowsWaves = 16, kRowsMaxM = 16;
+
+template <int KW>
+__global__ void __launch_bounds__(64 * kRowsWaves) __attribute__((amdgpu_waves_per_eu(1, 4))) project_rows_kernel(ProjArgs a) {
+  constexpr int TPW = kRowsWaves / KW, U = 8;  // column tiles per workgroup; steps in flight
+  __shared__ f32x4 red[KW > 1 ? 64 * kRowsWaves : 1];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int i16 = lane & 15, g = lane >> 4;
+  const int kw = wave % KW;
+  const int64_t n0 = (int64_t(blockIdx.x) * TPW + wave / KW) * 16;
+  const int64_t K = a.K, KS = ceil_div(K, 32);
+  const bf16_raw* wp = static_cast<const bf16_raw*>(a.W) + std::min<int64_t>(n0 + i16, a.N - 1) * a.ldw;
+  const bf16_raw* ap = static_cast<const bf16_raw*>(a.A) + std::min<int64_t>(i16, a.M - 1) * a.lda;
+  const bool mrow = i16 < a.M;
+  // the wave's steps j = 0 .. nst-1 are k-steps kw + j*KW; unit u of group i
+  // is step i*U + u, and its registers are refilled with step (i+1)*U + u as
+  // soon as its MFMA has read them.  Every load is unconditional (past the
+  // wave's steps from a clamped address, masked), so the compiler keeps all
+  // U steps in flight across iterations.
+  const int64_t nst = KS > kw ? ceil_div(KS - kw, int64_t(KW)) : 0;
+  const int64_t ng = ceil_div(nst, int64_t(U));
+  uint4 wv[U], av[U];
+  bool in[U];
+  auto load = [&](int64_t j, int u) {  // K % 8 == 0: a lane's eight elements are all in or all out
+    const int64_t k = 32 * (kw + j * KW) + 8 * g;
+    in[u] = j < nst && k < K;
+    const int64_t kc = in[u] ? k : K - 8;
+    wv[u] = *reinterpret_cast<const uint4*>(wp + kc);
+    av[u] = *reinterpret_cast<const uint4*>(ap + kc);
+  };
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  // (the empty asm statements with a memory clobber keep the compiler from
+  // merging a step's loads from both loop entries into one load at the
+  // loop head, which would leave nothing in flight across iterations)
+  if (ng > 0) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) load(u, u);
+    asm volatile("" ::: "memory");
+    for (int64_t i = 0; i < ng; ++i) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const uint4 z = make_uint4(0, 0, 0, 0);
+        const uint4 w = in[u] ? wv[u] : z;
+        const uint4 x = in[u] && mrow ? av[u] : z;
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, w), __builtin_bit_cast(bf16x8, x),
+                                                      acc, 0, 0, 0);
+        load((i + 1) * U + u, u);
+      }
+      asm volatile("" ::: "memory");
+    }
+  }
+  if constexpr (KW > 1) {
+    red[tid] = acc;
+    __syncthreads();
+    if (kw != 0) return;
+    for (int w = 1; w < KW; ++w) {
+      const f32x4 v = red[tid + 64 * w];
+      acc[0] += v[0]; acc[1] += v[1]; acc[2] += v[2]; acc[3] += v[3];
+    }
+  }
+  // D: lane l holds rows n0 + 4(l/16) + r of column m = l%16
+  if (!mrow) return;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int64_t n = n0 + 4 * g + r;
+    if (n < a.N) {
+      if (a.out_bf16)
+        static_cast<bf16_raw*>(a.out)[i16 * a.ldo + n] = f32_to_bf16(acc[r]);
+      else
+        static_cast<float*>(a.out)[i16 * a.ldo + n] = acc[r];
+    }
+  }
+}
+
 }  // namespace
 }  // namespace dlc
 
@@ -94,7 +179,23 @@ extern "C" int dlc_project(int dtype, int64_t M, int64_t N, int64_t K, const voi
   hipStream_t s = as_stream(stream);
   const bool mfma = dtype == DLC_BF16 && K % 8 == 0 && lda % 8 == 0 && ldw % 8 == 0 && aligned(A, 16) &&
                     aligned(Wt, 16);
-  if (mfma) {
+  if (mfma && M <= kRowsMaxM) {
+    // waves per column tile: doubled while the grid is under one workgroup
+    // per CU and every wave keeps two steps at least
+    const int64_t NT = ceil_div(N, 16), KS = ceil_div(K, 32);
+    int kw = 1;
+    while (kw < kRowsWaves && ceil_div(NT, kRowsWaves / kw) < 256 && KS >= 4 * kw) kw *= 2;
+    const int64_t blocks = ceil_div(NT, kRowsWaves / kw);
+    DLC_REQUIRE(blocks < (int64_t(1) << 31), DLC_E_UNSUPPORTED, "dlc_project: too many column tiles");
+    const dim3 grid{(unsigned)blocks, 1u, 1u}, block{64u * kRowsWaves, 1u, 1u};
+    switch (kw) {
+      case 1: hipLaunchKernelGGL(project_rows_kernel<1>, grid, block, 0, s, a); break;
+      case 2: hipLaunchKernelGGL(project_rows_kernel<2>, grid, block, 0, s, a); break;
+      case 4: hipLaunchKernelGGL(project_rows_kernel<4>, grid, block, 0, s, a); break;
+      case 8: hipLaunchKernelGGL(project_rows_kernel<8>, grid, block, 0, s, a); break;
+      default: hipLaunchKernelGGL(project_rows_kernel<16>, grid, block, 0, s, a); break;
+    }
+  } else if (mfma) {
     const int64_t tiles = ceil_div(M, TM) * ceil_div(N, TN);
     DLC_REQUIRE(tiles < (int64_t(1) << 31), DLC_E_UNSUPPORTED, "dlc_project: too many tiles");
     hipLaunchKernelGGL(project_mfma_kernel, dim3((unsigned)tiles), dim3(256), 0, s, a);

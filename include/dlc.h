@@ -110,7 +110,9 @@ int hca_compress(int dtype, int64_t B, int64_t n, int64_t c, int64_t m_prime,
  * HCA streams alike) and its pooling (§4-§5, §10) in one pass: the projected
  * streams are never written.  The result equals dlc_project of each stream
  * (stored in bf16) followed by csa_compress / hca_compress with the same
- * biases and entry range, bit for bit.
+ * biases and entry range, bit for bit, where n > 16 (with at most 16 rows
+ * dlc_project takes its row-vector path, which adds the same fp32 products
+ * in another order).
  *
  *  dtype          DLC_BF16 (hidden rows, weights and output)
  *  B, n, d        sequences, valid rows per sequence, hidden width (d % 8 == 0)
@@ -352,6 +354,11 @@ int attend_sink(int64_t rows, int64_t n_h, int64_t c, float* out, float* lse, co
  *  Wt   the weight matrix W [K][N] stored transposed, Wt[N][K] with row
  *       stride ldw, in dtype
  *  out  [M][N] with row stride ldo, stored in out_dtype (DLC_F32 or dtype)
+ *
+ * bf16 with K, lda, ldw multiples of 8 and A, Wt 16-byte aligned runs on
+ * MFMA: 128x128 output tiles, or at M <= 16 (a decode step's tokens) a
+ * row-vector path that streams the weight rows across the whole chip (its
+ * cost is the read of Wt).  Other cases run a VALU kernel.
  */
 int dlc_project(int dtype, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
                 const void* Wt, int64_t ldw, void* out, int64_t ldo, int out_dtype, void* stream);

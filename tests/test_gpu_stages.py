@@ -431,15 +431,23 @@ def test_hca_attend_window_long_splits():
     ("f32", 33, 70, 19, "f32"),
     ("bf16", 300, 260, 1024, "bf16"),
     ("bf16", 129, 64, 72, "f32"),
-    ("bf16", 1, 8192, 512, "bf16"),
+    ("bf16", 1, 8192, 512, "bf16"),     # row-vector path (M <= 16) from here on: one wave per column tile
+    ("bf16", 4, 1000, 520, "f32"),      # ragged column tiles, K % 32 = 8 (last step partly masked), 4 waves a tile
+    ("bf16", 3, 70, 40, "f32"),         # two steps, the second with one lane group in range
+    ("bf16", 7, 512, 7168, "bf16"),     # the query down-projection's shape, 16 waves a tile
+    ("bf16", 16, 64, 7168, "f32"),      # M = 16, four column tiles
+    ("bf16", 17, 300, 256, "f32"),      # M = 17: back on the 128-row tile path
 ])
 def test_project(dtype, M, N, K, out_dtype):
     A = synth.normal((M, K), 41, dtype=dtype)
     W = synth.normal((K, N), 42, std=K ** -0.5, dtype=dtype)
-    out = dlc.dlc_project(A.to(DEV), W.t().contiguous().to(DEV), out_dtype=TD[out_dtype])
+    dA, dW = A.to(DEV), W.t().contiguous().to(DEV)
+    out = dlc.dlc_project(dA, dW, out_dtype=TD[out_dtype])
     ref = O.project(A, W)
     tol = 1e-5 if out_dtype == "f32" else 8e-3
     assert_rows_close(out.cpu(), O.store_as(ref, out_dtype) if out_dtype == "bf16" else ref, tol, "project")
+    again = dlc.dlc_project(dA, dW, out_dtype=TD[out_dtype])
+    assert torch.equal(out, again), "dlc_project must give the same bits on a repeated call"
 
 
 # ------------------------------------------------------------ sliding window
