@@ -558,21 +558,39 @@ def query_projections(cfg, wl, n):
     q = torch.empty((B, cfg.n_h * cfg.c), dtype=torch.bfloat16, device=H.device)
     qh = torch.empty_like(q)
 
+    from dense_long_context_amd import binding
+
+    # one workspace for the five calls (each leaves it zeroed): the k-split of
+    # the row path where a projection has few output columns
+    ws_n = max(dlc.dlc_project_ws(B, W.shape[0], W.shape[1]) for W in Wq.values())
+    ws = torch.zeros(max(ws_n, 1), dtype=torch.uint8, device=H.device)
+    # the C-ABI argument tuples, marshalled once (as the decode steps are)
+    L = binding.lib()
+    stream = torch.cuda.current_stream(H.device).cuda_stream
+
+    def call(A, W, out):
+        M, K = A.shape
+        N = W.shape[0]
+        dt = binding.DLC_F32 if out.dtype == torch.float32 else binding.DLC_BF16
+        return (binding.DLC_BF16, M, N, K, A.data_ptr(), K, W.data_ptr(), K, out.data_ptr(), N, dt,
+                ws.data_ptr(), ws.numel(), stream)
+    calls = [[call(h, Wq["DQ"], cQ), call(cQ, Wq["IUQ"], qI), call(h, Wq["w"], wI), call(cQ, Wq["UQ"], q),
+              call(cQ, Wq["UQ_hca"], qh)] for h in hs]
+
     def step(i):
-        h = hs[i % len(hs)]
-        dlc.dlc_project(h, Wq["DQ"], out=cQ)
-        dlc.dlc_project(cQ, Wq["IUQ"], out=qI)
-        dlc.dlc_project(h, Wq["w"], out=wI)
-        dlc.dlc_project(cQ, Wq["UQ"], out=q)
-        dlc.dlc_project(cQ, Wq["UQ_hca"], out=qh)
+        for a in calls[i % len(calls)]:
+            rc = L.dlc_project(*a)
+            if rc != 0:
+                raise RuntimeError(binding.last_error())
     mean_ms, per = timed_calls(step, n)
     wbytes = 2 * (d * cfg.d_c + cfg.d_c * cfg.n_hI * cfg.cI + d * cfg.n_hI + 2 * cfg.d_c * cfg.n_h * cfg.c)
     flop = 2.0 * B * (d * cfg.d_c + cfg.d_c * cfg.n_hI * cfg.cI + d * cfg.n_hI + 2 * cfg.d_c * cfg.n_h * cfg.c)
     return {"ms_per_step": round(mean_ms, 5), "ms_per_step_events": percentiles(per),
             "weight_bytes_per_step": int(wbytes), "weight_gbs": round(wbytes / (mean_ms * 1e-3) / 1e9, 1),
             "tflops": round(flop / (mean_ms * 1e-3) / 1e12, 2),
-            "note": "dlc_project x5 for the B decode tokens of a step (c^Q, q^I, w^I, q, HCA q); weight-read "
-                    "bound at this batch; outside the compressed-attention step and its value"}
+            "note": "dlc_project x5 for the B decode tokens of a step (c^Q, q^I, w^I, q, HCA q) on the row-vector "
+                    "path with a k-split workspace; weight-read bound at this batch; outside the compressed-attention "
+                    "step and its value"}
 
 
 def run_steps(steps, s0, n, n_dec):

@@ -19,6 +19,7 @@ from .binding import (  # noqa: F401
     csa_index_topk_ws,
     default_scale,
     dlc_project,
+    dlc_project_ws,
     hca_attend,
     hca_attend_window,
     hca_attend_ws,
@@ -27,6 +28,7 @@ from .binding import (  # noqa: F401
     last_error,
     lib,
     mxfp4_quantize,
+    project_workspace,
     status_str,
     window_attend,
     window_attend_ws,

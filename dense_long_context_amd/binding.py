@@ -62,7 +62,8 @@ SIGNATURES = {
     "hca_attend_window": (_i32, [_i32, _i64, _i64, _i64, _i64, _i64, _vp, _vp, _i64, _vp, _i64, _vp, _i64, _i64,
                                  _f32, _vp, _vp, _vp, _sz, _vp]),
     "attend_sink": (_i32, [_i64, _i64, _i64, _vp, _vp, _vp, _vp]),
-    "dlc_project": (_i32, [_i32, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _i32, _vp]),
+    "dlc_project_ws": (_sz, [_i32, _i64, _i64, _i64]),
+    "dlc_project": (_i32, [_i32, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _i32, _vp, _sz, _vp]),
     "dlc_timing_arm": (_i32, [_i32, _vp, _vp]),
     "dlc_copy": (_i32, [_vp, _vp, _sz, _vp]),
     "dlc_read": (_i32, [_vp, _sz, _i32, _vp]),
@@ -511,9 +512,23 @@ def hca_attend_window(q, Chca, t, t_max, m_prime, Cwin, n_win, scale=0.0, out=No
 
 # --------------------------------------------------------------- projection
 
-def dlc_project(A, Wt, out=None, out_dtype=None):
-    """out[M][N] = A[M][K] . W with W given transposed as Wt [N][K]; fp32 accumulation."""
-    _on_device(A.device, A=A, Wt=Wt, out=out)
+def dlc_project_ws(M, N, K, dtype=torch.bfloat16):
+    """Bytes of the optional dlc_project workspace for an [M][K] x [K][N] call (0: none used)."""
+    return lib().dlc_project_ws(DLC_BF16 if dtype == torch.bfloat16 else DLC_F32, M, N, K)
+
+
+def project_workspace(M, N, K, device, dtype=torch.bfloat16):
+    """A zeroed workspace for dlc_project calls of this shape (None if the call uses none); every
+    call leaves it zeroed, so calls of any shape it is large enough for can reuse it."""
+    n = dlc_project_ws(M, N, K, dtype)
+    return torch.zeros(n, dtype=torch.uint8, device=device) if n else None
+
+
+def dlc_project(A, Wt, out=None, out_dtype=None, ws=None):
+    """out[M][N] = A[M][K] . W with W given transposed as Wt [N][K]; fp32 accumulation.
+    ws: optional zeroed workspace (project_workspace) that lets a call with few rows spread
+    its k-range over more workgroups."""
+    _on_device(A.device, A=A, Wt=Wt, out=out, ws=ws)
     M, K = A.shape
     N = Wt.shape[0]
     _need(Wt.dim() == 2 and Wt.shape[1] == K and Wt.dtype == A.dtype, "Wt must be [N][K] in A's dtype")
@@ -522,9 +537,10 @@ def dlc_project(A, Wt, out=None, out_dtype=None):
         out = torch.empty((M, N), dtype=out_dtype or A.dtype, device=A.device)
     _need(out.stride(1) == 1 and tuple(out.shape) == (M, N), "out must be [M][N] with contiguous rows")
     _need(out.dtype in (torch.float32, A.dtype), "out must be fp32 or A's dtype")
+    _need(ws is None or ws.is_contiguous(), "ws must be contiguous")
     _check("dlc_project", lib().dlc_project(
         _dt(A), M, N, K, _p(A), _stride(A, 0, K), _p(Wt), _stride(Wt, 0, K), _p(out), _stride(out, 0, N), _dt(out),
-        _stream(A.device)))
+        None if ws is None else _p(ws), 0 if ws is None else ws.numel() * ws.element_size(), _stream(A.device)))
     return out
 
 

@@ -158,6 +158,20 @@ __device__ __forceinline__ void wait_vm() {
   __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
 }
 
+// Values that cross workgroups within one kernel are written and read with
+// agent-scope atomic accesses, which this chip performs at the point of
+// coherence of all its L2 caches (global_store / global_load with sc1): once
+// a wave's stores have completed (vmcnt 0), another workgroup's atomic loads
+// see them, with no L2 write-back or invalidation, whichever XCD it runs on.
+template <typename T>
+__device__ __forceinline__ void st_agent(T* p, T v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+template <typename T>
+__device__ __forceinline__ T ld_agent(const T* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // Workgroup barrier that waits only for LDS and scalar-memory operations:
 // __syncthreads would also drain every vector-memory load in flight (the
 // direct global->LDS loads of the next tiles).

@@ -1050,19 +1050,8 @@ __device__ __forceinline__ void find_in_lds(const uint32_t* h, uint32_t need, ui
 }
 
 // Values that cross workgroups inside the selection kernel (the chunk lists,
-// counts and the second histogram) are written and read with agent-scope
-// atomic accesses, which this chip performs at the point of coherence of
-// all its L2 caches (global_store / global_load with sc1): once a wave's
-// stores have completed (vmcnt 0), another workgroup's atomic loads see
-// them, with no L2 write-back or invalidation, whichever XCD it runs on.
-template <typename T>
-__device__ __forceinline__ void st_agent(T* p, T v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-template <typename T>
-__device__ __forceinline__ T ld_agent(const T* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
+// counts and the second histogram) are written and read with the
+// agent-scope accesses of st_agent / ld_agent.
 
 struct FinishLds {
   uint32_t off_sel[kMaxChunks], off_cand[kMaxChunks];

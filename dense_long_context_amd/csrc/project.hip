@@ -84,60 +84,81 @@ __global__ void __launch_bounds__(256) project_mfma_kernel(ProjArgs a) {
 // operand.  In each 32-deep step s, lane l loads 16 bytes of weight row
 // n0 + l%16 and of activation row l%16 (zero from row M on) at k = 32s +
 // 8(l/16): one load instruction reads 64 contiguous bytes of 16 weight rows.
-// The KW waves that share a 16-column tile take its steps interleaved (wave
-// w of the tile: steps w, w + KW, ...), U steps in flight; their partial sums
-// meet in LDS and are added in wave order, so the bits do not depend on
-// timing.  Steps past K are loaded from a clamped address and masked.
+// A column tile's steps are split over KW waves of one workgroup (wave w:
+// steps w, w + KW, ... of the workgroup's k-slice) and, with a workspace,
+// over S workgroups (blockIdx.y: k-slice y of S).  The wave sums meet in LDS
+// and are added in wave order; the slice sums go to the workspace, and the
+// last workgroup of a tile to arrive adds them in slice order.  So the bits
+// do not depend on timing.  Steps past K are masked.
 constexpr int kRowsWaves = 16, kRowsMaxM = 16;
 
-template <int KW>
-__global__ void __launch_bounds__(64 * kRowsWaves) __attribute__((amdgpu_waves_per_eu(1, 4))) project_rows_kernel(ProjArgs a) {
+struct RowsSplit {
+  uint32_t* cnt;   // [NT] arrival counters, zero between calls
+  float* part;     // [NT][S][64 lanes][4] slice sums in the D fragment layout
+  int64_t S, kss;  // slices per tile; k-steps per slice
+};
+
+template <int KW, bool SPLIT>
+__global__ void __launch_bounds__(64 * kRowsWaves) __attribute__((amdgpu_waves_per_eu(1, 4)))
+project_rows_kernel(ProjArgs a, RowsSplit sp) {
   constexpr int TPW = kRowsWaves / KW, U = 8;  // column tiles per workgroup; steps in flight
   __shared__ f32x4 red[KW > 1 ? 64 * kRowsWaves : 1];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int i16 = lane & 15, g = lane >> 4;
   const int kw = wave % KW;
-  const int64_t n0 = (int64_t(blockIdx.x) * TPW + wave / KW) * 16;
+  const int64_t tile = int64_t(blockIdx.x) * TPW + wave / KW, n0 = tile * 16;
   const int64_t K = a.K, KS = ceil_div(K, 32);
+  const int64_t ks0 = SPLIT ? int64_t(blockIdx.y) * sp.kss : 0;
+  const int64_t ks1 = SPLIT ? std::min(KS, ks0 + sp.kss) : KS;
   const bf16_raw* wp = static_cast<const bf16_raw*>(a.W) + std::min<int64_t>(n0 + i16, a.N - 1) * a.ldw;
   const bf16_raw* ap = static_cast<const bf16_raw*>(a.A) + std::min<int64_t>(i16, a.M - 1) * a.lda;
   const bool mrow = i16 < a.M;
-  // the wave's steps j = 0 .. nst-1 are k-steps kw + j*KW; unit u of group i
-  // is step i*U + u, and its registers are refilled with step (i+1)*U + u as
-  // soon as its MFMA has read them.  Every load is unconditional (past the
-  // wave's steps from a clamped address, masked), so the compiler keeps all
-  // U steps in flight across iterations.
-  const int64_t nst = KS > kw ? ceil_div(KS - kw, int64_t(KW)) : 0;
+  // the wave's steps j = 0 .. nst-1 are k-steps ks0 + kw + j*KW; unit u of
+  // group i is step i*U + u, and its registers are refilled with step
+  // (i+1)*U + u as soon as its MFMA has read them.  Inside the loop every
+  // load is unconditional (past the wave's steps from a clamped address,
+  // masked), so the compiler keeps all U steps in flight across iterations;
+  // the last group is peeled and loads nothing more.
+  const int64_t span = ks1 - ks0;
+  const int64_t nst = span > kw ? ceil_div(span - kw, int64_t(KW)) : 0;
   const int64_t ng = ceil_div(nst, int64_t(U));
   uint4 wv[U], av[U];
   bool in[U];
   auto load = [&](int64_t j, int u) {  // K % 8 == 0: a lane's eight elements are all in or all out
-    const int64_t k = 32 * (kw + j * KW) + 8 * g;
+    const int64_t k = 32 * (ks0 + kw + j * KW) + 8 * g;
     in[u] = j < nst && k < K;
     const int64_t kc = in[u] ? k : K - 8;
     wv[u] = *reinterpret_cast<const uint4*>(wp + kc);
     av[u] = *reinterpret_cast<const uint4*>(ap + kc);
   };
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  auto mfma = [&](int u) {
+    const uint4 z = make_uint4(0, 0, 0, 0);
+    const uint4 w = in[u] ? wv[u] : z;
+    const uint4 x = in[u] && mrow ? av[u] : z;
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, w), __builtin_bit_cast(bf16x8, x), acc,
+                                                  0, 0, 0);
+  };
   // (the empty asm statements with a memory clobber keep the compiler from
-  // merging a step's loads from both loop entries into one load at the
-  // loop head, which would leave nothing in flight across iterations)
+  // merging a step's loads from both loop entries into one load at the loop
+  // head, which would leave nothing in flight across iterations)
   if (ng > 0) {
 #pragma unroll
-    for (int u = 0; u < U; ++u) load(u, u);
+    for (int u = 0; u < U; ++u) {
+      in[u] = false;
+      if (u < nst) load(u, u);  // uniform: a wave with fewer steps loads no more than it has
+    }
     asm volatile("" ::: "memory");
-    for (int64_t i = 0; i < ng; ++i) {
+    for (int64_t i = 0; i + 1 < ng; ++i) {
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        const uint4 z = make_uint4(0, 0, 0, 0);
-        const uint4 w = in[u] ? wv[u] : z;
-        const uint4 x = in[u] && mrow ? av[u] : z;
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, w), __builtin_bit_cast(bf16x8, x),
-                                                      acc, 0, 0, 0);
+        mfma(u);
         load((i + 1) * U + u, u);
+        asm volatile("" ::: "memory");
       }
-      asm volatile("" ::: "memory");
     }
+#pragma unroll
+    for (int u = 0; u < U; ++u) mfma(u);
   }
   if constexpr (KW > 1) {
     red[tid] = acc;
@@ -147,6 +168,29 @@ __global__ void __launch_bounds__(64 * kRowsWaves) __attribute__((amdgpu_waves_p
       const f32x4 v = red[tid + 64 * w];
       acc[0] += v[0]; acc[1] += v[1]; acc[2] += v[2]; acc[3] += v[3];
     }
+  }
+  if constexpr (SPLIT) {
+    if (n0 >= a.N) return;  // a tile past N (last workgroup): no counter
+    float* mine = sp.part + ((tile * sp.S + blockIdx.y) * 64 + lane) * 4;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) st_agent(mine + r, acc[r]);
+    wait_vm<0>();  // the slice sum is visible before the arrival
+    uint32_t prev = 0;
+    if (lane == 0) prev = __hip_atomic_fetch_add(sp.cnt + tile, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    prev = __shfl(prev, 0);
+    if (prev != uint32_t(sp.S - 1)) return;
+    // the slice sums in slice order; the tile's slots and counter are left
+    // zero, so that the next call, whatever its shape, finds the workspace
+    // as the first one did
+    float* all = sp.part + (tile * sp.S * 64 + lane) * 4;
+    acc = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int64_t y = 0; y < sp.S; ++y)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc[r] += ld_agent(all + y * 256 + r);
+    for (int64_t y = 0; y < sp.S; ++y)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) st_agent(all + y * 256 + r, 0.f);
+    if (lane == 0) st_agent(sp.cnt + tile, 0u);
   }
   // D: lane l holds rows n0 + 4(l/16) + r of column m = l%16
   if (!mrow) return;
@@ -162,11 +206,41 @@ __global__ void __launch_bounds__(64 * kRowsWaves) __attribute__((amdgpu_waves_p
   }
 }
 
+// The row path's plan: waves per column tile inside a workgroup (doubled
+// while the grid is under one workgroup per CU and every wave keeps four
+// steps at least), then, with a workspace, k-slices over workgroups (doubled
+// while the grid is under 256 workgroups and every wave keeps a step).
+struct RowsPlan {
+  int kw;
+  int64_t blocks, S, kss, NT;
+};
+RowsPlan rows_plan(int64_t N, int64_t K, bool split) {
+  RowsPlan p{1, 0, 1, 0, ceil_div(N, int64_t(16))};
+  const int64_t KS = ceil_div(K, int64_t(32));
+  while (p.kw < kRowsWaves && ceil_div(p.NT, int64_t(kRowsWaves / p.kw)) < 256 && KS >= 4 * p.kw) p.kw *= 2;
+  p.blocks = ceil_div(p.NT, int64_t(kRowsWaves / p.kw));
+  if (split)
+    while (p.blocks * p.S < 256 && ceil_div(KS, 2 * p.S) >= p.kw) p.S *= 2;
+  p.kss = ceil_div(KS, p.S);
+  p.S = ceil_div(KS, p.kss);
+  return p;
+}
+size_t rows_ws_bytes(const RowsPlan& p) {
+  return p.S > 1 ? align_up(size_t(p.NT) * 4, 256) + size_t(p.NT) * size_t(p.S) * 64 * 16 : 0;
+}
+
 }  // namespace
 }  // namespace dlc
 
+extern "C" size_t dlc_project_ws(int dtype, int64_t M, int64_t N, int64_t K) {
+  using namespace dlc;
+  if (dtype != DLC_BF16 || M < 1 || M > kRowsMaxM || N < 1 || K < 1) return 0;
+  return rows_ws_bytes(rows_plan(N, K, true));
+}
+
 extern "C" int dlc_project(int dtype, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* Wt,
-                           int64_t ldw, void* out, int64_t ldo, int out_dtype, void* stream) {
+                           int64_t ldw, void* out, int64_t ldo, int out_dtype, void* ws, size_t ws_bytes,
+                           void* stream) {
   using namespace dlc;
   DLC_REQUIRE(dtype == DLC_F32 || dtype == DLC_BF16, DLC_E_DTYPE, "dlc_project: unsupported dtype %d", dtype);
   DLC_REQUIRE(out_dtype == DLC_F32 || out_dtype == dtype, DLC_E_DTYPE,
@@ -180,21 +254,26 @@ extern "C" int dlc_project(int dtype, int64_t M, int64_t N, int64_t K, const voi
   const bool mfma = dtype == DLC_BF16 && K % 8 == 0 && lda % 8 == 0 && ldw % 8 == 0 && aligned(A, 16) &&
                     aligned(Wt, 16);
   if (mfma && M <= kRowsMaxM) {
-    // waves per column tile: doubled while the grid is under one workgroup
-    // per CU and every wave keeps two steps at least
-    const int64_t NT = ceil_div(N, 16), KS = ceil_div(K, 32);
-    int kw = 1;
-    while (kw < kRowsWaves && ceil_div(NT, kRowsWaves / kw) < 256 && KS >= 4 * kw) kw *= 2;
-    const int64_t blocks = ceil_div(NT, kRowsWaves / kw);
-    DLC_REQUIRE(blocks < (int64_t(1) << 31), DLC_E_UNSUPPORTED, "dlc_project: too many column tiles");
-    const dim3 grid{(unsigned)blocks, 1u, 1u}, block{64u * kRowsWaves, 1u, 1u};
-    switch (kw) {
-      case 1: hipLaunchKernelGGL(project_rows_kernel<1>, grid, block, 0, s, a); break;
-      case 2: hipLaunchKernelGGL(project_rows_kernel<2>, grid, block, 0, s, a); break;
-      case 4: hipLaunchKernelGGL(project_rows_kernel<4>, grid, block, 0, s, a); break;
-      case 8: hipLaunchKernelGGL(project_rows_kernel<8>, grid, block, 0, s, a); break;
-      default: hipLaunchKernelGGL(project_rows_kernel<16>, grid, block, 0, s, a); break;
+    const RowsPlan full = rows_plan(N, K, true);
+    const size_t need = rows_ws_bytes(full);
+    DLC_REQUIRE(!ws || ws_bytes >= need, DLC_E_WORKSPACE, "dlc_project: workspace of %zu bytes, %zu needed",
+                ws_bytes, need);
+    const bool split = ws && need > 0;
+    const RowsPlan p = split ? full : rows_plan(N, K, false);
+    DLC_REQUIRE(p.blocks < (int64_t(1) << 31), DLC_E_UNSUPPORTED, "dlc_project: too many column tiles");
+    RowsSplit sp{nullptr, nullptr, p.S, p.kss};
+    if (split) {
+      sp.cnt = static_cast<uint32_t*>(ws);
+      sp.part = reinterpret_cast<float*>(static_cast<char*>(ws) + align_up(size_t(p.NT) * 4, 256));
     }
+    const dim3 grid{(unsigned)p.blocks, (unsigned)p.S, 1u}, block{64u * kRowsWaves, 1u, 1u};
+#define DLC_ROWS(kw_)                                                                    \
+  if (p.kw == kw_) {                                                                     \
+    if (split) hipLaunchKernelGGL((project_rows_kernel<kw_, true>), grid, block, 0, s, a, sp);  \
+    else hipLaunchKernelGGL((project_rows_kernel<kw_, false>), grid, block, 0, s, a, sp);       \
+  }
+    DLC_ROWS(1) DLC_ROWS(2) DLC_ROWS(4) DLC_ROWS(8) DLC_ROWS(16)
+#undef DLC_ROWS
   } else if (mfma) {
     const int64_t tiles = ceil_div(M, TM) * ceil_div(N, TN);
     DLC_REQUIRE(tiles < (int64_t(1) << 31), DLC_E_UNSUPPORTED, "dlc_project: too many tiles");

@@ -354,14 +354,28 @@ int attend_sink(int64_t rows, int64_t n_h, int64_t c, float* out, float* lse, co
  *  Wt   the weight matrix W [K][N] stored transposed, Wt[N][K] with row
  *       stride ldw, in dtype
  *  out  [M][N] with row stride ldo, stored in out_dtype (DLC_F32 or dtype)
+ *  ws   optional workspace of ws_bytes >= dlc_project_ws(dtype, M, N, K)
+ *       bytes, or NULL.  It must be all zero before its first use; every
+ *       call leaves it all zero again, so calls of any shape can reuse it
+ *       (calls that share one workspace must not run at the same time).  A
+ *       smaller non-NULL workspace returns DLC_E_WORKSPACE.
  *
  * bf16 with K, lda, ldw multiples of 8 and A, Wt 16-byte aligned runs on
  * MFMA: 128x128 output tiles, or at M <= 16 (a decode step's tokens) a
- * row-vector path that streams the weight rows across the whole chip (its
- * cost is the read of Wt).  Other cases run a VALU kernel.
+ * row-vector path that streams the weight rows (its cost is the read of
+ * Wt).  With a workspace the row path also splits the k-range of a column
+ * tile over several workgroups, which pays where N is small and K large;
+ * the slices are added in a fixed order, so the result is bitwise the same
+ * from call to call (but not the same bits as without the workspace).
+ * Other cases run a VALU kernel.
+ *
+ * dlc_project_ws - the workspace bytes that let dlc_project split the
+ * k-range at this shape (0: it never splits here, pass NULL).
  */
 int dlc_project(int dtype, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
-                const void* Wt, int64_t ldw, void* out, int64_t ldo, int out_dtype, void* stream);
+                const void* Wt, int64_t ldw, void* out, int64_t ldo, int out_dtype,
+                void* ws, size_t ws_bytes, void* stream);
+size_t dlc_project_ws(int dtype, int64_t M, int64_t N, int64_t K);
 
 /*
  * Measurement support (not part of the method).

@@ -278,10 +278,17 @@ def test_timing_arm_stages(L):
 
 
 def test_project_validation(L):
-    assert L.dlc_project(BF16, 4, 4, 0, P, 8, P, 8, P, 4, BF16, None) == E_INVAL
-    assert L.dlc_project(BF16, 4, 4, 8, P, 4, P, 8, P, 4, BF16, None) == E_SHAPE
-    assert L.dlc_project(F32, 4, 4, 8, P, 8, P, 8, P, 4, BF16, None) == E_DTYPE
-    assert L.dlc_project(BF16, 0, 4, 8, P, 8, P, 8, P, 4, BF16, None) == OK
+    assert L.dlc_project(BF16, 4, 4, 0, P, 8, P, 8, P, 4, BF16, None, 0, None) == E_INVAL
+    assert L.dlc_project(BF16, 4, 4, 8, P, 4, P, 8, P, 4, BF16, None, 0, None) == E_SHAPE
+    assert L.dlc_project(F32, 4, 4, 8, P, 8, P, 8, P, 4, BF16, None, 0, None) == E_DTYPE
+    assert L.dlc_project(BF16, 0, 4, 8, P, 8, P, 8, P, 4, BF16, None, 0, None) == OK
+    # the row path's k-split workspace: used where N is small and K large, never above 16 rows
+    need = L.dlc_project_ws(BF16, 4, 512, 7168)
+    assert need >= 32 * 8 * 1024                                   # 32 column tiles, 8 slices of 1 KB each
+    assert L.dlc_project_ws(BF16, 4, 65536, 512) == 0              # enough column tiles already
+    assert L.dlc_project_ws(BF16, 17, 512, 7168) == 0              # the 128-row tile path
+    assert L.dlc_project_ws(F32, 4, 512, 7168) == 0
+    assert L.dlc_project(BF16, 4, 512, 7168, P, 7168, P, 7168, P, 512, BF16, P, need - 1, None) == E_WORKSPACE
 
 
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):

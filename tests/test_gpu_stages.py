@@ -437,17 +437,42 @@ def test_hca_attend_window_long_splits():
     ("bf16", 7, 512, 7168, "bf16"),     # the query down-projection's shape, 16 waves a tile
     ("bf16", 16, 64, 7168, "f32"),      # M = 16, four column tiles
     ("bf16", 17, 300, 256, "f32"),      # M = 17: back on the 128-row tile path
+    ("bf16", 4, 64, 7168, "f32"),       # the indexer weight projection's shape: 4 tiles, k split 8 ways
+    ("bf16", 2, 200, 968, "bf16"),      # 13 tiles (last one ragged), k split 4 ways into slices of 8, 8, 8, 7 steps
 ])
 def test_project(dtype, M, N, K, out_dtype):
     A = synth.normal((M, K), 41, dtype=dtype)
     W = synth.normal((K, N), 42, std=K ** -0.5, dtype=dtype)
     dA, dW = A.to(DEV), W.t().contiguous().to(DEV)
-    out = dlc.dlc_project(dA, dW, out_dtype=TD[out_dtype])
     ref = O.project(A, W)
+    want = O.store_as(ref, out_dtype) if out_dtype == "bf16" else ref
     tol = 1e-5 if out_dtype == "f32" else 8e-3
-    assert_rows_close(out.cpu(), O.store_as(ref, out_dtype) if out_dtype == "bf16" else ref, tol, "project")
+    out = dlc.dlc_project(dA, dW, out_dtype=TD[out_dtype])
+    assert_rows_close(out.cpu(), want, tol, "project")
     again = dlc.dlc_project(dA, dW, out_dtype=TD[out_dtype])
     assert torch.equal(out, again), "dlc_project must give the same bits on a repeated call"
+    # with a workspace: the row path may split the k-range over workgroups
+    ws = dlc.project_workspace(M, N, K, DEV, TD[dtype])
+    if ws is not None:
+        split = dlc.dlc_project(dA, dW, out_dtype=TD[out_dtype], ws=ws)
+        assert_rows_close(split.cpu(), want, tol, "project, k split over workgroups")
+        assert int(ws.count_nonzero()) == 0, "the workspace is left all zero"
+        again = dlc.dlc_project(dA, dW, out_dtype=TD[out_dtype], ws=ws)
+        assert torch.equal(split, again), "the k-split result must be the same bits on a reused workspace"
+
+
+@pytest.mark.gpu
+def test_project_workspace_shared():
+    """One workspace for calls of different shapes (each leaves it zeroed): the
+    query down-projection, the indexer weights and a wide projection in turn."""
+    shapes = [(4, 512, 7168), (4, 64, 7168), (4, 8192, 512), (3, 200, 968), (4, 512, 7168)]
+    ws = torch.zeros(max(dlc.dlc_project_ws(M, N, K) for M, N, K in shapes), dtype=torch.uint8, device=DEV)
+    for i, (M, N, K) in enumerate(shapes):
+        A = synth.normal((M, K), 60 + i, dtype="bf16")
+        W = synth.normal((K, N), 70 + i, std=K ** -0.5, dtype="bf16")
+        out = dlc.dlc_project(A.to(DEV), W.t().contiguous().to(DEV), out_dtype=torch.float32, ws=ws)
+        assert_rows_close(out.cpu(), O.project(A, W), 1e-5, f"project {M}x{N}x{K}, shared workspace")
+        assert int(ws.count_nonzero()) == 0
 
 
 # ------------------------------------------------------------ sliding window
