@@ -17,6 +17,7 @@ import pytest
 import torch
 
 import dense_long_context_amd as dlc
+from dense_long_context_amd import binding
 import oracle as O
 import synth
 from devtools import DEV, FlipTally, assert_rows_close, check_scores, check_topk, f64, need_gpu, score_bound
@@ -593,3 +594,19 @@ def test_hca_attend_window(dtype, B, n_h, c, mp, cap, ts, ring):
         o_r, l_r = O.merge_lse(o1, l1, o2, l2)
         assert_rows_close(o[b, 0], o_r, TOL_ATT[dtype], f"hca+window b={b}")
         assert np.abs(lse[b, 0].cpu().numpy() - l_r).max() <= TOL_ATT[dtype]
+
+
+# ------------------------------------------------------------------ copy kernel
+
+@pytest.mark.parametrize("nbytes", [16, 4096, 4096 + 48, (1 << 20) + 16 * 37])
+def test_copy_kernel(nbytes):
+    """dlc_copy moves every byte: one 16-byte element per thread and pass,
+    ragged last block (the bandwidth reference also copies the benchmark's
+    caches)."""
+    src = torch.randint(0, 256, (nbytes,), dtype=torch.uint8, device=DEV)
+    buf = torch.full((nbytes + 4096,), 7, dtype=torch.uint8, device=DEV)
+    dst = buf[:nbytes]                      # the bytes after it must stay untouched
+    binding.dlc_copy(dst, src)
+    torch.cuda.synchronize()
+    assert torch.equal(dst, src)
+    assert (buf[nbytes:] == 7).all()
