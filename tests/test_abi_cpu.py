@@ -197,6 +197,9 @@ def test_attend_validation(L):
     assert csa(q=P + 2) == E_INVAL                       # MFMA path needs 16-byte alignment
     assert csa(dtype=F32, c=2048) == E_UNSUPPORTED
     assert csa(B=4, n_h=128, c=512, k=1024) == E_WORKSPACE
+    # the c = 512 kernel lists a split's gathered rows in LDS: at most 256
+    # splits of 2048 keys, refused beyond that before anything is launched
+    assert csa(n_h=128, c=512, k=256 * 2048 + 1, ws=P, wsb=1 << 40) == E_UNSUPPORTED
     assert L.hca_attend(BF16, 1, 1, 4, 128, 128, P, P, 4, P, 1024, 0.0, P, None, None, 0, None) == E_SHAPE
     assert L.hca_attend(BF16, 1, 1, 4, 128, 0, P, P, 4, P, 100, 0.0, P, None, None, 0, None) == E_INVAL
 
