@@ -180,6 +180,25 @@ __global__ void __launch_bounds__(256) scores_valu_kernel(IdxArgs a) {
 #define DLC_SCORES_RWGS 768  // its workgroups per call (three per CU, one round)
 #endif
 
+// Scores a decode scores wave keeps in LDS while it streams keys, written
+// out after its last tile: interleaving the score stores with the key stream
+// costs the stream more than the same stores issued together at the end.
+// Waves with more tiles store each tile's scores as they come.
+#ifndef DLC_SCORE_STAGE_TILES
+#define DLC_SCORE_STAGE_TILES 64
+#endif
+constexpr int kStageTiles = DLC_SCORE_STAGE_TILES;
+
+// the staged scores of a wave (lane group g takes tiles g, g+4, ...)
+__device__ __forceinline__ void store_staged(float* srow, const float (*st)[16], int64_t my_tiles, int64_t first,
+                                             int64_t step, int64_t nvis, int lane) {
+  const int r16 = lane & 15, g = lane >> 4;
+  for (int64_t i = g; i < my_tiles; i += 4) {
+    const int64_t s = (first + i * step) * 16 + r16;
+    if (s < nvis) srow[s] = st[i][r16];
+  }
+}
+
 // The bf16 kernel loads the key operands straight into registers: each
 // lane loads, per 16-key tile, the four 16-byte pieces of its key row that
 // its K^T operand needs (row r16 of the tile, bytes 64*kt + 16*g), so one
@@ -210,6 +229,7 @@ scores_reg_kernel(IdxArgs a) {
   static_assert(HT <= 4, "one 16-head block of queries per staging wave");
   __shared__ uint32_t hist[kBins];
   __shared__ __attribute__((aligned(1024))) unsigned char sQ[HT][16 * ROWB];
+  __shared__ float sS[4][kStageTiles][16];
   const int64_t bq = blockIdx.y;
   clear_select_state(a, bq);
   const int64_t vmax = visible_max(a);  // rows below vmax exist whatever this query's t
@@ -252,6 +272,7 @@ scores_reg_kernel(IdxArgs a) {
     return;
   }
   const int64_t my_tiles = n_tiles > first ? (n_tiles - first + step - 1) / step : 0;
+  const bool staged = my_tiles <= kStageTiles;  // wave-uniform
   for (int i = threadIdx.x; i < kBins; i += blockDim.x) hist[i] = 0;
   float wv[HT][4];
 #pragma unroll
@@ -302,12 +323,14 @@ scores_reg_kernel(IdxArgs a) {
       const int64_t s = (first + it * step) * 16 + r16;
       if (g == 0 && s < nvis) {
         const float score = canon_zero(part);
-        srow[s] = score;
+        if (staged) sS[wave][it][r16] = score;
+        else srow[s] = score;
         atomicAdd(&hist[order_key(score) >> kShift1], 1u);
       }
     }
   }
   __builtin_amdgcn_s_waitcnt(0);  // the tiles loaded past the end
+  if (staged) store_staged(srow, sS[wave], my_tiles, first, step, nvis, lane);
   flush_hist(hist, a.hist + bq * kBins);
 }
 
@@ -343,6 +366,7 @@ __global__ void __launch_bounds__(256) scores_fp4_reg_kernel(IdxArgs a) {
   constexpr int HT = 4;          // head tiles: up to 64 heads
   static_assert(CI == 128 || CI == 256, "c^I");
   __shared__ uint32_t hist[kBins];
+  __shared__ float sS[4][kStageTiles][16];
   const int64_t bq = blockIdx.y;
   clear_select_state(a, bq);
   const int64_t vmax = visible_max(a);  // rows below vmax exist whatever this query's t
@@ -376,6 +400,7 @@ __global__ void __launch_bounds__(256) scores_fp4_reg_kernel(IdxArgs a) {
     return;
   }
   const int64_t my_tiles = n_tiles > first ? (n_tiles - first + step - 1) / step : 0;
+  const bool staged = my_tiles <= kStageTiles;  // wave-uniform
   for (int i = threadIdx.x; i < kBins; i += blockDim.x) hist[i] = 0;
   // queries (A operand, rows = heads): head ht*16 + r16, block 4j + g; heads
   // past n_hI take zero codes (their weight is 0 too)
@@ -440,12 +465,14 @@ __global__ void __launch_bounds__(256) scores_fp4_reg_kernel(IdxArgs a) {
       const int64_t s = (first + it * step) * 16 + r16;
       if (g == 0 && s < nvis) {
         const float score = canon_zero(part);
-        srow[s] = score;
+        if (staged) sS[wave][it][r16] = score;
+        else srow[s] = score;
         atomicAdd(&hist[order_key(score) >> kShift1], 1u);
       }
     }
   }
   __builtin_amdgcn_s_waitcnt(0);  // the tiles loaded past the end
+  if (staged) store_staged(srow, sS[wave], my_tiles, first, step, nvis, lane);
   flush_hist(hist, a.hist + bq * kBins);
 }
 
