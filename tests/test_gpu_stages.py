@@ -160,6 +160,9 @@ def test_compress_neg_inf_logits(dtype, c, m, n):
     ("bf16", 1, 1, 64, 256, 4, 16, 600, [2400]),
     ("bf16", 1, 2, 64, 128, 4, 8192, 20000, [80000, 40003]),  # the largest k the ABI takes
     ("bf16", 1, 1, 64, 128, 4, 2048, 200000, [800000]),     # 447 chunks of 448 entries
+    # 3.2M visible entries: 65 or 66 tiles a wave, past the 64 whose scores a
+    # wave keeps in LDS, so these waves store each tile's scores as they go
+    ("bf16", 1, 1, 64, 128, 4, 1024, 3200000, [12800000]),
 ])
 def test_index_topk(dtype, B, n_q, n_hI, cI, m, k, cap, ts):
     seed = 500 + cap
