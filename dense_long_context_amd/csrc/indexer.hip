@@ -305,12 +305,14 @@ scores_reg_kernel(IdxArgs a) {
       f32x4 acc[HT];
 #pragma unroll
       for (int ht = 0; ht < HT; ++ht) acc[ht] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (it < my_tiles) {  // the last group's tiles past my_tiles are loaded, not computed
 #pragma unroll
-      for (int kt = 0; kt < KT; ++kt)
+        for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
-        for (int ht = 0; ht < HT; ++ht)
-          acc[ht] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qf[ht][kt], __builtin_bit_cast(bf16x8, kb[u][kt]),
-                                                            acc[ht], 0, 0, 0);
+          for (int ht = 0; ht < HT; ++ht)
+            acc[ht] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qf[ht][kt], __builtin_bit_cast(bf16x8, kb[u][kt]),
+                                                              acc[ht], 0, 0, 0);
+      }
       load(it + U, kb[u]);
       float ps[4];
 #pragma unroll
