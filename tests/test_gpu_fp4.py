@@ -170,3 +170,30 @@ def test_index_topk_fp4_nothing_visible():
     idx, cnt = dlc.csa_index_topk_fp4(qI.to(DEV), wI.to(DEV), KIc, KIs, t.to(DEV), 3, 4, 8)
     assert cnt.cpu().tolist() == [[0], [0]]
     assert (idx.cpu() == -1).all()
+
+
+def test_index_topk_fp4_unstaged_waves():
+    """3.2M visible entries: every wave of the FP4 decode scores kernel has 65
+    tiles, past the 64 whose scores it keeps in LDS, so it stores each tile's
+    scores as they come.  The selection must equal the rule applied to the
+    device's own scores exactly; the scores of 20000 sampled entries are
+    checked against the oracle (the oracle's quantizer over all 3.2M rows
+    would take minutes)."""
+    B, n_q, n_hI, cI, m, k, cap = 1, 1, 64, 128, 4, 1024, 3200000
+    t_q = 4 * cap
+    qI = synth.normal((B, n_q, n_hI, cI), 990, dtype="bf16")
+    wI = synth.normal((B, n_q, n_hI), 991, dtype="f32")
+    KI = synth.normal((B, cap, cI), 992, dtype="bf16")
+    KIc, KIs = dlc.mxfp4_quantize(KI.to(DEV))
+    t = torch.tensor([[t_q]], dtype=torch.int64)
+    scores = torch.full((B, n_q, cap), float("nan"), dtype=torch.float32, device=DEV)
+    idx, cnt = dlc.csa_index_topk_fp4(qI.to(DEV), wI.to(DEV), KIc, KIs, t.to(DEV), t_q, m, k, scores=scores)
+    torch.cuda.synchronize()
+    idx, cnt, sc = idx.cpu().numpy(), cnt.cpu().numpy(), scores.cpu().numpy()
+    assert np.isfinite(sc[0, 0]).all(), "every visible entry's score is written"
+    rows = np.sort(np.random.default_rng(3).choice(cap, 20000, replace=False))
+    Ks = KI[0, rows]
+    ref = O.index_scores_fp4(qI[0, 0], wI[0, 0], Ks, 4 * len(rows), m)
+    check_scores(sc[0, 0, rows], ref, _bound_fp4(qI[0, 0], wI[0, 0], Ks), "sampled fp4 scores")
+    exact = O.topk_select(sc[0, 0], k)
+    assert int(cnt[0, 0]) == k and np.array_equal(idx[0, 0], exact)
