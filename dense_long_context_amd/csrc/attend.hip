@@ -442,6 +442,21 @@ constexpr int kTileBytes = 34816;   // 32 rows of 1 KB at the offsets of h16_row
 constexpr int kMaxGatherKeys = 2048;  // keys per split whose rows sit in LDS
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 
+// One 16-byte piece of a bf16 split partial.  The partials are read once,
+// by the combine kernel (on any XCD), so they are written as nontemporal
+// stores rather than left as dirty lines in this XCD's L2 for the write-back
+// at the kernel's end.
+#ifndef DLC_NT_PARTIALS
+#define DLC_NT_PARTIALS 1
+#endif
+typedef unsigned int u32x4_nt __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void store_partial(bf16_raw* p, const bf16x8& v) {
+  if constexpr (DLC_NT_PARTIALS != 0)
+    __builtin_nontemporal_store(__builtin_bit_cast(u32x4_nt, v), reinterpret_cast<u32x4_nt*>(p));
+  else
+    *reinterpret_cast<bf16x8*>(p) = v;
+}
+
 // ------------------------------------------------------------------ MFMA path, c = 512, 16 heads per wave
 //
 // Eight waves, each owning 16 heads over all 512 dims, so no partial S^T is
@@ -888,7 +903,7 @@ __global__ void __launch_bounds__(64 * NW) attend512_kernel(AttArgs a) {
             v[e] = (__bf16)(o[4 * hb + 2 * jj][e] * inv[e]);
             v[4 + e] = (__bf16)(o[4 * hb + 2 * jj + 1][e] * inv[e]);
           }
-          *reinterpret_cast<bf16x8*>(dst0 + int64_t(16 * hb) * CD + 512 * (2 * wave + jj)) = v;
+          store_partial(dst0 + int64_t(16 * hb) * CD + 512 * (2 * wave + jj), v);
         }
       }
       return;
@@ -936,7 +951,7 @@ __global__ void __launch_bounds__(64 * NW) attend512_kernel(AttArgs a) {
         v[e] = (__bf16)(o[2 * j][e] * inv[e]);
         v[4 + e] = (__bf16)(o[2 * j + 1][e] * inv[e]);
       }
-      *reinterpret_cast<bf16x8*>(dst + 512 * j) = v;
+      store_partial(dst + 512 * j, v);
     }
     return;
   }
