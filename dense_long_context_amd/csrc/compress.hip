@@ -24,6 +24,11 @@ constexpr int kChunk = kPoolChunk;
 #define DLC_POOL_EPT 2
 #endif
 constexpr int64_t kEntriesPerThread = DLC_POOL_EPT;
+#ifndef DLC_NT_ENTRIES
+#define DLC_NT_ENTRIES 1
+#endif
+constexpr bool kNtEntries = DLC_NT_ENTRIES != 0;
+typedef unsigned int u32x4_pool __attribute__((ext_vector_type(4)));
 
 struct PoolArgs {
   const void* Z[2];      // [0]: a-stream (HCA: its only stream), [1]: b-stream
@@ -106,6 +111,12 @@ __global__ void __launch_bounds__(256) pool_kernel(PoolArgs a) {
     T* out = static_cast<T*>(a.out) + (int64_t(blockIdx.y) * a.cap + i) * a.c + j0;
     if constexpr (VEC == 1) {
       Fmt<T>::store(out, o[0]);
+    } else if constexpr (kNtEntries) {
+      // the entries are read by later calls only: nontemporal stores keep
+      // them out of the L2 that the stream passes through
+      T tmp[16 / sizeof(T)];
+      Fmt<T>::store_vec(tmp, o);
+      __builtin_nontemporal_store(*reinterpret_cast<const u32x4_pool*>(tmp), reinterpret_cast<u32x4_pool*>(out));
     } else {
       Fmt<T>::store_vec(out, o);
     }
