@@ -114,7 +114,7 @@ __global__ void __launch_bounds__(256) pool_kernel(PoolArgs a) {
     } else if constexpr (kNtEntries) {
       // the entries are read by later calls only: nontemporal stores keep
       // them out of the L2 that the stream passes through
-      T tmp[16 / sizeof(T)];
+      alignas(16) T tmp[16 / sizeof(T)];
       Fmt<T>::store_vec(tmp, o);
       __builtin_nontemporal_store(*reinterpret_cast<const u32x4_pool*>(tmp), reinterpret_cast<u32x4_pool*>(out));
     } else {
