@@ -61,7 +61,7 @@ def check_scores(got, ref, bound, what=""):
 
 
 def check_topk(idx_row, count, scores_ref, k, rel_tie=1e-4, dev_scores=None):
-    """Top-k parity for one query, at the band the benchmark spec fixes.
+    """Top-k parity for one query, at the target tie band (1e-4 relative at s_k).
 
     The device set must have k_eff = min(k, n) members, ascending, distinct,
     each visible, padded with -1.  It must equal the oracle's set (score

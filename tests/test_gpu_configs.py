@@ -16,7 +16,7 @@
 
 Tolerances: stored bf16 results 8e-3 row-relative (one bf16 rounding of an
 fp32 result); attention outputs 2e-2 row-relative for bf16 inputs and 1e-5
-for fp32; lse absolute at the same bars; top-k sets exact up to the benchmark spec's tie
+for fp32; lse absolute at the same bars; top-k sets exact up to the target tie
 band (devtools.check_topk: ties within 1e-4 relative at the k-th score), and,
 where the call returns its scores, exactly the selection rule applied to the
 device's own fp32 scores, which lie within their fp32 bound (score_bound).

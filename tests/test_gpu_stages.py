@@ -4,8 +4,8 @@ the degenerate cases (nothing visible, k >= visible, ties, masked indices).
 
 Tolerances (derived in the design notes): fp32 outputs 1e-5 row-relative;
 bf16-stored outputs 8e-3 row-relative (one bf16 rounding of an fp32 result);
-fp32 attention outputs from bf16 inputs 2e-2 row-relative (north-star bar);
-top-k per the tie rule in devtools.check_topk (the benchmark spec's band: ties within
+fp32 attention outputs from bf16 inputs 2e-2 row-relative (the target bar);
+top-k per the tie rule in devtools.check_topk (the target band: ties within
 1e-4 relative at the k-th score), and exactly the selection rule applied to the
 device's own fp32 scores; scores within their fp32 bound (devtools.score_bound).
 """
