@@ -446,6 +446,10 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 // by the combine kernel (on any XCD), so they are written as nontemporal
 // stores rather than left as dirty lines in this XCD's L2 for the write-back
 // at the kernel's end.
+#ifndef DLC_COMBINE8
+#define DLC_COMBINE8 1
+#endif
+constexpr bool kCombine8 = DLC_COMBINE8 != 0;  // more than 32 splits: eight waves a store
 #ifndef DLC_NT_PARTIALS
 #define DLC_NT_PARTIALS 1
 #endif
@@ -1054,7 +1058,7 @@ __global__ void __launch_bounds__(NT) combine_frag_kernel(const bf16_raw* op, co
   constexpr int CD = 512;
   __shared__ __attribute__((aligned(16))) float wsh[(kMaxSplits + 1) * 16];  // [part][head of the block]
   __shared__ float mh[16], lh[16];
-  __shared__ float4 red[4 * 2 * 64];  // wave sums [wave][2][lane] (W > 1 only with JB = 1, W <= 4)
+  __shared__ float4 red[8 * 2 * 64];  // wave sums [wave][2][lane] (W > 1 only with JB = 1, W <= 8)
   const int64_t nb = (n_h + 15) / 16;
   const int64_t bq = blockIdx.x / nb, hb = (int64_t(blockIdx.x) - bq * nb) * 16;
   const int tid = threadIdx.x, nthr = blockDim.x;
@@ -1344,6 +1348,9 @@ int run_attend(const char* name, int dtype, AttArgs a, int64_t BQ, int64_t nkeys
       else if (p.splits <= 32)
         hipLaunchKernelGGL((combine_frag_kernel<256, 8>), dim3(nb, 16u, 1u), dim3(256), 0, s, a.ob, a.lse, p.splits,
                            a.n_h, 4, out, lse, o_in, lse_in);
+      else if (kCombine8)
+        hipLaunchKernelGGL((combine_frag_kernel<512, 8>), dim3(nb, 16u, 1u), dim3(512), 0, s, a.ob, a.lse, p.splits,
+                           a.n_h, 8, out, lse, o_in, lse_in);
       else
         hipLaunchKernelGGL((combine_frag_kernel<256, 16>), dim3(nb, 16u, 1u), dim3(256), 0, s, a.ob, a.lse, p.splits,
                            a.n_h, 4, out, lse, o_in, lse_in);
